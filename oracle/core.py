@@ -1,0 +1,170 @@
+"""ctypes wrapper of the plain C oracle (``kvq_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  The wrapper marshals
+arrays; every step of the arithmetic is in the C file.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kvq_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+GCC_FLAGS = ["-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-std=c11"]
+
+
+def build_oracle(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc (no fast-math: IEEE division and rintf)."""
+    cmd = ["gcc", *GCC_FLAGS, "-o", out, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def load(path: str | None = None):
+    """Load (building first if absent) the oracle shared library."""
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    p = path or _LIB
+    if not os.path.exists(p):
+        build_oracle(out=p)
+    lib = ctypes.CDLL(p)
+    u8p = ctypes.POINTER(ctypes.c_uint8)
+    f32p = ctypes.POINTER(ctypes.c_float)
+    f64p = ctypes.POINTER(ctypes.c_double)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    lib.kvqo_f32_to_f16.argtypes = [ctypes.c_float]
+    lib.kvqo_f32_to_f16.restype = ctypes.c_uint16
+    lib.kvqo_f16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.kvqo_f16_to_f32.restype = ctypes.c_float
+    lib.kvqo_f32_to_f16_array.argtypes = [f32p, u16p, ctypes.c_int64]
+    for name in ("kvqo_q8_0_encode", "kvqo_q5_1_encode"):
+        getattr(lib, name).argtypes = [f32p, u8p]
+    for name in ("kvqo_q8_0_decode", "kvqo_q5_1_decode"):
+        getattr(lib, name).argtypes = [u8p, f64p]
+    for name in ("kvqo_quantize_k", "kvqo_quantize_v"):
+        getattr(lib, name).argtypes = [f32p, ctypes.c_int64, u8p]
+    lib.kvqo_attention.argtypes = [
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        f32p, ctypes.POINTER(u8p), ctypes.POINTER(u8p), i64p, i64p, ctypes.c_int32,
+        f32p, ctypes.c_float, i64p, ctypes.c_int64, f32p, f32p]
+    lib.kvqo_attention.restype = ctypes.c_int
+    lib.kvqo_max_threads.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> the float32 values they denote (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def f32_to_f16(x, lib=None) -> np.ndarray:
+    lib = lib or load()
+    x = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib.kvqo_f32_to_f16_array(_ptr(x, ctypes.c_float), _ptr(out, ctypes.c_uint16), x.size)
+    return out
+
+
+def f16_to_f32(h, lib=None) -> np.ndarray:
+    lib = lib or load()
+    h = np.asarray(h, dtype=np.uint16).ravel()
+    return np.array([lib.kvqo_f16_to_f32(int(v)) for v in h], dtype=np.float32)
+
+
+def _block_op(fn, x, in_dtype, in_size, out_dtype, out_size):
+    x = np.ascontiguousarray(x, dtype=in_dtype)
+    assert x.size == in_size
+    out = np.empty(out_size, dtype=out_dtype)
+    in_c = ctypes.c_float if in_dtype == np.float32 else ctypes.c_uint8
+    out_c = ctypes.c_uint8 if out_dtype == np.uint8 else ctypes.c_double
+    fn(_ptr(x, in_c), _ptr(out, out_c))
+    return out
+
+
+def q8_0_encode(x, lib=None):
+    return _block_op((lib or load()).kvqo_q8_0_encode, x, np.float32, 32, np.uint8, 34)
+
+
+def q8_0_decode(b, lib=None):
+    return _block_op((lib or load()).kvqo_q8_0_decode, b, np.uint8, 34, np.float64, 32)
+
+
+def q5_1_encode(x, lib=None):
+    return _block_op((lib or load()).kvqo_q5_1_encode, x, np.float32, 32, np.uint8, 24)
+
+
+def q5_1_decode(b, lib=None):
+    return _block_op((lib or load()).kvqo_q5_1_decode, b, np.uint8, 24, np.float64, 32)
+
+
+def _quantize(fn, x, blk_bytes):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    assert x.size % 32 == 0
+    out = np.empty(x.size // 32 * blk_bytes, dtype=np.uint8)
+    fn(_ptr(x, ctypes.c_float), x.size, _ptr(out, ctypes.c_uint8))
+    return out
+
+
+def quantize_k(x, lib=None) -> np.ndarray:
+    """float32 values (any shape, size % 32 == 0) -> q8_0 bytes, flat."""
+    return _quantize((lib or load()).kvqo_quantize_k, x, 34)
+
+
+def quantize_v(x, lib=None) -> np.ndarray:
+    """float32 values (any shape, size % 32 == 0) -> q5_1 bytes, flat."""
+    return _quantize((lib or load()).kvqo_quantize_v, x, 24)
+
+
+def attention(q, k_planes, v_planes, base, length, *, n_kv_heads, window=0,
+              sinks=None, scale, sel=None, want_lse=True, lib=None):
+    """Exact attention.  q: float32 [B, T, H, hd].  k_planes / v_planes: per
+    session uint8 arrays whose row 0 holds logical row base[b].  Returns
+    (out [B,T,H,hd] float32, lse [B,T,H] float32 or None); entries not in
+    ``sel`` are NaN."""
+    lib = lib or load()
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    B, T, H, hd = q.shape
+    u8p = ctypes.POINTER(ctypes.c_uint8)
+    kp = [np.ascontiguousarray(p, dtype=np.uint8) for p in k_planes]
+    vp = [np.ascontiguousarray(p, dtype=np.uint8) for p in v_planes]
+    karr = (u8p * B)(*[_ptr(p, ctypes.c_uint8) for p in kp])
+    varr = (u8p * B)(*[_ptr(p, ctypes.c_uint8) for p in vp])
+    base = np.ascontiguousarray(base, dtype=np.int64)
+    length = np.ascontiguousarray(length, dtype=np.int64)
+    out = np.full((B, T, H, hd), np.nan, dtype=np.float32)
+    lse = np.full((B, T, H), np.nan, dtype=np.float32) if want_lse else None
+    s = None
+    if sinks is not None:
+        s = np.ascontiguousarray(sinks, dtype=np.float32)
+        assert s.shape == (H,)
+    selarr = None
+    if sel is not None:
+        selarr = np.ascontiguousarray(sel, dtype=np.int64)
+    rc = lib.kvqo_attention(
+        B, T, H, int(n_kv_heads), hd, _ptr(q, ctypes.c_float), karr, varr,
+        _ptr(base, ctypes.c_int64), _ptr(length, ctypes.c_int64), int(window),
+        _ptr(s, ctypes.c_float) if s is not None else None, float(scale),
+        _ptr(selarr, ctypes.c_int64) if selarr is not None else None,
+        0 if selarr is None else selarr.size,
+        _ptr(out, ctypes.c_float), _ptr(lse, ctypes.c_float) if lse is not None else None)
+    if rc != 0:
+        raise ValueError("oracle attention: argument outside the method's domain")
+    return out, lse
+
+
+def max_threads(lib=None) -> int:
+    return int((lib or load()).kvqo_max_threads())
