@@ -1,0 +1,415 @@
+// kvq_host.cpp -- the C ABI of libkvq (include/kvq.h): argument validation,
+// the host mirror of len/base, the ring planner, the split-K plan, and the
+// enqueueing of kernels through the launcher interface (kvq_internal.h).
+//
+// Pages followed (docs.rs):
+//  * memra-engine "Struct KvLayer": len is kept in lock-step with the device
+//    counter len_d; base_d mirrors ring.base(); physical = row - base; the
+//    live window is [max(0, len - window), len); the rebase arm is the only
+//    writer of base_d and runs on the host; rewinds move len only.
+//  * memra-engine "Struct Cache", rollback: full-attention KV is rolled back
+//    by setting len, with no copy.
+//  * memra-engine "Struct KvLayer", physical_rows: a logical range that is not
+//    resident is an error (here KVQ_ERANGE), not a silent clamp.
+//  * cortiq-engine "Struct LayerKvCache", export_wire / import_wire: geometry
+//    is checked, not assumed, and a call refuses rather than half-applying.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+
+struct kvq_cache {
+    kvq_config cfg;
+    kvq_sizes sz;
+    uint8_t* k;
+    uint8_t* v;
+    int32_t* counters;
+    std::vector<int64_t> len;    // host mirror of len_d
+    std::vector<int64_t> base;   // host mirror of base_d
+    int32_t split_rows;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+kvq_status fail(kvq_status s, const std::string& msg) {
+    g_err = msg;
+    return s;
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+kvq_status check_config(const kvq_config* c) {
+    if (!c) return fail(KVQ_EINVAL, "config is NULL");
+    if (c->k_fmt != KVQ_FMT_Q8_0 || c->v_fmt != KVQ_FMT_Q5_1)
+        return fail(KVQ_EUNSUPPORTED, "only K = q8_0 and V = q5_1 are implemented");
+    if (c->n_seqs < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1)
+        return fail(KVQ_EINVAL, "n_seqs, n_q_heads and n_kv_heads must be >= 1");
+    if (c->n_q_heads % c->n_kv_heads != 0)
+        return fail(KVQ_EINVAL, "n_q_heads must be a multiple of n_kv_heads");
+    if (c->head_dim < 32 || c->head_dim % 32 != 0)
+        return fail(KVQ_EINVAL, "head_dim must be a positive multiple of 32");
+    if (c->head_dim > kvq::kMaxHeadDim)
+        return fail(KVQ_EUNSUPPORTED, "head_dim above 256 is not implemented");
+    if (c->capacity < 1) return fail(KVQ_EINVAL, "capacity must be >= 1");
+    if (c->window < 0 || c->ring_step < 0) return fail(KVQ_EINVAL, "window and ring_step must be >= 0");
+    if (c->ring_step > 0 && (c->window <= 0 || (int64_t)c->window + c->ring_step > c->capacity))
+        return fail(KVQ_EINVAL, "a ring needs window > 0 and window + ring_step <= capacity");
+    int64_t row = (int64_t)c->n_kv_heads * c->head_dim / 32 * 34;
+    if (row * (int64_t)c->capacity > (int64_t)INT32_MAX * 4)
+        return fail(KVQ_EUNSUPPORTED, "a session plane above 8 GiB is not supported");
+    if ((int64_t)c->n_kv_heads * c->head_dim > (1 << 20))
+        return fail(KVQ_EUNSUPPORTED, "row too wide");
+    return KVQ_OK;
+}
+
+void sizes_of(const kvq_config* c, kvq_sizes* s) {
+    int64_t blocks = (int64_t)c->n_kv_heads * c->head_dim / 32;
+    s->k_row_bytes = (size_t)(blocks * 34);
+    s->v_row_bytes = (size_t)(blocks * 24);
+    s->k_session_stride = (size_t)round_up((int64_t)s->k_row_bytes * c->capacity, 256);
+    s->v_session_stride = (size_t)round_up((int64_t)s->v_row_bytes * c->capacity, 256);
+    s->k_planes_bytes = s->k_session_stride * (size_t)c->n_seqs;
+    s->v_planes_bytes = s->v_session_stride * (size_t)c->n_seqs;
+    s->counters_bytes = (size_t)round_up(((int64_t)2 * c->n_seqs + 4) * 4, 256);
+}
+
+int32_t* len_d(const kvq_cache* h) { return h->counters; }
+int32_t* base_d(const kvq_cache* h) { return h->counters + h->cfg.n_seqs; }
+int32_t* scratch_d(const kvq_cache* h) { return h->counters + 2 * h->cfg.n_seqs; }
+
+// Write dst[idx[i]] = val[i], in launches of up to kMaxSetPerLaunch entries.
+kvq_status enqueue_sets(int32_t* dst, const std::vector<int32_t>& idx,
+                        const std::vector<int32_t>& val, void* stream) {
+    for (size_t i0 = 0; i0 < idx.size(); i0 += kvq::kMaxSetPerLaunch) {
+        kvq::SetParams p{};
+        p.dst = dst;
+        p.n = (int32_t)std::min<size_t>(kvq::kMaxSetPerLaunch, idx.size() - i0);
+        for (int i = 0; i < p.n; ++i) {
+            p.idx[i] = idx[i0 + i];
+            p.val[i] = val[i0 + i];
+        }
+        const char* err = nullptr;
+        if (kvq::launch_set(p, stream, &err)) return fail(KVQ_EDEVICE, err ? err : "set kernel launch failed");
+    }
+    return KVQ_OK;
+}
+
+// Rows of the union of the T query rows' visible ranges: [lo, len).
+int64_t visible_lo(const kvq_cache* h, int64_t len, int32_t T) {
+    if (h->cfg.window <= 0) return 0;
+    return std::max<int64_t>(0, len - T + 1 - h->cfg.window);
+}
+
+struct Plan {
+    int32_t chunk;
+    int32_t splits;
+    size_t ml_bytes;
+    size_t o_bytes;
+};
+
+Plan make_plan(const kvq_cache* h, int32_t T) {
+    const kvq_config& c = h->cfg;
+    int64_t total = 0, maxvis = 1;
+    for (int b = 0; b < c.n_seqs; ++b) {
+        int64_t vis = std::max<int64_t>(0, h->len[b] - visible_lo(h, h->len[b], T));
+        total += vis;
+        maxvis = std::max(maxvis, vis);
+    }
+    int64_t chunk = h->split_rows;
+    if (chunk <= 0) {
+        // aim at about 512 workgroups of (session, chunk, KV head)
+        chunk = round_up(ceil_div(std::max<int64_t>(total, 1) * c.n_kv_heads, 512), kvq::kSplitQuantum);
+        chunk = std::min<int64_t>(std::max<int64_t>(chunk, 256), 1 << 16);
+    }
+    Plan p;
+    p.chunk = (int32_t)chunk;
+    p.splits = (int32_t)std::max<int64_t>(1, ceil_div(maxvis, chunk));
+    int64_t entries = (int64_t)c.n_seqs * p.splits * T * c.n_q_heads;
+    p.ml_bytes = (size_t)round_up(entries * 2 * 4, 256);
+    p.o_bytes = (size_t)round_up(entries * c.head_dim * 4, 256);
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_last_error(void) { return g_err.c_str(); }
+
+kvq_status kvq_required_bytes(const kvq_config* cfg, kvq_sizes* out) {
+    kvq_status s = check_config(cfg);
+    if (s != KVQ_OK) return s;
+    if (!out) return fail(KVQ_EINVAL, "out is NULL");
+    sizes_of(cfg, out);
+    return KVQ_OK;
+}
+
+kvq_status kvq_create(const kvq_config* cfg, void* k_planes, void* v_planes,
+                      int32_t* counters, kvq_stream stream, kvq_cache** out) {
+    kvq_status s = check_config(cfg);
+    if (s != KVQ_OK) return s;
+    if (!out) return fail(KVQ_EINVAL, "out is NULL");
+    if (!k_planes || !v_planes || !counters) return fail(KVQ_EINVAL, "a device buffer is NULL");
+    if (!aligned(k_planes, 256) || !aligned(v_planes, 256) || !aligned(counters, 256))
+        return fail(KVQ_EINVAL, "planes and counters must be 256-byte aligned");
+    kvq_cache* h = new kvq_cache();
+    h->cfg = *cfg;
+    sizes_of(cfg, &h->sz);
+    h->k = static_cast<uint8_t*>(k_planes);
+    h->v = static_cast<uint8_t*>(v_planes);
+    h->counters = counters;
+    h->len.assign(cfg->n_seqs, 0);
+    h->base.assign(cfg->n_seqs, 0);
+    h->split_rows = 0;
+    int n = 2 * cfg->n_seqs + 4;
+    std::vector<int32_t> idx(n), val(n, 0);
+    for (int i = 0; i < n; ++i) idx[i] = i;
+    s = enqueue_sets(counters, idx, val, stream);
+    if (s != KVQ_OK) {
+        delete h;
+        return s;
+    }
+    *out = h;
+    return KVQ_OK;
+}
+
+kvq_status kvq_append(kvq_cache* h, const void* k_new, const void* v_new, kvq_dtype dtype,
+                      int32_t T, const int32_t* n_new, kvq_stream stream) {
+    if (!h) return fail(KVQ_EINVAL, "handle is NULL");
+    if (!k_new || !v_new) return fail(KVQ_EINVAL, "k_new or v_new is NULL");
+    if (dtype != KVQ_F32 && dtype != KVQ_BF16) return fail(KVQ_EINVAL, "dtype must be F32 or BF16");
+    if (T < 1) return fail(KVQ_EINVAL, "T must be >= 1");
+    const kvq_config& c = h->cfg;
+    const int B = c.n_seqs;
+    std::vector<int64_t> cnt(B, T), nbase(h->base);
+    if (n_new)
+        for (int b = 0; b < B; ++b) {
+            if (n_new[b] < 0 || n_new[b] > T) return fail(KVQ_EINVAL, "n_new[b] must lie in [0, T]");
+            cnt[b] = n_new[b];
+        }
+    // Plan every session before touching anything.
+    for (int b = 0; b < B; ++b) {
+        if (cnt[b] == 0) continue;
+        int64_t L = h->len[b];
+        if (L + cnt[b] > INT32_MAX) return fail(KVQ_EINVAL, "length would overflow int32");
+        if (c.ring_step == 0) {
+            if (L + cnt[b] > c.capacity)
+                return fail(KVQ_ECAPACITY, "session " + std::to_string(b) + ": append past capacity");
+            continue;
+        }
+        int64_t nb = h->base[b];
+        while (L + cnt[b] - nb > c.capacity) nb += c.ring_step;
+        if (nb != h->base[b] && std::max<int64_t>(0, L + 1 - c.window) < nb)
+            return fail(KVQ_ERANGE, "session " + std::to_string(b) +
+                                        ": rebase would drop rows the first new row still sees");
+        nbase[b] = nb;
+    }
+    // Rebase: move the surviving rows down in non-overlapping slabs, then base_d.
+    std::vector<int32_t> set_idx, set_val;
+    int64_t max_slabs = 0;
+    for (int b = 0; b < B; ++b)
+        if (nbase[b] != h->base[b]) {
+            int64_t shift = nbase[b] - h->base[b];
+            int64_t keep = h->len[b] - nbase[b];
+            max_slabs = std::max(max_slabs, ceil_div(std::max<int64_t>(keep, 0), shift));
+            set_idx.push_back(B + b);
+            set_val.push_back((int32_t)nbase[b]);
+        }
+    for (int64_t slab = 0; slab < max_slabs; ++slab) {
+        kvq::MoveParams mp{};
+        mp.k_planes = h->k;
+        mp.v_planes = h->v;
+        mp.k_stride = (int64_t)h->sz.k_session_stride;
+        mp.v_stride = (int64_t)h->sz.v_session_stride;
+        mp.k_row = (int32_t)h->sz.k_row_bytes;
+        mp.v_row = (int32_t)h->sz.v_row_bytes;
+        mp.n = 0;
+        auto flush = [&]() -> kvq_status {
+            if (mp.n == 0) return KVQ_OK;
+            const char* err = nullptr;
+            if (kvq::launch_move(mp, stream, &err)) return fail(KVQ_EDEVICE, err ? err : "move kernel launch failed");
+            mp.n = 0;
+            return KVQ_OK;
+        };
+        for (int b = 0; b < B; ++b) {
+            if (nbase[b] == h->base[b]) continue;
+            int64_t shift = nbase[b] - h->base[b];
+            int64_t keep = h->len[b] - nbase[b];
+            int64_t k0 = slab * shift;
+            if (k0 >= keep) continue;
+            mp.sess[mp.n] = b;
+            mp.src_row[mp.n] = (int32_t)(shift + k0);
+            mp.dst_row[mp.n] = (int32_t)k0;
+            mp.rows[mp.n] = (int32_t)std::min(shift, keep - k0);
+            if (++mp.n == kvq::kMaxSessionsPerLaunch) {
+                kvq_status s = flush();
+                if (s != KVQ_OK) return s;
+            }
+        }
+        kvq_status s = flush();
+        if (s != KVQ_OK) return s;
+    }
+    if (!set_idx.empty()) {
+        kvq_status s = enqueue_sets(h->counters, set_idx, set_val, stream);
+        if (s != KVQ_OK) return s;
+    }
+    // Quantize-and-append, sessions in launches of up to kMaxSessionsPerLaunch.
+    for (int b0 = 0; b0 < B; b0 += kvq::kMaxSessionsPerLaunch) {
+        kvq::AppendParams ap{};
+        ap.k_new = k_new;
+        ap.v_new = v_new;
+        ap.k_planes = h->k;
+        ap.v_planes = h->v;
+        ap.k_stride = (int64_t)h->sz.k_session_stride;
+        ap.v_stride = (int64_t)h->sz.v_session_stride;
+        ap.len_d = len_d(h);
+        ap.base_d = base_d(h);
+        ap.done = scratch_d(h);
+        ap.dtype = dtype;
+        ap.B = B;
+        ap.T = T;
+        ap.Hkv = c.n_kv_heads;
+        ap.hd = c.head_dim;
+        ap.capacity = c.capacity;
+        ap.b0 = b0;
+        ap.nsess = std::min(kvq::kMaxSessionsPerLaunch, B - b0);
+        int64_t any = 0;
+        for (int i = 0; i < ap.nsess; ++i) {
+            ap.n_new[i] = (int32_t)cnt[b0 + i];
+            any += cnt[b0 + i];
+        }
+        if (!any) continue;
+        const char* err = nullptr;
+        if (kvq::launch_append(ap, stream, &err)) return fail(KVQ_EDEVICE, err ? err : "append kernel launch failed");
+    }
+    for (int b = 0; b < B; ++b) {
+        h->base[b] = nbase[b];
+        h->len[b] += cnt[b];
+    }
+    return KVQ_OK;
+}
+
+kvq_status kvq_decode_workspace_bytes(const kvq_cache* h, int32_t T, size_t* bytes) {
+    if (!h || !bytes) return fail(KVQ_EINVAL, "NULL argument");
+    if (T < 1) return fail(KVQ_EINVAL, "T must be >= 1");
+    Plan p = make_plan(h, T);
+    *bytes = p.ml_bytes + p.o_bytes;
+    return KVQ_OK;
+}
+
+kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, const float* sinks,
+                      float scale, float* out, float* lse, void* ws, size_t ws_bytes,
+                      kvq_stream stream) {
+    if (!h) return fail(KVQ_EINVAL, "handle is NULL");
+    if (!q || !out) return fail(KVQ_EINVAL, "q or out is NULL");
+    if (dtype != KVQ_F32 && dtype != KVQ_BF16) return fail(KVQ_EINVAL, "dtype must be F32 or BF16");
+    if (!std::isfinite(scale)) return fail(KVQ_EINVAL, "scale must be finite");
+    const kvq_config& c = h->cfg;
+    const int hpk = c.n_q_heads / c.n_kv_heads;
+    if (T < 1 || (int64_t)T * hpk > kvq::kMaxRows)
+        return fail(KVQ_EINVAL, "need 1 <= T * n_q_heads / n_kv_heads <= 64");
+    if ((int64_t)T * hpk * c.head_dim > kvq::kMaxQFloats)
+        return fail(KVQ_EUNSUPPORTED, "T * n_q_heads / n_kv_heads * head_dim above 8192");
+    for (int b = 0; b < c.n_seqs; ++b) {
+        if (h->len[b] < T)
+            return fail(KVQ_EINVAL, "session " + std::to_string(b) + " holds fewer than T rows");
+        if (visible_lo(h, h->len[b], T) < h->base[b])
+            return fail(KVQ_ERANGE, "session " + std::to_string(b) + ": visible rows were rebased away");
+    }
+    Plan p = make_plan(h, T);
+    if (!ws || ws_bytes < p.ml_bytes + p.o_bytes) return fail(KVQ_EINVAL, "workspace missing or too small");
+    if (!aligned(ws, 256)) return fail(KVQ_EINVAL, "workspace must be 256-byte aligned");
+    kvq::DecodeParams dp{};
+    dp.q = q;
+    dp.dtype = dtype;
+    dp.B = c.n_seqs;
+    dp.T = T;
+    dp.H = c.n_q_heads;
+    dp.Hkv = c.n_kv_heads;
+    dp.hd = c.head_dim;
+    dp.hpk = hpk;
+    dp.window = c.window;
+    dp.k_planes = h->k;
+    dp.v_planes = h->v;
+    dp.k_stride = (int64_t)h->sz.k_session_stride;
+    dp.v_stride = (int64_t)h->sz.v_session_stride;
+    dp.k_row = (int32_t)h->sz.k_row_bytes;
+    dp.v_row = (int32_t)h->sz.v_row_bytes;
+    dp.len_d = len_d(h);
+    dp.base_d = base_d(h);
+    dp.chunk = p.chunk;
+    dp.splits = p.splits;
+    dp.scale = scale;
+    dp.part_ml = static_cast<float*>(ws);
+    dp.part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + p.ml_bytes);
+    dp.sinks = sinks;
+    dp.out = out;
+    dp.lse = lse;
+    const char* err = nullptr;
+    if (kvq::launch_decode(dp, stream, &err)) return fail(KVQ_EDEVICE, err ? err : "decode launch failed");
+    return KVQ_OK;
+}
+
+kvq_status kvq_truncate(kvq_cache* h, const int32_t* new_len, kvq_stream stream) {
+    if (!h || !new_len) return fail(KVQ_EINVAL, "NULL argument");
+    const kvq_config& c = h->cfg;
+    for (int b = 0; b < c.n_seqs; ++b) {
+        if (new_len[b] < 0 || new_len[b] > h->len[b])
+            return fail(KVQ_EINVAL, "session " + std::to_string(b) + ": truncate only shrinks");
+        if (c.ring_step > 0 && std::max<int64_t>(0, (int64_t)new_len[b] - c.window) < h->base[b])
+            return fail(KVQ_ERANGE, "session " + std::to_string(b) +
+                                        ": the ring no longer holds rows the new length would expose");
+    }
+    std::vector<int32_t> idx, val;
+    for (int b = 0; b < c.n_seqs; ++b)
+        if (new_len[b] != h->len[b]) {
+            idx.push_back(b);
+            val.push_back(new_len[b]);
+        }
+    kvq_status s = enqueue_sets(h->counters, idx, val, stream);
+    if (s != KVQ_OK) return s;
+    for (int b = 0; b < c.n_seqs; ++b) h->len[b] = new_len[b];
+    return KVQ_OK;
+}
+
+kvq_status kvq_set_split_rows(kvq_cache* h, int32_t rows) {
+    if (!h) return fail(KVQ_EINVAL, "handle is NULL");
+    if (rows < 0 || rows % kvq::kSplitQuantum != 0)
+        return fail(KVQ_EINVAL, "split rows must be 0 or a positive multiple of 64");
+    h->split_rows = rows;
+    return KVQ_OK;
+}
+
+kvq_status kvq_info(const kvq_cache* h, kvq_info_t* out) {
+    if (!h || !out) return fail(KVQ_EINVAL, "NULL argument");
+    out->config = h->cfg;
+    out->sizes = h->sz;
+    out->k_planes = h->k;
+    out->v_planes = h->v;
+    out->counters = h->counters;
+    out->split_rows = h->split_rows;
+    return KVQ_OK;
+}
+
+kvq_status kvq_host_lengths(const kvq_cache* h, int64_t* len, int64_t* base) {
+    if (!h) return fail(KVQ_EINVAL, "handle is NULL");
+    for (int b = 0; b < h->cfg.n_seqs; ++b) {
+        if (len) len[b] = h->len[b];
+        if (base) base[b] = h->base[b];
+    }
+    return KVQ_OK;
+}
+
+void kvq_destroy(kvq_cache* h) { delete h; }
+
+}  // extern "C"

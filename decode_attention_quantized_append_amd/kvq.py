@@ -1,0 +1,301 @@
+"""Python binding of libkvq (include/kvq.h).
+
+The functions below carry the C names and only marshal arguments: every step
+of the path runs in the HIP kernels of libkvq.so.  torch provides device
+memory and streams.  Loading fails loudly when the library has not been built;
+there is no fallback.
+
+``KvqLayerCache`` is a convenience owner of the device buffers one handle
+needs (planes, counters, decode workspace), allocated with torch.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvq.so")
+NODEV_PATH = os.path.join(_PKG, "libkvq_nodev.so")
+
+KVQ_OK, KVQ_EINVAL, KVQ_ECAPACITY, KVQ_ERANGE, KVQ_EUNSUPPORTED, KVQ_EDEVICE = range(6)
+KVQ_F32, KVQ_BF16 = 0, 1
+KVQ_FMT_Q8_0, KVQ_FMT_Q5_1 = 1, 2
+STATUS_NAMES = {0: "KVQ_OK", 1: "KVQ_EINVAL", 2: "KVQ_ECAPACITY", 3: "KVQ_ERANGE",
+                4: "KVQ_EUNSUPPORTED", 5: "KVQ_EDEVICE"}
+
+# Every entry point the header declares.
+EXPORTS = ("kvq_required_bytes", "kvq_create", "kvq_append", "kvq_decode_workspace_bytes",
+           "kvq_decode", "kvq_truncate", "kvq_set_split_rows", "kvq_info", "kvq_host_lengths",
+           "kvq_destroy", "kvq_last_error")
+
+
+class kvq_config(ctypes.Structure):
+    _fields_ = [("n_seqs", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("capacity", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("ring_step", ctypes.c_int32), ("k_fmt", ctypes.c_int32),
+                ("v_fmt", ctypes.c_int32)]
+
+
+class kvq_sizes(ctypes.Structure):
+    _fields_ = [("k_planes_bytes", ctypes.c_size_t), ("v_planes_bytes", ctypes.c_size_t),
+                ("counters_bytes", ctypes.c_size_t), ("k_row_bytes", ctypes.c_size_t),
+                ("v_row_bytes", ctypes.c_size_t), ("k_session_stride", ctypes.c_size_t),
+                ("v_session_stride", ctypes.c_size_t)]
+
+
+class kvq_info_t(ctypes.Structure):
+    _fields_ = [("config", kvq_config), ("sizes", kvq_sizes), ("k_planes", ctypes.c_void_p),
+                ("v_planes", ctypes.c_void_p), ("counters", ctypes.c_void_p),
+                ("split_rows", ctypes.c_int32)]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def _declare(lib):
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    st = ctypes.c_int
+    cfgp, szp = ctypes.POINTER(kvq_config), ctypes.POINTER(kvq_sizes)
+    i32p, i64p = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    sig = {
+        "kvq_required_bytes": (st, [cfgp, szp]),
+        "kvq_create": (st, [cfgp, vp, vp, vp, vp, ctypes.POINTER(vp)]),
+        "kvq_append": (st, [vp, vp, vp, i32, i32, i32p, vp]),
+        "kvq_decode_workspace_bytes": (st, [vp, i32, ctypes.POINTER(ctypes.c_size_t)]),
+        "kvq_decode": (st, [vp, vp, i32, i32, vp, f32, vp, vp, vp, ctypes.c_size_t, vp]),
+        "kvq_truncate": (st, [vp, i32p, vp]),
+        "kvq_set_split_rows": (st, [vp, i32]),
+        "kvq_info": (st, [vp, ctypes.POINTER(kvq_info_t)]),
+        "kvq_host_lengths": (st, [vp, i64p, i64p]),
+        "kvq_destroy": (None, [vp]),
+        "kvq_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = None
+
+
+def load(path: Optional[str] = None):
+    """Load libkvq.so (after torch, so that both share torch's HIP runtime)."""
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is not built; run python -m decode_attention_quantized_append_amd.build")
+    if p == LIB_PATH:
+        import torch  # noqa: F401  -- its HIP runtime must be the one libkvq binds to
+    lib = _declare(ctypes.CDLL(p))
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def load_nodev():
+    """The host logic linked to a recording launcher (CPU tests only)."""
+    lib = _declare(ctypes.CDLL(NODEV_PATH))
+    lib.kvq_nodev_log.restype = ctypes.c_char_p
+    lib.kvq_nodev_clear.restype = None
+    lib.kvq_nodev_fail_next.restype = None
+    return lib
+
+
+def _check(lib, status):
+    if status != KVQ_OK:
+        raise KvqError(status, lib.kvq_last_error().decode())
+
+
+def _i32_array(values):
+    if values is None:
+        return None
+    vals = [int(v) for v in values]
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
+def make_config(n_seqs, n_q_heads, n_kv_heads, head_dim, capacity, window=0, ring_step=0):
+    return kvq_config(n_seqs, n_q_heads, n_kv_heads, head_dim, capacity, window, ring_step,
+                      KVQ_FMT_Q8_0, KVQ_FMT_Q5_1)
+
+
+# -- thin wrappers with the C names -------------------------------------------
+def kvq_required_bytes(cfg: kvq_config, lib=None) -> kvq_sizes:
+    lib = lib or load()
+    out = kvq_sizes()
+    _check(lib, lib.kvq_required_bytes(ctypes.byref(cfg), ctypes.byref(out)))
+    return out
+
+
+def kvq_create(cfg: kvq_config, k_planes: int, v_planes: int, counters: int, stream: int = 0,
+               lib=None) -> int:
+    lib = lib or load()
+    h = ctypes.c_void_p()
+    _check(lib, lib.kvq_create(ctypes.byref(cfg), k_planes, v_planes, counters, stream or None,
+                               ctypes.byref(h)))
+    return h.value
+
+
+def kvq_append(h: int, k_new: int, v_new: int, dtype: int, T: int,
+               n_new: Optional[Sequence[int]] = None, stream: int = 0, lib=None) -> None:
+    lib = lib or load()
+    _check(lib, lib.kvq_append(h, k_new, v_new, dtype, T, _i32_array(n_new), stream or None))
+
+
+def kvq_decode_workspace_bytes(h: int, T: int, lib=None) -> int:
+    lib = lib or load()
+    n = ctypes.c_size_t()
+    _check(lib, lib.kvq_decode_workspace_bytes(h, T, ctypes.byref(n)))
+    return n.value
+
+
+def kvq_decode(h: int, q: int, dtype: int, T: int, sinks: Optional[int], scale: float, out: int,
+               lse: Optional[int], ws: int, ws_bytes: int, stream: int = 0, lib=None) -> None:
+    lib = lib or load()
+    _check(lib, lib.kvq_decode(h, q, dtype, T, sinks or None, scale, out, lse or None, ws,
+                               ws_bytes, stream or None))
+
+
+def kvq_truncate(h: int, new_len: Sequence[int], stream: int = 0, lib=None) -> None:
+    lib = lib or load()
+    _check(lib, lib.kvq_truncate(h, _i32_array(new_len), stream or None))
+
+
+def kvq_set_split_rows(h: int, rows: int, lib=None) -> None:
+    lib = lib or load()
+    _check(lib, lib.kvq_set_split_rows(h, rows))
+
+
+def kvq_info(h: int, lib=None) -> kvq_info_t:
+    lib = lib or load()
+    out = kvq_info_t()
+    _check(lib, lib.kvq_info(h, ctypes.byref(out)))
+    return out
+
+
+def kvq_host_lengths(h: int, n_seqs: int, lib=None):
+    lib = lib or load()
+    ln = (ctypes.c_int64 * n_seqs)()
+    bs = (ctypes.c_int64 * n_seqs)()
+    _check(lib, lib.kvq_host_lengths(h, ln, bs))
+    return list(ln), list(bs)
+
+
+def kvq_destroy(h: int, lib=None) -> None:
+    (lib or load()).kvq_destroy(h)
+
+
+def kvq_last_error(lib=None) -> str:
+    return (lib or load()).kvq_last_error().decode()
+
+
+# -- convenience owner of device buffers -----------------------------------------
+class KvqLayerCache:
+    """One kvq handle plus torch-allocated planes, counters and workspace on
+    `device`.  Tensors passed in must already live on that device."""
+
+    def __init__(self, n_seqs, n_q_heads, n_kv_heads, head_dim, capacity, window=0,
+                 ring_step=0, device="cuda", stream=None):
+        import torch
+        self.lib = load()
+        self.cfg = make_config(n_seqs, n_q_heads, n_kv_heads, head_dim, capacity, window, ring_step)
+        self.sizes = kvq_required_bytes(self.cfg, self.lib)
+        self.device = torch.device(device)
+        alloc = lambda n: torch.empty(int(n) + 256, dtype=torch.uint8, device=self.device)  # noqa: E731
+        self._k_raw, self._v_raw = alloc(self.sizes.k_planes_bytes), alloc(self.sizes.v_planes_bytes)
+        self._c_raw = alloc(self.sizes.counters_bytes)
+        self.k_planes = self._aligned(self._k_raw, self.sizes.k_planes_bytes)
+        self.v_planes = self._aligned(self._v_raw, self.sizes.v_planes_bytes)
+        self.counters = self._aligned(self._c_raw, self.sizes.counters_bytes).view(torch.int32)
+        self.stream = stream
+        self.h = kvq_create(self.cfg, self.k_planes.data_ptr(), self.v_planes.data_ptr(),
+                            self.counters.data_ptr(), self._stream(), self.lib)
+        self._ws = None
+
+    @staticmethod
+    def _aligned(raw, nbytes):
+        off = (-raw.data_ptr()) % 256
+        return raw[off:off + int(nbytes)]
+
+    def _stream(self):
+        import torch
+        s = self.stream if self.stream is not None else torch.cuda.current_stream(self.device)
+        return s.cuda_stream
+
+    @staticmethod
+    def _dtype(t):
+        import torch
+        if t.dtype == torch.float32:
+            return KVQ_F32
+        if t.dtype == torch.bfloat16:
+            return KVQ_BF16
+        raise TypeError(f"unsupported dtype {t.dtype}")
+
+    def append(self, k_new, v_new, n_new=None):
+        B, T = k_new.shape[:2]
+        assert k_new.is_contiguous() and v_new.is_contiguous() and k_new.shape == v_new.shape
+        assert tuple(k_new.shape) == (self.cfg.n_seqs, T, self.cfg.n_kv_heads, self.cfg.head_dim)
+        assert k_new.device == self.device and v_new.device == self.device and v_new.dtype == k_new.dtype
+        kvq_append(self.h, k_new.data_ptr(), v_new.data_ptr(), self._dtype(k_new), T, n_new,
+                   self._stream(), self.lib)
+
+    def workspace(self, T):
+        import torch
+        n = kvq_decode_workspace_bytes(self.h, T, self.lib)
+        if self._ws is None or self._ws.numel() < n + 256:
+            self._ws = torch.empty(n + 256, dtype=torch.uint8, device=self.device)
+        return self._aligned(self._ws, n)
+
+    def decode(self, q, scale, sinks=None, want_lse=True, out=None, lse=None):
+        import torch
+        B, T, H, hd = q.shape
+        assert q.is_contiguous() and q.device == self.device
+        assert (B, H, hd) == (self.cfg.n_seqs, self.cfg.n_q_heads, self.cfg.head_dim)
+        if out is None:
+            out = torch.empty((B, T, H, hd), dtype=torch.float32, device=self.device)
+        if want_lse and lse is None:
+            lse = torch.empty((B, T, H), dtype=torch.float32, device=self.device)
+        if sinks is not None:
+            assert sinks.dtype == torch.float32 and sinks.is_contiguous() and sinks.numel() == H
+        ws = self.workspace(T)
+        kvq_decode(self.h, q.data_ptr(), self._dtype(q), T,
+                   sinks.data_ptr() if sinks is not None else None, float(scale), out.data_ptr(),
+                   lse.data_ptr() if want_lse else None, ws.data_ptr(), ws.numel(),
+                   self._stream(), self.lib)
+        return out, (lse if want_lse else None)
+
+    def truncate(self, new_len):
+        kvq_truncate(self.h, new_len, self._stream(), self.lib)
+
+    def set_split_rows(self, rows):
+        kvq_set_split_rows(self.h, rows, self.lib)
+
+    def host_lengths(self):
+        return kvq_host_lengths(self.h, self.cfg.n_seqs, self.lib)
+
+    def planes(self):
+        """(K, V) uint8 device views [B, capacity, row_bytes] of the physical planes."""
+        s = self.sizes
+        B, cap = self.cfg.n_seqs, self.cfg.capacity
+        k = self.k_planes.view(B, s.k_session_stride)[:, :cap * s.k_row_bytes].reshape(B, cap, s.k_row_bytes)
+        v = self.v_planes.view(B, s.v_session_stride)[:, :cap * s.v_row_bytes].reshape(B, cap, s.v_row_bytes)
+        return k, v
+
+    def close(self):
+        if getattr(self, "h", None):
+            kvq_destroy(self.h, self.lib)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

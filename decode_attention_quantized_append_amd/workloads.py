@@ -35,7 +35,7 @@ from typing import Optional
 
 import numpy as np
 
-CHUNK = 4096          # rows per generator chunk
+CHUNK = 1024          # rows per generator chunk
 _Q, _K, _V, _SINK, _OUTL, _LEN = 1, 2, 3, 4, 5, 6
 
 
@@ -156,6 +156,24 @@ class Workload:
             if n:
                 k[b, :n], v[b, :n] = self.kv_rows(b, s, s + n)
         return k, v
+
+    def pre_step_lengths(self) -> np.ndarray:
+        """Committed rows per session before a step appends its T rows."""
+        return self.lengths() - self.T
+
+    def prefill_pieces(self, piece: int = 1024):
+        """Setup appends that bring an empty cache to ``pre_step_lengths()``:
+        yields (rows per session, first logical row per session, T) for each
+        append call.  A ring gets pieces no longer than capacity - window -
+        ring_step + 2 rows, so that no rebase can drop a visible row."""
+        target = self.pre_step_lengths()
+        if self.ring_cap:
+            piece = min(piece, self.ring_cap - self.window - self.ring_step + 2)
+        done = np.zeros(self.B, dtype=np.int64)
+        while np.any(done < target):
+            n = np.minimum(target - done, piece)
+            yield n.copy(), done.copy(), int(n.max())
+            done += n
 
     def q(self, step: int = 0) -> np.ndarray:
         """float32 [B, T, H, hd] query rows of decode step ``step``."""

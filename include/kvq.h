@@ -1,0 +1,197 @@
+/*
+ * kvq.h -- C ABI of libkvq: append to, and decode attention over, a per-layer
+ * quantized KV cache on an AMD Instinct MI355X (gfx950).
+ *
+ * The cache (memra-engine, "Struct KvLayer" page, struct description and
+ * fields k, v, k_tok_bytes, v_tok_bytes, len, ring, len_d, base_d):
+ *   - K is stored q8_0: 34 bytes per 32 elements (fp16 scale d, then 32
+ *     signed 8-bit codes; value = d * code).
+ *   - V is stored q5_1: 24 bytes per 32 elements (fp16 step d, fp16 offset m,
+ *     4 bytes holding bit 4 of each code, 16 bytes of nibbles where byte j
+ *     holds code j in its low and code j+16 in its high nibble;
+ *     value = d * code + m).
+ *   - A token row keeps [kv_head, dim] order: element index kv_head*head_dim+d,
+ *     block index/32, lane index%32; head_dim % 32 == 0, so no block
+ *     straddles a head.  K row bytes = n_kv_heads*head_dim/32*34, V row bytes
+ *     = n_kv_heads*head_dim/32*24.
+ *   - Every session has a device-resident committed length len_d (int32) and
+ *     ring base base_d (int32).  An append writes its rows at the slot held
+ *     in len_d and then advances len_d; a decode takes its length from len_d;
+ *     so a step needs no device-to-host read.  A logical row lives at
+ *     physical row (row - base); the live view of a windowed session is
+ *     [max(0, len - window), len).  Only a ring rebase moves base; a truncate
+ *     moves len only.
+ *
+ * Attention (cortiq-engine, "Struct LayerKvCache" page, methods attend_group
+ * and attend_group_upto, field sinks): Q head h reads KV head h / (H/Hkv);
+ * query row t of a T-row call sees logical rows [first_t, upto_t) with
+ * upto_t = len - T + t + 1 and first_t = max(0, upto_t - window) (0 without a
+ * window); score = scale * <q, k>; an optional per-Q-head sink logit joins the
+ * softmax max and denominator and carries no value.  Output per (b, t, h) is
+ *   out = sum_j e^(s_j - M) v_j / (sum_j e^(s_j - M) + e^(sink_h - M)),
+ *   lse = M + log(denominator),   M = max(max_j s_j, sink_h).
+ *
+ * Ownership: the caller owns every device buffer (planes, counters, inputs,
+ * outputs, workspace) and every stream.  The library owns only the host
+ * handle.  It never allocates device memory, never synchronizes and never
+ * reads device memory back to the host.
+ *
+ * Ordering: every call enqueues its work on the given stream (NULL = the
+ * default stream).  All calls on one handle must be stream-ordered (the same
+ * stream, or ordered by the caller), because the host keeps a mirror of
+ * len/base in lock-step with the device counters.  A handle is not
+ * thread-safe; distinct handles are independent.
+ *
+ * Errors: a call that returns anything but KVQ_OK enqueued nothing and
+ * changed nothing (host mirror and device state are as before), except
+ * KVQ_EDEVICE, which reports a failed kernel launch.  kvq_last_error() gives
+ * a thread-local message for the last failure.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvq_status {
+    KVQ_OK = 0,
+    KVQ_EINVAL = 1,       /* bad argument, size, alignment or state */
+    KVQ_ECAPACITY = 2,    /* a flat cache has no physical row left */
+    KVQ_ERANGE = 3,       /* a row the call needs is no longer resident in the ring */
+    KVQ_EUNSUPPORTED = 4, /* a format or shape this build does not implement */
+    KVQ_EDEVICE = 5       /* a kernel launch failed */
+} kvq_status;
+
+typedef enum kvq_dtype {
+    KVQ_F32 = 0,   /* IEEE binary32 */
+    KVQ_BF16 = 1   /* bfloat16, widened exactly to binary32 on load */
+} kvq_dtype;
+
+typedef enum kvq_format {
+    KVQ_FMT_Q8_0 = 1,
+    KVQ_FMT_Q5_1 = 2
+} kvq_format;
+
+/* Geometry of one attention layer's cache for n_seqs sessions. */
+typedef struct kvq_config {
+    int32_t n_seqs;      /* B >= 1 */
+    int32_t n_q_heads;   /* H >= 1, a multiple of n_kv_heads */
+    int32_t n_kv_heads;  /* Hkv >= 1 */
+    int32_t head_dim;    /* hd: a multiple of 32, at most 256 */
+    int32_t capacity;    /* physical rows per session (max context, or ring rows) */
+    int32_t window;      /* 0 = full attention; else the sliding-window length */
+    int32_t ring_step;   /* 0 = flat [0, capacity); else rebase granularity in rows
+                            (needs window > 0 and window + ring_step <= capacity) */
+    int32_t k_fmt;       /* must be KVQ_FMT_Q8_0 */
+    int32_t v_fmt;       /* must be KVQ_FMT_Q5_1 */
+} kvq_config;
+
+/* Device bytes the caller must provide for a configuration. */
+typedef struct kvq_sizes {
+    size_t k_planes_bytes;    /* n_seqs * k_session_stride */
+    size_t v_planes_bytes;    /* n_seqs * v_session_stride */
+    size_t counters_bytes;    /* int32 len_d[B], base_d[B], then library scratch */
+    size_t k_row_bytes;       /* Hkv*hd/32*34 */
+    size_t v_row_bytes;       /* Hkv*hd/32*24 */
+    size_t k_session_stride;  /* capacity*k_row_bytes rounded up to 256 */
+    size_t v_session_stride;  /* capacity*v_row_bytes rounded up to 256 */
+} kvq_sizes;
+
+typedef struct kvq_cache kvq_cache;   /* opaque host handle */
+typedef void* kvq_stream;             /* a hipStream_t; NULL = default stream */
+
+/* State of a handle, for callers and tests. */
+typedef struct kvq_info_t {
+    kvq_config config;
+    kvq_sizes sizes;
+    void* k_planes;       /* session b's K plane at k_planes + b*k_session_stride */
+    void* v_planes;
+    int32_t* counters;    /* len_d at counters[0..B), base_d at counters[B..2B) */
+    int32_t split_rows;   /* rows per split-K chunk; 0 = chosen per call */
+} kvq_info_t;
+
+/* Fills *out for cfg.  Pure host computation.
+ * Errors: EINVAL (NULL pointer, bad geometry), EUNSUPPORTED (format, head_dim). */
+kvq_status kvq_required_bytes(const kvq_config* cfg, kvq_sizes* out);
+
+/* Creates a handle over caller-owned device memory: k_planes / v_planes
+ * (256-byte aligned, at least the sizes from kvq_required_bytes) and counters
+ * (256-byte aligned, counters_bytes).  Enqueues the zeroing of len_d, base_d
+ * and the library scratch on `stream`; plane contents are not touched.  The
+ * host mirror starts at len = base = 0.
+ * Errors: EINVAL, EUNSUPPORTED, EDEVICE. */
+kvq_status kvq_create(const kvq_config* cfg, void* k_planes, void* v_planes,
+                      int32_t* counters, kvq_stream stream, kvq_cache** out);
+
+/* Appends rows (memra KvLayer append-dc / append_kv_quantized_dcw, cortiq
+ * LayerKvCache::append).  k_new and v_new are device arrays
+ * [n_seqs, T, n_kv_heads, head_dim] of dtype.  Session b appends its first
+ * n_new[b] rows (n_new is a HOST array of n_seqs entries in [0, T], or NULL
+ * for all T).  The rows are quantized (K to q8_0, V to q5_1, each 32-element
+ * block from its own absmax / min-max with fp16 scales rounded to nearest
+ * even and codes computed from the stored scales, rounded half to even) and
+ * written at physical rows len_d[b] - base_d[b] + t; len_d[b] then grows by
+ * n_new[b] inside the same launch.  In ring mode, if a session's rows would
+ * pass the last physical row, the library first rebases it: base grows by
+ * whole ring_step units until the rows fit, the surviving rows
+ * [new_base, len) are moved to physical row 0, and base_d is updated.
+ * Errors: EINVAL (NULL, dtype, T < 1, n_new out of range), ECAPACITY (flat
+ * cache full), ERANGE (a rebase would drop rows the first new row still
+ * sees), EDEVICE. */
+kvq_status kvq_append(kvq_cache* h, const void* k_new, const void* v_new,
+                      kvq_dtype dtype, int32_t T, const int32_t* n_new,
+                      kvq_stream stream);
+
+/* Device workspace bytes kvq_decode needs for T query rows at the handle's
+ * current lengths. */
+kvq_status kvq_decode_workspace_bytes(const kvq_cache* h, int32_t T, size_t* bytes);
+
+/* Decode attention (memra fa_decode_dc / fa_decode_dcw; cortiq attend_group
+ * and attend_group_upto).  q: device [n_seqs, T, n_q_heads, head_dim] of
+ * dtype; its T rows are the last T committed rows of every session (causal
+ * among themselves).  sinks: device float[n_q_heads] or NULL.  scale: the
+ * score scale (normally 1/sqrt(head_dim)).  out: device float
+ * [n_seqs, T, n_q_heads, head_dim].  lse: device float [n_seqs, T, n_q_heads]
+ * or NULL.  ws: device workspace of at least kvq_decode_workspace_bytes
+ * bytes, 256-byte aligned.  The committed length is read from len_d on the
+ * device.  Requires len >= T for every session and 1 <= T*H/Hkv <= 64.
+ * Errors: EINVAL, ERANGE (a visible row was rebased away), EDEVICE. */
+kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T,
+                      const float* sinks, float scale, float* out, float* lse,
+                      void* ws, size_t ws_bytes, kvq_stream stream);
+
+/* Rollback (memra Cache::rollback, full-attention part: len = snapshot_len +
+ * accept_len, no copy; cortiq LayerKvCache::truncate_last).  new_len is a
+ * HOST array of n_seqs lengths, each <= the current length.  Enqueues the
+ * write of len_d; rows at or past new_len become dead and are not cleared;
+ * base is never moved.
+ * Errors: EINVAL (NULL, growth, negative), ERANGE (a windowed ring would
+ * expose rows it no longer holds), EDEVICE. */
+kvq_status kvq_truncate(kvq_cache* h, const int32_t* new_len, kvq_stream stream);
+
+/* Tuning: rows per split-K chunk of kvq_decode (a positive multiple of 64),
+ * or 0 to let each call choose.  The result does not depend on it beyond
+ * float rounding.  Errors: EINVAL. */
+kvq_status kvq_set_split_rows(kvq_cache* h, int32_t rows);
+
+/* Copies the handle's configuration, sizes and buffer pointers. */
+kvq_status kvq_info(const kvq_cache* h, kvq_info_t* out);
+
+/* Copies the host mirror: len[b] and base[b] for every session (HOST arrays
+ * of n_seqs entries; either may be NULL). */
+kvq_status kvq_host_lengths(const kvq_cache* h, int64_t* len, int64_t* base);
+
+/* Frees the host handle only; device memory stays with the caller. */
+void kvq_destroy(kvq_cache* h);
+
+/* Thread-local message describing the last failed call on this thread. */
+const char* kvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

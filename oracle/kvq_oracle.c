@@ -145,6 +145,7 @@ void kvqo_q5_1_encode(const float* x, uint8_t* blk) {
         if (x[i] < mn) mn = x[i];
         if (x[i] > mx) mx = x[i];
     }
+    mn = mn + 0.0f;  /* a zero minimum is stored as +0 whatever the sign of the zeros */
     float d = (mx - mn) / 31.0f;
     uint16_t d16 = kvqo_f32_to_f16(d);
     uint16_t m16 = kvqo_f32_to_f16(mn);

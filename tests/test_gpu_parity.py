@@ -1,0 +1,274 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, element by
+element, on seeded inputs at sizes the oracle finishes in seconds that still
+span several 64-row tiles, several split-K chunks and ragged tails.
+
+Codes and scales must be bit-exact; attention outputs and log-sum-exps must
+satisfy |gpu - oracle| <= 2e-3 + 1e-2 |oracle| for every element.
+"""
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_quantized_append_amd import KvqError, kvq
+from decode_attention_quantized_append_amd.workloads import round_bf16
+
+pytestmark = pytest.mark.gpu
+
+from gpu_pair import DEV, Pair, assert_close, to_dev  # noqa: E402
+
+
+def rows(rng, B, T, Hkv, hd, io="bf16", scale=1.0, outliers=False):
+    k = rng.standard_normal((B, T, Hkv, hd)).astype(np.float32) * scale
+    v = rng.standard_normal((B, T, Hkv, hd)).astype(np.float32) * scale
+    if outliers:
+        for g in range(Hkv):
+            k[:, :, g, rng.choice(hd, 4, replace=False)] *= 8.0
+        v *= 0.5
+    return (round_bf16(k), round_bf16(v)) if io == "bf16" else (k, v)
+
+
+def qrows(rng, B, T, H, hd, io="bf16"):
+    q = rng.standard_normal((B, T, H, hd)).astype(np.float32)
+    return round_bf16(q) if io == "bf16" else q
+
+
+# -- append: codes bit-exact -------------------------------------------------------
+@pytest.mark.parametrize("B,Hkv,hd,io", [(1, 1, 64, "f32"), (1, 8, 128, "bf16"), (3, 8, 128, "bf16"),
+                                         (4, 8, 64, "bf16"), (2, 4, 256, "bf16"), (2, 3, 96, "f32"),
+                                         (1, 2, 32, "f32")])
+def test_append_codes_bit_exact(B, Hkv, hd, io):
+    rng = np.random.default_rng(hd * 7 + B)
+    p = Pair(B, 4 * Hkv, Hkv, hd, 400, io=io)
+    for T, counts in [(1, None), (7, None), (64, [64 - b for b in range(B)]), (130, None), (3, [0] + [3] * (B - 1))]:
+        k, v = rows(rng, B, T, Hkv, hd, io, scale=rng.choice([0.01, 1.0, 30.0]), outliers=(hd == 128))
+        p.append(k, v, counts)
+        p.check_mirror()
+    p.check_planes()
+
+
+def test_append_edge_blocks():
+    """Ties at half a step, zero and constant blocks, subnormal fp16 scales,
+    -0.0, a huge range and one-hot blocks: every byte equals the oracle's."""
+    hd = 32 * 16
+    blocks = []
+    d = 0.125
+    tie = np.zeros(32, np.float32)
+    tie[0] = 127 * d
+    tie[1:] = (np.arange(31) - 15 + 0.5) * d
+    blocks.append(tie)
+    blocks.append(np.zeros(32, np.float32))
+    blocks.append(np.full(32, 1.5, np.float32))
+    blocks.append(np.full(32, -0.0, np.float32))
+    blocks.append(np.linspace(-1e-6, 1e-6, 32).astype(np.float32))           # subnormal fp16 scale
+    blocks.append((np.arange(32) * 2.0 ** -24).astype(np.float32))
+    blocks.append(np.linspace(-3e4, 3e4, 32).astype(np.float32))
+    one = np.zeros(32, np.float32)
+    one[5] = -7.0
+    blocks.append(one)
+    q5tie = np.zeros(32, np.float32)
+    q5tie[1] = 31 * 0.25
+    q5tie[2:] = (np.arange(30) + 0.5) * 0.25
+    blocks.append(q5tie)
+    stored_min = np.full(32, 0.1, np.float32)
+    stored_min[1], stored_min[2] = 7.85, 0.4749875
+    blocks.append(stored_min)
+    mixed_zero = np.zeros(32, np.float32)
+    mixed_zero[1::3] = -0.0
+    mixed_zero[2::5] = 2.5
+    blocks.append(mixed_zero)
+    rng = np.random.default_rng(3)
+    while len(blocks) < 16:
+        blocks.append((rng.standard_normal(32) * 10.0 ** rng.integers(-5, 4)).astype(np.float32))
+    row = np.concatenate(blocks).reshape(1, 1, 1, hd)
+    for io in ("f32", "bf16"):
+        x = row if io == "f32" else round_bf16(row)
+        p = Pair(1, 1, 1, hd, 4, io=io)
+        p.append(x, -x)
+        p.append(x[:, :, :, ::-1].copy(), x)
+        p.check_planes()
+
+
+# -- decode parity -----------------------------------------------------------------
+SMALL = {
+    # name: (B, H, Hkv, hd, T, lengths, window, cap, step, sinks, io, outliers)
+    "tiny": (1, 4, 1, 64, 1, [256], 0, 300, 0, False, "f32", False),
+    "qwen_gqa_small": (1, 32, 8, 128, 1, [1500], 0, 1600, 0, False, "bf16", True),
+    "batched_small": (16, 40, 8, 128, 1, [1, 2, 63, 64, 65, 127, 128, 129, 700, 1023, 1024, 1025,
+                                          333, 900, 5, 1100], 0, 1200, 0, False, "bf16", False),
+    "sink_ring_small": (4, 64, 8, 64, 1, [1000, 1000, 1000, 1000], 64, 128, 32, True, "bf16", False),
+    "verify_small": (2, 16, 4, 256, 8, [600, 333], 0, 700, 0, False, "bf16", False),
+    "hd32_gqa7": (2, 7, 1, 32, 3, [200, 70], 0, 256, 0, True, "f32", False),
+    "hd96_window": (3, 6, 2, 96, 2, [300, 40, 2], 50, 320, 0, False, "bf16", False),
+}
+
+
+def build_small(name, seed=0):
+    B, H, Hkv, hd, T, lens, window, cap, step, sinks, io, outl = SMALL[name]
+    rng = np.random.default_rng(seed + len(name))
+    p = Pair(B, H, Hkv, hd, cap, window, step, io=io)
+    lens = np.asarray(lens)
+    done = np.zeros(B, np.int64)
+    piece = 64 if step else 400
+    while np.any(done < lens):
+        n = np.minimum(lens - done, piece)
+        k, v = rows(rng, B, int(n.max()), Hkv, hd, io, outliers=outl)
+        p.append(k, v, n.tolist())
+        done += n
+    q = qrows(rng, B, T, H, hd, io)
+    s = rng.standard_normal(H).astype(np.float32) if sinks else None
+    return p, q, s, float(np.float32(1 / np.sqrt(hd)))
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_decode_parity(name):
+    p, q, s, scale = build_small(name)
+    p.check_mirror()
+    p.check_planes()
+    p.decode(q, scale, sinks=s, what=name)
+
+
+def test_decode_split_invariance():
+    """Output is invariant across split plans (log-sum-exp identity)."""
+    p, q, s, scale = build_small("batched_small")
+    qd = to_dev(q, "bf16")
+    outs = []
+    for rows_ in (64, 128, 320, 1024, 0):
+        p.gpu.set_split_rows(rows_)
+        o, l = p.gpu.decode(qd, scale)
+        outs.append((o.cpu().numpy(), l.cpu().numpy()))
+    for o, l in outs[1:]:
+        np.testing.assert_allclose(o, outs[0][0], atol=2e-6, rtol=1e-5)
+        np.testing.assert_allclose(l, outs[0][1], atol=2e-6, rtol=1e-6)
+    p.decode(q, scale)
+
+
+def test_ring_equals_flat():
+    """The base-offset ring serves the same rows as a flat cache: identical
+    live bytes and identical outputs, step after step, through rebases."""
+    rng = np.random.default_rng(11)
+    B, H, Hkv, hd, W, cap, step = 2, 16, 4, 64, 40, 96, 24
+    ring = Pair(B, H, Hkv, hd, cap, W, step)
+    flat = Pair(B, H, Hkv, hd, 2000, W, 0)
+    L = 0
+    for it in range(30):
+        n = int(rng.integers(1, 33))
+        k, v = rows(rng, B, n, Hkv, hd)
+        ring.append(k, v)
+        flat.append(k, v)
+        L += n
+        ring.check_mirror()
+        base = int(ring.ref.base[0])
+        kr, vr = ring.gpu.planes()
+        kf, vf = flat.gpu.planes()
+        assert torch.equal(kr[:, :L - base], kf[:, base:L]) and torch.equal(vr[:, :L - base], vf[:, base:L])
+        q = qrows(rng, B, 1, H, hd)
+        o1, l1 = ring.gpu.decode(to_dev(q, "bf16"), 0.125)
+        o2, l2 = flat.gpu.decode(to_dev(q, "bf16"), 0.125)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        if it % 7 == 0:
+            ring.decode(q, 0.125, what="ring")
+    assert int(ring.ref.base[0]) > 0
+
+
+def test_truncate_reappend_equals_fresh():
+    """Rollback sets len only (memra Cache::rollback): append P+8, truncate to
+    P+3, re-append 8 == a fresh cache of the committed P+3 rows plus the 8."""
+    rng = np.random.default_rng(12)
+    B, H, Hkv, hd, P = 2, 16, 4, 256, 300
+    k0, v0 = rows(rng, B, P + 8, Hkv, hd)
+    k1, v1 = rows(rng, B, 8, Hkv, hd)
+    a = Pair(B, H, Hkv, hd, 400)
+    a.append(k0, v0)
+    a.truncate([P + 3, P + 3])
+    a.check_mirror()
+    a.append(k1, v1)
+    f = Pair(B, H, Hkv, hd, 400)
+    f.append(k0[:, :P + 3], v0[:, :P + 3])
+    f.append(k1, v1)
+    ka, va = a.gpu.planes()
+    kf, vf = f.gpu.planes()
+    assert torch.equal(ka[:, :P + 11], kf[:, :P + 11]) and torch.equal(va[:, :P + 11], vf[:, :P + 11])
+    q = qrows(rng, B, 8, H, hd)
+    oa, la = a.gpu.decode(to_dev(q, "bf16"), 1 / 16)
+    of, lf = f.gpu.decode(to_dev(q, "bf16"), 1 / 16)
+    assert torch.equal(oa, of) and torch.equal(la, lf)
+    a.decode(q, 1 / 16, what="after rollback")
+
+
+def test_verify_rows_equal_sequential_single_rows():
+    """T causal rows == T single-row decodes made as the rows arrive."""
+    rng = np.random.default_rng(13)
+    B, H, Hkv, hd, N0, T = 2, 16, 4, 128, 500, 8
+    k, v = rows(rng, B, N0 + T, Hkv, hd)
+    q = qrows(rng, B, T, H, hd)
+    a = Pair(B, H, Hkv, hd, 600)
+    a.append(k, v)
+    oa, la = a.gpu.decode(to_dev(q, "bf16"), 0.088)
+    a.decode(q, 0.088, what="T=8")
+    s = Pair(B, H, Hkv, hd, 600)
+    s.append(k[:, :N0], v[:, :N0])
+    for t in range(T):
+        s.append(k[:, N0 + t:N0 + t + 1], v[:, N0 + t:N0 + t + 1])
+        o1, l1 = s.gpu.decode(to_dev(q[:, t:t + 1], "bf16"), 0.088)
+        np.testing.assert_allclose(o1.cpu().numpy()[:, 0], oa.cpu().numpy()[:, t], atol=1e-5, rtol=1e-5)
+        np.testing.assert_allclose(l1.cpu().numpy()[:, 0], la.cpu().numpy()[:, t], atol=1e-5, rtol=1e-6)
+
+
+def test_gqa_equals_repeated_heads():
+    rng = np.random.default_rng(14)
+    B, H, Hkv, hd, N = 1, 10, 2, 64, 300
+    k, v = rows(rng, B, N, Hkv, hd)
+    q = qrows(rng, B, 1, H, hd)
+    g = Pair(B, H, Hkv, hd, N)
+    g.append(k, v)
+    r = Pair(B, H, H, hd, N)
+    r.append(np.repeat(k, H // Hkv, axis=2), np.repeat(v, H // Hkv, axis=2))
+    og, lg = g.gpu.decode(to_dev(q, "bf16"), 0.125)
+    orr, lr = r.gpu.decode(to_dev(q, "bf16"), 0.125)
+    np.testing.assert_allclose(og.cpu().numpy(), orr.cpu().numpy(), atol=1e-5, rtol=1e-5)
+    g.decode(q, 0.125, what="gqa")
+
+
+def test_len_one_and_zero_query_closed_forms():
+    """len 1: out = V'_0; q = 0: out = mean of the visible V' rows (the oracle
+    decodes V'; the GPU must agree within tolerance)."""
+    rng = np.random.default_rng(15)
+    p = Pair(2, 4, 2, 64, 16, window=5)
+    k, v = rows(rng, 2, 1, 2, 64)
+    p.append(k, v)
+    p.decode(qrows(rng, 2, 1, 4, 64), 0.125, what="len1")
+    k, v = rows(rng, 2, 11, 2, 64)
+    p.append(k, v)
+    p.decode(np.zeros((2, 1, 4, 64), np.float32), 0.125, what="q0")
+
+
+def test_decode_without_lse_and_f32_inputs():
+    rng = np.random.default_rng(16)
+    p = Pair(2, 8, 2, 128, 300, io="f32")
+    k, v = rows(rng, 2, 250, 2, 128, io="f32")
+    p.append(k, v)
+    q = qrows(rng, 2, 2, 8, 128, io="f32")
+    out, lse = p.gpu.decode(to_dev(q, "f32"), 0.1, want_lse=False)
+    assert lse is None
+    want, _ = p.ref.attention(q, scale=0.1)
+    assert_close(out.cpu().numpy(), want, "f32 no-lse")
+
+
+def test_host_detected_errors_enqueue_nothing():
+    rng = np.random.default_rng(17)
+    p = Pair(2, 8, 2, 64, 20)
+    k, v = rows(rng, 2, 5, 2, 64)
+    p.append(k, v)
+    before = [t.clone() for t in p.gpu.planes()]
+    with pytest.raises(KvqError) as e:
+        p.gpu.decode(to_dev(qrows(rng, 2, 6, 8, 64), "bf16"), 0.1)       # T > len
+    assert e.value.status == kvq.KVQ_EINVAL
+    with pytest.raises(KvqError) as e:
+        p.gpu.append(*(to_dev(x, "bf16") for x in rows(rng, 2, 16, 2, 64)))  # past capacity
+    assert e.value.status == kvq.KVQ_ECAPACITY
+    with pytest.raises(KvqError):
+        p.gpu.truncate([6, 5])
+    torch.cuda.synchronize(DEV)
+    after = p.gpu.planes()
+    assert torch.equal(before[0], after[0]) and torch.equal(before[1], after[1])
+    p.check_mirror()

@@ -1,0 +1,279 @@
+"""Host logic of libkvq on the CPU: validation, host mirror, ring planner,
+split-K plan and the "refuse, enqueue nothing, change nothing" rule.
+
+libkvq_nodev.so is the same kvq_host.cpp linked to a launcher that records
+each launch as a line of text instead of running it.  Device pointers are
+plain 256-aligned integers that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from decode_attention_quantized_append_amd import build, kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+K, V, C, Q, O, WS = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000, 0x60000000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kvq.NODEV_PATH):
+        build.build_nodev(verbose=False)
+    return kvq.load_nodev()
+
+
+def log(lib):
+    return lib.kvq_nodev_log().decode().splitlines()
+
+
+def create(lib, **kw):
+    cfg = kvq.make_config(**{**dict(n_seqs=2, n_q_heads=8, n_kv_heads=2, head_dim=64, capacity=100), **kw})
+    lib.kvq_nodev_clear()
+    return kvq.kvq_create(cfg, K, V, C, 0, lib)
+
+
+def err(lib, fn, *a):
+    with pytest.raises(kvq.KvqError) as e:
+        fn(*a, lib=lib)
+    return e.value.status
+
+
+def lengths(lib, h, B):
+    return kvq.kvq_host_lengths(h, B, lib)
+
+
+# -- header and exports ------------------------------------------------------
+def test_header_declares_exactly_the_exports():
+    text = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    declared = set(re.findall(r"^(?:kvq_status|void|const char\*)\s+(kvq_\w+)\(", text, re.M))
+    assert declared == set(kvq.EXPORTS)
+
+
+def test_nodev_library_exports_every_symbol(lib):
+    for name in kvq.EXPORTS:
+        assert hasattr(lib, name)
+
+
+def test_hip_library_loads_and_exports_every_symbol():
+    if not os.path.exists(kvq.LIB_PATH):
+        build.build_hip(verbose=False)
+    out = subprocess.run(["nm", "-D", "--defined-only", kvq.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    syms = set(re.findall(r" T (kvq_\w+)", out))
+    assert set(kvq.EXPORTS) <= syms
+    lib = ctypes.CDLL(kvq.LIB_PATH)          # loads without a GPU; nothing is called
+    for name in kvq.EXPORTS:
+        assert hasattr(lib, name)
+
+
+# -- sizes and create ---------------------------------------------------------
+def test_required_bytes(lib):
+    cfg = kvq.make_config(16, 40, 8, 128, 33000)
+    s = kvq.kvq_required_bytes(cfg, lib)
+    assert (s.k_row_bytes, s.v_row_bytes) == (32 * 34, 32 * 24) == (1088, 768)
+    assert s.k_session_stride == -(-1088 * 33000 // 256) * 256
+    assert s.k_planes_bytes == 16 * s.k_session_stride and s.v_planes_bytes == 16 * s.v_session_stride
+    assert s.counters_bytes >= (2 * 16 + 4) * 4 and s.counters_bytes % 256 == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=48), kvq.KVQ_EINVAL), (dict(head_dim=0), kvq.KVQ_EINVAL),
+    (dict(head_dim=288), kvq.KVQ_EUNSUPPORTED), (dict(n_q_heads=7), kvq.KVQ_EINVAL),
+    (dict(n_seqs=0), kvq.KVQ_EINVAL), (dict(capacity=0), kvq.KVQ_EINVAL),
+    (dict(ring_step=16), kvq.KVQ_EINVAL), (dict(window=90, ring_step=16), kvq.KVQ_EINVAL),
+    (dict(window=-1), kvq.KVQ_EINVAL)])
+def test_bad_config(lib, kw, status):
+    cfg = kvq.make_config(**{**dict(n_seqs=2, n_q_heads=8, n_kv_heads=2, head_dim=64, capacity=100), **kw})
+    assert err(lib, kvq.kvq_required_bytes, cfg) == status
+    lib.kvq_nodev_clear()
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_create(cfg, K, V, C, 0, lib)
+    assert log(lib) == []
+
+
+def test_formats_other_than_q8_0_q5_1_are_unsupported(lib):
+    cfg = kvq.make_config(1, 4, 1, 64, 10)
+    cfg.v_fmt = kvq.KVQ_FMT_Q8_0
+    assert err(lib, kvq.kvq_required_bytes, cfg) == kvq.KVQ_EUNSUPPORTED
+
+
+def test_create_zeroes_counters_and_checks_alignment(lib):
+    h = create(lib)
+    assert log(lib) == ["set " + " ".join(f"{i}=0" for i in range(2 * 2 + 4))]
+    cfg = kvq.make_config(2, 8, 2, 64, 100)
+    lib.kvq_nodev_clear()
+    for k, v, c in ((K + 8, V, C), (K, V + 128, C), (K, V, C + 4), (0, V, C)):
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.kvq_create(cfg, k, v, c, 0, lib)
+        assert e.value.status == kvq.KVQ_EINVAL
+    assert log(lib) == []
+    kvq.kvq_destroy(h, lib)
+
+
+# -- append ---------------------------------------------------------------------
+def test_append_flat_and_capacity(lib):
+    h = create(lib)
+    lib.kvq_nodev_clear()
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 60, None, 0, lib)
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 40, [40, 7], 0, lib)
+    assert log(lib) == ["append b0=0 T=60 n=60,60", "append b0=0 T=40 n=40,7"]
+    assert lengths(lib, h, 2) == ([100, 67], [0, 0])
+    lib.kvq_nodev_clear()
+    assert err(lib, kvq.kvq_append, h, Q, Q, kvq.KVQ_BF16, 1) == kvq.KVQ_ECAPACITY
+    assert err(lib, kvq.kvq_append, h, Q, Q, kvq.KVQ_BF16, 2, [2, 3]) == kvq.KVQ_EINVAL
+    assert err(lib, kvq.kvq_append, h, Q, Q, 7, 1) == kvq.KVQ_EINVAL
+    assert err(lib, kvq.kvq_append, h, Q, Q, kvq.KVQ_F32, 0) == kvq.KVQ_EINVAL
+    assert err(lib, kvq.kvq_append, h, 0, Q, kvq.KVQ_F32, 1) == kvq.KVQ_EINVAL
+    assert log(lib) == [] and lengths(lib, h, 2) == ([100, 67], [0, 0])
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_F32, 5, [0, 5], 0, lib)     # session 0 appends nothing
+    assert lengths(lib, h, 2)[0] == [100, 72]
+
+
+def test_append_sessions_split_across_launches(lib):
+    h = create(lib, n_seqs=70, capacity=10)
+    lib.kvq_nodev_clear()
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_F32, 2, [1] * 64 + [2] * 6, 0, lib)
+    assert log(lib) == ["append b0=0 T=2 n=" + ",".join(["1"] * 64), "append b0=64 T=2 n=2,2,2,2,2,2"]
+
+
+def test_ring_rebase_plan_matches_the_oracle_cache_model(lib):
+    from oracle.cache_model import OracleCache
+    B, cap, W, step = 3, 16, 8, 4
+    h = create(lib, n_seqs=B, capacity=cap, window=W, ring_step=step)
+    model = OracleCache(B, 2, 64, cap, window=W, ring_step=step)
+    rng = np.random.default_rng(0)
+    for _ in range(40):
+        n = rng.integers(0, 6, size=B)
+        T = int(n.max()) or 1
+        lib.kvq_nodev_clear()
+        before = lengths(lib, h, B)
+        kvq.kvq_append(h, Q, Q, kvq.KVQ_F32, T, n.tolist(), 0, lib)
+        z = np.zeros((B, T, 2, 64), np.float32)
+        model.append(z, z, n)
+        after = lengths(lib, h, B)
+        assert after == (model.len.tolist(), model.base.tolist())
+        # every rebase is a sequence of non-overlapping slabs, then the base_d write
+        moved = [ln for ln in log(lib) if ln.startswith("move")]
+        for b in range(B):
+            shift = after[1][b] - before[1][b]
+            if shift == 0:
+                continue
+            keep = before[0][b] - after[1][b]
+            slabs = [tuple(map(int, re.match(r"(\d+):(\d+)>(\d+)x(\d+)", tok).groups()))
+                     for ln in moved for tok in ln.split()[1:] if tok.startswith(f"{b}:")]
+            covered = 0
+            for (_, src, dst, rows) in slabs:
+                assert src == dst + shift and rows <= shift and dst == covered
+                covered += rows
+            assert covered == keep
+            assert f"{B + b}={after[1][b]}" in [t for ln in log(lib) if ln.startswith("set") for t in ln.split()]
+
+
+def test_ring_refuses_to_drop_visible_rows(lib):
+    h = create(lib, n_seqs=1, capacity=16, window=8, ring_step=4)
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_F32, 14, None, 0, lib)
+    lib.kvq_nodev_clear()
+    assert err(lib, kvq.kvq_append, h, Q, Q, kvq.KVQ_F32, 9) == kvq.KVQ_ERANGE
+    assert log(lib) == [] and lengths(lib, h, 1) == ([14], [0])
+
+
+# -- truncate -------------------------------------------------------------------
+def test_truncate(lib):
+    h = create(lib)
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_F32, 50, None, 0, lib)
+    lib.kvq_nodev_clear()
+    kvq.kvq_truncate(h, [47, 50], 0, lib)
+    assert log(lib) == ["set 0=47"] and lengths(lib, h, 2)[0] == [47, 50]
+    lib.kvq_nodev_clear()
+    assert err(lib, kvq.kvq_truncate, h, [48, 50]) == kvq.KVQ_EINVAL
+    assert err(lib, kvq.kvq_truncate, h, [-1, 50]) == kvq.KVQ_EINVAL
+    assert log(lib) == []
+
+
+def test_truncate_never_moves_base_and_guards_the_window(lib):
+    h = create(lib, n_seqs=1, capacity=16, window=8, ring_step=4)
+    for _ in range(30):
+        kvq.kvq_append(h, Q, Q, kvq.KVQ_F32, 1, None, 0, lib)
+    L, base = lengths(lib, h, 1)
+    assert base[0] > 0
+    lib.kvq_nodev_clear()
+    kvq.kvq_truncate(h, [base[0] + 8], 0, lib)
+    assert lengths(lib, h, 1) == ([base[0] + 8], base)
+    assert err(lib, kvq.kvq_truncate, h, [base[0] + 7]) == kvq.KVQ_ERANGE
+    assert all(not ln.startswith("move") for ln in log(lib))
+
+
+# -- decode -----------------------------------------------------------------------
+def test_decode_validation_and_plan(lib):
+    h = create(lib, n_seqs=2, capacity=5000)
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 3000, [3000, 1000], 0, lib)
+    ws = kvq.kvq_decode_workspace_bytes(h, 2, lib)
+    lib.kvq_nodev_clear()
+    kvq.kvq_decode(h, Q, kvq.KVQ_BF16, 2, None, 0.125, O, None, WS, ws, 0, lib)
+    (line,) = log(lib)
+    chunk, splits = map(int, re.search(r"chunk=(\d+) splits=(\d+)", line).groups())
+    assert chunk % 64 == 0 and splits == -(-3000 // chunk)
+    ml = int(re.search(r"ml_to_o=(\d+)", line).group(1))
+    assert ml >= 2 * splits * 2 * 8 * 4 and ml % 256 == 0
+    assert ws >= ml + 2 * splits * 2 * 8 * 64 * 4
+    lib.kvq_nodev_clear()
+    assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 2, None, 0.125, O, None, WS, ws - 1) == kvq.KVQ_EINVAL
+    assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 2, None, 0.125, O, None, WS + 16, ws) == kvq.KVQ_EINVAL
+    assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 17, None, 0.125, O, None, WS, 1 << 40) == kvq.KVQ_EINVAL
+    assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 2, None, float("nan"), O, None, WS, ws) == kvq.KVQ_EINVAL
+    assert err(lib, kvq.kvq_decode, h, 0, kvq.KVQ_BF16, 2, None, 0.125, O, None, WS, ws) == kvq.KVQ_EINVAL
+    kvq.kvq_truncate(h, [3000, 1], 0, lib)
+    lib.kvq_nodev_clear()
+    assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 2, None, 0.125, O, None, WS, 1 << 40) == kvq.KVQ_EINVAL
+    assert log(lib) == []
+
+
+def test_decode_query_tile_limits(lib):
+    h = create(lib, n_seqs=1, n_q_heads=64, n_kv_heads=1, head_dim=256, capacity=100)
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 50, None, 0, lib)
+    # 64 query rows of head_dim 256 exceed the 8192-float query tile
+    assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 1, None, 0.1, O, None, WS, 1 << 40) == kvq.KVQ_EUNSUPPORTED
+
+
+def test_decode_refuses_rebased_rows(lib):
+    h = create(lib, n_seqs=1, capacity=16, window=8, ring_step=4)
+    for _ in range(30):
+        kvq.kvq_append(h, Q, Q, kvq.KVQ_F32, 1, None, 0, lib)
+    L, base = lengths(lib, h, 1)
+    ok_T = L[0] - 8 + 1 - base[0]      # largest T whose first row's window is resident
+    kvq.kvq_decode(h, Q, kvq.KVQ_F32, ok_T, None, 0.1, O, None, WS, 1 << 40, 0, lib)
+    assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_F32, ok_T + 1, None, 0.1, O, None, WS, 1 << 40) == kvq.KVQ_ERANGE
+
+
+def test_split_rows_setting(lib):
+    h = create(lib, n_seqs=1, capacity=5000)
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_F32, 4000, None, 0, lib)
+    assert err(lib, kvq.kvq_set_split_rows, h, 100) == kvq.KVQ_EINVAL
+    kvq.kvq_set_split_rows(h, 640, lib)
+    lib.kvq_nodev_clear()
+    kvq.kvq_decode(h, Q, kvq.KVQ_F32, 1, None, 0.1, O, None, WS, 1 << 40, 0, lib)
+    assert "chunk=640 splits=7" in log(lib)[0]
+    assert kvq.kvq_info(h, lib).split_rows == 640
+
+
+def test_launch_failure_reports_edevice_and_keeps_the_mirror(lib):
+    h = create(lib)
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_F32, 10, None, 0, lib)
+    lib.kvq_nodev_fail_next()
+    assert err(lib, kvq.kvq_truncate, h, [5, 5]) == kvq.KVQ_EDEVICE
+    assert lengths(lib, h, 2)[0] == [10, 10]
+    lib.kvq_nodev_fail_next()
+    assert err(lib, kvq.kvq_append, h, Q, Q, kvq.KVQ_F32, 1) == kvq.KVQ_EDEVICE
+    assert lengths(lib, h, 2)[0] == [10, 10]
+    assert "simulated" in kvq.kvq_last_error(lib)
+
+
+def test_info(lib):
+    h = create(lib, n_seqs=3, capacity=77, window=5)
+    info = kvq.kvq_info(h, lib)
+    assert (info.config.n_seqs, info.config.capacity, info.config.window) == (3, 77, 5)
+    assert (info.k_planes, info.v_planes, info.counters) == (K, V, C)

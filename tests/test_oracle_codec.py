@@ -197,3 +197,12 @@ def test_q5_1_codes_in_range_and_monotone():
         c = _unpack_q5_1(oracle.q5_1_encode(row))
         assert c.min() >= 0 and c.max() <= 31
         assert np.all(np.diff(c) >= 0)
+
+
+def test_q5_1_zero_minimum_is_stored_as_positive_zero():
+    x = np.zeros(32, np.float32)
+    x[1::3] = -0.0
+    x[2::5] = 2.5
+    for arr in (x, x[::-1].copy(), np.full(32, -0.0, np.float32)):
+        blk = oracle.q5_1_encode(arr)
+        assert blk[2] == 0 and blk[3] == 0
