@@ -144,7 +144,10 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
         mn = fminf(mn, __shfl_xor(mn, m));
         mx = fmaxf(mx, __shfl_xor(mx, m));
     }
-    mn = mn + 0.0f;   // a zero minimum is stored as +0 whatever the sign of the zeros
+    // signed zeros: a zero extreme is taken as +0, so that neither the stored
+    // offset nor the step of a block is ever -0
+    if (mn == 0.0f) mn = 0.0f;
+    if (mx == 0.0f) mx = 0.0f;
     const uint16_t dv16 = f16_bits((mx - mn) / 31.0f);
     const uint16_t mv16 = f16_bits(mn);
     const float dvs = f16_value(dv16);

@@ -145,7 +145,10 @@ void kvqo_q5_1_encode(const float* x, uint8_t* blk) {
         if (x[i] < mn) mn = x[i];
         if (x[i] > mx) mx = x[i];
     }
-    mn = mn + 0.0f;  /* a zero minimum is stored as +0 whatever the sign of the zeros */
+    /* signed zeros: a zero extreme is taken as +0, so that neither the stored
+     * offset nor the step of a block is ever -0 */
+    if (mn == 0.0f) mn = 0.0f;
+    if (mx == 0.0f) mx = 0.0f;
     float d = (mx - mn) / 31.0f;
     uint16_t d16 = kvqo_f32_to_f16(d);
     uint16_t m16 = kvqo_f32_to_f16(mn);

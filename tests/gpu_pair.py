@@ -70,12 +70,15 @@ class Pair:
             gk = kp[b].index_select(0, idx).cpu().numpy()
             gv = vp[b].index_select(0, idx).cpu().numpy()
             rk, rv = self.ref.k[b][sel], self.ref.v[b][sel]
-            if not np.array_equal(gk, rk):
-                r = sel[np.nonzero((gk != rk).any(1))[0][0]]
-                raise AssertionError(f"K bytes differ: session {b}, physical row {r}")
-            if not np.array_equal(gv, rv):
-                r = sel[np.nonzero((gv != rv).any(1))[0][0]]
-                raise AssertionError(f"V bytes differ: session {b}, physical row {r}")
+            for name, g, r, bb in (("K", gk, rk, 34), ("V", gv, rv, 24)):
+                if not np.array_equal(g, r):
+                    i = np.nonzero((g != r).any(1))[0][0]
+                    gb, rb = g[i].reshape(-1, bb), r[i].reshape(-1, bb)
+                    blks = np.nonzero((gb != rb).any(1))[0]
+                    j = blks[0]
+                    raise AssertionError(
+                        f"{name} bytes differ: session {b}, physical row {sel[i]}, blocks {blks.tolist()}; "
+                        f"block {j}: gpu {bytes(gb[j]).hex(' ')} oracle {bytes(rb[j]).hex(' ')}")
 
     def decode(self, q, scale, sinks=None, sel=None, what="decode"):
         T = q.shape[1]

@@ -79,10 +79,10 @@ def test_append_edge_blocks():
     rng = np.random.default_rng(3)
     while len(blocks) < 16:
         blocks.append((rng.standard_normal(32) * 10.0 ** rng.integers(-5, 4)).astype(np.float32))
-    row = np.concatenate(blocks).reshape(1, 1, 1, hd)
+    row = np.concatenate(blocks).reshape(1, 1, 4, hd // 4)     # 4 KV heads of 128
     for io in ("f32", "bf16"):
         x = row if io == "f32" else round_bf16(row)
-        p = Pair(1, 1, 1, hd, 4, io=io)
+        p = Pair(1, 4, 4, hd // 4, 4, io=io)
         p.append(x, -x)
         p.append(x[:, :, :, ::-1].copy(), x)
         p.check_planes()

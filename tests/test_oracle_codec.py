@@ -206,3 +206,8 @@ def test_q5_1_zero_minimum_is_stored_as_positive_zero():
     for arr in (x, x[::-1].copy(), np.full(32, -0.0, np.float32)):
         blk = oracle.q5_1_encode(arr)
         assert blk[2] == 0 and blk[3] == 0
+
+
+def test_q5_1_negative_zero_block_has_positive_zero_step_and_offset():
+    blk = oracle.q5_1_encode(np.full(32, -0.0, np.float32))
+    assert np.array_equal(blk, np.zeros(24, np.uint8))
