@@ -1,0 +1,463 @@
+// kvq_decode.hip -- split-K flash decode over the quantized cache (gfx950).
+// Included by kvq_kernels.hip (inside namespace kvq).
+//
+// What it computes (cortiq-engine "Struct LayerKvCache", attend_group and
+// attend_group_upto; memra-engine "Struct KvLayer", len_d / base_d): for one
+// session b, one KV head g and one chunk of logical rows, the unnormalised
+// online-softmax partial (m, l, o) of each of the group's R = T*H/Hkv query
+// rows.  Row r = t*hpk + hh is Q head g*hpk + hh at verify row t and sees the
+// rows [max(0, upto_t - window), upto_t), upto_t = len - T + t + 1; the score is
+// scale * <q, k> with k the dequantized q8_0 row.
+//
+// Organisation.  A workgroup is (session, chunk, KV head): 4 waves, each
+// streaming its own 32-row tiles of the chunk (tiles w, w+4, ...) through a
+// private LDS area, with no workgroup barrier inside the loop.  Per tile:
+//   1. stage: K blocks are re-aligned (34-byte blocks sit at 2-byte alignment)
+//      into [row][dim] code bytes plus fp32 scales; V blocks are unpacked from
+//      q5_1 into [row][dim] code bytes (0..31) plus fp32 steps and fp16 offsets.
+//   2. scores: S = Q K^T with v_mfma_f32_16x16x32_f16, one MFMA per 32-element
+//      block: the codes are exact in fp16 and Q is split into fp16 hi (+ lo for
+//      fp32 input); each lane owns one key of the output tile and scales the
+//      block's partial dot products by that key's q8_0 scale in fp32.
+//   3. online softmax in base 2 (v_exp_f32), row maxima by DPP row rotations.
+//   4. P V with the same MFMA: P is written to LDS as [row][query] fp16 and
+//      read back with ds_read_b64_tr_b16 as the A operand; V codes come back
+//      as the B operand with ds_read_b64_tr_b8 (8 keys of one dim per lane),
+//      so the token-major plane needs no explicit transpose.  The q5_1 step is
+//      folded into P (P' = P * step per block) and the q5_1 offset term
+//      sum_j P_j * m_j is one more MFMA against the [row][block] offsets.
+// The four waves' partials are merged in a fixed order (deterministic), and
+// one partial per (session, chunk, query row) goes to the workspace.
+namespace dec {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef int i2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i2 lds_i2;
+typedef __attribute__((address_space(3))) s4 lds_s4;
+
+constexpr int kWaves = 4;
+constexpr int kTile = 32;                        // keys per wave tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <int NB, int RT>
+struct Layout {
+    static constexpr int HD = NB * 32;
+    static constexpr int KROW = NB * 32 + 16;    // padded row strides (bytes)
+    static constexpr int VROW = NB * 32 + 16;
+    static constexpr int PROW = RT * 32;         // [key][RT*16] fp16
+    static constexpr int KC = 0;                                  // K codes [32][KROW]
+    static constexpr int VC = KC + kTile * KROW;                  // V codes [32][VROW]
+    static constexpr int KS = VC + kTile * VROW;                  // K scales f32 [32][NB]
+    static constexpr int VD = KS + ((kTile * NB * 4 + 15) & ~15); // V steps  f32 [32][NB]
+    static constexpr int VM = VD + ((kTile * NB * 4 + 15) & ~15); // V offsets f16 [32][16]
+    static constexpr int PU = VM + kTile * 32;                    // P  f16 [32][RT*16]
+    static constexpr int PP = PU + kTile * PROW;                  // P' f16 [32][RT*16]
+    static constexpr int WAVE = PP + kTile * PROW;
+    static constexpr int QFRAG = RT * NB * 64 * 16;               // Q fragments, fp16
+    static constexpr int Q = kWaves * WAVE;
+    static constexpr int ML = Q + 2 * QFRAG;                      // [wave][RT*16][2] f32
+    static constexpr int BYTES = ML + kWaves * RT * 16 * 2 * 4;
+    static_assert(RT * 16 * HD * 4 <= kWaves * WAVE, "merge buffer must fit in the wave areas");
+};
+
+__device__ __forceinline__ float row_max16(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false)));
+    return v;
+}
+
+__device__ __forceinline__ float row_sum16(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false));
+    return v;
+}
+
+// 4 unsigned bytes u -> two fp16 pairs (1024 + u): v_perm_b32 with 0x64 as the high byte.
+__device__ __forceinline__ h2 bytes_lo(uint32_t x) {
+    return __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u));
+}
+__device__ __forceinline__ h2 bytes_hi(uint32_t x) {
+    return __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u));
+}
+
+// 8 signed q8_0 codes -> fp16 (exact): (c ^ 0x80) = c + 128, then 1024 + c + 128 - 1152.
+__device__ __forceinline__ h8 k_codes_f16(uint32_t lo, uint32_t hi) {
+    const h2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
+    lo ^= 0x80808080u;
+    hi ^= 0x80808080u;
+    h2 a = bytes_lo(lo) - off, b = bytes_hi(lo) - off, c = bytes_lo(hi) - off, d = bytes_hi(hi) - off;
+    return (h8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// 8 q5_1 codes (bytes 0..31) -> fp16 (exact).
+__device__ __forceinline__ h8 v_codes_f16(uint32_t lo, uint32_t hi) {
+    const h2 off = {(_Float16)1024.0f, (_Float16)1024.0f};
+    h2 a = bytes_lo(lo) - off, b = bytes_hi(lo) - off, c = bytes_lo(hi) - off, d = bytes_hi(hi) - off;
+    return (h8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// bit k of the low 4 bits of x -> bit 4 of byte k
+__device__ __forceinline__ uint32_t fifth_bits(uint32_t x4) {
+    return ((x4 * 0x204081u) & 0x01010101u) << 4;
+}
+
+__device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ h8 tr16_pair(const uint8_t* p0, const uint8_t* p1) {
+    s4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0));
+    s4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p1));
+    h4 ha = __builtin_bit_cast(h4, a), hb = __builtin_bit_cast(h4, b);
+    return (h8){ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
+}
+
+__device__ __forceinline__ void lds_order() {
+    // DS instructions of one wave execute in order; this only stops the
+    // compiler from moving LDS accesses across the point.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int NB, int RT, bool QLO>
+__global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
+    using LY = Layout<NB, RT>;
+    constexpr int HD = LY::HD;
+    constexpr int KSEG = NB * 34;
+    constexpr int VSEG = NB * 24;
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int q4 = lane >> 4, j16 = lane & 15;
+
+    // XCD-aware order: consecutive logical items (the KV heads of one chunk)
+    // land on one XCD, which receives every 8th workgroup id.
+    const int W = gridDim.x;
+    const int wid = blockIdx.x;
+    const int L = (wid & 7) * (W >> 3) + (wid >> 3);
+    const int g = L % p.Hkv;
+    const int s = (L / p.Hkv) % p.splits;
+    const int b = L / (p.Hkv * p.splits);
+    if (b >= p.B) return;
+    const int len = p.len_d[b];
+    const int base = p.base_d[b];
+    const int lo_all = p.window > 0 ? max(0, len - p.T + 1 - p.window) : 0;
+    const int c0 = lo_all + s * p.chunk;
+    const int c1 = min(c0 + p.chunk, len);
+    if (c0 >= c1) return;
+    const int R = p.T * p.hpk;
+
+    // Q fragments: fragment (rt, blk), lane l holds q[r = rt*16 + l%16][blk*32 + 8*(l/16) .. +7]
+    for (int f = tid; f < RT * NB * 64; f += 256) {
+        const int l = f & 63, fb = f >> 6;
+        const int blk = fb % NB, rt = fb / NB;
+        const int r = rt * 16 + (l & 15);
+        h8 hi = {}, lo = {};
+        if (r < R) {
+            const int t = r / p.hpk, hh = r % p.hpk;
+            const size_t i0 = (((size_t)b * p.T + t) * p.H + g * p.hpk + hh) * HD + blk * 32 + 8 * (l >> 4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = load_in(p.q, p.dtype, i0 + e);
+                const _Float16 xh = (_Float16)x;
+                hi[e] = xh;
+                if (QLO) lo[e] = (_Float16)(x - (float)xh);
+            }
+        }
+        *reinterpret_cast<h8*>(smem + LY::Q + f * 16) = hi;
+        if (QLO) *reinterpret_cast<h8*>(smem + LY::Q + LY::QFRAG + f * 16) = lo;
+    }
+
+    // visible range of this lane's score rows r = rt*16 + 4*q4 + i
+    int vis_lo[RT][4], vis_hi[RT][4];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = rt * 16 + 4 * q4 + i;
+            int hi = 0, lo = 0;
+            if (r < R) {
+                hi = len - p.T + r / p.hpk + 1;
+                lo = p.window > 0 ? max(0, hi - p.window) : 0;
+            }
+            vis_lo[rt][i] = max(lo, c0);
+            vis_hi[rt][i] = min(hi, c1);
+        }
+
+    f4 oacc[RT][2 * NB];
+    f4 macc[RT];
+    float mrow[RT][4], lsum[RT][4];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        macc[rt] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dt = 0; dt < 2 * NB; ++dt) oacc[rt][dt] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            mrow[rt][i] = -INFINITY;
+            lsum[rt][i] = 0.0f;
+        }
+    }
+    const float sc2 = p.scale * kLog2e;
+    __syncthreads();   // Q fragments are in LDS
+
+    const uint8_t* kplane = p.k_planes + (int64_t)b * p.k_stride + (int64_t)g * KSEG;
+    const uint8_t* vplane = p.v_planes + (int64_t)b * p.v_stride + (int64_t)g * VSEG;
+    uint8_t* Wb = smem + wave * LY::WAVE;
+    float* ks = reinterpret_cast<float*>(Wb + LY::KS);
+    float* vd = reinterpret_cast<float*>(Wb + LY::VD);
+    uint16_t* vm = reinterpret_cast<uint16_t*>(Wb + LY::VM);
+
+    for (int t0 = c0 + wave * kTile; t0 < c1; t0 += kWaves * kTile) {
+        // ---- 1. stage the tile's K and V blocks (rows past c1 repeat row c1-1)
+#pragma unroll
+        for (int u0 = 0; u0 < kTile * NB; u0 += 64) {
+            const int u = u0 + lane;
+            if (kTile * NB % 64 == 0 || u < kTile * NB) {
+                const int key = u / NB, blk = u - key * NB;
+                const int64_t row = (int64_t)(min(t0 + key, c1 - 1) - base);
+                const uint8_t* kb = kplane + row * p.k_row + blk * 34;
+                const uint8_t* vb = vplane + row * p.v_row + blk * 24;
+                // K: scale at kb, codes at kb+2 (2-byte aligned): 8 aligned dwords
+                // from the aligned-down code address, the last 2 code bytes
+                // separately, funnel-shifted by 0 or 2 bytes.
+                const uint16_t ds16 = *reinterpret_cast<const uint16_t*>(kb);
+                const uintptr_t ca = reinterpret_cast<uintptr_t>(kb + 2);
+                const uint32_t* kw = reinterpret_cast<const uint32_t*>(ca & ~(uintptr_t)3);
+                const uint32_t sh = (uint32_t)(ca & 3);
+                uint32_t w[9];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) w[i] = kw[i];
+                w[8] = *reinterpret_cast<const uint16_t*>(kb + 32);
+                uint32_t cd[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) cd[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], sh);
+                uint4* kd = reinterpret_cast<uint4*>(Wb + LY::KC + key * LY::KROW + blk * 32);
+                kd[0] = (uint4){cd[0], cd[1], cd[2], cd[3]};
+                kd[1] = (uint4){cd[4], cd[5], cd[6], cd[7]};
+                ks[key * NB + blk] = f16_value(ds16);
+                // V: [d16 | m16 << 16][fifth bits][16 nibble bytes], 8-byte aligned
+                const uint2 va = reinterpret_cast<const uint2*>(vb)[0];
+                const uint2 vn0 = reinterpret_cast<const uint2*>(vb)[1];
+                const uint2 vn1 = reinterpret_cast<const uint2*>(vb)[2];
+                const uint32_t qh = va.y;
+                const uint32_t nib[4] = {vn0.x, vn0.y, vn1.x, vn1.y};
+                uint32_t vc[8];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    vc[t] = (nib[t] & 0x0F0F0F0Fu) | fifth_bits((qh >> (4 * t)) & 15u);
+                    vc[4 + t] = ((nib[t] >> 4) & 0x0F0F0F0Fu) | fifth_bits((qh >> (16 + 4 * t)) & 15u);
+                }
+                uint4* vdst = reinterpret_cast<uint4*>(Wb + LY::VC + key * LY::VROW + blk * 32);
+                vdst[0] = (uint4){vc[0], vc[1], vc[2], vc[3]};
+                vdst[1] = (uint4){vc[4], vc[5], vc[6], vc[7]};
+                vd[key * NB + blk] = f16_value((uint16_t)(va.x & 0xFFFF));
+                vm[key * 16 + blk] = (uint16_t)(va.x >> 16);
+            }
+        }
+        lds_order();
+
+        // ---- 2. scores: sacc[rt][h][i] = S[r = rt*16 + 4*q4 + i][key = 16h + j16]
+        f4 sacc[RT][2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int key = 16 * h + j16;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) sacc[rt][h] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk) {
+                const uint2 raw = *reinterpret_cast<const uint2*>(Wb + LY::KC + key * LY::KROW + blk * 32 + 8 * q4);
+                const h8 kf = k_codes_f16(raw.x, raw.y);
+                const float kscale = ks[key * NB + blk];
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    const h8 qa = *reinterpret_cast<const h8*>(smem + LY::Q + ((rt * NB + blk) * 64 + lane) * 16);
+                    f4 d = mfma(qa, kf, (f4){0.f, 0.f, 0.f, 0.f});
+                    if (QLO) {
+                        const h8 ql = *reinterpret_cast<const h8*>(smem + LY::Q + LY::QFRAG + ((rt * NB + blk) * 64 + lane) * 16);
+                        d = mfma(ql, kf, d);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sacc[rt][h][i] = fmaf(kscale, d[i], sacc[rt][h][i]);
+                }
+            }
+        }
+
+        // ---- 3. online softmax (base 2)
+        float pv[RT][2][4];
+        float alpha[RT][4];
+        bool rescale = false;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j0 = t0 + j16, j1 = t0 + 16 + j16;
+                const float s0 = (j0 >= vis_lo[rt][i] && j0 < vis_hi[rt][i]) ? sacc[rt][0][i] * sc2 : -INFINITY;
+                const float s1 = (j1 >= vis_lo[rt][i] && j1 < vis_hi[rt][i]) ? sacc[rt][1][i] * sc2 : -INFINITY;
+                const float mt = row_max16(fmaxf(s0, s1));
+                const float mold = mrow[rt][i];
+                const float mnew = fmaxf(mold, mt);
+                float a = 1.0f, p0 = 0.0f, p1 = 0.0f;
+                if (mnew != -INFINITY) {
+                    a = __builtin_amdgcn_exp2f(mold - mnew);      // 0 when mold is -inf
+                    p0 = __builtin_amdgcn_exp2f(s0 - mnew);
+                    p1 = __builtin_amdgcn_exp2f(s1 - mnew);
+                }
+                rescale |= (a != 1.0f);
+                alpha[rt][i] = a;
+                mrow[rt][i] = mnew;
+                lsum[rt][i] = fmaf(lsum[rt][i], a, p0 + p1);
+                pv[rt][0][i] = p0;
+                pv[rt][1][i] = p1;
+            }
+        if (__any(rescale)) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                    for (int dt = 0; dt < 2 * NB; ++dt) oacc[rt][dt][i] *= alpha[rt][i];
+                    macc[rt][i] *= alpha[rt][i];
+                }
+        }
+        // P to LDS as [key][r] fp16
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const h4 ph = {(_Float16)pv[rt][h][0], (_Float16)pv[rt][h][1], (_Float16)pv[rt][h][2],
+                               (_Float16)pv[rt][h][3]};
+                *reinterpret_cast<h4*>(Wb + LY::PU + (16 * h + j16) * LY::PROW + rt * 32 + 8 * q4) = ph;
+            }
+
+        // ---- 4. P V.  tr16 rows: keys 8*q4 + (j16>>2) (+4), columns r; lane j16 supplies chunk j16&3.
+        const int trow = 8 * q4 + (j16 >> 2);
+        const int tcol = 8 * (j16 & 3);
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const float st = vd[(16 * h + j16) * NB + blk];
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    const h4 ph = {(_Float16)(pv[rt][h][0] * st), (_Float16)(pv[rt][h][1] * st),
+                                   (_Float16)(pv[rt][h][2] * st), (_Float16)(pv[rt][h][3] * st)};
+                    *reinterpret_cast<h4*>(Wb + LY::PP + (16 * h + j16) * LY::PROW + rt * 32 + 8 * q4) = ph;
+                }
+            }
+            lds_order();
+            h8 pa[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                pa[rt] = tr16_pair(Wb + LY::PP + trow * LY::PROW + rt * 32 + tcol,
+                                   Wb + LY::PP + (trow + 4) * LY::PROW + rt * 32 + tcol);
+#pragma unroll
+            for (int dd = 0; dd < 2; ++dd) {
+                const int d0 = blk * 32 + 16 * dd;
+                const i2 vb = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (lds_i2*)(Wb + LY::VC + (8 * q4 + (j16 >> 1)) * LY::VROW + d0 + 8 * (j16 & 1)));
+                const h8 vf = v_codes_f16((uint32_t)vb[0], (uint32_t)vb[1]);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) oacc[rt][2 * blk + dd] = mfma(pa[rt], vf, oacc[rt][2 * blk + dd]);
+            }
+            lds_order();   // the next block overwrites P'
+        }
+        // q5_1 offset term: macc[r][blk] += sum_key P[r][key] * m[key][blk]
+        {
+            const h8 mb = tr16_pair(Wb + LY::VM + trow * 32 + tcol, Wb + LY::VM + (trow + 4) * 32 + tcol);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const h8 pu = tr16_pair(Wb + LY::PU + trow * LY::PROW + rt * 32 + tcol,
+                                        Wb + LY::PU + (trow + 4) * LY::PROW + rt * 32 + tcol);
+                macc[rt] = mfma(pu, mb, macc[rt]);
+            }
+        }
+        lds_order();   // the next tile's staging overwrites this tile
+    }
+
+    // ---- finish the wave: full row sums, fold the offset term into O
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lsum[rt][i] = row_sum16(lsum[rt][i]);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int dt = 0; dt < 2 * NB; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) oacc[rt][dt][i] += __shfl(macc[rt][i], 16 * q4 + dt / 2);
+
+    // ---- merge the four waves in a fixed order
+    float* ml = reinterpret_cast<float*>(smem + LY::ML);
+    if (j16 == 0) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = rt * 16 + 4 * q4 + i;
+                ml[(wave * RT * 16 + r) * 2] = mrow[rt][i];
+                ml[(wave * RT * 16 + r) * 2 + 1] = lsum[rt][i];
+            }
+    }
+    __syncthreads();   // all waves are past their tiles; the wave areas become the merge buffer
+    float fac[RT][4];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = rt * 16 + 4 * q4 + i;
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml[(w * RT * 16 + r) * 2]);
+            fac[rt][i] = (mrow[rt][i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mrow[rt][i] - M);
+        }
+    float* obuf = reinterpret_cast<float*>(smem);
+    for (int w = 0; w < kWaves; ++w) {
+        if (wave == w) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int dt = 0; dt < 2 * NB; ++dt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = rt * 16 + 4 * q4 + i;
+                        float* o = obuf + r * HD + 16 * dt + j16;
+                        const float v = oacc[rt][dt][i] * fac[rt][i];
+                        *o = (w == 0) ? v : *o + v;
+                    }
+        }
+        __syncthreads();
+    }
+    const size_t row0 = ((size_t)b * p.splits + s) * p.T;
+    for (int r = tid; r < R; r += 256) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml[(w * RT * 16 + r) * 2]);
+        float l = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float mw = ml[(w * RT * 16 + r) * 2];
+            if (mw != -INFINITY) l += ml[(w * RT * 16 + r) * 2 + 1] * __builtin_amdgcn_exp2f(mw - M);
+        }
+        const int t = r / p.hpk, h = g * p.hpk + r % p.hpk;
+        const size_t idx = (row0 + t) * p.H + h;
+        p.part_ml[2 * idx] = (M == -INFINITY) ? -INFINITY : M * kLn2;
+        p.part_ml[2 * idx + 1] = l;
+    }
+    for (int e = tid; e < R * HD; e += 256) {
+        const int r = e / HD, d = e - r * HD;
+        const int t = r / p.hpk, h = g * p.hpk + r % p.hpk;
+        p.part_o[((row0 + t) * p.H + h) * HD + d] = obuf[r * HD + d];
+    }
+}
+
+}  // namespace dec

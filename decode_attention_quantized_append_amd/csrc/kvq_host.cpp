@@ -131,6 +131,8 @@ Plan make_plan(const kvq_cache* h, int32_t T) {
         chunk = round_up(ceil_div(std::max<int64_t>(total, 1) * c.n_kv_heads, 512), kvq::kSplitQuantum);
         chunk = std::min<int64_t>(std::max<int64_t>(chunk, 256), 1 << 16);
     }
+    // at most kMaxSplits chunks per session
+    chunk = std::max<int64_t>(chunk, round_up(ceil_div(maxvis, kvq::kMaxSplits), kvq::kSplitQuantum));
     Plan p;
     p.chunk = (int32_t)chunk;
     p.splits = (int32_t)std::max<int64_t>(1, ceil_div(maxvis, chunk));
@@ -317,9 +319,7 @@ kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, c
     const kvq_config& c = h->cfg;
     const int hpk = c.n_q_heads / c.n_kv_heads;
     if (T < 1 || (int64_t)T * hpk > kvq::kMaxRows)
-        return fail(KVQ_EINVAL, "need 1 <= T * n_q_heads / n_kv_heads <= 64");
-    if ((int64_t)T * hpk * c.head_dim > kvq::kMaxQFloats)
-        return fail(KVQ_EUNSUPPORTED, "T * n_q_heads / n_kv_heads * head_dim above 8192");
+        return fail(KVQ_EINVAL, "need 1 <= T * n_q_heads / n_kv_heads <= 32");
     for (int b = 0; b < c.n_seqs; ++b) {
         if (h->len[b] < T)
             return fail(KVQ_EINVAL, "session " + std::to_string(b) + " holds fewer than T rows");

@@ -18,6 +18,7 @@
 //   combine_kernel  log-sum-exp fold of the splits plus the sink column.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -105,16 +106,13 @@ __global__ void move_kernel(MoveParams p) {
 // rounded to fp16 to nearest even, and codes from the STORED fp16 values,
 // rounded half to even (v_rndne_f32) and clamped.
 #pragma clang fp contract(off)
-__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
-    const int nblk = p.Hkv * p.hd / 32;
+__device__ __forceinline__ void append_unit(const AppendParams& p, int64_t unit, int64_t units, int nblk) {
     const int lane = threadIdx.x & 31;
-    const int64_t unit = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 5;
-    const int64_t units = (int64_t)p.nsess * p.T * nblk;
     bool active = unit < units;
     int bi = 0, t = 0, blk = 0;
     if (active) {
         blk = (int)(unit % nblk);
-        int64_t rt = unit / nblk;
+        const int64_t rt = unit / nblk;
         t = (int)(rt % p.T);
         bi = (int)(rt / p.T);
         active = t < p.n_new[bi];
@@ -168,245 +166,78 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
         }
         if (lane < 16) vd[8 + lane] = (uint8_t)((cv & 15) | ((cv_hi & 15) << 4));
     }
-    // The last workgroup to finish advances len_d: every workgroup has read
-    // its slot from len_d before it counts itself done.
+}
+
+// Grid-stride over units of 8 blocks per workgroup step; the last workgroup
+// to finish advances len_d.  Every workgroup has consumed its len_d reads
+// (they fix its store addresses) before thread 0 counts it done, so a relaxed
+// device-scope counter orders the reads before the final write.
+__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
+    const int nblk = p.Hkv * p.hd / 32;
+    const int64_t units = (int64_t)p.nsess * p.T * nblk;
+    for (int64_t u0 = (int64_t)blockIdx.x * 8; u0 < units; u0 += (int64_t)gridDim.x * 8)
+        append_unit(p, u0 + (threadIdx.x >> 5), units, nblk);
     __syncthreads();
     if (threadIdx.x == 0) {
-        __threadfence();
         const int prev = atomicAdd(p.done, 1);
         if (prev == (int)gridDim.x - 1) {
             for (int i = 0; i < p.nsess; ++i) p.len_d[p.b0 + i] += p.n_new[i];
             atomicExch(p.done, 0);
-            __threadfence();
         }
     }
 }
 #pragma clang fp contract(on)
 
 // ---------------------------------------------------------------------------
-// Decode, first version: plain fp32 VALU arithmetic on codes staged in LDS.
-// Workgroup = (session b, split s, KV head g), 256 threads; the split covers
-// rows [lo + s*chunk, min(lo + (s+1)*chunk, len)) of the union of the visible
-// ranges of the T query rows.  Query row r = t*hpk + hh is Q head g*hpk + hh
-// at verify row t.
-constexpr int kTK = 64;   // keys per tile
-
-__device__ __forceinline__ int round16(int x) { return (x + 15) & ~15; }
-
-template <int NB>
-__host__ __device__ constexpr int decode_lds_bytes(int R) {
-    return R * NB * 32 * 4 + ((kTK * NB * 34 + 15) & ~15) + ((kTK * NB * 24 + 15) & ~15) +
-           R * kTK * 4 + 3 * kMaxRows * 4;
-}
-
-template <int NB>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
-    constexpr int HD = NB * 32;
-    constexpr int KSEG = NB * 34;
-    constexpr int VSEG = NB * 24;
-    constexpr int RG = (256 / HD) > 0 ? 256 / HD : 1;       // row groups in the PV phase
-    constexpr int MAXO = kMaxQFloats / 256;                  // accumulators per thread
-    extern __shared__ __align__(16) uint8_t smem[];
-    const int R = p.T * p.hpk;
-    float* q_s = reinterpret_cast<float*>(smem);
-    uint8_t* kt = smem + R * HD * 4;
-    uint8_t* vt = kt + round16(kTK * KSEG);
-    float* sp = reinterpret_cast<float*>(vt + round16(kTK * VSEG));
-    float* m_s = sp + R * kTK;
-    float* l_s = m_s + kMaxRows;
-    float* a_s = l_s + kMaxRows;
-
-    // XCD-aware order: consecutive logical items (the KV heads of one chunk)
-    // land on the same XCD, which dispatches workgroup ids round-robin.
-    const int W = gridDim.x;
-    const int w = blockIdx.x;
-    const int L = (w & 7) * (W >> 3) + (w >> 3);
-    const int g = L % p.Hkv;
-    const int s = (L / p.Hkv) % p.splits;
-    const int b = L / (p.Hkv * p.splits);
-    if (b >= p.B) return;
-    const int len = p.len_d[b];
-    const int base = p.base_d[b];
-    const int lo = p.window > 0 ? max(0, len - p.T + 1 - p.window) : 0;
-    const int c0 = lo + s * p.chunk;
-    const int c1 = min(c0 + p.chunk, len);
-    if (c0 >= c1) return;
-    const int tid = threadIdx.x;
-
-    for (int i = tid; i < R * HD; i += 256) {
-        const int r = i / HD, d = i % HD;
-        const int t = r / p.hpk, hh = r % p.hpk;
-        q_s[i] = load_in(p.q, p.dtype, (((size_t)b * p.T + t) * p.H + g * p.hpk + hh) * HD + d);
-    }
-    for (int r = tid; r < R; r += 256) {
-        m_s[r] = -INFINITY;
-        l_s[r] = 0.0f;
-    }
-    const int d = tid % HD;
-    const int rg = tid / HD;
-    float o[MAXO];
-#pragma unroll
-    for (int i = 0; i < MAXO; ++i) o[i] = 0.0f;
-    __syncthreads();
-
-    const uint8_t* kp = p.k_planes + (int64_t)b * p.k_stride + (int64_t)g * KSEG;
-    const uint8_t* vp = p.v_planes + (int64_t)b * p.v_stride + (int64_t)g * VSEG;
-    for (int j0 = c0; j0 < c1; j0 += kTK) {
-        const int nk = min(kTK, c1 - j0);
-        // stage the group's K and V segments of rows j0 .. j0+nk-1
-        for (int u = tid; u < nk * (KSEG / 2); u += 256) {
-            const int key = u / (KSEG / 2), off = u % (KSEG / 2);
-            reinterpret_cast<uint16_t*>(kt + key * KSEG)[off] =
-                reinterpret_cast<const uint16_t*>(kp + (int64_t)(j0 + key - base) * p.k_row)[off];
-        }
-        for (int u = tid; u < nk * (VSEG / 2); u += 256) {
-            const int key = u / (VSEG / 2), off = u % (VSEG / 2);
-            reinterpret_cast<uint16_t*>(vt + key * VSEG)[off] =
-                reinterpret_cast<const uint16_t*>(vp + (int64_t)(j0 + key - base) * p.v_row)[off];
-        }
-        __syncthreads();
-        // scores: thread -> key tid%64, rows r = tid/64 + 4*i
-        {
-            const int key = tid & 63;
-            const int r0 = tid >> 6;
-            float acc[kMaxRows / 4];
-#pragma unroll
-            for (int i = 0; i < kMaxRows / 4; ++i) acc[i] = 0.0f;
-            if (key < nk) {
-                const uint16_t* kr = reinterpret_cast<const uint16_t*>(kt + key * KSEG);
-                for (int kb = 0; kb < NB; ++kb) {
-                    const float ds = f16_value(kr[kb * 17]);
-                    float c[32];
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const uint16_t wd = kr[kb * 17 + 1 + i];
-                        c[2 * i] = (float)(int8_t)(wd & 0xFF);
-                        c[2 * i + 1] = (float)(int8_t)(wd >> 8);
-                    }
-#pragma unroll
-                    for (int i = 0; i < kMaxRows / 4; ++i) {
-                        const int r = r0 + 4 * i;
-                        if (r < R) {
-                            const float* qr = q_s + r * HD + kb * 32;
-                            float dot = 0.0f;
-#pragma unroll
-                            for (int e = 0; e < 32; ++e) dot = fmaf(qr[e], c[e], dot);
-                            acc[i] = fmaf(ds, dot, acc[i]);
-                        }
-                    }
-                }
-            }
-            const int j = j0 + key;
-#pragma unroll
-            for (int i = 0; i < kMaxRows / 4; ++i) {
-                const int r = r0 + 4 * i;
-                if (r < R) {
-                    const int t = r / p.hpk;
-                    const int hi = len - p.T + t + 1;
-                    const int lo_t = p.window > 0 ? max(0, hi - p.window) : 0;
-                    const bool vis = key < nk && j >= lo_t && j < hi;
-                    sp[r * kTK + key] = vis ? acc[i] * p.scale : -INFINITY;
-                }
-            }
-        }
-        __syncthreads();
-        // online softmax: wave -> rows r = wave + 4*i, lane -> key
-        {
-            const int wv = tid >> 6, lane = tid & 63;
-            for (int r = wv; r < R; r += 4) {
-                const float sv = sp[r * kTK + lane];
-                const float m_old = m_s[r];
-                const float m_new = fmaxf(m_old, wave_max(sv));
-                float pv = 0.0f, alpha = 1.0f;
-                if (m_new != -INFINITY) {
-                    pv = (sv == -INFINITY) ? 0.0f : expf(sv - m_new);
-                    alpha = (m_old == -INFINITY) ? 0.0f : expf(m_old - m_new);
-                }
-                const float sum = wave_sum(pv);
-                sp[r * kTK + lane] = pv;
-                if (lane == 0) {
-                    l_s[r] = l_s[r] * alpha + sum;
-                    m_s[r] = m_new;
-                    a_s[r] = alpha;
-                }
-            }
-        }
-        __syncthreads();
-        // P.V: thread -> dim d, rows r = rg + RG*i
-        {
-            const int blk = d >> 5, e = d & 31;
-#pragma unroll
-            for (int i = 0; i < MAXO; ++i) {
-                const int r = rg + RG * i;
-                if (r < R) o[i] *= a_s[r];
-            }
-            for (int key = 0; key < nk; ++key) {
-                const uint8_t* vb = vt + key * VSEG + blk * 24;
-                const float dsv = f16_value(*reinterpret_cast<const uint16_t*>(vb));
-                const float msv = f16_value(*reinterpret_cast<const uint16_t*>(vb + 2));
-                const uint32_t qh = *reinterpret_cast<const uint32_t*>(vb + 4);
-                const int nib = (vb[8 + (e & 15)] >> ((e >> 4) * 4)) & 15;
-                const int code = nib | (int)(((qh >> e) & 1u) << 4);
-                const float v = fmaf(dsv, (float)code, msv);
-#pragma unroll
-                for (int i = 0; i < MAXO; ++i) {
-                    const int r = rg + RG * i;
-                    if (r < R) o[i] = fmaf(sp[r * kTK + key], v, o[i]);
-                }
-            }
-        }
-        __syncthreads();
-    }
-    // partials
-    const size_t row0 = ((size_t)b * p.splits + s) * p.T;
-    for (int r = tid; r < R; r += 256) {
-        const int t = r / p.hpk, h = g * p.hpk + r % p.hpk;
-        const size_t idx = (row0 + t) * p.H + h;
-        p.part_ml[2 * idx] = m_s[r];
-        p.part_ml[2 * idx + 1] = l_s[r];
-    }
-#pragma unroll
-    for (int i = 0; i < MAXO; ++i) {
-        const int r = rg + RG * i;
-        if (r < R) {
-            const int t = r / p.hpk, h = g * p.hpk + r % p.hpk;
-            p.part_o[((row0 + t) * p.H + h) * HD + d] = o[i];
-        }
-    }
-}
+#include "kvq_decode.hip"
 
 // One 64-lane workgroup per (session, row t, Q head h): fold the session's
-// splits, adding the sink once as a value-less column.
+// split partials, adding the sink once as a value-less column.  The splits'
+// maxima and weights are read by all lanes in parallel; the weighted sums over
+// splits run with lanes on dims.
 __global__ __launch_bounds__(64) void combine_kernel(DecodeParams p) {
+    __shared__ float wts[kMaxSplits];
     const int idx = blockIdx.x;
     const int h = idx % p.H;
     const int t = (idx / p.H) % p.T;
     const int b = idx / (p.H * p.T);
+    const int lane = threadIdx.x;
     const int len = p.len_d[b];
     const int lo = p.window > 0 ? max(0, len - p.T + 1 - p.window) : 0;
     const int ns = min(p.splits, (len - lo + p.chunk - 1) / p.chunk);
     const size_t stride = (size_t)p.T * p.H;
     const size_t e0 = ((size_t)b * p.splits * p.T + t) * p.H + h;   // split 0 entry
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, p.part_ml[2 * (e0 + s * stride)]);
+    float m_loc = -INFINITY;
+    for (int s = lane; s < ns; s += 64) m_loc = fmaxf(m_loc, p.part_ml[2 * (e0 + s * stride)]);
+    float M = wave_max(m_loc);
     const bool has_sink = p.sinks != nullptr;
     const float sink = has_sink ? p.sinks[h] : 0.0f;
     if (has_sink) M = fmaxf(M, sink);
-    float Z = has_sink ? expf(sink - M) : 0.0f;
-    for (int s = 0; s < ns; ++s) {
+    float z = 0.0f;
+    for (int s = lane; s < ns; s += 64) {
         const float m = p.part_ml[2 * (e0 + s * stride)];
-        if (m != -INFINITY) Z += p.part_ml[2 * (e0 + s * stride) + 1] * expf(m - M);
+        const float w = (m == -INFINITY) ? 0.0f : expf(m - M);
+        wts[s] = w;
+        z = fmaf(w, p.part_ml[2 * (e0 + s * stride) + 1], z);
     }
+    const float Z = wave_sum(z) + (has_sink ? expf(sink - M) : 0.0f);
+    __syncthreads();
     const float invZ = 1.0f / Z;
-    for (int d = threadIdx.x; d < p.hd; d += 64) {
-        float acc = 0.0f;
-        for (int s = 0; s < ns; ++s) {
-            const float m = p.part_ml[2 * (e0 + s * stride)];
-            if (m != -INFINITY) acc += expf(m - M) * p.part_o[(e0 + s * stride) * p.hd + d];
+    for (int d = lane; d < p.hd; d += 64) {
+        const float* o = p.part_o + e0 * p.hd + d;
+        const size_t so = stride * p.hd;
+        float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+        int s = 0;
+        for (; s + 4 <= ns; s += 4) {
+            a0 = fmaf(wts[s], o[(size_t)s * so], a0);
+            a1 = fmaf(wts[s + 1], o[(size_t)(s + 1) * so], a1);
+            a2 = fmaf(wts[s + 2], o[(size_t)(s + 2) * so], a2);
+            a3 = fmaf(wts[s + 3], o[(size_t)(s + 3) * so], a3);
         }
-        p.out[(((size_t)b * p.T + t) * p.H + h) * p.hd + d] = acc * invZ;
+        for (; s < ns; ++s) a0 = fmaf(wts[s], o[(size_t)s * so], a0);
+        p.out[(((size_t)b * p.T + t) * p.H + h) * p.hd + d] = ((a0 + a1) + (a2 + a3)) * invZ;
     }
-    if (p.lse && threadIdx.x == 0) p.lse[((size_t)b * p.T + t) * p.H + h] = M + logf(Z);
+    if (p.lse && lane == 0) p.lse[((size_t)b * p.T + t) * p.H + h] = M + logf(Z);
 }
 
 // ---------------------------------------------------------------------------
@@ -419,26 +250,32 @@ int check(const char** err) {
     return 0;
 }
 
-template <int NB>
-int launch_decode_nb(const DecodeParams& p, hipStream_t st, const char** err) {
-    const int R = p.T * p.hpk;
-    const int lds = decode_lds_bytes<NB>(R);
-    static int configured = 0;
+template <int NB, int RT, bool QLO>
+int launch_decode_t(const DecodeParams& p, hipStream_t st, const char** err) {
+    constexpr int lds = dec::Layout<NB, RT>::BYTES;
+    static bool configured = false;
     if (!configured) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<NB>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                decode_lds_bytes<NB>(kMaxRows)) != hipSuccess) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&dec::decode_mfma<NB, RT, QLO>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess) {
             *err = "cannot raise the LDS limit of the decode kernel";
             return 1;
         }
-        configured = 1;
+        configured = true;
     }
     const int items = p.B * p.splits * p.Hkv;
     const int grid = (items + 7) & ~7;
-    hipLaunchKernelGGL(decode_kernel<NB>, dim3(grid), dim3(256), lds, st, p);
+    hipLaunchKernelGGL((dec::decode_mfma<NB, RT, QLO>), dim3(grid), dim3(256), lds, st, p);
     if (check(err)) return 1;
     hipLaunchKernelGGL(combine_kernel, dim3(p.B * p.T * p.H), dim3(64), 0, st, p);
     return check(err);
+}
+
+template <int NB>
+int launch_decode_nb(const DecodeParams& p, hipStream_t st, const char** err) {
+    const int R = p.T * p.hpk;
+    const bool qlo = p.dtype == 0;   // fp32 queries keep a low fp16 part
+    if (R <= 16) return qlo ? launch_decode_t<NB, 1, true>(p, st, err) : launch_decode_t<NB, 1, false>(p, st, err);
+    return qlo ? launch_decode_t<NB, 2, true>(p, st, err) : launch_decode_t<NB, 2, false>(p, st, err);
 }
 
 }  // namespace
@@ -458,11 +295,7 @@ int launch_move(const MoveParams& p, void* stream, const char** err) {
 
 int launch_append(const AppendParams& p, void* stream, const char** err) {
     const int64_t units = (int64_t)p.nsess * p.T * (p.Hkv * p.hd / 32);
-    const int64_t grid = (units * 32 + 255) / 256;
-    if (grid > INT32_MAX) {
-        *err = "append too large for one launch";
-        return 1;
-    }
+    const int64_t grid = std::min<int64_t>((units + 7) / 8, 1024);
     hipLaunchKernelGGL(append_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, p);
     return check(err);
 }

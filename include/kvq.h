@@ -158,7 +158,9 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache* h, int32_t T, size_t* byt
  * [n_seqs, T, n_q_heads, head_dim].  lse: device float [n_seqs, T, n_q_heads]
  * or NULL.  ws: device workspace of at least kvq_decode_workspace_bytes
  * bytes, 256-byte aligned.  The committed length is read from len_d on the
- * device.  Requires len >= T for every session and 1 <= T*H/Hkv <= 64.
+ * device.  Requires len >= T for every session and 1 <= T*H/Hkv <= 32.
+ * fp32 queries are used to about 2^-22 relative precision (fp16 hi + lo
+ * parts); bf16 queries exactly while |q| < 65504 and |q| >= 2^-14 (fp16 range).
  * Errors: EINVAL, ERANGE (a visible row was rebased away), EDEVICE. */
 kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T,
                       const float* sinks, float scale, float* out, float* lse,
@@ -174,8 +176,9 @@ kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T,
 kvq_status kvq_truncate(kvq_cache* h, const int32_t* new_len, kvq_stream stream);
 
 /* Tuning: rows per split-K chunk of kvq_decode (a positive multiple of 64),
- * or 0 to let each call choose.  The result does not depend on it beyond
- * float rounding.  Errors: EINVAL. */
+ * or 0 to let each call choose; a call raises it when a session would need
+ * more than 1024 chunks.  The result does not depend on it beyond float
+ * rounding.  Errors: EINVAL. */
 kvq_status kvq_set_split_rows(kvq_cache* h, int32_t rows);
 
 /* Copies the handle's configuration, sizes and buffer pointers. */

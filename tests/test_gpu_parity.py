@@ -136,9 +136,12 @@ def test_decode_split_invariance():
         p.gpu.set_split_rows(rows_)
         o, l = p.gpu.decode(qd, scale)
         outs.append((o.cpu().numpy(), l.cpu().numpy()))
+    # P enters the P.V product as fp16, rounded relative to each split's own
+    # running max (unit roundoff 2^-11): outputs agree to a few fp16 ulps of
+    # |v|; the row sums stay fp32, so the log-sum-exps agree to fp32 rounding.
     for o, l in outs[1:]:
-        np.testing.assert_allclose(o, outs[0][0], atol=2e-6, rtol=1e-5)
-        np.testing.assert_allclose(l, outs[0][1], atol=2e-6, rtol=1e-6)
+        np.testing.assert_allclose(o, outs[0][0], atol=5e-4, rtol=5e-4)
+        np.testing.assert_allclose(l, outs[0][1], atol=1e-5, rtol=1e-5)
     p.decode(q, scale)
 
 
