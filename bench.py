@@ -52,7 +52,25 @@ def parse():
     ap.add_argument("--split-rows", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES, 10 times "
+                         "(reference for scaling HBM traffic counters)")
     return ap.parse_args()
+
+
+def calibrate_copy(nbytes: int):
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    dt = (time.perf_counter() - t0) / 10
+    print(json.dumps({"calibrate_copy_bytes": nbytes, "read_bytes": nbytes, "write_bytes": nbytes,
+                      "ms": round(dt * 1e3, 4), "GBps_read_plus_write": round(2 * nbytes / dt / 1e9, 1)}))
 
 
 def build_layers(w, L, dev, split_rows):
@@ -200,6 +218,9 @@ def run_cpu_baseline(w, seconds):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this path has no "
               "multi-GPU mode", file=sys.stderr)
