@@ -107,7 +107,7 @@ __device__ __forceinline__ h8 v_codes_f16(uint32_t lo, uint32_t hi) {
 
 // bit k of the low 4 bits of x -> bit 4 of byte k
 __device__ __forceinline__ uint32_t fifth_bits(uint32_t x4) {
-    return ((x4 * 0x204081u) & 0x01010101u) << 4;
+    return (__umul24(x4, 0x204081u) & 0x01010101u) << 4;
 }
 
 __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
@@ -127,6 +127,81 @@ __device__ __forceinline__ void lds_order() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Raw blocks of one 32-row tile held in registers between the global loads
+// and the LDS stores (software prefetch of the next tile).  Unit u = (row,
+// block) with the block index fastest; lane handles units lane, lane+64, ...
+template <int NB>
+struct Raw {
+    static constexpr int U = (kTile * NB + 63) / 64;
+    uint32_t kw[U][8];     // aligned dwords from the code address rounded down
+    uint32_t kt[U];        // code bytes 30, 31 (needed when the codes start 2 bytes in)
+    uint32_t kh[U];        // scale bits | shift << 16
+    uint2 va[U], vn0[U], vn1[U];
+};
+
+template <int NB>
+__device__ __forceinline__ void stage_load(Raw<NB>& r, const uint8_t* kplane, const uint8_t* vplane,
+                                           int k_row, int v_row, int t0, int c1, int base, int lane) {
+#pragma unroll
+    for (int x = 0; x < Raw<NB>::U; ++x) {
+        const int u = x * 64 + lane;
+        if (kTile * NB % 64 == 0 || u < kTile * NB) {
+            const int key = u / NB, blk = u - key * NB;
+            const int64_t row = (int64_t)(min(t0 + key, c1 - 1) - base);
+            const uint8_t* kb = kplane + row * k_row + blk * 34;
+            const uint8_t* vb = vplane + row * v_row + blk * 24;
+            // K: scale at kb, codes at kb + 2 (2-byte aligned)
+            const uint32_t sh = (uint32_t)((reinterpret_cast<uintptr_t>(kb) + 2) & 3);
+            const uint32_t* kw = reinterpret_cast<const uint32_t*>(kb + 2 - sh);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) r.kw[x][i] = kw[i];
+            r.kt[x] = *reinterpret_cast<const uint16_t*>(kb + 32);
+            r.kh[x] = (uint32_t)*reinterpret_cast<const uint16_t*>(kb) | (sh << 16);
+            // V: [d16 | m16 << 16][fifth bits][16 nibble bytes], 8-byte aligned
+            r.va[x] = reinterpret_cast<const uint2*>(vb)[0];
+            r.vn0[x] = reinterpret_cast<const uint2*>(vb)[1];
+            r.vn1[x] = reinterpret_cast<const uint2*>(vb)[2];
+        }
+    }
+}
+
+template <int NB>
+__device__ __forceinline__ void stage_store(const Raw<NB>& r, uint8_t* Wb, int lane) {
+    using LY = Layout<NB, 1>;
+    float* ks = reinterpret_cast<float*>(Wb + LY::KS);
+    float* vd = reinterpret_cast<float*>(Wb + LY::VD);
+    uint16_t* vm = reinterpret_cast<uint16_t*>(Wb + LY::VM);
+#pragma unroll
+    for (int x = 0; x < Raw<NB>::U; ++x) {
+        const int u = x * 64 + lane;
+        if (kTile * NB % 64 == 0 || u < kTile * NB) {
+            const int key = u / NB, blk = u - key * NB;
+            const uint32_t sh = r.kh[x] >> 16;
+            uint32_t cd[8];
+#pragma unroll
+            for (int i = 0; i < 7; ++i) cd[i] = __builtin_amdgcn_alignbyte(r.kw[x][i + 1], r.kw[x][i], sh);
+            cd[7] = __builtin_amdgcn_alignbyte(r.kt[x], r.kw[x][7], sh);
+            uint4* kd = reinterpret_cast<uint4*>(Wb + LY::KC + key * LY::KROW + blk * 32);
+            kd[0] = (uint4){cd[0], cd[1], cd[2], cd[3]};
+            kd[1] = (uint4){cd[4], cd[5], cd[6], cd[7]};
+            ks[key * NB + blk] = f16_value((uint16_t)(r.kh[x] & 0xFFFF));
+            const uint32_t qh = r.va[x].y;
+            const uint32_t nib[4] = {r.vn0[x].x, r.vn0[x].y, r.vn1[x].x, r.vn1[x].y};
+            uint32_t vc[8];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                vc[t] = (nib[t] & 0x0F0F0F0Fu) | fifth_bits((qh >> (4 * t)) & 15u);
+                vc[4 + t] = ((nib[t] >> 4) & 0x0F0F0F0Fu) | fifth_bits((qh >> (16 + 4 * t)) & 15u);
+            }
+            uint4* vdst = reinterpret_cast<uint4*>(Wb + LY::VC + key * LY::VROW + blk * 32);
+            vdst[0] = (uint4){vc[0], vc[1], vc[2], vc[3]};
+            vdst[1] = (uint4){vc[4], vc[5], vc[6], vc[7]};
+            vd[key * NB + blk] = f16_value((uint16_t)(r.va[x].x & 0xFFFF));
+            vm[key * 16 + blk] = (uint16_t)(r.va[x].x >> 16);
+        }
+    }
 }
 
 template <int NB, int RT, bool QLO>
@@ -217,82 +292,47 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
     float* vd = reinterpret_cast<float*>(Wb + LY::VD);
     uint16_t* vm = reinterpret_cast<uint16_t*>(Wb + LY::VM);
 
+    Raw<NB> raw;
+    if (c0 + wave * kTile < c1)
+        stage_load<NB>(raw, kplane, vplane, p.k_row, p.v_row, c0 + wave * kTile, c1, base, lane);
     for (int t0 = c0 + wave * kTile; t0 < c1; t0 += kWaves * kTile) {
-        // ---- 1. stage the tile's K and V blocks (rows past c1 repeat row c1-1)
-#pragma unroll
-        for (int u0 = 0; u0 < kTile * NB; u0 += 64) {
-            const int u = u0 + lane;
-            if (kTile * NB % 64 == 0 || u < kTile * NB) {
-                const int key = u / NB, blk = u - key * NB;
-                const int64_t row = (int64_t)(min(t0 + key, c1 - 1) - base);
-                const uint8_t* kb = kplane + row * p.k_row + blk * 34;
-                const uint8_t* vb = vplane + row * p.v_row + blk * 24;
-                // K: scale at kb, codes at kb+2 (2-byte aligned): 8 aligned dwords
-                // from the aligned-down code address, the last 2 code bytes
-                // separately, funnel-shifted by 0 or 2 bytes.
-                const uint16_t ds16 = *reinterpret_cast<const uint16_t*>(kb);
-                const uintptr_t ca = reinterpret_cast<uintptr_t>(kb + 2);
-                const uint32_t* kw = reinterpret_cast<const uint32_t*>(ca & ~(uintptr_t)3);
-                const uint32_t sh = (uint32_t)(ca & 3);
-                uint32_t w[9];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) w[i] = kw[i];
-                w[8] = *reinterpret_cast<const uint16_t*>(kb + 32);
-                uint32_t cd[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) cd[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], sh);
-                uint4* kd = reinterpret_cast<uint4*>(Wb + LY::KC + key * LY::KROW + blk * 32);
-                kd[0] = (uint4){cd[0], cd[1], cd[2], cd[3]};
-                kd[1] = (uint4){cd[4], cd[5], cd[6], cd[7]};
-                ks[key * NB + blk] = f16_value(ds16);
-                // V: [d16 | m16 << 16][fifth bits][16 nibble bytes], 8-byte aligned
-                const uint2 va = reinterpret_cast<const uint2*>(vb)[0];
-                const uint2 vn0 = reinterpret_cast<const uint2*>(vb)[1];
-                const uint2 vn1 = reinterpret_cast<const uint2*>(vb)[2];
-                const uint32_t qh = va.y;
-                const uint32_t nib[4] = {vn0.x, vn0.y, vn1.x, vn1.y};
-                uint32_t vc[8];
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    vc[t] = (nib[t] & 0x0F0F0F0Fu) | fifth_bits((qh >> (4 * t)) & 15u);
-                    vc[4 + t] = ((nib[t] >> 4) & 0x0F0F0F0Fu) | fifth_bits((qh >> (16 + 4 * t)) & 15u);
-                }
-                uint4* vdst = reinterpret_cast<uint4*>(Wb + LY::VC + key * LY::VROW + blk * 32);
-                vdst[0] = (uint4){vc[0], vc[1], vc[2], vc[3]};
-                vdst[1] = (uint4){vc[4], vc[5], vc[6], vc[7]};
-                vd[key * NB + blk] = f16_value((uint16_t)(va.x & 0xFFFF));
-                vm[key * 16 + blk] = (uint16_t)(va.x >> 16);
-            }
-        }
+        // ---- 1. store the tile's prefetched blocks; prefetch the next tile
+        stage_store<NB>(raw, Wb, lane);
         lds_order();
+        if (t0 + kWaves * kTile < c1)
+            stage_load<NB>(raw, kplane, vplane, p.k_row, p.v_row, t0 + kWaves * kTile, c1, base, lane);
 
         // ---- 2. scores: sacc[rt][h][i] = S[r = rt*16 + 4*q4 + i][key = 16h + j16]
         f4 sacc[RT][2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int key = 16 * h + j16;
+        for (int rt = 0; rt < RT; ++rt) sacc[rt][0] = sacc[rt][1] = (f4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) sacc[rt][h] = (f4){0.f, 0.f, 0.f, 0.f};
+        for (int blk = 0; blk < NB; ++blk) {
+            h8 qa[RT], ql[RT];
 #pragma unroll
-            for (int blk = 0; blk < NB; ++blk) {
-                const uint2 raw = *reinterpret_cast<const uint2*>(Wb + LY::KC + key * LY::KROW + blk * 32 + 8 * q4);
-                const h8 kf = k_codes_f16(raw.x, raw.y);
+            for (int rt = 0; rt < RT; ++rt) {
+                qa[rt] = *reinterpret_cast<const h8*>(smem + LY::Q + ((rt * NB + blk) * 64 + lane) * 16);
+                if (QLO) ql[rt] = *reinterpret_cast<const h8*>(smem + LY::Q + LY::QFRAG + ((rt * NB + blk) * 64 + lane) * 16);
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int key = 16 * h + j16;
+                const uint2 kraw = *reinterpret_cast<const uint2*>(Wb + LY::KC + key * LY::KROW + blk * 32 + 8 * q4);
+                const h8 kf = k_codes_f16(kraw.x, kraw.y);
                 const float kscale = ks[key * NB + blk];
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
-                    const h8 qa = *reinterpret_cast<const h8*>(smem + LY::Q + ((rt * NB + blk) * 64 + lane) * 16);
-                    f4 d = mfma(qa, kf, (f4){0.f, 0.f, 0.f, 0.f});
-                    if (QLO) {
-                        const h8 ql = *reinterpret_cast<const h8*>(smem + LY::Q + LY::QFRAG + ((rt * NB + blk) * 64 + lane) * 16);
-                        d = mfma(ql, kf, d);
-                    }
+                    f4 d = mfma(qa[rt], kf, (f4){0.f, 0.f, 0.f, 0.f});
+                    if (QLO) d = mfma(ql[rt], kf, d);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) sacc[rt][h][i] = fmaf(kscale, d[i], sacc[rt][h][i]);
                 }
             }
         }
 
-        // ---- 3. online softmax (base 2)
+        // ---- 3. online softmax in base 2 against a reference max mref that
+        // only moves when a score exceeds it by more than 2^8 (then p <= 256,
+        // well inside fp16), so the accumulators are rarely rescaled.
         float pv[RT][2][4];
         float alpha[RT][4];
         bool rescale = false;
@@ -305,14 +345,15 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
                 const float s1 = (j1 >= vis_lo[rt][i] && j1 < vis_hi[rt][i]) ? sacc[rt][1][i] * sc2 : -INFINITY;
                 const float mt = row_max16(fmaxf(s0, s1));
                 const float mold = mrow[rt][i];
-                const float mnew = fmaxf(mold, mt);
+                const bool move = mt > mold + 8.0f;            // false when mt is -inf
+                const float mnew = move ? mt : mold;
                 float a = 1.0f, p0 = 0.0f, p1 = 0.0f;
                 if (mnew != -INFINITY) {
-                    a = __builtin_amdgcn_exp2f(mold - mnew);      // 0 when mold is -inf
+                    if (move) a = __builtin_amdgcn_exp2f(mold - mnew);   // 0 when mold is -inf
                     p0 = __builtin_amdgcn_exp2f(s0 - mnew);
                     p1 = __builtin_amdgcn_exp2f(s1 - mnew);
                 }
-                rescale |= (a != 1.0f);
+                rescale |= move;
                 alpha[rt][i] = a;
                 mrow[rt][i] = mnew;
                 lsum[rt][i] = fmaf(lsum[rt][i], a, p0 + p1);

@@ -127,9 +127,14 @@ Plan make_plan(const kvq_cache* h, int32_t T) {
     }
     int64_t chunk = h->split_rows;
     if (chunk <= 0) {
-        // aim at about 512 workgroups of (session, chunk, KV head)
-        chunk = round_up(ceil_div(std::max<int64_t>(total, 1) * c.n_kv_heads, 512), kvq::kSplitQuantum);
-        chunk = std::min<int64_t>(std::max<int64_t>(chunk, 256), 1 << 16);
+        // About 2048 workgroups of (session, chunk, KV head), i.e. several per
+        // CU so that the last round is a small fraction of the work, but at
+        // least 64 rows per query row so that the partials (R x (hd + 2)
+        // floats written and read back per chunk) stay within a few percent
+        // of the chunk's K/V bytes (R x (hd + 2) x 8 / (64 R x 1.8125 hd)).
+        const int64_t R = (int64_t)T * (c.n_q_heads / c.n_kv_heads);
+        chunk = round_up(ceil_div(std::max<int64_t>(total, 1) * c.n_kv_heads, 2048), kvq::kSplitQuantum);
+        chunk = std::min<int64_t>(std::max<int64_t>(chunk, std::max<int64_t>(256, 64 * R)), 1 << 16);
     }
     // at most kMaxSplits chunks per session
     chunk = std::max<int64_t>(chunk, round_up(ceil_div(maxvis, kvq::kMaxSplits), kvq::kSplitQuantum));

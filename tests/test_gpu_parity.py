@@ -213,8 +213,9 @@ def test_verify_rows_equal_sequential_single_rows():
     for t in range(T):
         s.append(k[:, N0 + t:N0 + t + 1], v[:, N0 + t:N0 + t + 1])
         o1, l1 = s.gpu.decode(to_dev(q[:, t:t + 1], "bf16"), 0.088)
-        np.testing.assert_allclose(o1.cpu().numpy()[:, 0], oa.cpu().numpy()[:, t], atol=1e-5, rtol=1e-5)
-        np.testing.assert_allclose(l1.cpu().numpy()[:, 0], la.cpu().numpy()[:, t], atol=1e-5, rtol=1e-6)
+        # equal up to the fp16 rounding of P (see test_decode_split_invariance)
+        np.testing.assert_allclose(o1.cpu().numpy()[:, 0], oa.cpu().numpy()[:, t], atol=5e-4, rtol=5e-4)
+        np.testing.assert_allclose(l1.cpu().numpy()[:, 0], la.cpu().numpy()[:, t], atol=1e-5, rtol=1e-5)
 
 
 def test_gqa_equals_repeated_heads():
@@ -228,7 +229,8 @@ def test_gqa_equals_repeated_heads():
     r.append(np.repeat(k, H // Hkv, axis=2), np.repeat(v, H // Hkv, axis=2))
     og, lg = g.gpu.decode(to_dev(q, "bf16"), 0.125)
     orr, lr = r.gpu.decode(to_dev(q, "bf16"), 0.125)
-    np.testing.assert_allclose(og.cpu().numpy(), orr.cpu().numpy(), atol=1e-5, rtol=1e-5)
+    np.testing.assert_allclose(og.cpu().numpy(), orr.cpu().numpy(), atol=5e-4, rtol=5e-4)   # fp16 P
+    np.testing.assert_allclose(lg.cpu().numpy(), lr.cpu().numpy(), atol=1e-5, rtol=1e-5)
     g.decode(q, 0.125, what="gqa")
 
 
