@@ -49,15 +49,15 @@ struct Layout {
     static constexpr int HD = NB * 32;
     static constexpr int KROW = NB * 32 + 16;    // padded row strides (bytes)
     static constexpr int VROW = NB * 32 + 16;
-    static constexpr int PROW = RT * 32;         // [key][RT*16] fp16
+    static constexpr int PROW = 32;              // P rows: [rt][key][16] fp16
     static constexpr int KC = 0;                                  // K codes [32][KROW]
     static constexpr int VC = KC + kTile * KROW;                  // V codes [32][VROW]
-    static constexpr int KS = VC + kTile * VROW;                  // K scales f32 [32][NB]
-    static constexpr int VD = KS + ((kTile * NB * 4 + 15) & ~15); // V steps  f32 [32][NB]
+    static constexpr int KS = VC + kTile * VROW;                  // K scales f32 [NB][32]
+    static constexpr int VD = KS + ((kTile * NB * 4 + 15) & ~15); // V steps  f32 [NB][32]
     static constexpr int VM = VD + ((kTile * NB * 4 + 15) & ~15); // V offsets f16 [32][16]
-    static constexpr int PU = VM + kTile * 32;                    // P  f16 [32][RT*16]
-    static constexpr int PP = PU + kTile * PROW;                  // P' f16 [32][RT*16]
-    static constexpr int WAVE = PP + kTile * PROW;
+    static constexpr int PU = VM + kTile * 32;                    // P  f16 [RT][32][16]
+    static constexpr int PP = PU + RT * kTile * PROW;             // P' f16 [RT][32][16]
+    static constexpr int WAVE = PP + RT * kTile * PROW;
     static constexpr int QFRAG = RT * NB * 64 * 16;               // Q fragments, fp16
     static constexpr int Q = kWaves * WAVE;
     static constexpr int ML = Q + 2 * QFRAG;                      // [wave][RT*16][2] f32
@@ -109,6 +109,12 @@ __device__ __forceinline__ h8 v_codes_f16(uint32_t lo, uint32_t hi) {
 __device__ __forceinline__ uint32_t fifth_bits(uint32_t x4) {
     return (__umul24(x4, 0x204081u) & 0x01010101u) << 4;
 }
+
+// LDS swizzles (32 banks of 4 bytes): a 16-lane group touches 32 distinct banks.
+// K code rows: 8-byte chunk c of row `key` lives at chunk c ^ ((key >> 3) & 1).
+__device__ __forceinline__ int kc_chunk(int key, int c) { return c ^ ((key >> 3) & 1); }
+// P rows (16 halves = four 8-byte chunks): chunk c of row `key` at c ^ ((key >> 2) & 3).
+__device__ __forceinline__ int p_chunk(int key, int c) { return c ^ ((key >> 2) & 3); }
 
 __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -184,9 +190,14 @@ __device__ __forceinline__ void stage_store(const Raw<NB>& r, uint8_t* Wb, int l
             for (int i = 0; i < 7; ++i) cd[i] = __builtin_amdgcn_alignbyte(r.kw[x][i + 1], r.kw[x][i], sh);
             cd[7] = __builtin_amdgcn_alignbyte(r.kt[x], r.kw[x][7], sh);
             uint4* kd = reinterpret_cast<uint4*>(Wb + LY::KC + key * LY::KROW + blk * 32);
-            kd[0] = (uint4){cd[0], cd[1], cd[2], cd[3]};
-            kd[1] = (uint4){cd[4], cd[5], cd[6], cd[7]};
-            ks[key * NB + blk] = f16_value((uint16_t)(r.kh[x] & 0xFFFF));
+            if (key & 8) {   // chunks 0<->1, 2<->3 (kc_chunk)
+                kd[0] = (uint4){cd[2], cd[3], cd[0], cd[1]};
+                kd[1] = (uint4){cd[6], cd[7], cd[4], cd[5]};
+            } else {
+                kd[0] = (uint4){cd[0], cd[1], cd[2], cd[3]};
+                kd[1] = (uint4){cd[4], cd[5], cd[6], cd[7]};
+            }
+            ks[blk * kTile + key] = f16_value((uint16_t)(r.kh[x] & 0xFFFF));
             const uint32_t qh = r.va[x].y;
             const uint32_t nib[4] = {r.vn0[x].x, r.vn0[x].y, r.vn1[x].x, r.vn1[x].y};
             uint32_t vc[8];
@@ -198,11 +209,163 @@ __device__ __forceinline__ void stage_store(const Raw<NB>& r, uint8_t* Wb, int l
             uint4* vdst = reinterpret_cast<uint4*>(Wb + LY::VC + key * LY::VROW + blk * 32);
             vdst[0] = (uint4){vc[0], vc[1], vc[2], vc[3]};
             vdst[1] = (uint4){vc[4], vc[5], vc[6], vc[7]};
-            vd[key * NB + blk] = f16_value((uint16_t)(r.va[x].x & 0xFFFF));
+            vd[blk * kTile + key] = f16_value((uint16_t)(r.va[x].x & 0xFFFF));
             vm[key * 16 + blk] = (uint16_t)(r.va[x].x >> 16);
         }
     }
 }
+
+// Per-wave state of the online softmax and the output accumulators.
+template <int NB, int RT>
+struct WaveState {
+    f4 oacc[RT][2 * NB];     // O[r][d]: r = rt*16 + 4*q4 + i, d = 16*dt + j16
+    f4 macc[RT];             // sum_key P[r][key] * m[key][blk], blk = j16
+    float mrow[RT][4];       // reference max (base 2) of rows r
+    float lsum[RT][4];       // this lane's share of the row sums
+    int vis_lo[RT][4], vis_hi[RT][4];
+};
+
+// One 32-row tile from the wave's LDS area: scores, online softmax, P V.
+template <int NB, int RT, bool QLO>
+__device__ __forceinline__ void tile_compute(WaveState<NB, RT>& ws, const uint8_t* smem, uint8_t* Wb,
+                                             int t0, float sc2, int lane) {
+    using LY = Layout<NB, RT>;
+    const int q4 = lane >> 4, j16 = lane & 15;
+    const float* ks = reinterpret_cast<const float*>(Wb + LY::KS);
+    const float* vd = reinterpret_cast<const float*>(Wb + LY::VD);
+
+    // ---- scores: sacc[rt][h][i] = S[r = rt*16 + 4*q4 + i][key = 16h + j16]
+    f4 sacc[RT][2];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) sacc[rt][0] = sacc[rt][1] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+        h8 qa[RT], ql[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            qa[rt] = *reinterpret_cast<const h8*>(smem + LY::Q + ((rt * NB + blk) * 64 + lane) * 16);
+            if (QLO) ql[rt] = *reinterpret_cast<const h8*>(smem + LY::Q + LY::QFRAG + ((rt * NB + blk) * 64 + lane) * 16);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int key = 16 * h + j16;
+            const uint2 kraw = *reinterpret_cast<const uint2*>(Wb + LY::KC + key * LY::KROW + blk * 32 +
+                                                               8 * kc_chunk(key, q4));
+            const h8 kf = k_codes_f16(kraw.x, kraw.y);
+            const float kscale = ks[blk * kTile + key];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                f4 d = mfma(qa[rt], kf, (f4){0.f, 0.f, 0.f, 0.f});
+                if (QLO) d = mfma(ql[rt], kf, d);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sacc[rt][h][i] = fmaf(kscale, d[i], sacc[rt][h][i]);
+            }
+        }
+    }
+
+    // ---- online softmax in base 2 against a reference max that only moves
+    // when a score exceeds it by more than 2^8 (then p <= 256, well inside
+    // fp16), so the accumulators are rarely rescaled.
+    float pv[RT][2][4];
+    float alpha[RT][4];
+    bool rescale = false;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j0 = t0 + j16, j1 = t0 + 16 + j16;
+            const float s0 = (j0 >= ws.vis_lo[rt][i] && j0 < ws.vis_hi[rt][i]) ? sacc[rt][0][i] * sc2 : -INFINITY;
+            const float s1 = (j1 >= ws.vis_lo[rt][i] && j1 < ws.vis_hi[rt][i]) ? sacc[rt][1][i] * sc2 : -INFINITY;
+            const float mt = row_max16(fmaxf(s0, s1));
+            const float mold = ws.mrow[rt][i];
+            const bool move = mt > mold + 8.0f;            // false when mt is -inf
+            const float mnew = move ? mt : mold;
+            float a = 1.0f, p0 = 0.0f, p1 = 0.0f;
+            if (mnew != -INFINITY) {
+                if (move) a = __builtin_amdgcn_exp2f(mold - mnew);   // 0 when mold is -inf
+                p0 = __builtin_amdgcn_exp2f(s0 - mnew);
+                p1 = __builtin_amdgcn_exp2f(s1 - mnew);
+            }
+            rescale |= move;
+            alpha[rt][i] = a;
+            ws.mrow[rt][i] = mnew;
+            ws.lsum[rt][i] = fmaf(ws.lsum[rt][i], a, p0 + p1);
+            pv[rt][0][i] = p0;
+            pv[rt][1][i] = p1;
+        }
+    if (__any(rescale)) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int dt = 0; dt < 2 * NB; ++dt) ws.oacc[rt][dt][i] *= alpha[rt][i];
+                ws.macc[rt][i] *= alpha[rt][i];
+            }
+    }
+    // P to LDS as [rt][key][16] fp16
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const h4 ph = {(_Float16)pv[rt][h][0], (_Float16)pv[rt][h][1], (_Float16)pv[rt][h][2],
+                           (_Float16)pv[rt][h][3]};
+            const int key = 16 * h + j16;
+            *reinterpret_cast<h4*>(Wb + LY::PU + (rt * kTile + key) * LY::PROW + 8 * p_chunk(key, q4)) = ph;
+        }
+
+    // ---- P V.  tr16 rows: keys 8*q4 + (j16>>2) (+4), columns r; lane j16 supplies chunk j16&3.
+    const int trow = 8 * q4 + (j16 >> 2);
+    const int tcol = 8 * (j16 & 3);                           // unswizzled (offset rows)
+    const int pcol0 = 8 * p_chunk(trow, j16 & 3);             // P rows trow
+    const int pcol1 = 8 * p_chunk(trow + 4, j16 & 3);         // P rows trow + 4
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int key = 16 * h + j16;
+            const float st = vd[blk * kTile + key];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const h4 ph = {(_Float16)(pv[rt][h][0] * st), (_Float16)(pv[rt][h][1] * st),
+                               (_Float16)(pv[rt][h][2] * st), (_Float16)(pv[rt][h][3] * st)};
+                *reinterpret_cast<h4*>(Wb + LY::PP + (rt * kTile + key) * LY::PROW + 8 * p_chunk(key, q4)) = ph;
+            }
+        }
+        lds_order();
+        h8 pa[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+            pa[rt] = tr16_pair(Wb + LY::PP + (rt * kTile + trow) * LY::PROW + pcol0,
+                               Wb + LY::PP + (rt * kTile + trow + 4) * LY::PROW + pcol1);
+#pragma unroll
+        for (int dd = 0; dd < 2; ++dd) {
+            const int d0 = blk * 32 + 16 * dd;
+            const i2 vb = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (lds_i2*)(Wb + LY::VC + (8 * q4 + (j16 >> 1)) * LY::VROW + d0 + 8 * (j16 & 1)));
+            const h8 vf = v_codes_f16((uint32_t)vb[0], (uint32_t)vb[1]);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) ws.oacc[rt][2 * blk + dd] = mfma(pa[rt], vf, ws.oacc[rt][2 * blk + dd]);
+        }
+        lds_order();   // the next block overwrites P'
+    }
+    // q5_1 offset term: macc[r][blk] += sum_key P[r][key] * m[key][blk]
+    {
+        const h8 mb = tr16_pair(Wb + LY::VM + trow * 32 + tcol, Wb + LY::VM + (trow + 4) * 32 + tcol);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const h8 pu = tr16_pair(Wb + LY::PU + (rt * kTile + trow) * LY::PROW + pcol0,
+                                    Wb + LY::PU + (rt * kTile + trow + 4) * LY::PROW + pcol1);
+            ws.macc[rt] = mfma(pu, mb, ws.macc[rt]);
+        }
+    }
+    lds_order();   // the next tile's staging overwrites this tile
+}
+
+// Tiles prefetched ahead of the one being computed: two, unless the register
+// file cannot hold them next to the accumulators (head_dim 256 with 32 rows).
+template <int NB, int RT>
+constexpr int prefetch_depth() { return NB * RT >= 12 ? 1 : 2; }
 
 template <int NB, int RT, bool QLO>
 __global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
@@ -210,6 +373,8 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
     constexpr int HD = LY::HD;
     constexpr int KSEG = NB * 34;
     constexpr int VSEG = NB * 24;
+    constexpr int NFRAG = RT * NB * 64;
+    constexpr int FPT = (NFRAG + 255) / 256;              // Q fragments per thread
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int q4 = lane >> 4, j16 = lane & 15;
@@ -223,219 +388,124 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
     const int s = (L / p.Hkv) % p.splits;
     const int b = L / (p.Hkv * p.splits);
     if (b >= p.B) return;
+    const int R = p.T * p.hpk;
+
+    // Q fragment (rt, blk) lane l: q[r = rt*16 + l%16][blk*32 + 8*(l/16) .. +7].
+    // Loaded first: they do not depend on the session length.
+    float qv[FPT][8];
+#pragma unroll
+    for (int x = 0; x < FPT; ++x) {
+        const int f = x * 256 + tid;
+        const int l = f & 63, fb = f >> 6;
+        const int blk = fb % NB, rt = fb / NB;
+        const int r = rt * 16 + (l & 15);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[x][e] = 0.0f;
+        if (f < NFRAG && r < R) {
+            const int t = r / p.hpk, hh = r % p.hpk;
+            const size_t i0 = (((size_t)b * p.T + t) * p.H + g * p.hpk + hh) * HD + blk * 32 + 8 * (l >> 4);
+            if (p.dtype == 1) {
+                const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + i0);
+                const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    qv[x][2 * e] = __uint_as_float(w4[e] << 16);
+                    qv[x][2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
+                }
+            } else {
+                const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(p.q) + i0);
+                const float4 c = *reinterpret_cast<const float4*>(static_cast<const float*>(p.q) + i0 + 4);
+                qv[x][0] = a.x; qv[x][1] = a.y; qv[x][2] = a.z; qv[x][3] = a.w;
+                qv[x][4] = c.x; qv[x][5] = c.y; qv[x][6] = c.z; qv[x][7] = c.w;
+            }
+        }
+    }
+
     const int len = p.len_d[b];
     const int base = p.base_d[b];
     const int lo_all = p.window > 0 ? max(0, len - p.T + 1 - p.window) : 0;
     const int c0 = lo_all + s * p.chunk;
     const int c1 = min(c0 + p.chunk, len);
     if (c0 >= c1) return;
-    const int R = p.T * p.hpk;
 
-    // Q fragments: fragment (rt, blk), lane l holds q[r = rt*16 + l%16][blk*32 + 8*(l/16) .. +7]
-    for (int f = tid; f < RT * NB * 64; f += 256) {
-        const int l = f & 63, fb = f >> 6;
-        const int blk = fb % NB, rt = fb / NB;
-        const int r = rt * 16 + (l & 15);
-        h8 hi = {}, lo = {};
-        if (r < R) {
-            const int t = r / p.hpk, hh = r % p.hpk;
-            const size_t i0 = (((size_t)b * p.T + t) * p.H + g * p.hpk + hh) * HD + blk * 32 + 8 * (l >> 4);
+    const uint8_t* kplane = p.k_planes + (int64_t)b * p.k_stride + (int64_t)g * KSEG;
+    const uint8_t* vplane = p.v_planes + (int64_t)b * p.v_stride + (int64_t)g * VSEG;
+    constexpr int kStride = kWaves * kTile;
+    constexpr int kDepth = prefetch_depth<NB, RT>();
+    // prefetch the wave's first kDepth tiles before anything waits on memory
+    // (row indices are clamped to c1 - 1, so every load is in bounds)
+    const int first = c0 + wave * kTile;
+    Raw<NB> raw[kDepth];
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i)
+        stage_load<NB>(raw[i], kplane, vplane, p.k_row, p.v_row, first + i * kStride, c1, base, lane);
+
+#pragma unroll
+    for (int x = 0; x < FPT; ++x) {
+        const int f = x * 256 + tid;
+        if (f < NFRAG) {
+            h8 hi, lo;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float x = load_in(p.q, p.dtype, i0 + e);
-                const _Float16 xh = (_Float16)x;
+                const _Float16 xh = (_Float16)qv[x][e];
                 hi[e] = xh;
-                if (QLO) lo[e] = (_Float16)(x - (float)xh);
+                lo[e] = (_Float16)(qv[x][e] - (float)xh);
             }
+            *reinterpret_cast<h8*>(smem + LY::Q + f * 16) = hi;
+            if (QLO) *reinterpret_cast<h8*>(smem + LY::Q + LY::QFRAG + f * 16) = lo;
         }
-        *reinterpret_cast<h8*>(smem + LY::Q + f * 16) = hi;
-        if (QLO) *reinterpret_cast<h8*>(smem + LY::Q + LY::QFRAG + f * 16) = lo;
     }
 
-    // visible range of this lane's score rows r = rt*16 + 4*q4 + i
-    int vis_lo[RT][4], vis_hi[RT][4];
+    WaveState<NB, RT> ws;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt) {
+        ws.macc[rt] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dt = 0; dt < 2 * NB; ++dt) ws.oacc[rt][dt] = (f4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            ws.mrow[rt][i] = -INFINITY;
+            ws.lsum[rt][i] = 0.0f;
             const int r = rt * 16 + 4 * q4 + i;
             int hi = 0, lo = 0;
             if (r < R) {
                 hi = len - p.T + r / p.hpk + 1;
                 lo = p.window > 0 ? max(0, hi - p.window) : 0;
             }
-            vis_lo[rt][i] = max(lo, c0);
-            vis_hi[rt][i] = min(hi, c1);
-        }
-
-    f4 oacc[RT][2 * NB];
-    f4 macc[RT];
-    float mrow[RT][4], lsum[RT][4];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        macc[rt] = (f4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int dt = 0; dt < 2 * NB; ++dt) oacc[rt][dt] = (f4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            mrow[rt][i] = -INFINITY;
-            lsum[rt][i] = 0.0f;
+            ws.vis_lo[rt][i] = max(lo, c0);
+            ws.vis_hi[rt][i] = min(hi, c1);
         }
     }
     const float sc2 = p.scale * kLog2e;
     __syncthreads();   // Q fragments are in LDS
 
-    const uint8_t* kplane = p.k_planes + (int64_t)b * p.k_stride + (int64_t)g * KSEG;
-    const uint8_t* vplane = p.v_planes + (int64_t)b * p.v_stride + (int64_t)g * VSEG;
     uint8_t* Wb = smem + wave * LY::WAVE;
-    float* ks = reinterpret_cast<float*>(Wb + LY::KS);
-    float* vd = reinterpret_cast<float*>(Wb + LY::VD);
-    uint16_t* vm = reinterpret_cast<uint16_t*>(Wb + LY::VM);
-
-    Raw<NB> raw;
-    if (c0 + wave * kTile < c1)
-        stage_load<NB>(raw, kplane, vplane, p.k_row, p.v_row, c0 + wave * kTile, c1, base, lane);
-    for (int t0 = c0 + wave * kTile; t0 < c1; t0 += kWaves * kTile) {
-        // ---- 1. store the tile's prefetched blocks; prefetch the next tile
-        stage_store<NB>(raw, Wb, lane);
-        lds_order();
-        if (t0 + kWaves * kTile < c1)
-            stage_load<NB>(raw, kplane, vplane, p.k_row, p.v_row, t0 + kWaves * kTile, c1, base, lane);
-
-        // ---- 2. scores: sacc[rt][h][i] = S[r = rt*16 + 4*q4 + i][key = 16h + j16]
-        f4 sacc[RT][2];
+    // kDepth-deep pipeline, unrolled so that the register buffers keep static
+    // indices, and branch-free inside so that the compiler's wait counts see
+    // the loads of every buffer in issue order: a tile past c1 (only in a
+    // session's last chunk) is computed fully masked and adds nothing.
+    for (int t0 = first; t0 < c1; t0 += kDepth * kStride) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) sacc[rt][0] = sacc[rt][1] = (f4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int blk = 0; blk < NB; ++blk) {
-            h8 qa[RT], ql[RT];
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                qa[rt] = *reinterpret_cast<const h8*>(smem + LY::Q + ((rt * NB + blk) * 64 + lane) * 16);
-                if (QLO) ql[rt] = *reinterpret_cast<const h8*>(smem + LY::Q + LY::QFRAG + ((rt * NB + blk) * 64 + lane) * 16);
-            }
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int key = 16 * h + j16;
-                const uint2 kraw = *reinterpret_cast<const uint2*>(Wb + LY::KC + key * LY::KROW + blk * 32 + 8 * q4);
-                const h8 kf = k_codes_f16(kraw.x, kraw.y);
-                const float kscale = ks[key * NB + blk];
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    f4 d = mfma(qa[rt], kf, (f4){0.f, 0.f, 0.f, 0.f});
-                    if (QLO) d = mfma(ql[rt], kf, d);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) sacc[rt][h][i] = fmaf(kscale, d[i], sacc[rt][h][i]);
-                }
-            }
-        }
-
-        // ---- 3. online softmax in base 2 against a reference max mref that
-        // only moves when a score exceeds it by more than 2^8 (then p <= 256,
-        // well inside fp16), so the accumulators are rarely rescaled.
-        float pv[RT][2][4];
-        float alpha[RT][4];
-        bool rescale = false;
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int j0 = t0 + j16, j1 = t0 + 16 + j16;
-                const float s0 = (j0 >= vis_lo[rt][i] && j0 < vis_hi[rt][i]) ? sacc[rt][0][i] * sc2 : -INFINITY;
-                const float s1 = (j1 >= vis_lo[rt][i] && j1 < vis_hi[rt][i]) ? sacc[rt][1][i] * sc2 : -INFINITY;
-                const float mt = row_max16(fmaxf(s0, s1));
-                const float mold = mrow[rt][i];
-                const bool move = mt > mold + 8.0f;            // false when mt is -inf
-                const float mnew = move ? mt : mold;
-                float a = 1.0f, p0 = 0.0f, p1 = 0.0f;
-                if (mnew != -INFINITY) {
-                    if (move) a = __builtin_amdgcn_exp2f(mold - mnew);   // 0 when mold is -inf
-                    p0 = __builtin_amdgcn_exp2f(s0 - mnew);
-                    p1 = __builtin_amdgcn_exp2f(s1 - mnew);
-                }
-                rescale |= move;
-                alpha[rt][i] = a;
-                mrow[rt][i] = mnew;
-                lsum[rt][i] = fmaf(lsum[rt][i], a, p0 + p1);
-                pv[rt][0][i] = p0;
-                pv[rt][1][i] = p1;
-            }
-        if (__any(rescale)) {
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-#pragma unroll
-                    for (int dt = 0; dt < 2 * NB; ++dt) oacc[rt][dt][i] *= alpha[rt][i];
-                    macc[rt][i] *= alpha[rt][i];
-                }
-        }
-        // P to LDS as [key][r] fp16
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                const h4 ph = {(_Float16)pv[rt][h][0], (_Float16)pv[rt][h][1], (_Float16)pv[rt][h][2],
-                               (_Float16)pv[rt][h][3]};
-                *reinterpret_cast<h4*>(Wb + LY::PU + (16 * h + j16) * LY::PROW + rt * 32 + 8 * q4) = ph;
-            }
-
-        // ---- 4. P V.  tr16 rows: keys 8*q4 + (j16>>2) (+4), columns r; lane j16 supplies chunk j16&3.
-        const int trow = 8 * q4 + (j16 >> 2);
-        const int tcol = 8 * (j16 & 3);
-#pragma unroll
-        for (int blk = 0; blk < NB; ++blk) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const float st = vd[(16 * h + j16) * NB + blk];
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    const h4 ph = {(_Float16)(pv[rt][h][0] * st), (_Float16)(pv[rt][h][1] * st),
-                                   (_Float16)(pv[rt][h][2] * st), (_Float16)(pv[rt][h][3] * st)};
-                    *reinterpret_cast<h4*>(Wb + LY::PP + (16 * h + j16) * LY::PROW + rt * 32 + 8 * q4) = ph;
-                }
-            }
+        for (int i = 0; i < kDepth; ++i) {
+            const int tt = t0 + i * kStride;
+            stage_store<NB>(raw[i], Wb, lane);
             lds_order();
-            h8 pa[RT];
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                pa[rt] = tr16_pair(Wb + LY::PP + trow * LY::PROW + rt * 32 + tcol,
-                                   Wb + LY::PP + (trow + 4) * LY::PROW + rt * 32 + tcol);
-#pragma unroll
-            for (int dd = 0; dd < 2; ++dd) {
-                const int d0 = blk * 32 + 16 * dd;
-                const i2 vb = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (lds_i2*)(Wb + LY::VC + (8 * q4 + (j16 >> 1)) * LY::VROW + d0 + 8 * (j16 & 1)));
-                const h8 vf = v_codes_f16((uint32_t)vb[0], (uint32_t)vb[1]);
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) oacc[rt][2 * blk + dd] = mfma(pa[rt], vf, oacc[rt][2 * blk + dd]);
-            }
-            lds_order();   // the next block overwrites P'
+            stage_load<NB>(raw[i], kplane, vplane, p.k_row, p.v_row, tt + kDepth * kStride, c1, base, lane);
+            tile_compute<NB, RT, QLO>(ws, smem, Wb, tt, sc2, lane);
         }
-        // q5_1 offset term: macc[r][blk] += sum_key P[r][key] * m[key][blk]
-        {
-            const h8 mb = tr16_pair(Wb + LY::VM + trow * 32 + tcol, Wb + LY::VM + (trow + 4) * 32 + tcol);
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                const h8 pu = tr16_pair(Wb + LY::PU + trow * LY::PROW + rt * 32 + tcol,
-                                        Wb + LY::PU + (trow + 4) * LY::PROW + rt * 32 + tcol);
-                macc[rt] = mfma(pu, mb, macc[rt]);
-            }
-        }
-        lds_order();   // the next tile's staging overwrites this tile
     }
 
     // ---- finish the wave: full row sums, fold the offset term into O
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lsum[rt][i] = row_sum16(lsum[rt][i]);
+        for (int i = 0; i < 4; ++i) ws.lsum[rt][i] = row_sum16(ws.lsum[rt][i]);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int dt = 0; dt < 2 * NB; ++dt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) oacc[rt][dt][i] += __shfl(macc[rt][i], 16 * q4 + dt / 2);
+            for (int i = 0; i < 4; ++i) ws.oacc[rt][dt][i] += __shfl(ws.macc[rt][i], 16 * q4 + dt / 2);
 
     // ---- merge the four waves in a fixed order
     float* ml = reinterpret_cast<float*>(smem + LY::ML);
@@ -445,8 +515,8 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = rt * 16 + 4 * q4 + i;
-                ml[(wave * RT * 16 + r) * 2] = mrow[rt][i];
-                ml[(wave * RT * 16 + r) * 2 + 1] = lsum[rt][i];
+                ml[(wave * RT * 16 + r) * 2] = ws.mrow[rt][i];
+                ml[(wave * RT * 16 + r) * 2 + 1] = ws.lsum[rt][i];
             }
     }
     __syncthreads();   // all waves are past their tiles; the wave areas become the merge buffer
@@ -459,7 +529,7 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
             float M = -INFINITY;
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml[(w * RT * 16 + r) * 2]);
-            fac[rt][i] = (mrow[rt][i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mrow[rt][i] - M);
+            fac[rt][i] = (ws.mrow[rt][i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ws.mrow[rt][i] - M);
         }
     float* obuf = reinterpret_cast<float*>(smem);
     for (int w = 0; w < kWaves; ++w) {
@@ -472,7 +542,7 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
                     for (int i = 0; i < 4; ++i) {
                         const int r = rt * 16 + 4 * q4 + i;
                         float* o = obuf + r * HD + 16 * dt + j16;
-                        const float v = oacc[rt][dt][i] * fac[rt][i];
+                        const float v = ws.oacc[rt][dt][i] * fac[rt][i];
                         *o = (w == 0) ? v : *o + v;
                     }
         }

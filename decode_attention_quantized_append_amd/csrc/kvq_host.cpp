@@ -135,6 +135,7 @@ Plan make_plan(const kvq_cache* h, int32_t T) {
         const int64_t R = (int64_t)T * (c.n_q_heads / c.n_kv_heads);
         chunk = round_up(ceil_div(std::max<int64_t>(total, 1) * c.n_kv_heads, 2048), kvq::kSplitQuantum);
         chunk = std::min<int64_t>(std::max<int64_t>(chunk, std::max<int64_t>(256, 64 * R)), 1 << 16);
+        chunk = round_up(chunk, 256);   // whole rounds of 4 waves x 32 rows x 2 prefetched tiles
     }
     // at most kMaxSplits chunks per session
     chunk = std::max<int64_t>(chunk, round_up(ceil_div(maxvis, kvq::kMaxSplits), kvq::kSplitQuantum));
