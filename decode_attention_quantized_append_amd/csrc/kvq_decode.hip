@@ -107,7 +107,9 @@ __device__ __forceinline__ h8 v_codes_f16(uint32_t lo, uint32_t hi) {
 
 // bit k of the low 4 bits of x -> bit 4 of byte k
 __device__ __forceinline__ uint32_t fifth_bits(uint32_t x4) {
-    return (__umul24(x4, 0x204081u) & 0x01010101u) << 4;
+    uint32_t m;
+    asm("v_mul_u32_u24 %0, %1, %2" : "=v"(m) : "v"(x4), "s"(0x204081u));
+    return (m & 0x01010101u) << 4;
 }
 
 // LDS swizzles (32 banks of 4 bytes): a 16-lane group touches 32 distinct banks.
@@ -174,7 +176,7 @@ __device__ __forceinline__ void stage_load(Raw<NB>& r, const uint8_t* kplane, co
 }
 
 template <int NB>
-__device__ __forceinline__ void stage_store(const Raw<NB>& r, uint8_t* Wb, int lane) {
+__device__ __forceinline__ void stage_store(const Raw<NB>& r, uint8_t* Wb, int lane, float sc2) {
     using LY = Layout<NB, 1>;
     float* ks = reinterpret_cast<float*>(Wb + LY::KS);
     float* vd = reinterpret_cast<float*>(Wb + LY::VD);
@@ -197,7 +199,7 @@ __device__ __forceinline__ void stage_store(const Raw<NB>& r, uint8_t* Wb, int l
                 kd[0] = (uint4){cd[0], cd[1], cd[2], cd[3]};
                 kd[1] = (uint4){cd[4], cd[5], cd[6], cd[7]};
             }
-            ks[blk * kTile + key] = f16_value((uint16_t)(r.kh[x] & 0xFFFF));
+            ks[blk * kTile + key] = f16_value((uint16_t)(r.kh[x] & 0xFFFF)) * sc2;   // scale * log2(e) folded in
             const uint32_t qh = r.va[x].y;
             const uint32_t nib[4] = {r.vn0[x].x, r.vn0[x].y, r.vn1[x].x, r.vn1[x].y};
             uint32_t vc[8];
@@ -223,6 +225,7 @@ struct WaveState {
     float mrow[RT][4];       // reference max (base 2) of rows r
     float lsum[RT][4];       // this lane's share of the row sums
     int vis_lo[RT][4], vis_hi[RT][4];
+    int full_lo, full_hi;    // every row sees all of [full_lo, full_hi)
 };
 
 // One 32-row tile from the wave's LDS area: scores, online softmax, P V.
@@ -263,37 +266,41 @@ __device__ __forceinline__ void tile_compute(WaveState<NB, RT>& ws, const uint8_
         }
     }
 
-    // ---- online softmax in base 2 against a reference max that only moves
-    // when a score exceeds it by more than 2^8 (then p <= 256, well inside
-    // fp16), so the accumulators are rarely rescaled.
-    float pv[RT][2][4];
-    float alpha[RT][4];
-    bool rescale = false;
+    // ---- online softmax in base 2 against a reference max mrow that only
+    // moves when a score exceeds it by more than 8 (so p = 2^(s - mrow) <= 256,
+    // well inside fp16).  The common case needs no row maximum: one compare
+    // per score and a wave vote; only when some score passes its row's
+    // threshold are the row maxima taken and the accumulators rescaled.
+    float sv[RT][2][4];
+    const bool interior = t0 >= ws.full_lo && t0 + kTile <= ws.full_hi;   // no score masked
+    bool over = false;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int j0 = t0 + j16, j1 = t0 + 16 + j16;
-            const float s0 = (j0 >= ws.vis_lo[rt][i] && j0 < ws.vis_hi[rt][i]) ? sacc[rt][0][i] * sc2 : -INFINITY;
-            const float s1 = (j1 >= ws.vis_lo[rt][i] && j1 < ws.vis_hi[rt][i]) ? sacc[rt][1][i] * sc2 : -INFINITY;
-            const float mt = row_max16(fmaxf(s0, s1));
-            const float mold = ws.mrow[rt][i];
-            const bool move = mt > mold + 8.0f;            // false when mt is -inf
-            const float mnew = move ? mt : mold;
-            float a = 1.0f, p0 = 0.0f, p1 = 0.0f;
-            if (mnew != -INFINITY) {
-                if (move) a = __builtin_amdgcn_exp2f(mold - mnew);   // 0 when mold is -inf
-                p0 = __builtin_amdgcn_exp2f(s0 - mnew);
-                p1 = __builtin_amdgcn_exp2f(s1 - mnew);
+            float s0 = sacc[rt][0][i], s1 = sacc[rt][1][i];
+            if (!interior) {
+                const int j0 = t0 + j16, j1 = t0 + 16 + j16;
+                s0 = (j0 >= ws.vis_lo[rt][i] && j0 < ws.vis_hi[rt][i]) ? s0 : -INFINITY;
+                s1 = (j1 >= ws.vis_lo[rt][i] && j1 < ws.vis_hi[rt][i]) ? s1 : -INFINITY;
             }
-            rescale |= move;
-            alpha[rt][i] = a;
-            ws.mrow[rt][i] = mnew;
-            ws.lsum[rt][i] = fmaf(ws.lsum[rt][i], a, p0 + p1);
-            pv[rt][0][i] = p0;
-            pv[rt][1][i] = p1;
+            sv[rt][0][i] = s0;
+            sv[rt][1][i] = s1;
+            over |= fmaxf(s0, s1) > ws.mrow[rt][i] + 8.0f;      // -inf never passes
         }
-    if (__any(rescale)) {
+    if (__any(over)) {
+        float alpha[RT][4];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float mt = row_max16(fmaxf(sv[rt][0][i], sv[rt][1][i]));
+                const float mold = ws.mrow[rt][i];
+                const bool move = mt > mold + 8.0f;
+                alpha[rt][i] = move ? __builtin_amdgcn_exp2f(mold - mt) : 1.0f;   // 0 when mold is -inf
+                ws.mrow[rt][i] = move ? mt : mold;
+                ws.lsum[rt][i] *= alpha[rt][i];
+            }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -303,6 +310,19 @@ __device__ __forceinline__ void tile_compute(WaveState<NB, RT>& ws, const uint8_
                 ws.macc[rt][i] *= alpha[rt][i];
             }
     }
+    float pv[RT][2][4];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float m = ws.mrow[rt][i];
+            // rows that have seen nothing yet (m = -inf) give p = 0
+            const float p0 = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sv[rt][0][i] - m);
+            const float p1 = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sv[rt][1][i] - m);
+            ws.lsum[rt][i] += p0 + p1;
+            pv[rt][0][i] = p0;
+            pv[rt][1][i] = p1;
+        }
     // P to LDS as [rt][key][16] fp16
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -367,8 +387,13 @@ __device__ __forceinline__ void tile_compute(WaveState<NB, RT>& ws, const uint8_
 template <int NB, int RT>
 constexpr int prefetch_depth() { return NB * RT >= 12 ? 1 : 2; }
 
+// Workgroups per CU the register allocation targets: two (two waves per SIMD)
+// where the accumulators and the prefetch buffers fit in 256 registers.
+template <int NB, int RT>
+constexpr int min_blocks() { return NB * RT <= 4 ? 2 : 1; }
+
 template <int NB, int RT, bool QLO>
-__global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
+__global__ __launch_bounds__(256, (min_blocks<NB, RT>())) void decode_mfma(DecodeParams p) {
     using LY = Layout<NB, RT>;
     constexpr int HD = LY::HD;
     constexpr int KSEG = NB * 34;
@@ -476,6 +501,9 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
             ws.vis_hi[rt][i] = min(hi, c1);
         }
     }
+    // rows' visible ranges are nested by t; the intersection over real rows
+    ws.full_hi = min(len - p.T + 1, c1);
+    ws.full_lo = max(p.window > 0 ? max(0, len - p.window) : 0, c0);
     const float sc2 = p.scale * kLog2e;
     __syncthreads();   // Q fragments are in LDS
 
@@ -488,7 +516,7 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
 #pragma unroll
         for (int i = 0; i < kDepth; ++i) {
             const int tt = t0 + i * kStride;
-            stage_store<NB>(raw[i], Wb, lane);
+            stage_store<NB>(raw[i], Wb, lane, sc2);
             lds_order();
             stage_load<NB>(raw[i], kplane, vplane, p.k_row, p.v_row, tt + kDepth * kStride, c1, base, lane);
             tile_compute<NB, RT, QLO>(ws, smem, Wb, tt, sc2, lane);
