@@ -15,7 +15,9 @@ Prints ONE JSON line.  ``value`` is the effective KV read bandwidth of the
 whole step (algorithmic K+V bytes the decode must read / wall time per step).
 ``roofline`` reports the decode call (decode kernel + combine kernel), timed
 with HIP events on the stream the library launches on, against the 8 TB/s HBM
-peak.  ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+peak; its ``traffic`` is the HBM bytes per decode call that the committed
+rocprofv3 counter passes measured (profiles/decode_traffic.json), reported only
+while the kernel sources still hash to the measured state.  ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
 workload.
 """
 from __future__ import annotations
@@ -33,6 +35,34 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 METRIC = "decode attn effective KV GB/s (% of HBM peak) + steps/s; append tokens/s"
 MALL_BYTES = 256 << 20
+
+
+def source_hash() -> str:
+    """sha256 (first 16 hex) over the kernel and host-library sources, in name order."""
+    import hashlib
+    d = os.path.join(ROOT, "decode_attention_quantized_append_amd", "csrc")
+    h = hashlib.sha256()
+    for n in sorted(os.listdir(d)):
+        if n.endswith((".hip", ".cpp", ".h")):
+            h.update(n.encode())
+            with open(os.path.join(d, n), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode call (decode + combine kernels) from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE passes, scaled by the copy calibration;
+    None when the sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash() or workload not in t.get("workloads", {}):
+        return None
+    return round(t["workloads"][workload]["call_bytes"])
 
 
 def default_layers(w) -> int:
@@ -246,7 +276,9 @@ def main():
         "decode_call_ms": {"mean": round(r["dec_ms"], 5), "p10": round(r["dec_p10"], 5),
                            "p90": round(r["dec_p90"], 5)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(w.name), "traffic_unit": "bytes per decode call",
+                     "algorithmic": r["kv_bytes"],
                      "kernel": "kvq_decode call (decode_kernel + combine_kernel), HIP events"},
     }
     if not args.no_cpu_baseline:
