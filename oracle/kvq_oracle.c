@@ -16,12 +16,15 @@
  *                          half-even ties; the round-trip error bound.
  *                          Parity with another implementation's bytes is
  *                          unpinned: the pages print no encoded block.
- *   kvqo_attention         a second, independent numpy route (own decoder,
- *                          own softmax); textbook attention when the codec
- *                          is exact; sink == value-less column; window ==
- *                          masked full row; T causal rows == T sequential
- *                          single-row calls; GQA == repeated KV heads;
- *                          closed forms at len 1 and q = 0.
+ *   kvqo_attention         textbook attention (torch's fp64
+ *                          scaled_dot_product_attention with repeated KV
+ *                          heads and explicit masks) on K/V rows the codec
+ *                          stores exactly, with a sink written as one extra
+ *                          key whose value row is zero; closed forms at
+ *                          len 1 and q = 0; window == masked full row;
+ *                          T causal rows == T sequential single-row calls;
+ *                          GQA == repeated KV heads; ring == flat cache;
+ *                          truncate == fresh cache of the kept prefix.
  */
 #include "kvq_oracle.h"
 
