@@ -151,13 +151,13 @@ struct Raw {
 
 template <int NB>
 __device__ __forceinline__ void stage_load(Raw<NB>& r, const uint8_t* kplane, const uint8_t* vplane,
-                                           int k_row, int v_row, int t0, int c1, int base, int lane) {
+                                           int k_row, int v_row, int t0, int lo, int c1, int base, int lane) {
 #pragma unroll
     for (int x = 0; x < Raw<NB>::U; ++x) {
         const int u = x * 64 + lane;
         if (kTile * NB % 64 == 0 || u < kTile * NB) {
             const int key = u / NB, blk = u - key * NB;
-            const int64_t row = (int64_t)(min(t0 + key, c1 - 1) - base);
+            const int64_t row = (int64_t)(min(max(t0 + key, lo), c1 - 1) - base);
             const uint8_t* kb = kplane + row * k_row + blk * 34;
             const uint8_t* vb = vplane + row * v_row + blk * 24;
             // K: scale at kb, codes at kb + 2 (2-byte aligned)
@@ -449,7 +449,7 @@ __global__ __launch_bounds__(256, (min_blocks<NB, RT>())) void decode_mfma(Decod
     const int len = p.len_d[b];
     const int base = p.base_d[b];
     const int lo_all = p.window > 0 ? max(0, len - p.T + 1 - p.window) : 0;
-    const int c0 = lo_all + s * p.chunk;
+    const int c0 = (lo_all & ~31) + s * p.chunk;   // chunks start on a 32-row boundary
     const int c1 = min(c0 + p.chunk, len);
     if (c0 >= c1) return;
 
@@ -458,12 +458,13 @@ __global__ __launch_bounds__(256, (min_blocks<NB, RT>())) void decode_mfma(Decod
     constexpr int kStride = kWaves * kTile;
     constexpr int kDepth = prefetch_depth<NB, RT>();
     // prefetch the wave's first kDepth tiles before anything waits on memory
-    // (row indices are clamped to c1 - 1, so every load is in bounds)
+    // (row indices are clamped to [lo_all, c1 - 1], so every load reads a
+    // resident row)
     const int first = c0 + wave * kTile;
     Raw<NB> raw[kDepth];
 #pragma unroll
     for (int i = 0; i < kDepth; ++i)
-        stage_load<NB>(raw[i], kplane, vplane, p.k_row, p.v_row, first + i * kStride, c1, base, lane);
+        stage_load<NB>(raw[i], kplane, vplane, p.k_row, p.v_row, first + i * kStride, lo_all, c1, base, lane);
 
 #pragma unroll
     for (int x = 0; x < FPT; ++x) {
@@ -518,7 +519,7 @@ __global__ __launch_bounds__(256, (min_blocks<NB, RT>())) void decode_mfma(Decod
             const int tt = t0 + i * kStride;
             stage_store<NB>(raw[i], Wb, lane, sc2);
             lds_order();
-            stage_load<NB>(raw[i], kplane, vplane, p.k_row, p.v_row, tt + kDepth * kStride, c1, base, lane);
+            stage_load<NB>(raw[i], kplane, vplane, p.k_row, p.v_row, tt + kDepth * kStride, lo_all, c1, base, lane);
             tile_compute<NB, RT, QLO>(ws, smem, Wb, tt, sc2, lane);
         }
     }

@@ -32,6 +32,9 @@ struct kvq_cache {
     std::vector<int64_t> len;    // host mirror of len_d
     std::vector<int64_t> base;   // host mirror of base_d
     int32_t split_rows;
+    int32_t head_group;          // decode tiling: 0 automatic, -1 one KV head per workgroup,
+                                 // k > 0 whole-row kernel with k heads per workgroup
+    int32_t sub_tiles;           // whole-row kernel: rows per buffer / 32 (0 automatic)
 };
 
 namespace {
@@ -113,33 +116,112 @@ int64_t visible_lo(const kvq_cache* h, int64_t len, int32_t T) {
 struct Plan {
     int32_t chunk;
     int32_t splits;
+    int32_t gh;        // 0: one KV head per workgroup; > 0: whole-row kernel
+    int32_t sub;
+    kvq::RowGeo geo;
     size_t ml_bytes;
     size_t o_bytes;
 };
 
+// Is the whole-row kernel built for gh heads per workgroup and buffers of
+// 32*sub rows at this shape?  (gh divides Hkv; the group's K row segment is a
+// whole number of 16-byte pieces; at most 8 waves; the loads of a buffer fit
+// the kernel's per-wave slots; two buffers and the head areas fit in LDS.)
+bool rows_ok(const kvq_config& c, int R, int gh, int sub, kvq::RowGeo* geo) {
+    const int NB = c.head_dim / 32;
+    if (NB != 2 && NB != 4 && NB != 8) return false;
+    if (gh < 1 || c.n_kv_heads % gh != 0 || (gh * NB) % 8 != 0) return false;
+    if (sub != 1 && sub != 2 && sub != 4) return false;
+    const int RT = (R + 15) / 16;
+    const int nw = gh * RT;
+    if (nw > 8) return false;
+    kvq::RowGeo g = kvq::row_geo(gh, NB, sub);
+    if ((g.NKI + g.NVI + nw - 1) / nw > kvq::kRowMaxSlots || g.lds > kvq::kLdsBytes) return false;
+    if (geo) *geo = g;
+    return true;
+}
+
+// Is every session's first visible row, rounded down to 32, still resident?
+bool aligned_start_resident(const kvq_cache* h, int32_t T) {
+    for (int b = 0; b < h->cfg.n_seqs; ++b)
+        if ((visible_lo(h, h->len[b], T) & ~int64_t(31)) < h->base[b]) return false;
+    return true;
+}
+
+// Rows each session's chunks cover: from the first visible row rounded down
+// to 32 up to len.
+int64_t span_of(const kvq_cache* h, int b, int32_t T) {
+    return std::max<int64_t>(0, h->len[b] - (visible_lo(h, h->len[b], T) & ~int64_t(31)));
+}
+
 Plan make_plan(const kvq_cache* h, int32_t T) {
     const kvq_config& c = h->cfg;
+    const int R = T * (c.n_q_heads / c.n_kv_heads);
     int64_t total = 0, maxvis = 1;
     for (int b = 0; b < c.n_seqs; ++b) {
-        int64_t vis = std::max<int64_t>(0, h->len[b] - visible_lo(h, h->len[b], T));
+        const int64_t vis = span_of(h, b, T);
         total += vis;
         maxvis = std::max(maxvis, vis);
     }
+    Plan p{};
+    // kernel and tiling.  The whole-row kernel starts a session's first buffer
+    // at the first visible row rounded down to 32 and reads it whole, so that
+    // row must still be resident (at or above base).
+    if (!aligned_start_resident(h, T)) {
+        // one KV head per workgroup: its loads clamp rows to the visible range
+    } else if (h->head_group > 0) {
+        const int sub = h->sub_tiles > 0 ? h->sub_tiles : 1;
+        if (rows_ok(c, R, h->head_group, sub, &p.geo)) {
+            p.gh = h->head_group;
+            p.sub = sub;
+        }
+    } else if (h->head_group == 0 && R > 16) {
+        // whole-row workgroups where the group has two row tiles (verify
+        // rows); one KV head per workgroup is faster below that.  The largest
+        // head group whose buffers carry >= 48 KB (the load in flight per
+        // workgroup while the other buffer is computed)
+        for (int gh = std::min(c.n_kv_heads, 8); gh >= 1 && p.gh == 0; --gh)
+            for (int sub : {1, 2, 4}) {
+                kvq::RowGeo g;
+                if (h->sub_tiles > 0 && sub != h->sub_tiles) continue;
+                if (!rows_ok(c, R, gh, sub, &g)) continue;
+                if (g.RAWB < 48 * 1024 && sub < 4 && rows_ok(c, R, gh, sub * 2, nullptr)) continue;
+                p.gh = gh;
+                p.sub = sub;
+                p.geo = g;
+                break;
+            }
+    }
     int64_t chunk = h->split_rows;
-    if (chunk <= 0) {
+    if (p.gh > 0) {
+        if (chunk <= 0) {
+            // one round of workgroups: as many as fit on the 256 CUs at once
+            // (LDS-bound), each a whole number of buffers
+            const int64_t ngrp = c.n_kv_heads / p.gh;
+            const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kvq::kLdsBytes / p.geo.lds,
+                                                                           8 / (p.gh * ((R + 15) / 16))));
+            const int64_t slots = 256 * per_cu;
+            chunk = round_up(std::max<int64_t>(1, ceil_div(total * ngrp, slots)), p.geo.TRB);
+            for (;;) {
+                int64_t wgs = 0;
+                for (int b = 0; b < c.n_seqs; ++b) wgs += ceil_div(span_of(h, b, T), chunk) * ngrp;
+                if (wgs <= slots) break;
+                chunk += p.geo.TRB;
+            }
+        }
+        chunk = round_up(chunk, p.geo.TRB);
+    } else if (chunk <= 0) {
         // About 2048 workgroups of (session, chunk, KV head), i.e. several per
         // CU so that the last round is a small fraction of the work, but at
         // least 64 rows per query row so that the partials (R x (hd + 2)
         // floats written and read back per chunk) stay within a few percent
         // of the chunk's K/V bytes (R x (hd + 2) x 8 / (64 R x 1.8125 hd)).
-        const int64_t R = (int64_t)T * (c.n_q_heads / c.n_kv_heads);
         chunk = round_up(ceil_div(std::max<int64_t>(total, 1) * c.n_kv_heads, 2048), kvq::kSplitQuantum);
-        chunk = std::min<int64_t>(std::max<int64_t>(chunk, std::max<int64_t>(256, 64 * R)), 1 << 16);
+        chunk = std::min<int64_t>(std::max<int64_t>(chunk, std::max<int64_t>(256, 64 * (int64_t)R)), 1 << 16);
         chunk = round_up(chunk, 256);   // whole rounds of 4 waves x 32 rows x 2 prefetched tiles
     }
     // at most kMaxSplits chunks per session
-    chunk = std::max<int64_t>(chunk, round_up(ceil_div(maxvis, kvq::kMaxSplits), kvq::kSplitQuantum));
-    Plan p;
+    chunk = std::max<int64_t>(chunk, round_up(ceil_div(maxvis, kvq::kMaxSplits), p.gh > 0 ? p.geo.TRB : 64));
     p.chunk = (int32_t)chunk;
     p.splits = (int32_t)std::max<int64_t>(1, ceil_div(maxvis, chunk));
     int64_t entries = (int64_t)c.n_seqs * p.splits * T * c.n_q_heads;
@@ -179,6 +261,8 @@ kvq_status kvq_create(const kvq_config* cfg, void* k_planes, void* v_planes,
     h->len.assign(cfg->n_seqs, 0);
     h->base.assign(cfg->n_seqs, 0);
     h->split_rows = 0;
+    h->head_group = 0;
+    h->sub_tiles = 0;
     int n = 2 * cfg->n_seqs + 4;
     std::vector<int32_t> idx(n), val(n, 0);
     for (int i = 0; i < n; ++i) idx[i] = i;
@@ -333,6 +417,8 @@ kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, c
             return fail(KVQ_ERANGE, "session " + std::to_string(b) + ": visible rows were rebased away");
     }
     Plan p = make_plan(h, T);
+    if (h->head_group > 0 && p.gh == 0 && aligned_start_resident(h, T))
+        return fail(KVQ_EINVAL, "the decode tiling set with kvq_set_decode_tiling does not fit this shape");
     if (!ws || ws_bytes < p.ml_bytes + p.o_bytes) return fail(KVQ_EINVAL, "workspace missing or too small");
     if (!aligned(ws, 256)) return fail(KVQ_EINVAL, "workspace must be 256-byte aligned");
     kvq::DecodeParams dp{};
@@ -355,6 +441,9 @@ kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, c
     dp.base_d = base_d(h);
     dp.chunk = p.chunk;
     dp.splits = p.splits;
+    dp.gh = p.gh;
+    dp.sub = p.sub;
+    dp.geo = p.geo;
     dp.scale = scale;
     dp.part_ml = static_cast<float*>(ws);
     dp.part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + p.ml_bytes);
@@ -393,6 +482,17 @@ kvq_status kvq_set_split_rows(kvq_cache* h, int32_t rows) {
     if (rows < 0 || rows % kvq::kSplitQuantum != 0)
         return fail(KVQ_EINVAL, "split rows must be 0 or a positive multiple of 64");
     h->split_rows = rows;
+    return KVQ_OK;
+}
+
+kvq_status kvq_set_decode_tiling(kvq_cache* h, int32_t head_group, int32_t sub_tiles) {
+    if (!h) return fail(KVQ_EINVAL, "handle is NULL");
+    if (head_group < -1 || (head_group > 0 && h->cfg.n_kv_heads % head_group != 0))
+        return fail(KVQ_EINVAL, "head_group must be -1, 0 or a divisor of n_kv_heads");
+    if (sub_tiles != 0 && sub_tiles != 1 && sub_tiles != 2 && sub_tiles != 4)
+        return fail(KVQ_EINVAL, "sub_tiles must be 0, 1, 2 or 4");
+    h->head_group = head_group;
+    h->sub_tiles = sub_tiles;
     return KVQ_OK;
 }
 

@@ -63,6 +63,50 @@ struct MoveParams {
     int32_t rows[kMaxSessionsPerLaunch];
 };
 
+// Geometry of the whole-row decode kernel (one workgroup per session, chunk
+// and group of gh KV heads; buffers of 32*sub rows).  Byte counts are per
+// row segment of the group.
+struct RowGeo {
+    int32_t SK, SV;      // K / V bytes of the group per row
+    int32_t KC, KCP;     // 16-byte pieces of a K row segment; LDS count, made odd
+    int32_t VC, VCP;     // 16-byte pieces of a V row segment; LDS count, made odd
+    int32_t KSTR;        // LDS K row stride (KCP * 16)
+    int32_t VSTR;        // LDS V row stride (VCP * 16)
+    int32_t TRB;         // rows per buffer
+    int32_t NKI, NVI;    // wave-wide 16-byte-per-lane load instructions per buffer
+    int32_t RAWB;        // bytes per buffer (K rows, then V rows)
+    int32_t HB;          // bytes per KV-head area
+    int32_t lds;         // dynamic LDS bytes: two buffers and gh head areas
+    uint32_t kmagic;     // ceil(2^32 / KCP): n / KCP == umulhi(n, kmagic) for the n used
+    uint32_t vmagic;     // ceil(2^32 / VCP)
+};
+
+constexpr int kRowTile = 32;          // rows per tile of the whole-row kernel
+constexpr int kRowMaxSlots = 16;      // load instructions per wave and buffer it is built for
+constexpr int kLdsBytes = 160 * 1024;
+
+inline RowGeo row_geo(int gh, int NB, int sub) {
+    RowGeo g{};
+    g.SK = gh * NB * 34;
+    g.SV = gh * NB * 24;
+    g.KC = g.SK / 16;
+    g.KCP = g.KC | 1;
+    g.VC = g.SV / 16;
+    g.VCP = g.VC | 1;
+    g.KSTR = g.KCP * 16;
+    g.VSTR = g.VCP * 16;
+    g.TRB = kRowTile * sub;
+    g.NKI = (g.TRB * g.KCP + 63) / 64;
+    g.NVI = (g.TRB * g.VCP + 63) / 64;
+    g.RAWB = g.TRB * g.KSTR + g.TRB * g.VSTR;
+    g.HB = NB * (1024 + 128 + 128) + 64 * (NB < 4 ? 4 : NB);
+    g.lds = 2 * g.RAWB + gh * g.HB;
+    // exact for n < 2^32 / d, far above the piece counts of a buffer
+    g.kmagic = (uint32_t)(((1ull << 32) + g.KCP - 1) / g.KCP);
+    g.vmagic = (uint32_t)(((1ull << 32) + g.VCP - 1) / g.VCP);
+    return g;
+}
+
 // Split-K decode plus the log-sum-exp combine.
 struct DecodeParams {
     const void* q;              // [B, T, H, hd]
@@ -76,8 +120,13 @@ struct DecodeParams {
     int32_t v_row;
     const int32_t* len_d;
     const int32_t* base_d;
-    int32_t chunk;              // rows per split (multiple of kSplitQuantum)
+    int32_t chunk;              // rows per split (multiple of kSplitQuantum); chunks
+                                // start at the first visible row rounded down to 32
     int32_t splits;             // split slots per session
+    int32_t gh;                 // > 0: whole-row kernel with gh KV heads per workgroup;
+                                // 0: one KV head per workgroup
+    int32_t sub;                // whole-row kernel: rows per buffer / 32
+    RowGeo geo;                 // whole-row kernel geometry
     float scale;
     float* part_ml;             // [B, splits, T, H, 2]  running max, running sum
     float* part_o;              // [B, splits, T, H, hd] unnormalised output

@@ -190,54 +190,102 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 
 // ---------------------------------------------------------------------------
 #include "kvq_decode.hip"
+#include "kvq_decode_rows.hip"
 
-// One 64-lane workgroup per (session, row t, Q head h): fold the session's
-// split partials, adding the sink once as a value-less column.  The splits'
-// maxima and weights are read by all lanes in parallel; the weighted sums over
-// splits run with lanes on dims.
-__global__ __launch_bounds__(64) void combine_kernel(DecodeParams p) {
+// One workgroup per (session, row t, Q head h): fold the session's split
+// partials (m in natural-log units, l, o), adding the sink once as a
+// value-less column.  The splits' maxima and weights are computed by all
+// threads in parallel; then each thread sums a 4-float slice of o over every
+// G-th split (G = 256 / (hd / 4) groups of splits, 8 loads in flight), and
+// the G group sums are added in a fixed order.
+constexpr int kCombineThreads = 256;
+
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p) {
     __shared__ float wts[kMaxSplits];
+    __shared__ float red[kCombineThreads / 32 > 8 ? kCombineThreads / 32 : 8];
+    __shared__ __align__(16) float part[kCombineThreads * 4];
     const int idx = blockIdx.x;
     const int h = idx % p.H;
     const int t = (idx / p.H) % p.T;
     const int b = idx / (p.H * p.T);
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int len = p.len_d[b];
     const int lo = p.window > 0 ? max(0, len - p.T + 1 - p.window) : 0;
-    const int ns = min(p.splits, (len - lo + p.chunk - 1) / p.chunk);
+    const int org = lo & ~31;   // chunks start on a 32-row boundary
+    const int ns = min(p.splits, (len - org + p.chunk - 1) / p.chunk);
     const size_t stride = (size_t)p.T * p.H;
     const size_t e0 = ((size_t)b * p.splits * p.T + t) * p.H + h;   // split 0 entry
+
+    // M = max over splits (and the sink)
     float m_loc = -INFINITY;
-    for (int s = lane; s < ns; s += 64) m_loc = fmaxf(m_loc, p.part_ml[2 * (e0 + s * stride)]);
-    float M = wave_max(m_loc);
+    for (int s = tid; s < ns; s += kCombineThreads) m_loc = fmaxf(m_loc, p.part_ml[2 * (e0 + s * stride)]);
+    m_loc = wave_max(m_loc);
+    if (lane == 0) red[wave] = m_loc;
+    __syncthreads();
+    float M = red[0];
+    for (int w = 1; w < kCombineThreads / 64; ++w) M = fmaxf(M, red[w]);
     const bool has_sink = p.sinks != nullptr;
     const float sink = has_sink ? p.sinks[h] : 0.0f;
     if (has_sink) M = fmaxf(M, sink);
+    __syncthreads();   // red is reused below
+
+    // weights w_s = e^(m_s - M), Z = sum_s w_s l_s (+ e^(sink - M))
     float z = 0.0f;
-    for (int s = lane; s < ns; s += 64) {
+    for (int s = tid; s < ns; s += kCombineThreads) {
         const float m = p.part_ml[2 * (e0 + s * stride)];
         const float w = (m == -INFINITY) ? 0.0f : expf(m - M);
         wts[s] = w;
         z = fmaf(w, p.part_ml[2 * (e0 + s * stride) + 1], z);
     }
-    const float Z = wave_sum(z) + (has_sink ? expf(sink - M) : 0.0f);
-    __syncthreads();
-    const float invZ = 1.0f / Z;
-    for (int d = lane; d < p.hd; d += 64) {
-        const float* o = p.part_o + e0 * p.hd + d;
-        const size_t so = stride * p.hd;
-        float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-        int s = 0;
-        for (; s + 4 <= ns; s += 4) {
-            a0 = fmaf(wts[s], o[(size_t)s * so], a0);
-            a1 = fmaf(wts[s + 1], o[(size_t)(s + 1) * so], a1);
-            a2 = fmaf(wts[s + 2], o[(size_t)(s + 2) * so], a2);
-            a3 = fmaf(wts[s + 3], o[(size_t)(s + 3) * so], a3);
+    z = wave_sum(z);
+    if (lane == 0) red[wave] = z;
+    __syncthreads();   // wts and red are complete
+    float Z = 0.0f;
+    for (int w = 0; w < kCombineThreads / 64; ++w) Z += red[w];
+    if (has_sink) Z += expf(sink - M);
+
+    // weighted sum of o over the splits
+    const int nq = p.hd >> 2;                 // float4 slices per row (16, 32 .. 64)
+    const int G = kCombineThreads / nq;       // split groups
+    const int dq = tid % nq, sg = tid / nq;
+    const float* o = p.part_o + e0 * p.hd + 4 * dq;
+    const size_t so = stride * p.hd;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    int s = (sg < G) ? sg : ns;               // threads past G groups idle (hd not dividing 1024)
+    for (; s + 7 * G < ns; s += 8 * G) {
+        float4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = *reinterpret_cast<const float4*>(o + (size_t)(s + k * G) * so);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float w = wts[s + k * G];
+            acc.x = fmaf(w, v[k].x, acc.x);
+            acc.y = fmaf(w, v[k].y, acc.y);
+            acc.z = fmaf(w, v[k].z, acc.z);
+            acc.w = fmaf(w, v[k].w, acc.w);
         }
-        for (; s < ns; ++s) a0 = fmaf(wts[s], o[(size_t)s * so], a0);
-        p.out[(((size_t)b * p.T + t) * p.H + h) * p.hd + d] = ((a0 + a1) + (a2 + a3)) * invZ;
     }
-    if (p.lse && lane == 0) p.lse[((size_t)b * p.T + t) * p.H + h] = M + logf(Z);
+    for (; s < ns; s += G) {
+        const float4 v = *reinterpret_cast<const float4*>(o + (size_t)s * so);
+        const float w = wts[s];
+        acc.x = fmaf(w, v.x, acc.x);
+        acc.y = fmaf(w, v.y, acc.y);
+        acc.z = fmaf(w, v.z, acc.z);
+        acc.w = fmaf(w, v.w, acc.w);
+    }
+    reinterpret_cast<float4*>(part)[sg * nq + dq] = acc;
+    __syncthreads();
+    if (tid < nq) {
+        float4 r = reinterpret_cast<const float4*>(part)[tid];
+        for (int g = 1; g < G; ++g) {
+            const float4 x = reinterpret_cast<const float4*>(part)[g * nq + tid];
+            r.x += x.x; r.y += x.y; r.z += x.z; r.w += x.w;
+        }
+        const float invZ = 1.0f / Z;
+        r.x *= invZ; r.y *= invZ; r.z *= invZ; r.w *= invZ;
+        reinterpret_cast<float4*>(p.out + (((size_t)b * p.T + t) * p.H + h) * p.hd)[tid] = r;
+    }
+    if (p.lse && tid == 0) p.lse[((size_t)b * p.T + t) * p.H + h] = M + logf(Z);
 }
 
 // ---------------------------------------------------------------------------
@@ -266,8 +314,35 @@ int launch_decode_t(const DecodeParams& p, hipStream_t st, const char** err) {
     const int grid = (items + 7) & ~7;
     hipLaunchKernelGGL((dec::decode_mfma<NB, RT, QLO>), dim3(grid), dim3(256), lds, st, p);
     if (check(err)) return 1;
-    hipLaunchKernelGGL(combine_kernel, dim3(p.B * p.T * p.H), dim3(64), 0, st, p);
+    hipLaunchKernelGGL(combine_kernel, dim3(p.B * p.T * p.H), dim3(kCombineThreads), 0, st, p);
     return check(err);
+}
+
+template <int NB, int RT, bool QLO>
+int launch_rows_t(const DecodeParams& p, hipStream_t st, const char** err) {
+    static bool configured = false;
+    if (!configured) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&rows::decode_rows<NB, RT, QLO>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) != hipSuccess) {
+            *err = "cannot raise the LDS limit of the decode kernel";
+            return 1;
+        }
+        configured = true;
+    }
+    const int items = p.B * p.splits * (p.Hkv / p.gh);
+    const int grid = (items + 7) & ~7;
+    hipLaunchKernelGGL((rows::decode_rows<NB, RT, QLO>), dim3(grid), dim3(64 * p.gh * RT), p.geo.lds, st, p);
+    if (check(err)) return 1;
+    hipLaunchKernelGGL(combine_kernel, dim3(p.B * p.T * p.H), dim3(kCombineThreads), 0, st, p);
+    return check(err);
+}
+
+template <int NB>
+int launch_rows_nb(const DecodeParams& p, hipStream_t st, const char** err) {
+    const int R = p.T * p.hpk;
+    const bool qlo = p.dtype == 0;
+    if (R <= 16) return qlo ? launch_rows_t<NB, 1, true>(p, st, err) : launch_rows_t<NB, 1, false>(p, st, err);
+    return qlo ? launch_rows_t<NB, 2, true>(p, st, err) : launch_rows_t<NB, 2, false>(p, st, err);
 }
 
 template <int NB>
@@ -302,6 +377,14 @@ int launch_append(const AppendParams& p, void* stream, const char** err) {
 
 int launch_decode(const DecodeParams& p, void* stream, const char** err) {
     hipStream_t st = (hipStream_t)stream;
+    if (p.gh > 0) {
+        switch (p.hd / 32) {
+            case 2: return launch_rows_nb<2>(p, st, err);
+            case 4: return launch_rows_nb<4>(p, st, err);
+            case 8: return launch_rows_nb<8>(p, st, err);
+            default: *err = "the whole-row decode supports head_dim 64, 128 and 256"; return 1;
+        }
+    }
     switch (p.hd / 32) {
         case 1: return launch_decode_nb<1>(p, st, err);
         case 2: return launch_decode_nb<2>(p, st, err);

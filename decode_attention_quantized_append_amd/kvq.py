@@ -26,8 +26,8 @@ STATUS_NAMES = {0: "KVQ_OK", 1: "KVQ_EINVAL", 2: "KVQ_ECAPACITY", 3: "KVQ_ERANGE
 
 # Every entry point the header declares.
 EXPORTS = ("kvq_required_bytes", "kvq_create", "kvq_append", "kvq_decode_workspace_bytes",
-           "kvq_decode", "kvq_truncate", "kvq_set_split_rows", "kvq_info", "kvq_host_lengths",
-           "kvq_destroy", "kvq_last_error")
+           "kvq_decode", "kvq_truncate", "kvq_set_split_rows", "kvq_set_decode_tiling", "kvq_info",
+           "kvq_host_lengths", "kvq_destroy", "kvq_last_error")
 
 
 class kvq_config(ctypes.Structure):
@@ -70,6 +70,7 @@ def _declare(lib):
         "kvq_decode": (st, [vp, vp, i32, i32, vp, f32, vp, vp, vp, ctypes.c_size_t, vp]),
         "kvq_truncate": (st, [vp, i32p, vp]),
         "kvq_set_split_rows": (st, [vp, i32]),
+        "kvq_set_decode_tiling": (st, [vp, i32, i32]),
         "kvq_info": (st, [vp, ctypes.POINTER(kvq_info_t)]),
         "kvq_host_lengths": (st, [vp, i64p, i64p]),
         "kvq_destroy": (None, [vp]),
@@ -167,6 +168,11 @@ def kvq_decode(h: int, q: int, dtype: int, T: int, sinks: Optional[int], scale: 
 def kvq_truncate(h: int, new_len: Sequence[int], stream: int = 0, lib=None) -> None:
     lib = lib or load()
     _check(lib, lib.kvq_truncate(h, _i32_array(new_len), stream or None))
+
+
+def kvq_set_decode_tiling(h: int, head_group: int, sub_tiles: int = 0, lib=None) -> None:
+    lib = lib or load()
+    _check(lib, lib.kvq_set_decode_tiling(h, head_group, sub_tiles))
 
 
 def kvq_set_split_rows(h: int, rows: int, lib=None) -> None:
@@ -277,6 +283,9 @@ class KvqLayerCache:
 
     def set_split_rows(self, rows):
         kvq_set_split_rows(self.h, rows, self.lib)
+
+    def set_decode_tiling(self, head_group, sub_tiles=0):
+        kvq_set_decode_tiling(self.h, head_group, sub_tiles, self.lib)
 
     def host_lengths(self):
         return kvq_host_lengths(self.h, self.cfg.n_seqs, self.lib)

@@ -181,6 +181,15 @@ kvq_status kvq_truncate(kvq_cache* h, const int32_t* new_len, kvq_stream stream)
  * rounding.  Errors: EINVAL. */
 kvq_status kvq_set_split_rows(kvq_cache* h, int32_t rows);
 
+/* Tuning: how kvq_decode tiles the cache.  head_group = 0 lets each call
+ * choose; -1 selects one KV head per workgroup; k > 0 selects workgroups that
+ * stream whole row segments of k adjacent KV heads (k must divide n_kv_heads;
+ * head_dim 64, 128 or 256), with buffers of 32 * sub_tiles rows (sub_tiles 1,
+ * 2 or 4; 0 = chosen per call).  A k that does not fit a call's shape makes
+ * that kvq_decode fail with EINVAL.  The result does not depend on the tiling
+ * beyond float rounding.  Errors: EINVAL. */
+kvq_status kvq_set_decode_tiling(kvq_cache* h, int32_t head_group, int32_t sub_tiles);
+
 /* Copies the handle's configuration, sizes and buffer pointers. */
 kvq_status kvq_info(const kvq_cache* h, kvq_info_t* out);
 

@@ -42,10 +42,20 @@ class Pair:
         self.B, self.H, self.Hkv, self.hd, self.io = B, H, Hkv, hd, io
         self.gpu = KvqLayerCache(B, H, Hkv, hd, capacity, window, ring_step, device=DEV)
         self.ref = OracleCache(B, Hkv, hd, capacity, window, ring_step)
+        self.vmax = 0.0
 
     def append(self, k, v, counts=None):
         self.gpu.append(to_dev(k, self.io), to_dev(v, self.io), counts)
         self.ref.append(k, v, counts)
+        self.vmax = max(self.vmax, float(np.abs(v).max()))
+
+    def pv_atol(self):
+        """Bound on |o1 - o2| between two GPU decodes of the same rows that
+        round P differently to fp16 (other split plans, tilings or row
+        groupings): each is within 2^-11 * sum_j p_j |v_j| / sum_j p_j of the
+        fp32 result, so together within 2^-10 * max |v|.  max |v| is taken
+        from the appended rows, with 5 % for the q5_1 rounding of the codes."""
+        return 2.0 ** -10 * 1.05 * self.vmax
 
     def truncate(self, new_len):
         self.gpu.truncate(list(new_len))

@@ -99,6 +99,7 @@ SMALL = {
     "verify_small": (2, 16, 4, 256, 8, [600, 333], 0, 700, 0, False, "bf16", False),
     "hd32_gqa7": (2, 7, 1, 32, 3, [200, 70], 0, 256, 0, True, "f32", False),
     "hd96_window": (3, 6, 2, 96, 2, [300, 40, 2], 50, 320, 0, False, "bf16", False),
+    "qwen_f32_small": (2, 32, 8, 128, 2, [900, 161], 0, 1000, 0, True, "f32", True),
 }
 
 
@@ -137,21 +138,64 @@ def test_decode_split_invariance():
         o, l = p.gpu.decode(qd, scale)
         outs.append((o.cpu().numpy(), l.cpu().numpy()))
     # P enters the P.V product as fp16, rounded relative to each split's own
-    # running max (unit roundoff 2^-11): outputs agree to a few fp16 ulps of
-    # |v|; the row sums stay fp32, so the log-sum-exps agree to fp32 rounding.
+    # running max (unit roundoff 2^-11): outputs agree within Pair.pv_atol;
+    # the row sums stay fp32, so the log-sum-exps agree to fp32 rounding.
     for o, l in outs[1:]:
-        np.testing.assert_allclose(o, outs[0][0], atol=5e-4, rtol=5e-4)
+        np.testing.assert_allclose(o, outs[0][0], atol=p.pv_atol(), rtol=0)
         np.testing.assert_allclose(l, outs[0][1], atol=1e-5, rtol=1e-5)
     p.decode(q, scale)
 
 
-def test_ring_equals_flat():
+# Whole-row decode tilings (KV heads per workgroup, rows per buffer / 32) that
+# fit each shape; the automatic choice is covered by test_decode_parity.
+TILINGS = {
+    "qwen_gqa_small": [(8, 1), (4, 1), (4, 2), (2, 1), (2, 2)],
+    "batched_small": [(8, 1), (4, 2), (2, 1)],
+    "sink_ring_small": [(8, 1), (8, 2), (4, 1), (4, 4)],
+    "verify_small": [(4, 1), (2, 1), (2, 2), (1, 1), (1, 2)],
+    "qwen_f32_small": [(8, 1), (2, 2)],
+}
+
+
+@pytest.mark.parametrize("name,gh,sub", [(n, g, s) for n, lst in TILINGS.items() for g, s in lst])
+def test_decode_tiling_parity(name, gh, sub):
+    p, q, s, scale = build_small(name)
+    p.gpu.set_decode_tiling(gh, sub)
+    p.decode(q, scale, sinks=s, what=f"{name} gh={gh} sub={sub}")
+
+
+@pytest.mark.parametrize("name", sorted(TILINGS))
+def test_decode_tilings_agree(name):
+    """Every tiling, and one KV head per workgroup, give the same outputs up
+    to the fp16 rounding of P (Pair.pv_atol)."""
+    p, q, s, scale = build_small(name)
+    io = SMALL[name][10]
+    qd = to_dev(q, io)
+    sd = torch.from_numpy(s).to(DEV) if s is not None else None
+    outs = []
+    for gh, sub in [(-1, 0), (0, 0)] + TILINGS[name]:
+        p.gpu.set_decode_tiling(gh, sub)
+        for rows_ in (0, 64, 256):
+            p.gpu.set_split_rows(rows_)
+            o, l = p.gpu.decode(qd, scale, sinks=sd)
+            outs.append((o.cpu().numpy(), l.cpu().numpy()))
+    for o, l in outs[1:]:
+        np.testing.assert_allclose(o, outs[0][0], atol=p.pv_atol(), rtol=0)
+        np.testing.assert_allclose(l, outs[0][1], atol=1e-5, rtol=1e-5)
+
+
+@pytest.mark.parametrize("step,tiling", [(24, -1), (32, 4), (32, 0)])
+def test_ring_equals_flat(step, tiling):
     """The base-offset ring serves the same rows as a flat cache: identical
-    live bytes and identical outputs, step after step, through rebases."""
+    live bytes and identical outputs, step after step, through rebases.  Both
+    caches decode with the same kernel (one KV head per workgroup, or whole
+    row segments of 4 heads when the ring's base stays a multiple of 32)."""
     rng = np.random.default_rng(11)
-    B, H, Hkv, hd, W, cap, step = 2, 16, 4, 64, 40, 96, 24
+    B, H, Hkv, hd, W, cap = 2, 16, 4, 64, 40, 96
     ring = Pair(B, H, Hkv, hd, cap, W, step)
     flat = Pair(B, H, Hkv, hd, 2000, W, 0)
+    ring.gpu.set_decode_tiling(tiling)
+    flat.gpu.set_decode_tiling(tiling)
     L = 0
     for it in range(30):
         n = int(rng.integers(1, 33))
@@ -213,8 +257,8 @@ def test_verify_rows_equal_sequential_single_rows():
     for t in range(T):
         s.append(k[:, N0 + t:N0 + t + 1], v[:, N0 + t:N0 + t + 1])
         o1, l1 = s.gpu.decode(to_dev(q[:, t:t + 1], "bf16"), 0.088)
-        # equal up to the fp16 rounding of P (see test_decode_split_invariance)
-        np.testing.assert_allclose(o1.cpu().numpy()[:, 0], oa.cpu().numpy()[:, t], atol=5e-4, rtol=5e-4)
+        # equal up to the fp16 rounding of P (Pair.pv_atol)
+        np.testing.assert_allclose(o1.cpu().numpy()[:, 0], oa.cpu().numpy()[:, t], atol=a.pv_atol(), rtol=0)
         np.testing.assert_allclose(l1.cpu().numpy()[:, 0], la.cpu().numpy()[:, t], atol=1e-5, rtol=1e-5)
 
 
@@ -229,7 +273,7 @@ def test_gqa_equals_repeated_heads():
     r.append(np.repeat(k, H // Hkv, axis=2), np.repeat(v, H // Hkv, axis=2))
     og, lg = g.gpu.decode(to_dev(q, "bf16"), 0.125)
     orr, lr = r.gpu.decode(to_dev(q, "bf16"), 0.125)
-    np.testing.assert_allclose(og.cpu().numpy(), orr.cpu().numpy(), atol=5e-4, rtol=5e-4)   # fp16 P
+    np.testing.assert_allclose(og.cpu().numpy(), orr.cpu().numpy(), atol=g.pv_atol(), rtol=0)   # fp16 P
     np.testing.assert_allclose(lg.cpu().numpy(), lr.cpu().numpy(), atol=1e-5, rtol=1e-5)
     g.decode(q, 0.125, what="gqa")
 

@@ -235,8 +235,8 @@ def test_decode_validation_and_plan(lib):
 def test_decode_query_tile_limits(lib):
     h = create(lib, n_seqs=1, n_q_heads=64, n_kv_heads=1, head_dim=256, capacity=100)
     kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 50, None, 0, lib)
-    # 64 query rows of head_dim 256 exceed the 8192-float query tile
-    assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 1, None, 0.1, O, None, WS, 1 << 40) == kvq.KVQ_EUNSUPPORTED
+    # 64 query rows per KV head exceed the 32 that kvq_decode accepts (EINVAL, as declared)
+    assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 1, None, 0.1, O, None, WS, 1 << 40) == kvq.KVQ_EINVAL
 
 
 def test_decode_refuses_rebased_rows(lib):
@@ -258,6 +258,68 @@ def test_split_rows_setting(lib):
     kvq.kvq_decode(h, Q, kvq.KVQ_F32, 1, None, 0.1, O, None, WS, 1 << 40, 0, lib)
     assert "chunk=640 splits=7" in log(lib)[0]
     assert kvq.kvq_info(h, lib).split_rows == 640
+
+
+def plan_of(lib, h, T=1):
+    lib.kvq_nodev_clear()
+    kvq.kvq_decode(h, Q, kvq.KVQ_BF16, T, None, 0.1, O, None, WS, 1 << 40, 0, lib)
+    (line,) = log(lib)
+    return {k: int(v) for k, v in re.findall(r"(\w+)=(-?\d+)", line)}
+
+
+def test_decode_kernel_choice(lib):
+    # 8 KV heads x 128, 4 query rows per KV head: one KV head per workgroup;
+    # on request, whole-row workgroups over all 8 heads with 32-row buffers
+    h = create(lib, n_seqs=1, n_q_heads=32, n_kv_heads=8, head_dim=128, capacity=9000)
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 8192, None, 0, lib)
+    assert plan_of(lib, h)["gh"] == 0
+    kvq.kvq_set_decode_tiling(h, 8, 1, lib)
+    p = plan_of(lib, h)
+    assert (p["gh"], p["sub"]) == (8, 1) and 0 < p["lds"] <= 160 * 1024 and p["chunk"] % 32 == 0
+    assert p["splits"] == -(-8192 // p["chunk"])
+    kvq.kvq_set_decode_tiling(h, -1, 0, lib)           # one KV head per workgroup
+    assert plan_of(lib, h)["gh"] == 0
+    kvq.kvq_set_decode_tiling(h, 4, 2, lib)            # an explicit group and buffer depth
+    p = plan_of(lib, h)
+    assert (p["gh"], p["sub"]) == (4, 2) and p["chunk"] % 64 == 0
+    assert err(lib, kvq.kvq_set_decode_tiling, h, 3, 0) == kvq.KVQ_EINVAL    # does not divide 8
+    assert err(lib, kvq.kvq_set_decode_tiling, h, 2, 3) == kvq.KVQ_EINVAL    # no such depth
+    assert err(lib, kvq.kvq_set_decode_tiling, h, -2, 0) == kvq.KVQ_EINVAL
+    # one head of 128 is not a whole number of 16-byte pieces: that call fails
+    kvq.kvq_set_decode_tiling(h, 1, 0, lib)
+    lib.kvq_nodev_clear()
+    assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 1, None, 0.1, O, None, WS, 1 << 40) == kvq.KVQ_EINVAL
+    assert log(lib) == []
+    # verify rows (T=8, 4 query heads per KV head: 32 rows, two row tiles per head)
+    h = create(lib, n_seqs=2, n_q_heads=16, n_kv_heads=4, head_dim=256, capacity=5000)
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 4000, None, 0, lib)
+    p = plan_of(lib, h, T=8)
+    assert p["gh"] == 4 and p["lds"] <= 160 * 1024
+    # head_dim 96 and a single KV head of 64 have no whole-row kernel
+    h = create(lib, n_seqs=1, n_q_heads=8, n_kv_heads=8, head_dim=96, capacity=100)
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 50, None, 0, lib)
+    assert plan_of(lib, h)["gh"] == 0
+    h = create(lib, n_seqs=1, n_q_heads=4, n_kv_heads=1, head_dim=64, capacity=300)
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 256, None, 0, lib)
+    assert plan_of(lib, h)["gh"] == 0
+
+
+def test_decode_ring_start_below_base_falls_back(lib):
+    # ring_step 10: base is not always a multiple of 32, and the whole-row
+    # kernel, which starts at the first visible row rounded down to 32, is
+    # used only while that row is still resident
+    h = create(lib, n_seqs=1, n_q_heads=32, n_kv_heads=8, head_dim=128, capacity=100, window=90,
+               ring_step=10)
+    kvq.kvq_set_decode_tiling(h, 8, 1, lib)
+    seen = set()
+    for _ in range(300):
+        kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 1, None, 0, lib)
+        L, base = lengths(lib, h, 1)
+        lo = max(0, L[0] - 90)
+        gh = plan_of(lib, h)["gh"]
+        assert gh == (8 if (lo & ~31) >= base[0] else 0)
+        seen.add(gh)
+    assert seen == {0, 8}
 
 
 def test_launch_failure_reports_edevice_and_keeps_the_mirror(lib):
