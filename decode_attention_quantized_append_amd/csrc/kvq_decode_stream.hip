@@ -1,0 +1,407 @@
+// kvq_decode_stream.hip -- split-K flash decode, one KV head per wave, each
+// wave streaming its own head's row windows through a private LDS double
+// buffer (gfx950).  Included by kvq_kernels.hip (inside namespace kvq), after
+// kvq_decode_rows.hip.
+//
+// The same partials as the other decode kernels (cortiq-engine "Struct
+// LayerKvCache", attend_group and attend_group_upto; memra-engine "Struct
+// KvLayer", len_d and base_d):
+//   * a workgroup is (session, chunk of rows, group of gh KV heads); wave w
+//     is KV head g = hg*gh + w and computes all R = T*H/Hkv query rows of the
+//     group (one or two 16-row tiles).  The waves of a workgroup read the same
+//     rows at about the same time, so the CU fetches whole row segments from
+//     HBM, but no wave waits for another: there is no workgroup barrier.
+//   * per 32-row tile, the wave copies its head's K window (the q8_0 blocks,
+//     from the 16-byte boundary at or below them) and V window (the q5_1
+//     blocks) of every row into LDS with global_load_lds_dwordx4, into one of
+//     two buffers: the next buffer is in flight while the wave computes the
+//     current one.  Row strides in LDS are odd numbers of 16-byte pieces,
+//     which keeps 8 consecutive rows on distinct banks.
+//   * scores are computed transposed, S^T = K Q^T, one v_mfma_f32_16x16x32_f16
+//     per 32-element block, 16 keys and row tile; the K codes, exact in fp16,
+//     are converted once per tile and feed every row tile.  Each lane ends up
+//     with 8 keys of one query row, which after the softmax are the A operand
+//     of the P V product, in key order 4*q4 + i, 16 + 4*q4 + i.
+//   * the V operand comes straight from the q5_1 bytes: ds_read_b64_tr_b8 of
+//     the 16 nibble bytes of 8 keys gives a lane the codes of its dimension
+//     (low nibble) and of dimension + 16 (high nibble); a second transposed
+//     read of the block headers gives the high-bit bytes, which a DPP row
+//     broadcast hands to the lanes that need them.
+//   * the q5_1 step multiplies P per block (P' = P * step, fp16); the offset
+//     term sum_key P * m is one more MFMA per tile against the offsets.
+namespace stream {
+
+using dec::f4;
+using dec::h8;
+using dec::i2;
+using dec::kLn2;
+using dec::kLog2e;
+using dec::lds_i2;
+using rows::dma16;
+using rows::pkey;
+
+constexpr int kTile = 32;
+
+template <int NB>
+using Win = StreamWin<NB>;
+
+template <int NL>
+__device__ __forceinline__ void wait_loads_upto() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((NL & 15) | 0x0F70 | (((NL >> 4) & 3) << 14));   // vmcnt(NL)
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t bcast_row(uint32_t x, int n) {
+    // lane n of each 16-lane row, to every lane of the row (DPP row_newbcast)
+    switch (n) {
+        case 4: return __builtin_amdgcn_update_dpp(0, (int)x, 0x154, 0xF, 0xF, false);
+        case 5: return __builtin_amdgcn_update_dpp(0, (int)x, 0x155, 0xF, 0xF, false);
+        case 6: return __builtin_amdgcn_update_dpp(0, (int)x, 0x156, 0xF, 0xF, false);
+        default: return __builtin_amdgcn_update_dpp(0, (int)x, 0x157, 0xF, 0xF, false);
+    }
+}
+
+template <int NB, int RTW, bool QLO>
+__global__ __launch_bounds__(RTW == 1 ? 512 : 256) void decode_stream(DecodeParams p) {
+    using WN = Win<NB>;
+    constexpr int HD = NB * 32;
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int q4 = lane >> 4, j16 = lane & 15;
+    const int gh = p.gh, ngrp = p.Hkv / gh;
+
+    const int W = gridDim.x, wid = blockIdx.x;
+    const int L = (wid & 7) * (W >> 3) + (wid >> 3);
+    const int hg = L % ngrp;
+    const int s = (L / ngrp) % p.splits;
+    const int b = L / (ngrp * p.splits);
+    if (b >= p.B) return;
+    const int g = hg * gh + wave;
+    const int R = p.T * p.hpk;
+
+    // Q rows rt*16 + j16 as the B operand of S^T = K Q^T
+    h8 qh[RTW][NB], ql[RTW][NB];
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+        const int r = rt * 16 + j16;
+        const bool real = r < R;
+        const int t = real ? r / p.hpk : 0, hh = real ? r % p.hpk : 0;
+        const size_t i0 = (((size_t)b * p.T + t) * p.H + g * p.hpk + hh) * HD + 8 * q4;
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+            float qv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qv[e] = 0.0f;
+            if (real) {
+                if (p.dtype == 1) {
+                    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + i0 + blk * 32);
+                    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        qv[2 * e] = __uint_as_float(w4[e] << 16);
+                        qv[2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
+                    }
+                } else {
+                    const float* src = static_cast<const float*>(p.q) + i0 + blk * 32;
+                    const float4 a = *reinterpret_cast<const float4*>(src);
+                    const float4 c = *reinterpret_cast<const float4*>(src + 4);
+                    qv[0] = a.x; qv[1] = a.y; qv[2] = a.z; qv[3] = a.w;
+                    qv[4] = c.x; qv[5] = c.y; qv[6] = c.z; qv[7] = c.w;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const _Float16 xh = (_Float16)qv[e];
+                qh[rt][blk][e] = xh;
+                if (QLO) ql[rt][blk][e] = (_Float16)(qv[e] - (float)xh);
+            }
+        }
+    }
+
+    const int len = p.len_d[b];
+    const int base = p.base_d[b];
+    const int lo = p.window > 0 ? max(0, len - p.T + 1 - p.window) : 0;
+    const int c0 = (lo & ~(kTile - 1)) + s * p.chunk;
+    const int c1 = min(c0 + p.chunk, len);
+    if (c0 >= c1) return;
+
+    uint8_t* const wb = smem + wave * WN::BYTES;
+    // This head's windows: K from the 16-byte boundary at or below its first
+    // block (kofs bytes before it), V exactly its blocks.
+    const int kstart = g * NB * 34;
+    const int kofs = kstart & 15;
+    const uint8_t* const kwin = p.k_planes + (int64_t)b * p.k_stride + (kstart - kofs);
+    const uint8_t* const vwin = p.v_planes + (int64_t)b * p.v_stride + g * NB * 24;
+    // per lane, the byte offset of its piece (instruction x) from the buffer's first row
+    uint32_t koff[WN::NKI], voff[WN::NVI];
+#pragma unroll
+    for (int x = 0; x < WN::NKI; ++x) {
+        const int pc = x * 64 + lane, row = pc / WN::KWP, col = pc - row * WN::KWP;
+        koff[x] = (uint32_t)(row * p.k_row + min(col, WN::KW - 1) * 16);
+    }
+#pragma unroll
+    for (int x = 0; x < WN::NVI; ++x) {
+        const int pc = x * 64 + lane, row = pc / WN::VWP, col = pc - row * WN::VWP;
+        voff[x] = (uint32_t)(row * p.v_row + min(col, WN::VW - 1) * 16);   // the pad piece re-reads a real one
+    }
+    // Load the buffer of rows [t0, t0 + TR) into slot `slot`.  Rows from c1 on
+    // (a session's last buffer) are not loaded; rows below lo (first buffer)
+    // are resident and masked.
+    auto issue = [&](int t0, int slot) {
+        uint8_t* const dst = wb + slot * WN::SLOT;
+        const int nrows = min(WN::TR, c1 - t0);
+        const uint8_t* const kt = kwin + (int64_t)(t0 - base) * p.k_row;
+        const uint8_t* const vt = vwin + (int64_t)(t0 - base) * p.v_row;
+#pragma unroll
+        for (int x = 0; x < WN::NKI; ++x) {
+            uint32_t o = koff[x];
+            asm volatile("" : "+v"(o));
+            if (lane < nrows * WN::KWP - x * 64) dma16(kt, o, dst + x * 1024);
+        }
+#pragma unroll
+        for (int x = 0; x < WN::NVI; ++x) {
+            uint32_t o = voff[x];
+            asm volatile("" : "+v"(o));
+            if (lane < nrows * WN::VWP - x * 64) dma16(vt, o, dst + WN::TR * WN::KSTR + x * 1024);
+        }
+    };
+
+    f4 oacc[RTW][2 * NB], macc[RTW];
+    float mrow[RTW], lsum[RTW];
+    int vis_lo[RTW], vis_hi[RTW];
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+        macc[rt] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dt = 0; dt < 2 * NB; ++dt) oacc[rt][dt] = (f4){0.f, 0.f, 0.f, 0.f};
+        mrow[rt] = -INFINITY;
+        lsum[rt] = 0.0f;
+        vis_lo[rt] = vis_hi[rt] = 0;
+        const int r = rt * 16 + j16;
+        if (r < R) {
+            vis_hi[rt] = len - p.T + r / p.hpk + 1;
+            vis_lo[rt] = p.window > 0 ? max(0, vis_hi[rt] - p.window) : 0;
+        }
+    }
+    const int full_hi = min(len - p.T + 1, c1);
+    const int full_lo = max(p.window > 0 ? max(0, len - p.window) : 0, c0);
+    const float sc2 = p.scale * kLog2e;
+    float* const KSa = reinterpret_cast<float*>(wb + WN::KS);
+    float* const VDa = reinterpret_cast<float*>(wb + WN::VD);
+    uint16_t* const VMa = reinterpret_cast<uint16_t*>(wb + WN::VM);
+    const int vkey = pkey(q4, j16 >> 1);                 // V row of this lane's tr8 reads
+    const int mk0 = pkey(q4, j16 >> 2), mk1 = pkey(q4, 4 + (j16 >> 2));
+    const int mc = (4 * (j16 & 3) < NB) ? (j16 & 3) : 0;   // columns past NB of the offset product are unused
+
+    const int nt = (c1 - c0 + WN::TR - 1) / WN::TR;
+    issue(c0, 0);
+    if (nt > 1) issue(c0 + WN::TR, 1);
+    for (int it = 0; it < nt; ++it) {
+        // this buffer's loads have landed; the next buffer's may stay in flight
+        // when it is a whole one (a partial last buffer issues fewer loads)
+        if (c0 + (it + 2) * WN::TR <= c1) wait_loads_upto<WN::NL>(); else wait_loads_upto<0>();
+        const uint8_t* const rk0 = wb + (it & 1) * WN::SLOT;
+        const uint8_t* const rv0 = rk0 + WN::TR * WN::KSTR;
+#pragma unroll
+        for (int sb = 0; sb < WN::SUB; ++sb) {
+            const int t0 = c0 + it * WN::TR + sb * kTile;
+            if (t0 >= c1) break;
+            const uint8_t* const rk = rk0 + sb * kTile * WN::KSTR;
+            const uint8_t* const rv = rv0 + sb * kTile * WN::VSTR;
+            dec::lds_order();   // the previous tile's reads of the scale arrays come first
+            // ---- K scales, V steps and offsets of the tile (rows past c1 hold stale bytes)
+#pragma unroll
+            for (int x = 0; x < (kTile * NB + 63) / 64; ++x) {
+                const int u = x * 64 + lane;
+                if (kTile * NB % 64 == 0 || u < kTile * NB) {
+                    const int key = u / NB, blk = u - (u / NB) * NB;
+                    const bool live = t0 + key < c1;
+                    const uint16_t kd = *reinterpret_cast<const uint16_t*>(rk + key * WN::KSTR + kofs + blk * 34);
+                    const uint32_t dm = *reinterpret_cast<const uint32_t*>(rv + key * WN::VSTR + blk * 24);
+                    KSa[blk * kTile + key] = live ? f16_value(kd) * sc2 : 0.0f;
+                    VDa[blk * kTile + key] = live ? f16_value((uint16_t)(dm & 0xFFFF)) : 0.0f;
+                    VMa[key * WN::VMS + blk] = live ? (uint16_t)(dm >> 16) : (uint16_t)0;
+                }
+            }
+            dec::lds_order();
+
+            // ---- scores S^T: sv[rt][h][i] = S[row rt*16 + j16][key 16h + 4*q4 + i] (base 2)
+            float sv[RTW][2][4];
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sv[rt][h][i] = 0.0f;
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk) {
+                const float4 ks0 = *reinterpret_cast<const float4*>(KSa + blk * kTile + 4 * q4);
+                const float4 ks1 = *reinterpret_cast<const float4*>(KSa + blk * kTile + 16 + 4 * q4);
+                const float ksv[2][4] = {{ks0.x, ks0.y, ks0.z, ks0.w}, {ks1.x, ks1.y, ks1.z, ks1.w}};
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int key = 16 * h + j16;
+                    const uint32_t a = (uint32_t)(key * WN::KSTR + kofs + blk * 34 + 2 + 8 * q4);
+                    const uint32_t* w = reinterpret_cast<const uint32_t*>(rk + (a & ~3u));
+                    const uint32_t sh = a & 3u;
+                    const uint32_t w0 = w[0], w1 = w[1], w2 = w[2];
+                    h8 kf = dec::k_codes_f16(__builtin_amdgcn_alignbyte(w1, w0, sh),
+                                             __builtin_amdgcn_alignbyte(w2, w1, sh));
+                    // tie this block's products to the previous block's sums, so
+                    // that the products of all blocks are not held at once
+                    if (NB > 4) {
+#pragma unroll
+                        for (int rt = 0; rt < RTW; ++rt)
+                            asm volatile("" : "+v"(kf) : "v"(sv[rt][h][0]), "v"(sv[rt][h][1]), "v"(sv[rt][h][2]), "v"(sv[rt][h][3]));
+                    }
+#pragma unroll
+                    for (int rt = 0; rt < RTW; ++rt) {
+                        f4 d = dec::mfma(kf, qh[rt][blk], (f4){0.f, 0.f, 0.f, 0.f});
+                        if (QLO) d = dec::mfma(kf, ql[rt][blk], d);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sv[rt][h][i] = fmaf(ksv[h][i], d[i], sv[rt][h][i]);
+                    }
+                }
+            }
+
+            // ---- online softmax against a reference max that moves only when a
+            // score passes it by more than 8 (so p <= 256, well inside fp16)
+            const bool interior = t0 >= full_lo && t0 + kTile <= full_hi;
+            float pv[RTW][2][4];
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt) {
+                float smax = -INFINITY;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float x = sv[rt][h][i];
+                        if (!interior) {
+                            const int j = t0 + 16 * h + 4 * q4 + i;
+                            x = (j >= vis_lo[rt] && j < vis_hi[rt]) ? x : -INFINITY;
+                        }
+                        sv[rt][h][i] = x;
+                        smax = fmaxf(smax, x);
+                    }
+                if (__any(smax > mrow[rt] + 8.0f)) {   // -inf never passes
+                    float mt = fmaxf(smax, __shfl_xor(smax, 16));
+                    mt = fmaxf(mt, __shfl_xor(mt, 32));
+                    const bool move = mt > mrow[rt] + 8.0f;
+                    const float alpha = move ? __builtin_amdgcn_exp2f(mrow[rt] - mt) : 1.0f;
+                    mrow[rt] = move ? mt : mrow[rt];
+                    lsum[rt] *= alpha;
+                    float ar[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * q4 + i);   // O rows 4*q4 + i
+#pragma unroll
+                    for (int dt = 0; dt < 2 * NB; ++dt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) oacc[rt][dt][i] *= ar[i];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) macc[rt][i] *= ar[i];
+                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float pe = (mrow[rt] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sv[rt][h][i] - mrow[rt]);
+                        pv[rt][h][i] = pe;
+                        lsum[rt] += pe;
+                    }
+            }
+
+            // ---- P V with the V codes built from the q5_1 bytes of 8 keys per lane group
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk) {
+                const uint8_t* vb = rv + vkey * WN::VSTR + blk * 24 + 8 * (j16 & 1);
+                const i2 nib = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(vb + 8));   // nibble bytes
+                const i2 hdr = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(vb));       // d, m, high bits
+                // high-bit byte of dims 8*(j16>>3).. (first half) and 16 + 8*(j16>>3).. (second
+                // half).  Every lane runs all four broadcasts before selecting: a DPP read
+                // from a lane that is inactive (as in a divergent branch) returns 0.
+                uint32_t bc[2][4];
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    bc[k][0] = bcast_row((uint32_t)hdr[k], 4);
+                    bc[k][1] = bcast_row((uint32_t)hdr[k], 5);
+                    bc[k][2] = bcast_row((uint32_t)hdr[k], 6);
+                    bc[k][3] = bcast_row((uint32_t)hdr[k], 7);
+                }
+                const bool hi8 = j16 >= 8;
+                const uint32_t qa0 = hi8 ? bc[0][1] : bc[0][0], qa1 = hi8 ? bc[1][1] : bc[1][0];
+                const uint32_t qb0 = hi8 ? bc[0][3] : bc[0][2], qb1 = hi8 ? bc[1][3] : bc[1][2];
+                const int sh = j16 & 7;
+                const uint32_t c00 = ((uint32_t)nib[0] & 0x0F0F0F0Fu) | (((qa0 >> sh) & 0x01010101u) << 4);
+                const uint32_t c01 = ((uint32_t)nib[1] & 0x0F0F0F0Fu) | (((qa1 >> sh) & 0x01010101u) << 4);
+                const uint32_t c10 = (((uint32_t)nib[0] >> 4) & 0x0F0F0F0Fu) | (((qb0 >> sh) & 0x01010101u) << 4);
+                const uint32_t c11 = (((uint32_t)nib[1] >> 4) & 0x0F0F0F0Fu) | (((qb1 >> sh) & 0x01010101u) << 4);
+                const h8 vf0 = dec::v_codes_f16(c00, c01);
+                const h8 vf1 = dec::v_codes_f16(c10, c11);
+                const float4 d0 = *reinterpret_cast<const float4*>(VDa + blk * kTile + 4 * q4);
+                const float4 d1 = *reinterpret_cast<const float4*>(VDa + blk * kTile + 16 + 4 * q4);
+#pragma unroll
+                for (int rt = 0; rt < RTW; ++rt) {
+                    const h8 pa = {(_Float16)(pv[rt][0][0] * d0.x), (_Float16)(pv[rt][0][1] * d0.y),
+                                   (_Float16)(pv[rt][0][2] * d0.z), (_Float16)(pv[rt][0][3] * d0.w),
+                                   (_Float16)(pv[rt][1][0] * d1.x), (_Float16)(pv[rt][1][1] * d1.y),
+                                   (_Float16)(pv[rt][1][2] * d1.z), (_Float16)(pv[rt][1][3] * d1.w)};
+                    oacc[rt][2 * blk] = dec::mfma(pa, vf0, oacc[rt][2 * blk]);
+                    oacc[rt][2 * blk + 1] = dec::mfma(pa, vf1, oacc[rt][2 * blk + 1]);
+                }
+                if (NB > 4) asm volatile("" ::: "memory");
+            }
+            // q5_1 offset term: macc[rt][row][blk] += sum_key P[row][key] * m[key][blk]
+            {
+                const h8 mb = dec::tr16_pair(wb + WN::VM + (mk0 * WN::VMS + 4 * mc) * 2,
+                                             wb + WN::VM + (mk1 * WN::VMS + 4 * mc) * 2);
+#pragma unroll
+                for (int rt = 0; rt < RTW; ++rt) {
+                    const h8 pu = {(_Float16)pv[rt][0][0], (_Float16)pv[rt][0][1], (_Float16)pv[rt][0][2],
+                                   (_Float16)pv[rt][0][3], (_Float16)pv[rt][1][0], (_Float16)pv[rt][1][1],
+                                   (_Float16)pv[rt][1][2], (_Float16)pv[rt][1][3]};
+                    macc[rt] = dec::mfma(pu, mb, macc[rt]);
+                }
+            }
+        }
+        if (it + 2 < nt) {
+            // every LDS read of this buffer has returned before it is refilled
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+            issue(c0 + (it + 2) * WN::TR, it & 1);
+        }
+    }
+
+    // ---- finish: row sums over the four lane groups; offsets into O; partials
+    const size_t row0 = ((size_t)b * p.splits + s) * p.T;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+        float l = lsum[rt];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+#pragma unroll
+        for (int dt = 0; dt < 2 * NB; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) oacc[rt][dt][i] += __shfl(macc[rt][i], 16 * q4 + dt / 2);
+        const int r = rt * 16 + j16;
+        if (q4 == 0 && r < R) {
+            const int t = r / p.hpk, hq = g * p.hpk + r % p.hpk;
+            const size_t idx = (row0 + t) * p.H + hq;
+            p.part_ml[2 * idx] = (mrow[rt] == -INFINITY) ? -INFINITY : mrow[rt] * kLn2;
+            p.part_ml[2 * idx + 1] = l;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ro = rt * 16 + 4 * q4 + i;
+            if (ro < R) {
+                const int t = ro / p.hpk, hq = g * p.hpk + ro % p.hpk;
+                float* o = p.part_o + ((row0 + t) * p.H + hq) * HD + j16;
+#pragma unroll
+                for (int dt = 0; dt < 2 * NB; ++dt) o[16 * dt] = oacc[rt][dt][i];
+            }
+        }
+    }
+}
+
+}  // namespace stream

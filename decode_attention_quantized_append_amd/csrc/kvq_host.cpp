@@ -32,9 +32,9 @@ struct kvq_cache {
     std::vector<int64_t> len;    // host mirror of len_d
     std::vector<int64_t> base;   // host mirror of base_d
     int32_t split_rows;
-    int32_t head_group;          // decode tiling: 0 automatic, -1 one KV head per workgroup,
-                                 // k > 0 whole-row kernel with k heads per workgroup
-    int32_t sub_tiles;           // whole-row kernel: rows per buffer / 32 (0 automatic)
+    int32_t decode_kernel;       // kvq_decode_kernel (KVQ_DECODE_AUTO: chosen per call)
+    int32_t head_group;          // KV heads per workgroup (0: chosen per call)
+    int32_t sub_tiles;           // whole-row kernel: rows per buffer / 32 (0: chosen per call)
 };
 
 namespace {
@@ -81,7 +81,10 @@ void sizes_of(const kvq_config* c, kvq_sizes* s) {
     s->v_row_bytes = (size_t)(blocks * 24);
     s->k_session_stride = (size_t)round_up((int64_t)s->k_row_bytes * c->capacity, 256);
     s->v_session_stride = (size_t)round_up((int64_t)s->v_row_bytes * c->capacity, 256);
-    s->k_planes_bytes = s->k_session_stride * (size_t)c->n_seqs;
+    // + a 256-byte tail: the decode reads each KV head's q8_0 blocks from the
+    // 16-byte boundary at or below them, up to 12 bytes past the last head's
+    // blocks of a row
+    s->k_planes_bytes = s->k_session_stride * (size_t)c->n_seqs + 256;
     s->v_planes_bytes = s->v_session_stride * (size_t)c->n_seqs;
     s->counters_bytes = (size_t)round_up(((int64_t)2 * c->n_seqs + 4) * 4, 256);
 }
@@ -114,10 +117,13 @@ int64_t visible_lo(const kvq_cache* h, int64_t len, int32_t T) {
 }
 
 struct Plan {
+    int32_t kernel;    // kvq::DecodeKernel
     int32_t chunk;
     int32_t splits;
-    int32_t gh;        // 0: one KV head per workgroup; > 0: whole-row kernel
-    int32_t sub;
+    int32_t gh;        // KV heads per workgroup (whole-row and stream kernels)
+    int32_t sub;       // whole-row kernel: rows per buffer / 32
+    int32_t lds;       // dynamic LDS bytes
+    int32_t rows;      // rows per buffer (chunks are a multiple)
     kvq::RowGeo geo;
     size_t ml_bytes;
     size_t o_bytes;
@@ -141,6 +147,16 @@ bool rows_ok(const kvq_config& c, int R, int gh, int sub, kvq::RowGeo* geo) {
     return true;
 }
 
+// Is the per-wave stream kernel built for gh heads (one wave each) at this shape?
+bool stream_ok(const kvq_config& c, int R, int gh) {
+    const int NB = c.head_dim / 32;
+    if (NB != 2 && NB != 4 && NB != 8) return false;
+    if (gh < 1 || c.n_kv_heads % gh != 0) return false;
+    const int RT = (R + 15) / 16;
+    if (gh > (RT == 1 ? 8 : 4)) return false;
+    return gh * kvq::stream_wave_bytes(NB) <= kvq::kLdsBytes;
+}
+
 // Is every session's first visible row, rounded down to 32, still resident?
 bool aligned_start_resident(const kvq_cache* h, int32_t T) {
     for (int b = 0; b < h->cfg.n_seqs; ++b)
@@ -154,7 +170,61 @@ int64_t span_of(const kvq_cache* h, int b, int32_t T) {
     return std::max<int64_t>(0, h->len[b] - (visible_lo(h, h->len[b], T) & ~int64_t(31)));
 }
 
-Plan make_plan(const kvq_cache* h, int32_t T) {
+// Chooses the decode kernel and its tiling.  Returns false when a kernel or
+// tiling set with kvq_set_decode_tiling does not fit the shape.
+bool choose_kernel(const kvq_cache* h, int R, int32_t T, Plan* p) {
+    const kvq_config& c = h->cfg;
+    const int NB = c.head_dim / 32;
+    const int RT = (R + 15) / 16;
+    p->kernel = kvq::kPerHead;
+    p->gh = 0;
+    p->sub = 0;
+    p->lds = 0;
+    p->rows = 256;
+    int want = h->decode_kernel;
+    if (want == KVQ_DECODE_AUTO) want = (NB == 2 || NB == 4 || NB == 8) ? KVQ_DECODE_STREAM : KVQ_DECODE_PER_HEAD;
+    if (want == KVQ_DECODE_PER_HEAD) return true;
+    // The whole-row and stream kernels start a session's first buffer at the
+    // first visible row rounded down to 32 and read it whole, so that row
+    // must still be resident (at or above base); else one KV head per
+    // workgroup, whose loads clamp rows to the visible range.
+    if (!aligned_start_resident(h, T)) return true;
+    if (want == KVQ_DECODE_STREAM) {
+        int gh = h->head_group;
+        if (gh == 0)
+            for (int k = std::min(c.n_kv_heads, 8); k >= 1 && gh == 0; --k)
+                if (stream_ok(c, R, k)) gh = k;
+        if (!stream_ok(c, R, gh)) return h->decode_kernel == KVQ_DECODE_AUTO;
+        p->kernel = kvq::kStream;
+        p->gh = gh;
+        p->lds = gh * kvq::stream_wave_bytes(NB);
+        p->rows = kvq::stream_rows_per_buffer(NB);
+        return true;
+    }
+    // whole-row: the largest head group whose buffers carry >= 48 KB (the
+    // load in flight per workgroup while the other buffer is computed)
+    const int gh0 = h->head_group, sub0 = h->sub_tiles;
+    for (int gh = gh0 ? gh0 : std::min(c.n_kv_heads, 8); gh >= 1; --gh) {
+        for (int sub : {1, 2, 4}) {
+            kvq::RowGeo g;
+            if (sub0 > 0 && sub != sub0) continue;
+            if (!rows_ok(c, R, gh, sub, &g)) continue;
+            if (sub0 == 0 && g.RAWB < 48 * 1024 && sub < 4 && rows_ok(c, R, gh, sub * 2, nullptr)) continue;
+            p->kernel = kvq::kWholeRow;
+            p->gh = gh;
+            p->sub = sub;
+            p->geo = g;
+            p->lds = g.lds;
+            p->rows = g.TRB;
+            return true;
+        }
+        if (gh0) break;
+    }
+    (void)RT;
+    return false;
+}
+
+Plan make_plan(const kvq_cache* h, int32_t T, bool* fits = nullptr) {
     const kvq_config& c = h->cfg;
     const int R = T * (c.n_q_heads / c.n_kv_heads);
     int64_t total = 0, maxvis = 1;
@@ -164,52 +234,29 @@ Plan make_plan(const kvq_cache* h, int32_t T) {
         maxvis = std::max(maxvis, vis);
     }
     Plan p{};
-    // kernel and tiling.  The whole-row kernel starts a session's first buffer
-    // at the first visible row rounded down to 32 and reads it whole, so that
-    // row must still be resident (at or above base).
-    if (!aligned_start_resident(h, T)) {
-        // one KV head per workgroup: its loads clamp rows to the visible range
-    } else if (h->head_group > 0) {
-        const int sub = h->sub_tiles > 0 ? h->sub_tiles : 1;
-        if (rows_ok(c, R, h->head_group, sub, &p.geo)) {
-            p.gh = h->head_group;
-            p.sub = sub;
-        }
-    } else if (h->head_group == 0 && R > 16) {
-        // whole-row workgroups where the group has two row tiles (verify
-        // rows); one KV head per workgroup is faster below that.  The largest
-        // head group whose buffers carry >= 48 KB (the load in flight per
-        // workgroup while the other buffer is computed)
-        for (int gh = std::min(c.n_kv_heads, 8); gh >= 1 && p.gh == 0; --gh)
-            for (int sub : {1, 2, 4}) {
-                kvq::RowGeo g;
-                if (h->sub_tiles > 0 && sub != h->sub_tiles) continue;
-                if (!rows_ok(c, R, gh, sub, &g)) continue;
-                if (g.RAWB < 48 * 1024 && sub < 4 && rows_ok(c, R, gh, sub * 2, nullptr)) continue;
-                p.gh = gh;
-                p.sub = sub;
-                p.geo = g;
-                break;
-            }
-    }
+    const bool ok = choose_kernel(h, R, T, &p);
+    if (fits) *fits = ok;
     int64_t chunk = h->split_rows;
-    if (p.gh > 0) {
+    if (p.kernel != kvq::kPerHead) {
         if (chunk <= 0) {
             // one round of workgroups: as many as fit on the 256 CUs at once
-            // (LDS-bound), each a whole number of buffers
+            // (bound by LDS and by the waves the register file holds), each a
+            // whole number of buffers
             const int64_t ngrp = c.n_kv_heads / p.gh;
-            const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kvq::kLdsBytes / p.geo.lds,
-                                                                           8 / (p.gh * ((R + 15) / 16))));
+            const int64_t waves_per_wg = p.kernel == kvq::kStream ? p.gh : p.gh * ((R + 15) / 16);
+            const int64_t waves_per_cu = (p.kernel == kvq::kStream && R > 16) ? 4 : 8;
+            const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kvq::kLdsBytes / p.lds,
+                                                                           waves_per_cu / waves_per_wg));
             const int64_t slots = 256 * per_cu;
-            chunk = round_up(std::max<int64_t>(1, ceil_div(total * ngrp, slots)), p.geo.TRB);
+            chunk = round_up(std::max<int64_t>(1, ceil_div(total * ngrp, slots)), p.rows);
             for (;;) {
                 int64_t wgs = 0;
                 for (int b = 0; b < c.n_seqs; ++b) wgs += ceil_div(span_of(h, b, T), chunk) * ngrp;
                 if (wgs <= slots) break;
-                chunk += p.geo.TRB;
+                chunk += p.rows;
             }
         }
-        chunk = round_up(chunk, p.geo.TRB);
+        chunk = round_up(chunk, p.rows);
     } else if (chunk <= 0) {
         // About 2048 workgroups of (session, chunk, KV head), i.e. several per
         // CU so that the last round is a small fraction of the work, but at
@@ -221,7 +268,7 @@ Plan make_plan(const kvq_cache* h, int32_t T) {
         chunk = round_up(chunk, 256);   // whole rounds of 4 waves x 32 rows x 2 prefetched tiles
     }
     // at most kMaxSplits chunks per session
-    chunk = std::max<int64_t>(chunk, round_up(ceil_div(maxvis, kvq::kMaxSplits), p.gh > 0 ? p.geo.TRB : 64));
+    chunk = std::max<int64_t>(chunk, round_up(ceil_div(maxvis, kvq::kMaxSplits), p.rows));
     p.chunk = (int32_t)chunk;
     p.splits = (int32_t)std::max<int64_t>(1, ceil_div(maxvis, chunk));
     int64_t entries = (int64_t)c.n_seqs * p.splits * T * c.n_q_heads;
@@ -261,6 +308,7 @@ kvq_status kvq_create(const kvq_config* cfg, void* k_planes, void* v_planes,
     h->len.assign(cfg->n_seqs, 0);
     h->base.assign(cfg->n_seqs, 0);
     h->split_rows = 0;
+    h->decode_kernel = KVQ_DECODE_AUTO;
     h->head_group = 0;
     h->sub_tiles = 0;
     int n = 2 * cfg->n_seqs + 4;
@@ -416,9 +464,9 @@ kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, c
         if (visible_lo(h, h->len[b], T) < h->base[b])
             return fail(KVQ_ERANGE, "session " + std::to_string(b) + ": visible rows were rebased away");
     }
-    Plan p = make_plan(h, T);
-    if (h->head_group > 0 && p.gh == 0 && aligned_start_resident(h, T))
-        return fail(KVQ_EINVAL, "the decode tiling set with kvq_set_decode_tiling does not fit this shape");
+    bool fits = true;
+    Plan p = make_plan(h, T, &fits);
+    if (!fits) return fail(KVQ_EINVAL, "the decode tiling set with kvq_set_decode_tiling does not fit this shape");
     if (!ws || ws_bytes < p.ml_bytes + p.o_bytes) return fail(KVQ_EINVAL, "workspace missing or too small");
     if (!aligned(ws, 256)) return fail(KVQ_EINVAL, "workspace must be 256-byte aligned");
     kvq::DecodeParams dp{};
@@ -441,8 +489,10 @@ kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, c
     dp.base_d = base_d(h);
     dp.chunk = p.chunk;
     dp.splits = p.splits;
+    dp.kernel = p.kernel;
     dp.gh = p.gh;
     dp.sub = p.sub;
+    dp.lds = p.lds;
     dp.geo = p.geo;
     dp.scale = scale;
     dp.part_ml = static_cast<float*>(ws);
@@ -485,12 +535,16 @@ kvq_status kvq_set_split_rows(kvq_cache* h, int32_t rows) {
     return KVQ_OK;
 }
 
-kvq_status kvq_set_decode_tiling(kvq_cache* h, int32_t head_group, int32_t sub_tiles) {
+kvq_status kvq_set_decode_tiling(kvq_cache* h, int32_t kernel, int32_t head_group, int32_t sub_tiles) {
     if (!h) return fail(KVQ_EINVAL, "handle is NULL");
-    if (head_group < -1 || (head_group > 0 && h->cfg.n_kv_heads % head_group != 0))
-        return fail(KVQ_EINVAL, "head_group must be -1, 0 or a divisor of n_kv_heads");
-    if (sub_tiles != 0 && sub_tiles != 1 && sub_tiles != 2 && sub_tiles != 4)
-        return fail(KVQ_EINVAL, "sub_tiles must be 0, 1, 2 or 4");
+    if (kernel < KVQ_DECODE_AUTO || kernel > KVQ_DECODE_STREAM) return fail(KVQ_EINVAL, "unknown decode kernel");
+    if (head_group < 0 || (head_group > 0 && h->cfg.n_kv_heads % head_group != 0))
+        return fail(KVQ_EINVAL, "head_group must be 0 or a divisor of n_kv_heads");
+    if (head_group > 0 && kernel != KVQ_DECODE_WHOLE_ROW && kernel != KVQ_DECODE_STREAM)
+        return fail(KVQ_EINVAL, "head_group applies to the whole-row and stream kernels");
+    if (sub_tiles != 0 && (kernel != KVQ_DECODE_WHOLE_ROW || (sub_tiles != 1 && sub_tiles != 2 && sub_tiles != 4)))
+        return fail(KVQ_EINVAL, "sub_tiles must be 0, or 1, 2 or 4 for the whole-row kernel");
+    h->decode_kernel = kernel;
     h->head_group = head_group;
     h->sub_tiles = sub_tiles;
     return KVQ_OK;

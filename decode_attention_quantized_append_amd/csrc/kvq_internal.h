@@ -107,6 +107,43 @@ inline RowGeo row_geo(int gh, int NB, int sub) {
     return g;
 }
 
+// Geometry of the per-wave stream decode kernel for head_dim = 32 * NB (NB
+// even): each wave copies its KV head's row windows, in 16-byte pieces, into
+// a private double buffer, then builds per-tile scale arrays.
+template <int NB>
+struct StreamWin {
+    static constexpr int MAXKOFS = (NB % 8 == 0) ? 0 : (NB % 4 == 0) ? 8 : 12;   // (g*NB*34) mod 16, at most
+    static constexpr int KW = (MAXKOFS + 34 * NB + 15) / 16;   // K pieces per row window
+    static constexpr int KWP = KW | 1;                          // LDS row stride in pieces (odd)
+    static constexpr int VW = 24 * NB / 16;                     // V pieces per row
+    static constexpr int VWP = VW | 1;
+    static constexpr int SUB = NB <= 2 ? 2 : 1;                 // 32-row tiles per buffer
+    static constexpr int TR = kRowTile * SUB;                   // rows per buffer
+    static constexpr int KSTR = KWP * 16, VSTR = VWP * 16;
+    static constexpr int NKI = (TR * KWP + 63) / 64;            // load instructions per buffer
+    static constexpr int NVI = (TR * VWP + 63) / 64;
+    static constexpr int NL = NKI + NVI;
+    static constexpr int SLOT = TR * (KSTR + VSTR);             // bytes per buffer
+    static constexpr int VMS = NB < 4 ? 4 : NB;
+    static constexpr int KS = 2 * SLOT;                         // f32 [NB][32] K scales * scale * log2 e
+    static constexpr int VD = KS + NB * kRowTile * 4;           // f32 [NB][32] V steps
+    static constexpr int VM = VD + NB * kRowTile * 4;           // fp16 [32][VMS] V offsets
+    static constexpr int BYTES = VM + kRowTile * VMS * 2;       // per wave
+    static_assert(NL <= 32, "load count must fit vmcnt");
+};
+
+inline int stream_wave_bytes(int NB) {
+    switch (NB) {
+        case 2: return StreamWin<2>::BYTES;
+        case 4: return StreamWin<4>::BYTES;
+        case 8: return StreamWin<8>::BYTES;
+        default: return 0;
+    }
+}
+inline int stream_rows_per_buffer(int NB) { return NB <= 2 ? 2 * kRowTile : kRowTile; }
+
+enum DecodeKernel : int32_t { kPerHead = 0, kWholeRow = 1, kStream = 2 };
+
 // Split-K decode plus the log-sum-exp combine.
 struct DecodeParams {
     const void* q;              // [B, T, H, hd]
@@ -123,9 +160,10 @@ struct DecodeParams {
     int32_t chunk;              // rows per split (multiple of kSplitQuantum); chunks
                                 // start at the first visible row rounded down to 32
     int32_t splits;             // split slots per session
-    int32_t gh;                 // > 0: whole-row kernel with gh KV heads per workgroup;
-                                // 0: one KV head per workgroup
+    int32_t kernel;             // DecodeKernel
+    int32_t gh;                 // KV heads per workgroup (whole-row and stream kernels)
     int32_t sub;                // whole-row kernel: rows per buffer / 32
+    int32_t lds;                // dynamic LDS bytes of the decode workgroup
     RowGeo geo;                 // whole-row kernel geometry
     float scale;
     float* part_ml;             // [B, splits, T, H, 2]  running max, running sum

@@ -191,6 +191,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 // ---------------------------------------------------------------------------
 #include "kvq_decode.hip"
 #include "kvq_decode_rows.hip"
+#include "kvq_decode_stream.hip"
 
 // One workgroup per (session, row t, Q head h): fold the session's split
 // partials (m in natural-log units, l, o), adding the sink once as a
@@ -331,10 +332,37 @@ int launch_rows_t(const DecodeParams& p, hipStream_t st, const char** err) {
     }
     const int items = p.B * p.splits * (p.Hkv / p.gh);
     const int grid = (items + 7) & ~7;
-    hipLaunchKernelGGL((rows::decode_rows<NB, RT, QLO>), dim3(grid), dim3(64 * p.gh * RT), p.geo.lds, st, p);
+    hipLaunchKernelGGL((rows::decode_rows<NB, RT, QLO>), dim3(grid), dim3(64 * p.gh * RT), p.lds, st, p);
     if (check(err)) return 1;
     hipLaunchKernelGGL(combine_kernel, dim3(p.B * p.T * p.H), dim3(kCombineThreads), 0, st, p);
     return check(err);
+}
+
+template <int NB, int RTW, bool QLO>
+int launch_stream_t(const DecodeParams& p, hipStream_t st, const char** err) {
+    static bool configured = false;
+    if (!configured) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&stream::decode_stream<NB, RTW, QLO>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) != hipSuccess) {
+            *err = "cannot raise the LDS limit of the decode kernel";
+            return 1;
+        }
+        configured = true;
+    }
+    const int items = p.B * p.splits * (p.Hkv / p.gh);
+    const int grid = (items + 7) & ~7;
+    hipLaunchKernelGGL((stream::decode_stream<NB, RTW, QLO>), dim3(grid), dim3(64 * p.gh), p.lds, st, p);
+    if (check(err)) return 1;
+    hipLaunchKernelGGL(combine_kernel, dim3(p.B * p.T * p.H), dim3(kCombineThreads), 0, st, p);
+    return check(err);
+}
+
+template <int NB>
+int launch_stream_nb(const DecodeParams& p, hipStream_t st, const char** err) {
+    const int R = p.T * p.hpk;
+    const bool qlo = p.dtype == 0;
+    if (R <= 16) return qlo ? launch_stream_t<NB, 1, true>(p, st, err) : launch_stream_t<NB, 1, false>(p, st, err);
+    return qlo ? launch_stream_t<NB, 2, true>(p, st, err) : launch_stream_t<NB, 2, false>(p, st, err);
 }
 
 template <int NB>
@@ -377,12 +405,20 @@ int launch_append(const AppendParams& p, void* stream, const char** err) {
 
 int launch_decode(const DecodeParams& p, void* stream, const char** err) {
     hipStream_t st = (hipStream_t)stream;
-    if (p.gh > 0) {
+    if (p.kernel == kWholeRow) {
         switch (p.hd / 32) {
             case 2: return launch_rows_nb<2>(p, st, err);
             case 4: return launch_rows_nb<4>(p, st, err);
             case 8: return launch_rows_nb<8>(p, st, err);
             default: *err = "the whole-row decode supports head_dim 64, 128 and 256"; return 1;
+        }
+    }
+    if (p.kernel == kStream) {
+        switch (p.hd / 32) {
+            case 2: return launch_stream_nb<2>(p, st, err);
+            case 4: return launch_stream_nb<4>(p, st, err);
+            case 8: return launch_stream_nb<8>(p, st, err);
+            default: *err = "the stream decode supports head_dim 64, 128 and 256"; return 1;
         }
     }
     switch (p.hd / 32) {

@@ -52,8 +52,8 @@ int launch_decode(const DecodeParams& p, void*, const char** err) {
     std::string s = "decode T=" + std::to_string(p.T) + " chunk=" + std::to_string(p.chunk) +
                     " splits=" + std::to_string(p.splits) + " ml_to_o=" +
                     std::to_string((const char*)p.part_o - (const char*)p.part_ml) +
-                    " gh=" + std::to_string(p.gh) + " sub=" + std::to_string(p.sub) +
-                    " lds=" + std::to_string(p.geo.lds);
+                    " kernel=" + std::to_string(p.kernel) + " gh=" + std::to_string(p.gh) +
+                    " sub=" + std::to_string(p.sub) + " lds=" + std::to_string(p.lds);
     return record(s, err);
 }
 

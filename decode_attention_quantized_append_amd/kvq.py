@@ -21,6 +21,7 @@ NODEV_PATH = os.path.join(_PKG, "libkvq_nodev.so")
 KVQ_OK, KVQ_EINVAL, KVQ_ECAPACITY, KVQ_ERANGE, KVQ_EUNSUPPORTED, KVQ_EDEVICE = range(6)
 KVQ_F32, KVQ_BF16 = 0, 1
 KVQ_FMT_Q8_0, KVQ_FMT_Q5_1 = 1, 2
+KVQ_DECODE_AUTO, KVQ_DECODE_PER_HEAD, KVQ_DECODE_WHOLE_ROW, KVQ_DECODE_STREAM = range(4)
 STATUS_NAMES = {0: "KVQ_OK", 1: "KVQ_EINVAL", 2: "KVQ_ECAPACITY", 3: "KVQ_ERANGE",
                 4: "KVQ_EUNSUPPORTED", 5: "KVQ_EDEVICE"}
 
@@ -70,7 +71,7 @@ def _declare(lib):
         "kvq_decode": (st, [vp, vp, i32, i32, vp, f32, vp, vp, vp, ctypes.c_size_t, vp]),
         "kvq_truncate": (st, [vp, i32p, vp]),
         "kvq_set_split_rows": (st, [vp, i32]),
-        "kvq_set_decode_tiling": (st, [vp, i32, i32]),
+        "kvq_set_decode_tiling": (st, [vp, i32, i32, i32]),
         "kvq_info": (st, [vp, ctypes.POINTER(kvq_info_t)]),
         "kvq_host_lengths": (st, [vp, i64p, i64p]),
         "kvq_destroy": (None, [vp]),
@@ -170,9 +171,9 @@ def kvq_truncate(h: int, new_len: Sequence[int], stream: int = 0, lib=None) -> N
     _check(lib, lib.kvq_truncate(h, _i32_array(new_len), stream or None))
 
 
-def kvq_set_decode_tiling(h: int, head_group: int, sub_tiles: int = 0, lib=None) -> None:
+def kvq_set_decode_tiling(h: int, kernel: int, head_group: int = 0, sub_tiles: int = 0, lib=None) -> None:
     lib = lib or load()
-    _check(lib, lib.kvq_set_decode_tiling(h, head_group, sub_tiles))
+    _check(lib, lib.kvq_set_decode_tiling(h, kernel, head_group, sub_tiles))
 
 
 def kvq_set_split_rows(h: int, rows: int, lib=None) -> None:
@@ -284,8 +285,8 @@ class KvqLayerCache:
     def set_split_rows(self, rows):
         kvq_set_split_rows(self.h, rows, self.lib)
 
-    def set_decode_tiling(self, head_group, sub_tiles=0):
-        kvq_set_decode_tiling(self.h, head_group, sub_tiles, self.lib)
+    def set_decode_tiling(self, kernel, head_group=0, sub_tiles=0):
+        kvq_set_decode_tiling(self.h, kernel, head_group, sub_tiles, self.lib)
 
     def host_lengths(self):
         return kvq_host_lengths(self.h, self.cfg.n_seqs, self.lib)
@@ -294,9 +295,9 @@ class KvqLayerCache:
         """(K, V) uint8 device views [B, capacity, row_bytes] of the physical planes."""
         s = self.sizes
         B, cap = self.cfg.n_seqs, self.cfg.capacity
-        k = self.k_planes.view(B, s.k_session_stride)[:, :cap * s.k_row_bytes].reshape(B, cap, s.k_row_bytes)
-        v = self.v_planes.view(B, s.v_session_stride)[:, :cap * s.v_row_bytes].reshape(B, cap, s.v_row_bytes)
-        return k, v
+        k = self.k_planes[:B * s.k_session_stride].view(B, s.k_session_stride)[:, :cap * s.k_row_bytes]
+        v = self.v_planes[:B * s.v_session_stride].view(B, s.v_session_stride)[:, :cap * s.v_row_bytes]
+        return k.reshape(B, cap, s.k_row_bytes), v.reshape(B, cap, s.v_row_bytes)
 
     def close(self):
         if getattr(self, "h", None):

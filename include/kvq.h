@@ -92,7 +92,8 @@ typedef struct kvq_config {
 
 /* Device bytes the caller must provide for a configuration. */
 typedef struct kvq_sizes {
-    size_t k_planes_bytes;    /* n_seqs * k_session_stride */
+    size_t k_planes_bytes;    /* n_seqs * k_session_stride + 256 (read-only tail the
+                                 decode may read past the last row; never written) */
     size_t v_planes_bytes;    /* n_seqs * v_session_stride */
     size_t counters_bytes;    /* int32 len_d[B], base_d[B], then library scratch */
     size_t k_row_bytes;       /* Hkv*hd/32*34 */
@@ -181,14 +182,24 @@ kvq_status kvq_truncate(kvq_cache* h, const int32_t* new_len, kvq_stream stream)
  * rounding.  Errors: EINVAL. */
 kvq_status kvq_set_split_rows(kvq_cache* h, int32_t rows);
 
-/* Tuning: how kvq_decode tiles the cache.  head_group = 0 lets each call
- * choose; -1 selects one KV head per workgroup; k > 0 selects workgroups that
- * stream whole row segments of k adjacent KV heads (k must divide n_kv_heads;
- * head_dim 64, 128 or 256), with buffers of 32 * sub_tiles rows (sub_tiles 1,
- * 2 or 4; 0 = chosen per call).  A k that does not fit a call's shape makes
- * that kvq_decode fail with EINVAL.  The result does not depend on the tiling
- * beyond float rounding.  Errors: EINVAL. */
-kvq_status kvq_set_decode_tiling(kvq_cache* h, int32_t head_group, int32_t sub_tiles);
+/* Decode kernels (kvq_set_decode_tiling). */
+typedef enum kvq_decode_kernel {
+    KVQ_DECODE_AUTO = 0,        /* chosen per call */
+    KVQ_DECODE_PER_HEAD = 1,    /* one KV head per workgroup, any head_dim */
+    KVQ_DECODE_WHOLE_ROW = 2,   /* workgroups stream whole row segments of adjacent KV heads */
+    KVQ_DECODE_STREAM = 3       /* one KV head per wave, each wave streaming its own rows */
+} kvq_decode_kernel;
+
+/* Tuning: which kernel kvq_decode runs and how it tiles the cache.
+ * head_group: KV heads per workgroup for the whole-row and stream kernels (a
+ * divisor of n_kv_heads), 0 = chosen per call.  sub_tiles: rows per buffer /
+ * 32 for the whole-row kernel (1, 2 or 4), 0 = chosen per call.  The
+ * whole-row and stream kernels need head_dim 64, 128 or 256; a kernel or
+ * tiling that does not fit a call's shape makes that kvq_decode fail with
+ * EINVAL, except that a session whose first visible row, rounded down to 32,
+ * was rebased away is served by the per-head kernel.  The result does not
+ * depend on the choice beyond float rounding.  Errors: EINVAL. */
+kvq_status kvq_set_decode_tiling(kvq_cache* h, int32_t kernel, int32_t head_group, int32_t sub_tiles);
 
 /* Copies the handle's configuration, sizes and buffer pointers. */
 kvq_status kvq_info(const kvq_cache* h, kvq_info_t* out);

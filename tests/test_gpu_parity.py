@@ -146,35 +146,39 @@ def test_decode_split_invariance():
     p.decode(q, scale)
 
 
-# Whole-row decode tilings (KV heads per workgroup, rows per buffer / 32) that
-# fit each shape; the automatic choice is covered by test_decode_parity.
+# Decode kernels and tilings (kernel, KV heads per workgroup, rows per
+# buffer / 32) that fit each shape; the automatic choice is covered by
+# test_decode_parity.
+PH, WR, ST = kvq.KVQ_DECODE_PER_HEAD, kvq.KVQ_DECODE_WHOLE_ROW, kvq.KVQ_DECODE_STREAM
 TILINGS = {
-    "qwen_gqa_small": [(8, 1), (4, 1), (4, 2), (2, 1), (2, 2)],
-    "batched_small": [(8, 1), (4, 2), (2, 1)],
-    "sink_ring_small": [(8, 1), (8, 2), (4, 1), (4, 4)],
-    "verify_small": [(4, 1), (2, 1), (2, 2), (1, 1), (1, 2)],
-    "qwen_f32_small": [(8, 1), (2, 2)],
+    "qwen_gqa_small": [(WR, 8, 1), (WR, 4, 1), (WR, 4, 2), (WR, 2, 1), (WR, 2, 2), (ST, 8, 0), (ST, 2, 0),
+                       (ST, 1, 0)],
+    "batched_small": [(WR, 8, 1), (WR, 4, 2), (WR, 2, 1), (ST, 8, 0), (ST, 4, 0)],
+    "sink_ring_small": [(WR, 8, 1), (WR, 8, 2), (WR, 4, 1), (WR, 4, 4), (ST, 8, 0), (ST, 2, 0)],
+    "verify_small": [(WR, 4, 1), (WR, 2, 1), (WR, 2, 2), (WR, 1, 1), (WR, 1, 2), (ST, 4, 0), (ST, 1, 0)],
+    "qwen_f32_small": [(WR, 8, 1), (WR, 2, 2), (ST, 8, 0), (ST, 4, 0)],
+    "tiny": [(ST, 1, 0)],
 }
 
 
-@pytest.mark.parametrize("name,gh,sub", [(n, g, s) for n, lst in TILINGS.items() for g, s in lst])
-def test_decode_tiling_parity(name, gh, sub):
+@pytest.mark.parametrize("name,kernel,gh,sub", [(n, *t) for n, lst in TILINGS.items() for t in lst])
+def test_decode_tiling_parity(name, kernel, gh, sub):
     p, q, s, scale = build_small(name)
-    p.gpu.set_decode_tiling(gh, sub)
-    p.decode(q, scale, sinks=s, what=f"{name} gh={gh} sub={sub}")
+    p.gpu.set_decode_tiling(kernel, gh, sub)
+    p.decode(q, scale, sinks=s, what=f"{name} kernel={kernel} gh={gh} sub={sub}")
 
 
 @pytest.mark.parametrize("name", sorted(TILINGS))
 def test_decode_tilings_agree(name):
-    """Every tiling, and one KV head per workgroup, give the same outputs up
-    to the fp16 rounding of P (Pair.pv_atol)."""
+    """Every kernel and tiling gives the same outputs up to the fp16 rounding
+    of P (Pair.pv_atol)."""
     p, q, s, scale = build_small(name)
     io = SMALL[name][10]
     qd = to_dev(q, io)
     sd = torch.from_numpy(s).to(DEV) if s is not None else None
     outs = []
-    for gh, sub in [(-1, 0), (0, 0)] + TILINGS[name]:
-        p.gpu.set_decode_tiling(gh, sub)
+    for kernel, gh, sub in [(PH, 0, 0), (kvq.KVQ_DECODE_AUTO, 0, 0)] + TILINGS[name]:
+        p.gpu.set_decode_tiling(kernel, gh, sub)
         for rows_ in (0, 64, 256):
             p.gpu.set_split_rows(rows_)
             o, l = p.gpu.decode(qd, scale, sinks=sd)
@@ -184,18 +188,20 @@ def test_decode_tilings_agree(name):
         np.testing.assert_allclose(l, outs[0][1], atol=1e-5, rtol=1e-5)
 
 
-@pytest.mark.parametrize("step,tiling", [(24, -1), (32, 4), (32, 0)])
+@pytest.mark.parametrize("step,tiling", [(24, (kvq.KVQ_DECODE_PER_HEAD, 0)), (32, (kvq.KVQ_DECODE_WHOLE_ROW, 4)),
+                                         (32, (kvq.KVQ_DECODE_STREAM, 0)), (32, (kvq.KVQ_DECODE_AUTO, 0))])
 def test_ring_equals_flat(step, tiling):
     """The base-offset ring serves the same rows as a flat cache: identical
     live bytes and identical outputs, step after step, through rebases.  Both
-    caches decode with the same kernel (one KV head per workgroup, or whole
-    row segments of 4 heads when the ring's base stays a multiple of 32)."""
+    caches decode with the same kernel (one KV head per workgroup, or the
+    kernels that start at a 32-row boundary when the ring's base stays a
+    multiple of 32)."""
     rng = np.random.default_rng(11)
     B, H, Hkv, hd, W, cap = 2, 16, 4, 64, 40, 96
     ring = Pair(B, H, Hkv, hd, cap, W, step)
     flat = Pair(B, H, Hkv, hd, 2000, W, 0)
-    ring.gpu.set_decode_tiling(tiling)
-    flat.gpu.set_decode_tiling(tiling)
+    ring.gpu.set_decode_tiling(*tiling)
+    flat.gpu.set_decode_tiling(*tiling)
     L = 0
     for it in range(30):
         n = int(rng.integers(1, 33))

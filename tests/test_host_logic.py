@@ -76,7 +76,7 @@ def test_required_bytes(lib):
     s = kvq.kvq_required_bytes(cfg, lib)
     assert (s.k_row_bytes, s.v_row_bytes) == (32 * 34, 32 * 24) == (1088, 768)
     assert s.k_session_stride == -(-1088 * 33000 // 256) * 256
-    assert s.k_planes_bytes == 16 * s.k_session_stride and s.v_planes_bytes == 16 * s.v_session_stride
+    assert s.k_planes_bytes == 16 * s.k_session_stride + 256 and s.v_planes_bytes == 16 * s.v_session_stride
     assert s.counters_bytes >= (2 * 16 + 4) * 4 and s.counters_bytes % 256 == 0
 
 
@@ -268,40 +268,54 @@ def plan_of(lib, h, T=1):
 
 
 def test_decode_kernel_choice(lib):
-    # 8 KV heads x 128, 4 query rows per KV head: one KV head per workgroup;
-    # on request, whole-row workgroups over all 8 heads with 32-row buffers
+    PER_HEAD, WHOLE_ROW, STREAM = 0, 1, 2          # as recorded by the launcher
+    # 8 KV heads x 128: by default one wave per KV head, 8 heads per workgroup
     h = create(lib, n_seqs=1, n_q_heads=32, n_kv_heads=8, head_dim=128, capacity=9000)
     kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 8192, None, 0, lib)
-    assert plan_of(lib, h)["gh"] == 0
-    kvq.kvq_set_decode_tiling(h, 8, 1, lib)
     p = plan_of(lib, h)
-    assert (p["gh"], p["sub"]) == (8, 1) and 0 < p["lds"] <= 160 * 1024 and p["chunk"] % 32 == 0
+    assert (p["kernel"], p["gh"]) == (STREAM, 8) and 0 < p["lds"] <= 160 * 1024 and p["chunk"] % 32 == 0
     assert p["splits"] == -(-8192 // p["chunk"])
-    kvq.kvq_set_decode_tiling(h, -1, 0, lib)           # one KV head per workgroup
-    assert plan_of(lib, h)["gh"] == 0
-    kvq.kvq_set_decode_tiling(h, 4, 2, lib)            # an explicit group and buffer depth
+    kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_PER_HEAD, 0, 0, lib)
+    assert plan_of(lib, h)["kernel"] == PER_HEAD
+    kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_WHOLE_ROW, 8, 1, lib)
     p = plan_of(lib, h)
-    assert (p["gh"], p["sub"]) == (4, 2) and p["chunk"] % 64 == 0
-    assert err(lib, kvq.kvq_set_decode_tiling, h, 3, 0) == kvq.KVQ_EINVAL    # does not divide 8
-    assert err(lib, kvq.kvq_set_decode_tiling, h, 2, 3) == kvq.KVQ_EINVAL    # no such depth
-    assert err(lib, kvq.kvq_set_decode_tiling, h, -2, 0) == kvq.KVQ_EINVAL
-    # one head of 128 is not a whole number of 16-byte pieces: that call fails
-    kvq.kvq_set_decode_tiling(h, 1, 0, lib)
+    assert (p["kernel"], p["gh"], p["sub"]) == (WHOLE_ROW, 8, 1) and p["lds"] <= 160 * 1024
+    kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_WHOLE_ROW, 4, 2, lib)
+    p = plan_of(lib, h)
+    assert (p["kernel"], p["gh"], p["sub"]) == (WHOLE_ROW, 4, 2) and p["chunk"] % 64 == 0
+    kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_STREAM, 2, 0, lib)
+    p = plan_of(lib, h)
+    assert (p["kernel"], p["gh"]) == (STREAM, 2)
+    E = kvq.KVQ_EINVAL
+    assert err(lib, kvq.kvq_set_decode_tiling, h, kvq.KVQ_DECODE_WHOLE_ROW, 3, 0) == E   # does not divide 8
+    assert err(lib, kvq.kvq_set_decode_tiling, h, kvq.KVQ_DECODE_WHOLE_ROW, 2, 3) == E   # no such depth
+    assert err(lib, kvq.kvq_set_decode_tiling, h, kvq.KVQ_DECODE_STREAM, 2, 1) == E      # depth is whole-row only
+    assert err(lib, kvq.kvq_set_decode_tiling, h, kvq.KVQ_DECODE_PER_HEAD, 2, 0) == E    # no head groups there
+    assert err(lib, kvq.kvq_set_decode_tiling, h, 4, 0, 0) == E
+    # one head of 128 is not a whole number of 16-byte pieces for the whole-row kernel: that call fails
+    kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_WHOLE_ROW, 1, 0, lib)
     lib.kvq_nodev_clear()
-    assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 1, None, 0.1, O, None, WS, 1 << 40) == kvq.KVQ_EINVAL
+    assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 1, None, 0.1, O, None, WS, 1 << 40) == E
     assert log(lib) == []
-    # verify rows (T=8, 4 query heads per KV head: 32 rows, two row tiles per head)
+    # verify rows (T=8, 4 query heads per KV head: 32 rows, two row tiles per wave)
     h = create(lib, n_seqs=2, n_q_heads=16, n_kv_heads=4, head_dim=256, capacity=5000)
     kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 4000, None, 0, lib)
     p = plan_of(lib, h, T=8)
-    assert p["gh"] == 4 and p["lds"] <= 160 * 1024
-    # head_dim 96 and a single KV head of 64 have no whole-row kernel
+    assert (p["kernel"], p["gh"]) == (STREAM, 4) and p["lds"] <= 160 * 1024
+    kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_WHOLE_ROW, 0, 0, lib)
+    p = plan_of(lib, h, T=8)
+    assert (p["kernel"], p["gh"]) == (WHOLE_ROW, 4)
+    # head_dim 96 has no whole-row or stream kernel
     h = create(lib, n_seqs=1, n_q_heads=8, n_kv_heads=8, head_dim=96, capacity=100)
     kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 50, None, 0, lib)
-    assert plan_of(lib, h)["gh"] == 0
+    assert plan_of(lib, h)["kernel"] == PER_HEAD
+    kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_STREAM, 0, 0, lib)
+    assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 1, None, 0.1, O, None, WS, 1 << 40) == E
+    # a single KV head of 64: one wave per workgroup
     h = create(lib, n_seqs=1, n_q_heads=4, n_kv_heads=1, head_dim=64, capacity=300)
     kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 256, None, 0, lib)
-    assert plan_of(lib, h)["gh"] == 0
+    p = plan_of(lib, h)
+    assert (p["kernel"], p["gh"]) == (STREAM, 1) and p["chunk"] % 64 == 0
 
 
 def test_decode_ring_start_below_base_falls_back(lib):
@@ -310,16 +324,17 @@ def test_decode_ring_start_below_base_falls_back(lib):
     # used only while that row is still resident
     h = create(lib, n_seqs=1, n_q_heads=32, n_kv_heads=8, head_dim=128, capacity=100, window=90,
                ring_step=10)
-    kvq.kvq_set_decode_tiling(h, 8, 1, lib)
-    seen = set()
-    for _ in range(300):
-        kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 1, None, 0, lib)
-        L, base = lengths(lib, h, 1)
-        lo = max(0, L[0] - 90)
-        gh = plan_of(lib, h)["gh"]
-        assert gh == (8 if (lo & ~31) >= base[0] else 0)
-        seen.add(gh)
-    assert seen == {0, 8}
+    for kernel, want in ((kvq.KVQ_DECODE_WHOLE_ROW, 1), (kvq.KVQ_DECODE_STREAM, 2)):
+        kvq.kvq_set_decode_tiling(h, kernel, 8, 0, lib)
+        seen = set()
+        for _ in range(150):
+            kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 1, None, 0, lib)
+            L, base = lengths(lib, h, 1)
+            lo = max(0, L[0] - 90)
+            k = plan_of(lib, h)["kernel"]
+            assert k == (want if (lo & ~31) >= base[0] else 0)
+            seen.add(k)
+        assert seen == {0, want}
 
 
 def test_launch_failure_reports_edevice_and_keeps_the_mirror(lib):
