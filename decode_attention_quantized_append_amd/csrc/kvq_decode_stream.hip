@@ -13,10 +13,12 @@
 //     HBM, but no wave waits for another: there is no workgroup barrier.
 //   * per 32-row tile, the wave copies its head's K window (the q8_0 blocks,
 //     from the 16-byte boundary at or below them) and V window (the q5_1
-//     blocks) of every row into LDS with global_load_lds_dwordx4, into one of
-//     two buffers: the next buffer is in flight while the wave computes the
-//     current one.  Row strides in LDS are odd numbers of 16-byte pieces,
-//     which keeps 8 consecutive rows on distinct banks.
+//     blocks) of every row into its LDS buffer with global_load_lds_dwordx4.
+//     The next tile's K rows are requested as soon as the scores have read
+//     this tile's, its V rows as soon as P V has read these: each half has a
+//     whole phase of the wave's work to arrive, and the small buffer lets 16
+//     waves share a CU.  Row strides in LDS are odd numbers of 16-byte
+//     pieces, which keeps 8 consecutive rows on distinct banks.
 //   * scores are computed transposed, S^T = K Q^T, one v_mfma_f32_16x16x32_f16
 //     per 32-element block, 16 keys and row tile; the K codes, exact in fp16,
 //     are converted once per tile and feed every row tile.  Each lane ends up
@@ -55,15 +57,15 @@ __device__ __forceinline__ void wait_loads_upto() {
 __device__ __forceinline__ uint32_t bcast_row(uint32_t x, int n) {
     // lane n of each 16-lane row, to every lane of the row (DPP row_newbcast)
     switch (n) {
-        case 4: return __builtin_amdgcn_update_dpp(0, (int)x, 0x154, 0xF, 0xF, false);
-        case 5: return __builtin_amdgcn_update_dpp(0, (int)x, 0x155, 0xF, 0xF, false);
-        case 6: return __builtin_amdgcn_update_dpp(0, (int)x, 0x156, 0xF, 0xF, false);
-        default: return __builtin_amdgcn_update_dpp(0, (int)x, 0x157, 0xF, 0xF, false);
+        case 4: return __builtin_amdgcn_mov_dpp((int)x, 0x154, 0xF, 0xF, true);
+        case 5: return __builtin_amdgcn_mov_dpp((int)x, 0x155, 0xF, 0xF, true);
+        case 6: return __builtin_amdgcn_mov_dpp((int)x, 0x156, 0xF, 0xF, true);
+        default: return __builtin_amdgcn_mov_dpp((int)x, 0x157, 0xF, 0xF, true);
     }
 }
 
 template <int NB, int RTW, bool QLO>
-__global__ __launch_bounds__(RTW == 1 ? 512 : 256) void decode_stream(DecodeParams p) {
+__global__ __launch_bounds__(RTW == 1 ? 512 : 256, stream_waves_per_simd(NB, RTW, QLO)) void decode_stream(DecodeParams p) {
     using WN = Win<NB>;
     constexpr int HD = NB * 32;
     extern __shared__ __align__(16) uint8_t smem[];
@@ -128,13 +130,15 @@ __global__ __launch_bounds__(RTW == 1 ? 512 : 256) void decode_stream(DecodePara
     if (c0 >= c1) return;
 
     uint8_t* const wb = smem + wave * WN::BYTES;
+    const uint8_t* const rk = wb + WN::KB;   // K rows of the tile, stride KSTR
+    const uint8_t* const rv = wb + WN::VB;   // V rows of the tile, stride VSTR
     // This head's windows: K from the 16-byte boundary at or below its first
     // block (kofs bytes before it), V exactly its blocks.
     const int kstart = g * NB * 34;
     const int kofs = kstart & 15;
     const uint8_t* const kwin = p.k_planes + (int64_t)b * p.k_stride + (kstart - kofs);
     const uint8_t* const vwin = p.v_planes + (int64_t)b * p.v_stride + g * NB * 24;
-    // per lane, the byte offset of its piece (instruction x) from the buffer's first row
+    // per lane, the byte offset of its piece (instruction x) from the tile's first row
     uint32_t koff[WN::NKI], voff[WN::NVI];
 #pragma unroll
     for (int x = 0; x < WN::NKI; ++x) {
@@ -146,25 +150,32 @@ __global__ __launch_bounds__(RTW == 1 ? 512 : 256) void decode_stream(DecodePara
         const int pc = x * 64 + lane, row = pc / WN::VWP, col = pc - row * WN::VWP;
         voff[x] = (uint32_t)(row * p.v_row + min(col, WN::VW - 1) * 16);   // the pad piece re-reads a real one
     }
-    // Load the buffer of rows [t0, t0 + TR) into slot `slot`.  Rows from c1 on
-    // (a session's last buffer) are not loaded; rows below lo (first buffer)
-    // are resident and masked.
-    auto issue = [&](int t0, int slot) {
-        uint8_t* const dst = wb + slot * WN::SLOT;
-        const int nrows = min(WN::TR, c1 - t0);
+    // Copy the K (or V) rows of the tile [t0, t0 + 32) into the buffer.  Rows
+    // from c1 on (a session's last tile) are not loaded; rows below lo (first
+    // tile) are resident and masked.  Every LDS read of the half being
+    // refilled has returned first.
+    auto issue_k = [&](int t0) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        const int nrows = min(kTile, c1 - t0);
         const uint8_t* const kt = kwin + (int64_t)(t0 - base) * p.k_row;
-        const uint8_t* const vt = vwin + (int64_t)(t0 - base) * p.v_row;
 #pragma unroll
         for (int x = 0; x < WN::NKI; ++x) {
             uint32_t o = koff[x];
             asm volatile("" : "+v"(o));
-            if (lane < nrows * WN::KWP - x * 64) dma16(kt, o, dst + x * 1024);
+            if (lane < nrows * WN::KWP - x * 64) dma16(kt, o, wb + WN::KB + x * 1024);
         }
+    };
+    auto issue_v = [&](int t0) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        const int nrows = min(kTile, c1 - t0);
+        const uint8_t* const vt = vwin + (int64_t)(t0 - base) * p.v_row;
 #pragma unroll
         for (int x = 0; x < WN::NVI; ++x) {
             uint32_t o = voff[x];
             asm volatile("" : "+v"(o));
-            if (lane < nrows * WN::VWP - x * 64) dma16(vt, o, dst + WN::TR * WN::KSTR + x * 1024);
+            if (lane < nrows * WN::VWP - x * 64) dma16(vt, o, wb + WN::VB + x * 1024);
         }
     };
 
@@ -194,183 +205,191 @@ __global__ __launch_bounds__(RTW == 1 ? 512 : 256) void decode_stream(DecodePara
     const int vkey = pkey(q4, j16 >> 1);                 // V row of this lane's tr8 reads
     const int mk0 = pkey(q4, j16 >> 2), mk1 = pkey(q4, 4 + (j16 >> 2));
     const int mc = (4 * (j16 & 3) < NB) ? (j16 & 3) : 0;   // columns past NB of the offset product are unused
+    const int sh_rot = ((j16 & 7) - 4) & 31;             // moves bit (j16 & 7) of each byte to bit 4
 
-    const int nt = (c1 - c0 + WN::TR - 1) / WN::TR;
-    issue(c0, 0);
-    if (nt > 1) issue(c0 + WN::TR, 1);
-    for (int it = 0; it < nt; ++it) {
-        // this buffer's loads have landed; the next buffer's may stay in flight
-        // when it is a whole one (a partial last buffer issues fewer loads)
-        if (c0 + (it + 2) * WN::TR <= c1) wait_loads_upto<WN::NL>(); else wait_loads_upto<0>();
-        const uint8_t* const rk0 = wb + (it & 1) * WN::SLOT;
-        const uint8_t* const rv0 = rk0 + WN::TR * WN::KSTR;
+    // Loads in issue order: K(0) V(0) | K(1) .. V(1) | ...  K(t+1) is issued
+    // once the scores of tile t have read the K rows, V(t+1) once its P V has
+    // read the V rows.
+    issue_k(c0);
+    issue_v(c0);
+    for (int t0 = c0; t0 < c1; t0 += kTile) {
+        const bool whole = t0 + kTile <= c1;             // this tile issued all its loads
+        const bool next = t0 + kTile < c1;
+        const bool next_whole = t0 + 2 * kTile <= c1;
+        // K(t) has landed; V(t), issued after it, may still be in flight
+        if (whole) wait_loads_upto<WN::NVI>(); else wait_loads_upto<0>();
+
+        // ---- K scales (rows past c1 hold stale bytes)
 #pragma unroll
-        for (int sb = 0; sb < WN::SUB; ++sb) {
-            const int t0 = c0 + it * WN::TR + sb * kTile;
-            if (t0 >= c1) break;
-            const uint8_t* const rk = rk0 + sb * kTile * WN::KSTR;
-            const uint8_t* const rv = rv0 + sb * kTile * WN::VSTR;
-            dec::lds_order();   // the previous tile's reads of the scale arrays come first
-            // ---- K scales, V steps and offsets of the tile (rows past c1 hold stale bytes)
+        for (int x = 0; x < (kTile * NB + 63) / 64; ++x) {
+            const int u = x * 64 + lane;
+            if (kTile * NB % 64 == 0 || u < kTile * NB) {
+                const int key = u / NB, blk = u - (u / NB) * NB;
+                const uint16_t kd = *reinterpret_cast<const uint16_t*>(rk + key * WN::KSTR + kofs + blk * 34);
+                KSa[blk * kTile + key] = (t0 + key < c1) ? f16_value(kd) * sc2 : 0.0f;
+            }
+        }
+        dec::lds_order();
+
+        // ---- scores S^T: sv[rt][h][i] = S[row rt*16 + j16][key 16h + 4*q4 + i] (base 2)
+        float sv[RTW][2][4];
 #pragma unroll
-            for (int x = 0; x < (kTile * NB + 63) / 64; ++x) {
-                const int u = x * 64 + lane;
-                if (kTile * NB % 64 == 0 || u < kTile * NB) {
-                    const int key = u / NB, blk = u - (u / NB) * NB;
-                    const bool live = t0 + key < c1;
-                    const uint16_t kd = *reinterpret_cast<const uint16_t*>(rk + key * WN::KSTR + kofs + blk * 34);
-                    const uint32_t dm = *reinterpret_cast<const uint32_t*>(rv + key * WN::VSTR + blk * 24);
-                    KSa[blk * kTile + key] = live ? f16_value(kd) * sc2 : 0.0f;
-                    VDa[blk * kTile + key] = live ? f16_value((uint16_t)(dm & 0xFFFF)) : 0.0f;
-                    VMa[key * WN::VMS + blk] = live ? (uint16_t)(dm >> 16) : (uint16_t)0;
+        for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sv[rt][h][i] = 0.0f;
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+            const float4 ks0 = *reinterpret_cast<const float4*>(KSa + blk * kTile + 4 * q4);
+            const float4 ks1 = *reinterpret_cast<const float4*>(KSa + blk * kTile + 16 + 4 * q4);
+            const float ksv[2][4] = {{ks0.x, ks0.y, ks0.z, ks0.w}, {ks1.x, ks1.y, ks1.z, ks1.w}};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int key = 16 * h + j16;
+                const uint32_t a = (uint32_t)(key * WN::KSTR + kofs + blk * 34 + 2 + 8 * q4);
+                const uint32_t* w = reinterpret_cast<const uint32_t*>(rk + (a & ~3u));
+                const uint32_t sh = a & 3u;
+                const uint32_t w0 = w[0], w1 = w[1], w2 = w[2];
+                h8 kf = dec::k_codes_f16(__builtin_amdgcn_alignbyte(w1, w0, sh),
+                                         __builtin_amdgcn_alignbyte(w2, w1, sh));
+                // tie this block's products to the previous block's sums, so
+                // that the products of all blocks are not held at once
+                if (NB >= 4) {
+#pragma unroll
+                    for (int rt = 0; rt < RTW; ++rt)
+                        asm volatile("" : "+v"(kf) : "v"(sv[rt][h][0]), "v"(sv[rt][h][1]), "v"(sv[rt][h][2]), "v"(sv[rt][h][3]));
+                }
+#pragma unroll
+                for (int rt = 0; rt < RTW; ++rt) {
+                    f4 d = dec::mfma(kf, qh[rt][blk], (f4){0.f, 0.f, 0.f, 0.f});
+                    if (QLO) d = dec::mfma(kf, ql[rt][blk], d);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sv[rt][h][i] = fmaf(ksv[h][i], d[i], sv[rt][h][i]);
                 }
             }
-            dec::lds_order();
+        }
+        if (next) issue_k(t0 + kTile);
 
-            // ---- scores S^T: sv[rt][h][i] = S[row rt*16 + j16][key 16h + 4*q4 + i] (base 2)
-            float sv[RTW][2][4];
+        // ---- online softmax against a reference max that moves only when a
+        // score passes it by more than 8 (so p <= 256, well inside fp16)
+        const bool interior = t0 >= full_lo && t0 + kTile <= full_hi;
+        float pv[RTW][2][4];
 #pragma unroll
-            for (int rt = 0; rt < RTW; ++rt)
+        for (int rt = 0; rt < RTW; ++rt) {
+            float smax = -INFINITY;
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) sv[rt][h][i] = 0.0f;
-#pragma unroll
-            for (int blk = 0; blk < NB; ++blk) {
-                const float4 ks0 = *reinterpret_cast<const float4*>(KSa + blk * kTile + 4 * q4);
-                const float4 ks1 = *reinterpret_cast<const float4*>(KSa + blk * kTile + 16 + 4 * q4);
-                const float ksv[2][4] = {{ks0.x, ks0.y, ks0.z, ks0.w}, {ks1.x, ks1.y, ks1.z, ks1.w}};
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int key = 16 * h + j16;
-                    const uint32_t a = (uint32_t)(key * WN::KSTR + kofs + blk * 34 + 2 + 8 * q4);
-                    const uint32_t* w = reinterpret_cast<const uint32_t*>(rk + (a & ~3u));
-                    const uint32_t sh = a & 3u;
-                    const uint32_t w0 = w[0], w1 = w[1], w2 = w[2];
-                    h8 kf = dec::k_codes_f16(__builtin_amdgcn_alignbyte(w1, w0, sh),
-                                             __builtin_amdgcn_alignbyte(w2, w1, sh));
-                    // tie this block's products to the previous block's sums, so
-                    // that the products of all blocks are not held at once
-                    if (NB > 4) {
-#pragma unroll
-                        for (int rt = 0; rt < RTW; ++rt)
-                            asm volatile("" : "+v"(kf) : "v"(sv[rt][h][0]), "v"(sv[rt][h][1]), "v"(sv[rt][h][2]), "v"(sv[rt][h][3]));
+                for (int i = 0; i < 4; ++i) {
+                    float x = sv[rt][h][i];
+                    if (!interior) {
+                        const int j = t0 + 16 * h + 4 * q4 + i;
+                        x = (j >= vis_lo[rt] && j < vis_hi[rt]) ? x : -INFINITY;
                     }
-#pragma unroll
-                    for (int rt = 0; rt < RTW; ++rt) {
-                        f4 d = dec::mfma(kf, qh[rt][blk], (f4){0.f, 0.f, 0.f, 0.f});
-                        if (QLO) d = dec::mfma(kf, ql[rt][blk], d);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) sv[rt][h][i] = fmaf(ksv[h][i], d[i], sv[rt][h][i]);
-                    }
+                    sv[rt][h][i] = x;
+                    smax = fmaxf(smax, x);
                 }
+            if (__any(smax > mrow[rt] + 8.0f)) {   // -inf never passes
+                float mt = fmaxf(smax, __shfl_xor(smax, 16));
+                mt = fmaxf(mt, __shfl_xor(mt, 32));
+                const bool move = mt > mrow[rt] + 8.0f;
+                const float alpha = move ? __builtin_amdgcn_exp2f(mrow[rt] - mt) : 1.0f;
+                mrow[rt] = move ? mt : mrow[rt];
+                lsum[rt] *= alpha;
+                float ar[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * q4 + i);   // O rows 4*q4 + i
+#pragma unroll
+                for (int dt = 0; dt < 2 * NB; ++dt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) oacc[rt][dt][i] *= ar[i];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) macc[rt][i] *= ar[i];
             }
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float pe = (mrow[rt] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sv[rt][h][i] - mrow[rt]);
+                    pv[rt][h][i] = pe;
+                    lsum[rt] += pe;
+                }
+        }
 
-            // ---- online softmax against a reference max that moves only when a
-            // score passes it by more than 8 (so p <= 256, well inside fp16)
-            const bool interior = t0 >= full_lo && t0 + kTile <= full_hi;
-            float pv[RTW][2][4];
+        // V(t) has landed; K(t+1), issued after it, may still be in flight
+        if (!next) wait_loads_upto<0>();
+        else if (next_whole) wait_loads_upto<WN::NKI>();
+        else wait_loads_upto<0>();
+        // ---- V steps and offsets of the tile (rows past c1 hold stale bytes)
+#pragma unroll
+        for (int x = 0; x < (kTile * NB + 63) / 64; ++x) {
+            const int u = x * 64 + lane;
+            if (kTile * NB % 64 == 0 || u < kTile * NB) {
+                const int key = u / NB, blk = u - (u / NB) * NB;
+                const bool live = t0 + key < c1;
+                const uint32_t dm = *reinterpret_cast<const uint32_t*>(rv + key * WN::VSTR + blk * 24);
+                VDa[blk * kTile + key] = live ? f16_value((uint16_t)(dm & 0xFFFF)) : 0.0f;
+                VMa[key * WN::VMS + blk] = live ? (uint16_t)(dm >> 16) : (uint16_t)0;
+            }
+        }
+        dec::lds_order();
+
+        // ---- P V with the V codes built from the q5_1 bytes of 8 keys per lane group
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+            const uint8_t* vb = rv + vkey * WN::VSTR + blk * 24 + 8 * (j16 & 1);
+            const i2 nib = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(vb + 8));   // nibble bytes
+            const i2 hdr = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(vb));       // d, m, high bits
+            // high-bit byte of dims 8*(j16>>3).. (first half) and 16 + 8*(j16>>3).. (second
+            // half).  Every lane runs all four broadcasts before selecting: a DPP read
+            // from a lane that is inactive (as in a divergent branch) returns nothing.
+            uint32_t bc[2][4];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                bc[k][0] = bcast_row((uint32_t)hdr[k], 4);
+                bc[k][1] = bcast_row((uint32_t)hdr[k], 5);
+                bc[k][2] = bcast_row((uint32_t)hdr[k], 6);
+                bc[k][3] = bcast_row((uint32_t)hdr[k], 7);
+            }
+            const bool hi8 = j16 >= 8;
+            const uint32_t qa0 = hi8 ? bc[0][1] : bc[0][0], qa1 = hi8 ? bc[1][1] : bc[1][0];
+            const uint32_t qb0 = hi8 ? bc[0][3] : bc[0][2], qb1 = hi8 ? bc[1][3] : bc[1][2];
+            // code = nibble | high bit << 4: rotating the high-bit bytes right by
+            // (j16 & 7) - 4 puts bit (j16 & 7) of each byte at bit 4
+            const uint32_t m4 = 0x10101010u, m0 = 0x0F0F0F0Fu;
+            const uint32_t c00 = (__builtin_amdgcn_alignbit(qa0, qa0, sh_rot) & m4) | ((uint32_t)nib[0] & m0);
+            const uint32_t c01 = (__builtin_amdgcn_alignbit(qa1, qa1, sh_rot) & m4) | ((uint32_t)nib[1] & m0);
+            const uint32_t c10 = (__builtin_amdgcn_alignbit(qb0, qb0, sh_rot) & m4) | (((uint32_t)nib[0] >> 4) & m0);
+            const uint32_t c11 = (__builtin_amdgcn_alignbit(qb1, qb1, sh_rot) & m4) | (((uint32_t)nib[1] >> 4) & m0);
+            const h8 vf0 = dec::v_codes_f16(c00, c01);
+            const h8 vf1 = dec::v_codes_f16(c10, c11);
+            const float4 d0 = *reinterpret_cast<const float4*>(VDa + blk * kTile + 4 * q4);
+            const float4 d1 = *reinterpret_cast<const float4*>(VDa + blk * kTile + 16 + 4 * q4);
 #pragma unroll
             for (int rt = 0; rt < RTW; ++rt) {
-                float smax = -INFINITY;
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float x = sv[rt][h][i];
-                        if (!interior) {
-                            const int j = t0 + 16 * h + 4 * q4 + i;
-                            x = (j >= vis_lo[rt] && j < vis_hi[rt]) ? x : -INFINITY;
-                        }
-                        sv[rt][h][i] = x;
-                        smax = fmaxf(smax, x);
-                    }
-                if (__any(smax > mrow[rt] + 8.0f)) {   // -inf never passes
-                    float mt = fmaxf(smax, __shfl_xor(smax, 16));
-                    mt = fmaxf(mt, __shfl_xor(mt, 32));
-                    const bool move = mt > mrow[rt] + 8.0f;
-                    const float alpha = move ? __builtin_amdgcn_exp2f(mrow[rt] - mt) : 1.0f;
-                    mrow[rt] = move ? mt : mrow[rt];
-                    lsum[rt] *= alpha;
-                    float ar[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * q4 + i);   // O rows 4*q4 + i
-#pragma unroll
-                    for (int dt = 0; dt < 2 * NB; ++dt)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) oacc[rt][dt][i] *= ar[i];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) macc[rt][i] *= ar[i];
-                }
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float pe = (mrow[rt] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sv[rt][h][i] - mrow[rt]);
-                        pv[rt][h][i] = pe;
-                        lsum[rt] += pe;
-                    }
+                const h8 pa = {(_Float16)(pv[rt][0][0] * d0.x), (_Float16)(pv[rt][0][1] * d0.y),
+                               (_Float16)(pv[rt][0][2] * d0.z), (_Float16)(pv[rt][0][3] * d0.w),
+                               (_Float16)(pv[rt][1][0] * d1.x), (_Float16)(pv[rt][1][1] * d1.y),
+                               (_Float16)(pv[rt][1][2] * d1.z), (_Float16)(pv[rt][1][3] * d1.w)};
+                oacc[rt][2 * blk] = dec::mfma(pa, vf0, oacc[rt][2 * blk]);
+                oacc[rt][2 * blk + 1] = dec::mfma(pa, vf1, oacc[rt][2 * blk + 1]);
             }
-
-            // ---- P V with the V codes built from the q5_1 bytes of 8 keys per lane group
+            if (NB > 4) asm volatile("" ::: "memory");
+        }
+        // q5_1 offset term: macc[rt][row][blk] += sum_key P[row][key] * m[key][blk]
+        {
+            const h8 mb = dec::tr16_pair(wb + WN::VM + (mk0 * WN::VMS + 4 * mc) * 2,
+                                         wb + WN::VM + (mk1 * WN::VMS + 4 * mc) * 2);
 #pragma unroll
-            for (int blk = 0; blk < NB; ++blk) {
-                const uint8_t* vb = rv + vkey * WN::VSTR + blk * 24 + 8 * (j16 & 1);
-                const i2 nib = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(vb + 8));   // nibble bytes
-                const i2 hdr = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(vb));       // d, m, high bits
-                // high-bit byte of dims 8*(j16>>3).. (first half) and 16 + 8*(j16>>3).. (second
-                // half).  Every lane runs all four broadcasts before selecting: a DPP read
-                // from a lane that is inactive (as in a divergent branch) returns 0.
-                uint32_t bc[2][4];
-#pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    bc[k][0] = bcast_row((uint32_t)hdr[k], 4);
-                    bc[k][1] = bcast_row((uint32_t)hdr[k], 5);
-                    bc[k][2] = bcast_row((uint32_t)hdr[k], 6);
-                    bc[k][3] = bcast_row((uint32_t)hdr[k], 7);
-                }
-                const bool hi8 = j16 >= 8;
-                const uint32_t qa0 = hi8 ? bc[0][1] : bc[0][0], qa1 = hi8 ? bc[1][1] : bc[1][0];
-                const uint32_t qb0 = hi8 ? bc[0][3] : bc[0][2], qb1 = hi8 ? bc[1][3] : bc[1][2];
-                const int sh = j16 & 7;
-                const uint32_t c00 = ((uint32_t)nib[0] & 0x0F0F0F0Fu) | (((qa0 >> sh) & 0x01010101u) << 4);
-                const uint32_t c01 = ((uint32_t)nib[1] & 0x0F0F0F0Fu) | (((qa1 >> sh) & 0x01010101u) << 4);
-                const uint32_t c10 = (((uint32_t)nib[0] >> 4) & 0x0F0F0F0Fu) | (((qb0 >> sh) & 0x01010101u) << 4);
-                const uint32_t c11 = (((uint32_t)nib[1] >> 4) & 0x0F0F0F0Fu) | (((qb1 >> sh) & 0x01010101u) << 4);
-                const h8 vf0 = dec::v_codes_f16(c00, c01);
-                const h8 vf1 = dec::v_codes_f16(c10, c11);
-                const float4 d0 = *reinterpret_cast<const float4*>(VDa + blk * kTile + 4 * q4);
-                const float4 d1 = *reinterpret_cast<const float4*>(VDa + blk * kTile + 16 + 4 * q4);
-#pragma unroll
-                for (int rt = 0; rt < RTW; ++rt) {
-                    const h8 pa = {(_Float16)(pv[rt][0][0] * d0.x), (_Float16)(pv[rt][0][1] * d0.y),
-                                   (_Float16)(pv[rt][0][2] * d0.z), (_Float16)(pv[rt][0][3] * d0.w),
-                                   (_Float16)(pv[rt][1][0] * d1.x), (_Float16)(pv[rt][1][1] * d1.y),
-                                   (_Float16)(pv[rt][1][2] * d1.z), (_Float16)(pv[rt][1][3] * d1.w)};
-                    oacc[rt][2 * blk] = dec::mfma(pa, vf0, oacc[rt][2 * blk]);
-                    oacc[rt][2 * blk + 1] = dec::mfma(pa, vf1, oacc[rt][2 * blk + 1]);
-                }
-                if (NB > 4) asm volatile("" ::: "memory");
-            }
-            // q5_1 offset term: macc[rt][row][blk] += sum_key P[row][key] * m[key][blk]
-            {
-                const h8 mb = dec::tr16_pair(wb + WN::VM + (mk0 * WN::VMS + 4 * mc) * 2,
-                                             wb + WN::VM + (mk1 * WN::VMS + 4 * mc) * 2);
-#pragma unroll
-                for (int rt = 0; rt < RTW; ++rt) {
-                    const h8 pu = {(_Float16)pv[rt][0][0], (_Float16)pv[rt][0][1], (_Float16)pv[rt][0][2],
-                                   (_Float16)pv[rt][0][3], (_Float16)pv[rt][1][0], (_Float16)pv[rt][1][1],
-                                   (_Float16)pv[rt][1][2], (_Float16)pv[rt][1][3]};
-                    macc[rt] = dec::mfma(pu, mb, macc[rt]);
-                }
+            for (int rt = 0; rt < RTW; ++rt) {
+                const h8 pu = {(_Float16)pv[rt][0][0], (_Float16)pv[rt][0][1], (_Float16)pv[rt][0][2],
+                               (_Float16)pv[rt][0][3], (_Float16)pv[rt][1][0], (_Float16)pv[rt][1][1],
+                               (_Float16)pv[rt][1][2], (_Float16)pv[rt][1][3]};
+                macc[rt] = dec::mfma(pu, mb, macc[rt]);
             }
         }
-        if (it + 2 < nt) {
-            // every LDS read of this buffer has returned before it is refilled
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-            issue(c0 + (it + 2) * WN::TR, it & 1);
-        }
+        if (next) issue_v(t0 + kTile);
     }
 
     // ---- finish: row sums over the four lane groups; offsets into O; partials

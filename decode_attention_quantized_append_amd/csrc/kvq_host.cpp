@@ -224,7 +224,7 @@ bool choose_kernel(const kvq_cache* h, int R, int32_t T, Plan* p) {
     return false;
 }
 
-Plan make_plan(const kvq_cache* h, int32_t T, bool* fits = nullptr) {
+Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nullptr) {
     const kvq_config& c = h->cfg;
     const int R = T * (c.n_q_heads / c.n_kv_heads);
     int64_t total = 0, maxvis = 1;
@@ -244,7 +244,8 @@ Plan make_plan(const kvq_cache* h, int32_t T, bool* fits = nullptr) {
             // whole number of buffers
             const int64_t ngrp = c.n_kv_heads / p.gh;
             const int64_t waves_per_wg = p.kernel == kvq::kStream ? p.gh : p.gh * ((R + 15) / 16);
-            const int64_t waves_per_cu = (p.kernel == kvq::kStream && R > 16) ? 4 : 8;
+            const int64_t waves_per_cu =
+                p.kernel == kvq::kStream ? 4 * kvq::stream_waves_per_simd(c.head_dim / 32, R > 16 ? 2 : 1, f32_queries) : 8;
             const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kvq::kLdsBytes / p.lds,
                                                                            waves_per_cu / waves_per_wg));
             const int64_t slots = 256 * per_cu;
@@ -442,8 +443,9 @@ kvq_status kvq_append(kvq_cache* h, const void* k_new, const void* v_new, kvq_dt
 kvq_status kvq_decode_workspace_bytes(const kvq_cache* h, int32_t T, size_t* bytes) {
     if (!h || !bytes) return fail(KVQ_EINVAL, "NULL argument");
     if (T < 1) return fail(KVQ_EINVAL, "T must be >= 1");
-    Plan p = make_plan(h, T);
-    *bytes = p.ml_bytes + p.o_bytes;
+    // the larger of the plans for fp32 and bf16 queries
+    const Plan p32 = make_plan(h, T, true), p16 = make_plan(h, T, false);
+    *bytes = std::max(p32.ml_bytes + p32.o_bytes, p16.ml_bytes + p16.o_bytes);
     return KVQ_OK;
 }
 
@@ -465,7 +467,7 @@ kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, c
             return fail(KVQ_ERANGE, "session " + std::to_string(b) + ": visible rows were rebased away");
     }
     bool fits = true;
-    Plan p = make_plan(h, T, &fits);
+    Plan p = make_plan(h, T, dtype == KVQ_F32, &fits);
     if (!fits) return fail(KVQ_EINVAL, "the decode tiling set with kvq_set_decode_tiling does not fit this shape");
     if (!ws || ws_bytes < p.ml_bytes + p.o_bytes) return fail(KVQ_EINVAL, "workspace missing or too small");
     if (!aligned(ws, 256)) return fail(KVQ_EINVAL, "workspace must be 256-byte aligned");

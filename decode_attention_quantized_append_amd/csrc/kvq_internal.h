@@ -108,8 +108,9 @@ inline RowGeo row_geo(int gh, int NB, int sub) {
 }
 
 // Geometry of the per-wave stream decode kernel for head_dim = 32 * NB (NB
-// even): each wave copies its KV head's row windows, in 16-byte pieces, into
-// a private double buffer, then builds per-tile scale arrays.
+// even): each wave copies its KV head's row windows of a 32-row tile, in
+// 16-byte pieces, into one private LDS buffer (K rows, then V rows), and
+// builds per-tile scale arrays.
 template <int NB>
 struct StreamWin {
     static constexpr int MAXKOFS = (NB % 8 == 0) ? 0 : (NB % 4 == 0) ? 8 : 12;   // (g*NB*34) mod 16, at most
@@ -117,19 +118,18 @@ struct StreamWin {
     static constexpr int KWP = KW | 1;                          // LDS row stride in pieces (odd)
     static constexpr int VW = 24 * NB / 16;                     // V pieces per row
     static constexpr int VWP = VW | 1;
-    static constexpr int SUB = NB <= 2 ? 2 : 1;                 // 32-row tiles per buffer
-    static constexpr int TR = kRowTile * SUB;                   // rows per buffer
+    static constexpr int TR = kRowTile;                         // rows per tile
     static constexpr int KSTR = KWP * 16, VSTR = VWP * 16;
-    static constexpr int NKI = (TR * KWP + 63) / 64;            // load instructions per buffer
-    static constexpr int NVI = (TR * VWP + 63) / 64;
-    static constexpr int NL = NKI + NVI;
-    static constexpr int SLOT = TR * (KSTR + VSTR);             // bytes per buffer
+    static constexpr int NKI = (TR * KWP + 63) / 64;            // load instructions per tile, K
+    static constexpr int NVI = (TR * VWP + 63) / 64;            // and V
+    static constexpr int KB = 0;                                // K rows
+    static constexpr int VB = TR * KSTR;                        // V rows
     static constexpr int VMS = NB < 4 ? 4 : NB;
-    static constexpr int KS = 2 * SLOT;                         // f32 [NB][32] K scales * scale * log2 e
+    static constexpr int KS = VB + TR * VSTR;                   // f32 [NB][32] K scales * scale * log2 e
     static constexpr int VD = KS + NB * kRowTile * 4;           // f32 [NB][32] V steps
     static constexpr int VM = VD + NB * kRowTile * 4;           // fp16 [32][VMS] V offsets
     static constexpr int BYTES = VM + kRowTile * VMS * 2;       // per wave
-    static_assert(NL <= 32, "load count must fit vmcnt");
+    static_assert(NKI <= 32 && NVI <= 32, "load counts must fit vmcnt");
 };
 
 inline int stream_wave_bytes(int NB) {
@@ -140,7 +140,14 @@ inline int stream_wave_bytes(int NB) {
         default: return 0;
     }
 }
-inline int stream_rows_per_buffer(int NB) { return NB <= 2 ? 2 * kRowTile : kRowTile; }
+inline int stream_rows_per_buffer(int) { return kRowTile; }
+// Waves per SIMD the stream kernel is compiled for (its register budget is
+// 512 / this): as many as its registers allow without spilling.  NB blocks of
+// 32 dims per head, RTW row tiles of 16 per wave, QLO = fp32 queries (a low
+// fp16 part is kept beside the high one).
+constexpr int stream_waves_per_simd(int NB, int RTW, bool QLO) {
+    return RTW > 1 ? 1 : NB >= 8 ? 2 : NB >= 4 ? (QLO ? 3 : 4) : 4;
+}
 
 enum DecodeKernel : int32_t { kPerHead = 0, kWholeRow = 1, kStream = 2 };
 

@@ -216,7 +216,7 @@ def test_decode_validation_and_plan(lib):
     kvq.kvq_decode(h, Q, kvq.KVQ_BF16, 2, None, 0.125, O, None, WS, ws, 0, lib)
     (line,) = log(lib)
     chunk, splits = map(int, re.search(r"chunk=(\d+) splits=(\d+)", line).groups())
-    assert chunk % 64 == 0 and splits == -(-3000 // chunk)
+    assert chunk % 32 == 0 and splits == -(-3000 // chunk)
     ml = int(re.search(r"ml_to_o=(\d+)", line).group(1))
     assert ml >= 2 * splits * 2 * 8 * 4 and ml % 256 == 0
     assert ws >= ml + 2 * splits * 2 * 8 * 64 * 4
@@ -315,7 +315,7 @@ def test_decode_kernel_choice(lib):
     h = create(lib, n_seqs=1, n_q_heads=4, n_kv_heads=1, head_dim=64, capacity=300)
     kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 256, None, 0, lib)
     p = plan_of(lib, h)
-    assert (p["kernel"], p["gh"]) == (STREAM, 1) and p["chunk"] % 64 == 0
+    assert (p["kernel"], p["gh"]) == (STREAM, 1) and p["chunk"] % 32 == 0
 
 
 def test_decode_ring_start_below_base_falls_back(lib):
