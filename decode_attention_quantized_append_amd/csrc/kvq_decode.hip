@@ -392,6 +392,43 @@ constexpr int prefetch_depth() { return NB * RT >= 12 ? 1 : 2; }
 template <int NB, int RT>
 constexpr int min_blocks() { return NB * RT <= 4 ? 2 : 1; }
 
+// Unit u of the decode grid -> (session b, chunk s).  The units are the
+// (session, chunk) pairs that hold rows, sessions in order, so that the grid
+// has no empty workgroups and an XCD's contiguous share of it is a fair share
+// of the rows whatever the length mix.  Chunk counts come from the device
+// lengths, 64 sessions per step (a wave-wide prefix sum).  b = -1 past the
+// last unit.  Every lane of the wave calls it with the same u.
+__device__ __forceinline__ void locate_unit(const DecodeParams& p, int u, int& b, int& s) {
+    const int lane = threadIdx.x & 63;
+    int fb = -1, fs = 0;
+    for (int b0 = 0; b0 < p.B && fb < 0; b0 += 64) {
+        const int bb = b0 + lane;
+        int n = 0;
+        if (bb < p.B) {
+            const int len = p.len_d[bb];
+            const int lo = p.window > 0 ? max(0, len - p.T + 1 - p.window) : 0;
+            const int span = len - (lo & ~31);
+            n = span > 0 ? (span + p.chunk - 1) / p.chunk : 0;
+        }
+        int incl = n;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(incl, d);
+            if (lane >= d) incl += y;
+        }
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        if (u < total) {
+            const int lb = __builtin_amdgcn_readfirstlane(__builtin_ctzll(__ballot(incl > u)));
+            fb = b0 + lb;
+            fs = u - __builtin_amdgcn_readlane(incl - n, lb);
+        } else {
+            u -= total;
+        }
+    }
+    b = __builtin_amdgcn_readfirstlane(fb);
+    s = __builtin_amdgcn_readfirstlane(fs);
+}
+
 template <int NB, int RT, bool QLO>
 __global__ __launch_bounds__(256, (min_blocks<NB, RT>())) void decode_mfma(DecodeParams p) {
     using LY = Layout<NB, RT>;
@@ -410,9 +447,9 @@ __global__ __launch_bounds__(256, (min_blocks<NB, RT>())) void decode_mfma(Decod
     const int wid = blockIdx.x;
     const int L = (wid & 7) * (W >> 3) + (wid >> 3);
     const int g = L % p.Hkv;
-    const int s = (L / p.Hkv) % p.splits;
-    const int b = L / (p.Hkv * p.splits);
-    if (b >= p.B) return;
+    int b, s;
+    locate_unit(p, L / p.Hkv, b, s);
+    if (b < 0) return;
     const int R = p.T * p.hpk;
 
     // Q fragment (rt, blk) lane l: q[r = rt*16 + l%16][blk*32 + 8*(l/16) .. +7].

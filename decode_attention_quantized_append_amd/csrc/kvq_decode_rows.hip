@@ -104,13 +104,14 @@ __global__ __launch_bounds__(512) void decode_rows(DecodeParams p) {
     const int gh = p.gh, nw = gh * RT, ngrp = p.Hkv / gh;
 
     // workgroup -> (session, chunk, head group), head group fastest; an XCD
-    // receives every 8th workgroup id, so logical neighbours share its L2
+    // receives every 8th workgroup id, so logical neighbours share its L2 and
+    // each XCD gets an equal share of the chunks
     const int W = gridDim.x, wid = blockIdx.x;
     const int L = (wid & 7) * (W >> 3) + (wid >> 3);
     const int hg = L % ngrp;
-    const int s = (L / ngrp) % p.splits;
-    const int b = L / (ngrp * p.splits);
-    if (b >= p.B) return;
+    int b, s;
+    dec::locate_unit(p, L / ngrp, b, s);
+    if (b < 0) return;
     const int gi = wave % gh, rt = wave / gh, g = hg * gh + gi;
     const int R = p.T * p.hpk;
 

@@ -54,14 +54,36 @@ __device__ __forceinline__ void wait_loads_upto() {
     asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ uint32_t bcast_row(uint32_t x, int n) {
-    // lane n of each 16-lane row, to every lane of the row (DPP row_newbcast)
-    switch (n) {
-        case 4: return __builtin_amdgcn_mov_dpp((int)x, 0x154, 0xF, 0xF, true);
-        case 5: return __builtin_amdgcn_mov_dpp((int)x, 0x155, 0xF, 0xF, true);
-        case 6: return __builtin_amdgcn_mov_dpp((int)x, 0x156, 0xF, 0xF, true);
-        default: return __builtin_amdgcn_mov_dpp((int)x, 0x157, 0xF, 0xF, true);
-    }
+// Two bytes of x (selector: 0x0401_0400 bytes 0,1; 0x0403_0402 bytes 2,3) as
+// the fp16 values 1024 + byte.
+__device__ __forceinline__ uint32_t spread_1024(uint32_t x, uint32_t sel) {
+    return __builtin_amdgcn_perm(0x64646464u, x, sel);
+}
+// Two bytes of x as fp16 subnormals, byte * 2^-24 (exact; the matrix cores
+// keep fp16 subnormal inputs).
+__device__ __forceinline__ uint32_t spread_sub(uint32_t x, uint32_t sel) {
+    return __builtin_amdgcn_perm(0u, x, sel);
+}
+constexpr uint32_t kSel01 = 0x04010400u, kSel23 = 0x04030402u;
+
+// 8 signed q8_0 codes, the pairs given by (word, selector), -> fp16 exactly:
+// (c ^ 0x80) = c + 128 in the low byte of 1024 + (c + 128), less 1152.
+__device__ __forceinline__ h8 k_codes(uint32_t w0, uint32_t s0, uint32_t w1, uint32_t s1, uint32_t w2, uint32_t s2,
+                                      uint32_t w3, uint32_t s3) {
+    typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+    const h2v off = {(_Float16)1152.0f, (_Float16)1152.0f};
+    const h2v a = __builtin_bit_cast(h2v, spread_1024(w0, s0)) - off;
+    const h2v b = __builtin_bit_cast(h2v, spread_1024(w1, s1)) - off;
+    const h2v c = __builtin_bit_cast(h2v, spread_1024(w2, s2)) - off;
+    const h2v d = __builtin_bit_cast(h2v, spread_1024(w3, s3)) - off;
+    return (h8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// 8 q5_1 codes (bytes 0..31 of lo, hi) -> fp16 subnormals code * 2^-24.
+__device__ __forceinline__ h8 v_codes_sub(uint32_t lo, uint32_t hi) {
+    typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+    const u4v w = {spread_sub(lo, kSel01), spread_sub(lo, kSel23), spread_sub(hi, kSel01), spread_sub(hi, kSel23)};
+    return __builtin_bit_cast(h8, w);
 }
 
 template <int NB, int RTW, bool QLO>
@@ -77,9 +99,9 @@ __global__ __launch_bounds__(RTW == 1 ? 512 : 256, stream_waves_per_simd(NB, RTW
     const int W = gridDim.x, wid = blockIdx.x;
     const int L = (wid & 7) * (W >> 3) + (wid >> 3);
     const int hg = L % ngrp;
-    const int s = (L / ngrp) % p.splits;
-    const int b = L / (ngrp * p.splits);
-    if (b >= p.B) return;
+    int b, s;
+    dec::locate_unit(p, L / ngrp, b, s);
+    if (b < 0) return;
     const int g = hg * gh + wave;
     const int R = p.T * p.hpk;
 
@@ -206,6 +228,8 @@ __global__ __launch_bounds__(RTW == 1 ? 512 : 256, stream_waves_per_simd(NB, RTW
     const int mk0 = pkey(q4, j16 >> 2), mk1 = pkey(q4, 4 + (j16 >> 2));
     const int mc = (4 * (j16 & 3) < NB) ? (j16 & 3) : 0;   // columns past NB of the offset product are unused
     const int sh_rot = ((j16 & 7) - 4) & 31;             // moves bit (j16 & 7) of each byte to bit 4
+    const int src_lo = (16 * q4 + 4 + (j16 >> 3)) * 4;   // byte addresses of the lanes holding
+    const int src_hi = (16 * q4 + 6 + (j16 >> 3)) * 4;   // this lane's high-bit bytes
 
     // Loads in issue order: K(0) V(0) | K(1) .. V(1) | ...  K(t+1) is issued
     // once the scores of tile t have read the K rows, V(t+1) once its P V has
@@ -247,12 +271,19 @@ __global__ __launch_bounds__(RTW == 1 ? 512 : 256, stream_waves_per_simd(NB, RTW
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int key = 16 * h + j16;
-                const uint32_t a = (uint32_t)(key * WN::KSTR + kofs + blk * 34 + 2 + 8 * q4);
-                const uint32_t* w = reinterpret_cast<const uint32_t*>(rk + (a & ~3u));
-                const uint32_t sh = a & 3u;
-                const uint32_t w0 = w[0], w1 = w[1], w2 = w[2];
-                h8 kf = dec::k_codes_f16(__builtin_amdgcn_alignbyte(w1, w0, sh),
-                                         __builtin_amdgcn_alignbyte(w2, w1, sh));
+                // kofs is a multiple of 4, so the codes start 2 bytes into a
+                // word for even blocks and on a word for odd ones
+                const int cb = blk * 34 + 2;
+                const uint32_t* w = reinterpret_cast<const uint32_t*>(
+                    rk + (uint32_t)(key * WN::KSTR + kofs + 8 * q4) + (cb & ~3));
+                h8 kf;
+                if ((cb & 3) == 2) {
+                    const uint32_t x0 = w[0] ^ 0x80808080u, x1 = w[1] ^ 0x80808080u, x2 = w[2] ^ 0x80808080u;
+                    kf = k_codes(x0, kSel23, x1, kSel01, x1, kSel23, x2, kSel01);
+                } else {
+                    const uint32_t x0 = w[0] ^ 0x80808080u, x1 = w[1] ^ 0x80808080u;
+                    kf = k_codes(x0, kSel01, x0, kSel23, x1, kSel01, x1, kSel23);
+                }
                 // tie this block's products to the previous block's sums, so
                 // that the products of all blocks are not held at once
                 if (NB >= 4) {
@@ -341,20 +372,13 @@ __global__ __launch_bounds__(RTW == 1 ? 512 : 256, stream_waves_per_simd(NB, RTW
             const uint8_t* vb = rv + vkey * WN::VSTR + blk * 24 + 8 * (j16 & 1);
             const i2 nib = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(vb + 8));   // nibble bytes
             const i2 hdr = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(vb));       // d, m, high bits
-            // high-bit byte of dims 8*(j16>>3).. (first half) and 16 + 8*(j16>>3).. (second
-            // half).  Every lane runs all four broadcasts before selecting: a DPP read
-            // from a lane that is inactive (as in a divergent branch) returns nothing.
-            uint32_t bc[2][4];
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                bc[k][0] = bcast_row((uint32_t)hdr[k], 4);
-                bc[k][1] = bcast_row((uint32_t)hdr[k], 5);
-                bc[k][2] = bcast_row((uint32_t)hdr[k], 6);
-                bc[k][3] = bcast_row((uint32_t)hdr[k], 7);
-            }
-            const bool hi8 = j16 >= 8;
-            const uint32_t qa0 = hi8 ? bc[0][1] : bc[0][0], qa1 = hi8 ? bc[1][1] : bc[1][0];
-            const uint32_t qb0 = hi8 ? bc[0][3] : bc[0][2], qb1 = hi8 ? bc[1][3] : bc[1][2];
+            // lanes 4..7 of each 16-lane group now hold high-bit bytes 0..3 of
+            // the 8 keys.  Dims j16 (first half) take byte j16 >> 3, dims
+            // 16 + j16 byte 2 + (j16 >> 3).
+            const uint32_t qa0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lo, hdr[0]);
+            const uint32_t qa1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lo, hdr[1]);
+            const uint32_t qb0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src_hi, hdr[0]);
+            const uint32_t qb1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src_hi, hdr[1]);
             // code = nibble | high bit << 4: rotating the high-bit bytes right by
             // (j16 & 7) - 4 puts bit (j16 & 7) of each byte at bit 4
             const uint32_t m4 = 0x10101010u, m0 = 0x0F0F0F0Fu;
@@ -362,8 +386,8 @@ __global__ __launch_bounds__(RTW == 1 ? 512 : 256, stream_waves_per_simd(NB, RTW
             const uint32_t c01 = (__builtin_amdgcn_alignbit(qa1, qa1, sh_rot) & m4) | ((uint32_t)nib[1] & m0);
             const uint32_t c10 = (__builtin_amdgcn_alignbit(qb0, qb0, sh_rot) & m4) | (((uint32_t)nib[0] >> 4) & m0);
             const uint32_t c11 = (__builtin_amdgcn_alignbit(qb1, qb1, sh_rot) & m4) | (((uint32_t)nib[1] >> 4) & m0);
-            const h8 vf0 = dec::v_codes_f16(c00, c01);
-            const h8 vf1 = dec::v_codes_f16(c10, c11);
+            const h8 vf0 = v_codes_sub(c00, c01);
+            const h8 vf1 = v_codes_sub(c10, c11);
             const float4 d0 = *reinterpret_cast<const float4*>(VDa + blk * kTile + 4 * q4);
             const float4 d1 = *reinterpret_cast<const float4*>(VDa + blk * kTile + 16 + 4 * q4);
 #pragma unroll
@@ -402,7 +426,8 @@ __global__ __launch_bounds__(RTW == 1 ? 512 : 256, stream_waves_per_simd(NB, RTW
 #pragma unroll
         for (int dt = 0; dt < 2 * NB; ++dt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) oacc[rt][dt][i] += __shfl(macc[rt][i], 16 * q4 + dt / 2);
+            for (int i = 0; i < 4; ++i)   // the code products carry a factor 2^-24
+                oacc[rt][dt][i] = fmaf(oacc[rt][dt][i], 0x1p24f, __shfl(macc[rt][i], 16 * q4 + dt / 2));
         const int r = rt * 16 + j16;
         if (q4 == 0 && r < R) {
             const int t = r / p.hpk, hq = g * p.hpk + r % p.hpk;

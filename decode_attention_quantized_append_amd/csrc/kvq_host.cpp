@@ -120,6 +120,7 @@ struct Plan {
     int32_t kernel;    // kvq::DecodeKernel
     int32_t chunk;
     int32_t splits;
+    int32_t units;     // (session, chunk) pairs with rows
     int32_t gh;        // KV heads per workgroup (whole-row and stream kernels)
     int32_t sub;       // whole-row kernel: rows per buffer / 32
     int32_t lds;       // dynamic LDS bytes
@@ -172,7 +173,7 @@ int64_t span_of(const kvq_cache* h, int b, int32_t T) {
 
 // Chooses the decode kernel and its tiling.  Returns false when a kernel or
 // tiling set with kvq_set_decode_tiling does not fit the shape.
-bool choose_kernel(const kvq_cache* h, int R, int32_t T, Plan* p) {
+bool choose_kernel(const kvq_cache* h, int R, int32_t T, bool f32_queries, Plan* p) {
     const kvq_config& c = h->cfg;
     const int NB = c.head_dim / 32;
     const int RT = (R + 15) / 16;
@@ -191,9 +192,17 @@ bool choose_kernel(const kvq_cache* h, int R, int32_t T, Plan* p) {
     if (!aligned_start_resident(h, T)) return true;
     if (want == KVQ_DECODE_STREAM) {
         int gh = h->head_group;
-        if (gh == 0)
-            for (int k = std::min(c.n_kv_heads, 8); k >= 1 && gh == 0; --k)
-                if (stream_ok(c, R, k)) gh = k;
+        if (gh == 0) {
+            // the head group that keeps the most waves resident per CU (the
+            // larger group on a tie): whole workgroups, within registers and LDS
+            const int waves = 4 * kvq::stream_waves_per_simd(NB, RT, f32_queries);
+            int best = 0;
+            for (int k = std::min(c.n_kv_heads, 8); k >= 1; --k) {
+                if (!stream_ok(c, R, k)) continue;
+                const int wgs = std::min(waves / k, kvq::kLdsBytes / (k * kvq::stream_wave_bytes(NB)));
+                if (wgs * k > best) best = wgs * k, gh = k;
+            }
+        }
         if (!stream_ok(c, R, gh)) return h->decode_kernel == KVQ_DECODE_AUTO;
         p->kernel = kvq::kStream;
         p->gh = gh;
@@ -234,7 +243,7 @@ Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nul
         maxvis = std::max(maxvis, vis);
     }
     Plan p{};
-    const bool ok = choose_kernel(h, R, T, &p);
+    const bool ok = choose_kernel(h, R, T, f32_queries, &p);
     if (fits) *fits = ok;
     int64_t chunk = h->split_rows;
     if (p.kernel != kvq::kPerHead) {
@@ -272,6 +281,8 @@ Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nul
     chunk = std::max<int64_t>(chunk, round_up(ceil_div(maxvis, kvq::kMaxSplits), p.rows));
     p.chunk = (int32_t)chunk;
     p.splits = (int32_t)std::max<int64_t>(1, ceil_div(maxvis, chunk));
+    p.units = 0;
+    for (int b = 0; b < c.n_seqs; ++b) p.units += (int32_t)ceil_div(span_of(h, b, T), chunk);
     int64_t entries = (int64_t)c.n_seqs * p.splits * T * c.n_q_heads;
     p.ml_bytes = (size_t)round_up(entries * 2 * 4, 256);
     p.o_bytes = (size_t)round_up(entries * c.head_dim * 4, 256);
@@ -491,6 +502,7 @@ kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, c
     dp.base_d = base_d(h);
     dp.chunk = p.chunk;
     dp.splits = p.splits;
+    dp.units = p.units;
     dp.kernel = p.kernel;
     dp.gh = p.gh;
     dp.sub = p.sub;

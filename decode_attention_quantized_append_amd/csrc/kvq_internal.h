@@ -167,6 +167,7 @@ struct DecodeParams {
     int32_t chunk;              // rows per split (multiple of kSplitQuantum); chunks
                                 // start at the first visible row rounded down to 32
     int32_t splits;             // split slots per session
+    int32_t units;              // (session, chunk) pairs with rows, over all sessions
     int32_t kernel;             // DecodeKernel
     int32_t gh;                 // KV heads per workgroup (whole-row and stream kernels)
     int32_t sub;                // whole-row kernel: rows per buffer / 32

@@ -311,7 +311,7 @@ int launch_decode_t(const DecodeParams& p, hipStream_t st, const char** err) {
         }
         configured = true;
     }
-    const int items = p.B * p.splits * p.Hkv;
+    const int items = std::max(1, p.units) * p.Hkv;
     const int grid = (items + 7) & ~7;
     hipLaunchKernelGGL((dec::decode_mfma<NB, RT, QLO>), dim3(grid), dim3(256), lds, st, p);
     if (check(err)) return 1;
@@ -330,7 +330,7 @@ int launch_rows_t(const DecodeParams& p, hipStream_t st, const char** err) {
         }
         configured = true;
     }
-    const int items = p.B * p.splits * (p.Hkv / p.gh);
+    const int items = std::max(1, p.units) * (p.Hkv / p.gh);
     const int grid = (items + 7) & ~7;
     hipLaunchKernelGGL((rows::decode_rows<NB, RT, QLO>), dim3(grid), dim3(64 * p.gh * RT), p.lds, st, p);
     if (check(err)) return 1;
@@ -349,7 +349,7 @@ int launch_stream_t(const DecodeParams& p, hipStream_t st, const char** err) {
         }
         configured = true;
     }
-    const int items = p.B * p.splits * (p.Hkv / p.gh);
+    const int items = std::max(1, p.units) * (p.Hkv / p.gh);
     const int grid = (items + 7) & ~7;
     hipLaunchKernelGGL((stream::decode_stream<NB, RTW, QLO>), dim3(grid), dim3(64 * p.gh), p.lds, st, p);
     if (check(err)) return 1;

@@ -260,9 +260,9 @@ def test_split_rows_setting(lib):
     assert kvq.kvq_info(h, lib).split_rows == 640
 
 
-def plan_of(lib, h, T=1):
+def plan_of(lib, h, T=1, dtype=kvq.KVQ_BF16):
     lib.kvq_nodev_clear()
-    kvq.kvq_decode(h, Q, kvq.KVQ_BF16, T, None, 0.1, O, None, WS, 1 << 40, 0, lib)
+    kvq.kvq_decode(h, Q, dtype, T, None, 0.1, O, None, WS, 1 << 40, 0, lib)
     (line,) = log(lib)
     return {k: int(v) for k, v in re.findall(r"(\w+)=(-?\d+)", line)}
 
@@ -275,6 +275,10 @@ def test_decode_kernel_choice(lib):
     p = plan_of(lib, h)
     assert (p["kernel"], p["gh"]) == (STREAM, 8) and 0 < p["lds"] <= 160 * 1024 and p["chunk"] % 32 == 0
     assert p["splits"] == -(-8192 // p["chunk"])
+    # fp32 queries keep a low fp16 part: more registers, 12 waves per CU, so
+    # groups of 4 heads (three workgroups per CU) keep all of them resident
+    p = plan_of(lib, h, dtype=kvq.KVQ_F32)
+    assert (p["kernel"], p["gh"]) == (STREAM, 4)
     kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_PER_HEAD, 0, 0, lib)
     assert plan_of(lib, h)["kernel"] == PER_HEAD
     kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_WHOLE_ROW, 8, 1, lib)
