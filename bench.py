@@ -82,6 +82,10 @@ def parse():
     ap.add_argument("--split-rows", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--graph", choices=("auto", "on", "off"), default="auto",
+                    help="replay each step as one captured HIP graph (auto: where the "
+                         "session lengths are the same at every step, so the captured "
+                         "launch plan stays valid)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES, 10 times "
                          "(reference for scaling HBM traffic counters)")
@@ -162,26 +166,33 @@ def run_gpu(w, args):
         if st != 0:
             raise RuntimeError(f"{what}: {lib.kvq_last_error().decode()}")
 
-    def one_step(i, ev=None):
+    def one_step(i, ev=None, st=None):
+        st = stream if st is None else st
         li = i % L
         h = caches[li].h
         if ev is not None:
             ev[0].record()
-        check(lib.kvq_append(h, kp, vp, dt, T, None, stream), "append")
+        check(lib.kvq_append(h, kp, vp, dt, T, None, st), "append")
         if ev is not None:
             ev[1].record()
-        check(lib.kvq_decode(h, qp, dt, T, sink_ptr, scale, op, lp, ws_ptr, ws_bytes, stream), "decode")
+        check(lib.kvq_decode(h, qp, dt, T, sink_ptr, scale, op, lp, ws_ptr, ws_bytes, st), "decode")
         if ev is not None:
             ev[2].record()
         if w.rollback_keep:                        # verify: keep rollback_keep of the T rows
             lens[li] = [x + w.rollback_keep for x in lens[li]]
-            check(lib.kvq_truncate(h, (ctypes.c_int32 * B)(*lens[li]), stream), "truncate")
+            check(lib.kvq_truncate(h, (ctypes.c_int32 * B)(*lens[li]), st), "truncate")
         elif not w.ring_cap:                       # steady length: drop the step's rows
-            check(lib.kvq_truncate(h, pre_arr, stream), "truncate")
+            check(lib.kvq_truncate(h, pre_arr, st), "truncate")
+
+    steady = not w.rollback_keep and not w.ring_cap
+    if args.graph == "on" and not steady:
+        raise SystemExit(f"--graph on: the {w.name} workload changes session lengths every step")
+    use_graph = args.graph == "on" or (args.graph == "auto" and steady)
 
     for i in range(args.warmup):
         one_step(i)
     torch.cuda.synchronize(dev)
+    # per-call times (HIP events between the library calls of eager steps)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -190,12 +201,41 @@ def run_gpu(w, args):
     wall = time.perf_counter() - t0
     app_ms = [e[0].elapsed_time(e[1]) for e in events]
     dec_ms = [e[1].elapsed_time(e[2]) for e in events]
+    if use_graph:
+        # one graph per layer for the whole step, one for its decode call alone
+        cap_st = torch.cuda.Stream(dev)
+        steps_g, dec_g = [], []
+        for li in range(L):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap_st):
+                one_step(li, st=cap_st.cuda_stream)
+            steps_g.append(g)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap_st):
+                check(lib.kvq_decode(caches[li].h, qp, dt, T, sink_ptr, scale, op, lp, ws_ptr, ws_bytes,
+                                     cap_st.cuda_stream), "decode")
+            dec_g.append(g)
+        for i in range(args.warmup):
+            steps_g[i % L].replay()
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            steps_g[(args.warmup + i) % L].replay()
+        torch.cuda.synchronize(dev)
+        wall = time.perf_counter() - t0
+        dev_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            dev_ev[i][0].record()
+            dec_g[(args.warmup + i) % L].replay()
+            dev_ev[i][1].record()
+        torch.cuda.synchronize(dev)
+        dec_ms = [e[0].elapsed_time(e[1]) for e in dev_ev]   # the decode call's graph replay
     kv_bytes = w.kv_bytes_per_decode()
     ms_step = wall * 1e3 / args.steps
     dec_avg = sum(dec_ms) / len(dec_ms)
     app_avg = sum(app_ms) / len(app_ms)
     dec_sorted = sorted(dec_ms)
-    return dict(L=L, cap=cap, ms_step=ms_step, dec_ms=dec_avg, app_ms=app_avg,
+    return dict(L=L, cap=cap, ms_step=ms_step, graph=use_graph, dec_ms=dec_avg, app_ms=app_avg,
                 dec_p10=dec_sorted[len(dec_ms) // 10], dec_p90=dec_sorted[(9 * len(dec_ms)) // 10],
                 kv_bytes=kv_bytes, ws_bytes=ws_bytes,
                 footprint=L * (caches[0].sizes.k_planes_bytes + caches[0].sizes.v_planes_bytes))
@@ -269,7 +309,7 @@ def main():
                    "head_dim": w.hd, "query_rows": w.T, "visible_rows": int(w.visible().sum()),
                    "window": w.window, "ring_rows": w.ring_cap, "layers_rotated": r["L"],
                    "kv_footprint_bytes": r["footprint"], "kv_bytes_per_step": r["kv_bytes"],
-                   "parallelism": "none (1 GPU)"},
+                   "parallelism": "none (1 GPU)", "step_launch": "hip graph" if r["graph"] else "eager"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "steps_per_s": round(1e3 / r["ms_step"], 1),
         "append_tokens_per_s": round(w.B * w.T / (r["app_ms"] * 1e-3), 1),

@@ -197,10 +197,10 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 // partials (m in natural-log units, l, o), adding the sink once as a
 // value-less column.  The splits' maxima and weights are computed by all
 // threads in parallel; then each thread sums a 4-float slice of o over every
-// G-th split (G = 256 / (hd / 4) groups of splits, 8 loads in flight), and
-// the G group sums are added in a fixed order.
-constexpr int kCombineThreads = 256;
-
+// G-th split (G = NT / (hd / 4) groups of splits, 8 loads in flight), and
+// the G group sums are added in a fixed order.  NT = 1024 threads when there
+// are many splits (few workgroups, each with much to read), else 256.
+template <int kCombineThreads>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p) {
     __shared__ float wts[kMaxSplits];
     __shared__ float red[kCombineThreads / 32 > 8 ? kCombineThreads / 32 : 8];
@@ -299,6 +299,14 @@ int check(const char** err) {
     return 0;
 }
 
+int launch_combine(const DecodeParams& p, hipStream_t st, const char** err) {
+    if (p.splits >= 64)
+        hipLaunchKernelGGL(combine_kernel<1024>, dim3(p.B * p.T * p.H), dim3(1024), 0, st, p);
+    else
+        hipLaunchKernelGGL(combine_kernel<256>, dim3(p.B * p.T * p.H), dim3(256), 0, st, p);
+    return check(err);
+}
+
 template <int NB, int RT, bool QLO>
 int launch_decode_t(const DecodeParams& p, hipStream_t st, const char** err) {
     constexpr int lds = dec::Layout<NB, RT>::BYTES;
@@ -315,8 +323,7 @@ int launch_decode_t(const DecodeParams& p, hipStream_t st, const char** err) {
     const int grid = (items + 7) & ~7;
     hipLaunchKernelGGL((dec::decode_mfma<NB, RT, QLO>), dim3(grid), dim3(256), lds, st, p);
     if (check(err)) return 1;
-    hipLaunchKernelGGL(combine_kernel, dim3(p.B * p.T * p.H), dim3(kCombineThreads), 0, st, p);
-    return check(err);
+    return launch_combine(p, st, err);
 }
 
 template <int NB, int RT, bool QLO>
@@ -334,8 +341,7 @@ int launch_rows_t(const DecodeParams& p, hipStream_t st, const char** err) {
     const int grid = (items + 7) & ~7;
     hipLaunchKernelGGL((rows::decode_rows<NB, RT, QLO>), dim3(grid), dim3(64 * p.gh * RT), p.lds, st, p);
     if (check(err)) return 1;
-    hipLaunchKernelGGL(combine_kernel, dim3(p.B * p.T * p.H), dim3(kCombineThreads), 0, st, p);
-    return check(err);
+    return launch_combine(p, st, err);
 }
 
 template <int NB, int RTW, bool QLO>
@@ -353,8 +359,7 @@ int launch_stream_t(const DecodeParams& p, hipStream_t st, const char** err) {
     const int grid = (items + 7) & ~7;
     hipLaunchKernelGGL((stream::decode_stream<NB, RTW, QLO>), dim3(grid), dim3(64 * p.gh), p.lds, st, p);
     if (check(err)) return 1;
-    hipLaunchKernelGGL(combine_kernel, dim3(p.B * p.T * p.H), dim3(kCombineThreads), 0, st, p);
-    return check(err);
+    return launch_combine(p, st, err);
 }
 
 template <int NB>
