@@ -80,6 +80,9 @@ def parse():
     ap.add_argument("--workload", default="qwen_gqa")
     ap.add_argument("--layers", type=int, default=0)
     ap.add_argument("--split-rows", type=int, default=0)
+    ap.add_argument("--tiling", default="", metavar="KERNEL,HEAD_GROUP",
+                    help="decode kernel (1 per-head, 2 whole-row, 3 stream) and KV heads per "
+                         "workgroup, as kvq_set_decode_tiling; default: the library's choice")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--graph", choices=("auto", "on", "off"), default="auto",
@@ -107,7 +110,7 @@ def calibrate_copy(nbytes: int):
                       "ms": round(dt * 1e3, 4), "GBps_read_plus_write": round(2 * nbytes / dt / 1e9, 1)}))
 
 
-def build_layers(w, L, dev, split_rows):
+def build_layers(w, L, dev, split_rows, tiling=""):
     import torch
 
     from decode_attention_quantized_append_amd import KvqLayerCache
@@ -123,6 +126,9 @@ def build_layers(w, L, dev, split_rows):
     for c in caches:
         if split_rows:
             c.set_split_rows(split_rows)
+        if tiling:
+            kern, gh = (int(x) for x in tiling.split(","))
+            c.set_decode_tiling(kern, gh, 0)
     torch.cuda.synchronize(dev)
     return caches, cap
 
@@ -131,7 +137,7 @@ def run_gpu(w, args):
     import torch
     dev = torch.device("cuda:0")
     L = args.layers or default_layers(w)
-    caches, cap = build_layers(w, L, dev, args.split_rows)
+    caches, cap = build_layers(w, L, dev, args.split_rows, args.tiling)
     tdt = torch.bfloat16 if w.io_dtype == "bf16" else torch.float32
     pre = w.pre_step_lengths()
     k, v = w.kv_block([w.T] * w.B, pre, w.T)
@@ -202,19 +208,15 @@ def run_gpu(w, args):
     app_ms = [e[0].elapsed_time(e[1]) for e in events]
     dec_ms = [e[1].elapsed_time(e[2]) for e in events]
     if use_graph:
-        # one graph per layer for the whole step, one for its decode call alone
+        # one graph per layer for the whole step; the per-call times stay those
+        # of the eager steps above (HIP events between the library calls)
         cap_st = torch.cuda.Stream(dev)
-        steps_g, dec_g = [], []
+        steps_g = []
         for li in range(L):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap_st):
                 one_step(li, st=cap_st.cuda_stream)
             steps_g.append(g)
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=cap_st):
-                check(lib.kvq_decode(caches[li].h, qp, dt, T, sink_ptr, scale, op, lp, ws_ptr, ws_bytes,
-                                     cap_st.cuda_stream), "decode")
-            dec_g.append(g)
         for i in range(args.warmup):
             steps_g[i % L].replay()
         torch.cuda.synchronize(dev)
@@ -223,13 +225,6 @@ def run_gpu(w, args):
             steps_g[(args.warmup + i) % L].replay()
         torch.cuda.synchronize(dev)
         wall = time.perf_counter() - t0
-        dev_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-        for i in range(args.steps):
-            dev_ev[i][0].record()
-            dec_g[(args.warmup + i) % L].replay()
-            dev_ev[i][1].record()
-        torch.cuda.synchronize(dev)
-        dec_ms = [e[0].elapsed_time(e[1]) for e in dev_ev]   # the decode call's graph replay
     kv_bytes = w.kv_bytes_per_decode()
     ms_step = wall * 1e3 / args.steps
     dec_avg = sum(dec_ms) / len(dec_ms)

@@ -300,6 +300,10 @@ __global__ __launch_bounds__(RTW == 1 ? 512 : 256, stream_waves_per_simd(NB, RTW
                 }
             }
         }
+        // The waves of a workgroup read adjacent head slices of the same rows,
+        // which share cache lines at the slice edges; requesting the next
+        // tile together lets those lines be fetched from HBM once.
+        if (p.gh > 1) __builtin_amdgcn_s_barrier();
         if (next) issue_k(t0 + kTile);
 
         // ---- online softmax against a reference max that moves only when a

@@ -173,7 +173,7 @@ int64_t span_of(const kvq_cache* h, int b, int32_t T) {
 
 // Chooses the decode kernel and its tiling.  Returns false when a kernel or
 // tiling set with kvq_set_decode_tiling does not fit the shape.
-bool choose_kernel(const kvq_cache* h, int R, int32_t T, bool f32_queries, Plan* p) {
+bool choose_kernel(const kvq_cache* h, int R, int32_t T, Plan* p) {
     const kvq_config& c = h->cfg;
     const int NB = c.head_dim / 32;
     const int RT = (R + 15) / 16;
@@ -192,17 +192,11 @@ bool choose_kernel(const kvq_cache* h, int R, int32_t T, bool f32_queries, Plan*
     if (!aligned_start_resident(h, T)) return true;
     if (want == KVQ_DECODE_STREAM) {
         int gh = h->head_group;
-        if (gh == 0) {
-            // the head group that keeps the most waves resident per CU (the
-            // larger group on a tie): whole workgroups, within registers and LDS
-            const int waves = 4 * kvq::stream_waves_per_simd(NB, RT, f32_queries);
-            int best = 0;
-            for (int k = std::min(c.n_kv_heads, 8); k >= 1; --k) {
-                if (!stream_ok(c, R, k)) continue;
-                const int wgs = std::min(waves / k, kvq::kLdsBytes / (k * kvq::stream_wave_bytes(NB)));
-                if (wgs * k > best) best = wgs * k, gh = k;
-            }
-        }
+        if (gh == 0)
+            // the largest head group: the waves of one workgroup share the
+            // cache lines at the edges of adjacent head slices
+            for (int k = std::min(c.n_kv_heads, 8); k >= 1 && gh == 0; --k)
+                if (stream_ok(c, R, k)) gh = k;
         if (!stream_ok(c, R, gh)) return h->decode_kernel == KVQ_DECODE_AUTO;
         p->kernel = kvq::kStream;
         p->gh = gh;
@@ -243,7 +237,7 @@ Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nul
         maxvis = std::max(maxvis, vis);
     }
     Plan p{};
-    const bool ok = choose_kernel(h, R, T, f32_queries, &p);
+    const bool ok = choose_kernel(h, R, T, &p);
     if (fits) *fits = ok;
     int64_t chunk = h->split_rows;
     if (p.kernel != kvq::kPerHead) {

@@ -275,10 +275,9 @@ def test_decode_kernel_choice(lib):
     p = plan_of(lib, h)
     assert (p["kernel"], p["gh"]) == (STREAM, 8) and 0 < p["lds"] <= 160 * 1024 and p["chunk"] % 32 == 0
     assert p["splits"] == -(-8192 // p["chunk"])
-    # fp32 queries keep a low fp16 part: more registers, 12 waves per CU, so
-    # groups of 4 heads (three workgroups per CU) keep all of them resident
+    # fp32 queries too: all heads of a row in one workgroup
     p = plan_of(lib, h, dtype=kvq.KVQ_F32)
-    assert (p["kernel"], p["gh"]) == (STREAM, 4)
+    assert (p["kernel"], p["gh"]) == (STREAM, 8)
     kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_PER_HEAD, 0, 0, lib)
     assert plan_of(lib, h)["kernel"] == PER_HEAD
     kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_WHOLE_ROW, 8, 1, lib)
