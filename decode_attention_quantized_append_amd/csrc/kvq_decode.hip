@@ -397,15 +397,17 @@ constexpr int min_blocks() { return NB * RT <= 4 ? 2 : 1; }
 // has no empty workgroups and an XCD's contiguous share of it is a fair share
 // of the rows whatever the length mix.  Chunk counts come from the device
 // lengths, 64 sessions per step (a wave-wide prefix sum).  b = -1 past the
-// last unit.  Every lane of the wave calls it with the same u.
-__device__ __forceinline__ void locate_unit(const DecodeParams& p, int u, int& b, int& s) {
+// last unit; len and base are session b's counters, read in the same step.
+// Every lane of the wave calls it with the same u.
+__device__ __forceinline__ void locate_unit(const DecodeParams& p, int u, int& b, int& s, int& len_b, int& base_b) {
     const int lane = threadIdx.x & 63;
-    int fb = -1, fs = 0;
+    int fb = -1, fs = 0, fl = 0, fbase = 0;
     for (int b0 = 0; b0 < p.B && fb < 0; b0 += 64) {
         const int bb = b0 + lane;
-        int n = 0;
+        int n = 0, len = 0, base = 0;
         if (bb < p.B) {
-            const int len = p.len_d[bb];
+            len = p.len_d[bb];
+            base = p.base_d[bb];
             const int lo = p.window > 0 ? max(0, len - p.T + 1 - p.window) : 0;
             const int span = len - (lo & ~31);
             n = span > 0 ? (span + p.chunk - 1) / p.chunk : 0;
@@ -421,12 +423,16 @@ __device__ __forceinline__ void locate_unit(const DecodeParams& p, int u, int& b
             const int lb = __builtin_amdgcn_readfirstlane(__builtin_ctzll(__ballot(incl > u)));
             fb = b0 + lb;
             fs = u - __builtin_amdgcn_readlane(incl - n, lb);
+            fl = __builtin_amdgcn_readlane(len, lb);
+            fbase = __builtin_amdgcn_readlane(base, lb);
         } else {
             u -= total;
         }
     }
     b = __builtin_amdgcn_readfirstlane(fb);
     s = __builtin_amdgcn_readfirstlane(fs);
+    len_b = __builtin_amdgcn_readfirstlane(fl);
+    base_b = __builtin_amdgcn_readfirstlane(fbase);
 }
 
 template <int NB, int RT, bool QLO>
@@ -447,8 +453,8 @@ __global__ __launch_bounds__(256, (min_blocks<NB, RT>())) void decode_mfma(Decod
     const int wid = blockIdx.x;
     const int L = (wid & 7) * (W >> 3) + (wid >> 3);
     const int g = L % p.Hkv;
-    int b, s;
-    locate_unit(p, L / p.Hkv, b, s);
+    int b, s, len, base;
+    locate_unit(p, L / p.Hkv, b, s, len, base);
     if (b < 0) return;
     const int R = p.T * p.hpk;
 
@@ -483,8 +489,6 @@ __global__ __launch_bounds__(256, (min_blocks<NB, RT>())) void decode_mfma(Decod
         }
     }
 
-    const int len = p.len_d[b];
-    const int base = p.base_d[b];
     const int lo_all = p.window > 0 ? max(0, len - p.T + 1 - p.window) : 0;
     const int c0 = (lo_all & ~31) + s * p.chunk;   // chunks start on a 32-row boundary
     const int c1 = min(c0 + p.chunk, len);

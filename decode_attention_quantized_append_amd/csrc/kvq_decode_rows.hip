@@ -109,8 +109,8 @@ __global__ __launch_bounds__(512) void decode_rows(DecodeParams p) {
     const int W = gridDim.x, wid = blockIdx.x;
     const int L = (wid & 7) * (W >> 3) + (wid >> 3);
     const int hg = L % ngrp;
-    int b, s;
-    dec::locate_unit(p, L / ngrp, b, s);
+    int b, s, len, base;
+    dec::locate_unit(p, L / ngrp, b, s, len, base);
     if (b < 0) return;
     const int gi = wave % gh, rt = wave / gh, g = hg * gh + gi;
     const int R = p.T * p.hpk;
@@ -154,8 +154,6 @@ __global__ __launch_bounds__(512) void decode_rows(DecodeParams p) {
         }
     }
 
-    const int len = p.len_d[b];
-    const int base = p.base_d[b];
     const int lo = p.window > 0 ? max(0, len - p.T + 1 - p.window) : 0;
     const int c0 = (lo & ~(kTile - 1)) + s * p.chunk;
     const int c1 = min(c0 + p.chunk, len);

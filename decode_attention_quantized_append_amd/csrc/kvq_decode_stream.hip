@@ -99,53 +99,12 @@ __global__ __launch_bounds__(RTW == 1 ? 512 : 256, stream_waves_per_simd(NB, RTW
     const int W = gridDim.x, wid = blockIdx.x;
     const int L = (wid & 7) * (W >> 3) + (wid >> 3);
     const int hg = L % ngrp;
-    int b, s;
-    dec::locate_unit(p, L / ngrp, b, s);
+    int b, s, len, base;
+    dec::locate_unit(p, L / ngrp, b, s, len, base);
     if (b < 0) return;
     const int g = hg * gh + wave;
     const int R = p.T * p.hpk;
 
-    // Q rows rt*16 + j16 as the B operand of S^T = K Q^T
-    h8 qh[RTW][NB], ql[RTW][NB];
-#pragma unroll
-    for (int rt = 0; rt < RTW; ++rt) {
-        const int r = rt * 16 + j16;
-        const bool real = r < R;
-        const int t = real ? r / p.hpk : 0, hh = real ? r % p.hpk : 0;
-        const size_t i0 = (((size_t)b * p.T + t) * p.H + g * p.hpk + hh) * HD + 8 * q4;
-#pragma unroll
-        for (int blk = 0; blk < NB; ++blk) {
-            float qv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qv[e] = 0.0f;
-            if (real) {
-                if (p.dtype == 1) {
-                    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + i0 + blk * 32);
-                    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        qv[2 * e] = __uint_as_float(w4[e] << 16);
-                        qv[2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
-                    }
-                } else {
-                    const float* src = static_cast<const float*>(p.q) + i0 + blk * 32;
-                    const float4 a = *reinterpret_cast<const float4*>(src);
-                    const float4 c = *reinterpret_cast<const float4*>(src + 4);
-                    qv[0] = a.x; qv[1] = a.y; qv[2] = a.z; qv[3] = a.w;
-                    qv[4] = c.x; qv[5] = c.y; qv[6] = c.z; qv[7] = c.w;
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const _Float16 xh = (_Float16)qv[e];
-                qh[rt][blk][e] = xh;
-                if (QLO) ql[rt][blk][e] = (_Float16)(qv[e] - (float)xh);
-            }
-        }
-    }
-
-    const int len = p.len_d[b];
-    const int base = p.base_d[b];
     const int lo = p.window > 0 ? max(0, len - p.T + 1 - p.window) : 0;
     const int c0 = (lo & ~(kTile - 1)) + s * p.chunk;
     const int c1 = min(c0 + p.chunk, len);
@@ -236,6 +195,47 @@ __global__ __launch_bounds__(RTW == 1 ? 512 : 256, stream_waves_per_simd(NB, RTW
     // read the V rows.
     issue_k(c0);
     issue_v(c0);
+
+    // Q rows rt*16 + j16 as the B operand of S^T = K Q^T, read while the
+    // first tile's rows are in flight
+    h8 qh[RTW][NB], ql[RTW][NB];
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+        const int r = rt * 16 + j16;
+        const bool real = r < R;
+        const int t = real ? r / p.hpk : 0, hh = real ? r % p.hpk : 0;
+        const size_t i0 = (((size_t)b * p.T + t) * p.H + g * p.hpk + hh) * HD + 8 * q4;
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+            float qv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qv[e] = 0.0f;
+            if (real) {
+                if (p.dtype == 1) {
+                    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + i0 + blk * 32);
+                    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        qv[2 * e] = __uint_as_float(w4[e] << 16);
+                        qv[2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
+                    }
+                } else {
+                    const float* src = static_cast<const float*>(p.q) + i0 + blk * 32;
+                    const float4 a = *reinterpret_cast<const float4*>(src);
+                    const float4 c = *reinterpret_cast<const float4*>(src + 4);
+                    qv[0] = a.x; qv[1] = a.y; qv[2] = a.z; qv[3] = a.w;
+                    qv[4] = c.x; qv[5] = c.y; qv[6] = c.z; qv[7] = c.w;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const _Float16 xh = (_Float16)qv[e];
+                qh[rt][blk][e] = xh;
+                if (QLO) ql[rt][blk][e] = (_Float16)(qv[e] - (float)xh);
+            }
+        }
+    }
+
     for (int t0 = c0; t0 < c1; t0 += kTile) {
         const bool whole = t0 + kTile <= c1;             // this tile issued all its loads
         const bool next = t0 + kTile < c1;
