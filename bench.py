@@ -80,9 +80,10 @@ def parse():
     ap.add_argument("--workload", default="qwen_gqa")
     ap.add_argument("--layers", type=int, default=0)
     ap.add_argument("--split-rows", type=int, default=0)
-    ap.add_argument("--tiling", default="", metavar="KERNEL,HEAD_GROUP",
-                    help="decode kernel (1 per-head, 2 whole-row, 3 stream) and KV heads per "
-                         "workgroup, as kvq_set_decode_tiling; default: the library's choice")
+    ap.add_argument("--tiling", default="", metavar="KERNEL,HEAD_GROUP[,SUB]",
+                    help="decode kernel (1 per-head, 2 whole-row, 3 stream), KV heads per "
+                         "workgroup and sub_tiles, as kvq_set_decode_tiling; default: the "
+                         "library's choice")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--graph", choices=("auto", "on", "off"), default="auto",
@@ -127,8 +128,8 @@ def build_layers(w, L, dev, split_rows, tiling=""):
         if split_rows:
             c.set_split_rows(split_rows)
         if tiling:
-            kern, gh = (int(x) for x in tiling.split(","))
-            c.set_decode_tiling(kern, gh, 0)
+            parts = [int(x) for x in tiling.split(",")]
+            c.set_decode_tiling(parts[0], parts[1], parts[2] if len(parts) > 2 else 0)
     torch.cuda.synchronize(dev)
     return caches, cap
 

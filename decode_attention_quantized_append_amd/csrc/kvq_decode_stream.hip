@@ -86,8 +86,12 @@ __device__ __forceinline__ h8 v_codes_sub(uint32_t lo, uint32_t hi) {
     return __builtin_bit_cast(h8, w);
 }
 
-template <int NB, int RTW, bool QLO>
-__global__ __launch_bounds__(RTW == 1 ? 512 : 256, stream_waves_per_simd(NB, RTW, QLO)) void decode_stream(DecodeParams p) {
+// NB blocks of 32 dims per head; RTW row tiles of 16 per wave; QLO: fp32
+// queries (a low fp16 part kept beside the high one); RS row streams.
+template <int NB, int RTW, bool QLO, int RS>
+__global__ __launch_bounds__(64 * RS * (RTW == 1 ? 8 : 4), stream_waves_per_simd(NB, RTW, QLO)) void decode_stream(
+    DecodeParams p) {
+    static_assert(RS == 1 || RTW == 1, "row streams need one row tile per wave");
     using WN = Win<NB>;
     constexpr int HD = NB * 32;
     extern __shared__ __align__(16) uint8_t smem[];
@@ -95,6 +99,8 @@ __global__ __launch_bounds__(RTW == 1 ? 512 : 256, stream_waves_per_simd(NB, RTW
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int q4 = lane >> 4, j16 = lane & 15;
     const int gh = p.gh, ngrp = p.Hkv / gh;
+    constexpr int rs = RS;
+    const int gi = wave % gh, str = wave / gh;   // head in the group, row stream
 
     const int W = gridDim.x, wid = blockIdx.x;
     const int L = (wid & 7) * (W >> 3) + (wid >> 3);
@@ -102,7 +108,7 @@ __global__ __launch_bounds__(RTW == 1 ? 512 : 256, stream_waves_per_simd(NB, RTW
     int b, s, len, base;
     dec::locate_unit(p, L / ngrp, b, s, len, base);
     if (b < 0) return;
-    const int g = hg * gh + wave;
+    const int g = hg * gh + gi;
     const int R = p.T * p.hpk;
 
     const int lo = p.window > 0 ? max(0, len - p.T + 1 - p.window) : 0;
@@ -193,8 +199,17 @@ __global__ __launch_bounds__(RTW == 1 ? 512 : 256, stream_waves_per_simd(NB, RTW
     // Loads in issue order: K(0) V(0) | K(1) .. V(1) | ...  K(t+1) is issued
     // once the scores of tile t have read the K rows, V(t+1) once its P V has
     // read the V rows.
-    issue_k(c0);
-    issue_v(c0);
+    // Row stream str takes the chunk's tiles str, str + rs, ...; a stream
+    // with fewer tiles than stream 0 meets stream 0's remaining barriers
+    // after its loop.
+    const int ntiles = (c1 - c0 + kTile - 1) / kTile;
+    const int nit = (ntiles + rs - 1) / rs;                   // stream 0's tiles
+    const int mine = ntiles > str ? (ntiles - str + rs - 1) / rs : 0;
+    const int first = c0 + str * kTile;
+    if (first < c1) {
+        issue_k(first);
+        issue_v(first);
+    }
 
     // Q rows rt*16 + j16 as the B operand of S^T = K Q^T, read while the
     // first tile's rows are in flight
@@ -236,10 +251,13 @@ __global__ __launch_bounds__(RTW == 1 ? 512 : 256, stream_waves_per_simd(NB, RTW
         }
     }
 
-    for (int t0 = c0; t0 < c1; t0 += kTile) {
+    for (int it = 0; it < mine; ++it) {
+        const int t0 = first + it * rs * kTile;
+        const int tn = t0 + rs * kTile;                  // its next tile
         const bool whole = t0 + kTile <= c1;             // this tile issued all its loads
-        const bool next = t0 + kTile < c1;
-        const bool next_whole = t0 + 2 * kTile <= c1;
+        const bool next = tn < c1;
+        const bool next_whole = tn + kTile <= c1;
+        float sv[RTW][2][4];
         // K(t) has landed; V(t), issued after it, may still be in flight
         if (whole) wait_loads_upto<WN::NVI>(); else wait_loads_upto<0>();
 
@@ -256,7 +274,6 @@ __global__ __launch_bounds__(RTW == 1 ? 512 : 256, stream_waves_per_simd(NB, RTW
         dec::lds_order();
 
         // ---- scores S^T: sv[rt][h][i] = S[row rt*16 + j16][key 16h + 4*q4 + i] (base 2)
-        float sv[RTW][2][4];
 #pragma unroll
         for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
@@ -302,9 +319,10 @@ __global__ __launch_bounds__(RTW == 1 ? 512 : 256, stream_waves_per_simd(NB, RTW
         }
         // The waves of a workgroup read adjacent head slices of the same rows,
         // which share cache lines at the slice edges; requesting the next
-        // tile together lets those lines be fetched from HBM once.
-        if (p.gh > 1) __builtin_amdgcn_s_barrier();
-        if (next) issue_k(t0 + kTile);
+        // tile together lets those lines be fetched from HBM once (and keeps
+        // the row streams of a CU in step).
+        if (gh * rs > 1) __builtin_amdgcn_s_barrier();
+        if (next) issue_k(tn);
 
         // ---- online softmax against a reference max that moves only when a
         // score passes it by more than 8 (so p <= 256, well inside fp16)
@@ -417,27 +435,84 @@ __global__ __launch_bounds__(RTW == 1 ? 512 : 256, stream_waves_per_simd(NB, RTW
                 macc[rt] = dec::mfma(pu, mb, macc[rt]);
             }
         }
-        if (next) issue_v(t0 + kTile);
+        if (next) issue_v(tn);
     }
+    if (RS > 1)
+        for (int it = mine; it < nit; ++it) __builtin_amdgcn_s_barrier();
 
-    // ---- finish: row sums over the four lane groups; offsets into O; partials
-    const size_t row0 = ((size_t)b * p.splits + s) * p.T;
+    // ---- finish: row sums over the four lane groups; offsets into O
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
         float l = lsum[rt];
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
+        lsum[rt] = l;
 #pragma unroll
         for (int dt = 0; dt < 2 * NB; ++dt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)   // the code products carry a factor 2^-24
                 oacc[rt][dt][i] = fmaf(oacc[rt][dt][i], 0x1p24f, __shfl(macc[rt][i], 16 * q4 + dt / 2));
+    }
+    // ---- row streams: the other streams hand (m, l, O) to stream 0 through
+    // their own LDS buffers (lane-major, so that the 64 lanes hit 64 banks);
+    // only one-row-tile shapes run more than one stream
+    if constexpr (RS > 1) {
+        constexpr int MOFS = RTW * 2 * NB * 4 * 64;      // floats before m, l
+        static_assert((MOFS + 64 * RTW) * 4 <= WN::BYTES, "row-stream hand-off does not fit the wave buffer");
+        __builtin_amdgcn_s_waitcnt(0xC07F);              // this wave's reads of its buffer are done
+        float* const xb = reinterpret_cast<float*>(wb);
+        if (str > 0) {
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt) {
+#pragma unroll
+                for (int dt = 0; dt < 2 * NB; ++dt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) xb[((rt * 2 * NB + dt) * 4 + i) * 64 + lane] = oacc[rt][dt][i];
+                if (q4 == 0) {
+                    xb[MOFS + rt * 32 + j16] = mrow[rt];
+                    xb[MOFS + rt * 32 + 16 + j16] = lsum[rt];
+                }
+            }
+        }
+        rows::lds_barrier();
+        if (str == 0) {
+            for (int o = 1; o < rs; ++o) {
+                const float* const yb = reinterpret_cast<const float*>(smem + (wave + o * gh) * WN::BYTES);
+#pragma unroll
+                for (int rt = 0; rt < RTW; ++rt) {
+                    const float m1 = yb[MOFS + rt * 32 + j16], l1 = yb[MOFS + rt * 32 + 16 + j16];
+                    const float M = fmaxf(mrow[rt], m1);
+                    const float a0 = (mrow[rt] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mrow[rt] - M);
+                    const float a1 = (m1 == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m1 - M);
+                    lsum[rt] = a0 * lsum[rt] + a1 * l1;
+                    mrow[rt] = M;
+                    float A0[4], A1[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {   // O rows 4*q4 + i
+                        A0[i] = __shfl(a0, 4 * q4 + i);
+                        A1[i] = __shfl(a1, 4 * q4 + i);
+                    }
+#pragma unroll
+                    for (int dt = 0; dt < 2 * NB; ++dt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            oacc[rt][dt][i] = A0[i] * oacc[rt][dt][i] +
+                                              A1[i] * yb[((rt * 2 * NB + dt) * 4 + i) * 64 + lane];
+                }
+            }
+        }
+        if (str > 0) return;
+    }
+    // ---- partials of this (session, chunk)
+    const size_t row0 = ((size_t)b * p.splits + s) * p.T;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
         const int r = rt * 16 + j16;
         if (q4 == 0 && r < R) {
             const int t = r / p.hpk, hq = g * p.hpk + r % p.hpk;
             const size_t idx = (row0 + t) * p.H + hq;
             p.part_ml[2 * idx] = (mrow[rt] == -INFINITY) ? -INFINITY : mrow[rt] * kLn2;
-            p.part_ml[2 * idx + 1] = l;
+            p.part_ml[2 * idx + 1] = lsum[rt];
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {

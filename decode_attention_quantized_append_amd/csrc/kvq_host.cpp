@@ -123,6 +123,7 @@ struct Plan {
     int32_t units;     // (session, chunk) pairs with rows
     int32_t gh;        // KV heads per workgroup (whole-row and stream kernels)
     int32_t sub;       // whole-row kernel: rows per buffer / 32
+    int32_t rs;        // stream kernel: row streams (waves per KV head)
     int32_t lds;       // dynamic LDS bytes
     int32_t rows;      // rows per buffer (chunks are a multiple)
     kvq::RowGeo geo;
@@ -156,6 +157,15 @@ bool stream_ok(const kvq_config& c, int R, int gh) {
     const int RT = (R + 15) / 16;
     if (gh > (RT == 1 ? 8 : 4)) return false;
     return gh * kvq::stream_wave_bytes(NB) <= kvq::kLdsBytes;
+}
+
+// Can the stream kernel run two waves per KV head (two row streams) in one
+// workgroup: one row tile per wave, and twice the waves and LDS still fit a CU?
+bool stream_rs2_ok(const kvq_config& c, int R, int gh) {
+    const int NB = c.head_dim / 32;
+    if (R > 16) return false;
+    const int waves = 4 * kvq::stream_waves_per_simd(NB, 1, false);
+    return 2 * gh * kvq::stream_wave_bytes(NB) <= kvq::kLdsBytes && 2 * gh <= waves;
 }
 
 // Is every session's first visible row, rounded down to 32, still resident?
@@ -200,7 +210,9 @@ bool choose_kernel(const kvq_cache* h, int R, int32_t T, Plan* p) {
         if (!stream_ok(c, R, gh)) return h->decode_kernel == KVQ_DECODE_AUTO;
         p->kernel = kvq::kStream;
         p->gh = gh;
-        p->lds = gh * kvq::stream_wave_bytes(NB);
+        p->rs = h->sub_tiles;                       // 0: chosen with the chunk
+        if (p->rs == 2 && !stream_rs2_ok(c, R, gh)) return false;
+        p->lds = gh * std::max(1, p->rs) * kvq::stream_wave_bytes(NB);
         p->rows = kvq::stream_rows_per_buffer(NB);
         return true;
     }
@@ -241,25 +253,38 @@ Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nul
     if (fits) *fits = ok;
     int64_t chunk = h->split_rows;
     if (p.kernel != kvq::kPerHead) {
-        if (chunk <= 0) {
-            // one round of workgroups: as many as fit on the 256 CUs at once
-            // (bound by LDS and by the waves the register file holds), each a
-            // whole number of buffers
-            const int64_t ngrp = c.n_kv_heads / p.gh;
-            const int64_t waves_per_wg = p.kernel == kvq::kStream ? p.gh : p.gh * ((R + 15) / 16);
+        const int64_t ngrp = c.n_kv_heads / p.gh;
+        const int RT = (R + 15) / 16;
+        // one round of workgroups: as many as fit on the 256 CUs at once
+        // (bound by LDS and by the waves the register file holds), each a
+        // whole number of buffers
+        auto one_round = [&](int rs) {
+            const int64_t waves_per_wg = p.kernel == kvq::kStream ? p.gh * rs : p.gh * RT;
             const int64_t waves_per_cu =
-                p.kernel == kvq::kStream ? 4 * kvq::stream_waves_per_simd(c.head_dim / 32, R > 16 ? 2 : 1, f32_queries) : 8;
-            const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kvq::kLdsBytes / p.lds,
+                p.kernel == kvq::kStream ? 4 * kvq::stream_waves_per_simd(c.head_dim / 32, RT, f32_queries) : 8;
+            const int64_t lds = p.kernel == kvq::kStream ? p.gh * rs * kvq::stream_wave_bytes(c.head_dim / 32) : p.lds;
+            const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kvq::kLdsBytes / lds,
                                                                            waves_per_cu / waves_per_wg));
             const int64_t slots = 256 * per_cu;
-            chunk = round_up(std::max<int64_t>(1, ceil_div(total * ngrp, slots)), p.rows);
+            int64_t ch = round_up(std::max<int64_t>(1, ceil_div(total * ngrp, slots)), p.rows);
             for (;;) {
                 int64_t wgs = 0;
-                for (int b = 0; b < c.n_seqs; ++b) wgs += ceil_div(span_of(h, b, T), chunk) * ngrp;
+                for (int b = 0; b < c.n_seqs; ++b) wgs += ceil_div(span_of(h, b, T), ch) * ngrp;
                 if (wgs <= slots) break;
-                chunk += p.rows;
+                ch += p.rows;
             }
+            return ch;
+        };
+        if (p.kernel == kvq::kStream) {
+            // two row streams per head when each still gets a few tiles of
+            // its chunk: the waves of a CU then advance together, and there
+            // are half as many partials to combine
+            const bool rs2 = stream_rs2_ok(c, R, p.gh) && !f32_queries;
+            if (p.rs == 0) p.rs = (rs2 && (chunk > 0 ? chunk : one_round(2)) >= 4 * 32) ? 2 : 1;
+            if (p.rs == 2 && !rs2 && fits) *fits = false;
+            p.lds = p.gh * p.rs * kvq::stream_wave_bytes(c.head_dim / 32);
         }
+        if (chunk <= 0) chunk = one_round(p.kernel == kvq::kStream ? p.rs : 1);
         chunk = round_up(chunk, p.rows);
     } else if (chunk <= 0) {
         // About 2048 workgroups of (session, chunk, KV head), i.e. several per
@@ -500,6 +525,7 @@ kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, c
     dp.kernel = p.kernel;
     dp.gh = p.gh;
     dp.sub = p.sub;
+    dp.rs = p.rs;
     dp.lds = p.lds;
     dp.geo = p.geo;
     dp.scale = scale;
@@ -550,8 +576,9 @@ kvq_status kvq_set_decode_tiling(kvq_cache* h, int32_t kernel, int32_t head_grou
         return fail(KVQ_EINVAL, "head_group must be 0 or a divisor of n_kv_heads");
     if (head_group > 0 && kernel != KVQ_DECODE_WHOLE_ROW && kernel != KVQ_DECODE_STREAM)
         return fail(KVQ_EINVAL, "head_group applies to the whole-row and stream kernels");
-    if (sub_tiles != 0 && (kernel != KVQ_DECODE_WHOLE_ROW || (sub_tiles != 1 && sub_tiles != 2 && sub_tiles != 4)))
-        return fail(KVQ_EINVAL, "sub_tiles must be 0, or 1, 2 or 4 for the whole-row kernel");
+    if (sub_tiles != 0 && !(kernel == KVQ_DECODE_WHOLE_ROW && (sub_tiles == 1 || sub_tiles == 2 || sub_tiles == 4)) &&
+        !(kernel == KVQ_DECODE_STREAM && (sub_tiles == 1 || sub_tiles == 2)))
+        return fail(KVQ_EINVAL, "sub_tiles must be 0, or 1, 2 or 4 for the whole-row kernel, 1 or 2 for the stream kernel");
     h->decode_kernel = kernel;
     h->head_group = head_group;
     h->sub_tiles = sub_tiles;

@@ -171,6 +171,8 @@ struct DecodeParams {
     int32_t kernel;             // DecodeKernel
     int32_t gh;                 // KV heads per workgroup (whole-row and stream kernels)
     int32_t sub;                // whole-row kernel: rows per buffer / 32
+    int32_t rs;                 // stream kernel: waves per KV head in a workgroup, each
+                                // taking every rs-th tile of the chunk (1 or 2)
     int32_t lds;                // dynamic LDS bytes of the decode workgroup
     RowGeo geo;                 // whole-row kernel geometry
     float scale;

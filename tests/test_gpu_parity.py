@@ -152,9 +152,9 @@ def test_decode_split_invariance():
 PH, WR, ST = kvq.KVQ_DECODE_PER_HEAD, kvq.KVQ_DECODE_WHOLE_ROW, kvq.KVQ_DECODE_STREAM
 TILINGS = {
     "qwen_gqa_small": [(WR, 8, 1), (WR, 4, 1), (WR, 4, 2), (WR, 2, 1), (WR, 2, 2), (ST, 8, 0), (ST, 2, 0),
-                       (ST, 1, 0)],
-    "batched_small": [(WR, 8, 1), (WR, 4, 2), (WR, 2, 1), (ST, 8, 0), (ST, 4, 0)],
-    "sink_ring_small": [(WR, 8, 1), (WR, 8, 2), (WR, 4, 1), (WR, 4, 4), (ST, 8, 0), (ST, 2, 0)],
+                       (ST, 1, 0), (ST, 8, 1), (ST, 8, 2), (ST, 2, 2)],
+    "batched_small": [(WR, 8, 1), (WR, 4, 2), (WR, 2, 1), (ST, 8, 0), (ST, 4, 0), (ST, 8, 2), (ST, 4, 2)],
+    "sink_ring_small": [(WR, 8, 1), (WR, 8, 2), (WR, 4, 1), (WR, 4, 4), (ST, 8, 0), (ST, 2, 0), (ST, 8, 2)],
     "verify_small": [(WR, 4, 1), (WR, 2, 1), (WR, 2, 2), (WR, 1, 1), (WR, 1, 2), (ST, 4, 0), (ST, 1, 0)],
     "qwen_f32_small": [(WR, 8, 1), (WR, 2, 2), (ST, 8, 0), (ST, 4, 0)],
     "tiny": [(ST, 1, 0)],

@@ -274,7 +274,9 @@ def test_decode_kernel_choice(lib):
     kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 8192, None, 0, lib)
     p = plan_of(lib, h)
     assert (p["kernel"], p["gh"]) == (STREAM, 8) and 0 < p["lds"] <= 160 * 1024 and p["chunk"] % 32 == 0
-    assert p["splits"] == -(-8192 // p["chunk"])
+    assert p["splits"] == -(-8192 // p["chunk"]) == p["units"]
+    # 8192 rows fill the GPU with one tile per wave: one row stream
+    assert p["rs"] == 1
     # fp32 queries too: all heads of a row in one workgroup
     p = plan_of(lib, h, dtype=kvq.KVQ_F32)
     assert (p["kernel"], p["gh"]) == (STREAM, 8)
@@ -292,7 +294,7 @@ def test_decode_kernel_choice(lib):
     E = kvq.KVQ_EINVAL
     assert err(lib, kvq.kvq_set_decode_tiling, h, kvq.KVQ_DECODE_WHOLE_ROW, 3, 0) == E   # does not divide 8
     assert err(lib, kvq.kvq_set_decode_tiling, h, kvq.KVQ_DECODE_WHOLE_ROW, 2, 3) == E   # no such depth
-    assert err(lib, kvq.kvq_set_decode_tiling, h, kvq.KVQ_DECODE_STREAM, 2, 1) == E      # depth is whole-row only
+    assert err(lib, kvq.kvq_set_decode_tiling, h, kvq.KVQ_DECODE_STREAM, 2, 4) == E      # 1 or 2 row streams
     assert err(lib, kvq.kvq_set_decode_tiling, h, kvq.KVQ_DECODE_PER_HEAD, 2, 0) == E    # no head groups there
     assert err(lib, kvq.kvq_set_decode_tiling, h, 4, 0, 0) == E
     # one head of 128 is not a whole number of 16-byte pieces for the whole-row kernel: that call fails
@@ -319,6 +321,26 @@ def test_decode_kernel_choice(lib):
     kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 256, None, 0, lib)
     p = plan_of(lib, h)
     assert (p["kernel"], p["gh"]) == (STREAM, 1) and p["chunk"] % 32 == 0
+
+
+def test_decode_row_streams(lib):
+    STREAM = 2
+    # long sessions: two row streams per head (16 waves per workgroup) for
+    # bf16 queries; fp32 queries need more registers and keep one
+    h = create(lib, n_seqs=4, n_q_heads=40, n_kv_heads=8, head_dim=128, capacity=31000)
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 30000, None, 0, lib)
+    p = plan_of(lib, h)
+    assert (p["kernel"], p["gh"], p["rs"]) == (STREAM, 8, 2) and p["lds"] <= 160 * 1024
+    assert p["units"] == 4 * -(-30000 // p["chunk"]) <= 256
+    assert plan_of(lib, h, dtype=kvq.KVQ_F32)["rs"] == 1
+    kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_STREAM, 8, 1, lib)
+    assert plan_of(lib, h)["rs"] == 1
+    kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_STREAM, 8, 2, lib)
+    assert plan_of(lib, h)["rs"] == 2
+    lib.kvq_nodev_clear()
+    assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_F32, 1, None, 0.1, O, None, WS, 1 << 40) == kvq.KVQ_EINVAL
+    # verify rows (two row tiles per wave) never take two streams
+    assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 8, None, 0.1, O, None, WS, 1 << 40) == kvq.KVQ_EINVAL
 
 
 def test_decode_ring_start_below_base_falls_back(lib):
