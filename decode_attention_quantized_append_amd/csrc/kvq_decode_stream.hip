@@ -87,11 +87,15 @@ __device__ __forceinline__ h8 v_codes_sub(uint32_t lo, uint32_t hi) {
 }
 
 // NB blocks of 32 dims per head; RTW row tiles of 16 per wave; QLO: fp32
-// queries (a low fp16 part kept beside the high one); RS row streams.
-template <int NB, int RTW, bool QLO, int RS>
-__global__ __launch_bounds__(64 * RS * (RTW == 1 ? 8 : 4), stream_waves_per_simd(NB, RTW, QLO)) void decode_stream(
+// queries (a low fp16 part kept beside the high one); RS row streams (waves
+// of one head taking alternate tiles); RG row groups (waves of one head
+// taking 16 query rows each of the same tiles, which they load in step so
+// that the second copy comes from L2).
+template <int NB, int RTW, bool QLO, int RS, int RG>
+__global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4), stream_waves_per_simd(NB, RTW, QLO)) void decode_stream(
     DecodeParams p) {
     static_assert(RS == 1 || RTW == 1, "row streams need one row tile per wave");
+    static_assert(RG == 1 || (RTW == 1 && RS == 1), "row groups are one row tile per wave");
     using WN = Win<NB>;
     constexpr int HD = NB * 32;
     extern __shared__ __align__(16) uint8_t smem[];
@@ -100,7 +104,9 @@ __global__ __launch_bounds__(64 * RS * (RTW == 1 ? 8 : 4), stream_waves_per_simd
     const int q4 = lane >> 4, j16 = lane & 15;
     const int gh = p.gh, ngrp = p.Hkv / gh;
     constexpr int rs = RS;
-    const int gi = wave % gh, str = wave / gh;   // head in the group, row stream
+    const int gi = wave % gh;                    // head in the group
+    const int str = RS > 1 ? wave / gh : 0;      // row stream
+    const int rb = RG > 1 ? (wave / gh) * 16 : 0;   // first query row of this wave
 
     const int W = gridDim.x, wid = blockIdx.x;
     const int L = (wid & 7) * (W >> 3) + (wid >> 3);
@@ -177,7 +183,7 @@ __global__ __launch_bounds__(64 * RS * (RTW == 1 ? 8 : 4), stream_waves_per_simd
         mrow[rt] = -INFINITY;
         lsum[rt] = 0.0f;
         vis_lo[rt] = vis_hi[rt] = 0;
-        const int r = rt * 16 + j16;
+        const int r = rb + rt * 16 + j16;
         if (r < R) {
             vis_hi[rt] = len - p.T + r / p.hpk + 1;
             vis_lo[rt] = p.window > 0 ? max(0, vis_hi[rt] - p.window) : 0;
@@ -216,7 +222,7 @@ __global__ __launch_bounds__(64 * RS * (RTW == 1 ? 8 : 4), stream_waves_per_simd
     h8 qh[RTW][NB], ql[RTW][NB];
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
-        const int r = rt * 16 + j16;
+        const int r = rb + rt * 16 + j16;
         const bool real = r < R;
         const int t = real ? r / p.hpk : 0, hh = real ? r % p.hpk : 0;
         const size_t i0 = (((size_t)b * p.T + t) * p.H + g * p.hpk + hh) * HD + 8 * q4;
@@ -321,7 +327,7 @@ __global__ __launch_bounds__(64 * RS * (RTW == 1 ? 8 : 4), stream_waves_per_simd
         // which share cache lines at the slice edges; requesting the next
         // tile together lets those lines be fetched from HBM once (and keeps
         // the row streams of a CU in step).
-        if (gh * rs > 1) __builtin_amdgcn_s_barrier();
+        if (gh * rs * RG > 1) __builtin_amdgcn_s_barrier();
         if (next) issue_k(tn);
 
         // ---- online softmax against a reference max that moves only when a
@@ -507,7 +513,7 @@ __global__ __launch_bounds__(64 * RS * (RTW == 1 ? 8 : 4), stream_waves_per_simd
     const size_t row0 = ((size_t)b * p.splits + s) * p.T;
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
-        const int r = rt * 16 + j16;
+        const int r = rb + rt * 16 + j16;
         if (q4 == 0 && r < R) {
             const int t = r / p.hpk, hq = g * p.hpk + r % p.hpk;
             const size_t idx = (row0 + t) * p.H + hq;
@@ -516,7 +522,7 @@ __global__ __launch_bounds__(64 * RS * (RTW == 1 ? 8 : 4), stream_waves_per_simd
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int ro = rt * 16 + 4 * q4 + i;
+            const int ro = rb + rt * 16 + 4 * q4 + i;
             if (ro < R) {
                 const int t = ro / p.hpk, hq = g * p.hpk + ro % p.hpk;
                 float* o = p.part_o + ((row0 + t) * p.H + hq) * HD + j16;

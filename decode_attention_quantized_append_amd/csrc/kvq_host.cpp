@@ -124,6 +124,7 @@ struct Plan {
     int32_t gh;        // KV heads per workgroup (whole-row and stream kernels)
     int32_t sub;       // whole-row kernel: rows per buffer / 32
     int32_t rs;        // stream kernel: row streams (waves per KV head)
+    int32_t rg;        // stream kernel: row groups of 16 query rows (waves per KV head)
     int32_t lds;       // dynamic LDS bytes
     int32_t rows;      // rows per buffer (chunks are a multiple)
     kvq::RowGeo geo;
@@ -168,6 +169,16 @@ bool stream_rs2_ok(const kvq_config& c, int R, int gh) {
     return 2 * gh * kvq::stream_wave_bytes(NB) <= kvq::kLdsBytes && 2 * gh <= waves;
 }
 
+// Can the stream kernel give each of the two 16-row groups of R > 16 query
+// rows its own wave (one row tile each, both loading the same tiles in step),
+// with twice the waves and LDS still fitting a CU?
+bool stream_rg2_ok(const kvq_config& c, int R, int gh, bool f32_queries) {
+    const int NB = c.head_dim / 32;
+    if (R <= 16) return false;
+    const int waves = 4 * kvq::stream_waves_per_simd(NB, 1, f32_queries);
+    return 2 * gh * kvq::stream_wave_bytes(NB) <= kvq::kLdsBytes && 2 * gh <= waves;
+}
+
 // Is every session's first visible row, rounded down to 32, still resident?
 bool aligned_start_resident(const kvq_cache* h, int32_t T) {
     for (int b = 0; b < h->cfg.n_seqs; ++b)
@@ -183,7 +194,7 @@ int64_t span_of(const kvq_cache* h, int b, int32_t T) {
 
 // Chooses the decode kernel and its tiling.  Returns false when a kernel or
 // tiling set with kvq_set_decode_tiling does not fit the shape.
-bool choose_kernel(const kvq_cache* h, int R, int32_t T, Plan* p) {
+bool choose_kernel(const kvq_cache* h, int R, int32_t T, bool f32_queries, Plan* p) {
     const kvq_config& c = h->cfg;
     const int NB = c.head_dim / 32;
     const int RT = (R + 15) / 16;
@@ -210,9 +221,16 @@ bool choose_kernel(const kvq_cache* h, int R, int32_t T, Plan* p) {
         if (!stream_ok(c, R, gh)) return h->decode_kernel == KVQ_DECODE_AUTO;
         p->kernel = kvq::kStream;
         p->gh = gh;
-        p->rs = h->sub_tiles;                       // 0: chosen with the chunk
+        // sub_tiles = waves per KV head: row streams for R <= 16 query rows,
+        // row groups above
+        p->rs = R <= 16 ? h->sub_tiles : 1;         // 0: chosen with the chunk
+        p->rg = R > 16 ? (h->sub_tiles == 1 ? 1 : stream_rg2_ok(c, R, gh, f32_queries) ? 2 : 0) : 1;
+        if (p->rg == 0) {
+            if (h->sub_tiles == 2) return false;
+            p->rg = 1;
+        }
         if (p->rs == 2 && !stream_rs2_ok(c, R, gh)) return false;
-        p->lds = gh * std::max(1, p->rs) * kvq::stream_wave_bytes(NB);
+        p->lds = gh * std::max(1, p->rs) * p->rg * kvq::stream_wave_bytes(NB);
         p->rows = kvq::stream_rows_per_buffer(NB);
         return true;
     }
@@ -249,7 +267,7 @@ Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nul
         maxvis = std::max(maxvis, vis);
     }
     Plan p{};
-    const bool ok = choose_kernel(h, R, T, &p);
+    const bool ok = choose_kernel(h, R, T, f32_queries, &p);
     if (fits) *fits = ok;
     int64_t chunk = h->split_rows;
     if (p.kernel != kvq::kPerHead) {
@@ -259,10 +277,12 @@ Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nul
         // (bound by LDS and by the waves the register file holds), each a
         // whole number of buffers
         auto one_round = [&](int rs) {
-            const int64_t waves_per_wg = p.kernel == kvq::kStream ? p.gh * rs : p.gh * RT;
+            const int64_t waves_per_wg = p.kernel == kvq::kStream ? p.gh * rs * p.rg : p.gh * RT;
+            const int rtw = p.rg == 2 ? 1 : RT;   // row tiles per wave
             const int64_t waves_per_cu =
-                p.kernel == kvq::kStream ? 4 * kvq::stream_waves_per_simd(c.head_dim / 32, RT, f32_queries) : 8;
-            const int64_t lds = p.kernel == kvq::kStream ? p.gh * rs * kvq::stream_wave_bytes(c.head_dim / 32) : p.lds;
+                p.kernel == kvq::kStream ? 4 * kvq::stream_waves_per_simd(c.head_dim / 32, rtw, f32_queries) : 8;
+            const int64_t lds =
+                p.kernel == kvq::kStream ? p.gh * rs * p.rg * kvq::stream_wave_bytes(c.head_dim / 32) : p.lds;
             const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kvq::kLdsBytes / lds,
                                                                            waves_per_cu / waves_per_wg));
             const int64_t slots = 256 * per_cu;
@@ -282,7 +302,7 @@ Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nul
             const bool rs2 = stream_rs2_ok(c, R, p.gh) && !f32_queries;
             if (p.rs == 0) p.rs = (rs2 && (chunk > 0 ? chunk : one_round(2)) >= 4 * 32) ? 2 : 1;
             if (p.rs == 2 && !rs2 && fits) *fits = false;
-            p.lds = p.gh * p.rs * kvq::stream_wave_bytes(c.head_dim / 32);
+            p.lds = p.gh * p.rs * p.rg * kvq::stream_wave_bytes(c.head_dim / 32);
         }
         if (chunk <= 0) chunk = one_round(p.kernel == kvq::kStream ? p.rs : 1);
         chunk = round_up(chunk, p.rows);
@@ -526,6 +546,7 @@ kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, c
     dp.gh = p.gh;
     dp.sub = p.sub;
     dp.rs = p.rs;
+    dp.rg = p.rg;
     dp.lds = p.lds;
     dp.geo = p.geo;
     dp.scale = scale;

@@ -173,6 +173,8 @@ struct DecodeParams {
     int32_t sub;                // whole-row kernel: rows per buffer / 32
     int32_t rs;                 // stream kernel: waves per KV head in a workgroup, each
                                 // taking every rs-th tile of the chunk (1 or 2)
+    int32_t rg;                 // stream kernel: waves per KV head in a workgroup, each
+                                // taking 16 of the query rows (1 or 2)
     int32_t lds;                // dynamic LDS bytes of the decode workgroup
     RowGeo geo;                 // whole-row kernel geometry
     float scale;

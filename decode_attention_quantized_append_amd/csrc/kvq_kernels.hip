@@ -344,11 +344,11 @@ int launch_rows_t(const DecodeParams& p, hipStream_t st, const char** err) {
     return launch_combine(p, st, err);
 }
 
-template <int NB, int RTW, bool QLO, int RS>
+template <int NB, int RTW, bool QLO, int RS, int RG>
 int launch_stream_t(const DecodeParams& p, hipStream_t st, const char** err) {
     static bool configured = false;
     if (!configured) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&stream::decode_stream<NB, RTW, QLO, RS>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&stream::decode_stream<NB, RTW, QLO, RS, RG>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) != hipSuccess) {
             *err = "cannot raise the LDS limit of the decode kernel";
             return 1;
@@ -357,7 +357,7 @@ int launch_stream_t(const DecodeParams& p, hipStream_t st, const char** err) {
     }
     const int items = std::max(1, p.units) * (p.Hkv / p.gh);
     const int grid = (items + 7) & ~7;
-    hipLaunchKernelGGL((stream::decode_stream<NB, RTW, QLO, RS>), dim3(grid), dim3(64 * p.gh * RS), p.lds, st, p);
+    hipLaunchKernelGGL((stream::decode_stream<NB, RTW, QLO, RS, RG>), dim3(grid), dim3(64 * p.gh * RS * RG), p.lds, st, p);
     if (check(err)) return 1;
     return launch_combine(p, st, err);
 }
@@ -366,16 +366,20 @@ template <int NB>
 int launch_stream_nb(const DecodeParams& p, hipStream_t st, const char** err) {
     const int R = p.T * p.hpk;
     const bool qlo = p.dtype == 0;
-    if (R > 16) return qlo ? launch_stream_t<NB, 2, true, 1>(p, st, err) : launch_stream_t<NB, 2, false, 1>(p, st, err);
+    if (R > 16) {
+        if (p.rg == 2)   // two 16-row groups, one wave each
+            return qlo ? launch_stream_t<NB, 1, true, 1, 2>(p, st, err) : launch_stream_t<NB, 1, false, 1, 2>(p, st, err);
+        return qlo ? launch_stream_t<NB, 2, true, 1, 1>(p, st, err) : launch_stream_t<NB, 2, false, 1, 1>(p, st, err);
+    }
     if (p.rs == 2) {
         // two row streams: bf16 queries and head_dim 64 or 128 only (the planner's rule)
         if constexpr (NB <= 4) {
-            if (!qlo) return launch_stream_t<NB, 1, false, 2>(p, st, err);
+            if (!qlo) return launch_stream_t<NB, 1, false, 2, 1>(p, st, err);
         }
         *err = "two row streams are not built for this shape";
         return 1;
     }
-    return qlo ? launch_stream_t<NB, 1, true, 1>(p, st, err) : launch_stream_t<NB, 1, false, 1>(p, st, err);
+    return qlo ? launch_stream_t<NB, 1, true, 1, 1>(p, st, err) : launch_stream_t<NB, 1, false, 1, 1>(p, st, err);
 }
 
 template <int NB>

@@ -53,7 +53,7 @@ int launch_decode(const DecodeParams& p, void*, const char** err) {
                     " splits=" + std::to_string(p.splits) + " ml_to_o=" +
                     std::to_string((const char*)p.part_o - (const char*)p.part_ml) +
                     " kernel=" + std::to_string(p.kernel) + " gh=" + std::to_string(p.gh) +
-                    " sub=" + std::to_string(p.sub) + " rs=" + std::to_string(p.rs) +
+                    " sub=" + std::to_string(p.sub) + " rs=" + std::to_string(p.rs) + " rg=" + std::to_string(p.rg) +
                     " lds=" + std::to_string(p.lds) + " units=" + std::to_string(p.units);
     return record(s, err);
 }

@@ -100,6 +100,7 @@ SMALL = {
     "hd32_gqa7": (2, 7, 1, 32, 3, [200, 70], 0, 256, 0, True, "f32", False),
     "hd96_window": (3, 6, 2, 96, 2, [300, 40, 2], 50, 320, 0, False, "bf16", False),
     "qwen_f32_small": (2, 32, 8, 128, 2, [900, 161], 0, 1000, 0, True, "f32", True),
+    "verify_f32_small": (2, 16, 4, 256, 8, [500, 75], 0, 600, 0, True, "f32", False),
 }
 
 
@@ -155,9 +156,11 @@ TILINGS = {
                        (ST, 1, 0), (ST, 8, 1), (ST, 8, 2), (ST, 2, 2)],
     "batched_small": [(WR, 8, 1), (WR, 4, 2), (WR, 2, 1), (ST, 8, 0), (ST, 4, 0), (ST, 8, 2), (ST, 4, 2)],
     "sink_ring_small": [(WR, 8, 1), (WR, 8, 2), (WR, 4, 1), (WR, 4, 4), (ST, 8, 0), (ST, 2, 0), (ST, 8, 2)],
-    "verify_small": [(WR, 4, 1), (WR, 2, 1), (WR, 2, 2), (WR, 1, 1), (WR, 1, 2), (ST, 4, 0), (ST, 1, 0)],
-    "qwen_f32_small": [(WR, 8, 1), (WR, 2, 2), (ST, 8, 0), (ST, 4, 0)],
+    "verify_small": [(WR, 4, 1), (WR, 2, 1), (WR, 2, 2), (WR, 1, 1), (WR, 1, 2), (ST, 4, 0), (ST, 1, 0),
+                     (ST, 4, 1), (ST, 4, 2), (ST, 2, 2), (ST, 1, 2)],
+    "qwen_f32_small": [(WR, 8, 1), (WR, 2, 2), (ST, 8, 0), (ST, 4, 0), (ST, 8, 1)],
     "tiny": [(ST, 1, 0)],
+    "verify_f32_small": [(ST, 4, 1), (ST, 4, 2), (ST, 2, 2)],
 }
 
 

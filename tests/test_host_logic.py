@@ -339,8 +339,16 @@ def test_decode_row_streams(lib):
     assert plan_of(lib, h)["rs"] == 2
     lib.kvq_nodev_clear()
     assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_F32, 1, None, 0.1, O, None, WS, 1 << 40) == kvq.KVQ_EINVAL
-    # verify rows (two row tiles per wave) never take two streams
-    assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 8, None, 0.1, O, None, WS, 1 << 40) == kvq.KVQ_EINVAL
+    # more than 16 query rows per KV head: sub_tiles 2 (the default) gives
+    # each 16-row group its own wave, 1 keeps two row tiles in one wave
+    h = create(lib, n_seqs=2, n_q_heads=16, n_kv_heads=4, head_dim=256, capacity=5000)
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 4000, None, 0, lib)
+    p = plan_of(lib, h, T=8)
+    assert (p["kernel"], p["gh"], p["rs"], p["rg"]) == (STREAM, 4, 1, 2) and p["lds"] <= 160 * 1024
+    kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_STREAM, 4, 1, lib)
+    assert plan_of(lib, h, T=8)["rg"] == 1
+    kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_STREAM, 2, 2, lib)
+    assert (plan_of(lib, h, T=8)["rg"], plan_of(lib, h, T=1)["rg"]) == (2, 1)
 
 
 def test_decode_ring_start_below_base_falls_back(lib):
