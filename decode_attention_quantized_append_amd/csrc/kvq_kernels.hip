@@ -195,16 +195,20 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 
 // One workgroup per (session, row t, Q head h): fold the session's split
 // partials (m in natural-log units, l, o), adding the sink once as a
-// value-less column.  The splits' maxima and weights are computed by all
-// threads in parallel; then each thread sums a 4-float slice of o over every
-// G-th split (G = NT / (hd / 4) groups of splits, 8 loads in flight), and
-// the G group sums are added in a fixed order.  NT = 1024 threads when there
-// are many splits (few workgroups, each with much to read), else 256.
+// value-less column.  Each thread first requests its slices of o: a 4-float
+// slice of every G-th split (G = NT / (hd / 4) groups of splits), up to 8 at
+// once, which do not depend on the weights.  Meanwhile thread s reads split
+// s's (m, l); the block maximum M (the sink included) gives the weights
+// e^(m_s - M) and Z = sum_s w_s l_s (+ e^(sink - M)).  The weighted slices are
+// then summed, the G group sums added in a fixed order.  NT = 1024 threads
+// when there are many splits (few workgroups, each with much to read), else
+// 256.
 template <int kCombineThreads>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p) {
+    constexpr int NT = kCombineThreads, NW = NT / 64;
     __shared__ float wts[kMaxSplits];
-    __shared__ float red[kCombineThreads / 32 > 8 ? kCombineThreads / 32 : 8];
-    __shared__ __align__(16) float part[kCombineThreads * 4];
+    __shared__ float red[2][NW];
+    __shared__ __align__(16) float part[NT * 4];
     const int idx = blockIdx.x;
     const int h = idx % p.H;
     const int t = (idx / p.H) % p.T;
@@ -217,62 +221,62 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
     const size_t stride = (size_t)p.T * p.H;
     const size_t e0 = ((size_t)b * p.splits * p.T + t) * p.H + h;   // split 0 entry
 
-    // M = max over splits (and the sink)
+    // this thread's slices of o: splits sg, sg + G, ... (the first 8 requested now)
+    const int nq = p.hd >> 2;                 // float4 slices per row (16, 32 .. 64)
+    const int G = NT / nq;                    // split groups
+    const int dq = tid % nq, sg = tid / nq;
+    const float* o = p.part_o + e0 * p.hd + 4 * dq;
+    const size_t so = stride * p.hd;
+    const int s0 = (sg < G) ? sg : ns;        // threads past G groups idle (hd not dividing NT)
+    float4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        v[k] = (s0 + k * G < ns) ? *reinterpret_cast<const float4*>(o + (size_t)(s0 + k * G) * so)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+
+    // M = max over splits (and the sink); weights; Z
     float m_loc = -INFINITY;
-    for (int s = tid; s < ns; s += kCombineThreads) m_loc = fmaxf(m_loc, p.part_ml[2 * (e0 + s * stride)]);
-    m_loc = wave_max(m_loc);
-    if (lane == 0) red[wave] = m_loc;
+    for (int s = tid; s < ns; s += NT) m_loc = fmaxf(m_loc, p.part_ml[2 * (e0 + s * stride)]);
+    float mw = wave_max(m_loc);
+    if (lane == 0) red[0][wave] = mw;
     __syncthreads();
-    float M = red[0];
-    for (int w = 1; w < kCombineThreads / 64; ++w) M = fmaxf(M, red[w]);
+    float M = red[0][0];
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, red[0][w]);
     const bool has_sink = p.sinks != nullptr;
     const float sink = has_sink ? p.sinks[h] : 0.0f;
     if (has_sink) M = fmaxf(M, sink);
-    __syncthreads();   // red is reused below
-
-    // weights w_s = e^(m_s - M), Z = sum_s w_s l_s (+ e^(sink - M))
     float z = 0.0f;
-    for (int s = tid; s < ns; s += kCombineThreads) {
+    for (int s = tid; s < ns; s += NT) {
         const float m = p.part_ml[2 * (e0 + s * stride)];
         const float w = (m == -INFINITY) ? 0.0f : expf(m - M);
         wts[s] = w;
         z = fmaf(w, p.part_ml[2 * (e0 + s * stride) + 1], z);
     }
     z = wave_sum(z);
-    if (lane == 0) red[wave] = z;
+    if (lane == 0) red[1][wave] = z;
     __syncthreads();   // wts and red are complete
     float Z = 0.0f;
-    for (int w = 0; w < kCombineThreads / 64; ++w) Z += red[w];
+    for (int w = 0; w < NW; ++w) Z += red[1][w];
     if (has_sink) Z += expf(sink - M);
 
     // weighted sum of o over the splits
-    const int nq = p.hd >> 2;                 // float4 slices per row (16, 32 .. 64)
-    const int G = kCombineThreads / nq;       // split groups
-    const int dq = tid % nq, sg = tid / nq;
-    const float* o = p.part_o + e0 * p.hd + 4 * dq;
-    const size_t so = stride * p.hd;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    int s = (sg < G) ? sg : ns;               // threads past G groups idle (hd not dividing 1024)
-    for (; s + 7 * G < ns; s += 8 * G) {
-        float4 v[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = *reinterpret_cast<const float4*>(o + (size_t)(s + k * G) * so);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float w = wts[s + k * G];
-            acc.x = fmaf(w, v[k].x, acc.x);
-            acc.y = fmaf(w, v[k].y, acc.y);
-            acc.z = fmaf(w, v[k].z, acc.z);
-            acc.w = fmaf(w, v[k].w, acc.w);
-        }
+    for (int k = 0; k < 8; ++k) {
+        const int s = s0 + k * G;
+        const float w = (s < ns) ? wts[s] : 0.0f;
+        acc.x = fmaf(w, v[k].x, acc.x);
+        acc.y = fmaf(w, v[k].y, acc.y);
+        acc.z = fmaf(w, v[k].z, acc.z);
+        acc.w = fmaf(w, v[k].w, acc.w);
     }
-    for (; s < ns; s += G) {
-        const float4 v = *reinterpret_cast<const float4*>(o + (size_t)s * so);
+    for (int s = s0 + 8 * G; s < ns; s += G) {   // more than 8 splits per group
+        const float4 x = *reinterpret_cast<const float4*>(o + (size_t)s * so);
         const float w = wts[s];
-        acc.x = fmaf(w, v.x, acc.x);
-        acc.y = fmaf(w, v.y, acc.y);
-        acc.z = fmaf(w, v.z, acc.z);
-        acc.w = fmaf(w, v.w, acc.w);
+        acc.x = fmaf(w, x.x, acc.x);
+        acc.y = fmaf(w, x.y, acc.y);
+        acc.z = fmaf(w, x.z, acc.z);
+        acc.w = fmaf(w, x.w, acc.w);
     }
     reinterpret_cast<float4*>(part)[sg * nq + dq] = acc;
     __syncthreads();
