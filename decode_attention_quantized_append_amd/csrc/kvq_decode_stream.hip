@@ -95,9 +95,17 @@ template <int NB, int RTW, bool QLO, int RS, int RG>
 __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4), stream_waves_per_simd(NB, RTW, QLO)) void decode_stream(
     DecodeParams p) {
     static_assert(RS == 1 || RTW == 1, "row streams need one row tile per wave");
-    static_assert(RG == 1 || (RTW == 1 && RS == 1), "row groups are one row tile per wave");
+    static_assert(RG == 1 || (RTW == 1 && RS == 1 && RG == 2), "row groups are two, one row tile per wave");
     using WN = Win<NB>;
     constexpr int HD = NB * 32;
+    // SH: the two row-group waves of a head share two tile buffers (each
+    // wave copies 16 of the 32 rows), so that a second tile is in flight
+    // while one is computed; per-wave scale arrays follow the shared buffers.
+    constexpr bool SH = RG == 2;
+    constexpr int RAW = SH ? WN::KS : WN::BYTES;          // bytes of one buffer's K and V rows
+    constexpr int NKH = SH ? (16 * WN::KWP + 63) / 64 : WN::NKI;   // load instructions per copy
+    constexpr int NVH = SH ? (16 * WN::VWP + 63) / 64 : WN::NVI;
+
     extern __shared__ __align__(16) uint8_t smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -123,8 +131,13 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4
     if (c0 >= c1) return;
 
     uint8_t* const wb = smem + wave * WN::BYTES;
-    const uint8_t* const rk = wb + WN::KB;   // K rows of the tile, stride KSTR
-    const uint8_t* const rv = wb + WN::VB;   // V rows of the tile, stride VSTR
+    // tile buffers: this wave's own, or its head's two shared ones
+    uint8_t* const tb0 = SH ? smem + gi * 2 * RAW : wb;
+    // scale arrays: at the end of the wave's buffer, or after all shared buffers
+    uint8_t* const scb = SH ? smem + gh * 2 * RAW + wave * (WN::BYTES - WN::KS) - WN::KS : wb;
+    const uint8_t* rk = tb0 + WN::KB;   // K rows of the current tile, stride KSTR
+    const uint8_t* rv = tb0 + WN::VB;   // V rows of the current tile, stride VSTR
+    const int hrow = SH ? rb : 0;       // first tile row this wave copies
     // This head's windows: K from the 16-byte boundary at or below its first
     // block (kofs bytes before it), V exactly its blocks.
     const int kstart = g * NB * 34;
@@ -132,43 +145,45 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4
     const uint8_t* const kwin = p.k_planes + (int64_t)b * p.k_stride + (kstart - kofs);
     const uint8_t* const vwin = p.v_planes + (int64_t)b * p.v_stride + g * NB * 24;
     // per lane, the byte offset of its piece (instruction x) from the tile's first row
-    uint32_t koff[WN::NKI], voff[WN::NVI];
+    uint32_t koff[NKH], voff[NVH];
 #pragma unroll
-    for (int x = 0; x < WN::NKI; ++x) {
+    for (int x = 0; x < NKH; ++x) {
         const int pc = x * 64 + lane, row = pc / WN::KWP, col = pc - row * WN::KWP;
-        koff[x] = (uint32_t)(row * p.k_row + min(col, WN::KW - 1) * 16);
+        koff[x] = (uint32_t)((hrow + row) * p.k_row + min(col, WN::KW - 1) * 16);
     }
 #pragma unroll
-    for (int x = 0; x < WN::NVI; ++x) {
+    for (int x = 0; x < NVH; ++x) {
         const int pc = x * 64 + lane, row = pc / WN::VWP, col = pc - row * WN::VWP;
-        voff[x] = (uint32_t)(row * p.v_row + min(col, WN::VW - 1) * 16);   // the pad piece re-reads a real one
+        voff[x] = (uint32_t)((hrow + row) * p.v_row + min(col, WN::VW - 1) * 16);   // the pad piece re-reads a real one
     }
     // Copy the K (or V) rows of the tile [t0, t0 + 32) into the buffer.  Rows
     // from c1 on (a session's last tile) are not loaded; rows below lo (first
     // tile) are resident and masked.  Every LDS read of the half being
     // refilled has returned first.
-    auto issue_k = [&](int t0) {
+    auto issue_k = [&](int t0, uint8_t* tb) {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-        const int nrows = min(kTile, c1 - t0);
+        const int nrows = SH ? min(16, max(0, c1 - t0 - hrow)) : min(kTile, c1 - t0);
         const uint8_t* const kt = kwin + (int64_t)(t0 - base) * p.k_row;
+        uint8_t* const d = tb + WN::KB + hrow * WN::KSTR;
 #pragma unroll
-        for (int x = 0; x < WN::NKI; ++x) {
+        for (int x = 0; x < NKH; ++x) {
             uint32_t o = koff[x];
             asm volatile("" : "+v"(o));
-            if (lane < nrows * WN::KWP - x * 64) dma16(kt, o, wb + WN::KB + x * 1024);
+            if (lane < nrows * WN::KWP - x * 64) dma16(kt, o, d + x * 1024);
         }
     };
-    auto issue_v = [&](int t0) {
+    auto issue_v = [&](int t0, uint8_t* tb) {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-        const int nrows = min(kTile, c1 - t0);
+        const int nrows = SH ? min(16, max(0, c1 - t0 - hrow)) : min(kTile, c1 - t0);
         const uint8_t* const vt = vwin + (int64_t)(t0 - base) * p.v_row;
+        uint8_t* const d = tb + WN::VB + hrow * WN::VSTR;
 #pragma unroll
-        for (int x = 0; x < WN::NVI; ++x) {
+        for (int x = 0; x < NVH; ++x) {
             uint32_t o = voff[x];
             asm volatile("" : "+v"(o));
-            if (lane < nrows * WN::VWP - x * 64) dma16(vt, o, wb + WN::VB + x * 1024);
+            if (lane < nrows * WN::VWP - x * 64) dma16(vt, o, d + x * 1024);
         }
     };
 
@@ -192,9 +207,9 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4
     const int full_hi = min(len - p.T + 1, c1);
     const int full_lo = max(p.window > 0 ? max(0, len - p.window) : 0, c0);
     const float sc2 = p.scale * kLog2e;
-    float* const KSa = reinterpret_cast<float*>(wb + WN::KS);
-    float* const VDa = reinterpret_cast<float*>(wb + WN::VD);
-    uint16_t* const VMa = reinterpret_cast<uint16_t*>(wb + WN::VM);
+    float* const KSa = reinterpret_cast<float*>(scb + WN::KS);
+    float* const VDa = reinterpret_cast<float*>(scb + WN::VD);
+    uint16_t* const VMa = reinterpret_cast<uint16_t*>(scb + WN::VM);
     const int vkey = pkey(q4, j16 >> 1);                 // V row of this lane's tr8 reads
     const int mk0 = pkey(q4, j16 >> 2), mk1 = pkey(q4, 4 + (j16 >> 2));
     const int mc = (4 * (j16 & 3) < NB) ? (j16 & 3) : 0;   // columns past NB of the offset product are unused
@@ -213,8 +228,12 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4
     const int mine = ntiles > str ? (ntiles - str + rs - 1) / rs : 0;
     const int first = c0 + str * kTile;
     if (first < c1) {
-        issue_k(first);
-        issue_v(first);
+        issue_k(first, tb0);
+        issue_v(first, tb0);
+        if (SH && first + kTile < c1) {
+            issue_k(first + kTile, tb0 + RAW);
+            issue_v(first + kTile, tb0 + RAW);
+        }
     }
 
     // Q rows rt*16 + j16 as the B operand of S^T = K Q^T, read while the
@@ -264,8 +283,21 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4
         const bool next = tn < c1;
         const bool next_whole = tn + kTile <= c1;
         float sv[RTW][2][4];
-        // K(t) has landed; V(t), issued after it, may still be in flight
-        if (whole) wait_loads_upto<WN::NVI>(); else wait_loads_upto<0>();
+        uint8_t* const tb = SH ? tb0 + (it & 1) * RAW : tb0;   // this tile's buffer
+        rk = tb + WN::KB;
+        rv = tb + WN::VB;
+        const bool has2 = tn + kTile < c1;                // SH: the tile after next
+        if constexpr (SH) {
+            // K(t) has landed (both copies); after it come V(t), K(t+1), V(t+1)
+            if (!whole) wait_loads_upto<0>();
+            else if (!next) wait_loads_upto<NVH>();
+            else if (next_whole) wait_loads_upto<NVH + NKH + NVH>();
+            else wait_loads_upto<0>();
+            rows::lds_barrier();
+        } else {
+            // K(t) has landed; V(t), issued after it, may still be in flight
+            if (whole) wait_loads_upto<WN::NVI>(); else wait_loads_upto<0>();
+        }
 
         // ---- K scales (rows past c1 hold stale bytes)
 #pragma unroll
@@ -327,8 +359,13 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4
         // which share cache lines at the slice edges; requesting the next
         // tile together lets those lines be fetched from HBM once (and keeps
         // the row streams of a CU in step).
-        if (gh * rs * RG > 1) __builtin_amdgcn_s_barrier();
-        if (next) issue_k(tn);
+        if constexpr (SH) {
+            rows::lds_barrier();                          // both copies of K(t) are read
+            if (has2) issue_k(tn + kTile, tb);
+        } else {
+            if (gh * rs > 1) __builtin_amdgcn_s_barrier();
+            if (next) issue_k(tn, tb);
+        }
 
         // ---- online softmax against a reference max that moves only when a
         // score passes it by more than 8 (so p <= 256, well inside fp16)
@@ -376,10 +413,19 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4
                 }
         }
 
-        // V(t) has landed; K(t+1), issued after it, may still be in flight
-        if (!next) wait_loads_upto<0>();
-        else if (next_whole) wait_loads_upto<WN::NKI>();
-        else wait_loads_upto<0>();
+        if constexpr (SH) {
+            // V(t) has landed (both copies); after it come K(t+1), V(t+1), K(t+2)
+            if (!next || !next_whole) wait_loads_upto<0>();
+            else if (!has2) wait_loads_upto<NKH + NVH>();
+            else if (tn + 2 * kTile <= c1) wait_loads_upto<NKH + NVH + NKH>();
+            else wait_loads_upto<0>();
+            rows::lds_barrier();
+        } else {
+            // V(t) has landed; K(t+1), issued after it, may still be in flight
+            if (!next) wait_loads_upto<0>();
+            else if (next_whole) wait_loads_upto<WN::NKI>();
+            else wait_loads_upto<0>();
+        }
         // ---- V steps and offsets of the tile (rows past c1 hold stale bytes)
 #pragma unroll
         for (int x = 0; x < (kTile * NB + 63) / 64; ++x) {
@@ -431,8 +477,8 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4
         }
         // q5_1 offset term: macc[rt][row][blk] += sum_key P[row][key] * m[key][blk]
         {
-            const h8 mb = dec::tr16_pair(wb + WN::VM + (mk0 * WN::VMS + 4 * mc) * 2,
-                                         wb + WN::VM + (mk1 * WN::VMS + 4 * mc) * 2);
+            const h8 mb = dec::tr16_pair(scb + WN::VM + (mk0 * WN::VMS + 4 * mc) * 2,
+                                         scb + WN::VM + (mk1 * WN::VMS + 4 * mc) * 2);
 #pragma unroll
             for (int rt = 0; rt < RTW; ++rt) {
                 const h8 pu = {(_Float16)pv[rt][0][0], (_Float16)pv[rt][0][1], (_Float16)pv[rt][0][2],
@@ -441,7 +487,12 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4
                 macc[rt] = dec::mfma(pu, mb, macc[rt]);
             }
         }
-        if (next) issue_v(tn);
+        if constexpr (SH) {
+            rows::lds_barrier();                          // both copies of V(t) are read
+            if (has2) issue_v(tn + kTile, tb);
+        } else {
+            if (next) issue_v(tn, tb);
+        }
     }
     if (RS > 1)
         for (int it = mine; it < nit; ++it) __builtin_amdgcn_s_barrier();
