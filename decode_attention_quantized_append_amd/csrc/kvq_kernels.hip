@@ -172,12 +172,18 @@ __device__ __forceinline__ void append_unit(const AppendParams& p, int64_t unit,
 // to finish advances len_d.  Every workgroup has consumed its len_d reads
 // (they fix its store addresses) before thread 0 counts it done, so a relaxed
 // device-scope counter orders the reads before the final write.
-__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
+__global__ __launch_bounds__(1024) void append_kernel(AppendParams p) {
     const int nblk = p.Hkv * p.hd / 32;
     const int64_t units = (int64_t)p.nsess * p.T * nblk;
-    for (int64_t u0 = (int64_t)blockIdx.x * 8; u0 < units; u0 += (int64_t)gridDim.x * 8)
+    const int per = blockDim.x >> 5;   // blocks per workgroup pass
+    for (int64_t u0 = (int64_t)blockIdx.x * per; u0 < units; u0 += (int64_t)gridDim.x * per)
         append_unit(p, u0 + (threadIdx.x >> 5), units, nblk);
     __syncthreads();
+    if (gridDim.x == 1) {   // a single workgroup (a few rows): no counter needed
+        if (threadIdx.x == 0)
+            for (int i = 0; i < p.nsess; ++i) p.len_d[p.b0 + i] += p.n_new[i];
+        return;
+    }
     if (threadIdx.x == 0) {
         const int prev = atomicAdd(p.done, 1);
         if (prev == (int)gridDim.x - 1) {
@@ -419,6 +425,12 @@ int launch_move(const MoveParams& p, void* stream, const char** err) {
 
 int launch_append(const AppendParams& p, void* stream, const char** err) {
     const int64_t units = (int64_t)p.nsess * p.T * (p.Hkv * p.hd / 32);
+    // up to 32 blocks in one workgroup of 1024 threads, which then needs no
+    // completion counter; more over a grid of 256-thread workgroups
+    if (units <= 32) {
+        hipLaunchKernelGGL(append_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, p);
+        return check(err);
+    }
     const int64_t grid = std::min<int64_t>((units + 7) / 8, 1024);
     hipLaunchKernelGGL(append_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, p);
     return check(err);
