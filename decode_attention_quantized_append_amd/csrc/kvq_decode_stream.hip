@@ -133,8 +133,9 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4
     uint8_t* const wb = smem + wave * WN::BYTES;
     // tile buffers: this wave's own, or its head's two shared ones
     uint8_t* const tb0 = SH ? smem + gi * 2 * RAW : wb;
-    // scale arrays: at the end of the wave's buffer, or after all shared buffers
-    uint8_t* const scb = SH ? smem + gh * 2 * RAW + wave * (WN::BYTES - WN::KS) - WN::KS : wb;
+    // scale arrays: at the end of the wave's buffer, or one set per head after
+    // all shared buffers (each of the head's two waves fills in its own rows)
+    uint8_t* const scb = SH ? smem + gh * 2 * RAW + gi * (WN::BYTES - WN::KS) - WN::KS : wb;
     const uint8_t* rk = tb0 + WN::KB;   // K rows of the current tile, stride KSTR
     const uint8_t* rv = tb0 + WN::VB;   // V rows of the current tile, stride VSTR
     const int hrow = SH ? rb : 0;       // first tile row this wave copies
@@ -293,23 +294,25 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4
             else if (!next) wait_loads_upto<NVH>();
             else if (next_whole) wait_loads_upto<NVH + NKH + NVH>();
             else wait_loads_upto<0>();
-            rows::lds_barrier();
         } else {
             // K(t) has landed; V(t), issued after it, may still be in flight
             if (whole) wait_loads_upto<WN::NVI>(); else wait_loads_upto<0>();
         }
 
-        // ---- K scales (rows past c1 hold stale bytes)
+        // ---- K scales (rows past c1 hold stale bytes); with shared buffers
+        // each wave converts the rows it copied, and the barrier that follows
+        // makes both halves of the rows and of the scales visible
+        constexpr int SROWS = SH ? 16 : kTile;
 #pragma unroll
-        for (int x = 0; x < (kTile * NB + 63) / 64; ++x) {
+        for (int x = 0; x < (SROWS * NB + 63) / 64; ++x) {
             const int u = x * 64 + lane;
-            if (kTile * NB % 64 == 0 || u < kTile * NB) {
-                const int key = u / NB, blk = u - (u / NB) * NB;
+            if (SROWS * NB % 64 == 0 || u < SROWS * NB) {
+                const int key = hrow + u / NB, blk = u - (u / NB) * NB;
                 const uint16_t kd = *reinterpret_cast<const uint16_t*>(rk + key * WN::KSTR + kofs + blk * 34);
                 KSa[blk * kTile + key] = (t0 + key < c1) ? f16_value(kd) * sc2 : 0.0f;
             }
         }
-        dec::lds_order();
+        if constexpr (SH) rows::lds_barrier(); else dec::lds_order();
 
         // ---- scores S^T: sv[rt][h][i] = S[row rt*16 + j16][key 16h + 4*q4 + i] (base 2)
 #pragma unroll
@@ -419,7 +422,6 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4
             else if (!has2) wait_loads_upto<NKH + NVH>();
             else if (tn + 2 * kTile <= c1) wait_loads_upto<NKH + NVH + NKH>();
             else wait_loads_upto<0>();
-            rows::lds_barrier();
         } else {
             // V(t) has landed; K(t+1), issued after it, may still be in flight
             if (!next) wait_loads_upto<0>();
@@ -428,17 +430,17 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4
         }
         // ---- V steps and offsets of the tile (rows past c1 hold stale bytes)
 #pragma unroll
-        for (int x = 0; x < (kTile * NB + 63) / 64; ++x) {
+        for (int x = 0; x < (SROWS * NB + 63) / 64; ++x) {
             const int u = x * 64 + lane;
-            if (kTile * NB % 64 == 0 || u < kTile * NB) {
-                const int key = u / NB, blk = u - (u / NB) * NB;
+            if (SROWS * NB % 64 == 0 || u < SROWS * NB) {
+                const int key = hrow + u / NB, blk = u - (u / NB) * NB;
                 const bool live = t0 + key < c1;
                 const uint32_t dm = *reinterpret_cast<const uint32_t*>(rv + key * WN::VSTR + blk * 24);
                 VDa[blk * kTile + key] = live ? f16_value((uint16_t)(dm & 0xFFFF)) : 0.0f;
                 VMa[key * WN::VMS + blk] = live ? (uint16_t)(dm >> 16) : (uint16_t)0;
             }
         }
-        dec::lds_order();
+        if constexpr (SH) rows::lds_barrier(); else dec::lds_order();
 
         // ---- P V with the V codes built from the q5_1 bytes of 8 keys per lane group
 #pragma unroll
