@@ -1,7 +1,7 @@
 """Benchmark: append + decode attention over a quantized KV cache on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--layers L] [--no-cpu-baseline]
+                    [--layers L] [--no-cpu-baseline] [--no-others]
 
 A step is one pass of the whole hot path over one layer cache: the fused
 quantize-and-append of T rows per session, the split-K decode plus the
@@ -17,8 +17,12 @@ whole step (algorithmic K+V bytes the decode must read / wall time per step).
 with HIP events on the stream the library launches on, against the 8 TB/s HBM
 peak; its ``traffic`` is the HBM bytes per decode call that the committed
 rocprofv3 counter passes measured (profiles/decode_traffic.json), reported only
-while the kernel sources still hash to the measured state.  ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
-workload.
+while the kernel sources still hash to the measured state.  ``cpu_baseline``
+times the CPU oracle on a bounded sample of the same workload.
+``other_workloads`` repeats the GPU measurement (fewer steps, no CPU
+baseline) for every other workload: the batched serving tick and the
+131072-row verify are the long-context shapes, tiny and the sink ring are
+launch-bound.
 """
 from __future__ import annotations
 
@@ -85,6 +89,10 @@ def parse():
                          "workgroup and sub_tiles, as kvq_set_decode_tiling; default: the "
                          "library's choice")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the summary of the other workloads (each timed after the "
+                         "main one, with --other-steps steps)")
+    ap.add_argument("--other-steps", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--graph", choices=("auto", "on", "off"), default="auto",
                     help="replay each step as one captured HIP graph (auto: where the "
@@ -317,6 +325,31 @@ def main():
                      "algorithmic": r["kv_bytes"],
                      "kernel": "kvq_decode call (decode_kernel + combine_kernel), HIP events"},
     }
+    if not args.no_others:
+        # the other workloads, same step and measurement, fewer steps; each
+        # is a parity case of the tests as well
+        import torch
+        others = {}
+        for name in workloads.WORKLOADS:
+            if name == w.name:
+                continue
+            torch.cuda.empty_cache()
+            wo = workloads.get(name)
+            ao = argparse.Namespace(**vars(args))
+            ao.steps, ao.warmup, ao.layers = args.other_steps, min(args.warmup, 10), 0
+            ro = run_gpu(wo, ao)
+            vo = ro["kv_bytes"] / (ro["ms_step"] * 1e-3) / 1e9
+            ac = ro["kv_bytes"] / (ro["dec_ms"] * 1e-3) / 1e9
+            others[name] = {
+                "value": round(vo, 2), "unit": "GB/s", "ms_per_step": round(ro["ms_step"], 5),
+                "steps_per_s": round(1e3 / ro["ms_step"], 1),
+                "append_tokens_per_s": round(wo.B * wo.T / (ro["app_ms"] * 1e-3), 1),
+                "decode_call_ms": round(ro["dec_ms"], 5), "decode_call_GBps": round(ac, 2),
+                "decode_call_frac_hbm_peak": round(ac / HBM_PEAK_GBPS, 4),
+                "kv_bytes_per_step": ro["kv_bytes"], "layers_rotated": ro["L"],
+                "steps": ao.steps, "step_launch": "hip graph" if ro["graph"] else "eager",
+                "traffic": measured_traffic(name)}
+        line["other_workloads"] = others
     if not args.no_cpu_baseline:
         cb = run_cpu_baseline(w, args.cpu_seconds)
         line["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in cb.items()}

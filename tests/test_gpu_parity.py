@@ -157,10 +157,10 @@ TILINGS = {
     "batched_small": [(WR, 8, 1), (WR, 4, 2), (WR, 2, 1), (ST, 8, 0), (ST, 4, 0), (ST, 8, 2), (ST, 4, 2)],
     "sink_ring_small": [(WR, 8, 1), (WR, 8, 2), (WR, 4, 1), (WR, 4, 4), (ST, 8, 0), (ST, 2, 0), (ST, 8, 2)],
     "verify_small": [(WR, 4, 1), (WR, 2, 1), (WR, 2, 2), (WR, 1, 1), (WR, 1, 2), (ST, 4, 0), (ST, 1, 0),
-                     (ST, 4, 1), (ST, 4, 2), (ST, 2, 2), (ST, 1, 2)],
+                     (ST, 4, 1), (ST, 2, 1), (ST, 1, 1), (ST, 4, 2), (ST, 2, 2), (ST, 1, 2)],
     "qwen_f32_small": [(WR, 8, 1), (WR, 2, 2), (ST, 8, 0), (ST, 4, 0), (ST, 8, 1)],
     "tiny": [(ST, 1, 0)],
-    "verify_f32_small": [(ST, 4, 1), (ST, 4, 2), (ST, 2, 2)],
+    "verify_f32_small": [(ST, 4, 1), (ST, 2, 1), (ST, 4, 2), (ST, 2, 2)],
 }
 
 
