@@ -259,7 +259,10 @@ bool choose_kernel(const kvq_cache* h, int R, int32_t T, bool f32_queries, Plan*
 
 Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nullptr) {
     const kvq_config& c = h->cfg;
-    const int R = T * (c.n_q_heads / c.n_kv_heads);
+    // the decode kernels take the T query rows in groups of at most 32 / hpk
+    // rows; R is the query rows per KV head of one group
+    const int hpk = c.n_q_heads / c.n_kv_heads;
+    const int R = std::min<int>(T, kvq::kMaxRows / hpk) * hpk;
     int64_t total = 0, maxvis = 1;
     for (int b = 0; b < c.n_seqs; ++b) {
         const int64_t vis = span_of(h, b, T);
@@ -493,6 +496,8 @@ kvq_status kvq_append(kvq_cache* h, const void* k_new, const void* v_new, kvq_dt
 kvq_status kvq_decode_workspace_bytes(const kvq_cache* h, int32_t T, size_t* bytes) {
     if (!h || !bytes) return fail(KVQ_EINVAL, "NULL argument");
     if (T < 1) return fail(KVQ_EINVAL, "T must be >= 1");
+    if (h->cfg.n_q_heads / h->cfg.n_kv_heads > kvq::kMaxRows)
+        return fail(KVQ_EINVAL, "need n_q_heads / n_kv_heads <= 32");
     // the larger of the plans for fp32 and bf16 queries
     const Plan p32 = make_plan(h, T, true), p16 = make_plan(h, T, false);
     *bytes = std::max(p32.ml_bytes + p32.o_bytes, p16.ml_bytes + p16.o_bytes);
@@ -508,8 +513,8 @@ kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, c
     if (!std::isfinite(scale)) return fail(KVQ_EINVAL, "scale must be finite");
     const kvq_config& c = h->cfg;
     const int hpk = c.n_q_heads / c.n_kv_heads;
-    if (T < 1 || (int64_t)T * hpk > kvq::kMaxRows)
-        return fail(KVQ_EINVAL, "need 1 <= T * n_q_heads / n_kv_heads <= 32");
+    if (T < 1) return fail(KVQ_EINVAL, "T must be >= 1");
+    if (hpk > kvq::kMaxRows) return fail(KVQ_EINVAL, "need n_q_heads / n_kv_heads <= 32");
     for (int b = 0; b < c.n_seqs; ++b) {
         if (h->len[b] < T)
             return fail(KVQ_EINVAL, "session " + std::to_string(b) + " holds fewer than T rows");
@@ -555,8 +560,16 @@ kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, c
     dp.sinks = sinks;
     dp.out = out;
     dp.lse = lse;
-    const char* err = nullptr;
-    if (kvq::launch_decode(dp, stream, &err)) return fail(KVQ_EDEVICE, err ? err : "decode launch failed");
+    // groups of at most 32 / hpk query rows, one decode launch each, writing
+    // their rows' partials; the combine after the last folds all T rows
+    const int tg = kvq::kMaxRows / hpk;
+    for (int t0 = 0; t0 < T; t0 += tg) {
+        dp.tq0 = t0;
+        dp.Tq = std::min(tg, T - t0);
+        dp.combine = t0 + tg >= T;
+        const char* err = nullptr;
+        if (kvq::launch_decode(dp, stream, &err)) return fail(KVQ_EDEVICE, err ? err : "decode launch failed");
+    }
     return KVQ_OK;
 }
 

@@ -332,8 +332,7 @@ int launch_decode_t(const DecodeParams& p, hipStream_t st, const char** err) {
     const int items = std::max(1, p.units) * p.Hkv;
     const int grid = (items + 7) & ~7;
     hipLaunchKernelGGL((dec::decode_mfma<NB, RT, QLO>), dim3(grid), dim3(256), lds, st, p);
-    if (check(err)) return 1;
-    return launch_combine(p, st, err);
+    return check(err);
 }
 
 template <int NB, int RT, bool QLO>
@@ -350,8 +349,7 @@ int launch_rows_t(const DecodeParams& p, hipStream_t st, const char** err) {
     const int items = std::max(1, p.units) * (p.Hkv / p.gh);
     const int grid = (items + 7) & ~7;
     hipLaunchKernelGGL((rows::decode_rows<NB, RT, QLO>), dim3(grid), dim3(64 * p.gh * RT), p.lds, st, p);
-    if (check(err)) return 1;
-    return launch_combine(p, st, err);
+    return check(err);
 }
 
 template <int NB, int RTW, bool QLO, int RS, int RG>
@@ -368,13 +366,12 @@ int launch_stream_t(const DecodeParams& p, hipStream_t st, const char** err) {
     const int items = std::max(1, p.units) * (p.Hkv / p.gh);
     const int grid = (items + 7) & ~7;
     hipLaunchKernelGGL((stream::decode_stream<NB, RTW, QLO, RS, RG>), dim3(grid), dim3(64 * p.gh * RS * RG), p.lds, st, p);
-    if (check(err)) return 1;
-    return launch_combine(p, st, err);
+    return check(err);
 }
 
 template <int NB>
 int launch_stream_nb(const DecodeParams& p, hipStream_t st, const char** err) {
-    const int R = p.T * p.hpk;
+    const int R = std::min(p.T, kMaxRows / p.hpk) * p.hpk;   // rows per group of the plan
     const bool qlo = p.dtype == 0;
     if (R > 16) {
         if (p.rg == 2)   // two 16-row groups, one wave each
@@ -394,7 +391,7 @@ int launch_stream_nb(const DecodeParams& p, hipStream_t st, const char** err) {
 
 template <int NB>
 int launch_rows_nb(const DecodeParams& p, hipStream_t st, const char** err) {
-    const int R = p.T * p.hpk;
+    const int R = std::min(p.T, kMaxRows / p.hpk) * p.hpk;   // rows per group of the plan
     const bool qlo = p.dtype == 0;
     if (R <= 16) return qlo ? launch_rows_t<NB, 1, true>(p, st, err) : launch_rows_t<NB, 1, false>(p, st, err);
     return qlo ? launch_rows_t<NB, 2, true>(p, st, err) : launch_rows_t<NB, 2, false>(p, st, err);
@@ -402,7 +399,7 @@ int launch_rows_nb(const DecodeParams& p, hipStream_t st, const char** err) {
 
 template <int NB>
 int launch_decode_nb(const DecodeParams& p, hipStream_t st, const char** err) {
-    const int R = p.T * p.hpk;
+    const int R = std::min(p.T, kMaxRows / p.hpk) * p.hpk;   // rows per group of the plan
     const bool qlo = p.dtype == 0;   // fp32 queries keep a low fp16 part
     if (R <= 16) return qlo ? launch_decode_t<NB, 1, true>(p, st, err) : launch_decode_t<NB, 1, false>(p, st, err);
     return qlo ? launch_decode_t<NB, 2, true>(p, st, err) : launch_decode_t<NB, 2, false>(p, st, err);
@@ -436,8 +433,8 @@ int launch_append(const AppendParams& p, void* stream, const char** err) {
     return check(err);
 }
 
-int launch_decode(const DecodeParams& p, void* stream, const char** err) {
-    hipStream_t st = (hipStream_t)stream;
+namespace {
+int launch_partials(const DecodeParams& p, hipStream_t st, const char** err) {
     if (p.kernel == kWholeRow) {
         switch (p.hd / 32) {
             case 2: return launch_rows_nb<2>(p, st, err);
@@ -465,6 +462,13 @@ int launch_decode(const DecodeParams& p, void* stream, const char** err) {
         case 8: return launch_decode_nb<8>(p, st, err);
         default: *err = "unsupported head_dim"; return 1;
     }
+}
+}  // namespace
+
+int launch_decode(const DecodeParams& p, void* stream, const char** err) {
+    hipStream_t st = (hipStream_t)stream;
+    if (launch_partials(p, st, err)) return 1;
+    return p.combine ? launch_combine(p, st, err) : 0;
 }
 
 }  // namespace kvq

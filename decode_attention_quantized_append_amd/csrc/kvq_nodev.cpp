@@ -54,7 +54,8 @@ int launch_decode(const DecodeParams& p, void*, const char** err) {
                     std::to_string((const char*)p.part_o - (const char*)p.part_ml) +
                     " kernel=" + std::to_string(p.kernel) + " gh=" + std::to_string(p.gh) +
                     " sub=" + std::to_string(p.sub) + " rs=" + std::to_string(p.rs) + " rg=" + std::to_string(p.rg) +
-                    " lds=" + std::to_string(p.lds) + " units=" + std::to_string(p.units);
+                    " lds=" + std::to_string(p.lds) + " units=" + std::to_string(p.units) +
+                    " rows=" + std::to_string(p.tq0) + "+" + std::to_string(p.Tq) + " combine=" + std::to_string(p.combine);
     return record(s, err);
 }
 

@@ -159,7 +159,11 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache* h, int32_t T, size_t* byt
  * [n_seqs, T, n_q_heads, head_dim].  lse: device float [n_seqs, T, n_q_heads]
  * or NULL.  ws: device workspace of at least kvq_decode_workspace_bytes
  * bytes, 256-byte aligned.  The committed length is read from len_d on the
- * device.  Requires len >= T for every session and 1 <= T*H/Hkv <= 32.
+ * device.  Requires len >= T for every session and H/Hkv <= 32.  Any T is
+ * accepted (a prompt chunk attending causally, cortiq attend_group_upto with
+ * many rows): the rows go to the decode kernel in groups of 32/(H/Hkv), one
+ * launch each, and one combine folds all T rows; the workspace holds the
+ * partials of all T rows.
  * fp32 queries are used to about 2^-22 relative precision (fp16 hi + lo
  * parts); bf16 queries exactly while |q| < 65504 and |q| >= 2^-14 (fp16 range).
  * Errors: EINVAL, ERANGE (a visible row was rebased away), EDEVICE. */

@@ -191,6 +191,54 @@ def test_decode_tilings_agree(name):
         np.testing.assert_allclose(l, outs[0][1], atol=1e-5, rtol=1e-5)
 
 
+# -- many query rows: groups of 32 / hpk rows per decode launch, one combine -------
+MANY = {
+    # name: (B, H, Hkv, hd, T, lengths, window, sinks, io, tiling)
+    "hd128_T40_sinks": (2, 8, 2, 128, 40, [700, 300], 0, True, "bf16", None),
+    "hd256_T19": (1, 16, 4, 256, 19, [500], 0, False, "bf16", None),
+    "hd256_T19_rows": (1, 16, 4, 256, 19, [500], 0, False, "bf16", (kvq.KVQ_DECODE_WHOLE_ROW, 0)),
+    "hd64_hpk1_T100": (1, 4, 4, 64, 100, [400], 0, False, "bf16", None),
+    "hd64_T70_window": (2, 16, 4, 64, 70, [330, 71], 45, True, "bf16", None),
+    "hd96_T33_window_f32": (2, 6, 2, 96, 33, [260, 40], 50, False, "f32", None),
+    "hd128_T24_perhead_f32": (2, 32, 8, 128, 24, [300, 129], 0, True, "f32", (kvq.KVQ_DECODE_PER_HEAD, 0)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MANY))
+def test_decode_many_query_rows(name):
+    """T * hpk above 32: every query row against the oracle's causal
+    attention (row t sees the rows below len - T + t + 1)."""
+    B, H, Hkv, hd, T, lens, window, sinks, io, tiling = MANY[name]
+    rng = np.random.default_rng(len(name) * 31 + T)
+    p = Pair(B, H, Hkv, hd, max(lens) + 8, window, 0, io=io)
+    if tiling:
+        p.gpu.set_decode_tiling(*tiling)
+    k, v = rows(rng, B, max(lens), Hkv, hd, io)
+    p.append(k, v, lens)
+    q = qrows(rng, B, T, H, hd, io)
+    s = rng.standard_normal(H).astype(np.float32) if sinks else None
+    p.decode(q, float(np.float32(1 / np.sqrt(hd))), sinks=s, what=name)
+
+
+def test_chunked_prime_into_ring():
+    """A prompt primed into a sliding-window ring in chunks: each chunk's rows
+    are appended, then its rows attend causally (each within its window) to
+    what the ring holds; the ring is one chunk plus the window plus a rebase
+    step.  Every chunk's outputs against the oracle's."""
+    rng = np.random.default_rng(21)
+    B, H, Hkv, hd, W, C, step = 2, 16, 4, 64, 64, 48, 32
+    p = Pair(B, H, Hkv, hd, W + C + step, W, step)
+    s = rng.standard_normal(H).astype(np.float32)
+    for it in range(9):
+        n = C if it < 8 else 13
+        k, v = rows(rng, B, n, Hkv, hd)
+        p.append(k, v)
+        p.check_mirror()
+        q = qrows(rng, B, n, H, hd)
+        p.decode(q, 0.125, sinks=s, what=f"prime chunk {it}")
+    assert int(p.ref.base[0]) > 0
+
+
 @pytest.mark.parametrize("step,tiling", [(24, (kvq.KVQ_DECODE_PER_HEAD, 0)), (32, (kvq.KVQ_DECODE_WHOLE_ROW, 4)),
                                          (32, (kvq.KVQ_DECODE_STREAM, 0)), (32, (kvq.KVQ_DECODE_AUTO, 0))])
 def test_ring_equals_flat(step, tiling):

@@ -30,6 +30,11 @@ def log(lib):
     return lib.kvq_nodev_log().decode().splitlines()
 
 
+def fields(line):
+    """key=integer fields of a recorded launch ("rows=a+b" gives rows=a)."""
+    return {k: int(v) for k, v in re.findall(r"(\w+)=(-?\d+)", line)}
+
+
 def create(lib, **kw):
     cfg = kvq.make_config(**{**dict(n_seqs=2, n_q_heads=8, n_kv_heads=2, head_dim=64, capacity=100), **kw})
     lib.kvq_nodev_clear()
@@ -223,13 +228,36 @@ def test_decode_validation_and_plan(lib):
     lib.kvq_nodev_clear()
     assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 2, None, 0.125, O, None, WS, ws - 1) == kvq.KVQ_EINVAL
     assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 2, None, 0.125, O, None, WS + 16, ws) == kvq.KVQ_EINVAL
-    assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 17, None, 0.125, O, None, WS, 1 << 40) == kvq.KVQ_EINVAL
+    assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 1001, None, 0.125, O, None, WS, 1 << 40) == kvq.KVQ_EINVAL
     assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 2, None, float("nan"), O, None, WS, ws) == kvq.KVQ_EINVAL
     assert err(lib, kvq.kvq_decode, h, 0, kvq.KVQ_BF16, 2, None, 0.125, O, None, WS, ws) == kvq.KVQ_EINVAL
     kvq.kvq_truncate(h, [3000, 1], 0, lib)
     lib.kvq_nodev_clear()
     assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 2, None, 0.125, O, None, WS, 1 << 40) == kvq.KVQ_EINVAL
     assert log(lib) == []
+
+
+def test_decode_query_row_groups(lib):
+    # more than 32 query rows per KV head: the T rows go to the decode kernel
+    # in groups of 32 / hpk, each launch writing its rows' partials, and one
+    # combine (after the last group) folds all T rows
+    h = create(lib, n_seqs=2, n_q_heads=8, n_kv_heads=2, head_dim=64, capacity=5000)
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 3000, [3000, 1000], 0, lib)
+    ws = kvq.kvq_decode_workspace_bytes(h, 20, lib)
+    lib.kvq_nodev_clear()
+    kvq.kvq_decode(h, Q, kvq.KVQ_BF16, 20, None, 0.125, O, None, WS, ws, 0, lib)
+    recs = [fields(ln) for ln in log(lib)]
+    assert [(r["rows"], r["combine"]) for r in recs] == [(0, 0), (8, 0), (16, 1)]
+    assert [re.search(r"rows=\d+\+(\d+)", ln).group(1) for ln in log(lib)] == ["8", "8", "4"]
+    assert len({(r["chunk"], r["splits"], r["kernel"], r["units"]) for r in recs}) == 1
+    splits = recs[0]["splits"]
+    assert ws >= recs[0]["ml_to_o"] + 2 * splits * 20 * 8 * 64 * 4   # partials of all 20 rows
+    assert recs[0]["ml_to_o"] >= 2 * splits * 20 * 8 * 2 * 4
+    # one row group: a single launch that combines
+    lib.kvq_nodev_clear()
+    kvq.kvq_decode(h, Q, kvq.KVQ_BF16, 8, None, 0.125, O, None, WS, ws, 0, lib)
+    (line,) = log(lib)
+    assert fields(line)["combine"] == 1 and fields(line)["rows"] == 0
 
 
 def test_decode_query_tile_limits(lib):
