@@ -346,6 +346,7 @@ def main():
                 "append_tokens_per_s": round(wo.B * wo.T / (ro["app_ms"] * 1e-3), 1),
                 "decode_call_ms": round(ro["dec_ms"], 5), "decode_call_GBps": round(ac, 2),
                 "decode_call_frac_hbm_peak": round(ac / HBM_PEAK_GBPS, 4),
+                "decode_call_attn_TFLOPs": round(wo.attn_flops_per_decode() / (ro["dec_ms"] * 1e-3) / 1e12, 3),
                 "kv_bytes_per_step": ro["kv_bytes"], "layers_rotated": ro["L"],
                 "steps": ao.steps, "step_launch": "hip graph" if ro["graph"] else "eager",
                 "traffic": measured_traffic(name)}

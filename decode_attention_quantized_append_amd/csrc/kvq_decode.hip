@@ -456,7 +456,10 @@ __global__ __launch_bounds__(256, (min_blocks<NB, RT>())) void decode_mfma(Decod
     int b, s, len, base;
     locate_unit(p, L / p.Hkv, b, s, len, base);
     if (b < 0) return;
-    const int R = p.Tq * p.hpk;   // query rows tq0 .. tq0 + Tq - 1 of the T
+    // query rows tq0 .. tq0 + Tq - 1 of the T: the grid's y index is the
+    // group of Tg rows
+    const int tq0 = blockIdx.y * p.Tg, Tq = min(p.Tg, p.T - tq0);
+    const int R = Tq * p.hpk;
 
     // Q fragment (rt, blk) lane l: q[r = rt*16 + l%16][blk*32 + 8*(l/16) .. +7].
     // Loaded first: they do not depend on the session length.
@@ -470,7 +473,7 @@ __global__ __launch_bounds__(256, (min_blocks<NB, RT>())) void decode_mfma(Decod
 #pragma unroll
         for (int e = 0; e < 8; ++e) qv[x][e] = 0.0f;
         if (f < NFRAG && r < R) {
-            const int t = p.tq0 + r / p.hpk, hh = r % p.hpk;
+            const int t = tq0 + r / p.hpk, hh = r % p.hpk;
             const size_t i0 = (((size_t)b * p.T + t) * p.H + g * p.hpk + hh) * HD + blk * 32 + 8 * (l >> 4);
             if (p.dtype == 1) {
                 const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + i0);
@@ -536,7 +539,7 @@ __global__ __launch_bounds__(256, (min_blocks<NB, RT>())) void decode_mfma(Decod
             const int r = rt * 16 + 4 * q4 + i;
             int hi = 0, lo = 0;
             if (r < R) {
-                hi = len - p.T + p.tq0 + r / p.hpk + 1;
+                hi = len - p.T + tq0 + r / p.hpk + 1;
                 lo = p.window > 0 ? max(0, hi - p.window) : 0;
             }
             ws.vis_lo[rt][i] = max(lo, c0);
@@ -544,7 +547,7 @@ __global__ __launch_bounds__(256, (min_blocks<NB, RT>())) void decode_mfma(Decod
         }
     }
     // rows' visible ranges are nested by t; the intersection over real rows
-    ws.full_hi = min(len - p.T + p.tq0 + 1, c1);
+    ws.full_hi = min(len - p.T + tq0 + 1, c1);
     ws.full_lo = max(p.window > 0 ? max(0, len - p.window) : 0, c0);
     const float sc2 = p.scale * kLog2e;
     __syncthreads();   // Q fragments are in LDS
@@ -629,14 +632,14 @@ __global__ __launch_bounds__(256, (min_blocks<NB, RT>())) void decode_mfma(Decod
             const float mw = ml[(w * RT * 16 + r) * 2];
             if (mw != -INFINITY) l += ml[(w * RT * 16 + r) * 2 + 1] * __builtin_amdgcn_exp2f(mw - M);
         }
-        const int t = p.tq0 + r / p.hpk, h = g * p.hpk + r % p.hpk;
+        const int t = tq0 + r / p.hpk, h = g * p.hpk + r % p.hpk;
         const size_t idx = (row0 + t) * p.H + h;
         p.part_ml[2 * idx] = (M == -INFINITY) ? -INFINITY : M * kLn2;
         p.part_ml[2 * idx + 1] = l;
     }
     for (int e = tid; e < R * HD; e += 256) {
         const int r = e / HD, d = e - r * HD;
-        const int t = p.tq0 + r / p.hpk, h = g * p.hpk + r % p.hpk;
+        const int t = tq0 + r / p.hpk, h = g * p.hpk + r % p.hpk;
         p.part_o[((row0 + t) * p.H + h) * HD + d] = obuf[r * HD + d];
     }
 }

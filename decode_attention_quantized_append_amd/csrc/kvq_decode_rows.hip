@@ -113,7 +113,10 @@ __global__ __launch_bounds__(512) void decode_rows(DecodeParams p) {
     dec::locate_unit(p, L / ngrp, b, s, len, base);
     if (b < 0) return;
     const int gi = wave % gh, rt = wave / gh, g = hg * gh + gi;
-    const int R = p.Tq * p.hpk;   // query rows tq0 .. tq0 + Tq - 1 of the T
+    // query rows tq0 .. tq0 + Tq - 1 of the T: the grid's y index is the
+    // group of Tg rows
+    const int tq0 = blockIdx.y * p.Tg, Tq = min(p.Tg, p.T - tq0);
+    const int R = Tq * p.hpk;
 
     // Q rows of this wave as the B operand of S^T = K Q^T:
     // lane (q4, j16) holds Q[row rt*16 + j16][blk*32 + 8*q4 .. +7]
@@ -121,7 +124,7 @@ __global__ __launch_bounds__(512) void decode_rows(DecodeParams p) {
     {
         const int r = rt * 16 + j16;
         const bool real = r < R;
-        const int t = real ? p.tq0 + r / p.hpk : 0, hh = real ? r % p.hpk : 0;
+        const int t = real ? tq0 + r / p.hpk : 0, hh = real ? r % p.hpk : 0;
         const size_t i0 = (((size_t)b * p.T + t) * p.H + g * p.hpk + hh) * HD + 8 * q4;
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) {
@@ -221,12 +224,12 @@ __global__ __launch_bounds__(512) void decode_rows(DecodeParams p) {
     {
         const int r = rt * 16 + j16;
         if (r < R) {
-            vis_hi = len - p.T + p.tq0 + r / p.hpk + 1;
+            vis_hi = len - p.T + tq0 + r / p.hpk + 1;
             vis_lo = p.window > 0 ? max(0, vis_hi - p.window) : 0;
         }
     }
     // every real row of the call sees all of [full_lo, full_hi)
-    const int full_hi = min(len - p.T + p.tq0 + 1, c1);
+    const int full_hi = min(len - p.T + tq0 + 1, c1);
     const int full_lo = max(p.window > 0 ? max(0, len - p.window) : 0, c0);
     const float sc2 = p.scale * kLog2e;
     const int kcol = gi * NB * 34;   // this head's first K block inside the row segment
@@ -401,7 +404,7 @@ __global__ __launch_bounds__(512) void decode_rows(DecodeParams p) {
     {
         const int r = rt * 16 + j16;
         if (q4 == 0 && r < R) {
-            const int t = p.tq0 + r / p.hpk, hq = g * p.hpk + r % p.hpk;
+            const int t = tq0 + r / p.hpk, hq = g * p.hpk + r % p.hpk;
             const size_t idx = (row0 + t) * p.H + hq;
             p.part_ml[2 * idx] = (mrow == -INFINITY) ? -INFINITY : mrow * kLn2;
             p.part_ml[2 * idx + 1] = lsum;
@@ -411,7 +414,7 @@ __global__ __launch_bounds__(512) void decode_rows(DecodeParams p) {
     for (int i = 0; i < 4; ++i) {
         const int r = rt * 16 + 4 * q4 + i;
         if (r < R) {
-            const int t = p.tq0 + r / p.hpk, hq = g * p.hpk + r % p.hpk;
+            const int t = tq0 + r / p.hpk, hq = g * p.hpk + r % p.hpk;
             float* o = p.part_o + ((row0 + t) * p.H + hq) * HD + j16;
 #pragma unroll
             for (int dt = 0; dt < 2 * NB; ++dt) o[16 * dt] = oacc[dt][i];

@@ -123,7 +123,10 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4
     dec::locate_unit(p, L / ngrp, b, s, len, base);
     if (b < 0) return;
     const int g = hg * gh + gi;
-    const int R = p.Tq * p.hpk;   // query rows tq0 .. tq0 + Tq - 1 of the T
+    // query rows tq0 .. tq0 + Tq - 1 of the T: the grid's y index is the
+    // group of Tg rows
+    const int tq0 = blockIdx.y * p.Tg, Tq = min(p.Tg, p.T - tq0);
+    const int R = Tq * p.hpk;
 
     const int lo = p.window > 0 ? max(0, len - p.T + 1 - p.window) : 0;
     const int c0 = (lo & ~(kTile - 1)) + s * p.chunk;
@@ -201,11 +204,11 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4
         vis_lo[rt] = vis_hi[rt] = 0;
         const int r = rb + rt * 16 + j16;
         if (r < R) {
-            vis_hi[rt] = len - p.T + p.tq0 + r / p.hpk + 1;
+            vis_hi[rt] = len - p.T + tq0 + r / p.hpk + 1;
             vis_lo[rt] = p.window > 0 ? max(0, vis_hi[rt] - p.window) : 0;
         }
     }
-    const int full_hi = min(len - p.T + p.tq0 + 1, c1);
+    const int full_hi = min(len - p.T + tq0 + 1, c1);
     const int full_lo = max(p.window > 0 ? max(0, len - p.window) : 0, c0);
     const float sc2 = p.scale * kLog2e;
     float* const KSa = reinterpret_cast<float*>(scb + WN::KS);
@@ -244,7 +247,7 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4
     for (int rt = 0; rt < RTW; ++rt) {
         const int r = rb + rt * 16 + j16;
         const bool real = r < R;
-        const int t = real ? p.tq0 + r / p.hpk : 0, hh = real ? r % p.hpk : 0;
+        const int t = real ? tq0 + r / p.hpk : 0, hh = real ? r % p.hpk : 0;
         const size_t i0 = (((size_t)b * p.T + t) * p.H + g * p.hpk + hh) * HD + 8 * q4;
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) {
@@ -568,7 +571,7 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4
     for (int rt = 0; rt < RTW; ++rt) {
         const int r = rb + rt * 16 + j16;
         if (q4 == 0 && r < R) {
-            const int t = p.tq0 + r / p.hpk, hq = g * p.hpk + r % p.hpk;
+            const int t = tq0 + r / p.hpk, hq = g * p.hpk + r % p.hpk;
             const size_t idx = (row0 + t) * p.H + hq;
             p.part_ml[2 * idx] = (mrow[rt] == -INFINITY) ? -INFINITY : mrow[rt] * kLn2;
             p.part_ml[2 * idx + 1] = lsum[rt];
@@ -577,7 +580,7 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4
         for (int i = 0; i < 4; ++i) {
             const int ro = rb + rt * 16 + 4 * q4 + i;
             if (ro < R) {
-                const int t = p.tq0 + ro / p.hpk, hq = g * p.hpk + ro % p.hpk;
+                const int t = tq0 + ro / p.hpk, hq = g * p.hpk + ro % p.hpk;
                 float* o = p.part_o + ((row0 + t) * p.H + hq) * HD + j16;
 #pragma unroll
                 for (int dt = 0; dt < 2 * NB; ++dt) o[16 * dt] = oacc[rt][dt][i];

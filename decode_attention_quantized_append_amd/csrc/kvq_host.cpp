@@ -560,16 +560,11 @@ kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, c
     dp.sinks = sinks;
     dp.out = out;
     dp.lse = lse;
-    // groups of at most 32 / hpk query rows, one decode launch each, writing
-    // their rows' partials; the combine after the last folds all T rows
-    const int tg = kvq::kMaxRows / hpk;
-    for (int t0 = 0; t0 < T; t0 += tg) {
-        dp.tq0 = t0;
-        dp.Tq = std::min(tg, T - t0);
-        dp.combine = t0 + tg >= T;
-        const char* err = nullptr;
-        if (kvq::launch_decode(dp, stream, &err)) return fail(KVQ_EDEVICE, err ? err : "decode launch failed");
-    }
+    // workgroups take groups of at most 32 / hpk query rows; the combine
+    // folds all T rows
+    dp.Tg = std::min(T, kvq::kMaxRows / hpk);
+    const char* err = nullptr;
+    if (kvq::launch_decode(dp, stream, &err)) return fail(KVQ_EDEVICE, err ? err : "decode launch failed");
     return KVQ_OK;
 }
 

@@ -156,9 +156,8 @@ struct DecodeParams {
     const void* q;              // [B, T, H, hd]
     int32_t dtype;
     int32_t B, T, H, Hkv, hd, hpk, window;
-    int32_t tq0, Tq;            // the decode kernel computes query rows tq0 .. tq0 + Tq - 1
-                                // of the T (Tq * hpk <= 32); the combine folds all T
-    int32_t combine;            // launch the combine after the decode kernel
+    int32_t Tg;                 // query rows per decode workgroup: the grid's y index
+                                // runs over the groups of Tg rows (Tg * hpk <= 32)
     const uint8_t* k_planes;
     const uint8_t* v_planes;
     int64_t k_stride;

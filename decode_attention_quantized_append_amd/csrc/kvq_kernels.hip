@@ -331,7 +331,7 @@ int launch_decode_t(const DecodeParams& p, hipStream_t st, const char** err) {
     }
     const int items = std::max(1, p.units) * p.Hkv;
     const int grid = (items + 7) & ~7;
-    hipLaunchKernelGGL((dec::decode_mfma<NB, RT, QLO>), dim3(grid), dim3(256), lds, st, p);
+    hipLaunchKernelGGL((dec::decode_mfma<NB, RT, QLO>), dim3(grid, (p.T + p.Tg - 1) / p.Tg), dim3(256), lds, st, p);
     return check(err);
 }
 
@@ -348,7 +348,7 @@ int launch_rows_t(const DecodeParams& p, hipStream_t st, const char** err) {
     }
     const int items = std::max(1, p.units) * (p.Hkv / p.gh);
     const int grid = (items + 7) & ~7;
-    hipLaunchKernelGGL((rows::decode_rows<NB, RT, QLO>), dim3(grid), dim3(64 * p.gh * RT), p.lds, st, p);
+    hipLaunchKernelGGL((rows::decode_rows<NB, RT, QLO>), dim3(grid, (p.T + p.Tg - 1) / p.Tg), dim3(64 * p.gh * RT), p.lds, st, p);
     return check(err);
 }
 
@@ -365,13 +365,13 @@ int launch_stream_t(const DecodeParams& p, hipStream_t st, const char** err) {
     }
     const int items = std::max(1, p.units) * (p.Hkv / p.gh);
     const int grid = (items + 7) & ~7;
-    hipLaunchKernelGGL((stream::decode_stream<NB, RTW, QLO, RS, RG>), dim3(grid), dim3(64 * p.gh * RS * RG), p.lds, st, p);
+    hipLaunchKernelGGL((stream::decode_stream<NB, RTW, QLO, RS, RG>), dim3(grid, (p.T + p.Tg - 1) / p.Tg), dim3(64 * p.gh * RS * RG), p.lds, st, p);
     return check(err);
 }
 
 template <int NB>
 int launch_stream_nb(const DecodeParams& p, hipStream_t st, const char** err) {
-    const int R = std::min(p.T, kMaxRows / p.hpk) * p.hpk;   // rows per group of the plan
+    const int R = p.Tg * p.hpk;   // query rows per KV head of one group
     const bool qlo = p.dtype == 0;
     if (R > 16) {
         if (p.rg == 2)   // two 16-row groups, one wave each
@@ -391,7 +391,7 @@ int launch_stream_nb(const DecodeParams& p, hipStream_t st, const char** err) {
 
 template <int NB>
 int launch_rows_nb(const DecodeParams& p, hipStream_t st, const char** err) {
-    const int R = std::min(p.T, kMaxRows / p.hpk) * p.hpk;   // rows per group of the plan
+    const int R = p.Tg * p.hpk;   // query rows per KV head of one group
     const bool qlo = p.dtype == 0;
     if (R <= 16) return qlo ? launch_rows_t<NB, 1, true>(p, st, err) : launch_rows_t<NB, 1, false>(p, st, err);
     return qlo ? launch_rows_t<NB, 2, true>(p, st, err) : launch_rows_t<NB, 2, false>(p, st, err);
@@ -399,7 +399,7 @@ int launch_rows_nb(const DecodeParams& p, hipStream_t st, const char** err) {
 
 template <int NB>
 int launch_decode_nb(const DecodeParams& p, hipStream_t st, const char** err) {
-    const int R = std::min(p.T, kMaxRows / p.hpk) * p.hpk;   // rows per group of the plan
+    const int R = p.Tg * p.hpk;   // query rows per KV head of one group
     const bool qlo = p.dtype == 0;   // fp32 queries keep a low fp16 part
     if (R <= 16) return qlo ? launch_decode_t<NB, 1, true>(p, st, err) : launch_decode_t<NB, 1, false>(p, st, err);
     return qlo ? launch_decode_t<NB, 2, true>(p, st, err) : launch_decode_t<NB, 2, false>(p, st, err);
@@ -468,7 +468,7 @@ int launch_partials(const DecodeParams& p, hipStream_t st, const char** err) {
 int launch_decode(const DecodeParams& p, void* stream, const char** err) {
     hipStream_t st = (hipStream_t)stream;
     if (launch_partials(p, st, err)) return 1;
-    return p.combine ? launch_combine(p, st, err) : 0;
+    return launch_combine(p, st, err);
 }
 
 }  // namespace kvq

@@ -55,7 +55,7 @@ int launch_decode(const DecodeParams& p, void*, const char** err) {
                     " kernel=" + std::to_string(p.kernel) + " gh=" + std::to_string(p.gh) +
                     " sub=" + std::to_string(p.sub) + " rs=" + std::to_string(p.rs) + " rg=" + std::to_string(p.rg) +
                     " lds=" + std::to_string(p.lds) + " units=" + std::to_string(p.units) +
-                    " rows=" + std::to_string(p.tq0) + "+" + std::to_string(p.Tq) + " combine=" + std::to_string(p.combine);
+                    " Tg=" + std::to_string(p.Tg) + " groups=" + std::to_string((p.T + p.Tg - 1) / p.Tg);
     return record(s, err);
 }
 

@@ -23,6 +23,10 @@ Workloads (one attention layer each):
             131072, sinks ~ N(0,1) fp32, bf16 q/k/v ~ N(0,1)
   verify    2 sessions, 16 Q / 4 KV heads, head_dim 256, 131072 cached rows,
             T=8 causal verify rows, then rollback to len+3, bf16 q/k/v ~ N(0,1)
+  prime     a prompt chunk: 1 session of the qwen_gqa shape and inputs, 512
+            rows appended and attending causally, each within a 4096-row
+            sliding window, at 32768 rows (not one of the five measured
+            configurations: the chunked prime of a long prompt)
 The k/v distribution named "as config 1" for the batched and verify shapes
 is read as the tiny shape's N(0,1); ``kv_dist="outlier"`` selects the other
 reading (the qwen_gqa distribution).
@@ -111,9 +115,27 @@ class Workload:
         grow = max(self.T, self.rollback_keep * max(extra_steps, 1) + self.T)
         return int(self.lengths().max()) + grow + 64
 
+    def span(self) -> np.ndarray:
+        """Rows per session that the step's T query rows see together: the
+        last row's visible rows and, with a window, the T - 1 rows below."""
+        n = self.lengths()
+        return np.minimum(n, self.window + self.T - 1) if self.window else n
+
+    def attn_flops_per_decode(self) -> int:
+        """Multiply-adds x 2 of the attention the T query rows make: for each
+        query row and Q head, q.k and p.v over the rows it sees."""
+        n = self.lengths()
+        total = 0
+        for t in range(self.T):
+            upto = n - self.T + t + 1
+            vis = np.minimum(upto, self.window) if self.window else upto
+            total += int(vis.sum())
+        return 4 * self.hd * self.H * total
+
     def kv_bytes_per_decode(self) -> int:
-        """Algorithmic K+V bytes one decode reads: visible rows x row bytes."""
-        return int(self.visible().sum()) * (self.k_row_bytes + self.v_row_bytes)
+        """Algorithmic K+V bytes one decode reads: the rows its query rows
+        see (each once) x row bytes."""
+        return int(self.span().sum()) * (self.k_row_bytes + self.v_row_bytes)
 
     # -- generators ------------------------------------------------------
     def _cast(self, x: np.ndarray) -> np.ndarray:
@@ -196,6 +218,8 @@ WORKLOADS = {
                           window=1024, ring_cap=2048, ring_step=512, sinks=True),
     "verify": Workload("verify", 105, B=2, H=16, Hkv=4, hd=256, T=8, cached=131072,
                        rollback_keep=3),
+    "prime": Workload("prime", 106, B=1, H=32, Hkv=8, hd=128, T=512, cached=32768,
+                      window=4096, kv_dist="outlier"),
 }
 
 

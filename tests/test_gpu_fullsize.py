@@ -45,7 +45,7 @@ def step(w, p, i):
     return w.q(i), w.sink_logits()
 
 
-@pytest.mark.parametrize("name", ["tiny", "qwen_gqa", "batched", "sink_ring", "verify"])
+@pytest.mark.parametrize("name", ["tiny", "qwen_gqa", "batched", "sink_ring", "verify", "prime"])
 def test_full_size(name):
     rng = np.random.default_rng(7)
     w, p = setup(name)

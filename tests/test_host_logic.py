@@ -238,26 +238,25 @@ def test_decode_validation_and_plan(lib):
 
 
 def test_decode_query_row_groups(lib):
-    # more than 32 query rows per KV head: the T rows go to the decode kernel
-    # in groups of 32 / hpk, each launch writing its rows' partials, and one
-    # combine (after the last group) folds all T rows
+    # more than 32 query rows per KV head: the decode workgroups take groups
+    # of 32 / hpk rows (the launch's y index), and the combine folds all T
     h = create(lib, n_seqs=2, n_q_heads=8, n_kv_heads=2, head_dim=64, capacity=5000)
     kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 3000, [3000, 1000], 0, lib)
     ws = kvq.kvq_decode_workspace_bytes(h, 20, lib)
     lib.kvq_nodev_clear()
     kvq.kvq_decode(h, Q, kvq.KVQ_BF16, 20, None, 0.125, O, None, WS, ws, 0, lib)
-    recs = [fields(ln) for ln in log(lib)]
-    assert [(r["rows"], r["combine"]) for r in recs] == [(0, 0), (8, 0), (16, 1)]
-    assert [re.search(r"rows=\d+\+(\d+)", ln).group(1) for ln in log(lib)] == ["8", "8", "4"]
-    assert len({(r["chunk"], r["splits"], r["kernel"], r["units"]) for r in recs}) == 1
-    splits = recs[0]["splits"]
-    assert ws >= recs[0]["ml_to_o"] + 2 * splits * 20 * 8 * 64 * 4   # partials of all 20 rows
-    assert recs[0]["ml_to_o"] >= 2 * splits * 20 * 8 * 2 * 4
-    # one row group: a single launch that combines
+    (line,) = log(lib)
+    r = fields(line)
+    assert (r["T"], r["Tg"], r["groups"]) == (20, 8, 3)
+    assert ws >= r["ml_to_o"] + 2 * r["splits"] * 20 * 8 * 64 * 4   # partials of all 20 rows
+    assert r["ml_to_o"] >= 2 * r["splits"] * 20 * 8 * 2 * 4
+    # the same plan as one group of 8 rows
     lib.kvq_nodev_clear()
     kvq.kvq_decode(h, Q, kvq.KVQ_BF16, 8, None, 0.125, O, None, WS, ws, 0, lib)
-    (line,) = log(lib)
-    assert fields(line)["combine"] == 1 and fields(line)["rows"] == 0
+    (line8,) = log(lib)
+    r8 = fields(line8)
+    assert (r8["Tg"], r8["groups"]) == (8, 1)
+    assert all(r8[k] == r[k] for k in ("chunk", "splits", "kernel", "gh", "rs", "rg", "units"))
 
 
 def test_decode_query_tile_limits(lib):
