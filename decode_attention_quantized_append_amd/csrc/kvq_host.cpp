@@ -263,6 +263,7 @@ Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nul
     // rows; R is the query rows per KV head of one group
     const int hpk = c.n_q_heads / c.n_kv_heads;
     const int R = std::min<int>(T, kvq::kMaxRows / hpk) * hpk;
+    const int64_t groups = ceil_div(T, R / hpk);   // workgroups per (session, chunk, head group)
     int64_t total = 0, maxvis = 1;
     for (int b = 0; b < c.n_seqs; ++b) {
         const int64_t vis = span_of(h, b, T);
@@ -289,10 +290,10 @@ Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nul
             const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kvq::kLdsBytes / lds,
                                                                            waves_per_cu / waves_per_wg));
             const int64_t slots = 256 * per_cu;
-            int64_t ch = round_up(std::max<int64_t>(1, ceil_div(total * ngrp, slots)), p.rows);
+            int64_t ch = round_up(std::max<int64_t>(1, ceil_div(total * ngrp * groups, slots)), p.rows);
             for (;;) {
                 int64_t wgs = 0;
-                for (int b = 0; b < c.n_seqs; ++b) wgs += ceil_div(span_of(h, b, T), ch) * ngrp;
+                for (int b = 0; b < c.n_seqs; ++b) wgs += ceil_div(span_of(h, b, T), ch) * ngrp * groups;
                 if (wgs <= slots) break;
                 ch += p.rows;
             }
@@ -315,7 +316,7 @@ Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nul
         // least 64 rows per query row so that the partials (R x (hd + 2)
         // floats written and read back per chunk) stay within a few percent
         // of the chunk's K/V bytes (R x (hd + 2) x 8 / (64 R x 1.8125 hd)).
-        chunk = round_up(ceil_div(std::max<int64_t>(total, 1) * c.n_kv_heads, 2048), kvq::kSplitQuantum);
+        chunk = round_up(ceil_div(std::max<int64_t>(total, 1) * c.n_kv_heads * groups, 2048), kvq::kSplitQuantum);
         chunk = std::min<int64_t>(std::max<int64_t>(chunk, std::max<int64_t>(256, 64 * (int64_t)R)), 1 << 16);
         chunk = round_up(chunk, 256);   // whole rounds of 4 waves x 32 rows x 2 prefetched tiles
     }
