@@ -91,13 +91,22 @@ __device__ __forceinline__ h8 v_codes_sub(uint32_t lo, uint32_t hi) {
 // of one head taking alternate tiles); RG row groups (waves of one head
 // taking 16 query rows each of the same tiles, which they load in step so
 // that the second copy comes from L2).
-template <int NB, int RTW, bool QLO, int RS, int RG>
-__global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4), stream_waves_per_simd(NB, RTW, QLO)) void decode_stream(
+template <int NB, int RTW, bool QLO, int RS, int RG, int DS>
+__global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 || DS == 2 ? 8 : RTW == 1 ? 8 : 4),
+                             DS == 2 ? 2 : stream_waves_per_simd(NB, RTW, QLO)) void decode_stream(
     DecodeParams p) {
     static_assert(RS == 1 || RTW == 1, "row streams need one row tile per wave");
     static_assert(RG == 1 || (RTW == 1 && RS == 1 && RG == 2), "row groups are two, one row tile per wave");
+    static_assert(DS == 1 || (DS == 2 && RTW == 2 && RS == 1 && RG == 1), "dim halves hold both row tiles");
     using WN = Win<NB>;
-    constexpr int HD = NB * 32;
+    constexpr int HD = NB * 32;     // dims of this wave's slice of a head
+    // DS = 2: the two waves of a head take half of its dims each (NB blocks
+    // of the 2 NB), for all R query rows: each loads and unpacks only its
+    // half of the K and V windows, and the two partial score sums meet in
+    // LDS (XCH bytes per wave, two slots by tile parity).
+    constexpr int HDR = HD * DS;    // dims of a head
+    constexpr int XCH = DS == 2 ? 2 * RTW * 2 * 64 * 16 : 0;
+    constexpr int WSTR = WN::BYTES + XCH;
     // SH: the two row-group waves of a head share two tile buffers (each
     // wave copies 16 of the 32 rows), so that a second tile is in flight
     // while one is computed; per-wave scale arrays follow the shared buffers.
@@ -112,7 +121,8 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4
     const int q4 = lane >> 4, j16 = lane & 15;
     const int gh = p.gh, ngrp = p.Hkv / gh;
     constexpr int rs = RS;
-    const int gi = wave % gh;                    // head in the group
+    const int gi = DS == 2 ? wave >> 1 : wave % gh;   // head in the group
+    const int half = DS == 2 ? wave & 1 : 0;          // DS = 2: this wave's half of the dims
     const int str = RS > 1 ? wave / gh : 0;      // row stream
     const int rb = RG > 1 ? (wave / gh) * 16 : 0;   // first query row of this wave
 
@@ -133,7 +143,7 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4
     const int c1 = min(c0 + p.chunk, len);
     if (c0 >= c1) return;
 
-    uint8_t* const wb = smem + wave * WN::BYTES;
+    uint8_t* const wb = smem + wave * WSTR;
     // tile buffers: this wave's own, or its head's two shared ones
     uint8_t* const tb0 = SH ? smem + gi * 2 * RAW : wb;
     // scale arrays: at the end of the wave's buffer, or one set per head after
@@ -144,10 +154,10 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4
     const int hrow = SH ? rb : 0;       // first tile row this wave copies
     // This head's windows: K from the 16-byte boundary at or below its first
     // block (kofs bytes before it), V exactly its blocks.
-    const int kstart = g * NB * 34;
+    const int kstart = (g * DS + half) * NB * 34;
     const int kofs = kstart & 15;
     const uint8_t* const kwin = p.k_planes + (int64_t)b * p.k_stride + (kstart - kofs);
-    const uint8_t* const vwin = p.v_planes + (int64_t)b * p.v_stride + g * NB * 24;
+    const uint8_t* const vwin = p.v_planes + (int64_t)b * p.v_stride + (g * DS + half) * NB * 24;
     // per lane, the byte offset of its piece (instruction x) from the tile's first row
     uint32_t koff[NKH], voff[NVH];
 #pragma unroll
@@ -248,7 +258,7 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4
         const int r = rb + rt * 16 + j16;
         const bool real = r < R;
         const int t = real ? tq0 + r / p.hpk : 0, hh = real ? r % p.hpk : 0;
-        const size_t i0 = (((size_t)b * p.T + t) * p.H + g * p.hpk + hh) * HD + 8 * q4;
+        const size_t i0 = (((size_t)b * p.T + t) * p.H + g * p.hpk + hh) * HDR + half * HD + 8 * q4;
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) {
             float qv[8];
@@ -368,6 +378,27 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4
         if constexpr (SH) {
             rows::lds_barrier();                          // both copies of K(t) are read
             if (has2) issue_k(tn + kTile, tb);
+        } else if constexpr (DS == 2) {
+            // the two halves' partial sums: each wave adds the other's to its
+            // own (a + b == b + a, so both hold the same scores)
+            f4* const xo = reinterpret_cast<f4*>(wb + WN::BYTES) + (it & 1) * (RTW * 2 * 64);
+            const f4* const xp =
+                reinterpret_cast<const f4*>(smem + (wave ^ 1) * WSTR + WN::BYTES) + (it & 1) * (RTW * 2 * 64);
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    xo[(rt * 2 + h) * 64 + lane] = (f4){sv[rt][h][0], sv[rt][h][1], sv[rt][h][2], sv[rt][h][3]};
+            rows::lds_barrier();
+            if (next) issue_k(tn, tb);
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const f4 y = xp[(rt * 2 + h) * 64 + lane];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sv[rt][h][i] += y[i];
+                }
         } else {
             if (gh * rs > 1) __builtin_amdgcn_s_barrier();
             if (next) issue_k(tn, tb);
@@ -570,7 +601,7 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
         const int r = rb + rt * 16 + j16;
-        if (q4 == 0 && r < R) {
+        if (q4 == 0 && r < R && half == 0) {
             const int t = tq0 + r / p.hpk, hq = g * p.hpk + r % p.hpk;
             const size_t idx = (row0 + t) * p.H + hq;
             p.part_ml[2 * idx] = (mrow[rt] == -INFINITY) ? -INFINITY : mrow[rt] * kLn2;
@@ -581,7 +612,7 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4
             const int ro = rb + rt * 16 + 4 * q4 + i;
             if (ro < R) {
                 const int t = tq0 + ro / p.hpk, hq = g * p.hpk + ro % p.hpk;
-                float* o = p.part_o + ((row0 + t) * p.H + hq) * HD + j16;
+                float* o = p.part_o + ((row0 + t) * p.H + hq) * HDR + half * HD + j16;
 #pragma unroll
                 for (int dt = 0; dt < 2 * NB; ++dt) o[16 * dt] = oacc[rt][dt][i];
             }

@@ -125,6 +125,7 @@ struct Plan {
     int32_t sub;       // whole-row kernel: rows per buffer / 32
     int32_t rs;        // stream kernel: row streams (waves per KV head)
     int32_t rg;        // stream kernel: row groups of 16 query rows (waves per KV head)
+    int32_t ds;        // stream kernel: 2 = two waves per KV head, each half of its dims
     int32_t lds;       // dynamic LDS bytes
     int32_t rows;      // rows per buffer (chunks are a multiple)
     kvq::RowGeo geo;
@@ -179,6 +180,15 @@ bool stream_rg2_ok(const kvq_config& c, int R, int gh, bool f32_queries) {
     return 2 * gh * kvq::stream_wave_bytes(NB) <= kvq::kLdsBytes && 2 * gh <= waves;
 }
 
+// Can the stream kernel give each 256-dim KV head two waves of 128 dims
+// (both row tiles of 17..32 query rows each), with 2 * gh waves and their
+// LDS fitting a CU?
+bool stream_ds_ok(const kvq_config& c, int R, int gh) {
+    if (c.head_dim != 256 || R <= 16 || R > 32) return false;
+    if (gh < 1 || c.n_kv_heads % gh != 0 || 2 * gh > 8) return false;
+    return gh * 2 * kvq::stream_ds_wave_bytes() <= kvq::kLdsBytes;
+}
+
 // Is every session's first visible row, rounded down to 32, still resident?
 bool aligned_start_resident(const kvq_cache* h, int32_t T) {
     for (int b = 0; b < h->cfg.n_seqs; ++b)
@@ -212,7 +222,12 @@ bool choose_kernel(const kvq_cache* h, int R, int32_t T, bool f32_queries, Plan*
     // workgroup, whose loads clamp rows to the visible range.
     if (!aligned_start_resident(h, T)) return true;
     if (want == KVQ_DECODE_STREAM) {
+        // 256-dim heads with 17..32 query rows: two waves per head, each half
+        // of the dims (no unpacking done twice), in independent workgroups
+        // of one head unless a head group is set
+        const bool ds = h->sub_tiles == 3 || (h->sub_tiles == 0 && stream_ds_ok(c, R, 1));
         int gh = h->head_group;
+        if (gh == 0 && ds) gh = 1;
         if (gh == 0)
             // the largest head group: the waves of one workgroup share the
             // cache lines at the edges of adjacent head slices
@@ -221,6 +236,19 @@ bool choose_kernel(const kvq_cache* h, int R, int32_t T, bool f32_queries, Plan*
         if (!stream_ok(c, R, gh)) return h->decode_kernel == KVQ_DECODE_AUTO;
         p->kernel = kvq::kStream;
         p->gh = gh;
+        p->ds = 1;
+        p->rs = 1;
+        p->rg = 1;
+        p->lds = gh * kvq::stream_wave_bytes(NB);
+        p->rows = kvq::stream_rows_per_buffer(NB);
+        if (ds) {
+            // two waves per KV head, each half of a 256-dim head's dims for
+            // all 17..32 query rows
+            if (!stream_ds_ok(c, R, gh)) return false;
+            p->ds = 2;
+            p->lds = gh * 2 * kvq::stream_ds_wave_bytes();
+            return true;
+        }
         // sub_tiles = waves per KV head: row streams for R <= 16 query rows,
         // row groups above
         p->rs = R <= 16 ? h->sub_tiles : 1;         // 0: chosen with the chunk
@@ -281,12 +309,14 @@ Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nul
         // (bound by LDS and by the waves the register file holds), each a
         // whole number of buffers
         auto one_round = [&](int rs) {
-            const int64_t waves_per_wg = p.kernel == kvq::kStream ? p.gh * rs * p.rg : p.gh * RT;
+            const bool ds = p.kernel == kvq::kStream && p.ds == 2;
+            const int64_t waves_per_wg = p.kernel == kvq::kStream ? p.gh * rs * p.rg * p.ds : p.gh * RT;
             const int rtw = p.rg == 2 ? 1 : RT;   // row tiles per wave
             const int64_t waves_per_cu =
-                p.kernel == kvq::kStream ? 4 * kvq::stream_waves_per_simd(c.head_dim / 32, rtw, f32_queries) : 8;
-            const int64_t lds =
-                p.kernel == kvq::kStream ? p.gh * rs * p.rg * kvq::stream_wave_bytes(c.head_dim / 32) : p.lds;
+                ds ? 8 : p.kernel == kvq::kStream ? 4 * kvq::stream_waves_per_simd(c.head_dim / 32, rtw, f32_queries) : 8;
+            const int64_t lds = ds ? p.lds
+                                   : p.kernel == kvq::kStream ? p.gh * rs * p.rg * kvq::stream_wave_bytes(c.head_dim / 32)
+                                                              : p.lds;
             const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kvq::kLdsBytes / lds,
                                                                            waves_per_cu / waves_per_wg));
             const int64_t slots = 256 * per_cu;
@@ -306,7 +336,7 @@ Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nul
             const bool rs2 = stream_rs2_ok(c, R, p.gh) && !f32_queries;
             if (p.rs == 0) p.rs = (rs2 && (chunk > 0 ? chunk : one_round(2)) >= 4 * 32) ? 2 : 1;
             if (p.rs == 2 && !rs2 && fits) *fits = false;
-            p.lds = p.gh * p.rs * p.rg * kvq::stream_wave_bytes(c.head_dim / 32);
+            if (p.ds != 2) p.lds = p.gh * p.rs * p.rg * kvq::stream_wave_bytes(c.head_dim / 32);
         }
         if (chunk <= 0) chunk = one_round(p.kernel == kvq::kStream ? p.rs : 1);
         chunk = round_up(chunk, p.rows);
@@ -553,6 +583,7 @@ kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, c
     dp.sub = p.sub;
     dp.rs = p.rs;
     dp.rg = p.rg;
+    dp.ds = p.kernel == kvq::kStream ? p.ds : 1;
     dp.lds = p.lds;
     dp.geo = p.geo;
     dp.scale = scale;
@@ -607,8 +638,8 @@ kvq_status kvq_set_decode_tiling(kvq_cache* h, int32_t kernel, int32_t head_grou
     if (head_group > 0 && kernel != KVQ_DECODE_WHOLE_ROW && kernel != KVQ_DECODE_STREAM)
         return fail(KVQ_EINVAL, "head_group applies to the whole-row and stream kernels");
     if (sub_tiles != 0 && !(kernel == KVQ_DECODE_WHOLE_ROW && (sub_tiles == 1 || sub_tiles == 2 || sub_tiles == 4)) &&
-        !(kernel == KVQ_DECODE_STREAM && (sub_tiles == 1 || sub_tiles == 2)))
-        return fail(KVQ_EINVAL, "sub_tiles must be 0, or 1, 2 or 4 for the whole-row kernel, 1 or 2 for the stream kernel");
+        !(kernel == KVQ_DECODE_STREAM && (sub_tiles >= 1 && sub_tiles <= 3)))
+        return fail(KVQ_EINVAL, "sub_tiles must be 0, or 1, 2 or 4 for the whole-row kernel, 1, 2 or 3 for the stream kernel");
     h->decode_kernel = kernel;
     h->head_group = head_group;
     h->sub_tiles = sub_tiles;

@@ -140,6 +140,10 @@ inline int stream_wave_bytes(int NB) {
         default: return 0;
     }
 }
+// LDS bytes per wave of the dim-split stream kernel (head_dim 256, two waves
+// per head of 128 dims each, both row tiles): the 128-dim window buffer and
+// two slots of partial scores.
+inline int stream_ds_wave_bytes() { return StreamWin<4>::BYTES + 2 * 2 * 2 * 64 * 16; }
 inline int stream_rows_per_buffer(int) { return kRowTile; }
 // Waves per SIMD the stream kernel is compiled for (its register budget is
 // 512 / this): as many as its registers allow without spilling.  NB blocks of
@@ -177,6 +181,8 @@ struct DecodeParams {
                                 // taking every rs-th tile of the chunk (1 or 2)
     int32_t rg;                 // stream kernel: waves per KV head in a workgroup, each
                                 // taking 16 of the query rows (1 or 2)
+    int32_t ds;                 // stream kernel: 2 = two waves per KV head, each taking half
+                                // of its dims for all query rows (head_dim 256); else 1
     int32_t lds;                // dynamic LDS bytes of the decode workgroup
     RowGeo geo;                 // whole-row kernel geometry
     float scale;

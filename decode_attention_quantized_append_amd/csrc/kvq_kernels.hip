@@ -352,11 +352,11 @@ int launch_rows_t(const DecodeParams& p, hipStream_t st, const char** err) {
     return check(err);
 }
 
-template <int NB, int RTW, bool QLO, int RS, int RG>
+template <int NB, int RTW, bool QLO, int RS, int RG, int DS = 1>
 int launch_stream_t(const DecodeParams& p, hipStream_t st, const char** err) {
     static bool configured = false;
     if (!configured) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&stream::decode_stream<NB, RTW, QLO, RS, RG>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&stream::decode_stream<NB, RTW, QLO, RS, RG, DS>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) != hipSuccess) {
             *err = "cannot raise the LDS limit of the decode kernel";
             return 1;
@@ -365,7 +365,8 @@ int launch_stream_t(const DecodeParams& p, hipStream_t st, const char** err) {
     }
     const int items = std::max(1, p.units) * (p.Hkv / p.gh);
     const int grid = (items + 7) & ~7;
-    hipLaunchKernelGGL((stream::decode_stream<NB, RTW, QLO, RS, RG>), dim3(grid, (p.T + p.Tg - 1) / p.Tg), dim3(64 * p.gh * RS * RG), p.lds, st, p);
+    hipLaunchKernelGGL((stream::decode_stream<NB, RTW, QLO, RS, RG, DS>), dim3(grid, (p.T + p.Tg - 1) / p.Tg),
+                       dim3(64 * p.gh * RS * RG * DS), p.lds, st, p);
     return check(err);
 }
 
@@ -374,6 +375,12 @@ int launch_stream_nb(const DecodeParams& p, hipStream_t st, const char** err) {
     const int R = p.Tg * p.hpk;   // query rows per KV head of one group
     const bool qlo = p.dtype == 0;
     if (R > 16) {
+        if (p.ds == 2) {   // two waves per head, each half of its dims (head_dim 256)
+            if constexpr (NB == 8)
+                return qlo ? launch_stream_t<4, 2, true, 1, 1, 2>(p, st, err) : launch_stream_t<4, 2, false, 1, 1, 2>(p, st, err);
+            *err = "dim halves are built for head_dim 256 only";
+            return 1;
+        }
         if (p.rg == 2)   // two 16-row groups, one wave each
             return qlo ? launch_stream_t<NB, 1, true, 1, 2>(p, st, err) : launch_stream_t<NB, 1, false, 1, 2>(p, st, err);
         return qlo ? launch_stream_t<NB, 2, true, 1, 1>(p, st, err) : launch_stream_t<NB, 2, false, 1, 1>(p, st, err);

@@ -53,7 +53,7 @@ int launch_decode(const DecodeParams& p, void*, const char** err) {
                     " splits=" + std::to_string(p.splits) + " ml_to_o=" +
                     std::to_string((const char*)p.part_o - (const char*)p.part_ml) +
                     " kernel=" + std::to_string(p.kernel) + " gh=" + std::to_string(p.gh) +
-                    " sub=" + std::to_string(p.sub) + " rs=" + std::to_string(p.rs) + " rg=" + std::to_string(p.rg) +
+                    " sub=" + std::to_string(p.sub) + " rs=" + std::to_string(p.rs) + " rg=" + std::to_string(p.rg) + " ds=" + std::to_string(p.ds) +
                     " lds=" + std::to_string(p.lds) + " units=" + std::to_string(p.units) +
                     " Tg=" + std::to_string(p.Tg) + " groups=" + std::to_string((p.T + p.Tg - 1) / p.Tg);
     return record(s, err);

@@ -157,10 +157,11 @@ TILINGS = {
     "batched_small": [(WR, 8, 1), (WR, 4, 2), (WR, 2, 1), (ST, 8, 0), (ST, 4, 0), (ST, 8, 2), (ST, 4, 2)],
     "sink_ring_small": [(WR, 8, 1), (WR, 8, 2), (WR, 4, 1), (WR, 4, 4), (ST, 8, 0), (ST, 2, 0), (ST, 8, 2)],
     "verify_small": [(WR, 4, 1), (WR, 2, 1), (WR, 2, 2), (WR, 1, 1), (WR, 1, 2), (ST, 4, 0), (ST, 1, 0),
-                     (ST, 4, 1), (ST, 2, 1), (ST, 1, 1), (ST, 4, 2), (ST, 2, 2), (ST, 1, 2)],
+                     (ST, 4, 1), (ST, 2, 1), (ST, 1, 1), (ST, 4, 2), (ST, 2, 2), (ST, 1, 2), (ST, 4, 3),
+                     (ST, 2, 3), (ST, 1, 3)],
     "qwen_f32_small": [(WR, 8, 1), (WR, 2, 2), (ST, 8, 0), (ST, 4, 0), (ST, 8, 1)],
     "tiny": [(ST, 1, 0)],
-    "verify_f32_small": [(ST, 4, 1), (ST, 2, 1), (ST, 4, 2), (ST, 2, 2)],
+    "verify_f32_small": [(ST, 4, 1), (ST, 2, 1), (ST, 4, 2), (ST, 2, 2), (ST, 4, 3), (ST, 2, 3)],
 }
 
 
@@ -197,6 +198,8 @@ MANY = {
     "hd128_T40_sinks": (2, 8, 2, 128, 40, [700, 300], 0, True, "bf16", None),
     "hd256_T19": (1, 16, 4, 256, 19, [500], 0, False, "bf16", None),
     "hd256_T19_rows": (1, 16, 4, 256, 19, [500], 0, False, "bf16", (kvq.KVQ_DECODE_WHOLE_ROW, 0)),
+    "hd256_T19_dimhalves": (1, 16, 4, 256, 19, [500], 0, True, "bf16", (kvq.KVQ_DECODE_STREAM, 0, 3)),
+    "hd256_T13_window_dimhalves_f32": (2, 8, 2, 256, 13, [300, 97], 70, True, "f32", (kvq.KVQ_DECODE_STREAM, 2, 3)),
     "hd64_hpk1_T100": (1, 4, 4, 64, 100, [400], 0, False, "bf16", None),
     "hd64_T70_window": (2, 16, 4, 64, 70, [330, 71], 45, True, "bf16", None),
     "hd96_T33_window_f32": (2, 6, 2, 96, 33, [260, 40], 50, False, "f32", None),

@@ -329,11 +329,23 @@ def test_decode_kernel_choice(lib):
     lib.kvq_nodev_clear()
     assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 1, None, 0.1, O, None, WS, 1 << 40) == E
     assert log(lib) == []
-    # verify rows (T=8, 4 query heads per KV head: 32 rows, two row tiles per wave)
+    # verify rows (T=8, 4 query heads per KV head: 32 rows): two waves per
+    # 256-dim head, each half of its dims, one head per workgroup
     h = create(lib, n_seqs=2, n_q_heads=16, n_kv_heads=4, head_dim=256, capacity=5000)
     kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 4000, None, 0, lib)
     p = plan_of(lib, h, T=8)
-    assert (p["kernel"], p["gh"]) == (STREAM, 4) and p["lds"] <= 160 * 1024
+    assert (p["kernel"], p["gh"], p["ds"], p["rg"]) == (STREAM, 1, 2, 1) and 4 * p["lds"] <= 160 * 1024
+    kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_STREAM, 4, 3, lib)
+    p = plan_of(lib, h, T=8)
+    assert (p["kernel"], p["gh"], p["ds"]) == (STREAM, 4, 2) and p["lds"] <= 160 * 1024
+    kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_STREAM, 0, 2, lib)        # two 16-row groups instead
+    p = plan_of(lib, h, T=8)
+    assert (p["kernel"], p["gh"], p["ds"], p["rg"]) == (STREAM, 4, 1, 2) and p["lds"] <= 160 * 1024
+    # dim halves need 17..32 rows of 256-dim heads
+    lib.kvq_nodev_clear()
+    kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_STREAM, 0, 3, lib)
+    assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 4, None, 0.1, O, None, WS, 1 << 40) == E
+    assert log(lib) == []
     kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_WHOLE_ROW, 0, 0, lib)
     p = plan_of(lib, h, T=8)
     assert (p["kernel"], p["gh"]) == (WHOLE_ROW, 4)
@@ -366,12 +378,16 @@ def test_decode_row_streams(lib):
     assert plan_of(lib, h)["rs"] == 2
     lib.kvq_nodev_clear()
     assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_F32, 1, None, 0.1, O, None, WS, 1 << 40) == kvq.KVQ_EINVAL
-    # more than 16 query rows per KV head: sub_tiles 2 (the default) gives
-    # each 16-row group its own wave, 1 keeps two row tiles in one wave
+    # more than 16 query rows per KV head: sub_tiles 2 gives each 16-row
+    # group its own wave, 1 keeps two row tiles in one wave; at head_dim 256
+    # the default is 3, two waves each taking half of the dims
     h = create(lib, n_seqs=2, n_q_heads=16, n_kv_heads=4, head_dim=256, capacity=5000)
     kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 4000, None, 0, lib)
     p = plan_of(lib, h, T=8)
-    assert (p["kernel"], p["gh"], p["rs"], p["rg"]) == (STREAM, 4, 1, 2) and p["lds"] <= 160 * 1024
+    assert (p["kernel"], p["gh"], p["rs"], p["rg"], p["ds"]) == (STREAM, 1, 1, 1, 2)
+    kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_STREAM, 0, 2, lib)
+    p = plan_of(lib, h, T=8)
+    assert (p["kernel"], p["gh"], p["rs"], p["rg"], p["ds"]) == (STREAM, 4, 1, 2, 1) and p["lds"] <= 160 * 1024
     kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_STREAM, 4, 1, lib)
     assert plan_of(lib, h, T=8)["rg"] == 1
     kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_STREAM, 2, 2, lib)
