@@ -93,7 +93,7 @@ __device__ __forceinline__ h8 v_codes_sub(uint32_t lo, uint32_t hi) {
 // that the second copy comes from L2).
 template <int NB, int RTW, bool QLO, int RS, int RG, int DS>
 __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 || DS == 2 ? 8 : RTW == 1 ? 8 : 4),
-                             DS == 2 ? 2 : stream_waves_per_simd(NB, RTW, QLO)) void decode_stream(
+                             DS == 2 ? stream_ds_waves_per_simd(NB) : stream_waves_per_simd(NB, RTW, QLO)) void decode_stream(
     DecodeParams p) {
     static_assert(RS == 1 || RTW == 1, "row streams need one row tile per wave");
     static_assert(RG == 1 || (RTW == 1 && RS == 1 && RG == 2), "row groups are two, one row tile per wave");

@@ -180,13 +180,14 @@ bool stream_rg2_ok(const kvq_config& c, int R, int gh, bool f32_queries) {
     return 2 * gh * kvq::stream_wave_bytes(NB) <= kvq::kLdsBytes && 2 * gh <= waves;
 }
 
-// Can the stream kernel give each 256-dim KV head two waves of 128 dims
-// (both row tiles of 17..32 query rows each), with 2 * gh waves and their
-// LDS fitting a CU?
+// Can the stream kernel give each 128- or 256-dim KV head two waves of half
+// its dims (both row tiles of 17..32 query rows each), with 2 * gh waves and
+// their LDS fitting a CU?
 bool stream_ds_ok(const kvq_config& c, int R, int gh) {
-    if (c.head_dim != 256 || R <= 16 || R > 32) return false;
-    if (gh < 1 || c.n_kv_heads % gh != 0 || 2 * gh > 8) return false;
-    return gh * 2 * kvq::stream_ds_wave_bytes() <= kvq::kLdsBytes;
+    if ((c.head_dim != 128 && c.head_dim != 256) || R <= 16 || R > 32) return false;
+    if (gh < 1 || c.n_kv_heads % gh != 0) return false;
+    if (2 * gh > 8 || 2 * gh > 4 * kvq::stream_ds_waves_per_simd(c.head_dim / 64)) return false;
+    return gh * 2 * kvq::stream_ds_wave_bytes(c.head_dim) <= kvq::kLdsBytes;
 }
 
 // Is every session's first visible row, rounded down to 32, still resident?
@@ -222,9 +223,9 @@ bool choose_kernel(const kvq_cache* h, int R, int32_t T, bool f32_queries, Plan*
     // workgroup, whose loads clamp rows to the visible range.
     if (!aligned_start_resident(h, T)) return true;
     if (want == KVQ_DECODE_STREAM) {
-        // 256-dim heads with 17..32 query rows: two waves per head, each half
-        // of the dims (no unpacking done twice), in independent workgroups
-        // of one head unless a head group is set
+        // 128- and 256-dim heads with 17..32 query rows: two waves per head,
+        // each half of the dims (no unpacking done twice), in independent
+        // workgroups of one head unless a head group is set
         const bool ds = h->sub_tiles == 3 || (h->sub_tiles == 0 && stream_ds_ok(c, R, 1));
         int gh = h->head_group;
         if (gh == 0 && ds) gh = 1;
@@ -246,7 +247,7 @@ bool choose_kernel(const kvq_cache* h, int R, int32_t T, bool f32_queries, Plan*
             // all 17..32 query rows
             if (!stream_ds_ok(c, R, gh)) return false;
             p->ds = 2;
-            p->lds = gh * 2 * kvq::stream_ds_wave_bytes();
+            p->lds = gh * 2 * kvq::stream_ds_wave_bytes(c.head_dim);
             return true;
         }
         // sub_tiles = waves per KV head: row streams for R <= 16 query rows,
@@ -313,7 +314,7 @@ Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nul
             const int64_t waves_per_wg = p.kernel == kvq::kStream ? p.gh * rs * p.rg * p.ds : p.gh * RT;
             const int rtw = p.rg == 2 ? 1 : RT;   // row tiles per wave
             const int64_t waves_per_cu =
-                ds ? 8 : p.kernel == kvq::kStream ? 4 * kvq::stream_waves_per_simd(c.head_dim / 32, rtw, f32_queries) : 8;
+                ds ? 4 * kvq::stream_ds_waves_per_simd(c.head_dim / 64) : p.kernel == kvq::kStream ? 4 * kvq::stream_waves_per_simd(c.head_dim / 32, rtw, f32_queries) : 8;
             const int64_t lds = ds ? p.lds
                                    : p.kernel == kvq::kStream ? p.gh * rs * p.rg * kvq::stream_wave_bytes(c.head_dim / 32)
                                                               : p.lds;

@@ -140,10 +140,12 @@ inline int stream_wave_bytes(int NB) {
         default: return 0;
     }
 }
-// LDS bytes per wave of the dim-split stream kernel (head_dim 256, two waves
-// per head of 128 dims each, both row tiles): the 128-dim window buffer and
+// LDS bytes per wave of the dim-split stream kernel (two waves per head of
+// head_dim / 2 dims each, both row tiles): the half-head window buffer and
 // two slots of partial scores.
-inline int stream_ds_wave_bytes() { return StreamWin<4>::BYTES + 2 * 2 * 2 * 64 * 16; }
+inline int stream_ds_wave_bytes(int head_dim) {
+    return (head_dim == 256 ? StreamWin<4>::BYTES : StreamWin<2>::BYTES) + 2 * 2 * 2 * 64 * 16;
+}
 inline int stream_rows_per_buffer(int) { return kRowTile; }
 // Waves per SIMD the stream kernel is compiled for (its register budget is
 // 512 / this): as many as its registers allow without spilling.  NB blocks of
@@ -152,6 +154,10 @@ inline int stream_rows_per_buffer(int) { return kRowTile; }
 constexpr int stream_waves_per_simd(int NB, int RTW, bool QLO) {
     return RTW > 1 ? 1 : NB >= 8 ? 2 : NB >= 4 ? (QLO ? 3 : 4) : 4;
 }
+
+// Waves per SIMD of the dim-split stream kernel, by the blocks of its half
+// head: 3 for 128-dim heads (64-dim halves), 2 for 256-dim heads.
+constexpr int stream_ds_waves_per_simd(int NB_half) { return NB_half <= 2 ? 3 : 2; }
 
 enum DecodeKernel : int32_t { kPerHead = 0, kWholeRow = 1, kStream = 2 };
 

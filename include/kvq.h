@@ -200,8 +200,8 @@ typedef enum kvq_decode_kernel {
  * 32 for the whole-row kernel (1, 2 or 4); waves per KV head for the stream
  * kernel: 1 or 2 row streams (up to 16 query rows per head), 1 wave holding
  * both 16-row tiles or 2 row-group waves (17 to 32 rows), or 3 = two waves
- * each taking half of a 256-dim head for all rows (17 to 32 rows); 0 = chosen
- * per call.  The
+ * each taking half of a 128- or 256-dim head for all rows (17 to 32 rows);
+ * 0 = chosen per call.  The
  * whole-row and stream kernels need head_dim 64, 128 or 256; a kernel or
  * tiling that does not fit a call's shape makes that kvq_decode fail with
  * EINVAL, except that a session whose first visible row, rounded down to 32,

@@ -199,6 +199,8 @@ MANY = {
     "hd256_T19": (1, 16, 4, 256, 19, [500], 0, False, "bf16", None),
     "hd256_T19_rows": (1, 16, 4, 256, 19, [500], 0, False, "bf16", (kvq.KVQ_DECODE_WHOLE_ROW, 0)),
     "hd256_T19_dimhalves": (1, 16, 4, 256, 19, [500], 0, True, "bf16", (kvq.KVQ_DECODE_STREAM, 0, 3)),
+    "hd128_T40_dimhalves": (2, 8, 2, 128, 40, [700, 300], 0, True, "bf16", (kvq.KVQ_DECODE_STREAM, 0, 3)),
+    "hd128_T21_window_dimhalves_f32": (2, 32, 8, 128, 21, [400, 130], 90, False, "f32", (kvq.KVQ_DECODE_STREAM, 4, 3)),
     "hd256_T13_window_dimhalves_f32": (2, 8, 2, 256, 13, [300, 97], 70, True, "f32", (kvq.KVQ_DECODE_STREAM, 2, 3)),
     "hd64_hpk1_T100": (1, 4, 4, 64, 100, [400], 0, False, "bf16", None),
     "hd64_T70_window": (2, 16, 4, 64, 70, [330, 71], 45, True, "bf16", None),
