@@ -35,6 +35,7 @@ struct kvq_cache {
     int32_t decode_kernel;       // kvq_decode_kernel (KVQ_DECODE_AUTO: chosen per call)
     int32_t head_group;          // KV heads per workgroup (0: chosen per call)
     int32_t sub_tiles;           // whole-row kernel: rows per buffer / 32 (0: chosen per call)
+    int32_t graph_mode;          // plan decodes for every session's largest span
 };
 
 namespace {
@@ -198,8 +199,15 @@ bool aligned_start_resident(const kvq_cache* h, int32_t T) {
 }
 
 // Rows each session's chunks cover: from the first visible row rounded down
-// to 32 up to len.
+// to 32 up to len.  In graph mode, the most they can cover while the session
+// stays within its plane: the window plus T - 1 rows plus 31 of alignment,
+// or the whole plane; a decode captured in a graph then stays valid while the
+// lengths grow.
 int64_t span_of(const kvq_cache* h, int b, int32_t T) {
+    if (h->graph_mode) {
+        const int64_t cap = h->cfg.capacity;
+        return h->cfg.window > 0 ? std::min<int64_t>(cap + 31, h->cfg.window + T - 1 + 31) : cap;
+    }
     return std::max<int64_t>(0, h->len[b] - (visible_lo(h, h->len[b], T) & ~int64_t(31)));
 }
 
@@ -397,6 +405,7 @@ kvq_status kvq_create(const kvq_config* cfg, void* k_planes, void* v_planes,
     h->decode_kernel = KVQ_DECODE_AUTO;
     h->head_group = 0;
     h->sub_tiles = 0;
+    h->graph_mode = 0;
     int n = 2 * cfg->n_seqs + 4;
     std::vector<int32_t> idx(n), val(n, 0);
     for (int i = 0; i < n; ++i) idx[i] = i;
@@ -501,6 +510,7 @@ kvq_status kvq_append(kvq_cache* h, const void* k_new, const void* v_new, kvq_dt
         ap.len_d = len_d(h);
         ap.base_d = base_d(h);
         ap.done = scratch_d(h);
+        ap.overflow = scratch_d(h) + 1;
         ap.dtype = dtype;
         ap.B = B;
         ap.T = T;
@@ -663,6 +673,29 @@ kvq_status kvq_host_lengths(const kvq_cache* h, int64_t* len, int64_t* base) {
     for (int b = 0; b < h->cfg.n_seqs; ++b) {
         if (len) len[b] = h->len[b];
         if (base) base[b] = h->base[b];
+    }
+    return KVQ_OK;
+}
+
+kvq_status kvq_set_graph_mode(kvq_cache* h, int32_t on) {
+    if (!h) return fail(KVQ_EINVAL, "handle is NULL");
+    if (on != 0 && on != 1) return fail(KVQ_EINVAL, "on must be 0 or 1");
+    h->graph_mode = on;
+    return KVQ_OK;
+}
+
+kvq_status kvq_set_host_lengths(kvq_cache* h, const int64_t* len, const int64_t* base) {
+    if (!h || !len || !base) return fail(KVQ_EINVAL, "NULL argument");
+    const kvq_config& c = h->cfg;
+    for (int b = 0; b < c.n_seqs; ++b) {
+        if (base[b] < 0 || len[b] < base[b] || len[b] > INT32_MAX || len[b] - base[b] > c.capacity)
+            return fail(KVQ_EINVAL, "session " + std::to_string(b) + ": need 0 <= base <= len <= base + capacity");
+        if (c.ring_step == 0 && base[b] != 0)
+            return fail(KVQ_EINVAL, "session " + std::to_string(b) + ": a flat cache has base 0");
+    }
+    for (int b = 0; b < c.n_seqs; ++b) {
+        h->len[b] = len[b];
+        h->base[b] = base[b];
     }
     return KVQ_OK;
 }

@@ -28,6 +28,7 @@ struct AppendParams {
     int32_t* len_d;
     int32_t* base_d;
     int32_t* done;              // completion counter, 0 between launches
+    int32_t* overflow;          // set to 1 when rows did not fit the plane (sticky)
     int32_t dtype;              // kvq_dtype
     int32_t B;                  // sessions in the input tensors
     int32_t T;                  // rows per session in the input tensors

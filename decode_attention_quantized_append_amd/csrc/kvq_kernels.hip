@@ -168,6 +168,21 @@ __device__ __forceinline__ void append_unit(const AppendParams& p, int64_t unit,
     }
 }
 
+// Advances len_d of the launch's sessions by their rows, as far as the plane
+// holds them: rows past physical row capacity - 1 were not written, len_d
+// stops at base_d + capacity and the overflow flag is set.  The host checks
+// room before every append it enqueues; this guard is for launches replayed
+// from a captured graph, which the host does not see.
+__device__ void advance_lengths(const AppendParams& p) {
+    for (int i = 0; i < p.nsess; ++i) {
+        const int b = p.b0 + i;
+        const int room = max(0, p.capacity - (p.len_d[b] - p.base_d[b]));
+        const int n = min(p.n_new[i], room);
+        if (n < p.n_new[i]) *p.overflow = 1;
+        p.len_d[b] += n;
+    }
+}
+
 // Grid-stride over units of 8 blocks per workgroup step; the last workgroup
 // to finish advances len_d.  Every workgroup has consumed its len_d reads
 // (they fix its store addresses) before thread 0 counts it done, so a relaxed
@@ -180,14 +195,13 @@ __global__ __launch_bounds__(1024) void append_kernel(AppendParams p) {
         append_unit(p, u0 + (threadIdx.x >> 5), units, nblk);
     __syncthreads();
     if (gridDim.x == 1) {   // a single workgroup (a few rows): no counter needed
-        if (threadIdx.x == 0)
-            for (int i = 0; i < p.nsess; ++i) p.len_d[p.b0 + i] += p.n_new[i];
+        if (threadIdx.x == 0) advance_lengths(p);
         return;
     }
     if (threadIdx.x == 0) {
         const int prev = atomicAdd(p.done, 1);
         if (prev == (int)gridDim.x - 1) {
-            for (int i = 0; i < p.nsess; ++i) p.len_d[p.b0 + i] += p.n_new[i];
+            advance_lengths(p);
             atomicExch(p.done, 0);
         }
     }

@@ -28,7 +28,7 @@ STATUS_NAMES = {0: "KVQ_OK", 1: "KVQ_EINVAL", 2: "KVQ_ECAPACITY", 3: "KVQ_ERANGE
 # Every entry point the header declares.
 EXPORTS = ("kvq_required_bytes", "kvq_create", "kvq_append", "kvq_decode_workspace_bytes",
            "kvq_decode", "kvq_truncate", "kvq_set_split_rows", "kvq_set_decode_tiling", "kvq_info",
-           "kvq_host_lengths", "kvq_destroy", "kvq_last_error")
+           "kvq_host_lengths", "kvq_set_graph_mode", "kvq_set_host_lengths", "kvq_destroy", "kvq_last_error")
 
 
 class kvq_config(ctypes.Structure):
@@ -74,6 +74,8 @@ def _declare(lib):
         "kvq_set_decode_tiling": (st, [vp, i32, i32, i32]),
         "kvq_info": (st, [vp, ctypes.POINTER(kvq_info_t)]),
         "kvq_host_lengths": (st, [vp, i64p, i64p]),
+        "kvq_set_graph_mode": (st, [vp, i32]),
+        "kvq_set_host_lengths": (st, [vp, i64p, i64p]),
         "kvq_destroy": (None, [vp]),
         "kvq_last_error": (ctypes.c_char_p, []),
     }
@@ -196,6 +198,19 @@ def kvq_host_lengths(h: int, n_seqs: int, lib=None):
     return list(ln), list(bs)
 
 
+def kvq_set_graph_mode(h: int, on: bool, lib=None) -> None:
+    lib = lib or load()
+    _check(lib, lib.kvq_set_graph_mode(h, int(bool(on))))
+
+
+def kvq_set_host_lengths(h: int, lengths, bases, lib=None) -> None:
+    lib = lib or load()
+    n = len(lengths)
+    ln = (ctypes.c_int64 * n)(*[int(x) for x in lengths])
+    bs = (ctypes.c_int64 * n)(*[int(x) for x in bases])
+    _check(lib, lib.kvq_set_host_lengths(h, ln, bs))
+
+
 def kvq_destroy(h: int, lib=None) -> None:
     (lib or load()).kvq_destroy(h)
 
@@ -290,6 +305,18 @@ class KvqLayerCache:
 
     def host_lengths(self):
         return kvq_host_lengths(self.h, self.cfg.n_seqs, self.lib)
+
+    def set_graph_mode(self, on=True):
+        kvq_set_graph_mode(self.h, on, self.lib)
+
+    def set_host_lengths(self, lengths, bases):
+        kvq_set_host_lengths(self.h, lengths, bases, self.lib)
+
+    def device_lengths(self):
+        """(len_d, base_d, overflow) read back from the counters (synchronizes)."""
+        B = self.cfg.n_seqs
+        c = self.counters[:2 * B + 2].cpu().tolist()
+        return c[:B], c[B:2 * B], c[2 * B + 1]
 
     def planes(self):
         """(K, V) uint8 device views [B, capacity, row_bytes] of the physical planes."""

@@ -216,6 +216,26 @@ kvq_status kvq_info(const kvq_cache* h, kvq_info_t* out);
  * of n_seqs entries; either may be NULL). */
 kvq_status kvq_host_lengths(const kvq_cache* h, int64_t* len, int64_t* base);
 
+/* Graph mode (memra KvLayer len_d: steps with no host round-trip; a captured
+ * append -> decode chain replayed while the lengths grow).  When on (1),
+ * kvq_decode and kvq_decode_workspace_bytes plan for every session's largest
+ * span instead of its current one: the window plus T - 1 rows (plus 31 rows
+ * of alignment) for a windowed cache, the whole plane otherwise.  The decode
+ * kernels find each session's rows from len_d and base_d on the device, so a
+ * decode captured in a graph stays valid at any later length as long as no
+ * rebase is due.  Appends replayed from a graph are not seen by the host:
+ * the append kernel itself writes only rows that fit the plane, stops len_d
+ * at base_d + capacity, and then sets the overflow word counters[2 * n_seqs
+ * + 1] to 1 (it stays 1).  After replays, kvq_set_host_lengths brings the
+ * host mirror back in step.  Off (0) by default.  Errors: EINVAL. */
+kvq_status kvq_set_graph_mode(kvq_cache* h, int32_t on);
+
+/* Sets the host mirror of len and base (HOST arrays of n_seqs entries), for
+ * example to the device counters read back after graph replays.  Requires
+ * 0 <= base <= len <= base + capacity, and base 0 for a flat cache.  Nothing
+ * is enqueued.  Errors: EINVAL (nothing changed). */
+kvq_status kvq_set_host_lengths(kvq_cache* h, const int64_t* len, const int64_t* base);
+
 /* Frees the host handle only; device memory stays with the caller. */
 void kvq_destroy(kvq_cache* h);
 

@@ -1,8 +1,10 @@
-"""A decode step captured as one HIP graph (append one row per session,
+"""Steps captured as HIP graphs.  A steady step (append one row per session,
 decode, roll the lengths back to where they were) replays to the eager
 step's result: on every replay, with eager steps, other work and
-synchronisations between the replays.  The eager step itself is checked
-against the oracle first."""
+synchronisations between the replays; the eager step itself is checked
+against the oracle first.  In graph mode one captured step (append, decode)
+replays as the lengths grow, each replay against the oracle, and replays
+past the plane stop at its capacity."""
 import numpy as np
 import pytest
 import torch
@@ -68,3 +70,113 @@ def test_step_graph_replays_equal_eager(B, H, Hkv, hd, lens):
         step()                                 # and an eager step
         torch.cuda.synchronize(DEV)
         assert torch.equal(out, want), f"eager step after replay {r} differs"
+
+
+@pytest.mark.parametrize("B,H,Hkv,hd,window,cap,step,pre,steps",
+                         [(2, 32, 8, 128, 0, 700, 0, [500, 77], 24),            # flat: the grid covers the plane
+                          (2, 16, 4, 64, 64, 128, 32, [200, 170], 20),         # ring: window + T - 1 + 31 rows
+                          (1, 16, 4, 256, 0, 500, 0, [300], 12)])
+def test_graph_mode_replays_as_lengths_grow(B, H, Hkv, hd, window, cap, step, pre, steps):
+    """Graph mode: ONE captured step (append a row per session, decode) is
+    replayed `steps` times with no host call between replays, each time on
+    the next row and query written into the captured input buffers; the
+    device lengths grow by one per replay and every replay's output is the
+    oracle's at that length.  Afterwards the host mirror is set from the
+    device counters and eager steps continue (through a ring rebase)."""
+    rng = np.random.default_rng(hd + cap)
+    p = Pair(B, H, Hkv, hd, cap, window, step)
+    done = np.zeros(B, np.int64)
+    while np.any(done < pre):                    # pieces a ring can take without dropping visible rows
+        n = np.minimum(np.asarray(pre) - done, 32)
+        p.append(bf16_normal(rng, (B, int(n.max()), Hkv, hd)), bf16_normal(rng, (B, int(n.max()), Hkv, hd)),
+                 n.tolist())
+        done += n
+    room = int(min(cap - (p.ref.len - p.ref.base)))
+    steps = min(steps, room)                     # replays cannot rebase: stay within the plane
+    assert steps >= 5
+    g = p.gpu
+    g.set_graph_mode(True)
+    scale = hd ** -0.5
+    kd = torch.zeros((B, 1, Hkv, hd), dtype=torch.bfloat16, device=DEV)
+    vd, qd = torch.zeros_like(kd), torch.zeros((B, 1, H, hd), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((B, 1, H, hd), dtype=torch.float32, device=DEV)
+    lse = torch.empty((B, 1, H), dtype=torch.float32, device=DEV)
+    g.workspace(1)                               # allocated before the capture
+    torch.cuda.synchronize(DEV)
+    graph = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream(DEV)
+    cs.wait_stream(torch.cuda.current_stream(DEV))
+    with torch.cuda.graph(graph, stream=cs):
+        g.append(kd, vd)
+        g.decode(qd, scale, out=out, lse=lse)
+    torch.cuda.synchronize(DEV)
+    assert g.device_lengths()[0] == pre          # captured, not run
+    for r in range(steps):
+        kn, vn = bf16_normal(rng, (B, 1, Hkv, hd)), bf16_normal(rng, (B, 1, Hkv, hd))
+        q = bf16_normal(rng, (B, 1, H, hd))
+        kd.copy_(to_dev(kn, "bf16"))
+        vd.copy_(to_dev(vn, "bf16"))
+        qd.copy_(to_dev(q, "bf16"))
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize(DEV)
+        p.ref.append(kn, vn)
+        ref_o, ref_lse = p.ref.attention(q, scale=scale)
+        assert_close(out.cpu().numpy(), ref_o, f"replay {r} out")
+        assert_close(lse.cpu().numpy(), ref_lse, f"replay {r} lse")
+    ln, bs, overflow = g.device_lengths()
+    assert ln == p.ref.len.tolist() and bs == p.ref.base.tolist() and overflow == 0
+    g.set_host_lengths(ln, bs)
+    p.check_mirror()
+    p.check_planes()
+    g.set_graph_mode(False)
+    for r in range(3):                           # eager steps from the resynced mirror
+        k, v = bf16_normal(rng, (B, 24, Hkv, hd)), bf16_normal(rng, (B, 24, Hkv, hd))
+        p.append(k, v)
+        p.check_mirror()
+        p.decode(bf16_normal(rng, (B, 1, H, hd)), scale, what=f"eager step {r} after replays")
+    p.check_planes()
+
+
+def test_graph_replay_past_the_plane_stops_at_capacity():
+    """Replays that would append past the plane: the append kernel drops the
+    rows that do not fit, stops len_d at the capacity and sets the overflow
+    word; the decode keeps attending to the rows the plane holds."""
+    rng = np.random.default_rng(5)
+    B, H, Hkv, hd, cap = 2, 8, 2, 128, 300
+    pre = [297, 250]
+    p = Pair(B, H, Hkv, hd, cap)
+    p.append(bf16_normal(rng, (B, 297, Hkv, hd)), bf16_normal(rng, (B, 297, Hkv, hd)), pre)
+    g = p.gpu
+    g.set_graph_mode(True)
+    kd = torch.zeros((B, 1, Hkv, hd), dtype=torch.bfloat16, device=DEV)
+    vd, qd = torch.zeros_like(kd), torch.zeros((B, 1, H, hd), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((B, 1, H, hd), dtype=torch.float32, device=DEV)
+    lse = torch.empty((B, 1, H), dtype=torch.float32, device=DEV)
+    g.workspace(1)
+    torch.cuda.synchronize(DEV)
+    graph = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream(DEV)
+    cs.wait_stream(torch.cuda.current_stream(DEV))
+    with torch.cuda.graph(graph, stream=cs):
+        g.append(kd, vd)
+        g.decode(qd, 0.125, out=out, lse=lse)
+    torch.cuda.synchronize(DEV)
+    for r in range(6):
+        kn, vn = bf16_normal(rng, (B, 1, Hkv, hd)), bf16_normal(rng, (B, 1, Hkv, hd))
+        q = bf16_normal(rng, (B, 1, H, hd))
+        kd.copy_(to_dev(kn, "bf16"))
+        vd.copy_(to_dev(vn, "bf16"))
+        qd.copy_(to_dev(q, "bf16"))
+        graph.replay()
+        torch.cuda.synchronize(DEV)
+        fits = [int(p.ref.len[b]) < cap for b in range(B)]
+        p.ref.append(kn, vn, [1 if f else 0 for f in fits])
+        ref_o, ref_lse = p.ref.attention(q, scale=0.125)
+        assert_close(out.cpu().numpy(), ref_o, f"replay {r} out")
+        ln, bs, overflow = g.device_lengths()
+        assert ln == p.ref.len.tolist() and overflow == (1 if r >= 3 else 0)
+    assert p.ref.len.tolist() == [300, 256]
+    g.set_host_lengths(*g.device_lengths()[:2])
+    p.check_mirror()
+    p.check_planes()

@@ -259,6 +259,38 @@ def test_decode_query_row_groups(lib):
     assert all(r8[k] == r[k] for k in ("chunk", "splits", "kernel", "gh", "rs", "rg", "units"))
 
 
+def test_graph_mode_plan_and_host_resync(lib):
+    # graph mode: the decode plan covers each session's largest span (the
+    # plane, or the window plus T - 1 plus 31 rows), whatever the lengths now
+    h = create(lib, n_seqs=2, capacity=5000)
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 3000, [3000, 1000], 0, lib)
+    now = plan_of(lib, h)
+    kvq.kvq_set_graph_mode(h, True, lib)
+    g = plan_of(lib, h)
+    assert g["splits"] == -(-5000 // g["chunk"]) and g["units"] == 2 * g["splits"]
+    assert g["units"] >= now["units"]
+    assert kvq.kvq_decode_workspace_bytes(h, 1, lib) >= (g["ml_to_o"] + 2 * g["splits"] * 8 * 64 * 4)
+    kvq.kvq_set_graph_mode(h, False, lib)
+    assert plan_of(lib, h) == now
+    assert lib.kvq_set_graph_mode(h, 2) == kvq.KVQ_EINVAL
+    hw = create(lib, n_seqs=1, capacity=4096, window=100, ring_step=512)
+    kvq.kvq_append(hw, Q, Q, kvq.KVQ_BF16, 50, None, 0, lib)
+    kvq.kvq_set_graph_mode(hw, True, lib)
+    pw = plan_of(lib, hw, T=3)
+    assert pw["splits"] == -(-(100 + 2 + 31) // pw["chunk"])
+    # the host mirror set from outside (after replays the host did not see)
+    lib.kvq_nodev_clear()
+    kvq.kvq_set_host_lengths(h, [3100, 1200], [0, 0], lib)
+    assert lengths(lib, h, 2) == ([3100, 1200], [0, 0])
+    assert log(lib) == []
+    assert err(lib, kvq.kvq_set_host_lengths, h, [5001, 10], [0, 0]) == kvq.KVQ_EINVAL   # past the plane
+    assert err(lib, kvq.kvq_set_host_lengths, h, [10, 10], [0, 11]) == kvq.KVQ_EINVAL    # base above len
+    assert err(lib, kvq.kvq_set_host_lengths, h, [10, 10], [0, 5]) == kvq.KVQ_EINVAL     # flat: base 0
+    assert lengths(lib, h, 2) == ([3100, 1200], [0, 0])
+    kvq.kvq_set_host_lengths(hw, [5000], [4000], lib)
+    assert lengths(lib, hw, 1) == ([5000], [4000])
+
+
 def test_decode_query_tile_limits(lib):
     h = create(lib, n_seqs=1, n_q_heads=64, n_kv_heads=1, head_dim=256, capacity=100)
     kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 50, None, 0, lib)
