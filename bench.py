@@ -196,10 +196,10 @@ def run_gpu(w, args):
         if w.rollback_keep:                        # verify: keep rollback_keep of the T rows
             lens[li] = [x + w.rollback_keep for x in lens[li]]
             check(lib.kvq_truncate(h, (ctypes.c_int32 * B)(*lens[li]), st), "truncate")
-        elif not w.ring_cap:                       # steady length: drop the step's rows
-            check(lib.kvq_truncate(h, pre_arr, st), "truncate")
+        else:                                      # steady length: drop the step's rows (a ring
+            check(lib.kvq_truncate(h, pre_arr, st), "truncate")   # keeps its window resident)
 
-    steady = not w.rollback_keep and not w.ring_cap
+    steady = not w.rollback_keep
     if args.graph == "on" and not steady:
         raise SystemExit(f"--graph on: the {w.name} workload changes session lengths every step")
     use_graph = args.graph == "on" or (args.graph == "auto" and steady)
@@ -234,12 +234,37 @@ def run_gpu(w, args):
             steps_g[(args.warmup + i) % L].replay()
         torch.cuda.synchronize(dev)
         wall = time.perf_counter() - t0
+    rebase = None
+    if w.ring_cap:
+        # the ring's rebase, off the steady path: fill a layer's plane, then
+        # time the append that has to move the live rows down first (HIP
+        # events around the library call), against a plain append
+        one = (ctypes.c_int32 * B)(*([1] * B))
+        times = []
+        for li in range(min(L, 16)):
+            h = caches[li].h
+            room = min(cap - (int(x) - int(y)) for x, y in zip(*caches[li].host_lengths()))
+            for _ in range(room):
+                check(lib.kvq_append(h, kp, vp, dt, T, one, stream), "append")
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            base0 = caches[li].host_lengths()[1][0]
+            e0.record()
+            check(lib.kvq_append(h, kp, vp, dt, T, one, stream), "append with rebase")
+            e1.record()
+            torch.cuda.synchronize(dev)
+            assert caches[li].host_lengths()[1][0] > base0, "the append did not rebase"
+            times.append(e0.elapsed_time(e1))
+        ln, bs = caches[0].host_lengths()
+        rebase = dict(append_with_rebase_ms=round(sum(times) / len(times), 5),
+                      rows_moved_per_session=int(ln[0] - 1 - bs[0]), ring_step=w.ring_step,
+                      amortized_ms_per_append=round((sum(times) / len(times) - sum(app_ms) / len(app_ms))
+                                                    / w.ring_step, 6))
     kv_bytes = w.kv_bytes_per_decode()
     ms_step = wall * 1e3 / args.steps
     dec_avg = sum(dec_ms) / len(dec_ms)
     app_avg = sum(app_ms) / len(app_ms)
     dec_sorted = sorted(dec_ms)
-    return dict(L=L, cap=cap, ms_step=ms_step, graph=use_graph, dec_ms=dec_avg, app_ms=app_avg,
+    return dict(L=L, cap=cap, ms_step=ms_step, graph=use_graph, dec_ms=dec_avg, app_ms=app_avg, rebase=rebase,
                 dec_p10=dec_sorted[len(dec_ms) // 10], dec_p90=dec_sorted[(9 * len(dec_ms)) // 10],
                 kv_bytes=kv_bytes, ws_bytes=ws_bytes,
                 footprint=L * (caches[0].sizes.k_planes_bytes + caches[0].sizes.v_planes_bytes))
@@ -325,6 +350,8 @@ def main():
                      "algorithmic": r["kv_bytes"],
                      "kernel": "kvq_decode call (decode_kernel + combine_kernel), HIP events"},
     }
+    if r["rebase"]:
+        line["ring_rebase"] = r["rebase"]
     if not args.no_others:
         # the other workloads, same step and measurement, fewer steps; each
         # is a parity case of the tests as well
@@ -350,6 +377,8 @@ def main():
                 "kv_bytes_per_step": ro["kv_bytes"], "layers_rotated": ro["L"],
                 "steps": ao.steps, "step_launch": "hip graph" if ro["graph"] else "eager",
                 "traffic": measured_traffic(name)}
+            if ro["rebase"]:
+                others[name]["ring_rebase"] = ro["rebase"]
         line["other_workloads"] = others
     if not args.no_cpu_baseline:
         cb = run_cpu_baseline(w, args.cpu_seconds)
