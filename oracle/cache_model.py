@@ -107,6 +107,16 @@ class OracleCache:
         """(first logical row held, len): physical rows [0, len - base)."""
         return int(self.base[b]), int(self.len[b])
 
+    def importance(self, q, *, scale, sinks=None):
+        """float64 [B, capacity]: probability mass per physical row, summed
+        over the T query rows (the last T rows) and the H heads of q."""
+        q = np.asarray(q, dtype=np.float32)
+        B, T, H, hd = q.shape
+        if np.any(self.len < T):
+            raise ValueError("each session needs at least T committed rows")
+        return core.importance(q, [self.k[b] for b in range(B)], self.base, self.len, self.cap,
+                               n_kv_heads=self.Hkv, window=self.window, sinks=sinks, scale=scale)
+
     def attention(self, q, *, scale, sinks=None, sel=None, want_lse=True):
         """q: float32 [B, T, H, hd]; the T query rows are the last T rows."""
         q = np.asarray(q, dtype=np.float32)

@@ -56,6 +56,10 @@ def load(path: str | None = None):
         f32p, ctypes.POINTER(u8p), ctypes.POINTER(u8p), i64p, i64p, ctypes.c_int32,
         f32p, ctypes.c_float, i64p, ctypes.c_int64, f32p, f32p]
     lib.kvqo_attention.restype = ctypes.c_int
+    lib.kvqo_importance.argtypes = [
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        f32p, ctypes.POINTER(u8p), i64p, i64p, ctypes.c_int32, f32p, ctypes.c_float, f64p, ctypes.c_int64]
+    lib.kvqo_importance.restype = ctypes.c_int
     lib.kvqo_max_threads.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -164,6 +168,33 @@ def attention(q, k_planes, v_planes, base, length, *, n_kv_heads, window=0,
     if rc != 0:
         raise ValueError("oracle attention: argument outside the method's domain")
     return out, lse
+
+
+def importance(q, k_planes, base, length, capacity, *, n_kv_heads, window=0, sinks=None, scale,
+               lib=None):
+    """Attention importance: float64 [B, capacity], the probability mass of
+    each physical row summed over the T query rows and H heads of q (float32
+    [B, T, H, hd], the last T rows); rows no query row sees stay 0."""
+    lib = lib or load()
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    B, T, H, hd = q.shape
+    u8p = ctypes.POINTER(ctypes.c_uint8)
+    kp = [np.ascontiguousarray(p, dtype=np.uint8) for p in k_planes]
+    karr = (u8p * B)(*[_ptr(p, ctypes.c_uint8) for p in kp])
+    base = np.ascontiguousarray(base, dtype=np.int64)
+    length = np.ascontiguousarray(length, dtype=np.int64)
+    s = None
+    if sinks is not None:
+        s = np.ascontiguousarray(sinks, dtype=np.float32)
+        assert s.shape == (H,)
+    imp = np.zeros((B, int(capacity)), dtype=np.float64)
+    rc = lib.kvqo_importance(B, T, H, int(n_kv_heads), hd, _ptr(q, ctypes.c_float), karr,
+                             _ptr(base, ctypes.c_int64), _ptr(length, ctypes.c_int64), int(window),
+                             _ptr(s, ctypes.c_float) if s is not None else None, float(scale),
+                             _ptr(imp, ctypes.c_double), int(capacity))
+    if rc != 0:
+        raise ValueError("oracle importance: argument outside the method's domain")
+    return imp
 
 
 def max_threads(lib=None) -> int:

@@ -16,6 +16,12 @@
  *                          half-even ties; the round-trip error bound.
  *                          Parity with another implementation's bytes is
  *                          unpinned: the pages print no encoded block.
+ *   kvqo_importance        per-row probability mass summed over query
+ *                          rows and heads: it sums to T*H less the sinks'
+ *                          shares (closed form); equals a numpy softmax of
+ *                          each (row, head) with the sink as an extra
+ *                          column (brute force on small inputs); rows
+ *                          outside every window get 0.
  *   kvqo_attention         textbook attention (torch's fp64
  *                          scaled_dot_product_attention with repeated KV
  *                          heads and explicit masks) on K/V rows the codec
@@ -312,6 +318,63 @@ int kvqo_attention(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t hd,
             bad |= lb;
         }
         free(s);
+    }
+    return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Attention importance (cortiq-engine "Struct LayerKvCache",           */
+/* attend_group's imp_acc and accumulate_imp): the probability mass     */
+/* each stored row receives, summed over every query row t and Q head   */
+/* h of the call.  With s_j, M and Z as for the attention above,        */
+/*   p_j = exp(s_j - M) / Z     for j in [first, upto), else 0,         */
+/* and imp[b][j - base_b] += p_j.  The sink takes its share of Z but    */
+/* is no row, so nothing is added for it.  imp: double [B][cap],        */
+/* indexed by physical row.                                             */
+/* ------------------------------------------------------------------ */
+int kvqo_importance(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t hd,
+                    const float* q, const uint8_t* const* k_plane,
+                    const int64_t* base, const int64_t* len, int32_t window,
+                    const float* sinks, float scale, double* imp, int64_t cap) {
+    if (B <= 0 || T <= 0 || H <= 0 || Hkv <= 0 || hd <= 0 || hd % 32 != 0 ||
+        H % Hkv != 0 || window < 0 || cap <= 0)
+        return -1;
+    const int32_t heads_per_group = H / Hkv;
+    const int32_t blocks = hd / 32;
+    const int64_t k_bytes = (int64_t)Hkv * blocks * 34;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int32_t b = 0; b < B; ++b) {
+        if (len[b] - base[b] > cap) { bad = 1; continue; }
+        double* score = (double*)malloc((size_t)(len[b] + 1) * sizeof(double));
+        double kdeq[32];
+        for (int32_t t = 0; t < T && !bad; ++t) {
+            const int64_t row_end = len[b] - T + t + 1;          /* rows below it are seen */
+            const int64_t row_start = window > 0 && row_end > window ? row_end - window : 0;
+            if (row_end <= row_start || row_start < base[b]) { bad = 1; break; }
+            for (int32_t h = 0; h < H; ++h) {
+                const int32_t kv_group = h / heads_per_group;
+                const float* qrow = q + (((int64_t)b * T + t) * H + h) * hd;
+                double top = -INFINITY;
+                for (int64_t j = row_start; j < row_end; ++j) {
+                    const uint8_t* krow = k_plane[b] + (j - base[b]) * k_bytes + (int64_t)kv_group * blocks * 34;
+                    double dot = 0.0;
+                    for (int32_t kb = 0; kb < blocks; ++kb) {
+                        kvqo_q8_0_decode(krow + 34 * kb, kdeq);
+                        for (int i = 0; i < 32; ++i) dot += kdeq[i] * (double)qrow[32 * kb + i];
+                    }
+                    score[j - row_start] = dot * (double)scale;
+                    if (score[j - row_start] > top) top = score[j - row_start];
+                }
+                const double sink = sinks ? (double)sinks[h] : -INFINITY;
+                if (sink > top) top = sink;
+                double denom = sinks ? exp(sink - top) : 0.0;      /* the sink's share */
+                for (int64_t j = row_start; j < row_end; ++j) denom += exp(score[j - row_start] - top);
+                for (int64_t j = row_start; j < row_end; ++j)
+                    imp[(int64_t)b * cap + (j - base[b])] += exp(score[j - row_start] - top) / denom;
+            }
+        }
+        free(score);
     }
     return bad ? -1 : 0;
 }

@@ -77,6 +77,11 @@ int kvqo_attention(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t hd,
                    float* out, float* lse);
 
 /* Threads the attention loop may use (OpenMP), for reporting. */
+int kvqo_importance(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t hd,
+                    const float* q, const uint8_t* const* k_plane,
+                    const int64_t* base, const int64_t* len, int32_t window,
+                    const float* sinks, float scale, double* imp, int64_t cap);
+
 int kvqo_max_threads(void);
 
 #ifdef __cplusplus

@@ -261,6 +261,60 @@ def check_truncate_equals_fresh(lib):
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+def importance_of(cache, lib, q, scale, sinks=None):
+    saved = core._lib
+    core._lib = lib
+    try:
+        return cache.importance(q, scale=scale, sinks=sinks)
+    finally:
+        core._lib = saved
+
+
+def check_importance_textbook(lib, *, B=2, T=3, H=6, Hkv=2, hd=64, N=40, window=9, sinks=True, seed=3):
+    """Representable K: the importance equals a textbook softmax (torch,
+    float64) of every (query row, head) over its visible rows plus the sink as
+    one more column, the row columns summed over heads and query rows; rows
+    that no query row sees, and physical rows past len, hold 0."""
+    rng = np.random.default_rng(seed)
+    k = exact_k(rng, B * N, Hkv, hd).reshape(B, N, Hkv, hd)
+    v = np.zeros_like(k)
+    q = rng.standard_normal((B, T, H, hd)).astype(np.float32)
+    s = rng.standard_normal(H).astype(np.float32) if sinks else None
+    scale = float(np.float32(1 / np.sqrt(hd)))
+    c = OracleCache(B, Hkv, hd, N + 8, window=window)
+    c_append(c, lib, k, v)
+    imp = importance_of(c, lib, q, scale, sinks=s)
+    qt = torch.from_numpy(q.astype(np.float64)).permute(0, 2, 1, 3)                       # B,H,T,hd
+    kt = torch.from_numpy(k.astype(np.float64)).permute(0, 2, 1, 3).repeat_interleave(H // Hkv, 1)
+    scores = (qt @ kt.transpose(-1, -2)) * scale                                          # B,H,T,N
+    j = torch.arange(N)
+    upto = N - T + torch.arange(T) + 1
+    mask = j[None, :] < upto[:, None]
+    if window:
+        mask &= j[None, :] >= (upto[:, None] - window)
+    scores = scores.masked_fill(~mask, float("-inf"))
+    if s is not None:
+        col = torch.from_numpy(s.astype(np.float64))[None, :, None, None].expand(B, H, T, 1)
+        scores = torch.cat([scores, col], -1)
+    p = torch.softmax(scores, -1)[..., :N]
+    want = np.zeros((B, N + 8))
+    want[:, :N] = p.sum(dim=(1, 2)).numpy()
+    np.testing.assert_allclose(imp, want, rtol=1e-10, atol=1e-13)
+
+
+def check_importance_mass(lib):
+    """Without sinks every (query row, head) spreads probability 1 over its
+    rows: the importance of a session sums to T * H."""
+    rng = np.random.default_rng(4)
+    B, T, H, Hkv, hd, N = 3, 5, 8, 2, 32, 50
+    c = OracleCache(B, Hkv, hd, N, window=17)
+    k = (rng.standard_normal((B, N, Hkv, hd)) * 3).astype(np.float32)
+    c_append(c, lib, k, k, [N, N - 7, T])
+    imp = importance_of(c, lib, rng.standard_normal((B, T, H, hd)).astype(np.float32), 0.2)
+    np.testing.assert_allclose(imp.sum(1), T * H, rtol=1e-12)
+    assert np.all(imp >= 0)
+
+
 ALL_CHECKS = {
     "golden_codec": check_golden_codec,
     "f16_sample": check_f16_sample,
@@ -272,4 +326,8 @@ ALL_CHECKS = {
     "gqa_repeat": check_gqa_equals_repeated_heads,
     "ring_flat": check_ring_equals_flat,
     "truncate_fresh": check_truncate_equals_fresh,
+    "importance_textbook": check_importance_textbook,
+    "importance_textbook_gqa4": lambda lib: check_importance_textbook(lib, B=1, T=2, H=8, Hkv=2, hd=96,
+                                                                       N=30, window=0, sinks=False, seed=5),
+    "importance_mass": check_importance_mass,
 }

@@ -40,6 +40,12 @@ MUTANTS = {
     "f16_subnormal_shift": ("int shift = (e >= -14) ? 13 : 13 + (-14 - e);",
                             "int shift = (e >= -14) ? 13 : 13 + (-15 - e);"),
     "v_weight_unnormalised": ("o[d] = (float)(acc[d] / Z);", "o[d] = (float)(acc[d]);"),
+    "imp_sink_not_in_denominator": ("double denom = sinks ? exp(sink - top) : 0.0;", "double denom = 0.0;"),
+    "imp_unnormalised": ("exp(score[j - row_start] - top) / denom;", "exp(score[j - row_start] - top);"),
+    "imp_causal_off_by_one": ("const int64_t row_end = len[b] - T + t + 1;",
+                              "const int64_t row_end = len[b] - T + t;"),
+    "imp_window_off_by_one": ("row_end > window ? row_end - window : 0;", "row_end > window ? row_end - window + 1 : 0;"),
+    "imp_group_modulo": ("const int32_t kv_group = h / heads_per_group;", "const int32_t kv_group = h % Hkv;"),
 }
 
 
