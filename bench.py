@@ -234,6 +234,26 @@ def run_gpu(w, args):
             steps_g[(args.warmup + i) % L].replay()
         torch.cuda.synchronize(dev)
         wall = time.perf_counter() - t0
+    # attention importance of a step's query rows (an optional extra pass:
+    # it re-reads the K rows the step sees), timed with HIP events on a few
+    # layers after a decode of the same rows supplied the log-sum-exps
+    imp = torch.zeros((B, cap), dtype=torch.float32, device=dev)
+    imp_ms = []
+    for li in range(min(L, 8)):
+        h = caches[li].h
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        check(lib.kvq_append(h, kp, vp, dt, T, None, stream), "append")
+        check(lib.kvq_decode(h, qp, dt, T, sink_ptr, scale, op, lp, ws_ptr, ws_bytes, stream), "decode")
+        e0.record()
+        check(lib.kvq_importance(h, qp, dt, T, scale, lp, imp.data_ptr(), stream), "importance")
+        e1.record()
+        if w.rollback_keep:
+            lens[li] = [x + w.rollback_keep for x in lens[li]]
+            check(lib.kvq_truncate(h, (ctypes.c_int32 * B)(*lens[li]), stream), "truncate")
+        else:
+            check(lib.kvq_truncate(h, pre_arr, stream), "truncate")
+        torch.cuda.synchronize(dev)
+        imp_ms.append(e0.elapsed_time(e1))
     rebase = None
     if w.ring_cap:
         # the ring's rebase, off the steady path: fill a layer's plane, then
@@ -265,9 +285,17 @@ def run_gpu(w, args):
     app_avg = sum(app_ms) / len(app_ms)
     dec_sorted = sorted(dec_ms)
     return dict(L=L, cap=cap, ms_step=ms_step, graph=use_graph, dec_ms=dec_avg, app_ms=app_avg, rebase=rebase,
+                imp_ms=sum(imp_ms) / len(imp_ms),
                 dec_p10=dec_sorted[len(dec_ms) // 10], dec_p90=dec_sorted[(9 * len(dec_ms)) // 10],
                 kv_bytes=kv_bytes, ws_bytes=ws_bytes,
                 footprint=L * (caches[0].sizes.k_planes_bytes + caches[0].sizes.v_planes_bytes))
+
+
+def importance_summary(w, r):
+    """The importance pass reads the K rows of the step's span once."""
+    kbytes = int(w.span().sum()) * w.k_row_bytes
+    return {"ms": round(r["imp_ms"], 5), "k_bytes": kbytes,
+            "GBps": round(kbytes / (r["imp_ms"] * 1e-3) / 1e9, 2)}
 
 
 def run_cpu_baseline(w, seconds):
@@ -350,6 +378,7 @@ def main():
                      "algorithmic": r["kv_bytes"],
                      "kernel": "kvq_decode call (decode_kernel + combine_kernel), HIP events"},
     }
+    line["importance_call"] = importance_summary(w, r)
     if r["rebase"]:
         line["ring_rebase"] = r["rebase"]
     if not args.no_others:
@@ -377,6 +406,7 @@ def main():
                 "kv_bytes_per_step": ro["kv_bytes"], "layers_rotated": ro["L"],
                 "steps": ao.steps, "step_launch": "hip graph" if ro["graph"] else "eager",
                 "traffic": measured_traffic(name)}
+            others[name]["importance_call"] = importance_summary(wo, ro)
             if ro["rebase"]:
                 others[name]["ring_rebase"] = ro["rebase"]
         line["other_workloads"] = others

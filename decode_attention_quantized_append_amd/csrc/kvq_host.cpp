@@ -611,6 +611,48 @@ kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, c
     return KVQ_OK;
 }
 
+kvq_status kvq_importance(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, float scale,
+                          const float* lse, float* imp, kvq_stream stream) {
+    if (!h) return fail(KVQ_EINVAL, "handle is NULL");
+    if (!q || !lse || !imp) return fail(KVQ_EINVAL, "q, lse or imp is NULL");
+    if (dtype != KVQ_F32 && dtype != KVQ_BF16) return fail(KVQ_EINVAL, "dtype must be F32 or BF16");
+    if (!std::isfinite(scale)) return fail(KVQ_EINVAL, "scale must be finite");
+    if (T < 1) return fail(KVQ_EINVAL, "T must be >= 1");
+    const kvq_config& c = h->cfg;
+    int64_t maxspan = 0;
+    for (int b = 0; b < c.n_seqs; ++b) {
+        if (h->len[b] < T)
+            return fail(KVQ_EINVAL, "session " + std::to_string(b) + " holds fewer than T rows");
+        const int64_t lo = visible_lo(h, h->len[b], T);
+        if (lo < h->base[b])
+            return fail(KVQ_ERANGE, "session " + std::to_string(b) + ": visible rows were rebased away");
+        maxspan = std::max(maxspan, h->len[b] - lo);
+    }
+    kvq::ImportanceParams ip{};
+    ip.q = q;
+    ip.dtype = dtype;
+    ip.B = c.n_seqs;
+    ip.T = T;
+    ip.H = c.n_q_heads;
+    ip.Hkv = c.n_kv_heads;
+    ip.hd = c.head_dim;
+    ip.hpk = c.n_q_heads / c.n_kv_heads;
+    ip.window = c.window;
+    ip.capacity = c.capacity;
+    ip.k_planes = h->k;
+    ip.k_stride = (int64_t)h->sz.k_session_stride;
+    ip.k_row = (int32_t)h->sz.k_row_bytes;
+    ip.len_d = len_d(h);
+    ip.base_d = base_d(h);
+    ip.scale = scale;
+    ip.lse = lse;
+    ip.imp = imp;
+    ip.tiles = (int32_t)ceil_div(std::max<int64_t>(maxspan, 1), 64);
+    const char* err = nullptr;
+    if (kvq::launch_importance(ip, stream, &err)) return fail(KVQ_EDEVICE, err ? err : "importance launch failed");
+    return KVQ_OK;
+}
+
 kvq_status kvq_truncate(kvq_cache* h, const int32_t* new_len, kvq_stream stream) {
     if (!h || !new_len) return fail(KVQ_EINVAL, "NULL argument");
     const kvq_config& c = h->cfg;

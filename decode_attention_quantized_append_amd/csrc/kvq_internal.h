@@ -64,6 +64,23 @@ struct MoveParams {
     int32_t rows[kMaxSessionsPerLaunch];
 };
 
+// Attention importance: per session b and row j of the T query rows' union,
+// imp[b][j - base] += sum over (t, h) of exp(scale q.K'_j - lse[b, t, h]).
+struct ImportanceParams {
+    const void* q;              // [B, T, H, hd]
+    int32_t dtype;
+    int32_t B, T, H, Hkv, hd, hpk, window, capacity;
+    const uint8_t* k_planes;
+    int64_t k_stride;
+    int32_t k_row;
+    const int32_t* len_d;
+    const int32_t* base_d;
+    float scale;
+    const float* lse;           // [B, T, H], natural log, the sink included
+    float* imp;                 // [B, capacity] by physical row
+    int32_t tiles;              // 64-row tiles per session in the grid
+};
+
 // Geometry of the whole-row decode kernel (one workgroup per session, chunk
 // and group of gh KV heads; buffers of 32*sub rows).  Byte counts are per
 // row segment of the group.
@@ -205,5 +222,6 @@ int launch_append(const AppendParams& p, void* stream, const char** err);
 int launch_set(const SetParams& p, void* stream, const char** err);
 int launch_move(const MoveParams& p, void* stream, const char** err);
 int launch_decode(const DecodeParams& p, void* stream, const char** err);
+int launch_importance(const ImportanceParams& p, void* stream, const char** err);
 
 }  // namespace kvq

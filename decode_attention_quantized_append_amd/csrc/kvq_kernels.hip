@@ -314,6 +314,80 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
 }
 
 // ---------------------------------------------------------------------------
+// Attention importance (cortiq-engine "Struct LayerKvCache": attend_group's
+// imp_acc, accumulate_imp).  Workgroup (tile, session) takes 64 rows of the
+// session's visible union, one row per lane; wave w takes the query rows
+// r = w, w + 4, ... of every KV head's R = T * hpk rows, in chunks of 8, and
+// dots each with its lane's dequantized K row block by block (fp32, the q8_0
+// scale applied per block).  The row's probability for query row r (query
+// row t = r / hpk, head g * hpk + r % hpk) is exp(scale s - lse) where the
+// row is visible to t, else 0; the four waves' sums meet in LDS and one
+// thread per row adds the total to imp.  The rows of a workgroup are its
+// own, so no atomics are needed.
+constexpr int kImpRows = 64, kImpChunk = 8;
+__global__ __launch_bounds__(256) void importance_kernel(ImportanceParams p) {
+    __shared__ float part[4][kImpRows];
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int len = p.len_d[b], base = p.base_d[b];
+    const int lo = p.window > 0 ? max(0, len - p.T + 1 - p.window) : 0;
+    const int j = lo + blockIdx.x * kImpRows + lane;
+    const bool row = j < len;
+    const int R = p.T * p.hpk;
+    const int nb = p.hd / 32;
+    const uint8_t* const krow =
+        p.k_planes + (int64_t)b * p.k_stride + (int64_t)(row ? j - base : 0) * p.k_row;
+    float acc_p = 0.0f;
+    for (int g = 0; g < p.Hkv; ++g) {
+        for (int r0 = wave; r0 < R; r0 += 4 * kImpChunk) {
+            float dot[kImpChunk];
+#pragma unroll
+            for (int c = 0; c < kImpChunk; ++c) dot[c] = 0.0f;
+            for (int blk = 0; blk < nb; ++blk) {
+                const uint8_t* kb = krow + (g * nb + blk) * 34;
+                const float d = row ? f16_value(*reinterpret_cast<const uint16_t*>(kb)) : 0.0f;
+                float code[32];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const uint16_t w = row ? *reinterpret_cast<const uint16_t*>(kb + 2 + 2 * i) : 0;
+                    code[2 * i] = (float)(int8_t)(w & 0xFF);
+                    code[2 * i + 1] = (float)(int8_t)(w >> 8);
+                }
+#pragma unroll
+                for (int c = 0; c < kImpChunk; ++c) {
+                    const int r = r0 + 4 * c;
+                    if (r < R) {
+                        const int t = r / p.hpk, h = g * p.hpk + r % p.hpk;
+                        const size_t qi = (((size_t)b * p.T + t) * p.H + h) * p.hd + blk * 32;
+                        float s = 0.0f;
+#pragma unroll
+                        for (int i = 0; i < 32; ++i) s = fmaf(load_in(p.q, p.dtype, qi + i), code[i], s);
+                        dot[c] = fmaf(d, s, dot[c]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < kImpChunk; ++c) {
+                const int r = r0 + 4 * c;
+                if (r < R && row) {
+                    const int t = r / p.hpk, h = g * p.hpk + r % p.hpk;
+                    const int upto = len - p.T + t + 1;
+                    const int first = p.window > 0 ? max(0, upto - p.window) : 0;
+                    if (j >= first && j < upto)
+                        acc_p += expf(p.scale * dot[c] - p.lse[((size_t)b * p.T + t) * p.H + h]);
+                }
+            }
+        }
+    }
+    part[wave][lane] = acc_p;
+    __syncthreads();
+    if (wave == 0 && row) {
+        float* dst = p.imp + (size_t)b * p.capacity + (j - base);
+        *dst += ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+    }
+}
+
+// ---------------------------------------------------------------------------
 int check(const char** err) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
@@ -487,6 +561,11 @@ int launch_partials(const DecodeParams& p, hipStream_t st, const char** err) {
     }
 }
 }  // namespace
+
+int launch_importance(const ImportanceParams& p, void* stream, const char** err) {
+    hipLaunchKernelGGL(importance_kernel, dim3(p.tiles, p.B), dim3(256), 0, (hipStream_t)stream, p);
+    return check(err);
+}
 
 int launch_decode(const DecodeParams& p, void* stream, const char** err) {
     hipStream_t st = (hipStream_t)stream;

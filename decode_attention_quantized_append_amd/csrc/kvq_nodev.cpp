@@ -59,6 +59,10 @@ int launch_decode(const DecodeParams& p, void*, const char** err) {
     return record(s, err);
 }
 
+int launch_importance(const ImportanceParams& p, void*, const char** err) {
+    return record("importance T=" + std::to_string(p.T) + " tiles=" + std::to_string(p.tiles), err);
+}
+
 }  // namespace kvq
 
 extern "C" {

@@ -28,7 +28,8 @@ STATUS_NAMES = {0: "KVQ_OK", 1: "KVQ_EINVAL", 2: "KVQ_ECAPACITY", 3: "KVQ_ERANGE
 # Every entry point the header declares.
 EXPORTS = ("kvq_required_bytes", "kvq_create", "kvq_append", "kvq_decode_workspace_bytes",
            "kvq_decode", "kvq_truncate", "kvq_set_split_rows", "kvq_set_decode_tiling", "kvq_info",
-           "kvq_host_lengths", "kvq_set_graph_mode", "kvq_set_host_lengths", "kvq_destroy", "kvq_last_error")
+           "kvq_host_lengths", "kvq_set_graph_mode", "kvq_set_host_lengths", "kvq_importance",
+           "kvq_destroy", "kvq_last_error")
 
 
 class kvq_config(ctypes.Structure):
@@ -75,6 +76,7 @@ def _declare(lib):
         "kvq_info": (st, [vp, ctypes.POINTER(kvq_info_t)]),
         "kvq_host_lengths": (st, [vp, i64p, i64p]),
         "kvq_set_graph_mode": (st, [vp, i32]),
+        "kvq_importance": (st, [vp, vp, i32, i32, f32, vp, vp, vp]),
         "kvq_set_host_lengths": (st, [vp, i64p, i64p]),
         "kvq_destroy": (None, [vp]),
         "kvq_last_error": (ctypes.c_char_p, []),
@@ -211,6 +213,12 @@ def kvq_set_host_lengths(h: int, lengths, bases, lib=None) -> None:
     _check(lib, lib.kvq_set_host_lengths(h, ln, bs))
 
 
+def kvq_importance(h: int, q: int, dtype: int, T: int, scale: float, lse: int, imp: int,
+                   stream: int = 0, lib=None) -> None:
+    lib = lib or load()
+    _check(lib, lib.kvq_importance(h, q, dtype, T, scale, lse, imp, stream or None))
+
+
 def kvq_destroy(h: int, lib=None) -> None:
     (lib or load()).kvq_destroy(h)
 
@@ -305,6 +313,20 @@ class KvqLayerCache:
 
     def host_lengths(self):
         return kvq_host_lengths(self.h, self.cfg.n_seqs, self.lib)
+
+    def importance(self, q, scale, lse, imp=None):
+        """Adds the step's attention importance to imp (float32 [B, capacity],
+        physical rows; zeros when None) and returns it.  lse: what decode of
+        the same q returned."""
+        import torch
+        B, T, H, hd = q.shape
+        assert q.is_contiguous() and lse.is_contiguous() and lse.dtype == torch.float32
+        if imp is None:
+            imp = torch.zeros((B, self.cfg.capacity), dtype=torch.float32, device=self.device)
+        assert imp.dtype == torch.float32 and imp.is_contiguous() and imp.shape == (B, self.cfg.capacity)
+        kvq_importance(self.h, q.data_ptr(), self._dtype(q), T, float(scale), lse.data_ptr(),
+                       imp.data_ptr(), self._stream(), self.lib)
+        return imp
 
     def set_graph_mode(self, on=True):
         kvq_set_graph_mode(self.h, on, self.lib)

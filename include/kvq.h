@@ -171,6 +171,21 @@ kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T,
                       const float* sinks, float scale, float* out, float* lse,
                       void* ws, size_t ws_bytes, kvq_stream stream);
 
+/* Attention importance (cortiq LayerKvCache attend_group's imp_acc and
+ * accumulate_imp: the attention mass each stored row receives, summed over
+ * heads).  For the q, dtype, T and scale of a kvq_decode call, and the lse it
+ * wrote (natural log, the sink included), adds to imp[b][row - base_b], for
+ * every row a query row t sees, the sum over t and the n_q_heads heads of
+ * exp(scale * q.K'_row - lse[b, t, h]): the row's softmax probability.  Rows
+ * no query row sees get nothing; the sink's share is in lse but lands on no
+ * row.  imp: device float [n_seqs, capacity], indexed by physical row (a ring
+ * rebase moves K and V rows, not importance).  Call it before the cache
+ * changes again.  One launch; the rows of a session are split over
+ * workgroups, each adding to its own rows only.
+ * Errors: EINVAL, ERANGE (a visible row was rebased away), EDEVICE. */
+kvq_status kvq_importance(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, float scale,
+                          const float* lse, float* imp, kvq_stream stream);
+
 /* Rollback (memra Cache::rollback, full-attention part: len = snapshot_len +
  * accept_len, no copy; cortiq LayerKvCache::truncate_last).  new_len is a
  * HOST array of n_seqs lengths, each <= the current length.  Enqueues the

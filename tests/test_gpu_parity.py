@@ -225,6 +225,46 @@ def test_decode_many_query_rows(name):
     p.decode(q, float(np.float32(1 / np.sqrt(hd))), sinks=s, what=name)
 
 
+IMPORTANCE = {
+    # name: (B, H, Hkv, hd, T, lengths, window, cap, step, sinks, io)
+    "hd128_gqa": (2, 32, 8, 128, 1, [700, 300], 0, 720, 0, False, "bf16"),
+    "hd64_sink_ring": (2, 16, 4, 64, 1, [330, 250], 64, 128, 32, True, "bf16"),
+    "hd256_verify_f32": (1, 16, 4, 256, 8, [400], 0, 420, 0, True, "f32"),
+    "hd128_prime_window": (1, 8, 2, 128, 40, [300], 100, 320, 0, True, "bf16"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(IMPORTANCE))
+def test_importance_parity(name):
+    """Attention importance through the C ABI against the oracle's, after a
+    decode of the same query rows supplies the log-sum-exps; a second call
+    adds the same mass again."""
+    B, H, Hkv, hd, T, lens, window, cap, step, sinks, io = IMPORTANCE[name]
+    rng = np.random.default_rng(len(name) + hd)
+    p = Pair(B, H, Hkv, hd, cap, window, step, io=io)
+    done = np.zeros(B, np.int64)
+    while np.any(done < lens):
+        n = np.minimum(np.asarray(lens) - done, 32 if step else 400)
+        k, v = rows(rng, B, int(n.max()), Hkv, hd, io)
+        p.append(k, v, n.tolist())
+        done += n
+    q = qrows(rng, B, T, H, hd, io)
+    s = rng.standard_normal(H).astype(np.float32) if sinks else None
+    scale = float(np.float32(1 / np.sqrt(hd)))
+    qd = to_dev(q, io)
+    sd = torch.from_numpy(s).to(DEV) if s is not None else None
+    out, lse = p.gpu.decode(qd, scale, sinks=sd)
+    imp = p.gpu.importance(qd, scale, lse)
+    torch.cuda.synchronize(DEV)
+    want = p.ref.importance(q, scale=scale, sinks=s)
+    assert_close(imp.cpu().numpy(), want, name + " importance")
+    p.gpu.importance(qd, scale, lse, imp)
+    torch.cuda.synchronize(DEV)
+    assert_close(imp.cpu().numpy(), 2 * want, name + " importance, second call")
+    if s is None:
+        np.testing.assert_allclose(imp.sum(1).cpu().numpy(), 2 * T * H, rtol=1e-4)
+
+
 def test_chunked_prime_into_ring():
     """A prompt primed into a sliding-window ring in chunks: each chunk's rows
     are appended, then its rows attend causally (each within its window) to
