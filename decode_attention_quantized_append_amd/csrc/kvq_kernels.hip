@@ -316,19 +316,21 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
 // ---------------------------------------------------------------------------
 // Attention importance (cortiq-engine "Struct LayerKvCache": attend_group's
 // imp_acc, accumulate_imp).  Workgroup (tile, session) takes 64 rows of the
-// session's visible union, one row per lane; wave w takes the query rows
-// r = w, w + 4, ... of every KV head's R = T * hpk rows, in chunks of 8, and
-// dots each with its lane's dequantized K row block by block (fp32, the q8_0
-// scale applied per block).  The row's probability for query row r (query
-// row t = r / hpk, head g * hpk + r % hpk) is exp(scale s - lse) where the
-// row is visible to t, else 0; the four waves' sums meet in LDS and one
-// thread per row adds the total to imp.  The rows of a workgroup are its
-// own, so no atomics are needed.
-constexpr int kImpRows = 64, kImpChunk = 8;
+// session's visible union, one row per lane.  Per KV head g, the R = T * hpk
+// query rows go through LDS 32 at a time (coalesced loads); wave w takes rows
+// w, w + 4, ... of each such chunk and dots them with its lane's K row block
+// by block (the 32 codes converted once per block, the q values read from
+// LDS as broadcasts, fp32, the q8_0 scale applied per block).  The row's
+// probability for query row r (query row t = r / hpk, head g * hpk + r % hpk)
+// is exp(scale s - lse) where the row is visible to t, else 0; the four
+// waves' sums meet in LDS and one thread per row adds the total to imp.  The
+// rows of a workgroup are its own, so no atomics are needed.
+constexpr int kImpRows = 64, kImpChunk = 32;
 __global__ __launch_bounds__(256) void importance_kernel(ImportanceParams p) {
+    __shared__ __align__(16) float qs[kImpChunk * kMaxHeadDim];
     __shared__ float part[4][kImpRows];
     const int b = blockIdx.y;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int len = p.len_d[b], base = p.base_d[b];
     const int lo = p.window > 0 ? max(0, len - p.T + 1 - p.window) : 0;
     const int j = lo + blockIdx.x * kImpRows + lane;
@@ -339,10 +341,21 @@ __global__ __launch_bounds__(256) void importance_kernel(ImportanceParams p) {
         p.k_planes + (int64_t)b * p.k_stride + (int64_t)(row ? j - base : 0) * p.k_row;
     float acc_p = 0.0f;
     for (int g = 0; g < p.Hkv; ++g) {
-        for (int r0 = wave; r0 < R; r0 += 4 * kImpChunk) {
-            float dot[kImpChunk];
+        for (int r0 = 0; r0 < R; r0 += kImpChunk) {
+            __syncthreads();   // the previous chunk's rows are read
+            for (int e = tid; e < kImpChunk * p.hd; e += 256) {
+                const int rr = e / p.hd, dd = e - rr * p.hd, r = r0 + rr;
+                float x = 0.0f;
+                if (r < R) {
+                    const int t = r / p.hpk, h = g * p.hpk + r % p.hpk;
+                    x = load_in(p.q, p.dtype, (((size_t)b * p.T + t) * p.H + h) * p.hd + dd);
+                }
+                qs[e] = x;
+            }
+            __syncthreads();
+            float dot[kImpChunk / 4];
 #pragma unroll
-            for (int c = 0; c < kImpChunk; ++c) dot[c] = 0.0f;
+            for (int c = 0; c < kImpChunk / 4; ++c) dot[c] = 0.0f;
             for (int blk = 0; blk < nb; ++blk) {
                 const uint8_t* kb = krow + (g * nb + blk) * 34;
                 const float d = row ? f16_value(*reinterpret_cast<const uint16_t*>(kb)) : 0.0f;
@@ -354,21 +367,25 @@ __global__ __launch_bounds__(256) void importance_kernel(ImportanceParams p) {
                     code[2 * i + 1] = (float)(int8_t)(w >> 8);
                 }
 #pragma unroll
-                for (int c = 0; c < kImpChunk; ++c) {
-                    const int r = r0 + 4 * c;
-                    if (r < R) {
-                        const int t = r / p.hpk, h = g * p.hpk + r % p.hpk;
-                        const size_t qi = (((size_t)b * p.T + t) * p.H + h) * p.hd + blk * 32;
+                for (int c = 0; c < kImpChunk / 4; ++c) {
+                    if (r0 + wave + 4 * c < R) {   // the chunk's real rows (wave-uniform)
+                        const float4* qv = reinterpret_cast<const float4*>(qs + (wave + 4 * c) * p.hd + blk * 32);
                         float s = 0.0f;
 #pragma unroll
-                        for (int i = 0; i < 32; ++i) s = fmaf(load_in(p.q, p.dtype, qi + i), code[i], s);
+                        for (int i = 0; i < 8; ++i) {
+                            const float4 x = qv[i];
+                            s = fmaf(x.x, code[4 * i], s);
+                            s = fmaf(x.y, code[4 * i + 1], s);
+                            s = fmaf(x.z, code[4 * i + 2], s);
+                            s = fmaf(x.w, code[4 * i + 3], s);
+                        }
                         dot[c] = fmaf(d, s, dot[c]);
                     }
                 }
             }
 #pragma unroll
-            for (int c = 0; c < kImpChunk; ++c) {
-                const int r = r0 + 4 * c;
+            for (int c = 0; c < kImpChunk / 4; ++c) {
+                const int r = r0 + wave + 4 * c;
                 if (r < R && row) {
                     const int t = r / p.hpk, h = g * p.hpk + r % p.hpk;
                     const int upto = len - p.T + t + 1;
