@@ -11,7 +11,7 @@ namespace kvq {
 
 constexpr int kMaxSessionsPerLaunch = 64;   // by-value per-session arrays
 constexpr int kMaxSetPerLaunch = 128;
-constexpr int kMaxRows = 32;                // R = T * H / Hkv query rows per KV head
+constexpr int kMaxRows = 32;                // query rows per KV head in one decode workgroup (Tg * H / Hkv)
 constexpr int kMaxSplits = 1024;            // split-K chunks per session
 constexpr int kMaxHeadDim = 256;
 constexpr int kSplitQuantum = 64;           // split-K chunk rows are a multiple of this
