@@ -347,7 +347,19 @@ Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nul
             if (p.rs == 2 && !rs2 && fits) *fits = false;
             if (p.ds != 2) p.lds = p.gh * p.rs * p.rg * kvq::stream_wave_bytes(c.head_dim / 32);
         }
-        if (chunk <= 0) chunk = one_round(p.kernel == kvq::kStream ? p.rs : 1);
+        if (chunk <= 0) {
+            chunk = one_round(p.kernel == kvq::kStream ? p.rs : 1);
+            // a chunk of one tile leaves each wave a single load-then-compute
+            // pass: with half the heads per workgroup, as many workgroups take
+            // two tiles each (the second in flight while the first is
+            // computed) and write half as many partials
+            if (p.kernel == kvq::kStream && h->head_group == 0 && p.rs == 1 && p.rg == 1 && p.ds == 1 &&
+                p.gh % 2 == 0 && chunk <= p.rows) {
+                p.gh /= 2;
+                p.lds = p.gh * kvq::stream_wave_bytes(c.head_dim / 32);
+                chunk = 2 * p.rows;
+            }
+        }
         chunk = round_up(chunk, p.rows);
     } else if (chunk <= 0) {
         // About 2048 workgroups of (session, chunk, KV head), i.e. several per

@@ -349,17 +349,25 @@ def plan_of(lib, h, T=1, dtype=kvq.KVQ_BF16):
 
 def test_decode_kernel_choice(lib):
     PER_HEAD, WHOLE_ROW, STREAM = 0, 1, 2          # as recorded by the launcher
-    # 8 KV heads x 128: by default one wave per KV head, 8 heads per workgroup
+    # 8 KV heads x 128: one wave per KV head; 8192 rows would give each wave a
+    # single tile with 8 heads per workgroup, so 4 heads per workgroup take
+    # two tiles each (64-row chunks, the same number of workgroups)
     h = create(lib, n_seqs=1, n_q_heads=32, n_kv_heads=8, head_dim=128, capacity=9000)
     kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 8192, None, 0, lib)
     p = plan_of(lib, h)
-    assert (p["kernel"], p["gh"]) == (STREAM, 8) and 0 < p["lds"] <= 160 * 1024 and p["chunk"] % 32 == 0
+    assert (p["kernel"], p["gh"], p["chunk"]) == (STREAM, 4, 64) and 0 < p["lds"] <= 160 * 1024
     assert p["splits"] == -(-8192 // p["chunk"]) == p["units"]
-    # 8192 rows fill the GPU with one tile per wave: one row stream
     assert p["rs"] == 1
-    # fp32 queries too: all heads of a row in one workgroup
-    p = plan_of(lib, h, dtype=kvq.KVQ_F32)
-    assert (p["kernel"], p["gh"]) == (STREAM, 8)
+    # a head group that is set is kept
+    kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_STREAM, 8, 0, lib)
+    p = plan_of(lib, h)
+    assert (p["kernel"], p["gh"], p["chunk"]) == (STREAM, 8, 32)
+    kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_AUTO, 0, 0, lib)
+    # longer sessions: chunks of several tiles, all heads of a row in one workgroup
+    h2 = create(lib, n_seqs=4, n_q_heads=32, n_kv_heads=8, head_dim=128, capacity=30000)
+    kvq.kvq_append(h2, Q, Q, kvq.KVQ_BF16, 20000, None, 0, lib)
+    p = plan_of(lib, h2, dtype=kvq.KVQ_F32)
+    assert (p["kernel"], p["gh"]) == (STREAM, 8) and p["chunk"] > 64
     kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_PER_HEAD, 0, 0, lib)
     assert plan_of(lib, h)["kernel"] == PER_HEAD
     kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_WHOLE_ROW, 8, 1, lib)
