@@ -1,24 +1,27 @@
-// kvq_decode_stream.hip -- split-K flash decode, one KV head per wave, each
-// wave streaming its own head's row windows through a private LDS double
-// buffer (gfx950).  Included by kvq_kernels.hip (inside namespace kvq), after
-// kvq_decode_rows.hip.
+// kvq_decode_stream.hip -- split-K flash decode, each wave streaming one KV
+// head's row windows through LDS (gfx950).  Included by kvq_kernels.hip
+// (inside namespace kvq), after kvq_decode_rows.hip.
 //
 // The same partials as the other decode kernels (cortiq-engine "Struct
 // LayerKvCache", attend_group and attend_group_upto; memra-engine "Struct
 // KvLayer", len_d and base_d):
-//   * a workgroup is (session, chunk of rows, group of gh KV heads); wave w
-//     is KV head g = hg*gh + w and computes all R = T*H/Hkv query rows of the
-//     group (one or two 16-row tiles).  The waves of a workgroup read the same
-//     rows at about the same time, so the CU fetches whole row segments from
-//     HBM, but no wave waits for another: there is no workgroup barrier.
-//   * per 32-row tile, the wave copies its head's K window (the q8_0 blocks,
+//   * a workgroup is (session, chunk of rows, group of gh KV heads, group of
+//     query rows on the grid's y index); by default wave w is KV head
+//     g = hg*gh + w and computes all R query rows of its group (one or two
+//     16-row tiles).  Other layouts give a head two waves: row streams (RS,
+//     alternate tiles of a longer chunk, merged in LDS at the end), row
+//     groups (RG, 16 query rows each, sharing two tile buffers) or dim halves
+//     (DS, half of the head's dims each, partial scores added through LDS).
+//   * per 32-row tile, a wave copies its head's K window (the q8_0 blocks,
 //     from the 16-byte boundary at or below them) and V window (the q5_1
-//     blocks) of every row into its LDS buffer with global_load_lds_dwordx4.
-//     The next tile's K rows are requested as soon as the scores have read
-//     this tile's, its V rows as soon as P V has read these: each half has a
-//     whole phase of the wave's work to arrive, and the small buffer lets 16
-//     waves share a CU.  Row strides in LDS are odd numbers of 16-byte
-//     pieces, which keeps 8 consecutive rows on distinct banks.
+//     blocks) of every row into LDS with global_load_lds_dwordx4.  With one
+//     buffer per wave, the next tile's K rows are requested as soon as the
+//     scores have read this tile's and its V rows as soon as P V has read
+//     these; with two buffers per head the tile after next is requested.  A
+//     workgroup barrier before each K refill keeps the heads of a row in
+//     step, so that cache lines shared by adjacent head slices are fetched
+//     once.  Row strides in LDS are odd numbers of 16-byte pieces, which
+//     keeps 8 consecutive rows on distinct banks.
 //   * scores are computed transposed, S^T = K Q^T, one v_mfma_f32_16x16x32_f16
 //     per 32-element block, 16 keys and row tile; the K codes, exact in fp16,
 //     are converted once per tile and feed every row tile.  Each lane ends up
@@ -27,8 +30,8 @@
 //   * the V operand comes straight from the q5_1 bytes: ds_read_b64_tr_b8 of
 //     the 16 nibble bytes of 8 keys gives a lane the codes of its dimension
 //     (low nibble) and of dimension + 16 (high nibble); a second transposed
-//     read of the block headers gives the high-bit bytes, which a DPP row
-//     broadcast hands to the lanes that need them.
+//     read of the block headers gives the high-bit bytes, which ds_bpermute
+//     hands to the lanes that need them.
 //   * the q5_1 step multiplies P per block (P' = P * step, fp16); the offset
 //     term sum_key P * m is one more MFMA per tile against the offsets.
 namespace stream {
