@@ -11,11 +11,13 @@
 //                   launch arguments: create, truncate and rebase.
 //   move_kernel     one non-overlapping slab of a ring rebase.
 //   append_kernel   fused quantize-and-append at slot len_d - base_d, with
-//                   the len_d advance done by the last workgroup to finish.
-//   decode_kernel   split-K flash decode over one (session, row chunk,
-//                   KV head): online softmax of the group's T*H/Hkv query
-//                   rows, unnormalised partial (m, l, o).
+//                   the len_d advance (stopped at the plane) done by the last
+//                   workgroup to finish.
+//   decode kernels  split-K flash decode (kvq_decode.hip, kvq_decode_rows.hip,
+//                   kvq_decode_stream.hip): online softmax of a group of query
+//                   rows over a chunk of rows, unnormalised partial (m, l, o).
 //   combine_kernel  log-sum-exp fold of the splits plus the sink column.
+//   importance_kernel  per-row attention mass from the decode's lse.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
