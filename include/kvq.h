@@ -95,7 +95,9 @@ typedef struct kvq_sizes {
     size_t k_planes_bytes;    /* n_seqs * k_session_stride + 256 (read-only tail the
                                  decode may read past the last row; never written) */
     size_t v_planes_bytes;    /* n_seqs * v_session_stride */
-    size_t counters_bytes;    /* int32 len_d[B], base_d[B], then library scratch */
+    size_t counters_bytes;    /* int32 len_d[B], base_d[B], then library scratch:
+                                 [2B] the append's completion counter, [2B + 1]
+                                 the overflow word (see kvq_set_graph_mode) */
     size_t k_row_bytes;       /* Hkv*hd/32*34 */
     size_t v_row_bytes;       /* Hkv*hd/32*24 */
     size_t k_session_stride;  /* capacity*k_row_bytes rounded up to 256 */
@@ -136,7 +138,8 @@ kvq_status kvq_create(const kvq_config* cfg, void* k_planes, void* v_planes,
  * block from its own absmax / min-max with fp16 scales rounded to nearest
  * even and codes computed from the stored scales, rounded half to even) and
  * written at physical rows len_d[b] - base_d[b] + t; len_d[b] then grows by
- * n_new[b] inside the same launch.  In ring mode, if a session's rows would
+ * n_new[b] inside the same launch (rows that would pass the plane are never
+ * written: see kvq_set_graph_mode).  In ring mode, if a session's rows would
  * pass the last physical row, the library first rebases it: base grows by
  * whole ring_step units until the rows fit, the surviving rows
  * [new_base, len) are moved to physical row 0, and base_d is updated.
@@ -148,7 +151,7 @@ kvq_status kvq_append(kvq_cache* h, const void* k_new, const void* v_new,
                       kvq_stream stream);
 
 /* Device workspace bytes kvq_decode needs for T query rows at the handle's
- * current lengths. */
+ * current lengths (in graph mode, at every length the plane allows). */
 kvq_status kvq_decode_workspace_bytes(const kvq_cache* h, int32_t T, size_t* bytes);
 
 /* Decode attention (memra fa_decode_dc / fa_decode_dcw; cortiq attend_group
@@ -161,9 +164,9 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache* h, int32_t T, size_t* byt
  * bytes, 256-byte aligned.  The committed length is read from len_d on the
  * device.  Requires len >= T for every session and H/Hkv <= 32.  Any T is
  * accepted (a prompt chunk attending causally, cortiq attend_group_upto with
- * many rows): the rows go to the decode kernel in groups of 32/(H/Hkv), one
- * launch each, and one combine folds all T rows; the workspace holds the
- * partials of all T rows.
+ * many rows): decode workgroups take the rows in groups of 32/(H/Hkv) (the
+ * launch's y index), and one combine folds all T rows; the workspace holds
+ * the partials of all T rows.
  * fp32 queries are used to about 2^-22 relative precision (fp16 hi + lo
  * parts); bf16 queries exactly while |q| < 65504 and |q| >= 2^-14 (fp16 range).
  * Errors: EINVAL, ERANGE (a visible row was rebased away), EDEVICE. */
@@ -206,7 +209,7 @@ typedef enum kvq_decode_kernel {
     KVQ_DECODE_AUTO = 0,        /* chosen per call */
     KVQ_DECODE_PER_HEAD = 1,    /* one KV head per workgroup, any head_dim */
     KVQ_DECODE_WHOLE_ROW = 2,   /* workgroups stream whole row segments of adjacent KV heads */
-    KVQ_DECODE_STREAM = 3       /* one KV head per wave, each wave streaming its own rows */
+    KVQ_DECODE_STREAM = 3       /* one or two waves per KV head, each streaming its rows through LDS */
 } kvq_decode_kernel;
 
 /* Tuning: which kernel kvq_decode runs and how it tiles the cache.
