@@ -95,12 +95,12 @@ __device__ __forceinline__ h8 v_codes_sub(uint32_t lo, uint32_t hi) {
 // taking 16 query rows each of the same tiles, which they load in step so
 // that the second copy comes from L2).
 template <int NB, int RTW, bool QLO, int RS, int RG, int DS>
-__global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 || DS == 2 ? 8 : RTW == 1 ? 8 : 4),
+__global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4),
                              DS == 2 ? stream_ds_waves_per_simd(NB) : stream_waves_per_simd(NB, RTW, QLO)) void decode_stream(
     DecodeParams p) {
-    static_assert(RS == 1 || RTW == 1, "row streams need one row tile per wave");
+    static_assert(RS == 1 || RTW == 1 || DS == 2, "row streams need one row tile per wave, or dim halves");
     static_assert(RG == 1 || (RTW == 1 && RS == 1 && RG == 2), "row groups are two, one row tile per wave");
-    static_assert(DS == 1 || (DS == 2 && RTW == 2 && RS == 1 && RG == 1), "dim halves hold both row tiles");
+    static_assert(DS == 1 || (DS == 2 && RTW == 2 && RG == 1), "dim halves hold both row tiles");
     using WN = Win<NB>;
     constexpr int HD = NB * 32;     // dims of this wave's slice of a head
     // DS = 2: the two waves of a head take half of its dims each (NB blocks
@@ -124,10 +124,11 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 || DS == 2 ? 8 : RTW =
     const int q4 = lane >> 4, j16 = lane & 15;
     const int gh = p.gh, ngrp = p.Hkv / gh;
     constexpr int rs = RS;
-    const int gi = DS == 2 ? wave >> 1 : wave % gh;   // head in the group
+    const int wv = DS == 2 ? wave >> 1 : wave;         // wave index without the dim half
+    const int gi = wv % gh;                            // head in the group
     const int half = DS == 2 ? wave & 1 : 0;          // DS = 2: this wave's half of the dims
-    const int str = RS > 1 ? wave / gh : 0;      // row stream
-    const int rb = RG > 1 ? (wave / gh) * 16 : 0;   // first query row of this wave
+    const int str = RS > 1 ? wv / gh : 0;        // row stream
+    const int rb = RG > 1 ? (wv / gh) * 16 : 0;     // first query row of this wave
 
     const int W = gridDim.x, wid = blockIdx.x;
     const int L = (wid & 7) * (W >> 3) + (wid >> 3);
@@ -551,10 +552,13 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 || DS == 2 ? 8 : RTW =
     }
     // ---- row streams: the other streams hand (m, l, O) to stream 0 through
     // their own LDS buffers (lane-major, so that the 64 lanes hit 64 banks);
-    // only one-row-tile shapes run more than one stream
+    // one-row-tile shapes, and dim halves (whose hand-off also covers their
+    // score slots: every wave's last read of its partner's slot is done
+    // first)
     if constexpr (RS > 1) {
         constexpr int MOFS = RTW * 2 * NB * 4 * 64;      // floats before m, l
-        static_assert((MOFS + 64 * RTW) * 4 <= WN::BYTES, "row-stream hand-off does not fit the wave buffer");
+        static_assert((MOFS + 64 * RTW) * 4 <= WSTR, "row-stream hand-off does not fit the wave buffer");
+        if constexpr (DS == 2) rows::lds_barrier();
         __builtin_amdgcn_s_waitcnt(0xC07F);              // this wave's reads of its buffer are done
         float* const xb = reinterpret_cast<float*>(wb);
         if (str > 0) {
@@ -573,7 +577,7 @@ __global__ __launch_bounds__(64 * (RS == 2 ? 16 : RG == 2 || DS == 2 ? 8 : RTW =
         rows::lds_barrier();
         if (str == 0) {
             for (int o = 1; o < rs; ++o) {
-                const float* const yb = reinterpret_cast<const float*>(smem + (wave + o * gh) * WN::BYTES);
+                const float* const yb = reinterpret_cast<const float*>(smem + (wave + o * gh * DS) * WSTR);
 #pragma unroll
                 for (int rt = 0; rt < RTW; ++rt) {
                     const float m1 = yb[MOFS + rt * 32 + j16], l1 = yb[MOFS + rt * 32 + 16 + j16];

@@ -191,6 +191,17 @@ bool stream_ds_ok(const kvq_config& c, int R, int gh) {
     return gh * 2 * kvq::stream_ds_wave_bytes(c.head_dim) <= kvq::kLdsBytes;
 }
 
+// Can dim halves also run two row streams per head (four waves per head,
+// alternate tiles of a twice-as-long chunk, half as many partials)?  At
+// head_dim 256 only: with 128-dim heads (three waves per SIMD) the prime
+// chunk ran 12 % slower with them.
+bool stream_ds_rs2_ok(const kvq_config& c, int R, int gh) {
+    if (c.head_dim != 256 || !stream_ds_ok(c, R, gh)) return false;
+    const int waves = 4 * gh;
+    return waves <= 8 && waves <= 4 * kvq::stream_ds_waves_per_simd(c.head_dim / 64) &&
+           gh * 4 * kvq::stream_ds_wave_bytes(c.head_dim) <= kvq::kLdsBytes;
+}
+
 // Is every session's first visible row, rounded down to 32, still resident?
 bool aligned_start_resident(const kvq_cache* h, int32_t T) {
     for (int b = 0; b < h->cfg.n_seqs; ++b)
@@ -251,10 +262,11 @@ bool choose_kernel(const kvq_cache* h, int R, int32_t T, bool f32_queries, Plan*
         p->lds = gh * kvq::stream_wave_bytes(NB);
         p->rows = kvq::stream_rows_per_buffer(NB);
         if (ds) {
-            // two waves per KV head, each half of a 256-dim head's dims for
-            // all 17..32 query rows
+            // two waves per KV head, each half of a 128- or 256-dim head's
+            // dims for all 17..32 query rows; row streams chosen with the chunk
             if (!stream_ds_ok(c, R, gh)) return false;
             p->ds = 2;
+            p->rs = 0;
             p->lds = gh * 2 * kvq::stream_ds_wave_bytes(c.head_dim);
             return true;
         }
@@ -323,7 +335,7 @@ Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nul
             const int rtw = p.rg == 2 ? 1 : RT;   // row tiles per wave
             const int64_t waves_per_cu =
                 ds ? 4 * kvq::stream_ds_waves_per_simd(c.head_dim / 64) : p.kernel == kvq::kStream ? 4 * kvq::stream_waves_per_simd(c.head_dim / 32, rtw, f32_queries) : 8;
-            const int64_t lds = ds ? p.lds
+            const int64_t lds = ds ? p.gh * rs * 2 * kvq::stream_ds_wave_bytes(c.head_dim)
                                    : p.kernel == kvq::kStream ? p.gh * rs * p.rg * kvq::stream_wave_bytes(c.head_dim / 32)
                                                               : p.lds;
             const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kvq::kLdsBytes / lds,
@@ -342,10 +354,11 @@ Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nul
             // two row streams per head when each still gets a few tiles of
             // its chunk: the waves of a CU then advance together, and there
             // are half as many partials to combine
-            const bool rs2 = stream_rs2_ok(c, R, p.gh) && !f32_queries;
+            const bool rs2 = p.ds == 2 ? stream_ds_rs2_ok(c, R, p.gh) : stream_rs2_ok(c, R, p.gh) && !f32_queries;
             if (p.rs == 0) p.rs = (rs2 && (chunk > 0 ? chunk : one_round(2)) >= 4 * 32) ? 2 : 1;
             if (p.rs == 2 && !rs2 && fits) *fits = false;
-            if (p.ds != 2) p.lds = p.gh * p.rs * p.rg * kvq::stream_wave_bytes(c.head_dim / 32);
+            p.lds = p.ds == 2 ? p.gh * p.rs * 2 * kvq::stream_ds_wave_bytes(c.head_dim)
+                              : p.gh * p.rs * p.rg * kvq::stream_wave_bytes(c.head_dim / 32);
         }
         if (chunk <= 0) {
             chunk = one_round(p.kernel == kvq::kStream ? p.rs : 1);

@@ -483,10 +483,14 @@ int launch_stream_nb(const DecodeParams& p, hipStream_t st, const char** err) {
     const bool qlo = p.dtype == 0;
     if (R > 16) {
         if (p.ds == 2) {   // two waves per head, each half of its dims (head_dim 128 or 256)
-            if constexpr (NB == 8)
-                return qlo ? launch_stream_t<4, 2, true, 1, 1, 2>(p, st, err) : launch_stream_t<4, 2, false, 1, 1, 2>(p, st, err);
-            if constexpr (NB == 4)
-                return qlo ? launch_stream_t<2, 2, true, 1, 1, 2>(p, st, err) : launch_stream_t<2, 2, false, 1, 1, 2>(p, st, err);
+            constexpr int NH = NB / 2;
+            if constexpr (NB == 8 || NB == 4) {
+                if (p.rs == 2)   // and two row streams
+                    return qlo ? launch_stream_t<NH, 2, true, 2, 1, 2>(p, st, err)
+                               : launch_stream_t<NH, 2, false, 2, 1, 2>(p, st, err);
+                return qlo ? launch_stream_t<NH, 2, true, 1, 1, 2>(p, st, err)
+                           : launch_stream_t<NH, 2, false, 1, 1, 2>(p, st, err);
+            }
             *err = "dim halves are built for head_dim 128 and 256";
             return 1;
         }
