@@ -672,7 +672,7 @@ kvq_status kvq_importance(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t 
     ip.scale = scale;
     ip.lse = lse;
     ip.imp = imp;
-    ip.tiles = (int32_t)ceil_div(std::max<int64_t>(maxspan, 1), 64);
+    ip.tiles = (int32_t)ceil_div(std::max<int64_t>(maxspan, 1), 16);
     const char* err = nullptr;
     if (kvq::launch_importance(ip, stream, &err)) return fail(KVQ_EDEVICE, err ? err : "importance launch failed");
     return KVQ_OK;

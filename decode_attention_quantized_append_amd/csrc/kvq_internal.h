@@ -78,7 +78,7 @@ struct ImportanceParams {
     float scale;
     const float* lse;           // [B, T, H], natural log, the sink included
     float* imp;                 // [B, capacity] by physical row
-    int32_t tiles;              // 64-row tiles per session in the grid
+    int32_t tiles;              // 16-row tiles per session in the grid
 };
 
 // Geometry of the whole-row decode kernel (one workgroup per session, chunk

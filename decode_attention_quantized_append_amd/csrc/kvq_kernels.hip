@@ -317,92 +317,133 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
 
 // ---------------------------------------------------------------------------
 // Attention importance (cortiq-engine "Struct LayerKvCache": attend_group's
-// imp_acc, accumulate_imp).  Workgroup (tile, session) takes 64 rows of the
-// session's visible union, one row per lane.  Per KV head g, the R = T * hpk
-// query rows go through LDS 32 at a time (coalesced loads); wave w takes rows
-// w, w + 4, ... of each such chunk and dots them with its lane's K row block
-// by block (the 32 codes converted once per block, the q values read from
-// LDS as broadcasts, fp32, the q8_0 scale applied per block).  The row's
-// probability for query row r (query row t = r / hpk, head g * hpk + r % hpk)
-// is exp(scale s - lse) where the row is visible to t, else 0; the four
-// waves' sums meet in LDS and one thread per row adds the total to imp.  The
-// rows of a workgroup are its own, so no atomics are needed.
-constexpr int kImpRows = 64, kImpChunk = 32;
+// imp_acc, accumulate_imp).  Workgroup (tile, session) takes 16 rows (keys)
+// of the session's visible union; its four waves share the (KV head, 16-row
+// tile of query rows) pairs.  Per pair, the scores of the 16 keys against the
+// 16 query rows are S^T = K Q^T on v_mfma_f32_16x16x32_f16, one per 32-dim
+// block (the K codes exact in fp16, converted once per head; bf16 queries
+// exact in fp16, fp32 queries as an fp16 high and low part), each block's
+// product scaled by its keys' q8_0 scales.  Lane (q4, j16) then holds keys
+// 4 q4 + i against query row j16: the probability exp(scale s - lse) where
+// the key is visible to the row, else 0, summed over the 16 rows by
+// shuffles.  The waves' sums meet in LDS and one thread per key adds the
+// total to imp; a key belongs to one workgroup, so no atomics are needed.
+constexpr int kImpKeys = 16;
 __global__ __launch_bounds__(256) void importance_kernel(ImportanceParams p) {
-    __shared__ __align__(16) float qs[kImpChunk * kMaxHeadDim];
-    __shared__ float part[4][kImpRows];
+    using dec::f4;
+    using dec::h8;
+    __shared__ float part[4][kImpKeys];
     const int b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int q4 = lane >> 4, j16 = lane & 15;
     const int len = p.len_d[b], base = p.base_d[b];
     const int lo = p.window > 0 ? max(0, len - p.T + 1 - p.window) : 0;
-    const int j = lo + blockIdx.x * kImpRows + lane;
-    const bool row = j < len;
+    const int k0 = lo + blockIdx.x * kImpKeys;     // first key (logical row) of the tile
     const int R = p.T * p.hpk;
     const int nb = p.hd / 32;
-    const uint8_t* const krow =
-        p.k_planes + (int64_t)b * p.k_stride + (int64_t)(row ? j - base : 0) * p.k_row;
-    float acc_p = 0.0f;
-    for (int g = 0; g < p.Hkv; ++g) {
-        for (int r0 = 0; r0 < R; r0 += kImpChunk) {
-            __syncthreads();   // the previous chunk's rows are read
-            for (int e = tid; e < kImpChunk * p.hd; e += 256) {
-                const int rr = e / p.hd, dd = e - rr * p.hd, r = r0 + rr;
-                float x = 0.0f;
-                if (r < R) {
-                    const int t = r / p.hpk, h = g * p.hpk + r % p.hpk;
-                    x = load_in(p.q, p.dtype, (((size_t)b * p.T + t) * p.H + h) * p.hd + dd);
-                }
-                qs[e] = x;
-            }
-            __syncthreads();
-            float dot[kImpChunk / 4];
+    const int nrt = (R + 15) / 16;
+    const int pairs = p.Hkv * nrt;
+    const uint8_t* const plane = p.k_planes + (int64_t)b * p.k_stride;
+    const int ka = k0 + j16;                       // this lane's key in the A operand
+    const bool ka_ok = ka < len;
+    const uint8_t* const krow_a = plane + (int64_t)(ka_ok ? ka - base : 0) * p.k_row;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    int gk = -1;
+    h8 kf[8];
+    float dk[8][4];
+    for (int pi = wave; pi < pairs; pi += 4) {
+        const int g = pi / nrt, rt = pi - g * nrt;
+        if (g != gk) {                             // K fragments and scales of head g
+            gk = g;
 #pragma unroll
-            for (int c = 0; c < kImpChunk / 4; ++c) dot[c] = 0.0f;
-            for (int blk = 0; blk < nb; ++blk) {
-                const uint8_t* kb = krow + (g * nb + blk) * 34;
-                const float d = row ? f16_value(*reinterpret_cast<const uint16_t*>(kb)) : 0.0f;
-                float code[32];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const uint16_t w = row ? *reinterpret_cast<const uint16_t*>(kb + 2 + 2 * i) : 0;
-                    code[2 * i] = (float)(int8_t)(w & 0xFF);
-                    code[2 * i + 1] = (float)(int8_t)(w >> 8);
-                }
-#pragma unroll
-                for (int c = 0; c < kImpChunk / 4; ++c) {
-                    if (r0 + wave + 4 * c < R) {   // the chunk's real rows (wave-uniform)
-                        const float4* qv = reinterpret_cast<const float4*>(qs + (wave + 4 * c) * p.hd + blk * 32);
-                        float s = 0.0f;
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            const float4 x = qv[i];
-                            s = fmaf(x.x, code[4 * i], s);
-                            s = fmaf(x.y, code[4 * i + 1], s);
-                            s = fmaf(x.z, code[4 * i + 2], s);
-                            s = fmaf(x.w, code[4 * i + 3], s);
-                        }
-                        dot[c] = fmaf(d, s, dot[c]);
+            for (int blk = 0; blk < 8; ++blk) {
+                if (blk < nb) {
+                    // the lane's 8 codes start 2 bytes into a word or on one:
+                    // three aligned words hold them
+                    const uint8_t* const kb = krow_a + (g * nb + blk) * 34;
+                    const uintptr_t a = reinterpret_cast<uintptr_t>(kb + 2 + 8 * q4);
+                    const uint32_t* const w = reinterpret_cast<const uint32_t*>(a & ~uintptr_t(3));
+                    uint32_t w0 = 0, w1 = 0, w2 = 0;
+                    if (ka_ok) {
+                        w0 = w[0];
+                        w1 = w[1];
+                        w2 = w[2];
                     }
-                }
-            }
+                    const bool odd = (a & 2) != 0;
+                    const uint32_t c0 = odd ? __builtin_amdgcn_alignbit(w1, w0, 16) : w0;
+                    const uint32_t c1 = odd ? __builtin_amdgcn_alignbit(w2, w1, 16) : w1;
+                    kf[blk] = dec::k_codes_f16(c0, c1);
+                    // the scale of this lane's key, handed to the lanes whose
+                    // D rows are keys 4 q4 + i
+                    const float dself = ka_ok ? f16_value(*reinterpret_cast<const uint16_t*>(kb)) : 0.0f;
 #pragma unroll
-            for (int c = 0; c < kImpChunk / 4; ++c) {
-                const int r = r0 + wave + 4 * c;
-                if (r < R && row) {
-                    const int t = r / p.hpk, h = g * p.hpk + r % p.hpk;
-                    const int upto = len - p.T + t + 1;
-                    const int first = p.window > 0 ? max(0, upto - p.window) : 0;
-                    if (j >= first && j < upto)
-                        acc_p += expf(p.scale * dot[c] - p.lse[((size_t)b * p.T + t) * p.H + h]);
+                    for (int i = 0; i < 4; ++i) dk[blk][i] = __shfl(dself, 4 * q4 + i);
                 }
             }
         }
+        const int r = rt * 16 + j16;               // this lane's query row in the B operand
+        const bool real = r < R;
+        const int t = real ? r / p.hpk : 0, h = g * p.hpk + (real ? r % p.hpk : 0);
+        const size_t qi = (((size_t)b * p.T + t) * p.H + h) * p.hd + 8 * q4;
+        f4 sv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) {
+            if (blk < nb) {
+                float qv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qv[e] = 0.0f;
+                if (real) {
+                    if (p.dtype == 1) {   // 8 bf16 values, 16 bytes
+                        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + qi + blk * 32);
+                        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            qv[2 * e] = __uint_as_float(w4[e] << 16);
+                            qv[2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
+                        }
+                    } else {
+                        const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(p.q) + qi + blk * 32);
+                        const float4 x0 = src[0], x1 = src[1];
+                        qv[0] = x0.x; qv[1] = x0.y; qv[2] = x0.z; qv[3] = x0.w;
+                        qv[4] = x1.x; qv[5] = x1.y; qv[6] = x1.z; qv[7] = x1.w;
+                    }
+                }
+                h8 qh, ql;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    qh[e] = (_Float16)qv[e];
+                    ql[e] = (_Float16)(qv[e] - (float)qh[e]);
+                }
+                f4 d = dec::mfma(kf[blk], qh, (f4){0.f, 0.f, 0.f, 0.f});
+                if (p.dtype == 0) d = dec::mfma(kf[blk], ql, d);   // fp32 queries: the low part too
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sv[i] = fmaf(dk[blk][i], d[i], sv[i]);
+            }
+        }
+        const float l = real ? p.lse[((size_t)b * p.T + t) * p.H + h] : 0.0f;
+        const int upto = len - p.T + t + 1;
+        const int first = p.window > 0 ? max(0, upto - p.window) : 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int key = k0 + 4 * q4 + i;
+            float pr = (real && key >= first && key < upto) ? expf(p.scale * sv[i] - l) : 0.0f;
+            pr += __shfl_xor(pr, 1);
+            pr += __shfl_xor(pr, 2);
+            pr += __shfl_xor(pr, 4);
+            pr += __shfl_xor(pr, 8);
+            acc[i] += pr;
+        }
     }
-    part[wave][lane] = acc_p;
+    if (j16 == 0)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[wave][4 * q4 + i] = acc[i];
     __syncthreads();
-    if (wave == 0 && row) {
-        float* dst = p.imp + (size_t)b * p.capacity + (j - base);
-        *dst += ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+    if (tid < kImpKeys) {
+        const int key = k0 + tid;
+        if (key < len) {
+            float* dst = p.imp + (size_t)b * p.capacity + (key - base);
+            *dst += ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
+        }
     }
 }
 

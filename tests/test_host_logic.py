@@ -292,13 +292,13 @@ def test_graph_mode_plan_and_host_resync(lib):
 
 
 def test_importance_launch(lib):
-    # one launch over the 64-row tiles of the longest span of visible rows
+    # one launch over the 16-row tiles of the longest span of visible rows
     h = create(lib, n_seqs=2, capacity=5000)
     kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 3000, [3000, 1000], 0, lib)
     lib.kvq_nodev_clear()
     kvq.kvq_importance(h, Q, kvq.KVQ_BF16, 2, 0.1, O, O, 0, lib)
     (line,) = log(lib)
-    assert fields(line)["tiles"] == -(-3000 // 64) and fields(line)["T"] == 2
+    assert fields(line)["tiles"] == -(-3000 // 16) and fields(line)["T"] == 2
     lib.kvq_nodev_clear()
     assert err(lib, kvq.kvq_importance, h, Q, kvq.KVQ_BF16, 1001, 0.1, O, O) == kvq.KVQ_EINVAL
     assert err(lib, kvq.kvq_importance, h, Q, kvq.KVQ_BF16, 1, 0.1, O, 0) == kvq.KVQ_EINVAL
@@ -309,7 +309,7 @@ def test_importance_launch(lib):
         kvq.kvq_append(hw, Q, Q, kvq.KVQ_BF16, 40, None, 0, lib)
     lib.kvq_nodev_clear()
     kvq.kvq_importance(hw, Q, kvq.KVQ_BF16, 3, 0.1, O, O, 0, lib)
-    assert fields(log(lib)[0])["tiles"] == -(-(100 + 2) // 64)
+    assert fields(log(lib)[0])["tiles"] == -(-(100 + 2) // 16)
 
 
 def test_decode_query_tile_limits(lib):
