@@ -95,9 +95,8 @@ def parse():
     ap.add_argument("--other-steps", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--graph", choices=("auto", "on", "off"), default="auto",
-                    help="replay each step as one captured HIP graph (auto: where the "
-                         "session lengths are the same at every step, so the captured "
-                         "launch plan stays valid)")
+                    help="replay each step as one captured HIP graph (auto and on: every "
+                         "workload; verify rounds, whose lengths grow, in graph mode)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES, 10 times "
                          "(reference for scaling HBM traffic counters)")
@@ -119,12 +118,17 @@ def calibrate_copy(nbytes: int):
                       "ms": round(dt * 1e3, 4), "GBps_read_plus_write": round(2 * nbytes / dt / 1e9, 1)}))
 
 
-def build_layers(w, L, dev, split_rows, tiling=""):
+def build_layers(w, L, dev, split_rows, tiling="", grow_rows=8 * 1024, graph_mode=False):
     import torch
 
     from decode_attention_quantized_append_amd import KvqLayerCache
-    cap = w.capacity(extra_steps=0) if w.ring_cap else int(w.lengths().max()) + 8 * 1024
+    cap = w.capacity(extra_steps=0) if w.ring_cap else int(w.lengths().max()) + grow_rows
     caches = [KvqLayerCache(w.B, w.H, w.Hkv, w.hd, cap, w.window, w.ring_step, device=dev) for _ in range(L)]
+    if graph_mode:
+        # decode plans for every length the plane allows, so that one
+        # captured round replays while the lengths grow
+        for c in caches:
+            c.set_graph_mode(True)
     tdt = torch.bfloat16 if w.io_dtype == "bf16" else torch.float32
     for counts, starts, T in w.prefill_pieces():
         k, v = w.kv_block(counts, starts, T)
@@ -146,7 +150,14 @@ def run_gpu(w, args):
     import torch
     dev = torch.device("cuda:0")
     L = args.layers or default_layers(w)
-    caches, cap = build_layers(w, L, dev, args.split_rows, args.tiling)
+    # verify rounds keep rollback_keep rows each: the planes are sized to the
+    # rows this run adds (eager and replayed rounds), so that graph-mode plans
+    # cover little more than the real lengths
+    growing = bool(w.rollback_keep)
+    rounds = -(-2 * (args.warmup + args.steps) // L) + 10
+    grow = w.rollback_keep * rounds + w.T + 64 if growing else 8 * 1024
+    caches, cap = build_layers(w, L, dev, args.split_rows, args.tiling, grow_rows=grow,
+                               graph_mode=growing and args.graph != "off")
     tdt = torch.bfloat16 if w.io_dtype == "bf16" else torch.float32
     pre = w.pre_step_lengths()
     k, v = w.kv_block([w.T] * w.B, pre, w.T)
@@ -174,7 +185,7 @@ def run_gpu(w, args):
     pre_arr = (ctypes.c_int32 * B)(*[int(x) for x in pre])
     sink_ptr = sinks.data_ptr() if sinks is not None else None
     kp, vp, qp, op, lp = k_step.data_ptr(), v_step.data_ptr(), q.data_ptr(), out.data_ptr(), lse.data_ptr()
-    lens = [[int(x) for x in pre] for _ in range(L)]
+    drop_arr = (ctypes.c_int32 * B)(*([w.T - w.rollback_keep] * B))
     scale = ctypes.c_float(w.scale)
 
     def check(st, what):
@@ -194,15 +205,13 @@ def run_gpu(w, args):
         if ev is not None:
             ev[2].record()
         if w.rollback_keep:                        # verify: keep rollback_keep of the T rows
-            lens[li] = [x + w.rollback_keep for x in lens[li]]
-            check(lib.kvq_truncate(h, (ctypes.c_int32 * B)(*lens[li]), st), "truncate")
+            check(lib.kvq_rollback(h, drop_arr, st), "rollback")
         else:                                      # steady length: drop the step's rows (a ring
             check(lib.kvq_truncate(h, pre_arr, st), "truncate")   # keeps its window resident)
 
-    steady = not w.rollback_keep
-    if args.graph == "on" and not steady:
-        raise SystemExit(f"--graph on: the {w.name} workload changes session lengths every step")
-    use_graph = args.graph == "on" or (args.graph == "auto" and steady)
+    # steady workloads replay the same lengths; verify rounds grow them, which
+    # graph mode (plans for every length) and the relative rollback allow
+    use_graph = args.graph != "off"
 
     for i in range(args.warmup):
         one_step(i)
@@ -234,6 +243,11 @@ def run_gpu(w, args):
             steps_g[(args.warmup + i) % L].replay()
         torch.cuda.synchronize(dev)
         wall = time.perf_counter() - t0
+        if growing:   # the replays moved the device lengths: bring the host mirrors back in step
+            for c in caches:
+                ln, bs, overflow = c.device_lengths()
+                assert overflow == 0, "a replayed round did not fit its plane"
+                c.set_host_lengths(ln, bs)
     # attention importance of a step's query rows (an optional extra pass:
     # it re-reads the K rows the step sees), timed with HIP events on a few
     # layers after a decode of the same rows supplied the log-sum-exps
@@ -248,8 +262,7 @@ def run_gpu(w, args):
         check(lib.kvq_importance(h, qp, dt, T, scale, lp, imp.data_ptr(), stream), "importance")
         e1.record()
         if w.rollback_keep:
-            lens[li] = [x + w.rollback_keep for x in lens[li]]
-            check(lib.kvq_truncate(h, (ctypes.c_int32 * B)(*lens[li]), stream), "truncate")
+            check(lib.kvq_rollback(h, drop_arr, stream), "rollback")
         else:
             check(lib.kvq_truncate(h, pre_arr, stream), "truncate")
         torch.cuda.synchronize(dev)
@@ -366,7 +379,7 @@ def main():
                    "head_dim": w.hd, "query_rows": w.T, "visible_rows": int(w.visible().sum()),
                    "window": w.window, "ring_rows": w.ring_cap, "layers_rotated": r["L"],
                    "kv_footprint_bytes": r["footprint"], "kv_bytes_per_step": r["kv_bytes"],
-                   "parallelism": "none (1 GPU)", "step_launch": "hip graph" if r["graph"] else "eager"},
+                   "parallelism": "none (1 GPU)", "step_launch": ("hip graph" + (" (graph mode)" if w.rollback_keep else "")) if r["graph"] else "eager"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "steps_per_s": round(1e3 / r["ms_step"], 1),
         "append_tokens_per_s": round(w.B * w.T / (r["app_ms"] * 1e-3), 1),
@@ -404,7 +417,7 @@ def main():
                 "decode_call_frac_hbm_peak": round(ac / HBM_PEAK_GBPS, 4),
                 "decode_call_attn_TFLOPs": round(wo.attn_flops_per_decode() / (ro["dec_ms"] * 1e-3) / 1e12, 3),
                 "kv_bytes_per_step": ro["kv_bytes"], "layers_rotated": ro["L"],
-                "steps": ao.steps, "step_launch": "hip graph" if ro["graph"] else "eager",
+                "steps": ao.steps, "step_launch": ("hip graph" + (" (graph mode)" if wo.rollback_keep else "")) if ro["graph"] else "eager",
                 "traffic": measured_traffic(name)}
             others[name]["importance_call"] = importance_summary(wo, ro)
             if ro["rebase"]:

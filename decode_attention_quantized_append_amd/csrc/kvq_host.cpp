@@ -96,10 +96,13 @@ int32_t* scratch_d(const kvq_cache* h) { return h->counters + 2 * h->cfg.n_seqs;
 
 // Write dst[idx[i]] = val[i], in launches of up to kMaxSetPerLaunch entries.
 kvq_status enqueue_sets(int32_t* dst, const std::vector<int32_t>& idx,
-                        const std::vector<int32_t>& val, void* stream) {
+                        const std::vector<int32_t>& val, void* stream, int add = 0, int B = 0, int window = 0) {
     for (size_t i0 = 0; i0 < idx.size(); i0 += kvq::kMaxSetPerLaunch) {
         kvq::SetParams p{};
         p.dst = dst;
+        p.add = add;
+        p.B = B;
+        p.window = window;
         p.n = (int32_t)std::min<size_t>(kvq::kMaxSetPerLaunch, idx.size() - i0);
         for (int i = 0; i < p.n; ++i) {
             p.idx[i] = idx[i0 + i];
@@ -697,6 +700,29 @@ kvq_status kvq_truncate(kvq_cache* h, const int32_t* new_len, kvq_stream stream)
     kvq_status s = enqueue_sets(h->counters, idx, val, stream);
     if (s != KVQ_OK) return s;
     for (int b = 0; b < c.n_seqs; ++b) h->len[b] = new_len[b];
+    return KVQ_OK;
+}
+
+kvq_status kvq_rollback(kvq_cache* h, const int32_t* drop, kvq_stream stream) {
+    if (!h || !drop) return fail(KVQ_EINVAL, "NULL argument");
+    const kvq_config& c = h->cfg;
+    for (int b = 0; b < c.n_seqs; ++b) {
+        if (drop[b] < 0 || drop[b] > h->len[b])
+            return fail(KVQ_EINVAL, "session " + std::to_string(b) + ": drop must lie in [0, len]");
+        const int64_t nl = h->len[b] - drop[b];
+        if (c.ring_step > 0 && std::max<int64_t>(0, nl - c.window) < h->base[b])
+            return fail(KVQ_ERANGE, "session " + std::to_string(b) +
+                                        ": the ring no longer holds rows the new length would expose");
+    }
+    std::vector<int32_t> idx, val;
+    for (int b = 0; b < c.n_seqs; ++b)
+        if (drop[b] != 0) {
+            idx.push_back(b);
+            val.push_back(-drop[b]);
+        }
+    kvq_status s = enqueue_sets(h->counters, idx, val, stream, 1, c.n_seqs, c.window);
+    if (s != KVQ_OK) return s;
+    for (int b = 0; b < c.n_seqs; ++b) h->len[b] -= drop[b];
     return KVQ_OK;
 }
 

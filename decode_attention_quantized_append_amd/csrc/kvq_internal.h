@@ -44,6 +44,11 @@ struct AppendParams {
 struct SetParams {
     int32_t* dst;
     int32_t n;
+    int32_t add;                // 0: dst[idx] = val.  1: dst[idx] += val for len_d entries
+                                // (idx < B), stopping at the shortest length whose
+                                // window is still resident: base_d + window when
+                                // base_d > 0, else 0
+    int32_t B, window;
     int32_t idx[kMaxSetPerLaunch];
     int32_t val[kMaxSetPerLaunch];
 };

@@ -61,7 +61,15 @@ __device__ __forceinline__ float wave_sum(float v) {
 // ---------------------------------------------------------------------------
 __global__ void set_kernel(SetParams p) {
     int i = threadIdx.x;
-    if (i < p.n) p.dst[p.idx[i]] = p.val[i];
+    if (i >= p.n) return;
+    if (p.add) {
+        const int b = p.idx[i];
+        const int base = p.dst[p.B + b];
+        const int floor = base > 0 ? base + p.window : 0;
+        p.dst[b] = max(p.dst[b] + p.val[i], floor);
+    } else {
+        p.dst[p.idx[i]] = p.val[i];
+    }
 }
 
 // ---------------------------------------------------------------------------

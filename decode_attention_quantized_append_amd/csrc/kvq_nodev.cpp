@@ -29,7 +29,7 @@ int record(const std::string& line, const char** err) {
 namespace kvq {
 
 int launch_set(const SetParams& p, void*, const char** err) {
-    std::string s = "set";
+    std::string s = p.add ? "add" : "set";
     for (int i = 0; i < p.n; ++i) s += " " + std::to_string(p.idx[i]) + "=" + std::to_string(p.val[i]);
     return record(s, err);
 }

@@ -29,7 +29,7 @@ STATUS_NAMES = {0: "KVQ_OK", 1: "KVQ_EINVAL", 2: "KVQ_ECAPACITY", 3: "KVQ_ERANGE
 EXPORTS = ("kvq_required_bytes", "kvq_create", "kvq_append", "kvq_decode_workspace_bytes",
            "kvq_decode", "kvq_truncate", "kvq_set_split_rows", "kvq_set_decode_tiling", "kvq_info",
            "kvq_host_lengths", "kvq_set_graph_mode", "kvq_set_host_lengths", "kvq_importance",
-           "kvq_destroy", "kvq_last_error")
+           "kvq_rollback", "kvq_destroy", "kvq_last_error")
 
 
 class kvq_config(ctypes.Structure):
@@ -71,6 +71,7 @@ def _declare(lib):
         "kvq_decode_workspace_bytes": (st, [vp, i32, ctypes.POINTER(ctypes.c_size_t)]),
         "kvq_decode": (st, [vp, vp, i32, i32, vp, f32, vp, vp, vp, ctypes.c_size_t, vp]),
         "kvq_truncate": (st, [vp, i32p, vp]),
+        "kvq_rollback": (st, [vp, i32p, vp]),
         "kvq_set_split_rows": (st, [vp, i32]),
         "kvq_set_decode_tiling": (st, [vp, i32, i32, i32]),
         "kvq_info": (st, [vp, ctypes.POINTER(kvq_info_t)]),
@@ -219,6 +220,11 @@ def kvq_importance(h: int, q: int, dtype: int, T: int, scale: float, lse: int, i
     _check(lib, lib.kvq_importance(h, q, dtype, T, scale, lse, imp, stream or None))
 
 
+def kvq_rollback(h: int, drop, stream: int = 0, lib=None) -> None:
+    lib = lib or load()
+    _check(lib, lib.kvq_rollback(h, _i32_array(drop), stream or None))
+
+
 def kvq_destroy(h: int, lib=None) -> None:
     (lib or load()).kvq_destroy(h)
 
@@ -304,6 +310,9 @@ class KvqLayerCache:
 
     def truncate(self, new_len):
         kvq_truncate(self.h, new_len, self._stream(), self.lib)
+
+    def rollback(self, drop):
+        kvq_rollback(self.h, drop, self._stream(), self.lib)
 
     def set_split_rows(self, rows):
         kvq_set_split_rows(self.h, rows, self.lib)

@@ -198,6 +198,18 @@ kvq_status kvq_importance(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t 
  * expose rows it no longer holds), EDEVICE. */
 kvq_status kvq_truncate(kvq_cache* h, const int32_t* new_len, kvq_stream stream);
 
+/* Rollback relative to the device length (memra Cache::rollback: drafted
+ * rows not accepted; cortiq LayerKvCache::truncate_last): len_d[b] -= drop[b]
+ * on the device, so that a captured append -> decode -> rollback round
+ * replays from a graph while the lengths grow (see kvq_set_graph_mode).
+ * drop is a HOST array of n_seqs entries in [0, len]; the host mirror moves
+ * by the same amount.  On the device the length never goes below the
+ * shortest one whose window is still resident (base_d + window in a rebased
+ * ring, else 0).  Rows past the new length become dead; base never moves.
+ * Errors: EINVAL, ERANGE (a windowed ring would expose rows it no longer
+ * holds), EDEVICE. */
+kvq_status kvq_rollback(kvq_cache* h, const int32_t* drop, kvq_stream stream);
+
 /* Tuning: rows per split-K chunk of kvq_decode (a positive multiple of 64),
  * or 0 to let each call choose; a call raises it when a session would need
  * more than 1024 chunks.  The result does not depend on it beyond float

@@ -180,3 +180,50 @@ def test_graph_replay_past_the_plane_stops_at_capacity():
     g.set_host_lengths(*g.device_lengths()[:2])
     p.check_mirror()
     p.check_planes()
+
+
+def test_graph_mode_verify_rounds_replay():
+    """A speculative-verify round (append 8 drafted rows, decode them
+    causally, roll back the 5 not accepted) captured once in graph mode and
+    replayed: each replay keeps 3 more rows, and every replay's output is the
+    oracle's."""
+    rng = np.random.default_rng(77)
+    B, H, Hkv, hd, T, keep = 2, 16, 4, 256, 8, 3
+    pre = [300, 177]
+    p = Pair(B, H, Hkv, hd, 420)
+    p.append(bf16_normal(rng, (B, 300, Hkv, hd)), bf16_normal(rng, (B, 300, Hkv, hd)), pre)
+    g = p.gpu
+    g.set_graph_mode(True)
+    scale = hd ** -0.5
+    kd = torch.zeros((B, T, Hkv, hd), dtype=torch.bfloat16, device=DEV)
+    vd, qd = torch.zeros_like(kd), torch.zeros((B, T, H, hd), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((B, T, H, hd), dtype=torch.float32, device=DEV)
+    lse = torch.empty((B, T, H), dtype=torch.float32, device=DEV)
+    g.workspace(T)
+    torch.cuda.synchronize(DEV)
+    graph = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream(DEV)
+    cs.wait_stream(torch.cuda.current_stream(DEV))
+    with torch.cuda.graph(graph, stream=cs):
+        g.append(kd, vd)
+        g.decode(qd, scale, out=out, lse=lse)
+        g.rollback([T - keep] * B)
+    torch.cuda.synchronize(DEV)
+    assert g.device_lengths()[0] == pre
+    for r in range(10):
+        kn, vn = bf16_normal(rng, (B, T, Hkv, hd)), bf16_normal(rng, (B, T, Hkv, hd))
+        q = bf16_normal(rng, (B, T, H, hd))
+        kd.copy_(to_dev(kn, "bf16"))
+        vd.copy_(to_dev(vn, "bf16"))
+        qd.copy_(to_dev(q, "bf16"))
+        graph.replay()
+        torch.cuda.synchronize(DEV)
+        p.ref.append(kn, vn)
+        ref_o, ref_lse = p.ref.attention(q, scale=scale)
+        p.ref.truncate(p.ref.len - (T - keep))
+        assert_close(out.cpu().numpy(), ref_o, f"round {r} out")
+        assert_close(lse.cpu().numpy(), ref_lse, f"round {r} lse")
+        assert g.device_lengths()[0] == p.ref.len.tolist()
+    g.set_host_lengths(*g.device_lengths()[:2])
+    p.check_mirror()
+    p.check_planes()

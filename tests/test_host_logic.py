@@ -312,6 +312,31 @@ def test_importance_launch(lib):
     assert fields(log(lib)[0])["tiles"] == -(-(100 + 2) // 16)
 
 
+def test_rollback_relative(lib):
+    # a rollback enqueues len_d -= drop (relative, so a captured round can be
+    # replayed) and moves the host mirror by the same amount
+    h = create(lib, n_seqs=3, capacity=500)
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 40, [40, 30, 10], 0, lib)
+    lib.kvq_nodev_clear()
+    kvq.kvq_rollback(h, [5, 0, 10], 0, lib)
+    assert log(lib) == ["add 0=-5 2=-10"]
+    assert lengths(lib, h, 3) == ([35, 30, 0], [0, 0, 0])
+    lib.kvq_nodev_clear()
+    assert err(lib, kvq.kvq_rollback, h, [36, 0, 0]) == kvq.KVQ_EINVAL     # past zero
+    assert err(lib, kvq.kvq_rollback, h, [-1, 0, 0]) == kvq.KVQ_EINVAL
+    assert log(lib) == [] and lengths(lib, h, 3) == ([35, 30, 0], [0, 0, 0])
+    # a windowed ring refuses to expose rows it no longer holds
+    hw = create(lib, n_seqs=1, capacity=16, window=8, ring_step=4)
+    for _ in range(30):
+        kvq.kvq_append(hw, Q, Q, kvq.KVQ_F32, 1, None, 0, lib)
+    L, base = lengths(lib, hw, 1)
+    ok = L[0] - 8 - base[0]                       # rows that can go before the window leaves the ring
+    lib.kvq_nodev_clear()
+    assert err(lib, kvq.kvq_rollback, hw, [ok + 1]) == kvq.KVQ_ERANGE
+    kvq.kvq_rollback(hw, [ok], 0, lib)
+    assert lengths(lib, hw, 1)[0] == [L[0] - ok]
+
+
 def test_decode_query_tile_limits(lib):
     h = create(lib, n_seqs=1, n_q_heads=64, n_kv_heads=1, head_dim=256, capacity=100)
     kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 50, None, 0, lib)
