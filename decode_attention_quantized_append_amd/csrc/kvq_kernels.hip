@@ -455,6 +455,75 @@ __global__ __launch_bounds__(256) void importance_kernel(ImportanceParams p) {
     }
 }
 
+// Few splits (at most 16): one wave per (session, row t, Q head h), four per
+// workgroup.  Lane s < ns holds split s's (m, l) and weight e^(m_s - M); lane
+// (sg, dq) sums the 4-float slice dq of o over the splits sg, sg + G, ...
+// (G = 64 / (hd / 4) groups), the weights handed over by shuffles; the group
+// sums meet by shuffles in a fixed order.  The sink enters once, in M and Z.
+constexpr int kCombineWaveSplits = 16;
+__global__ __launch_bounds__(256) void combine_wave_kernel(DecodeParams p) {
+    const int lane = threadIdx.x & 63;
+    const int idx = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (idx >= p.B * p.T * p.H) return;
+    const int h = idx % p.H;
+    const int t = (idx / p.H) % p.T;
+    const int b = idx / (p.H * p.T);
+    const int len = p.len_d[b];
+    const int lo = p.window > 0 ? max(0, len - p.T + 1 - p.window) : 0;
+    const int org = lo & ~31;
+    const int ns = min(p.splits, (len - org + p.chunk - 1) / p.chunk);
+    const size_t stride = (size_t)p.T * p.H;
+    const size_t e0 = ((size_t)b * p.splits * p.T + t) * p.H + h;
+    const int nq = p.hd >> 2, G = 64 / nq;
+    const int dq = lane % nq, sg = lane / nq;
+    // this lane's slices of o, requested before the weights are known
+    float4 v[kCombineWaveSplits];
+#pragma unroll
+    for (int k = 0; k < kCombineWaveSplits; ++k) {
+        const int sp = sg + k * G;
+        v[k] = (k * G < kCombineWaveSplits && sp < ns)
+                   ? *reinterpret_cast<const float4*>(p.part_o + (e0 + sp * stride) * p.hd + 4 * dq)
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float m = -INFINITY, l = 0.0f;
+    if (lane < ns) {
+        const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + 2 * (e0 + lane * stride));
+        m = ml.x;
+        l = ml.y;
+    }
+    const bool has_sink = p.sinks != nullptr;
+    const float sink = has_sink ? p.sinks[h] : 0.0f;
+    float M = wave_max(m);
+    if (has_sink) M = fmaxf(M, sink);
+    const float w = (m == -INFINITY) ? 0.0f : expf(m - M);
+    float Z = wave_sum(w * l);
+    if (has_sink) Z += expf(sink - M);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int k = 0; k < kCombineWaveSplits; ++k) {
+        const int sp = sg + k * G;
+        const float ws = __shfl(w, sp < 64 ? sp : 0);
+        if (k * G < kCombineWaveSplits && sp < ns) {
+            acc.x = fmaf(ws, v[k].x, acc.x);
+            acc.y = fmaf(ws, v[k].y, acc.y);
+            acc.z = fmaf(ws, v[k].z, acc.z);
+            acc.w = fmaf(ws, v[k].w, acc.w);
+        }
+    }
+    for (int off = nq; off < 64; off <<= 1) {   // the G group sums, same dq
+        acc.x += __shfl_xor(acc.x, off);
+        acc.y += __shfl_xor(acc.y, off);
+        acc.z += __shfl_xor(acc.z, off);
+        acc.w += __shfl_xor(acc.w, off);
+    }
+    if (sg == 0) {
+        const float invZ = 1.0f / Z;
+        acc.x *= invZ; acc.y *= invZ; acc.z *= invZ; acc.w *= invZ;
+        reinterpret_cast<float4*>(p.out + (((size_t)b * p.T + t) * p.H + h) * p.hd)[dq] = acc;
+    }
+    if (p.lse && lane == 0) p.lse[((size_t)b * p.T + t) * p.H + h] = M + logf(Z);
+}
+
 // ---------------------------------------------------------------------------
 int check(const char** err) {
     hipError_t e = hipGetLastError();
@@ -466,7 +535,12 @@ int check(const char** err) {
 }
 
 int launch_combine(const DecodeParams& p, hipStream_t st, const char** err) {
-    if (p.splits >= 64)
+    const int items = p.B * p.T * p.H;
+    // a wave per item where the splits are few and a head's 4-float slices
+    // fill the wave in whole groups (head_dim 64, 128 or 256)
+    if (p.splits <= kCombineWaveSplits && (p.hd == 64 || p.hd == 128 || p.hd == 256))
+        hipLaunchKernelGGL(combine_wave_kernel, dim3((items + 3) / 4), dim3(256), 0, st, p);
+    else if (p.splits >= 64)
         hipLaunchKernelGGL(combine_kernel<1024>, dim3(p.B * p.T * p.H), dim3(1024), 0, st, p);
     else
         hipLaunchKernelGGL(combine_kernel<256>, dim3(p.B * p.T * p.H), dim3(256), 0, st, p);
