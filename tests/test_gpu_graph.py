@@ -227,3 +227,30 @@ def test_graph_mode_verify_rounds_replay():
     g.set_host_lengths(*g.device_lengths()[:2])
     p.check_mirror()
     p.check_planes()
+
+
+def test_rollback_replays_stop_at_the_floor():
+    """A captured rollback replayed more often than rows were appended stops
+    at the shortest length whose window is resident: 0 in a flat cache, base
+    + window in a rebased ring.  Only counters change; no rows are read."""
+    rng = np.random.default_rng(9)
+    flat = Pair(2, 8, 2, 64, 64)
+    flat.append(bf16_normal(rng, (2, 12, 2, 64)), bf16_normal(rng, (2, 12, 2, 64)), [12, 7])
+    ring = Pair(1, 8, 2, 64, 48, 16, 16)
+    for _ in range(6):
+        ring.append(bf16_normal(rng, (1, 10, 2, 64)), bf16_normal(rng, (1, 10, 2, 64)))
+    lr, br, _ = ring.gpu.device_lengths()
+    assert br[0] > 0
+    for p, drop in ((flat, [5, 5]), (ring, [4])):
+        graph = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream(DEV)
+        cs.wait_stream(torch.cuda.current_stream(DEV))
+        with torch.cuda.graph(graph, stream=cs):
+            p.gpu.rollback(drop)
+        torch.cuda.synchronize(DEV)
+        for _ in range(8):
+            graph.replay()
+        torch.cuda.synchronize(DEV)
+    assert flat.gpu.device_lengths()[:2] == ([0, 0], [0, 0])
+    ln, bs, _ = ring.gpu.device_lengths()
+    assert bs == br and ln == [br[0] + 16]
