@@ -389,7 +389,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(w.name), "traffic_unit": "bytes per decode call",
                      "algorithmic": r["kv_bytes"],
-                     "kernel": "kvq_decode call (decode_kernel + combine_kernel), HIP events"},
+                     "kernel": "kvq_decode call (split-K partials kernel + LSE combine kernel), HIP events"},
     }
     line["importance_call"] = importance_summary(w, r)
     if r["rebase"]:

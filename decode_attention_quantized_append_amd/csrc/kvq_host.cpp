@@ -654,7 +654,8 @@ kvq_status kvq_importance(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t 
         const int64_t lo = visible_lo(h, h->len[b], T);
         if (lo < h->base[b])
             return fail(KVQ_ERANGE, "session " + std::to_string(b) + ": visible rows were rebased away");
-        maxspan = std::max(maxspan, h->len[b] - lo);
+        // rows of the union (in graph mode, of the largest one the plane allows)
+        maxspan = std::max(maxspan, span_of(h, b, T));
     }
     kvq::ImportanceParams ip{};
     ip.q = q;

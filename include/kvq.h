@@ -184,7 +184,8 @@ kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T,
  * row.  imp: device float [n_seqs, capacity], indexed by physical row (a ring
  * rebase moves K and V rows, not importance).  Call it before the cache
  * changes again.  One launch; the rows of a session are split over
- * workgroups, each adding to its own rows only.
+ * workgroups, each adding to its own rows only; in graph mode the grid
+ * covers every length the plane allows, like kvq_decode's.
  * Errors: EINVAL, ERANGE (a visible row was rebased away), EDEVICE. */
 kvq_status kvq_importance(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, float scale,
                           const float* lse, float* imp, kvq_stream stream);

@@ -77,11 +77,11 @@ def test_step_graph_replays_equal_eager(B, H, Hkv, hd, lens):
                           (2, 16, 4, 64, 64, 128, 32, [200, 170], 20),         # ring: window + T - 1 + 31 rows
                           (1, 16, 4, 256, 0, 500, 0, [300], 12)])
 def test_graph_mode_replays_as_lengths_grow(B, H, Hkv, hd, window, cap, step, pre, steps):
-    """Graph mode: ONE captured step (append a row per session, decode) is
-    replayed `steps` times with no host call between replays, each time on
-    the next row and query written into the captured input buffers; the
-    device lengths grow by one per replay and every replay's output is the
-    oracle's at that length.  Afterwards the host mirror is set from the
+    """Graph mode: ONE captured step (append a row per session, decode, add
+    the attention importance) is replayed `steps` times with no host call
+    between replays, each time on the next row and query written into the
+    captured input buffers; the device lengths grow by one per replay and
+    every replay's output and importance are the oracle's at that length.  Afterwards the host mirror is set from the
     device counters and eager steps continue (through a ring rebase)."""
     rng = np.random.default_rng(hd + cap)
     p = Pair(B, H, Hkv, hd, cap, window, step)
@@ -101,6 +101,7 @@ def test_graph_mode_replays_as_lengths_grow(B, H, Hkv, hd, window, cap, step, pr
     vd, qd = torch.zeros_like(kd), torch.zeros((B, 1, H, hd), dtype=torch.bfloat16, device=DEV)
     out = torch.empty((B, 1, H, hd), dtype=torch.float32, device=DEV)
     lse = torch.empty((B, 1, H), dtype=torch.float32, device=DEV)
+    imp = torch.zeros((B, cap), dtype=torch.float32, device=DEV)
     g.workspace(1)                               # allocated before the capture
     torch.cuda.synchronize(DEV)
     graph = torch.cuda.CUDAGraph()
@@ -109,6 +110,7 @@ def test_graph_mode_replays_as_lengths_grow(B, H, Hkv, hd, window, cap, step, pr
     with torch.cuda.graph(graph, stream=cs):
         g.append(kd, vd)
         g.decode(qd, scale, out=out, lse=lse)
+        g.importance(qd, scale, lse, imp)
     torch.cuda.synchronize(DEV)
     assert g.device_lengths()[0] == pre          # captured, not run
     for r in range(steps):
@@ -118,12 +120,14 @@ def test_graph_mode_replays_as_lengths_grow(B, H, Hkv, hd, window, cap, step, pr
         vd.copy_(to_dev(vn, "bf16"))
         qd.copy_(to_dev(q, "bf16"))
         out.fill_(float("nan"))
+        imp.zero_()
         graph.replay()
         torch.cuda.synchronize(DEV)
         p.ref.append(kn, vn)
         ref_o, ref_lse = p.ref.attention(q, scale=scale)
         assert_close(out.cpu().numpy(), ref_o, f"replay {r} out")
         assert_close(lse.cpu().numpy(), ref_lse, f"replay {r} lse")
+        assert_close(imp.cpu().numpy(), p.ref.importance(q, scale=scale), f"replay {r} importance")
     ln, bs, overflow = g.device_lengths()
     assert ln == p.ref.len.tolist() and bs == p.ref.base.tolist() and overflow == 0
     g.set_host_lengths(ln, bs)
