@@ -49,6 +49,12 @@ def load(path: str | None = None):
         getattr(lib, name).argtypes = [f32p, u8p]
     for name in ("kvqo_q8_0_decode", "kvqo_q5_1_decode"):
         getattr(lib, name).argtypes = [u8p, f64p]
+    lib.kvqo_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.kvqo_e4m3_value.restype = ctypes.c_double
+    lib.kvqo_e4m3_from_f32.argtypes = [ctypes.c_float]
+    lib.kvqo_e4m3_from_f32.restype = ctypes.c_uint8
+    lib.kvqo_f8_encode.argtypes = [f32p, u8p]
+    lib.kvqo_f8_decode.argtypes = [u8p, f64p]
     for name in ("kvqo_quantize_k", "kvqo_quantize_v"):
         getattr(lib, name).argtypes = [f32p, ctypes.c_int64, u8p]
     lib.kvqo_attention.argtypes = [
@@ -113,6 +119,29 @@ def q5_1_encode(x, lib=None):
 
 def q5_1_decode(b, lib=None):
     return _block_op((lib or load()).kvqo_q5_1_decode, b, np.uint8, 24, np.float64, 32)
+
+
+def e4m3_value(codes, lib=None) -> np.ndarray:
+    """Value of each e4m3 code (OCP FP8 E4M3; NaN for S.1111.111), float64."""
+    lib = lib or load()
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib.kvqo_e4m3_value(int(v)) for v in c.ravel()], dtype=np.float64).reshape(c.shape)
+
+
+def e4m3_from_f32(x, lib=None) -> np.ndarray:
+    """Nearest e4m3 code of each float32 (ties to even, saturating at +-448)."""
+    lib = lib or load()
+    a = np.asarray(x, dtype=np.float32)
+    return np.array([lib.kvqo_e4m3_from_f32(float(v)) for v in a.ravel()], dtype=np.uint8).reshape(a.shape)
+
+
+def f8_encode(x, lib=None):
+    """32 float32 values per block -> 34-byte FP8 blocks (fp16 scale + 32 e4m3 codes)."""
+    return _block_op((lib or load()).kvqo_f8_encode, x, np.float32, 32, np.uint8, 34)
+
+
+def f8_decode(b, lib=None):
+    return _block_op((lib or load()).kvqo_f8_decode, b, np.uint8, 34, np.float64, 32)
 
 
 def _quantize(fn, x, blk_bytes):

@@ -16,6 +16,14 @@
  *                          half-even ties; the round-trip error bound.
  *                          Parity with another implementation's bytes is
  *                          unpinned: the pages print no encoded block.
+ *   e4m3 / f8 codec        every code's value against the format's
+ *                          printed landmarks (448, 2^-6, 2^-9, NaN) and
+ *                          monotone order; the rounding of a float to a
+ *                          code against torch's float8_e4m3fn conversion
+ *                          on every quotient within +-448 (ties included);
+ *                          a hand-derived block; the round-trip bound.
+ *                          Parity with another implementation's bytes is
+ *                          unpinned: the pages print no encoded block.
  *   kvqo_importance        per-row probability mass summed over query
  *                          rows and heads: it sums to T*H less the sinks'
  *                          shares (closed form); equals a numpy softmax of
@@ -138,6 +146,64 @@ void kvqo_q8_0_decode(const uint8_t* blk, double* x) {
     double ds = (double)kvqo_f16_to_f32(d16);
     for (int i = 0; i < 32; ++i)
         x[i] = ds * (double)(int8_t)blk[2 + i];
+}
+
+/* ------------------------------------------------------------------ */
+/* e4m3: the 8-bit float of the FP8 K/V variant ("Module cache" index  */
+/* page, item kv_fp8_on).  OCP FP8 E4M3: bit 7 sign, bits 6..3 biased  */
+/* exponent (bias 7), bits 2..0 fraction.  Exponent field 0 holds zero  */
+/* and the subnormals f * 2^-9; S.1111.111 is NaN; there is no          */
+/* infinity, so the largest magnitude is 1.75 * 2^8 = 448.              */
+/* ------------------------------------------------------------------ */
+double kvqo_e4m3_value(uint8_t c) {
+    const int neg = c >> 7, ex = (c >> 3) & 15, fr = c & 7;
+    if (ex == 15 && fr == 7) return NAN;
+    const double mag = (ex == 0) ? ldexp((double)fr, -9)           /* f/8 * 2^(1-7) */
+                                 : ldexp(1.0 + fr / 8.0, ex - 7);
+    return neg ? -mag : mag;
+}
+
+/* The code nearest to x, found by trying every finite magnitude: ties go
+ * to the code with an even fraction (of two neighbours, whose codes differ
+ * by one, the even code), magnitudes past 448 give 0x7E = 448, the nearest
+ * finite code (saturation; the NaN code is never chosen), and the sign bit
+ * is x's, also when the magnitude rounds to zero. */
+uint8_t kvqo_e4m3_from_f32(float x) {
+    assert(!isnan(x));
+    const double a = fabs((double)x);
+    int best = 0;
+    double best_err = a;                 /* code 0: magnitude 0 */
+    for (int c = 1; c < 127; ++c) {      /* the finite positive codes */
+        const double err = fabs(kvqo_e4m3_value((uint8_t)c) - a);
+        if (err < best_err || (err == best_err && (c & 1) == 0)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return (uint8_t)(best | (signbit(x) ? 0x80 : 0));
+}
+
+/* One block: 34 bytes = fp16 scale d (little-endian) + 32 e4m3 codes.   */
+/* d = fp16(amax / 448); codes are e4m3(x / d) from the STORED d (an fp32 */
+/* IEEE quotient rounded once to e4m3); all codes 0 when d is 0.          */
+/* Value = d * e4m3 value.                                              */
+void kvqo_f8_encode(const float* x, uint8_t* blk) {
+    float amax = 0.0f;
+    for (int i = 0; i < 32; ++i) {
+        assert(isfinite(x[i]));
+        if (fabsf(x[i]) > amax) amax = fabsf(x[i]);
+    }
+    const uint16_t d16 = kvqo_f32_to_f16(amax / 448.0f);
+    const float ds = kvqo_f16_to_f32(d16);
+    blk[0] = (uint8_t)(d16 & 0xFF);
+    blk[1] = (uint8_t)(d16 >> 8);
+    for (int i = 0; i < 32; ++i)
+        blk[2 + i] = (ds != 0.0f) ? kvqo_e4m3_from_f32(x[i] / ds) : 0;
+}
+
+void kvqo_f8_decode(const uint8_t* blk, double* x) {
+    const double ds = (double)kvqo_f16_to_f32((uint16_t)(blk[0] | (blk[1] << 8)));
+    for (int i = 0; i < 32; ++i) x[i] = ds * kvqo_e4m3_value(blk[2 + i]);
 }
 
 /* ------------------------------------------------------------------ */

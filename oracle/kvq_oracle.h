@@ -47,6 +47,14 @@ void kvqo_q8_0_decode(const uint8_t* blk, double* x);
 void kvqo_q5_1_encode(const float* x, uint8_t* blk);
 void kvqo_q5_1_decode(const uint8_t* blk, double* x);
 
+/* e4m3 (OCP FP8 E4M3): one code's value (NaN for S.1111.111); the nearest
+ * code to x, ties to even, saturating at +-448, keeping x's sign. */
+double kvqo_e4m3_value(uint8_t c);
+uint8_t kvqo_e4m3_from_f32(float x);
+/* FP8 block, 34 bytes: fp16 scale + 32 e4m3 codes. */
+void kvqo_f8_encode(const float* x, uint8_t* blk);
+void kvqo_f8_decode(const uint8_t* blk, double* x);
+
 /* Encode n_elems (a multiple of 32) consecutive floats as consecutive
  * blocks.  Because head_dim % 32 == 0 and a token row is laid out as
  * [kv_head, dim], this is exactly the byte image of n_elems/(Hkv*hd) rows. */

@@ -97,7 +97,8 @@ def attend(cache, lib, q, scale, sinks=None, sel=None):
 def check_golden_codec(lib):
     """Hand-derived block images (tests/golden)."""
     for name, enc, dec, nbytes in (("q8_0_blocks.txt", core.q8_0_encode, core.q8_0_decode, 34),
-                                   ("q5_1_blocks.txt", core.q5_1_encode, core.q5_1_decode, 24)):
+                                   ("q5_1_blocks.txt", core.q5_1_encode, core.q5_1_decode, 24),
+                                   ("f8_blocks.txt", core.f8_encode, core.f8_decode, 34)):
         x = None
         for line in open(os.path.join(GOLDEN, name)):
             line = line.strip()
@@ -112,6 +113,79 @@ def check_golden_codec(lib):
     x = np.array([c * 0.125 for c in range(-16, 16)], np.float32)
     x[0] = -15.875
     assert np.array_equal(core.q8_0_decode(core.q8_0_encode(x, lib), lib), x.astype(np.float64))
+
+
+def check_e4m3_codes(lib):
+    """Every e4m3 code's value against the format's landmarks (OCP FP8 E4M3:
+    largest 448, smallest normal 2^-6, smallest subnormal 2^-9, NaN only at
+    S.1111.111, no infinity); the 126 positive finite values rise with the
+    code, eight equal steps per binade, and the sign bit only negates."""
+    v = core.e4m3_value(np.arange(256), lib)
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]) and np.isnan(v).sum() == 2
+    land = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x40: 2.0,
+            0x7E: 448.0, 0x77: 240.0, 0xC0: -2.0, 0xFE: -448.0}
+    for c, want in land.items():
+        assert v[c] == want, (hex(c), v[c], want)
+    assert np.signbit(v[0x80]) and v[0x80] == 0.0
+    pos = v[:127]
+    assert np.all(np.diff(pos) > 0)
+    assert np.array_equal(v[128:255], -pos)
+    steps = np.diff(pos)
+    assert np.all(steps[:8] == 2.0 ** -9)                      # subnormals and the first normal step
+    for e in range(1, 15):                                      # binade [2^(e-7), 2^(e-6))
+        assert np.all(steps[8 * e: 8 * e + 8] == 2.0 ** (e - 10)), e
+
+
+def check_e4m3_rounding(lib):
+    """Nearest-code rounding against torch's float8_e4m3fn conversion (round
+    to nearest even), on every code's value, every midpoint between codes
+    (the ties), their float32 neighbours, and log-uniform draws, all within
+    +-448 where torch does not turn values into NaN; past 448 the codes
+    saturate to +-448."""
+    import torch
+    pos = core.e4m3_value(np.arange(127), lib)
+    mids = (pos[:-1] + pos[1:]) / 2
+    m32 = mids.astype(np.float32)
+    rng = np.random.default_rng(11)
+    draws = np.exp2(rng.uniform(-13, np.log2(448.0), 20000)).astype(np.float32)
+    x = np.concatenate([pos.astype(np.float32), m32, np.nextafter(m32, np.float32(0)),
+                        np.nextafter(m32, np.float32(np.inf)), draws])
+    x = x[np.abs(x) <= 448]
+    x = np.concatenate([x, -x])
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(core.e4m3_from_f32(x, lib), want)
+    big = np.array([448.5, 464, 470, 1e6, 3e38], np.float32)
+    assert np.all(core.e4m3_from_f32(big, lib) == 0x7E)
+    assert np.all(core.e4m3_from_f32(-big, lib) == 0xFE)
+
+
+def check_f8_roundtrip(lib):
+    """Round trip of FP8 blocks: each value is within half a code step of the
+    stored-scale quotient (relative 2^-4 in the normal range, 2^-10 * d among
+    the subnormals), plus the stored scale's own shortfall at the saturated
+    maximum; a block of codes times an fp16 scale is reproduced exactly."""
+    rng = np.random.default_rng(12)
+    for dist in ("normal", "outlier", "tiny"):
+        x = rng.standard_normal((64, 32)).astype(np.float32)
+        if dist == "outlier":
+            x[:, 3] *= 40
+        if dist == "tiny":
+            x *= np.float32(1e-5)
+        for blk in x:
+            b = core.f8_encode(blk, lib)
+            d = float(core.f16_to_f32(b[:2].view(np.uint16), lib)[0])
+            y = core.f8_decode(b, lib)
+            amax = float(np.abs(blk).max())
+            bound = np.maximum(2.0 ** -4 * np.abs(blk), 2.0 ** -10 * d) + max(0.0, amax - 448 * d) + 1e-12
+            assert np.all(np.abs(y - blk) <= bound), dist
+    codes = rng.integers(0, 256, 32).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x10
+    codes[0] = 0x7E                                           # the block maximum is 448 * d
+    for d in (1.0, 0.25, 2.0 ** -10, 3.0):
+        x = (d * core.e4m3_value(codes, lib)).astype(np.float32)
+        b = core.f8_encode(x, lib)
+        assert np.array_equal(b[2:], np.where(x == 0, codes & 0x80, codes)), d
+        assert np.array_equal(core.f8_decode(b, lib), x.astype(np.float64)), d
 
 
 def check_f16_sample(lib):
@@ -318,6 +392,9 @@ def check_importance_mass(lib):
 ALL_CHECKS = {
     "golden_codec": check_golden_codec,
     "f16_sample": check_f16_sample,
+    "e4m3_codes": check_e4m3_codes,
+    "e4m3_rounding": check_e4m3_rounding,
+    "f8_roundtrip": check_f8_roundtrip,
     "textbook": check_textbook,
     "textbook_window_sink": lambda lib: check_textbook(lib, window=9, sinks=True, T=4, seed=1),
     "textbook_hd128": lambda lib: check_textbook(lib, B=1, T=1, H=8, Hkv=8, hd=128, N=33, seed=2),
