@@ -336,7 +336,12 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
 // the key is visible to the row, else 0, summed over the 16 rows by
 // shuffles.  The waves' sums meet in LDS and one thread per key adds the
 // total to imp; a key belongs to one workgroup, so no atomics are needed.
+// Workgroups whose 16 keys all lie past the session's length return at once
+// (the grid covers the longest session, or in graph mode the plane).
 constexpr int kImpKeys = 16;
+// NB = head_dim / 32 (1 .. 8) and the query dtype are template arguments, so
+// that no branch separates the loads of a pair from each other.
+template <int NB, bool F32>
 __global__ __launch_bounds__(256) void importance_kernel(ImportanceParams p) {
     using dec::f4;
     using dec::h8;
@@ -347,8 +352,9 @@ __global__ __launch_bounds__(256) void importance_kernel(ImportanceParams p) {
     const int len = p.len_d[b], base = p.base_d[b];
     const int lo = p.window > 0 ? max(0, len - p.T + 1 - p.window) : 0;
     const int k0 = lo + blockIdx.x * kImpKeys;     // first key (logical row) of the tile
+    if (k0 >= len) return;                         // a tile past this session's rows (whole workgroup)
     const int R = p.T * p.hpk;
-    const int nb = p.hd / 32;
+    constexpr int nb = NB;
     const int nrt = (R + 15) / 16;
     const int pairs = p.Hkv * nrt;
     const uint8_t* const plane = p.k_planes + (int64_t)b * p.k_stride;
@@ -361,31 +367,23 @@ __global__ __launch_bounds__(256) void importance_kernel(ImportanceParams p) {
     float dk[8][4];
     for (int pi = wave; pi < pairs; pi += 4) {
         const int g = pi / nrt, rt = pi - g * nrt;
-        if (g != gk) {                             // K fragments and scales of head g
-            gk = g;
+        const bool fresh = g != gk;                // K fragments and scales of head g needed
+        // Every load of the pair is issued before any value is used, so that
+        // they are in flight together: lanes whose key is past the length read
+        // row 0 of the plane, lanes past the R query rows read query row 0,
+        // and both drop what they read.
+        uint32_t kw[8][3];
+        uint16_t ks[8];
+        if (fresh) {
 #pragma unroll
             for (int blk = 0; blk < 8; ++blk) {
                 if (blk < nb) {
                     // the lane's 8 codes start 2 bytes into a word or on one:
-                    // three aligned words hold them
+                    // three aligned words (one 12-byte load) hold them
                     const uint8_t* const kb = krow_a + (g * nb + blk) * 34;
                     const uintptr_t a = reinterpret_cast<uintptr_t>(kb + 2 + 8 * q4);
-                    const uint32_t* const w = reinterpret_cast<const uint32_t*>(a & ~uintptr_t(3));
-                    uint32_t w0 = 0, w1 = 0, w2 = 0;
-                    if (ka_ok) {
-                        w0 = w[0];
-                        w1 = w[1];
-                        w2 = w[2];
-                    }
-                    const bool odd = (a & 2) != 0;
-                    const uint32_t c0 = odd ? __builtin_amdgcn_alignbit(w1, w0, 16) : w0;
-                    const uint32_t c1 = odd ? __builtin_amdgcn_alignbit(w2, w1, 16) : w1;
-                    kf[blk] = dec::k_codes_f16(c0, c1);
-                    // the scale of this lane's key, handed to the lanes whose
-                    // D rows are keys 4 q4 + i
-                    const float dself = ka_ok ? f16_value(*reinterpret_cast<const uint16_t*>(kb)) : 0.0f;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) dk[blk][i] = __shfl(dself, 4 * q4 + i);
+                    __builtin_memcpy(kw[blk], reinterpret_cast<const void*>(a & ~uintptr_t(3)), 12);
+                    ks[blk] = *reinterpret_cast<const uint16_t*>(kb);
                 }
             }
         }
@@ -393,29 +391,61 @@ __global__ __launch_bounds__(256) void importance_kernel(ImportanceParams p) {
         const bool real = r < R;
         const int t = real ? r / p.hpk : 0, h = g * p.hpk + (real ? r % p.hpk : 0);
         const size_t qi = (((size_t)b * p.T + t) * p.H + h) * p.hd + 8 * q4;
+        uint4 qw[8][2];                            // bf16: [blk][0]; fp32: both, as float bits
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) {
+            if (blk < nb) {
+                if constexpr (!F32) {
+                    qw[blk][0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + qi + blk * 32);
+                } else {
+                    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const float*>(p.q) + qi + blk * 32);
+                    qw[blk][0] = src[0];
+                    qw[blk][1] = src[1];
+                }
+            }
+        }
+        const float lraw = p.lse[((size_t)b * p.T + t) * p.H + h];
+        if (fresh) {
+            gk = g;
+#pragma unroll
+            for (int blk = 0; blk < 8; ++blk) {
+                if (blk < nb) {
+                    const uintptr_t a = reinterpret_cast<uintptr_t>(krow_a + (g * nb + blk) * 34 + 2 + 8 * q4);
+                    const uint32_t w0 = ka_ok ? kw[blk][0] : 0u;
+                    const uint32_t w1 = ka_ok ? kw[blk][1] : 0u;
+                    const uint32_t w2 = ka_ok ? kw[blk][2] : 0u;
+                    const bool odd = (a & 2) != 0;
+                    const uint32_t c0 = odd ? __builtin_amdgcn_alignbit(w1, w0, 16) : w0;
+                    const uint32_t c1 = odd ? __builtin_amdgcn_alignbit(w2, w1, 16) : w1;
+                    kf[blk] = dec::k_codes_f16(c0, c1);
+                    // the scale of this lane's key, handed to the lanes whose
+                    // D rows are keys 4 q4 + i
+                    const float dself = ka_ok ? f16_value(ks[blk]) : 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dk[blk][i] = __shfl(dself, 4 * q4 + i);
+                }
+            }
+        }
         f4 sv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int blk = 0; blk < 8; ++blk) {
             if (blk < nb) {
                 float qv[8];
+                if constexpr (!F32) {   // 8 bf16 values, 16 bytes
+                    const uint32_t w4[4] = {qw[blk][0].x, qw[blk][0].y, qw[blk][0].z, qw[blk][0].w};
 #pragma unroll
-                for (int e = 0; e < 8; ++e) qv[e] = 0.0f;
-                if (real) {
-                    if (p.dtype == 1) {   // 8 bf16 values, 16 bytes
-                        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + qi + blk * 32);
-                        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            qv[2 * e] = __uint_as_float(w4[e] << 16);
-                            qv[2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
-                        }
-                    } else {
-                        const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(p.q) + qi + blk * 32);
-                        const float4 x0 = src[0], x1 = src[1];
-                        qv[0] = x0.x; qv[1] = x0.y; qv[2] = x0.z; qv[3] = x0.w;
-                        qv[4] = x1.x; qv[5] = x1.y; qv[6] = x1.z; qv[7] = x1.w;
+                    for (int e = 0; e < 4; ++e) {
+                        qv[2 * e] = __uint_as_float(w4[e] << 16);
+                        qv[2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
                     }
+                } else {
+                    const uint32_t w8[8] = {qw[blk][0].x, qw[blk][0].y, qw[blk][0].z, qw[blk][0].w,
+                                            qw[blk][1].x, qw[blk][1].y, qw[blk][1].z, qw[blk][1].w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) qv[e] = __uint_as_float(w8[e]);
                 }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qv[e] = real ? qv[e] : 0.0f;
                 h8 qh, ql;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -423,12 +453,12 @@ __global__ __launch_bounds__(256) void importance_kernel(ImportanceParams p) {
                     ql[e] = (_Float16)(qv[e] - (float)qh[e]);
                 }
                 f4 d = dec::mfma(kf[blk], qh, (f4){0.f, 0.f, 0.f, 0.f});
-                if (p.dtype == 0) d = dec::mfma(kf[blk], ql, d);   // fp32 queries: the low part too
+                if constexpr (F32) d = dec::mfma(kf[blk], ql, d);   // fp32 queries: the low part too
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sv[i] = fmaf(dk[blk][i], d[i], sv[i]);
             }
         }
-        const float l = real ? p.lse[((size_t)b * p.T + t) * p.H + h] : 0.0f;
+        const float l = real ? lraw : 0.0f;
         const int upto = len - p.T + t + 1;
         const int first = p.window > 0 ? max(0, upto - p.window) : 0;
 #pragma unroll
@@ -708,8 +738,28 @@ int launch_partials(const DecodeParams& p, hipStream_t st, const char** err) {
 }
 }  // namespace
 
+template <bool F32>
+bool launch_importance_dtype(const ImportanceParams& p, hipStream_t st) {
+    const dim3 grid(p.tiles, p.B), block(256);
+    switch (p.hd / 32) {
+        case 1: hipLaunchKernelGGL((importance_kernel<1, F32>), grid, block, 0, st, p); return true;
+        case 2: hipLaunchKernelGGL((importance_kernel<2, F32>), grid, block, 0, st, p); return true;
+        case 3: hipLaunchKernelGGL((importance_kernel<3, F32>), grid, block, 0, st, p); return true;
+        case 4: hipLaunchKernelGGL((importance_kernel<4, F32>), grid, block, 0, st, p); return true;
+        case 5: hipLaunchKernelGGL((importance_kernel<5, F32>), grid, block, 0, st, p); return true;
+        case 6: hipLaunchKernelGGL((importance_kernel<6, F32>), grid, block, 0, st, p); return true;
+        case 7: hipLaunchKernelGGL((importance_kernel<7, F32>), grid, block, 0, st, p); return true;
+        case 8: hipLaunchKernelGGL((importance_kernel<8, F32>), grid, block, 0, st, p); return true;
+        default: return false;
+    }
+}
+
 int launch_importance(const ImportanceParams& p, void* stream, const char** err) {
-    hipLaunchKernelGGL(importance_kernel, dim3(p.tiles, p.B), dim3(256), 0, (hipStream_t)stream, p);
+    if (p.hd % 32 != 0 || !(p.dtype == 0 ? launch_importance_dtype<true>(p, (hipStream_t)stream)
+                                         : launch_importance_dtype<false>(p, (hipStream_t)stream))) {
+        *err = "importance: head_dim must be 32 .. 256 in steps of 32";
+        return 1;
+    }
     return check(err);
 }
 
