@@ -327,8 +327,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
 // Attention importance (cortiq-engine "Struct LayerKvCache": attend_group's
 // imp_acc, accumulate_imp).  Workgroup (tile, session) takes 16 rows (keys)
 // of the session's visible union; its four waves share the (KV head, 16-row
-// tile of query rows) pairs.  Per pair, the scores of the 16 keys against the
-// 16 query rows are S^T = K Q^T on v_mfma_f32_16x16x32_f16, one per 32-dim
+// tile of query rows) pairs, each a contiguous run of them.  Per pair, the
+// scores of the 16 keys against the 16 query rows are S^T = K Q^T on
+// v_mfma_f32_16x16x32_f16, one per 32-dim
 // block (the K codes exact in fp16, converted once per head; bf16 queries
 // exact in fp16, fp32 queries as an fp16 high and low part), each block's
 // product scaled by its keys' q8_0 scales.  Lane (q4, j16) then holds keys
@@ -365,7 +366,11 @@ __global__ __launch_bounds__(256) void importance_kernel(ImportanceParams p) {
     int gk = -1;
     h8 kf[8];
     float dk[8][4];
-    for (int pi = wave; pi < pairs; pi += 4) {
+    // wave w takes a contiguous run of pairs, so that the row tiles of one
+    // head follow each other and its K fragments are loaded once
+    const int ppw = (pairs + 3) / 4;
+    const int pend = min(pairs, (wave + 1) * ppw);
+    for (int pi = wave * ppw; pi < pend; ++pi) {
         const int g = pi / nrt, rt = pi - g * nrt;
         const bool fresh = g != gk;                // K fragments and scales of head g needed
         // Every load of the pair is issued before any value is used, so that
