@@ -85,7 +85,7 @@ def parse():
     ap.add_argument("--layers", type=int, default=0)
     ap.add_argument("--split-rows", type=int, default=0)
     ap.add_argument("--tiling", default="", metavar="KERNEL,HEAD_GROUP[,SUB]",
-                    help="decode kernel (1 per-head, 2 whole-row, 3 stream), KV heads per "
+                    help="decode kernel (1 per-head, 3 stream), KV heads per "
                          "workgroup and sub_tiles, as kvq_set_decode_tiling; default: the "
                          "library's choice")
     ap.add_argument("--no-cpu-baseline", action="store_true")

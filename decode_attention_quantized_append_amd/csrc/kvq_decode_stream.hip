@@ -1,6 +1,6 @@
 // kvq_decode_stream.hip -- split-K flash decode, each wave streaming one KV
 // head's row windows through LDS (gfx950).  Included by kvq_kernels.hip
-// (inside namespace kvq), after kvq_decode_rows.hip.
+// (inside namespace kvq), after kvq_decode.hip.
 //
 // The same partials as the other decode kernels (cortiq-engine "Struct
 // LayerKvCache", attend_group and attend_group_upto; memra-engine "Struct
@@ -42,10 +42,33 @@ using dec::i2;
 using dec::kLn2;
 using dec::kLog2e;
 using dec::lds_i2;
-using rows::dma16;
-using rows::pkey;
 
-constexpr int kTile = 32;
+constexpr int kTile = kRowTile;
+
+// Barrier for LDS hand-offs between the waves of a workgroup.  It waits for
+// this wave's LDS operations only: the tile loads in flight into the other
+// buffer are global->LDS transfers counted by vmcnt, which a fenced
+// __syncthreads() would drain.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt untouched
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// One 16-byte piece per lane, from base + off to LDS address lds + 16 * lane
+// (global_load_lds_dwordx4, scalar base form).  Written as asm because the
+// compiler's wait-count pass, unable to tell these LDS writes from the LDS
+// reads of the other buffer, would otherwise wait for them before every such
+// read; the kernel waits for them itself with explicit vmcnt counts.
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint8_t* lds) {
+    const uint32_t l = (uint32_t)(uintptr_t)(lds_u8*)lds;
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(l) : "memory");
+}
+
+// Key of slot k (0..7) of lane group q4 in the P V operands.
+__device__ __forceinline__ int pkey(int q4, int k) { return (k < 4) ? 4 * q4 + k : 16 + 4 * q4 + (k - 4); }
 
 template <int NB>
 using Win = StreamWin<NB>;
@@ -329,7 +352,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
                 KSa[blk * kTile + key] = (t0 + key < c1) ? f16_value(kd) * sc2 : 0.0f;
             }
         }
-        if constexpr (SH) rows::lds_barrier(); else dec::lds_order();
+        if constexpr (SH) lds_barrier(); else dec::lds_order();
 
         // ---- scores S^T: sv[rt][h][i] = S[row rt*16 + j16][key 16h + 4*q4 + i] (base 2)
 #pragma unroll
@@ -380,7 +403,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
         // tile together lets those lines be fetched from HBM once (and keeps
         // the row streams of a CU in step).
         if constexpr (SH) {
-            rows::lds_barrier();                          // both copies of K(t) are read
+            lds_barrier();                          // both copies of K(t) are read
             if (has2) issue_k(tn + kTile, tb);
         } else if constexpr (DS == 2) {
             // the two halves' partial sums: each wave adds the other's to its
@@ -393,7 +416,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
                     xo[(rt * 2 + h) * 64 + lane] = (f4){sv[rt][h][0], sv[rt][h][1], sv[rt][h][2], sv[rt][h][3]};
-            rows::lds_barrier();
+            lds_barrier();
             if (next) issue_k(tn, tb);
 #pragma unroll
             for (int rt = 0; rt < RTW; ++rt)
@@ -478,7 +501,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
                 VMa[key * WN::VMS + blk] = live ? (uint16_t)(dm >> 16) : (uint16_t)0;
             }
         }
-        if constexpr (SH) rows::lds_barrier(); else dec::lds_order();
+        if constexpr (SH) lds_barrier(); else dec::lds_order();
 
         // ---- P V with the V codes built from the q5_1 bytes of 8 keys per lane group
 #pragma unroll
@@ -528,7 +551,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
             }
         }
         if constexpr (SH) {
-            rows::lds_barrier();                          // both copies of V(t) are read
+            lds_barrier();                          // both copies of V(t) are read
             if (has2) issue_v(tn + kTile, tb);
         } else {
             if (next) issue_v(tn, tb);
@@ -558,7 +581,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
     if constexpr (RS > 1) {
         constexpr int MOFS = RTW * 2 * NB * 4 * 64;      // floats before m, l
         static_assert((MOFS + 64 * RTW) * 4 <= WSTR, "row-stream hand-off does not fit the wave buffer");
-        if constexpr (DS == 2) rows::lds_barrier();
+        if constexpr (DS == 2) lds_barrier();
         __builtin_amdgcn_s_waitcnt(0xC07F);              // this wave's reads of its buffer are done
         float* const xb = reinterpret_cast<float*>(wb);
         if (str > 0) {
@@ -574,7 +597,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
                 }
             }
         }
-        rows::lds_barrier();
+        lds_barrier();
         if (str == 0) {
             for (int o = 1; o < rs; ++o) {
                 const float* const yb = reinterpret_cast<const float*>(smem + (wave + o * gh * DS) * WSTR);

@@ -34,8 +34,9 @@ struct kvq_cache {
     int32_t split_rows;
     int32_t decode_kernel;       // kvq_decode_kernel (KVQ_DECODE_AUTO: chosen per call)
     int32_t head_group;          // KV heads per workgroup (0: chosen per call)
-    int32_t sub_tiles;           // whole-row kernel: rows per buffer / 32 (0: chosen per call)
+    int32_t sub_tiles;           // stream kernel: waves per KV head (0: chosen per call)
     int32_t graph_mode;          // plan decodes for every session's largest span
+    int32_t cus;                 // compute units of the device the handle was created on
 };
 
 namespace {
@@ -125,35 +126,15 @@ struct Plan {
     int32_t chunk;
     int32_t splits;
     int32_t units;     // (session, chunk) pairs with rows
-    int32_t gh;        // KV heads per workgroup (whole-row and stream kernels)
-    int32_t sub;       // whole-row kernel: rows per buffer / 32
+    int32_t gh;        // KV heads per workgroup (stream kernel)
     int32_t rs;        // stream kernel: row streams (waves per KV head)
     int32_t rg;        // stream kernel: row groups of 16 query rows (waves per KV head)
     int32_t ds;        // stream kernel: 2 = two waves per KV head, each half of its dims
     int32_t lds;       // dynamic LDS bytes
     int32_t rows;      // rows per buffer (chunks are a multiple)
-    kvq::RowGeo geo;
     size_t ml_bytes;
     size_t o_bytes;
 };
-
-// Is the whole-row kernel built for gh heads per workgroup and buffers of
-// 32*sub rows at this shape?  (gh divides Hkv; the group's K row segment is a
-// whole number of 16-byte pieces; at most 8 waves; the loads of a buffer fit
-// the kernel's per-wave slots; two buffers and the head areas fit in LDS.)
-bool rows_ok(const kvq_config& c, int R, int gh, int sub, kvq::RowGeo* geo) {
-    const int NB = c.head_dim / 32;
-    if (NB != 2 && NB != 4 && NB != 8) return false;
-    if (gh < 1 || c.n_kv_heads % gh != 0 || (gh * NB) % 8 != 0) return false;
-    if (sub != 1 && sub != 2 && sub != 4) return false;
-    const int RT = (R + 15) / 16;
-    const int nw = gh * RT;
-    if (nw > 8) return false;
-    kvq::RowGeo g = kvq::row_geo(gh, NB, sub);
-    if ((g.NKI + g.NVI + nw - 1) / nw > kvq::kRowMaxSlots || g.lds > kvq::kLdsBytes) return false;
-    if (geo) *geo = g;
-    return true;
-}
 
 // Is the per-wave stream kernel built for gh heads (one wave each) at this shape?
 bool stream_ok(const kvq_config& c, int R, int gh) {
@@ -230,83 +211,58 @@ int64_t span_of(const kvq_cache* h, int b, int32_t T) {
 bool choose_kernel(const kvq_cache* h, int R, int32_t T, bool f32_queries, Plan* p) {
     const kvq_config& c = h->cfg;
     const int NB = c.head_dim / 32;
-    const int RT = (R + 15) / 16;
     p->kernel = kvq::kPerHead;
     p->gh = 0;
-    p->sub = 0;
     p->lds = 0;
     p->rows = 256;
     int want = h->decode_kernel;
     if (want == KVQ_DECODE_AUTO) want = (NB == 2 || NB == 4 || NB == 8) ? KVQ_DECODE_STREAM : KVQ_DECODE_PER_HEAD;
     if (want == KVQ_DECODE_PER_HEAD) return true;
-    // The whole-row and stream kernels start a session's first buffer at the
-    // first visible row rounded down to 32 and read it whole, so that row
-    // must still be resident (at or above base); else one KV head per
-    // workgroup, whose loads clamp rows to the visible range.
+    // The stream kernel starts a session's first tile at the first visible
+    // row rounded down to 32 and reads it whole, so that row must still be
+    // resident (at or above base); else one KV head per workgroup, whose
+    // loads clamp rows to the visible range.
     if (!aligned_start_resident(h, T)) return true;
-    if (want == KVQ_DECODE_STREAM) {
-        // 128- and 256-dim heads with 17..32 query rows: two waves per head,
-        // each half of the dims (no unpacking done twice), in independent
-        // workgroups of one head unless a head group is set
-        const bool ds = h->sub_tiles == 3 || (h->sub_tiles == 0 && stream_ds_ok(c, R, 1));
-        int gh = h->head_group;
-        if (gh == 0 && ds) gh = 1;
-        if (gh == 0)
-            // the largest head group: the waves of one workgroup share the
-            // cache lines at the edges of adjacent head slices
-            for (int k = std::min(c.n_kv_heads, 8); k >= 1 && gh == 0; --k)
-                if (stream_ok(c, R, k)) gh = k;
-        if (!stream_ok(c, R, gh)) return h->decode_kernel == KVQ_DECODE_AUTO;
-        p->kernel = kvq::kStream;
-        p->gh = gh;
-        p->ds = 1;
-        p->rs = 1;
-        p->rg = 1;
-        p->lds = gh * kvq::stream_wave_bytes(NB);
-        p->rows = kvq::stream_rows_per_buffer(NB);
-        if (ds) {
-            // two waves per KV head, each half of a 128- or 256-dim head's
-            // dims for all 17..32 query rows; row streams chosen with the chunk
-            if (!stream_ds_ok(c, R, gh)) return false;
-            p->ds = 2;
-            p->rs = 0;
-            p->lds = gh * 2 * kvq::stream_ds_wave_bytes(c.head_dim);
-            return true;
-        }
-        // sub_tiles = waves per KV head: row streams for R <= 16 query rows,
-        // row groups above
-        p->rs = R <= 16 ? h->sub_tiles : 1;         // 0: chosen with the chunk
-        p->rg = R > 16 ? (h->sub_tiles == 1 ? 1 : stream_rg2_ok(c, R, gh, f32_queries) ? 2 : 0) : 1;
-        if (p->rg == 0) {
-            if (h->sub_tiles == 2) return false;
-            p->rg = 1;
-        }
-        if (p->rs == 2 && !stream_rs2_ok(c, R, gh)) return false;
-        p->lds = gh * std::max(1, p->rs) * p->rg * kvq::stream_wave_bytes(NB);
-        p->rows = kvq::stream_rows_per_buffer(NB);
+    // 128- and 256-dim heads with 17..32 query rows: two waves per head,
+    // each half of the dims (no unpacking done twice), in independent
+    // workgroups of one head unless a head group is set
+    const bool ds = h->sub_tiles == 3 || (h->sub_tiles == 0 && stream_ds_ok(c, R, 1));
+    int gh = h->head_group;
+    if (gh == 0 && ds) gh = 1;
+    if (gh == 0)
+        // the largest head group: the waves of one workgroup share the
+        // cache lines at the edges of adjacent head slices
+        for (int k = std::min(c.n_kv_heads, 8); k >= 1 && gh == 0; --k)
+            if (stream_ok(c, R, k)) gh = k;
+    if (!stream_ok(c, R, gh)) return h->decode_kernel == KVQ_DECODE_AUTO;
+    p->kernel = kvq::kStream;
+    p->gh = gh;
+    p->ds = 1;
+    p->rs = 1;
+    p->rg = 1;
+    p->lds = gh * kvq::stream_wave_bytes(NB);
+    p->rows = kvq::stream_rows_per_buffer(NB);
+    if (ds) {
+        // two waves per KV head, each half of a 128- or 256-dim head's
+        // dims for all 17..32 query rows; row streams chosen with the chunk
+        if (!stream_ds_ok(c, R, gh)) return false;
+        p->ds = 2;
+        p->rs = 0;
+        p->lds = gh * 2 * kvq::stream_ds_wave_bytes(c.head_dim);
         return true;
     }
-    // whole-row: the largest head group whose buffers carry >= 48 KB (the
-    // load in flight per workgroup while the other buffer is computed)
-    const int gh0 = h->head_group, sub0 = h->sub_tiles;
-    for (int gh = gh0 ? gh0 : std::min(c.n_kv_heads, 8); gh >= 1; --gh) {
-        for (int sub : {1, 2, 4}) {
-            kvq::RowGeo g;
-            if (sub0 > 0 && sub != sub0) continue;
-            if (!rows_ok(c, R, gh, sub, &g)) continue;
-            if (sub0 == 0 && g.RAWB < 48 * 1024 && sub < 4 && rows_ok(c, R, gh, sub * 2, nullptr)) continue;
-            p->kernel = kvq::kWholeRow;
-            p->gh = gh;
-            p->sub = sub;
-            p->geo = g;
-            p->lds = g.lds;
-            p->rows = g.TRB;
-            return true;
-        }
-        if (gh0) break;
+    // sub_tiles = waves per KV head: row streams for R <= 16 query rows,
+    // row groups above
+    p->rs = R <= 16 ? h->sub_tiles : 1;         // 0: chosen with the chunk
+    p->rg = R > 16 ? (h->sub_tiles == 1 ? 1 : stream_rg2_ok(c, R, gh, f32_queries) ? 2 : 0) : 1;
+    if (p->rg == 0) {
+        if (h->sub_tiles == 2) return false;
+        p->rg = 1;
     }
-    (void)RT;
-    return false;
+    if (p->rs == 2 && !stream_rs2_ok(c, R, gh)) return false;
+    p->lds = gh * std::max(1, p->rs) * p->rg * kvq::stream_wave_bytes(NB);
+    p->rows = kvq::stream_rows_per_buffer(NB);
+    return true;
 }
 
 Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nullptr) {
@@ -329,21 +285,20 @@ Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nul
     if (p.kernel != kvq::kPerHead) {
         const int64_t ngrp = c.n_kv_heads / p.gh;
         const int RT = (R + 15) / 16;
-        // one round of workgroups: as many as fit on the 256 CUs at once
+        // one round of workgroups: as many as fit on the device's CUs at once
         // (bound by LDS and by the waves the register file holds), each a
         // whole number of buffers
         auto one_round = [&](int rs) {
-            const bool ds = p.kernel == kvq::kStream && p.ds == 2;
-            const int64_t waves_per_wg = p.kernel == kvq::kStream ? p.gh * rs * p.rg * p.ds : p.gh * RT;
+            const bool ds = p.ds == 2;
+            const int64_t waves_per_wg = p.gh * rs * p.rg * p.ds;
             const int rtw = p.rg == 2 ? 1 : RT;   // row tiles per wave
-            const int64_t waves_per_cu =
-                ds ? 4 * kvq::stream_ds_waves_per_simd(c.head_dim / 64) : p.kernel == kvq::kStream ? 4 * kvq::stream_waves_per_simd(c.head_dim / 32, rtw, f32_queries) : 8;
+            const int64_t waves_per_cu = ds ? 4 * kvq::stream_ds_waves_per_simd(c.head_dim / 64)
+                                            : 4 * kvq::stream_waves_per_simd(c.head_dim / 32, rtw, f32_queries);
             const int64_t lds = ds ? p.gh * rs * 2 * kvq::stream_ds_wave_bytes(c.head_dim)
-                                   : p.kernel == kvq::kStream ? p.gh * rs * p.rg * kvq::stream_wave_bytes(c.head_dim / 32)
-                                                              : p.lds;
+                                   : p.gh * rs * p.rg * kvq::stream_wave_bytes(c.head_dim / 32);
             const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kvq::kLdsBytes / lds,
                                                                            waves_per_cu / waves_per_wg));
-            const int64_t slots = 256 * per_cu;
+            const int64_t slots = (int64_t)h->cus * per_cu;
             int64_t ch = round_up(std::max<int64_t>(1, ceil_div(total * ngrp * groups, slots)), p.rows);
             for (;;) {
                 int64_t wgs = 0;
@@ -353,7 +308,7 @@ Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nul
             }
             return ch;
         };
-        if (p.kernel == kvq::kStream) {
+        {
             // two row streams per head when each still gets a few tiles of
             // its chunk: the waves of a CU then advance together, and there
             // are half as many partials to combine
@@ -364,12 +319,12 @@ Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nul
                               : p.gh * p.rs * p.rg * kvq::stream_wave_bytes(c.head_dim / 32);
         }
         if (chunk <= 0) {
-            chunk = one_round(p.kernel == kvq::kStream ? p.rs : 1);
+            chunk = one_round(p.rs);
             // a chunk of one tile leaves each wave a single load-then-compute
             // pass: with half the heads per workgroup, as many workgroups take
             // two tiles each (the second in flight while the first is
             // computed) and write half as many partials
-            if (p.kernel == kvq::kStream && h->head_group == 0 && p.rs == 1 && p.rg == 1 && p.ds == 1 &&
+            if (h->head_group == 0 && p.rs == 1 && p.rg == 1 && p.ds == 1 &&
                 p.gh % 2 == 0 && chunk <= p.rows) {
                 p.gh /= 2;
                 p.lds = p.gh * kvq::stream_wave_bytes(c.head_dim / 32);
@@ -434,6 +389,12 @@ kvq_status kvq_create(const kvq_config* cfg, void* k_planes, void* v_planes,
     h->head_group = 0;
     h->sub_tiles = 0;
     h->graph_mode = 0;
+    // the split plan sizes one round of workgroups to the device's CUs
+    h->cus = kvq::device_compute_units();
+    if (h->cus <= 0) {
+        delete h;
+        return fail(KVQ_EDEVICE, "cannot read the compute-unit count of the current device");
+    }
     int n = 2 * cfg->n_seqs + 4;
     std::vector<int32_t> idx(n), val(n, 0);
     for (int i = 0; i < n; ++i) idx[i] = i;
@@ -619,12 +580,10 @@ kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, c
     dp.units = p.units;
     dp.kernel = p.kernel;
     dp.gh = p.gh;
-    dp.sub = p.sub;
     dp.rs = p.rs;
     dp.rg = p.rg;
     dp.ds = p.kernel == kvq::kStream ? p.ds : 1;
     dp.lds = p.lds;
-    dp.geo = p.geo;
     dp.scale = scale;
     dp.part_ml = static_cast<float*>(ws);
     dp.part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + p.ml_bytes);
@@ -737,14 +696,14 @@ kvq_status kvq_set_split_rows(kvq_cache* h, int32_t rows) {
 
 kvq_status kvq_set_decode_tiling(kvq_cache* h, int32_t kernel, int32_t head_group, int32_t sub_tiles) {
     if (!h) return fail(KVQ_EINVAL, "handle is NULL");
-    if (kernel < KVQ_DECODE_AUTO || kernel > KVQ_DECODE_STREAM) return fail(KVQ_EINVAL, "unknown decode kernel");
+    if (kernel != KVQ_DECODE_AUTO && kernel != KVQ_DECODE_PER_HEAD && kernel != KVQ_DECODE_STREAM)
+        return fail(KVQ_EINVAL, "unknown decode kernel");
     if (head_group < 0 || (head_group > 0 && h->cfg.n_kv_heads % head_group != 0))
         return fail(KVQ_EINVAL, "head_group must be 0 or a divisor of n_kv_heads");
-    if (head_group > 0 && kernel != KVQ_DECODE_WHOLE_ROW && kernel != KVQ_DECODE_STREAM)
-        return fail(KVQ_EINVAL, "head_group applies to the whole-row and stream kernels");
-    if (sub_tiles != 0 && !(kernel == KVQ_DECODE_WHOLE_ROW && (sub_tiles == 1 || sub_tiles == 2 || sub_tiles == 4)) &&
-        !(kernel == KVQ_DECODE_STREAM && (sub_tiles >= 1 && sub_tiles <= 3)))
-        return fail(KVQ_EINVAL, "sub_tiles must be 0, or 1, 2 or 4 for the whole-row kernel, 1, 2 or 3 for the stream kernel");
+    if (head_group > 0 && kernel != KVQ_DECODE_STREAM)
+        return fail(KVQ_EINVAL, "head_group applies to the stream kernel");
+    if (sub_tiles != 0 && !(kernel == KVQ_DECODE_STREAM && sub_tiles >= 1 && sub_tiles <= 3))
+        return fail(KVQ_EINVAL, "sub_tiles must be 0, or 1, 2 or 3 for the stream kernel");
     h->decode_kernel = kernel;
     h->head_group = head_group;
     h->sub_tiles = sub_tiles;

@@ -86,49 +86,8 @@ struct ImportanceParams {
     int32_t tiles;              // 16-row tiles per session in the grid
 };
 
-// Geometry of the whole-row decode kernel (one workgroup per session, chunk
-// and group of gh KV heads; buffers of 32*sub rows).  Byte counts are per
-// row segment of the group.
-struct RowGeo {
-    int32_t SK, SV;      // K / V bytes of the group per row
-    int32_t KC, KCP;     // 16-byte pieces of a K row segment; LDS count, made odd
-    int32_t VC, VCP;     // 16-byte pieces of a V row segment; LDS count, made odd
-    int32_t KSTR;        // LDS K row stride (KCP * 16)
-    int32_t VSTR;        // LDS V row stride (VCP * 16)
-    int32_t TRB;         // rows per buffer
-    int32_t NKI, NVI;    // wave-wide 16-byte-per-lane load instructions per buffer
-    int32_t RAWB;        // bytes per buffer (K rows, then V rows)
-    int32_t HB;          // bytes per KV-head area
-    int32_t lds;         // dynamic LDS bytes: two buffers and gh head areas
-    uint32_t kmagic;     // ceil(2^32 / KCP): n / KCP == umulhi(n, kmagic) for the n used
-    uint32_t vmagic;     // ceil(2^32 / VCP)
-};
-
-constexpr int kRowTile = 32;          // rows per tile of the whole-row kernel
-constexpr int kRowMaxSlots = 16;      // load instructions per wave and buffer it is built for
+constexpr int kRowTile = 32;          // rows per tile of the stream kernel
 constexpr int kLdsBytes = 160 * 1024;
-
-inline RowGeo row_geo(int gh, int NB, int sub) {
-    RowGeo g{};
-    g.SK = gh * NB * 34;
-    g.SV = gh * NB * 24;
-    g.KC = g.SK / 16;
-    g.KCP = g.KC | 1;
-    g.VC = g.SV / 16;
-    g.VCP = g.VC | 1;
-    g.KSTR = g.KCP * 16;
-    g.VSTR = g.VCP * 16;
-    g.TRB = kRowTile * sub;
-    g.NKI = (g.TRB * g.KCP + 63) / 64;
-    g.NVI = (g.TRB * g.VCP + 63) / 64;
-    g.RAWB = g.TRB * g.KSTR + g.TRB * g.VSTR;
-    g.HB = NB * (1024 + 128 + 128) + 64 * (NB < 4 ? 4 : NB);
-    g.lds = 2 * g.RAWB + gh * g.HB;
-    // exact for n < 2^32 / d, far above the piece counts of a buffer
-    g.kmagic = (uint32_t)(((1ull << 32) + g.KCP - 1) / g.KCP);
-    g.vmagic = (uint32_t)(((1ull << 32) + g.VCP - 1) / g.VCP);
-    return g;
-}
 
 // Geometry of the per-wave stream decode kernel for head_dim = 32 * NB (NB
 // even): each wave copies its KV head's row windows of a 32-row tile, in
@@ -182,7 +141,7 @@ constexpr int stream_waves_per_simd(int NB, int RTW, bool QLO) {
 // head: 3 for 128-dim heads (64-dim halves), 2 for 256-dim heads.
 constexpr int stream_ds_waves_per_simd(int NB_half) { return NB_half <= 2 ? 3 : 2; }
 
-enum DecodeKernel : int32_t { kPerHead = 0, kWholeRow = 1, kStream = 2 };
+enum DecodeKernel : int32_t { kPerHead = 0, kStream = 2 };
 
 // Split-K decode plus the log-sum-exp combine.
 struct DecodeParams {
@@ -204,8 +163,7 @@ struct DecodeParams {
     int32_t splits;             // split slots per session
     int32_t units;              // (session, chunk) pairs with rows, over all sessions
     int32_t kernel;             // DecodeKernel
-    int32_t gh;                 // KV heads per workgroup (whole-row and stream kernels)
-    int32_t sub;                // whole-row kernel: rows per buffer / 32
+    int32_t gh;                 // KV heads per workgroup (stream kernel)
     int32_t rs;                 // stream kernel: waves per KV head in a workgroup, each
                                 // taking every rs-th tile of the chunk (1 or 2)
     int32_t rg;                 // stream kernel: waves per KV head in a workgroup, each
@@ -213,7 +171,6 @@ struct DecodeParams {
     int32_t ds;                 // stream kernel: 2 = two waves per KV head, each taking half
                                 // of its dims for all query rows (head_dim 256); else 1
     int32_t lds;                // dynamic LDS bytes of the decode workgroup
-    RowGeo geo;                 // whole-row kernel geometry
     float scale;
     float* part_ml;             // [B, splits, T, H, 2]  running max, running sum
     float* part_o;              // [B, splits, T, H, hd] unnormalised output
@@ -221,6 +178,9 @@ struct DecodeParams {
     float* out;                 // [B, T, H, hd]
     float* lse;                 // [B, T, H] or null
 };
+
+// Compute units of the current device (0 if it cannot be read).
+int device_compute_units();
 
 // Launchers: return 0 on success, nonzero with a message in *err otherwise.
 int launch_append(const AppendParams& p, void* stream, const char** err);

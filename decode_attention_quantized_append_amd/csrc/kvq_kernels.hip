@@ -13,9 +13,9 @@
 //   append_kernel   fused quantize-and-append at slot len_d - base_d, with
 //                   the len_d advance (stopped at the plane) done by the last
 //                   workgroup to finish.
-//   decode kernels  split-K flash decode (kvq_decode.hip, kvq_decode_rows.hip,
-//                   kvq_decode_stream.hip): online softmax of a group of query
-//                   rows over a chunk of rows, unnormalised partial (m, l, o).
+//   decode kernels  split-K flash decode (kvq_decode.hip, kvq_decode_stream.hip):
+//                   online softmax of a group of query rows over a chunk of
+//                   rows, unnormalised partial (m, l, o).
 //   combine_kernel  log-sum-exp fold of the splits plus the sink column.
 //   importance_kernel  per-row attention mass from the decode's lse.
 #include <hip/hip_runtime.h>
@@ -220,7 +220,6 @@ __global__ __launch_bounds__(1024) void append_kernel(AppendParams p) {
 
 // ---------------------------------------------------------------------------
 #include "kvq_decode.hip"
-#include "kvq_decode_rows.hip"
 #include "kvq_decode_stream.hip"
 
 // One workgroup per (session, row t, Q head h): fold the session's split
@@ -600,23 +599,6 @@ int launch_decode_t(const DecodeParams& p, hipStream_t st, const char** err) {
     return check(err);
 }
 
-template <int NB, int RT, bool QLO>
-int launch_rows_t(const DecodeParams& p, hipStream_t st, const char** err) {
-    static bool configured = false;
-    if (!configured) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&rows::decode_rows<NB, RT, QLO>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) != hipSuccess) {
-            *err = "cannot raise the LDS limit of the decode kernel";
-            return 1;
-        }
-        configured = true;
-    }
-    const int items = std::max(1, p.units) * (p.Hkv / p.gh);
-    const int grid = (items + 7) & ~7;
-    hipLaunchKernelGGL((rows::decode_rows<NB, RT, QLO>), dim3(grid, (p.T + p.Tg - 1) / p.Tg), dim3(64 * p.gh * RT), p.lds, st, p);
-    return check(err);
-}
-
 template <int NB, int RTW, bool QLO, int RS, int RG, int DS = 1>
 int launch_stream_t(const DecodeParams& p, hipStream_t st, const char** err) {
     static bool configured = false;
@@ -668,14 +650,6 @@ int launch_stream_nb(const DecodeParams& p, hipStream_t st, const char** err) {
 }
 
 template <int NB>
-int launch_rows_nb(const DecodeParams& p, hipStream_t st, const char** err) {
-    const int R = p.Tg * p.hpk;   // query rows per KV head of one group
-    const bool qlo = p.dtype == 0;
-    if (R <= 16) return qlo ? launch_rows_t<NB, 1, true>(p, st, err) : launch_rows_t<NB, 1, false>(p, st, err);
-    return qlo ? launch_rows_t<NB, 2, true>(p, st, err) : launch_rows_t<NB, 2, false>(p, st, err);
-}
-
-template <int NB>
 int launch_decode_nb(const DecodeParams& p, hipStream_t st, const char** err) {
     const int R = p.Tg * p.hpk;   // query rows per KV head of one group
     const bool qlo = p.dtype == 0;   // fp32 queries keep a low fp16 part
@@ -684,6 +658,13 @@ int launch_decode_nb(const DecodeParams& p, hipStream_t st, const char** err) {
 }
 
 }  // namespace
+
+int device_compute_units() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return n;
+}
 
 int launch_set(const SetParams& p, void* stream, const char** err) {
     hipLaunchKernelGGL(set_kernel, dim3(1), dim3(kMaxSetPerLaunch), 0, (hipStream_t)stream, p);
@@ -713,14 +694,6 @@ int launch_append(const AppendParams& p, void* stream, const char** err) {
 
 namespace {
 int launch_partials(const DecodeParams& p, hipStream_t st, const char** err) {
-    if (p.kernel == kWholeRow) {
-        switch (p.hd / 32) {
-            case 2: return launch_rows_nb<2>(p, st, err);
-            case 4: return launch_rows_nb<4>(p, st, err);
-            case 8: return launch_rows_nb<8>(p, st, err);
-            default: *err = "the whole-row decode supports head_dim 64, 128 and 256"; return 1;
-        }
-    }
     if (p.kernel == kStream) {
         switch (p.hd / 32) {
             case 2: return launch_stream_nb<2>(p, st, err);

@@ -13,6 +13,7 @@
 namespace {
 std::string g_log;
 int g_fail_next = 0;
+int g_cus = 256;   // the compute units a handle sees (MI355X: 256)
 
 int record(const std::string& line, const char** err) {
     if (g_fail_next) {
@@ -27,6 +28,8 @@ int record(const std::string& line, const char** err) {
 }  // namespace
 
 namespace kvq {
+
+int device_compute_units() { return g_cus; }
 
 int launch_set(const SetParams& p, void*, const char** err) {
     std::string s = p.add ? "add" : "set";
@@ -53,7 +56,7 @@ int launch_decode(const DecodeParams& p, void*, const char** err) {
                     " splits=" + std::to_string(p.splits) + " ml_to_o=" +
                     std::to_string((const char*)p.part_o - (const char*)p.part_ml) +
                     " kernel=" + std::to_string(p.kernel) + " gh=" + std::to_string(p.gh) +
-                    " sub=" + std::to_string(p.sub) + " rs=" + std::to_string(p.rs) + " rg=" + std::to_string(p.rg) + " ds=" + std::to_string(p.ds) +
+                    " rs=" + std::to_string(p.rs) + " rg=" + std::to_string(p.rg) + " ds=" + std::to_string(p.ds) +
                     " lds=" + std::to_string(p.lds) + " units=" + std::to_string(p.units) +
                     " Tg=" + std::to_string(p.Tg) + " groups=" + std::to_string((p.T + p.Tg - 1) / p.Tg);
     return record(s, err);
@@ -69,4 +72,5 @@ extern "C" {
 const char* kvq_nodev_log(void) { return g_log.c_str(); }
 void kvq_nodev_clear(void) { g_log.clear(); }
 void kvq_nodev_fail_next(void) { g_fail_next = 1; }
+void kvq_nodev_set_cus(int n) { g_cus = n; }
 }

@@ -21,7 +21,7 @@ NODEV_PATH = os.path.join(_PKG, "libkvq_nodev.so")
 KVQ_OK, KVQ_EINVAL, KVQ_ECAPACITY, KVQ_ERANGE, KVQ_EUNSUPPORTED, KVQ_EDEVICE = range(6)
 KVQ_F32, KVQ_BF16 = 0, 1
 KVQ_FMT_Q8_0, KVQ_FMT_Q5_1 = 1, 2
-KVQ_DECODE_AUTO, KVQ_DECODE_PER_HEAD, KVQ_DECODE_WHOLE_ROW, KVQ_DECODE_STREAM = range(4)
+KVQ_DECODE_AUTO, KVQ_DECODE_PER_HEAD, KVQ_DECODE_STREAM = 0, 1, 3
 STATUS_NAMES = {0: "KVQ_OK", 1: "KVQ_EINVAL", 2: "KVQ_ECAPACITY", 3: "KVQ_ERANGE",
                 4: "KVQ_EUNSUPPORTED", 5: "KVQ_EDEVICE"}
 
@@ -114,6 +114,8 @@ def load_nodev():
     lib.kvq_nodev_log.restype = ctypes.c_char_p
     lib.kvq_nodev_clear.restype = None
     lib.kvq_nodev_fail_next.restype = None
+    lib.kvq_nodev_set_cus.restype = None
+    lib.kvq_nodev_set_cus.argtypes = [ctypes.c_int]
     return lib
 
 

@@ -117,7 +117,15 @@ typedef struct kvq_info_t {
     int32_t split_rows;   /* rows per split-K chunk; 0 = chosen per call */
 } kvq_info_t;
 
-/* Fills *out for cfg.  Pure host computation.
+/* Fills *out for cfg: the device bytes of the K and V planes, sized up front
+ * for capacity rows per session, and of the counters.  Pure host computation.
+ * Defined by: memra-engine "Module cache" page, functions
+ * cache_bytes_per_token (context-linear bytes per cached token) and
+ * kv_blk_bytes (bytes per 32-element block of the selected K and V formats);
+ * "Struct KvLayer" page, fields k_tok_bytes / v_tok_bytes (bytes per token
+ * row) and struct description (34 and 24 bytes per 32 elements); "Struct
+ * Cache" page, new (caches sized by the model geometry and the maximum
+ * context).
  * Errors: EINVAL (NULL pointer, bad geometry), EUNSUPPORTED (format, head_dim). */
 kvq_status kvq_required_bytes(const kvq_config* cfg, kvq_sizes* out);
 
@@ -125,8 +133,16 @@ kvq_status kvq_required_bytes(const kvq_config* cfg, kvq_sizes* out);
  * (256-byte aligned, at least the sizes from kvq_required_bytes) and counters
  * (256-byte aligned, counters_bytes).  Enqueues the zeroing of len_d, base_d
  * and the library scratch on `stream`; plane contents are not touched.  The
- * host mirror starts at len = base = 0.
- * Errors: EINVAL, EUNSUPPORTED, EDEVICE. */
+ * host mirror starts at len = base = 0 (an empty cache).  The current device
+ * is the one the handle's launches run on; its compute-unit count, read
+ * here, sizes the split-K plans.
+ * Defined by: memra-engine "Struct Cache" page, new (GPU-resident caches
+ * sized by architecture and maximum context); "Struct KvLayer" page, fields
+ * k, v (the planes), len, len_d and base_d (the counters); cortiq-engine
+ * "Struct LayerKvCache" page, new (a layer cache for num_kv_heads heads of
+ * head_dim).
+ * Errors: EINVAL, EUNSUPPORTED, EDEVICE (also when the device's compute-unit
+ * count cannot be read; then no handle is made and nothing is enqueued). */
 kvq_status kvq_create(const kvq_config* cfg, void* k_planes, void* v_planes,
                       int32_t* counters, kvq_stream stream, kvq_cache** out);
 
@@ -151,7 +167,12 @@ kvq_status kvq_append(kvq_cache* h, const void* k_new, const void* v_new,
                       kvq_stream stream);
 
 /* Device workspace bytes kvq_decode needs for T query rows at the handle's
- * current lengths (in graph mode, at every length the plane allows). */
+ * current lengths (in graph mode, at every length the plane allows): the
+ * split-K partials (m, l, o) of every (session, chunk, query row, Q head).
+ * No passage defines it: the pages' decode has no caller workspace.  It
+ * exists because this library never allocates device memory, so the
+ * partials of the split-K decode live in a caller buffer.
+ * Errors: EINVAL (NULL, T < 1, H/Hkv above 32). */
 kvq_status kvq_decode_workspace_bytes(const kvq_cache* h, int32_t T, size_t* bytes);
 
 /* Decode attention (memra fa_decode_dc / fa_decode_dcw; cortiq attend_group
@@ -214,37 +235,49 @@ kvq_status kvq_rollback(kvq_cache* h, const int32_t* drop, kvq_stream stream);
 /* Tuning: rows per split-K chunk of kvq_decode (a positive multiple of 64),
  * or 0 to let each call choose; a call raises it when a session would need
  * more than 1024 chunks.  The result does not depend on it beyond float
- * rounding.  Errors: EINVAL. */
+ * rounding: the chunks' partials are merged by the log-sum-exp identity, so
+ * the attention of cortiq-engine "Struct LayerKvCache" attend_group is the
+ * same for any split.  Errors: EINVAL. */
 kvq_status kvq_set_split_rows(kvq_cache* h, int32_t rows);
 
-/* Decode kernels (kvq_set_decode_tiling). */
+/* Decode kernels (kvq_set_decode_tiling).  The value 2 is not used. */
 typedef enum kvq_decode_kernel {
     KVQ_DECODE_AUTO = 0,        /* chosen per call */
     KVQ_DECODE_PER_HEAD = 1,    /* one KV head per workgroup, any head_dim */
-    KVQ_DECODE_WHOLE_ROW = 2,   /* workgroups stream whole row segments of adjacent KV heads */
     KVQ_DECODE_STREAM = 3       /* one or two waves per KV head, each streaming its rows through LDS */
 } kvq_decode_kernel;
 
-/* Tuning: which kernel kvq_decode runs and how it tiles the cache.
- * head_group: KV heads per workgroup for the whole-row and stream kernels (a
- * divisor of n_kv_heads), 0 = chosen per call.  sub_tiles: rows per buffer /
- * 32 for the whole-row kernel (1, 2 or 4); waves per KV head for the stream
- * kernel: 1 or 2 row streams (up to 16 query rows per head), 1 wave holding
- * both 16-row tiles or 2 row-group waves (17 to 32 rows), or 3 = two waves
- * each taking half of a 128- or 256-dim head for all rows (17 to 32 rows);
- * 0 = chosen per call.  The
- * whole-row and stream kernels need head_dim 64, 128 or 256; a kernel or
- * tiling that does not fit a call's shape makes that kvq_decode fail with
- * EINVAL, except that a session whose first visible row, rounded down to 32,
- * was rebased away is served by the per-head kernel.  The result does not
- * depend on the choice beyond float rounding.  Errors: EINVAL. */
+/* Tuning: which kernel kvq_decode runs and how it tiles the cache (the
+ * work split of cortiq-engine "Struct LayerKvCache" attend_group over the
+ * GPU; the pages fix no tiling).
+ * head_group: KV heads per workgroup for the stream kernel (a divisor of
+ * n_kv_heads), 0 = chosen per call.  sub_tiles: waves per KV head for the
+ * stream kernel: 1 or 2 row streams (up to 16 query rows per head), 1 wave
+ * holding both 16-row tiles or 2 row-group waves (17 to 32 rows), or 3 = two
+ * waves each taking half of a 128- or 256-dim head for all rows (17 to 32
+ * rows); 0 = chosen per call.  The stream kernel needs head_dim 64, 128 or
+ * 256; a kernel or tiling that does not fit a call's shape makes that
+ * kvq_decode fail with EINVAL, except that a session whose first visible
+ * row, rounded down to 32, was rebased away is served by the per-head
+ * kernel.  The result does not depend on the choice beyond float rounding.
+ * Errors: EINVAL (unknown kernel, head_group not dividing n_kv_heads,
+ * head_group or sub_tiles given for the per-head kernel). */
 kvq_status kvq_set_decode_tiling(kvq_cache* h, int32_t kernel, int32_t head_group, int32_t sub_tiles);
 
-/* Copies the handle's configuration, sizes and buffer pointers. */
+/* Copies the handle's configuration, sizes and buffer pointers.
+ * Defined by: cortiq-engine "Struct LayerKvCache" page, head_keys and
+ * head_len (a head's stored rows and how many there are: here the plane
+ * pointers, row bytes and capacity from which they are addressed);
+ * memra-engine "Struct KvLayer" page, fields k, v, k_tok_bytes, v_tok_bytes.
+ * Errors: EINVAL (NULL). */
 kvq_status kvq_info(const kvq_cache* h, kvq_info_t* out);
 
 /* Copies the host mirror: len[b] and base[b] for every session (HOST arrays
- * of n_seqs entries; either may be NULL). */
+ * of n_seqs entries; either may be NULL).
+ * Defined by: memra-engine "Struct KvLayer" page, fields len (the host
+ * length, kept in step with len_d) and ring / base_d (the ring base);
+ * cortiq-engine "Struct LayerKvCache" page, head_len.
+ * Errors: EINVAL (NULL handle). */
 kvq_status kvq_host_lengths(const kvq_cache* h, int64_t* len, int64_t* base);
 
 /* Graph mode (memra KvLayer len_d: steps with no host round-trip; a captured
@@ -262,15 +295,25 @@ kvq_status kvq_host_lengths(const kvq_cache* h, int64_t* len, int64_t* base);
 kvq_status kvq_set_graph_mode(kvq_cache* h, int32_t on);
 
 /* Sets the host mirror of len and base (HOST arrays of n_seqs entries), for
- * example to the device counters read back after graph replays.  Requires
- * 0 <= base <= len <= base + capacity, and base 0 for a flat cache.  Nothing
- * is enqueued.  Errors: EINVAL (nothing changed). */
+ * example to the device counters read back after graph replays (memra-engine
+ * "Struct KvLayer" page, len_d: the host len and the device counter are kept
+ * in step; here the caller restores that after replays the host did not
+ * see).  Requires 0 <= base <= len <= base + capacity, and base 0 for a flat
+ * cache.  Nothing is enqueued.  Errors: EINVAL (nothing changed). */
 kvq_status kvq_set_host_lengths(kvq_cache* h, const int64_t* len, const int64_t* base);
 
-/* Frees the host handle only; device memory stays with the caller. */
+/* Frees the host handle only; device memory stays with the caller, as it
+ * was allocated by the caller.  Defined by: cortiq-engine "Struct
+ * LayerKvCache" page, clear (the cache of a conversation is dropped; a new
+ * handle over the same planes starts empty, like a cleared cache).  NULL is
+ * accepted and ignored. */
 void kvq_destroy(kvq_cache* h);
 
-/* Thread-local message describing the last failed call on this thread. */
+/* Thread-local message describing the last failed call on this thread.
+ * Defined by: memra-engine "Struct KvLayer" page, physical_rows (a failure
+ * is returned with its message, Err(String), rather than clamped), and
+ * "Struct Cache" page, new / rollback (Result with a boxed error).  The
+ * string stays valid until the next failing call on the same thread. */
 const char* kvq_last_error(void);
 
 #ifdef __cplusplus

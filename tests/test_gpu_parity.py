@@ -147,19 +147,17 @@ def test_decode_split_invariance():
     p.decode(q, scale)
 
 
-# Decode kernels and tilings (kernel, KV heads per workgroup, rows per
-# buffer / 32) that fit each shape; the automatic choice is covered by
+# Decode kernels and tilings (kernel, KV heads per workgroup, waves per KV
+# head) that fit each shape; the automatic choice is covered by
 # test_decode_parity.
-PH, WR, ST = kvq.KVQ_DECODE_PER_HEAD, kvq.KVQ_DECODE_WHOLE_ROW, kvq.KVQ_DECODE_STREAM
+PH, ST = kvq.KVQ_DECODE_PER_HEAD, kvq.KVQ_DECODE_STREAM
 TILINGS = {
-    "qwen_gqa_small": [(WR, 8, 1), (WR, 4, 1), (WR, 4, 2), (WR, 2, 1), (WR, 2, 2), (ST, 8, 0), (ST, 2, 0),
-                       (ST, 1, 0), (ST, 8, 1), (ST, 8, 2), (ST, 2, 2)],
-    "batched_small": [(WR, 8, 1), (WR, 4, 2), (WR, 2, 1), (ST, 8, 0), (ST, 4, 0), (ST, 8, 2), (ST, 4, 2)],
-    "sink_ring_small": [(WR, 8, 1), (WR, 8, 2), (WR, 4, 1), (WR, 4, 4), (ST, 8, 0), (ST, 2, 0), (ST, 8, 2)],
-    "verify_small": [(WR, 4, 1), (WR, 2, 1), (WR, 2, 2), (WR, 1, 1), (WR, 1, 2), (ST, 4, 0), (ST, 1, 0),
-                     (ST, 4, 1), (ST, 2, 1), (ST, 1, 1), (ST, 4, 2), (ST, 2, 2), (ST, 1, 2), (ST, 4, 3),
-                     (ST, 2, 3), (ST, 1, 3)],
-    "qwen_f32_small": [(WR, 8, 1), (WR, 2, 2), (ST, 8, 0), (ST, 4, 0), (ST, 8, 1)],
+    "qwen_gqa_small": [(ST, 8, 0), (ST, 2, 0), (ST, 1, 0), (ST, 8, 1), (ST, 8, 2), (ST, 2, 2)],
+    "batched_small": [(ST, 8, 0), (ST, 4, 0), (ST, 8, 2), (ST, 4, 2)],
+    "sink_ring_small": [(ST, 8, 0), (ST, 2, 0), (ST, 8, 2)],
+    "verify_small": [(ST, 4, 0), (ST, 1, 0), (ST, 4, 1), (ST, 2, 1), (ST, 1, 1), (ST, 4, 2), (ST, 2, 2),
+                     (ST, 1, 2), (ST, 4, 3), (ST, 2, 3), (ST, 1, 3)],
+    "qwen_f32_small": [(ST, 8, 0), (ST, 4, 0), (ST, 8, 1)],
     "tiny": [(ST, 1, 0)],
     "verify_f32_small": [(ST, 4, 1), (ST, 2, 1), (ST, 4, 2), (ST, 2, 2), (ST, 4, 3), (ST, 2, 3)],
 }
@@ -197,7 +195,7 @@ MANY = {
     # name: (B, H, Hkv, hd, T, lengths, window, sinks, io, tiling)
     "hd128_T40_sinks": (2, 8, 2, 128, 40, [700, 300], 0, True, "bf16", None),
     "hd256_T19": (1, 16, 4, 256, 19, [500], 0, False, "bf16", None),
-    "hd256_T19_rows": (1, 16, 4, 256, 19, [500], 0, False, "bf16", (kvq.KVQ_DECODE_WHOLE_ROW, 0)),
+    "hd256_T19_rowgroups": (1, 16, 4, 256, 19, [500], 0, False, "bf16", (kvq.KVQ_DECODE_STREAM, 0, 2)),
     "hd256_T19_dimhalves": (1, 16, 4, 256, 19, [500], 0, True, "bf16", (kvq.KVQ_DECODE_STREAM, 0, 3)),
     "hd128_T40_dimhalves": (2, 8, 2, 128, 40, [700, 300], 0, True, "bf16", (kvq.KVQ_DECODE_STREAM, 0, 3)),
     "hd128_T21_window_dimhalves_f32": (2, 32, 8, 128, 21, [400, 130], 90, False, "f32", (kvq.KVQ_DECODE_STREAM, 4, 3)),
@@ -284,7 +282,7 @@ def test_chunked_prime_into_ring():
     assert int(p.ref.base[0]) > 0
 
 
-@pytest.mark.parametrize("step,tiling", [(24, (kvq.KVQ_DECODE_PER_HEAD, 0)), (32, (kvq.KVQ_DECODE_WHOLE_ROW, 4)),
+@pytest.mark.parametrize("step,tiling", [(24, (kvq.KVQ_DECODE_PER_HEAD, 0)), (32, (kvq.KVQ_DECODE_STREAM, 4)),
                                          (32, (kvq.KVQ_DECODE_STREAM, 0)), (32, (kvq.KVQ_DECODE_AUTO, 0))])
 def test_ring_equals_flat(step, tiling):
     """The base-offset ring serves the same rows as a flat cache: identical

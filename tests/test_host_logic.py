@@ -373,7 +373,7 @@ def plan_of(lib, h, T=1, dtype=kvq.KVQ_BF16):
 
 
 def test_decode_kernel_choice(lib):
-    PER_HEAD, WHOLE_ROW, STREAM = 0, 1, 2          # as recorded by the launcher
+    PER_HEAD, STREAM = 0, 2                        # as recorded by the launcher
     # 8 KV heads x 128: one wave per KV head; 8192 rows would give each wave a
     # single tile with 8 heads per workgroup, so 4 heads per workgroup take
     # two tiles each (64-row chunks, the same number of workgroups)
@@ -395,25 +395,19 @@ def test_decode_kernel_choice(lib):
     assert (p["kernel"], p["gh"]) == (STREAM, 8) and p["chunk"] > 64
     kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_PER_HEAD, 0, 0, lib)
     assert plan_of(lib, h)["kernel"] == PER_HEAD
-    kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_WHOLE_ROW, 8, 1, lib)
-    p = plan_of(lib, h)
-    assert (p["kernel"], p["gh"], p["sub"]) == (WHOLE_ROW, 8, 1) and p["lds"] <= 160 * 1024
-    kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_WHOLE_ROW, 4, 2, lib)
-    p = plan_of(lib, h)
-    assert (p["kernel"], p["gh"], p["sub"]) == (WHOLE_ROW, 4, 2) and p["chunk"] % 64 == 0
     kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_STREAM, 2, 0, lib)
     p = plan_of(lib, h)
     assert (p["kernel"], p["gh"]) == (STREAM, 2)
     E = kvq.KVQ_EINVAL
-    assert err(lib, kvq.kvq_set_decode_tiling, h, kvq.KVQ_DECODE_WHOLE_ROW, 3, 0) == E   # does not divide 8
-    assert err(lib, kvq.kvq_set_decode_tiling, h, kvq.KVQ_DECODE_WHOLE_ROW, 2, 3) == E   # no such depth
-    assert err(lib, kvq.kvq_set_decode_tiling, h, kvq.KVQ_DECODE_STREAM, 2, 4) == E      # 1 or 2 row streams
+    assert err(lib, kvq.kvq_set_decode_tiling, h, kvq.KVQ_DECODE_STREAM, 3, 0) == E      # does not divide 8
+    assert err(lib, kvq.kvq_set_decode_tiling, h, kvq.KVQ_DECODE_STREAM, 2, 4) == E      # 1 .. 3 waves per head
     assert err(lib, kvq.kvq_set_decode_tiling, h, kvq.KVQ_DECODE_PER_HEAD, 2, 0) == E    # no head groups there
+    assert err(lib, kvq.kvq_set_decode_tiling, h, 2, 0, 0) == E                          # no kernel 2
     assert err(lib, kvq.kvq_set_decode_tiling, h, 4, 0, 0) == E
-    # one head of 128 is not a whole number of 16-byte pieces for the whole-row kernel: that call fails
-    kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_WHOLE_ROW, 1, 0, lib)
+    # two row streams of fp32 queries are not built: that call fails, enqueueing nothing
+    kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_STREAM, 8, 2, lib)
     lib.kvq_nodev_clear()
-    assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 1, None, 0.1, O, None, WS, 1 << 40) == E
+    assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_F32, 1, None, 0.1, O, None, WS, 1 << 40) == E
     assert log(lib) == []
     # verify rows (T=8, 4 query heads per KV head: 32 rows): two waves per
     # 256-dim head, each half of its dims, one head per workgroup
@@ -432,10 +426,7 @@ def test_decode_kernel_choice(lib):
     kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_STREAM, 0, 3, lib)
     assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 4, None, 0.1, O, None, WS, 1 << 40) == E
     assert log(lib) == []
-    kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_WHOLE_ROW, 0, 0, lib)
-    p = plan_of(lib, h, T=8)
-    assert (p["kernel"], p["gh"]) == (WHOLE_ROW, 4)
-    # head_dim 96 has no whole-row or stream kernel
+    # head_dim 96 has no stream kernel
     h = create(lib, n_seqs=1, n_q_heads=8, n_kv_heads=8, head_dim=96, capacity=100)
     kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 50, None, 0, lib)
     assert plan_of(lib, h)["kernel"] == PER_HEAD
@@ -481,13 +472,13 @@ def test_decode_row_streams(lib):
 
 
 def test_decode_ring_start_below_base_falls_back(lib):
-    # ring_step 10: base is not always a multiple of 32, and the whole-row
+    # ring_step 10: base is not always a multiple of 32, and the stream
     # kernel, which starts at the first visible row rounded down to 32, is
     # used only while that row is still resident
     h = create(lib, n_seqs=1, n_q_heads=32, n_kv_heads=8, head_dim=128, capacity=100, window=90,
                ring_step=10)
-    for kernel, want in ((kvq.KVQ_DECODE_WHOLE_ROW, 1), (kvq.KVQ_DECODE_STREAM, 2)):
-        kvq.kvq_set_decode_tiling(h, kernel, 8, 0, lib)
+    for kernel, gh, want in ((kvq.KVQ_DECODE_STREAM, 8, 2), (kvq.KVQ_DECODE_AUTO, 0, 2)):
+        kvq.kvq_set_decode_tiling(h, kernel, gh, 0, lib)
         seen = set()
         for _ in range(150):
             kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 1, None, 0, lib)
@@ -516,3 +507,24 @@ def test_info(lib):
     info = kvq.kvq_info(h, lib)
     assert (info.config.n_seqs, info.config.capacity, info.config.window) == (3, 77, 5)
     assert (info.k_planes, info.v_planes, info.counters) == (K, V, C)
+
+
+def test_plan_follows_the_device_compute_units(lib):
+    """One round of decode workgroups is sized to the CUs of the device the
+    handle was created on (read at kvq_create), not to a fixed count."""
+    chunks = {}
+    try:
+        for cus in (256, 128, 64):
+            lib.kvq_nodev_set_cus(cus)
+            h = create(lib, n_seqs=4, n_q_heads=40, n_kv_heads=8, head_dim=128, capacity=31000)
+            kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 30000, None, 0, lib)
+            p = plan_of(lib, h)
+            chunks[cus] = p["chunk"]
+            assert p["units"] * (8 // p["gh"]) <= cus * 8   # at most one round of workgroups
+        assert chunks[256] < chunks[128] < chunks[64]
+        lib.kvq_nodev_set_cus(0)                             # an unreadable count: no handle
+        cfg = kvq.make_config(1, 4, 1, 64, 100)
+        out = ctypes.c_void_p()
+        assert lib.kvq_create(ctypes.byref(cfg), K, V, C, None, ctypes.byref(out)) == kvq.KVQ_EDEVICE
+    finally:
+        lib.kvq_nodev_set_cus(256)
