@@ -61,9 +61,33 @@ struct Layout {
     static constexpr int QFRAG = RT * NB * 64 * 16;               // Q fragments, fp16
     static constexpr int Q = kWaves * WAVE;
     static constexpr int ML = Q + 2 * QFRAG;                      // [wave][RT*16][2] f32
-    static constexpr int BYTES = ML + kWaves * RT * 16 * 2 * 4;
+    static constexpr int QE = ML + kWaves * RT * 16 * 2 * 4;      // u32 exponent of the largest |q|
+    static constexpr int BYTES = QE + 16;
+    static_assert(BYTES <= kLdsBytes, "the per-head layout must fit a CU's LDS");
     static_assert(RT * 16 * HD * 4 <= kWaves * WAVE, "merge buffer must fit in the wave areas");
 };
+
+// 2^k as a binary32, for -126 <= k <= 127.
+__device__ __forceinline__ float pow2(int k) { return __uint_as_float((uint32_t)(127 + k) << 23); }
+
+// Query rows enter the matrix cores as fp16.  A row is first divided by a
+// power of two chosen from the biased binary32 exponent e of its largest
+// |q| (taken as at least 15): 2^(e - 141) maps that element into
+// [2^14, 2^15), so every bf16 query is exact in fp16 whatever its magnitude,
+// and the scores computed from the scaled row are multiplied back by
+// q_up(e).  Both factors are normal binary32 numbers.
+__device__ __forceinline__ float q_down(uint32_t e) { return pow2(141 - (int)max(e, 15u)); }
+__device__ __forceinline__ float q_up(uint32_t e) { return pow2((int)max(e, 15u) - 141); }
+// The biased exponent of a magnitude held as binary32 bits (sign cleared).
+__device__ __forceinline__ uint32_t exp_of(uint32_t mag_bits) { return mag_bits >> 23; }
+
+// P V takes P' = P * d (softmax weight times a V block's step) as fp16, with
+// P <= 2^8.  While every step of a tile is below 2^7, P' < 2^15 (fp16 holds
+// up to 65504).  A tile whose largest step dmax is larger has its steps
+// stored times 2^-E, E = v_shift(dmax): then d * 2^-E < 2^7 again, and the
+// wave's P V accumulator holds its sum in units of 2^-E (rescaled exactly,
+// by a power of two, whenever E changes).
+__device__ __forceinline__ int v_shift(float dmax) { return max(0, (int)(__float_as_uint(dmax) >> 23) - 133); }
 
 __device__ __forceinline__ float row_max16(float v) {
     v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false)));
@@ -71,6 +95,18 @@ __device__ __forceinline__ float row_max16(float v) {
     v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false)));
     v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false)));
     return v;
+}
+
+// Largest v over the wave, in every lane: DPP maxima within each row of 16
+// lanes, then the four rows' results read as scalars (no lane-address
+// registers, unlike shuffles).
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    v = row_max16(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 __device__ __forceinline__ float row_sum16(float v) {
@@ -175,9 +211,11 @@ __device__ __forceinline__ void stage_load(Raw<NB>& r, const uint8_t* kplane, co
     }
 }
 
+// Returns the largest V step this lane converted (for dec::v_shift).
 template <int NB>
-__device__ __forceinline__ void stage_store(const Raw<NB>& r, uint8_t* Wb, int lane, float sc2) {
+__device__ __forceinline__ float stage_store(const Raw<NB>& r, uint8_t* Wb, int lane, float sc2) {
     using LY = Layout<NB, 1>;
+    float dmax = 0.0f;
     float* ks = reinterpret_cast<float*>(Wb + LY::KS);
     float* vd = reinterpret_cast<float*>(Wb + LY::VD);
     uint16_t* vm = reinterpret_cast<uint16_t*>(Wb + LY::VM);
@@ -211,9 +249,23 @@ __device__ __forceinline__ void stage_store(const Raw<NB>& r, uint8_t* Wb, int l
             uint4* vdst = reinterpret_cast<uint4*>(Wb + LY::VC + key * LY::VROW + blk * 32);
             vdst[0] = (uint4){vc[0], vc[1], vc[2], vc[3]};
             vdst[1] = (uint4){vc[4], vc[5], vc[6], vc[7]};
-            vd[blk * kTile + key] = f16_value((uint16_t)(r.va[x].x & 0xFFFF));
+            const float dv = f16_value((uint16_t)(r.va[x].x & 0xFFFF));
+            vd[blk * kTile + key] = dv;
+            dmax = fmaxf(dmax, dv);
             vm[key * 16 + blk] = (uint16_t)(r.va[x].x >> 16);
         }
+    }
+    return dmax;
+}
+
+// Multiplies the V steps this lane stored (stage_store's units) by f.
+template <int NB>
+__device__ __forceinline__ void rescale_steps(uint8_t* Wb, int lane, float f) {
+    float* vd = reinterpret_cast<float*>(Wb + Layout<NB, 1>::VD);
+#pragma unroll
+    for (int x = 0; x < Raw<NB>::U; ++x) {
+        const int u = x * 64 + lane;
+        if (kTile * NB % 64 == 0 || u < kTile * NB) vd[(u - (u / NB) * NB) * kTile + u / NB] *= f;
     }
 }
 
@@ -226,6 +278,8 @@ struct WaveState {
     float lsum[RT][4];       // this lane's share of the row sums
     int vis_lo[RT][4], vis_hi[RT][4];
     int full_lo, full_hi;    // every row sees all of [full_lo, full_hi)
+    float qup;               // the query rows were divided by 1 / qup (q_down)
+    int vsh;                 // oacc holds its sums in units of 2^-vsh (v_shift)
 };
 
 // One 32-row tile from the wave's LDS area: scores, online softmax, P V.
@@ -278,7 +332,7 @@ __device__ __forceinline__ void tile_compute(WaveState<NB, RT>& ws, const uint8_
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float s0 = sacc[rt][0][i], s1 = sacc[rt][1][i];
+            float s0 = sacc[rt][0][i] * ws.qup, s1 = sacc[rt][1][i] * ws.qup;
             if (!interior) {
                 const int j0 = t0 + j16, j1 = t0 + 16 + j16;
                 s0 = (j0 >= ws.vis_lo[rt][i] && j0 < ws.vis_hi[rt][i]) ? s0 : -INFINITY;
@@ -510,16 +564,36 @@ __global__ __launch_bounds__(256, (min_blocks<NB, RT>())) void decode_mfma(Decod
     for (int i = 0; i < kDepth; ++i)
         stage_load<NB>(raw[i], kplane, vplane, p.k_row, p.v_row, first + i * kStride, lo_all, c1, base, lane);
 
+    // the exponent of the largest |q| of the workgroup's query rows (whose
+    // fragments every wave holds a part of) meets in LDS; the rows are
+    // divided by q_down of it, and the scores multiplied back by q_up
+    uint32_t* const qexp = reinterpret_cast<uint32_t*>(smem + LY::QE);
+    if (tid == 0) *qexp = 0;
+    __syncthreads();
+    {
+        uint32_t mag = 0;
+#pragma unroll
+        for (int x = 0; x < FPT; ++x)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mag = max(mag, __float_as_uint(qv[x][e]) & 0x7FFFFFFFu);
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) mag = max(mag, (uint32_t)__shfl_xor((int)mag, m));
+        if (lane == 0) atomicMax(qexp, exp_of(mag));
+    }
+    __syncthreads();
+    const uint32_t qe = __builtin_amdgcn_readfirstlane(*qexp);
 #pragma unroll
     for (int x = 0; x < FPT; ++x) {
         const int f = x * 256 + tid;
         if (f < NFRAG) {
+            const float down = q_down(qe);
             h8 hi, lo;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const _Float16 xh = (_Float16)qv[x][e];
+                const float xs = qv[x][e] * down;
+                const _Float16 xh = (_Float16)xs;
                 hi[e] = xh;
-                lo[e] = (_Float16)(qv[x][e] - (float)xh);
+                lo[e] = (_Float16)(xs - (float)xh);
             }
             *reinterpret_cast<h8*>(smem + LY::Q + f * 16) = hi;
             if (QLO) *reinterpret_cast<h8*>(smem + LY::Q + LY::QFRAG + f * 16) = lo;
@@ -546,6 +620,8 @@ __global__ __launch_bounds__(256, (min_blocks<NB, RT>())) void decode_mfma(Decod
             ws.vis_hi[rt][i] = min(hi, c1);
         }
     }
+    ws.qup = q_up(qe);
+    ws.vsh = 0;
     // rows' visible ranges are nested by t; the intersection over real rows
     ws.full_hi = min(len - p.T + tq0 + 1, c1);
     ws.full_lo = max(p.window > 0 ? max(0, len - p.window) : 0, c0);
@@ -561,7 +637,24 @@ __global__ __launch_bounds__(256, (min_blocks<NB, RT>())) void decode_mfma(Decod
 #pragma unroll
         for (int i = 0; i < kDepth; ++i) {
             const int tt = t0 + i * kStride;
-            stage_store<NB>(raw[i], Wb, lane, sc2);
+            const float dmax = stage_store<NB>(raw[i], Wb, lane, sc2);
+            // steps of 2^7 or more: the tile's steps are stored times
+            // 2^-vsh (v_shift) and the accumulators switch units
+            const bool big = __any(dmax >= 128.0f);   // wave-uniform
+            if (big || ws.vsh != 0) {
+                const int want = big ? __builtin_amdgcn_readfirstlane(v_shift(wave_max_dpp(dmax))) : 0;
+                if (want != ws.vsh) {
+                    const float f = pow2(ws.vsh - want);
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                        for (int dt = 0; dt < 2 * NB; ++dt)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) ws.oacc[rt][dt][e] *= f;
+                    ws.vsh = want;
+                }
+                rescale_steps<NB>(Wb, lane, pow2(-ws.vsh));
+            }
             lds_order();
             stage_load<NB>(raw[i], kplane, vplane, p.k_row, p.v_row, tt + kDepth * kStride, lo_all, c1, base, lane);
             tile_compute<NB, RT, QLO>(ws, smem, Wb, tt, sc2, lane);
@@ -573,12 +666,14 @@ __global__ __launch_bounds__(256, (min_blocks<NB, RT>())) void decode_mfma(Decod
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) ws.lsum[rt][i] = row_sum16(ws.lsum[rt][i]);
+    const float ounit = pow2(ws.vsh);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int dt = 0; dt < 2 * NB; ++dt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ws.oacc[rt][dt][i] += __shfl(ws.macc[rt][i], 16 * q4 + dt / 2);
+            for (int i = 0; i < 4; ++i)
+                ws.oacc[rt][dt][i] = fmaf(ws.oacc[rt][dt][i], ounit, __shfl(ws.macc[rt][i], 16 * q4 + dt / 2));
 
     // ---- merge the four waves in a fixed order
     float* ml = reinterpret_cast<float*>(smem + LY::ML);

@@ -278,44 +278,72 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
     }
 
     // Q rows rt*16 + j16 as the B operand of S^T = K Q^T, read while the
-    // first tile's rows are in flight
+    // first tile's rows are in flight.  The wave's rows are divided by the
+    // power of two that puts their largest |q| in [2^14, 2^15) (dec::q_down;
+    // with dim halves the exponent covers both halves, so that their partial
+    // scores add up), which makes bf16 queries exact in fp16 at any
+    // magnitude; qup multiplies the scores back.
     h8 qh[RTW][NB], ql[RTW][NB];
+    constexpr int QW = QLO ? 8 : 4;          // words per lane and block: 8 fp32 or 8 bf16 values
+    uint32_t qw[RTW][NB][QW];
+    uint32_t mag = 0;
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
         const int r = rb + rt * 16 + j16;
         const bool real = r < R;
         const int t = real ? tq0 + r / p.hpk : 0, hh = real ? r % p.hpk : 0;
-        const size_t i0 = (((size_t)b * p.T + t) * p.H + g * p.hpk + hh) * HDR + half * HD + 8 * q4;
+        const size_t row0q = (((size_t)b * p.T + t) * p.H + g * p.hpk + hh) * HDR + 8 * q4;
 #pragma unroll
-        for (int blk = 0; blk < NB; ++blk) {
-            float qv[8];
+        for (int hf = 0; hf < DS; ++hf) {
+            // hf 0: this wave's dims; hf 1 (dim halves): the other half's,
+            // for the exponent only
 #pragma unroll
-            for (int e = 0; e < 8; ++e) qv[e] = 0.0f;
-            if (real) {
-                if (p.dtype == 1) {
-                    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + i0 + blk * 32);
-                    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+            for (int blk = 0; blk < NB; ++blk) {
+                uint32_t w[QW];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        qv[2 * e] = __uint_as_float(w4[e] << 16);
-                        qv[2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
+                for (int e = 0; e < QW; ++e) w[e] = 0u;
+                if (real) {
+                    const size_t i0 = row0q + (half ^ hf) * HD + blk * 32;
+                    if constexpr (QLO) {
+                        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const float*>(p.q) + i0);
+                        const uint4 a = src[0], c = src[1];
+                        const uint32_t w8[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+                        for (int e = 0; e < QW; ++e) w[e] = w8[e];
+                    } else {
+                        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + i0);
+                        w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
                     }
-                } else {
-                    const float* src = static_cast<const float*>(p.q) + i0 + blk * 32;
-                    const float4 a = *reinterpret_cast<const float4*>(src);
-                    const float4 c = *reinterpret_cast<const float4*>(src + 4);
-                    qv[0] = a.x; qv[1] = a.y; qv[2] = a.z; qv[3] = a.w;
-                    qv[4] = c.x; qv[5] = c.y; qv[6] = c.z; qv[7] = c.w;
                 }
-            }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const _Float16 xh = (_Float16)qv[e];
-                qh[rt][blk][e] = xh;
-                if (QLO) ql[rt][blk][e] = (_Float16)(qv[e] - (float)xh);
+                for (int e = 0; e < QW; ++e) {
+                    if (QLO) mag = max(mag, w[e] & 0x7FFFFFFFu);
+                    else mag = max(mag, max((w[e] << 16) & 0x7FFFFFFFu, w[e] & 0x7FFF0000u));
+                    if (hf == 0) qw[rt][blk][e] = w[e];
+                }
             }
         }
     }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) mag = max(mag, (uint32_t)__shfl_xor((int)mag, m));
+    const uint32_t qexp = __builtin_amdgcn_readfirstlane(dec::exp_of(mag));
+    const float qdown = dec::q_down(qexp), qup = dec::q_up(qexp);
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = QLO ? __uint_as_float(qw[rt][blk][e % QW])
+                                    : __uint_as_float((e & 1) ? (qw[rt][blk][e / 2] & 0xFFFF0000u) : (qw[rt][blk][e / 2] << 16));
+                const float x = v * qdown;
+                const _Float16 xh = (_Float16)x;
+                qh[rt][blk][e] = xh;
+                if (QLO) ql[rt][blk][e] = (_Float16)(x - (float)xh);
+            }
+    // E of dec::v_shift: the P V accumulators hold their sums in units of
+    // 2^-vsh (0 unless a tile held a V step of 2^7 or more)
+    int vsh = 0;
 
     for (int it = 0; it < mine; ++it) {
         const int t0 = first + it * rs * kTile;
@@ -450,6 +478,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
                     sv[rt][h][i] = x;
                     smax = fmaxf(smax, x);
                 }
+            smax *= qup;                           // the scores of the scaled query rows, times qup
             if (__any(smax > mrow[rt] + 8.0f)) {   // -inf never passes
                 float mt = fmaxf(smax, __shfl_xor(smax, 16));
                 mt = fmaxf(mt, __shfl_xor(mt, 32));
@@ -471,7 +500,9 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float pe = (mrow[rt] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sv[rt][h][i] - mrow[rt]);
+                    const float pe = (mrow[rt] == -INFINITY)
+                                         ? 0.0f
+                                         : __builtin_amdgcn_exp2f(fmaf(sv[rt][h][i], qup, -mrow[rt]));
                     pv[rt][h][i] = pe;
                     lsum[rt] += pe;
                 }
@@ -490,6 +521,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
             else wait_loads_upto<0>();
         }
         // ---- V steps and offsets of the tile (rows past c1 hold stale bytes)
+        float dmx = 0.0f;   // the largest step this lane converts
 #pragma unroll
         for (int x = 0; x < (SROWS * NB + 63) / 64; ++x) {
             const int u = x * 64 + lane;
@@ -497,11 +529,50 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
                 const int key = hrow + u / NB, blk = u - (u / NB) * NB;
                 const bool live = t0 + key < c1;
                 const uint32_t dm = *reinterpret_cast<const uint32_t*>(rv + key * WN::VSTR + blk * 24);
-                VDa[blk * kTile + key] = live ? f16_value((uint16_t)(dm & 0xFFFF)) : 0.0f;
+                const float dv = live ? f16_value((uint16_t)(dm & 0xFFFF)) : 0.0f;
+                VDa[blk * kTile + key] = dv;
+                dmx = fmaxf(dmx, dv);
                 VMa[key * WN::VMS + blk] = live ? (uint16_t)(dm >> 16) : (uint16_t)0;
             }
         }
-        if constexpr (SH) lds_barrier(); else dec::lds_order();
+        if constexpr (SH) {
+            lds_barrier();
+            // the other wave of the head converted the other 16 rows; both
+            // waves see every step and so take the same decisions below
+#pragma unroll
+            for (int x = 0; x < (16 * NB + 63) / 64; ++x) {
+                const int u = x * 64 + lane;
+                if (16 * NB % 64 == 0 || u < 16 * NB) dmx = fmaxf(dmx, VDa[(u - (u / NB) * NB) * kTile + (hrow ^ 16) + u / NB]);
+            }
+        } else {
+            dec::lds_order();
+        }
+        // A tile with a step of 2^7 or more: its steps are stored times
+        // 2^-vsh (dec::v_shift; each lane rescales the ones it converted) and
+        // the accumulators switch units.
+        const bool big = __any(dmx >= 128.0f);   // wave-uniform
+        if (big || vsh != 0) {
+            const int want = big ? __builtin_amdgcn_readfirstlane(dec::v_shift(dec::wave_max_dpp(dmx))) : 0;
+            if (want != vsh) {
+                const float f = dec::pow2(vsh - want);
+#pragma unroll
+                for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                    for (int dt = 0; dt < 2 * NB; ++dt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) oacc[rt][dt][i] *= f;
+                vsh = want;
+            }
+            if (vsh != 0) {
+                const float f = dec::pow2(-vsh);
+#pragma unroll
+                for (int x = 0; x < (SROWS * NB + 63) / 64; ++x) {
+                    const int u = x * 64 + lane;
+                    if (SROWS * NB % 64 == 0 || u < SROWS * NB) VDa[(u - (u / NB) * NB) * kTile + hrow + u / NB] *= f;
+                }
+                if constexpr (SH) lds_barrier(); else dec::lds_order();
+            }
+        }
 
         // ---- P V with the V codes built from the q5_1 bytes of 8 keys per lane group
 #pragma unroll
@@ -561,6 +632,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
         for (int it = mine; it < nit; ++it) __builtin_amdgcn_s_barrier();
 
     // ---- finish: row sums over the four lane groups; offsets into O
+    const float ounit = dec::pow2(24 + vsh);   // the code products carry 2^-24, P 2^-vsh
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
         float l = lsum[rt];
@@ -570,8 +642,8 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
 #pragma unroll
         for (int dt = 0; dt < 2 * NB; ++dt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)   // the code products carry a factor 2^-24
-                oacc[rt][dt][i] = fmaf(oacc[rt][dt][i], 0x1p24f, __shfl(macc[rt][i], 16 * q4 + dt / 2));
+            for (int i = 0; i < 4; ++i)
+                oacc[rt][dt][i] = fmaf(oacc[rt][dt][i], ounit, __shfl(macc[rt][i], 16 * q4 + dt / 2));
     }
     // ---- row streams: the other streams hand (m, l, O) to stream 0 through
     // their own LDS buffers (lane-major, so that the 64 lanes hit 64 banks);

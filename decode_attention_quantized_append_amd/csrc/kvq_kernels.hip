@@ -430,31 +430,48 @@ __global__ __launch_bounds__(256) void importance_kernel(ImportanceParams p) {
                 }
             }
         }
-        f4 sv = {0.f, 0.f, 0.f, 0.f};
+        // the query row (this lane's 8 dims of each block; the row's other
+        // dims are with lanes j16 + 16, + 32, + 48) divided by the power of
+        // two that puts its largest |q| in [2^14, 2^15) (dec::q_down), so that
+        // bf16 queries are exact in fp16 at any magnitude
+        float qv[8][8];
+        uint32_t mag = 0;
 #pragma unroll
         for (int blk = 0; blk < 8; ++blk) {
             if (blk < nb) {
-                float qv[8];
                 if constexpr (!F32) {   // 8 bf16 values, 16 bytes
                     const uint32_t w4[4] = {qw[blk][0].x, qw[blk][0].y, qw[blk][0].z, qw[blk][0].w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        qv[2 * e] = __uint_as_float(w4[e] << 16);
-                        qv[2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
+                        qv[blk][2 * e] = __uint_as_float(w4[e] << 16);
+                        qv[blk][2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
                     }
                 } else {
                     const uint32_t w8[8] = {qw[blk][0].x, qw[blk][0].y, qw[blk][0].z, qw[blk][0].w,
                                             qw[blk][1].x, qw[blk][1].y, qw[blk][1].z, qw[blk][1].w};
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) qv[e] = __uint_as_float(w8[e]);
+                    for (int e = 0; e < 8; ++e) qv[blk][e] = __uint_as_float(w8[e]);
                 }
 #pragma unroll
-                for (int e = 0; e < 8; ++e) qv[e] = real ? qv[e] : 0.0f;
+                for (int e = 0; e < 8; ++e) {
+                    qv[blk][e] = real ? qv[blk][e] : 0.0f;
+                    mag = max(mag, __float_as_uint(qv[blk][e]) & 0x7FFFFFFFu);
+                }
+            }
+        }
+        mag = max(mag, (uint32_t)__shfl_xor((int)mag, 16));
+        mag = max(mag, (uint32_t)__shfl_xor((int)mag, 32));
+        const float down = dec::q_down(dec::exp_of(mag));
+        f4 sv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) {
+            if (blk < nb) {
                 h8 qh, ql;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    qh[e] = (_Float16)qv[e];
-                    ql[e] = (_Float16)(qv[e] - (float)qh[e]);
+                    const float x = qv[blk][e] * down;
+                    qh[e] = (_Float16)x;
+                    ql[e] = (_Float16)(x - (float)qh[e]);
                 }
                 f4 d = dec::mfma(kf[blk], qh, (f4){0.f, 0.f, 0.f, 0.f});
                 if constexpr (F32) d = dec::mfma(kf[blk], ql, d);   // fp32 queries: the low part too
@@ -462,13 +479,14 @@ __global__ __launch_bounds__(256) void importance_kernel(ImportanceParams p) {
                 for (int i = 0; i < 4; ++i) sv[i] = fmaf(dk[blk][i], d[i], sv[i]);
             }
         }
+        const float up = dec::q_up(dec::exp_of(mag));
         const float l = real ? lraw : 0.0f;
         const int upto = len - p.T + t + 1;
         const int first = p.window > 0 ? max(0, upto - p.window) : 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int key = k0 + 4 * q4 + i;
-            float pr = (real && key >= first && key < upto) ? expf(p.scale * sv[i] - l) : 0.0f;
+            float pr = (real && key >= first && key < upto) ? expf(p.scale * (sv[i] * up) - l) : 0.0f;
             pr += __shfl_xor(pr, 1);
             pr += __shfl_xor(pr, 2);
             pr += __shfl_xor(pr, 4);

@@ -188,8 +188,15 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache* h, int32_t T, size_t* byt
  * many rows): decode workgroups take the rows in groups of 32/(H/Hkv) (the
  * launch's y index), and one combine folds all T rows; the workspace holds
  * the partials of all T rows.
- * fp32 queries are used to about 2^-22 relative precision (fp16 hi + lo
- * parts); bf16 queries exactly while |q| < 65504 and |q| >= 2^-14 (fp16 range).
+ * Input range: any finite queries and any q8_0 / q5_1 blocks (fp16 steps,
+ * offsets and K scales up to 65504), as long as the scores scale * <q, k>
+ * and the weighted V sums stay within binary32 range.  Query rows are
+ * divided by a power of two before their fp16 cast (exact, so bf16 queries
+ * keep every bit; fp32 queries keep about 22 bits as an fp16 high and low
+ * part), and V steps of 2^7 or more switch the P V accumulator to units of
+ * a power of two, so nothing overflows fp16.  The softmax weights enter
+ * P V as fp16 (relative error 2^-11 each), so an output is within about
+ * 2^-11 sum_j p_j |v_j| / sum_j p_j of the exact one.
  * Errors: EINVAL, ERANGE (a visible row was rebased away), EDEVICE. */
 kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T,
                       const float* sinks, float scale, float* out, float* lse,
@@ -206,7 +213,10 @@ kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T,
  * rebase moves K and V rows, not importance).  Call it before the cache
  * changes again.  One launch; the rows of a session are split over
  * workgroups, each adding to its own rows only; in graph mode the grid
- * covers every length the plane allows, like kvq_decode's.
+ * covers every length the plane allows, like kvq_decode's.  Queries of any
+ * finite magnitude are taken as kvq_decode takes them; each probability is
+ * exp of a binary32 score less the lse, so its relative error grows with
+ * the score's magnitude (about 1e-2 at |score| near 1e5, 1e-4 near 1e3).
  * Errors: EINVAL, ERANGE (a visible row was rebased away), EDEVICE. */
 kvq_status kvq_importance(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, float scale,
                           const float* lse, float* imp, kvq_stream stream);

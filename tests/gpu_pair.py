@@ -24,14 +24,15 @@ def to_dev(x: np.ndarray, io: str):
     return t.to(DEV)
 
 
-def assert_close(got, want, what=""):
+def assert_close(got, want, what="", atol=ATOL):
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
     assert got.shape == want.shape
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
     err = np.abs(got - want)
-    bad = err > ATOL + RTOL * np.abs(want)
+    bad = err > atol + RTOL * np.abs(want)
     if bad.any():
-        i = np.unravel_index(np.argmax(err - (ATOL + RTOL * np.abs(want))), err.shape)
+        i = np.unravel_index(np.argmax(err - (atol + RTOL * np.abs(want))), err.shape)
         raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; worst at {i}: "
                              f"gpu {got[i]!r} oracle {want[i]!r}; max abs err {err.max():.3e}")
     return float(err.max())
@@ -90,7 +91,7 @@ class Pair:
                         f"{name} bytes differ: session {b}, physical row {sel[i]}, blocks {blks.tolist()}; "
                         f"block {j}: gpu {bytes(gb[j]).hex(' ')} oracle {bytes(rb[j]).hex(' ')}")
 
-    def decode(self, q, scale, sinks=None, sel=None, what="decode"):
+    def decode(self, q, scale, sinks=None, sel=None, what="decode", atol=ATOL):
         T = q.shape[1]
         s_dev = torch.from_numpy(sinks).to(DEV) if sinks is not None else None
         out, lse = self.gpu.decode(to_dev(q, self.io), scale, sinks=s_dev)
@@ -102,7 +103,7 @@ class Pair:
             got = got.reshape(-1, self.hd)[flat]
             want = want.reshape(-1, self.hd)[flat]
             got_lse, want_lse = got_lse.reshape(-1)[flat], want_lse.reshape(-1)[flat]
-        e = assert_close(got, want, what + " out")
+        e = assert_close(got, want, what + " out", atol)
         assert_close(got_lse, want_lse, what + " lse")
         assert T == q.shape[1]
         return e
