@@ -1,5 +1,6 @@
-"""Build the HIP library (libkvq.so, gfx950) and its CPU twin for host-logic
-tests (libkvq_nodev.so), in-tree next to the sources.
+"""Build the HIP library (libkvq.so, gfx950), its CPU twin for host-logic
+tests (libkvq_nodev.so) and the benchmark's streaming-read probe
+(libkvq_probe.so), in-tree next to the sources.
 
     python -m decode_attention_quantized_append_amd.build
 """
@@ -15,6 +16,7 @@ ROOT = os.path.dirname(PKG)
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvq.so")
 LIB_NODEV = os.path.join(PKG, "libkvq_nodev.so")
+LIB_PROBE = os.path.join(PKG, "libkvq_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -47,8 +49,15 @@ def build_nodev(verbose: bool = True) -> str:
     return LIB_NODEV
 
 
+def build_probe(verbose: bool = True) -> str:
+    tmp = LIB_PROBE + ".tmp"
+    _run([HIPCC, *HIP_FLAGS, "-shared", "-o", tmp, os.path.join(CSRC, "kvq_probe.hip")], verbose)
+    os.replace(tmp, LIB_PROBE)
+    return LIB_PROBE
+
+
 def build_all(verbose: bool = True):
-    return build_hip(verbose), build_nodev(verbose)
+    return build_hip(verbose), build_nodev(verbose), build_probe(verbose)
 
 
 if __name__ == "__main__":

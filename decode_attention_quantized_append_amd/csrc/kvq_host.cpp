@@ -37,6 +37,7 @@ struct kvq_cache {
     int32_t sub_tiles;           // stream kernel: waves per KV head (0: chosen per call)
     int32_t graph_mode;          // plan decodes for every session's largest span
     int32_t cus;                 // compute units of the device the handle was created on
+    void* trace[3];              // events kvq_decode records around its kernels (or null)
 };
 
 namespace {
@@ -389,6 +390,7 @@ kvq_status kvq_create(const kvq_config* cfg, void* k_planes, void* v_planes,
     h->head_group = 0;
     h->sub_tiles = 0;
     h->graph_mode = 0;
+    h->trace[0] = h->trace[1] = h->trace[2] = nullptr;
     // the split plan sizes one round of workgroups to the device's CUs
     h->cus = kvq::device_compute_units();
     if (h->cus <= 0) {
@@ -594,7 +596,7 @@ kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, c
     // folds all T rows
     dp.Tg = std::min(T, kvq::kMaxRows / hpk);
     const char* err = nullptr;
-    if (kvq::launch_decode(dp, stream, &err)) return fail(KVQ_EDEVICE, err ? err : "decode launch failed");
+    if (kvq::launch_decode(dp, stream, h->trace, &err)) return fail(KVQ_EDEVICE, err ? err : "decode launch failed");
     return KVQ_OK;
 }
 
@@ -727,6 +729,15 @@ kvq_status kvq_host_lengths(const kvq_cache* h, int64_t* len, int64_t* base) {
         if (len) len[b] = h->len[b];
         if (base) base[b] = h->base[b];
     }
+    return KVQ_OK;
+}
+
+kvq_status kvq_set_trace_events(kvq_cache* h, void* before_partials, void* before_combine,
+                                void* after_combine) {
+    if (!h) return fail(KVQ_EINVAL, "handle is NULL");
+    h->trace[0] = before_partials;
+    h->trace[1] = before_combine;
+    h->trace[2] = after_combine;
     return KVQ_OK;
 }
 

@@ -186,7 +186,9 @@ int device_compute_units();
 int launch_append(const AppendParams& p, void* stream, const char** err);
 int launch_set(const SetParams& p, void* stream, const char** err);
 int launch_move(const MoveParams& p, void* stream, const char** err);
-int launch_decode(const DecodeParams& p, void* stream, const char** err);
+// ev[0..2] (hipEvent_t or null): recorded on the stream before the partials
+// kernel, between it and the combine, and after the combine.
+int launch_decode(const DecodeParams& p, void* stream, void* const ev[3], const char** err);
 int launch_importance(const ImportanceParams& p, void* stream, const char** err);
 
 }  // namespace kvq

@@ -759,10 +759,19 @@ int launch_importance(const ImportanceParams& p, void* stream, const char** err)
     return check(err);
 }
 
-int launch_decode(const DecodeParams& p, void* stream, const char** err) {
+int launch_decode(const DecodeParams& p, void* stream, void* const ev[3], const char** err) {
     hipStream_t st = (hipStream_t)stream;
-    if (launch_partials(p, st, err)) return 1;
-    return launch_combine(p, st, err);
+    auto mark = [&](int i) {
+        if (!ev[i]) return 0;
+        const hipError_t e = hipEventRecord((hipEvent_t)ev[i], st);
+        if (e != hipSuccess) {
+            *err = hipGetErrorString(e);
+            return 1;
+        }
+        return 0;
+    };
+    if (mark(0) || launch_partials(p, st, err) || mark(1) || launch_combine(p, st, err)) return 1;
+    return mark(2);
 }
 
 }  // namespace kvq

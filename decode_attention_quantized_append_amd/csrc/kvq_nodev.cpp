@@ -51,8 +51,8 @@ int launch_append(const AppendParams& p, void*, const char** err) {
     return record(s, err);
 }
 
-int launch_decode(const DecodeParams& p, void*, const char** err) {
-    std::string s = "decode T=" + std::to_string(p.T) + " chunk=" + std::to_string(p.chunk) +
+int launch_decode(const DecodeParams& p, void*, void* const ev[3], const char** err) {
+    std::string s = std::string(ev[0] || ev[1] || ev[2] ? "traced " : "") + "decode T=" + std::to_string(p.T) + " chunk=" + std::to_string(p.chunk) +
                     " splits=" + std::to_string(p.splits) + " ml_to_o=" +
                     std::to_string((const char*)p.part_o - (const char*)p.part_ml) +
                     " kernel=" + std::to_string(p.kernel) + " gh=" + std::to_string(p.gh) +

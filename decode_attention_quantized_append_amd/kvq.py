@@ -29,7 +29,7 @@ STATUS_NAMES = {0: "KVQ_OK", 1: "KVQ_EINVAL", 2: "KVQ_ECAPACITY", 3: "KVQ_ERANGE
 EXPORTS = ("kvq_required_bytes", "kvq_create", "kvq_append", "kvq_decode_workspace_bytes",
            "kvq_decode", "kvq_truncate", "kvq_set_split_rows", "kvq_set_decode_tiling", "kvq_info",
            "kvq_host_lengths", "kvq_set_graph_mode", "kvq_set_host_lengths", "kvq_importance",
-           "kvq_rollback", "kvq_destroy", "kvq_last_error")
+           "kvq_rollback", "kvq_set_trace_events", "kvq_destroy", "kvq_last_error")
 
 
 class kvq_config(ctypes.Structure):
@@ -77,6 +77,7 @@ def _declare(lib):
         "kvq_info": (st, [vp, ctypes.POINTER(kvq_info_t)]),
         "kvq_host_lengths": (st, [vp, i64p, i64p]),
         "kvq_set_graph_mode": (st, [vp, i32]),
+        "kvq_set_trace_events": (st, [vp, vp, vp, vp]),
         "kvq_importance": (st, [vp, vp, i32, i32, f32, vp, vp, vp]),
         "kvq_set_host_lengths": (st, [vp, i64p, i64p]),
         "kvq_destroy": (None, [vp]),
@@ -201,6 +202,13 @@ def kvq_host_lengths(h: int, n_seqs: int, lib=None):
     bs = (ctypes.c_int64 * n_seqs)()
     _check(lib, lib.kvq_host_lengths(h, ln, bs))
     return list(ln), list(bs)
+
+
+def kvq_set_trace_events(h: int, before_partials: Optional[int], before_combine: Optional[int],
+                         after_combine: Optional[int], lib=None) -> None:
+    lib = lib or load()
+    _check(lib, lib.kvq_set_trace_events(h, before_partials or None, before_combine or None,
+                                         after_combine or None))
 
 
 def kvq_set_graph_mode(h: int, on: bool, lib=None) -> None:

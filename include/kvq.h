@@ -304,6 +304,18 @@ kvq_status kvq_host_lengths(const kvq_cache* h, int64_t* len, int64_t* base);
  * host mirror back in step.  Off (0) by default.  Errors: EINVAL. */
 kvq_status kvq_set_graph_mode(kvq_cache* h, int32_t on);
 
+/* Instrumentation: events (hipEvent_t, created by the caller; NULL = none)
+ * that every later kvq_decode on this handle records on its stream: before
+ * the split-K partials kernel, between it and the log-sum-exp combine, and
+ * after the combine, so that a caller can time each kernel of the call
+ * with hipEventElapsedTime.  All three NULL (the default) records nothing.
+ * The events are recorded into a graph that captures the call.  No passage
+ * defines it; it exists so that the kernels' durations can be measured
+ * without a profiler.
+ * Errors: EINVAL (NULL handle). */
+kvq_status kvq_set_trace_events(kvq_cache* h, void* before_partials, void* before_combine,
+                                void* after_combine);
+
 /* Sets the host mirror of len and base (HOST arrays of n_seqs entries), for
  * example to the device counters read back after graph replays (memra-engine
  * "Struct KvLayer" page, len_d: the host len and the device counter are kept

@@ -67,6 +67,8 @@ def load(path: str | None = None):
         f32p, ctypes.POINTER(u8p), i64p, i64p, ctypes.c_int32, f32p, ctypes.c_float, f64p, ctypes.c_int64]
     lib.kvqo_importance.restype = ctypes.c_int
     lib.kvqo_max_threads.restype = ctypes.c_int
+    lib.kvqo_set_threads.argtypes = [ctypes.c_int]
+    lib.kvqo_set_threads.restype = None
     if path is None:
         _lib = lib
     return lib
@@ -228,3 +230,8 @@ def importance(q, k_planes, base, length, capacity, *, n_kv_heads, window=0, sin
 
 def max_threads(lib=None) -> int:
     return int((lib or load()).kvqo_max_threads())
+
+
+def set_threads(n: int, lib=None) -> None:
+    """Threads the oracle's attention loops use from now on."""
+    (lib or load()).kvqo_set_threads(int(n))

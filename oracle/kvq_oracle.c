@@ -452,3 +452,13 @@ int kvqo_max_threads(void) {
     return 1;
 #endif
 }
+
+/* Threads the attention loops use from now on (n >= 1); for timing the
+ * oracle on one thread and on all of them. */
+void kvqo_set_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

@@ -84,13 +84,19 @@ int kvqo_attention(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t hd,
                    const int64_t* sel, int64_t n_sel,
                    float* out, float* lse);
 
-/* Threads the attention loop may use (OpenMP), for reporting. */
+/* Attention importance: adds to imp[b * cap + (row - base[b])], for every
+ * row a query row sees, that row's softmax probability (sink in the
+ * denominator), summed over the T query rows and H heads.  Returns 0 or -1
+ * as kvqo_attention. */
 int kvqo_importance(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t hd,
                     const float* q, const uint8_t* const* k_plane,
                     const int64_t* base, const int64_t* len, int32_t window,
                     const float* sinks, float scale, double* imp, int64_t cap);
 
+/* Threads the attention loops may use (OpenMP), for reporting. */
 int kvqo_max_threads(void);
+/* Threads the attention loops use from now on (n >= 1). */
+void kvqo_set_threads(int n);
 
 #ifdef __cplusplus
 }

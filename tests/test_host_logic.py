@@ -528,3 +528,24 @@ def test_plan_follows_the_device_compute_units(lib):
         assert lib.kvq_create(ctypes.byref(cfg), K, V, C, None, ctypes.byref(out)) == kvq.KVQ_EDEVICE
     finally:
         lib.kvq_nodev_set_cus(256)
+
+
+def test_trace_events_are_recorded_around_the_decode_kernels(lib):
+    """kvq_set_trace_events: later decodes record the caller's events (the
+    recording launcher marks such a launch), NULL stops it; nothing else
+    changes."""
+    h = create(lib, n_seqs=1, n_q_heads=8, n_kv_heads=2, head_dim=64, capacity=300)
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 100, None, 0, lib)
+    lib.kvq_nodev_clear()
+    kvq.kvq_decode(h, Q, kvq.KVQ_BF16, 1, None, 0.1, O, None, WS, 1 << 40, 0, lib)
+    plain = log(lib)[0]
+    kvq.kvq_set_trace_events(h, 0x1000, 0x2000, 0x3000, lib)
+    lib.kvq_nodev_clear()
+    kvq.kvq_decode(h, Q, kvq.KVQ_BF16, 1, None, 0.1, O, None, WS, 1 << 40, 0, lib)
+    (traced,) = log(lib)
+    assert traced == "traced " + plain
+    kvq.kvq_set_trace_events(h, None, None, None, lib)
+    lib.kvq_nodev_clear()
+    kvq.kvq_decode(h, Q, kvq.KVQ_BF16, 1, None, 0.1, O, None, WS, 1 << 40, 0, lib)
+    assert log(lib) == [plain]
+    assert err(lib, kvq.kvq_set_trace_events, None, None, None, None) == kvq.KVQ_EINVAL
