@@ -38,6 +38,7 @@ struct kvq_cache {
     int32_t graph_mode;          // plan decodes for every session's largest span
     int32_t cus;                 // compute units of the device the handle was created on
     void* trace[3];              // events kvq_decode records around its kernels (or null)
+    void* scratch;               // the library's device scratch on the handle's device
 };
 
 namespace {
@@ -355,6 +356,79 @@ Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nul
     return p;
 }
 
+// kvq_decode and kvq_decode_noalloc: the partials go to the caller's
+// workspace ws, or (ws == nullptr with use_scratch) to the library's scratch.
+kvq_status decode_impl(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, const float* sinks, float scale,
+                       float* out, float* lse, void* ws, size_t ws_bytes, kvq_stream stream, bool use_scratch) {
+    if (!h) return fail(KVQ_EINVAL, "handle is NULL");
+    if (!q || !out) return fail(KVQ_EINVAL, "q or out is NULL");
+    if (dtype != KVQ_F32 && dtype != KVQ_BF16) return fail(KVQ_EINVAL, "dtype must be F32 or BF16");
+    if (!std::isfinite(scale)) return fail(KVQ_EINVAL, "scale must be finite");
+    const kvq_config& c = h->cfg;
+    const int hpk = c.n_q_heads / c.n_kv_heads;
+    if (T < 1) return fail(KVQ_EINVAL, "T must be >= 1");
+    if (hpk > kvq::kMaxRows) return fail(KVQ_EINVAL, "need n_q_heads / n_kv_heads <= 32");
+    for (int b = 0; b < c.n_seqs; ++b) {
+        if (h->len[b] < T)
+            return fail(KVQ_EINVAL, "session " + std::to_string(b) + " holds fewer than T rows");
+        if (visible_lo(h, h->len[b], T) < h->base[b])
+            return fail(KVQ_ERANGE, "session " + std::to_string(b) + ": visible rows were rebased away");
+    }
+    bool fits = true;
+    Plan p = make_plan(h, T, dtype == KVQ_F32, &fits);
+    if (!fits) return fail(KVQ_EINVAL, "the decode tiling set with kvq_set_decode_tiling does not fit this shape");
+    if (use_scratch) {
+        if (p.ml_bytes + p.o_bytes > kvq::kScratchBytes)
+            return fail(KVQ_ECAPACITY, "the decode partials of this call need " +
+                                           std::to_string(p.ml_bytes + p.o_bytes) +
+                                           " bytes; the library's scratch holds " +
+                                           std::to_string(kvq::kScratchBytes) + " (use kvq_decode with a workspace)");
+        ws = h->scratch;
+        ws_bytes = kvq::kScratchBytes;
+    }
+    if (!ws || ws_bytes < p.ml_bytes + p.o_bytes) return fail(KVQ_EINVAL, "workspace missing or too small");
+    if (!aligned(ws, 256)) return fail(KVQ_EINVAL, "workspace must be 256-byte aligned");
+    kvq::DecodeParams dp{};
+    dp.q = q;
+    dp.dtype = dtype;
+    dp.B = c.n_seqs;
+    dp.T = T;
+    dp.H = c.n_q_heads;
+    dp.Hkv = c.n_kv_heads;
+    dp.hd = c.head_dim;
+    dp.hpk = hpk;
+    dp.window = c.window;
+    dp.k_planes = h->k;
+    dp.v_planes = h->v;
+    dp.k_stride = (int64_t)h->sz.k_session_stride;
+    dp.v_stride = (int64_t)h->sz.v_session_stride;
+    dp.k_row = (int32_t)h->sz.k_row_bytes;
+    dp.v_row = (int32_t)h->sz.v_row_bytes;
+    dp.len_d = len_d(h);
+    dp.base_d = base_d(h);
+    dp.chunk = p.chunk;
+    dp.splits = p.splits;
+    dp.units = p.units;
+    dp.kernel = p.kernel;
+    dp.gh = p.gh;
+    dp.rs = p.rs;
+    dp.rg = p.rg;
+    dp.ds = p.kernel == kvq::kStream ? p.ds : 1;
+    dp.lds = p.lds;
+    dp.scale = scale;
+    dp.part_ml = static_cast<float*>(ws);
+    dp.part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + p.ml_bytes);
+    dp.sinks = sinks;
+    dp.out = out;
+    dp.lse = lse;
+    // workgroups take groups of at most 32 / hpk query rows; the combine
+    // folds all T rows
+    dp.Tg = std::min(T, kvq::kMaxRows / hpk);
+    const char* err = nullptr;
+    if (kvq::launch_decode(dp, stream, h->trace, &err)) return fail(KVQ_EDEVICE, err ? err : "decode launch failed");
+    return KVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -396,6 +470,16 @@ kvq_status kvq_create(const kvq_config* cfg, void* k_planes, void* v_planes,
     if (h->cus <= 0) {
         delete h;
         return fail(KVQ_EDEVICE, "cannot read the compute-unit count of the current device");
+    }
+    // the device address of the library's scratch (kvq_decode_noalloc),
+    // looked up once per device
+    {
+        const char* err = nullptr;
+        if (kvq::scratch_region(&h->scratch, &err)) {
+            delete h;
+            return fail(KVQ_EDEVICE, std::string("cannot locate the library's device scratch: ") +
+                                         (err ? err : "unknown error"));
+        }
     }
     int n = 2 * cfg->n_seqs + 4;
     std::vector<int32_t> idx(n), val(n, 0);
@@ -540,64 +624,12 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache* h, int32_t T, size_t* byt
 kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, const float* sinks,
                       float scale, float* out, float* lse, void* ws, size_t ws_bytes,
                       kvq_stream stream) {
-    if (!h) return fail(KVQ_EINVAL, "handle is NULL");
-    if (!q || !out) return fail(KVQ_EINVAL, "q or out is NULL");
-    if (dtype != KVQ_F32 && dtype != KVQ_BF16) return fail(KVQ_EINVAL, "dtype must be F32 or BF16");
-    if (!std::isfinite(scale)) return fail(KVQ_EINVAL, "scale must be finite");
-    const kvq_config& c = h->cfg;
-    const int hpk = c.n_q_heads / c.n_kv_heads;
-    if (T < 1) return fail(KVQ_EINVAL, "T must be >= 1");
-    if (hpk > kvq::kMaxRows) return fail(KVQ_EINVAL, "need n_q_heads / n_kv_heads <= 32");
-    for (int b = 0; b < c.n_seqs; ++b) {
-        if (h->len[b] < T)
-            return fail(KVQ_EINVAL, "session " + std::to_string(b) + " holds fewer than T rows");
-        if (visible_lo(h, h->len[b], T) < h->base[b])
-            return fail(KVQ_ERANGE, "session " + std::to_string(b) + ": visible rows were rebased away");
-    }
-    bool fits = true;
-    Plan p = make_plan(h, T, dtype == KVQ_F32, &fits);
-    if (!fits) return fail(KVQ_EINVAL, "the decode tiling set with kvq_set_decode_tiling does not fit this shape");
-    if (!ws || ws_bytes < p.ml_bytes + p.o_bytes) return fail(KVQ_EINVAL, "workspace missing or too small");
-    if (!aligned(ws, 256)) return fail(KVQ_EINVAL, "workspace must be 256-byte aligned");
-    kvq::DecodeParams dp{};
-    dp.q = q;
-    dp.dtype = dtype;
-    dp.B = c.n_seqs;
-    dp.T = T;
-    dp.H = c.n_q_heads;
-    dp.Hkv = c.n_kv_heads;
-    dp.hd = c.head_dim;
-    dp.hpk = hpk;
-    dp.window = c.window;
-    dp.k_planes = h->k;
-    dp.v_planes = h->v;
-    dp.k_stride = (int64_t)h->sz.k_session_stride;
-    dp.v_stride = (int64_t)h->sz.v_session_stride;
-    dp.k_row = (int32_t)h->sz.k_row_bytes;
-    dp.v_row = (int32_t)h->sz.v_row_bytes;
-    dp.len_d = len_d(h);
-    dp.base_d = base_d(h);
-    dp.chunk = p.chunk;
-    dp.splits = p.splits;
-    dp.units = p.units;
-    dp.kernel = p.kernel;
-    dp.gh = p.gh;
-    dp.rs = p.rs;
-    dp.rg = p.rg;
-    dp.ds = p.kernel == kvq::kStream ? p.ds : 1;
-    dp.lds = p.lds;
-    dp.scale = scale;
-    dp.part_ml = static_cast<float*>(ws);
-    dp.part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + p.ml_bytes);
-    dp.sinks = sinks;
-    dp.out = out;
-    dp.lse = lse;
-    // workgroups take groups of at most 32 / hpk query rows; the combine
-    // folds all T rows
-    dp.Tg = std::min(T, kvq::kMaxRows / hpk);
-    const char* err = nullptr;
-    if (kvq::launch_decode(dp, stream, h->trace, &err)) return fail(KVQ_EDEVICE, err ? err : "decode launch failed");
-    return KVQ_OK;
+    return decode_impl(h, q, dtype, T, sinks, scale, out, lse, ws, ws_bytes, stream, false);
+}
+
+kvq_status kvq_decode_noalloc(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, const float* sinks,
+                              float scale, float* out, float* lse, kvq_stream stream) {
+    return decode_impl(h, q, dtype, T, sinks, scale, out, lse, nullptr, 0, stream, true);
 }
 
 kvq_status kvq_importance(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, float scale,

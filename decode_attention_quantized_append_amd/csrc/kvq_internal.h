@@ -182,6 +182,12 @@ struct DecodeParams {
 // Compute units of the current device (0 if it cannot be read).
 int device_compute_units();
 
+// The library's device scratch for kvq_decode_noalloc: a file-scope device
+// array of kScratchBytes per device.  Fills *ptr with its address on the
+// current device (looked up once per device, then cached).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+int scratch_region(void** ptr, const char** err);
+
 // Launchers: return 0 on success, nonzero with a message in *err otherwise.
 int launch_append(const AppendParams& p, void* stream, const char** err);
 int launch_set(const SetParams& p, void* stream, const char** err);

@@ -23,8 +23,15 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "kvq_internal.h"
+
+// Device scratch of kvq_decode_noalloc (the split-K partials of one call),
+// one copy per device, held until the process ends.  Host code never uses
+// this name as an address: kvq::scratch_region looks the device address up
+// with hipGetSymbolAddress once per device and every launch takes that.
+static __device__ __align__(256) uint8_t scratch[kvq::kScratchBytes];
 
 namespace kvq {
 namespace {
@@ -676,6 +683,32 @@ int launch_decode_nb(const DecodeParams& p, hipStream_t st, const char** err) {
 }
 
 }  // namespace
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int scratch_region(void** ptr, const char** err) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *err = "cannot tell the current device";
+        return 1;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            *err = e != hipSuccess ? hipGetErrorString(e) : "the scratch symbol has no device address";
+            return 1;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return 0;
+}
 
 int device_compute_units() {
     int dev = 0, n = 0;

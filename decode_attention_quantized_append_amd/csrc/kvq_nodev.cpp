@@ -31,6 +31,13 @@ namespace kvq {
 
 int device_compute_units() { return g_cus; }
 
+// A stand-in address for the scratch region (nothing is ever written there:
+// launches are only recorded).
+int scratch_region(void** ptr, const char**) {
+    *ptr = reinterpret_cast<void*>(uintptr_t(0x5C0000000000ull));
+    return 0;
+}
+
 int launch_set(const SetParams& p, void*, const char** err) {
     std::string s = p.add ? "add" : "set";
     for (int i = 0; i < p.n; ++i) s += " " + std::to_string(p.idx[i]) + "=" + std::to_string(p.val[i]);

@@ -27,7 +27,7 @@ STATUS_NAMES = {0: "KVQ_OK", 1: "KVQ_EINVAL", 2: "KVQ_ECAPACITY", 3: "KVQ_ERANGE
 
 # Every entry point the header declares.
 EXPORTS = ("kvq_required_bytes", "kvq_create", "kvq_append", "kvq_decode_workspace_bytes",
-           "kvq_decode", "kvq_truncate", "kvq_set_split_rows", "kvq_set_decode_tiling", "kvq_info",
+           "kvq_decode", "kvq_decode_noalloc", "kvq_truncate", "kvq_set_split_rows", "kvq_set_decode_tiling", "kvq_info",
            "kvq_host_lengths", "kvq_set_graph_mode", "kvq_set_host_lengths", "kvq_importance",
            "kvq_rollback", "kvq_set_trace_events", "kvq_destroy", "kvq_last_error")
 
@@ -70,6 +70,7 @@ def _declare(lib):
         "kvq_append": (st, [vp, vp, vp, i32, i32, i32p, vp]),
         "kvq_decode_workspace_bytes": (st, [vp, i32, ctypes.POINTER(ctypes.c_size_t)]),
         "kvq_decode": (st, [vp, vp, i32, i32, vp, f32, vp, vp, vp, ctypes.c_size_t, vp]),
+        "kvq_decode_noalloc": (st, [vp, vp, i32, i32, vp, f32, vp, vp, vp]),
         "kvq_truncate": (st, [vp, i32p, vp]),
         "kvq_rollback": (st, [vp, i32p, vp]),
         "kvq_set_split_rows": (st, [vp, i32]),
@@ -172,6 +173,13 @@ def kvq_decode(h: int, q: int, dtype: int, T: int, sinks: Optional[int], scale: 
     lib = lib or load()
     _check(lib, lib.kvq_decode(h, q, dtype, T, sinks or None, scale, out, lse or None, ws,
                                ws_bytes, stream or None))
+
+
+def kvq_decode_noalloc(h: int, q: int, dtype: int, T: int, sinks: Optional[int], scale: float, out: int,
+                       lse: Optional[int], stream: int = 0, lib=None) -> None:
+    lib = lib or load()
+    _check(lib, lib.kvq_decode_noalloc(h, q, dtype, T, sinks or None, scale, out, lse or None,
+                                       stream or None))
 
 
 def kvq_truncate(h: int, new_len: Sequence[int], stream: int = 0, lib=None) -> None:

@@ -202,6 +202,26 @@ kvq_status kvq_decode(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T,
                       const float* sinks, float scale, float* out, float* lse,
                       void* ws, size_t ws_bytes, kvq_stream stream);
 
+/* kvq_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation): the split-K partials go to the library's own
+ * device scratch, a file-scope device array of 64 MiB (67108864 bytes) per
+ * device, held from the library's load until the process ends.  Its device
+ * address is looked up once per device by kvq_create; this call allocates
+ * nothing and frees nothing.  Same arguments, semantics and errors as
+ * kvq_decode otherwise, plus ECAPACITY when the call's partials (the bytes
+ * kvq_decode_workspace_bytes reports for T) exceed 64 MiB; then nothing is
+ * enqueued.  Every call on one device shares that device's scratch and
+ * leaves its partials there: two calls whose executions overlap on one
+ * device (on different streams, or from different threads without
+ * ordering) race and give wrong results; calls ordered on one stream are
+ * safe.  Nothing in the scratch needs to start at zero (each call writes
+ * every partial its combine reads).
+ * Errors: EINVAL, ERANGE, ECAPACITY, EDEVICE. */
+kvq_status kvq_decode_noalloc(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T,
+                              const float* sinks, float scale, float* out, float* lse,
+                              kvq_stream stream);
+
 /* Attention importance (cortiq LayerKvCache attend_group's imp_acc and
  * accumulate_imp: the attention mass each stored row receives, summed over
  * heads).  For the q, dtype, T and scale of a kvq_decode call, and the lse it

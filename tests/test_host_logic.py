@@ -549,3 +549,27 @@ def test_trace_events_are_recorded_around_the_decode_kernels(lib):
     kvq.kvq_decode(h, Q, kvq.KVQ_BF16, 1, None, 0.1, O, None, WS, 1 << 40, 0, lib)
     assert log(lib) == [plain]
     assert err(lib, kvq.kvq_set_trace_events, None, None, None, None) == kvq.KVQ_EINVAL
+
+
+def test_decode_noalloc_uses_the_scratch_and_refuses_what_does_not_fit(lib):
+    """kvq_decode_noalloc plans like kvq_decode and puts the partials in the
+    library's scratch (the recording launcher's stand-in address); a plan
+    whose partials exceed the 64 MiB scratch is refused with ECAPACITY and
+    enqueues nothing."""
+    h = create(lib, n_seqs=1, n_q_heads=32, n_kv_heads=8, head_dim=128, capacity=9000)
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 8192, None, 0, lib)
+    lib.kvq_nodev_clear()
+    kvq.kvq_decode(h, Q, kvq.KVQ_BF16, 1, None, 0.1, O, None, WS, 1 << 40, 0, lib)
+    with_ws = log(lib)[0]
+    lib.kvq_nodev_clear()
+    kvq.kvq_decode_noalloc(h, Q, kvq.KVQ_BF16, 1, None, 0.1, O, None, 0, lib)
+    assert log(lib) == [with_ws]
+    # 512 query rows of 32 heads over 64-row splits: far above 64 MiB of partials
+    kvq.kvq_set_split_rows(h, 64, lib)
+    need = kvq.kvq_decode_workspace_bytes(h, 512, lib)
+    assert need > 64 << 20
+    lib.kvq_nodev_clear()
+    assert err(lib, kvq.kvq_decode_noalloc, h, Q, kvq.KVQ_BF16, 512, None, 0.1, O, None) == kvq.KVQ_ECAPACITY
+    assert log(lib) == [] and "scratch" in kvq.kvq_last_error(lib)
+    kvq.kvq_decode(h, Q, kvq.KVQ_BF16, 512, None, 0.1, O, None, WS, 1 << 40, 0, lib)   # the workspace call still works
+    assert len(log(lib)) == 1
