@@ -13,7 +13,8 @@ page (method rollback).
 """
 from .core import (  # noqa: F401
     build_oracle, load, f32_to_f16, f16_to_f32, q8_0_encode, q8_0_decode,
-    q5_1_encode, q5_1_decode, quantize_k, quantize_v, attention, max_threads, set_threads,
+    q5_1_encode, q5_1_decode, quantize_k, quantize_v, quantize_f8_rows, attention, max_threads,
+    set_threads,
     widen_bf16,
 )
 from .cache_model import OracleCache, RangeError  # noqa: F401

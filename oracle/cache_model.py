@@ -35,15 +35,19 @@ class CapacityError(ValueError):
 
 
 class OracleCache:
-    def __init__(self, n_seqs, n_kv_heads, head_dim, capacity, window=0, ring_step=0):
+    """fmt: "q8_0/q5_1" (K q8_0, V q5_1) or "e4m3" (K and V FP8 rows: the
+    codes of a row's blocks, then their fp16 scales; see kvq_oracle.c)."""
+
+    def __init__(self, n_seqs, n_kv_heads, head_dim, capacity, window=0, ring_step=0, fmt="q8_0/q5_1"):
         if head_dim % 32 != 0:
             raise ValueError("head_dim must be a multiple of 32 (a block never straddles a head)")
+        self.fmt = core.FORMATS[fmt]
         if ring_step and (window <= 0 or window + ring_step > capacity):
             raise ValueError("a ring needs 0 < window and window + ring_step <= capacity")
         self.B, self.Hkv, self.hd = int(n_seqs), int(n_kv_heads), int(head_dim)
         self.cap, self.window, self.step = int(capacity), int(window), int(ring_step)
         nb = self.Hkv * self.hd // 32
-        self.k_row, self.v_row = nb * 34, nb * 24
+        self.k_row, self.v_row = nb * 34, nb * (34 if self.fmt == core.FMT_E4M3 else 24)
         self.k = np.zeros((self.B, self.cap, self.k_row), dtype=np.uint8)
         self.v = np.zeros((self.B, self.cap, self.v_row), dtype=np.uint8)
         self.len = np.zeros(self.B, dtype=np.int64)
@@ -88,8 +92,12 @@ class OracleCache:
                 self.v[b, :keep] = self.v[b, nb_ - old: L - old].copy()
                 self.base[b] = nb_
             p0 = L - nb_
-            self.k[b, p0:p0 + n] = core.quantize_k(k[b, :n]).reshape(n, self.k_row)
-            self.v[b, p0:p0 + n] = core.quantize_v(v[b, :n]).reshape(n, self.v_row)
+            if self.fmt == core.FMT_E4M3:
+                self.k[b, p0:p0 + n] = core.quantize_f8_rows(k[b, :n], Hkv * hd).reshape(n, self.k_row)
+                self.v[b, p0:p0 + n] = core.quantize_f8_rows(v[b, :n], Hkv * hd).reshape(n, self.v_row)
+            else:
+                self.k[b, p0:p0 + n] = core.quantize_k(k[b, :n]).reshape(n, self.k_row)
+                self.v[b, p0:p0 + n] = core.quantize_v(v[b, :n]).reshape(n, self.v_row)
             self.len[b] = L + n
 
     def truncate(self, new_len):
@@ -115,7 +123,8 @@ class OracleCache:
         if np.any(self.len < T):
             raise ValueError("each session needs at least T committed rows")
         return core.importance(q, [self.k[b] for b in range(B)], self.base, self.len, self.cap,
-                               n_kv_heads=self.Hkv, window=self.window, sinks=sinks, scale=scale)
+                               n_kv_heads=self.Hkv, window=self.window, sinks=sinks, scale=scale,
+                               fmt=self.fmt)
 
     def attention(self, q, *, scale, sinks=None, sel=None, want_lse=True):
         """q: float32 [B, T, H, hd]; the T query rows are the last T rows."""
@@ -131,4 +140,4 @@ class OracleCache:
             raise RangeError("full attention over a rebased ring")
         return core.attention(q, [self.k[b] for b in range(B)], [self.v[b] for b in range(B)],
                               self.base, self.len, n_kv_heads=self.Hkv, window=self.window,
-                              sinks=sinks, scale=scale, sel=sel, want_lse=want_lse)
+                              sinks=sinks, scale=scale, sel=sel, want_lse=want_lse, fmt=self.fmt)

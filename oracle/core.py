@@ -57,13 +57,14 @@ def load(path: str | None = None):
     lib.kvqo_f8_decode.argtypes = [u8p, f64p]
     for name in ("kvqo_quantize_k", "kvqo_quantize_v"):
         getattr(lib, name).argtypes = [f32p, ctypes.c_int64, u8p]
+    lib.kvqo_quantize_f8_rows.argtypes = [f32p, ctypes.c_int64, ctypes.c_int32, u8p]
     lib.kvqo_attention.argtypes = [
-        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
         f32p, ctypes.POINTER(u8p), ctypes.POINTER(u8p), i64p, i64p, ctypes.c_int32,
         f32p, ctypes.c_float, i64p, ctypes.c_int64, f32p, f32p]
     lib.kvqo_attention.restype = ctypes.c_int
     lib.kvqo_importance.argtypes = [
-        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
         f32p, ctypes.POINTER(u8p), i64p, i64p, ctypes.c_int32, f32p, ctypes.c_float, f64p, ctypes.c_int64]
     lib.kvqo_importance.restype = ctypes.c_int
     lib.kvqo_max_threads.restype = ctypes.c_int
@@ -164,12 +165,29 @@ def quantize_v(x, lib=None) -> np.ndarray:
     return _quantize((lib or load()).kvqo_quantize_v, x, 24)
 
 
+# cache formats (kvq_oracle.h KVQO_FMT_*)
+FMT_Q8_Q5, FMT_E4M3 = 0, 1
+FORMATS = {"q8_0/q5_1": FMT_Q8_Q5, "e4m3": FMT_E4M3}
+
+
+def quantize_f8_rows(x, row_elems, lib=None) -> np.ndarray:
+    """float32 values, rows of row_elems (a multiple of 32) -> FP8 row bytes,
+    flat: per row the codes of its blocks, then their fp16 scales."""
+    lib = lib or load()
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    assert x.size % row_elems == 0 and row_elems % 32 == 0
+    n_rows = x.size // row_elems
+    out = np.empty(n_rows * row_elems // 32 * 34, dtype=np.uint8)
+    lib.kvqo_quantize_f8_rows(_ptr(x, ctypes.c_float), n_rows, int(row_elems), _ptr(out, ctypes.c_uint8))
+    return out
+
+
 def attention(q, k_planes, v_planes, base, length, *, n_kv_heads, window=0,
-              sinks=None, scale, sel=None, want_lse=True, lib=None):
+              sinks=None, scale, sel=None, want_lse=True, fmt=FMT_Q8_Q5, lib=None):
     """Exact attention.  q: float32 [B, T, H, hd].  k_planes / v_planes: per
-    session uint8 arrays whose row 0 holds logical row base[b].  Returns
-    (out [B,T,H,hd] float32, lse [B,T,H] float32 or None); entries not in
-    ``sel`` are NaN."""
+    session uint8 arrays whose row 0 holds logical row base[b], in cache
+    format fmt.  Returns (out [B,T,H,hd] float32, lse [B,T,H] float32 or
+    None); entries not in ``sel`` are NaN."""
     lib = lib or load()
     q = np.ascontiguousarray(q, dtype=np.float32)
     B, T, H, hd = q.shape
@@ -190,7 +208,7 @@ def attention(q, k_planes, v_planes, base, length, *, n_kv_heads, window=0,
     if sel is not None:
         selarr = np.ascontiguousarray(sel, dtype=np.int64)
     rc = lib.kvqo_attention(
-        B, T, H, int(n_kv_heads), hd, _ptr(q, ctypes.c_float), karr, varr,
+        int(fmt), B, T, H, int(n_kv_heads), hd, _ptr(q, ctypes.c_float), karr, varr,
         _ptr(base, ctypes.c_int64), _ptr(length, ctypes.c_int64), int(window),
         _ptr(s, ctypes.c_float) if s is not None else None, float(scale),
         _ptr(selarr, ctypes.c_int64) if selarr is not None else None,
@@ -202,7 +220,7 @@ def attention(q, k_planes, v_planes, base, length, *, n_kv_heads, window=0,
 
 
 def importance(q, k_planes, base, length, capacity, *, n_kv_heads, window=0, sinks=None, scale,
-               lib=None):
+               fmt=FMT_Q8_Q5, lib=None):
     """Attention importance: float64 [B, capacity], the probability mass of
     each physical row summed over the T query rows and H heads of q (float32
     [B, T, H, hd], the last T rows); rows no query row sees stay 0."""
@@ -219,7 +237,7 @@ def importance(q, k_planes, base, length, capacity, *, n_kv_heads, window=0, sin
         s = np.ascontiguousarray(sinks, dtype=np.float32)
         assert s.shape == (H,)
     imp = np.zeros((B, int(capacity)), dtype=np.float64)
-    rc = lib.kvqo_importance(B, T, H, int(n_kv_heads), hd, _ptr(q, ctypes.c_float), karr,
+    rc = lib.kvqo_importance(int(fmt), B, T, H, int(n_kv_heads), hd, _ptr(q, ctypes.c_float), karr,
                              _ptr(base, ctypes.c_int64), _ptr(length, ctypes.c_int64), int(window),
                              _ptr(s, ctypes.c_float) if s is not None else None, float(scale),
                              _ptr(imp, ctypes.c_double), int(capacity))

@@ -24,6 +24,12 @@
  *                          a hand-derived block; the round-trip bound.
  *                          Parity with another implementation's bytes is
  *                          unpinned: the pages print no encoded block.
+ *   FP8 rows               the row layout of the FP8 variant (codes of the
+ *                          row's blocks in element order, then their fp16
+ *                          scales) against a row image assembled by hand
+ *                          from the hand-derived golden blocks; attention
+ *                          over FP8 rows against textbook attention on
+ *                          values the e4m3 codec stores exactly.
  *   kvqo_importance        per-row probability mass summed over query
  *                          rows and heads: it sums to T*H less the sinks'
  *                          shares (closed form); equals a numpy softmax of
@@ -280,6 +286,56 @@ void kvqo_quantize_v(const float* x, int64_t n_elems, uint8_t* out) {
 }
 
 /* ------------------------------------------------------------------ */
+/* FP8 token rows.  The pages name e4m3 K and V ("Module cache" index   */
+/* page, kv_fp8_on) and give no layout.  Reading: a row of row_elems    */
+/* (= n_kv_heads * head_dim) elements is encoded block by block as      */
+/* kvqo_f8_encode does; the row holds the 32 codes of every block in    */
+/* element order first (the code of element e is byte e), then the     */
+/* fp16 scales of its blocks in block order (block k's at bytes         */
+/* row_elems + 2k, little-endian): row_elems / 32 * 34 bytes, 34 per    */
+/* 32 elements as for one block.                                        */
+/* ------------------------------------------------------------------ */
+void kvqo_quantize_f8_rows(const float* x, int64_t n_rows, int32_t row_elems, uint8_t* out) {
+    assert(row_elems % 32 == 0);
+    const int64_t row_bytes = (int64_t)row_elems / 32 * 34;
+    uint8_t blk[34];
+    for (int64_t r = 0; r < n_rows; ++r) {
+        uint8_t* row = out + r * row_bytes;
+        for (int32_t k = 0; k < row_elems / 32; ++k) {
+            kvqo_f8_encode(x + r * row_elems + 32 * k, blk);
+            memcpy(row + 32 * k, blk + 2, 32);
+            row[row_elems + 2 * k] = blk[0];
+            row[row_elems + 2 * k + 1] = blk[1];
+        }
+    }
+}
+
+/* Bytes of one K or V token row, and the 32 dequantized values of block
+ * kb of KV head g in such a row, for cache format fmt (KVQO_FMT_*). */
+static int64_t row_bytes(int32_t fmt, int v_side, int32_t Hkv, int32_t nb) {
+    if (fmt == KVQO_FMT_E4M3) return (int64_t)Hkv * nb * 34;
+    return (int64_t)Hkv * nb * (v_side ? 24 : 34);
+}
+
+static void row_block(int32_t fmt, int v_side, const uint8_t* row, int32_t Hkv, int32_t nb,
+                      int32_t g, int32_t kb, double* out) {
+    const int64_t k = (int64_t)g * nb + kb;           /* block index in the row */
+    if (fmt == KVQO_FMT_E4M3) {
+        const int64_t row_elems = (int64_t)Hkv * nb * 32;
+        const uint8_t* scale = row + row_elems + 2 * k;
+        uint8_t blk[34];
+        blk[0] = scale[0];
+        blk[1] = scale[1];
+        memcpy(blk + 2, row + 32 * k, 32);
+        kvqo_f8_decode(blk, out);
+    } else if (v_side) {
+        kvqo_q5_1_decode(row + 24 * k, out);
+    } else {
+        kvqo_q8_0_decode(row + 34 * k, out);
+    }
+}
+
+/* ------------------------------------------------------------------ */
 /* Attention.  For session b, query row t and Q head h:                 */
 /*   g     = h / hpk                       (GQA grouping)               */
 /*   upto  = len_b - T + t + 1             (causal bound of row t)      */
@@ -290,7 +346,7 @@ void kvqo_quantize_v(const float* x, int64_t n_elems, uint8_t* out) {
 /*   out   = sum_j exp(s_j - M) * V'[j, g, :] / Z,   lse = M + log Z    */
 /* K', V' are the dequantized cache values, exact in double.            */
 /* ------------------------------------------------------------------ */
-static void one_query(int32_t T, int32_t H, int32_t Hkv, int32_t hd,
+static void one_query(int32_t fmt, int32_t T, int32_t H, int32_t Hkv, int32_t hd,
                       const float* q, const uint8_t* const* k_plane,
                       const uint8_t* const* v_plane, const int64_t* base,
                       const int64_t* len, int32_t window, const float* sinks,
@@ -299,8 +355,8 @@ static void one_query(int32_t T, int32_t H, int32_t Hkv, int32_t hd,
     const int32_t hpk = H / Hkv;
     const int32_t g = h / hpk;
     const int32_t nb = hd / 32;                    /* blocks per head */
-    const int64_t k_row = (int64_t)Hkv * nb * 34;  /* bytes per K token row */
-    const int64_t v_row = (int64_t)Hkv * nb * 24;  /* bytes per V token row */
+    const int64_t k_row = row_bytes(fmt, 0, Hkv, nb);   /* bytes per K token row */
+    const int64_t v_row = row_bytes(fmt, 1, Hkv, nb);   /* bytes per V token row */
     const int64_t upto = len[b] - T + t + 1;
     int64_t first = 0;
     if (window > 0) {
@@ -316,10 +372,10 @@ static void one_query(int32_t T, int32_t H, int32_t Hkv, int32_t hd,
 
     double M = -INFINITY;
     for (int64_t j = first; j < upto; ++j) {
-        const uint8_t* row = k_plane[b] + (j - base[b]) * k_row + (int64_t)g * nb * 34;
+        const uint8_t* row = k_plane[b] + (j - base[b]) * k_row;
         double acc = 0.0;
         for (int32_t kb = 0; kb < nb; ++kb) {
-            kvqo_q8_0_decode(row + 34 * kb, blk);
+            row_block(fmt, 0, row, Hkv, nb, g, kb, blk);
             for (int i = 0; i < 32; ++i)
                 acc += (double)qv[32 * kb + i] * blk[i];
         }
@@ -338,9 +394,9 @@ static void one_query(int32_t T, int32_t H, int32_t Hkv, int32_t hd,
     float* o = out + (((int64_t)b * T + t) * H + h) * hd;
     double* acc = (double*)calloc((size_t)hd, sizeof(double));
     for (int64_t j = first; j < upto; ++j) {
-        const uint8_t* row = v_plane[b] + (j - base[b]) * v_row + (int64_t)g * nb * 24;
+        const uint8_t* row = v_plane[b] + (j - base[b]) * v_row;
         for (int32_t vb = 0; vb < nb; ++vb) {
-            kvqo_q5_1_decode(row + 24 * vb, blk);
+            row_block(fmt, 1, row, Hkv, nb, g, vb, blk);
             for (int i = 0; i < 32; ++i)
                 acc[32 * vb + i] += s[j - first] * blk[i];
         }
@@ -351,7 +407,7 @@ static void one_query(int32_t T, int32_t H, int32_t Hkv, int32_t hd,
     if (lse) lse[((int64_t)b * T + t) * H + h] = (float)(M + log(Z));
 }
 
-int kvqo_attention(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t hd,
+int kvqo_attention(int32_t fmt, int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t hd,
                    const float* q,
                    const uint8_t* const* k_plane, const uint8_t* const* v_plane,
                    const int64_t* base, const int64_t* len, int32_t window,
@@ -359,7 +415,7 @@ int kvqo_attention(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t hd,
                    const int64_t* sel, int64_t n_sel,
                    float* out, float* lse) {
     if (B <= 0 || T <= 0 || H <= 0 || Hkv <= 0 || hd <= 0 || hd % 32 != 0 ||
-        H % Hkv != 0 || window < 0)
+        H % Hkv != 0 || window < 0 || (fmt != KVQO_FMT_Q8_Q5 && fmt != KVQO_FMT_E4M3))
         return -1;
     int64_t max_rows = 0;
     for (int32_t b = 0; b < B; ++b)
@@ -379,7 +435,7 @@ int kvqo_attention(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t hd,
             int32_t t = (int32_t)((f / H) % T);
             int64_t b = f / ((int64_t)H * T);
             int lb = 0;
-            one_query(T, H, Hkv, hd, q, k_plane, v_plane, base, len, window,
+            one_query(fmt, T, H, Hkv, hd, q, k_plane, v_plane, base, len, window,
                       sinks, scale, b, t, h, s, out, lse, &lb);
             bad |= lb;
         }
@@ -398,16 +454,16 @@ int kvqo_attention(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t hd,
 /* is no row, so nothing is added for it.  imp: double [B][cap],        */
 /* indexed by physical row.                                             */
 /* ------------------------------------------------------------------ */
-int kvqo_importance(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t hd,
+int kvqo_importance(int32_t fmt, int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t hd,
                     const float* q, const uint8_t* const* k_plane,
                     const int64_t* base, const int64_t* len, int32_t window,
                     const float* sinks, float scale, double* imp, int64_t cap) {
     if (B <= 0 || T <= 0 || H <= 0 || Hkv <= 0 || hd <= 0 || hd % 32 != 0 ||
-        H % Hkv != 0 || window < 0 || cap <= 0)
+        H % Hkv != 0 || window < 0 || cap <= 0 || (fmt != KVQO_FMT_Q8_Q5 && fmt != KVQO_FMT_E4M3))
         return -1;
     const int32_t heads_per_group = H / Hkv;
     const int32_t blocks = hd / 32;
-    const int64_t k_bytes = (int64_t)Hkv * blocks * 34;
+    const int64_t k_bytes = row_bytes(fmt, 0, Hkv, blocks);
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
     for (int32_t b = 0; b < B; ++b) {
@@ -423,10 +479,10 @@ int kvqo_importance(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t hd,
                 const float* qrow = q + (((int64_t)b * T + t) * H + h) * hd;
                 double top = -INFINITY;
                 for (int64_t j = row_start; j < row_end; ++j) {
-                    const uint8_t* krow = k_plane[b] + (j - base[b]) * k_bytes + (int64_t)kv_group * blocks * 34;
+                    const uint8_t* krow = k_plane[b] + (j - base[b]) * k_bytes;
                     double dot = 0.0;
                     for (int32_t kb = 0; kb < blocks; ++kb) {
-                        kvqo_q8_0_decode(krow + 34 * kb, kdeq);
+                        row_block(fmt, 0, krow, Hkv, blocks, kv_group, kb, kdeq);
                         for (int i = 0; i < 32; ++i) dot += kdeq[i] * (double)qrow[32 * kb + i];
                     }
                     score[j - row_start] = dot * (double)scale;

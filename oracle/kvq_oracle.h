@@ -55,14 +55,23 @@ uint8_t kvqo_e4m3_from_f32(float x);
 void kvqo_f8_encode(const float* x, uint8_t* blk);
 void kvqo_f8_decode(const uint8_t* blk, double* x);
 
+/* Cache formats of the attention and importance routines. */
+#define KVQO_FMT_Q8_Q5 0   /* K q8_0 blocks, V q5_1 blocks, consecutive in a row */
+#define KVQO_FMT_E4M3 1    /* K and V FP8 rows (kvqo_quantize_f8_rows) */
+
 /* Encode n_elems (a multiple of 32) consecutive floats as consecutive
  * blocks.  Because head_dim % 32 == 0 and a token row is laid out as
  * [kv_head, dim], this is exactly the byte image of n_elems/(Hkv*hd) rows. */
 void kvqo_quantize_k(const float* x, int64_t n_elems, uint8_t* out);
 void kvqo_quantize_v(const float* x, int64_t n_elems, uint8_t* out);
+/* n_rows FP8 token rows of row_elems floats each: per row, the codes of its
+ * 32-element blocks (kvqo_f8_encode) in element order, then the blocks'
+ * fp16 scales in block order; row_elems / 32 * 34 bytes per row. */
+void kvqo_quantize_f8_rows(const float* x, int64_t n_rows, int32_t row_elems, uint8_t* out);
 
 /*
  * Exact-softmax decode attention in double precision.
+ *   fmt      KVQO_FMT_Q8_Q5 or KVQO_FMT_E4M3 (the planes' format)
  *   q        [B, T, H, hd] floats (bf16 inputs widened exactly beforehand)
  *   k_plane  per session: pointer to the physical row 0 of its K plane
  *   v_plane  per session: pointer to the physical row 0 of its V plane
@@ -76,7 +85,7 @@ void kvqo_quantize_v(const float* x, int64_t n_elems, uint8_t* out);
  * Returns 0, or -1 on an argument the method does not define (a visible
  * set that would be empty, or a visible row outside the resident range).
  */
-int kvqo_attention(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t hd,
+int kvqo_attention(int32_t fmt, int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t hd,
                    const float* q,
                    const uint8_t* const* k_plane, const uint8_t* const* v_plane,
                    const int64_t* base, const int64_t* len, int32_t window,
@@ -88,7 +97,7 @@ int kvqo_attention(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t hd,
  * row a query row sees, that row's softmax probability (sink in the
  * denominator), summed over the T query rows and H heads.  Returns 0 or -1
  * as kvqo_attention. */
-int kvqo_importance(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t hd,
+int kvqo_importance(int32_t fmt, int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t hd,
                     const float* q, const uint8_t* const* k_plane,
                     const int64_t* base, const int64_t* len, int32_t window,
                     const float* sinks, float scale, double* imp, int64_t cap);

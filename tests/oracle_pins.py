@@ -41,6 +41,19 @@ def exact_v(rng, n, Hkv, hd):
     return (m.astype(np.float64) + c * 2.0 ** e).reshape(n, Hkv, hd).astype(np.float32)
 
 
+def exact_f8(rng, n, Hkv, hd):
+    """Rows whose FP8 encoding is exact: each 32-block is 2^e times finite
+    e4m3 values with one of magnitude 448 (then the scale amax / 448 is
+    exactly 2^e and every quotient is its own code)."""
+    codes = rng.integers(0, 256, size=(n, Hkv, hd // 32, 32)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3C                       # no NaN code
+    codes[(codes & 0x7F) == 0x7E] = 0x3D                       # 448 only where placed below
+    codes[..., 0] = np.where(rng.random((n, Hkv, hd // 32)) < 0.5, 0x7E, 0xFE)
+    e = rng.integers(-10, -3, size=(n, Hkv, hd // 32, 1))
+    vals = core.e4m3_value(codes.ravel()).reshape(codes.shape)
+    return (vals * 2.0 ** e).reshape(n, Hkv, hd).astype(np.float32)
+
+
 def sdpa_reference(q, k, v, hpk, scale, window=0, sinks=None):
     """Textbook attention through torch's scaled_dot_product_attention in
     float64 on the CPU.  q [B,T,H,hd]; k, v [B,N,Hkv,hd] (every row, logical
@@ -113,6 +126,32 @@ def check_golden_codec(lib):
     x = np.array([c * 0.125 for c in range(-16, 16)], np.float32)
     x[0] = -15.875
     assert np.array_equal(core.q8_0_decode(core.q8_0_encode(x, lib), lib), x.astype(np.float64))
+
+
+def check_f8_rows_golden(lib):
+    """FP8 token-row images assembled by hand from the golden blocks
+    (tests/golden/f8_rows.txt): the codes of the row's blocks, then their
+    scales."""
+    blocks = {}
+    n = 0
+    for line in open(os.path.join(GOLDEN, "f8_blocks.txt")):
+        if line.startswith("x:"):
+            n += 1
+            blocks[n] = np.array([float(t) for t in line[2:].split()], dtype=np.float32)
+    seen = 0
+    for line in open(os.path.join(GOLDEN, "f8_rows.txt")):
+        if line.startswith("blocks:"):
+            x = np.concatenate([blocks[int(t)] for t in line[7:].split()])
+        elif line.startswith("bytes:"):
+            want = np.array([int(t, 16) for t in line[6:].split()], dtype=np.uint8)
+            assert np.array_equal(core.quantize_f8_rows(x, x.size, lib), want)
+            # the same values as two rows of half the width are two such images
+            if x.size == 64:
+                two = core.quantize_f8_rows(x, 32, lib).reshape(2, 34)
+                for r in range(2):
+                    assert np.array_equal(two[r], core.f8_encode(x[32 * r:32 * r + 32], lib)[np.r_[2:34, 0:2]])
+            seen += 1
+    assert seen == 2
 
 
 def check_e4m3_codes(lib):
@@ -203,16 +242,21 @@ def check_f16_sample(lib):
     assert np.array_equal(core.f32_to_f16(x, lib), ref)
 
 
-def check_textbook(lib, *, B=2, T=3, H=6, Hkv=2, hd=64, N=40, window=0, sinks=False, seed=0):
+def check_textbook(lib, *, B=2, T=3, H=6, Hkv=2, hd=64, N=40, window=0, sinks=False, seed=0, fmt="q8_0/q5_1"):
     """Representable K/V: the oracle must equal textbook attention (torch SDPA,
-    float64) over the raw values, with GQA, causal T rows, window and sink."""
+    float64) over the raw values, with GQA, causal T rows, window and sink;
+    for either cache format (values the format stores exactly)."""
     rng = np.random.default_rng(seed)
-    k = exact_k(rng, B * N, Hkv, hd).reshape(B, N, Hkv, hd)
-    v = exact_v(rng, B * N, Hkv, hd).reshape(B, N, Hkv, hd)
+    if fmt == "e4m3":
+        k = exact_f8(rng, B * N, Hkv, hd).reshape(B, N, Hkv, hd)
+        v = exact_f8(rng, B * N, Hkv, hd).reshape(B, N, Hkv, hd)
+    else:
+        k = exact_k(rng, B * N, Hkv, hd).reshape(B, N, Hkv, hd)
+        v = exact_v(rng, B * N, Hkv, hd).reshape(B, N, Hkv, hd)
     q = rng.standard_normal((B, T, H, hd)).astype(np.float32)
     s = rng.standard_normal(H).astype(np.float32) if sinks else None
     scale = float(np.float32(1 / np.sqrt(hd)))
-    c = OracleCache(B, Hkv, hd, N + 8, window=window)
+    c = OracleCache(B, Hkv, hd, N + 8, window=window, fmt=fmt)
     c_append(c, lib, k, v)
     out, lse = attend(c, lib, q, scale, sinks=s)
     ref, ref_lse = sdpa_reference(q, k, v, H // Hkv, scale, window=window, sinks=s)
@@ -344,18 +388,19 @@ def importance_of(cache, lib, q, scale, sinks=None):
         core._lib = saved
 
 
-def check_importance_textbook(lib, *, B=2, T=3, H=6, Hkv=2, hd=64, N=40, window=9, sinks=True, seed=3):
+def check_importance_textbook(lib, *, B=2, T=3, H=6, Hkv=2, hd=64, N=40, window=9, sinks=True, seed=3,
+                              fmt="q8_0/q5_1"):
     """Representable K: the importance equals a textbook softmax (torch,
     float64) of every (query row, head) over its visible rows plus the sink as
     one more column, the row columns summed over heads and query rows; rows
     that no query row sees, and physical rows past len, hold 0."""
     rng = np.random.default_rng(seed)
-    k = exact_k(rng, B * N, Hkv, hd).reshape(B, N, Hkv, hd)
+    k = (exact_f8 if fmt == "e4m3" else exact_k)(rng, B * N, Hkv, hd).reshape(B, N, Hkv, hd)
     v = np.zeros_like(k)
     q = rng.standard_normal((B, T, H, hd)).astype(np.float32)
     s = rng.standard_normal(H).astype(np.float32) if sinks else None
     scale = float(np.float32(1 / np.sqrt(hd)))
-    c = OracleCache(B, Hkv, hd, N + 8, window=window)
+    c = OracleCache(B, Hkv, hd, N + 8, window=window, fmt=fmt)
     c_append(c, lib, k, v)
     imp = importance_of(c, lib, q, scale, sinks=s)
     qt = torch.from_numpy(q.astype(np.float64)).permute(0, 2, 1, 3)                       # B,H,T,hd
@@ -391,6 +436,12 @@ def check_importance_mass(lib):
 
 ALL_CHECKS = {
     "golden_codec": check_golden_codec,
+    "f8_rows_golden": check_f8_rows_golden,
+    "textbook_f8": lambda lib: check_textbook(lib, B=2, T=3, H=8, Hkv=4, hd=64, N=37, window=11, sinks=True,
+                                              seed=21, fmt="e4m3"),
+    "textbook_f8_hd256": lambda lib: check_textbook(lib, B=1, T=8, H=8, Hkv=2, hd=256, N=29, seed=22, fmt="e4m3"),
+    "importance_textbook_f8": lambda lib: check_importance_textbook(lib, B=1, T=2, H=8, Hkv=4, hd=96, N=30,
+                                                                     window=0, sinks=True, seed=23, fmt="e4m3"),
     "f16_sample": check_f16_sample,
     "e4m3_codes": check_e4m3_codes,
     "e4m3_rounding": check_e4m3_rounding,

@@ -54,6 +54,13 @@ MUTANTS = {
                               "const int64_t row_end = len[b] - T + t;"),
     "imp_window_off_by_one": ("row_end > window ? row_end - window : 0;", "row_end > window ? row_end - window + 1 : 0;"),
     "imp_group_modulo": ("const int32_t kv_group = h / heads_per_group;", "const int32_t kv_group = h % Hkv;"),
+    "f8_row_codes_at_block_stride": ("memcpy(row + 32 * k, blk + 2, 32);", "memcpy(row + 34 * k, blk + 2, 32);"),
+    "f8_row_scales_first": ("row[row_elems + 2 * k] = blk[0];", "row[2 * k] = blk[0];"),
+    "f8_read_scale_of_head_0": ("const uint8_t* scale = row + row_elems + 2 * k;",
+                                "const uint8_t* scale = row + row_elems + 2 * kb;"),
+    "f8_read_codes_of_head_0": ("memcpy(blk + 2, row + 32 * k, 32);", "memcpy(blk + 2, row + 32 * kb, 32);"),
+    "f8_v_rows_as_q5_1": ("if (fmt == KVQO_FMT_E4M3) return (int64_t)Hkv * nb * 34;",
+                          "if (fmt == KVQO_FMT_E4M3 && !v_side) return (int64_t)Hkv * nb * 34;"),
 }
 
 
