@@ -169,22 +169,36 @@ double kvqo_e4m3_value(uint8_t c) {
     return neg ? -mag : mag;
 }
 
-/* The code nearest to x, found by trying every finite magnitude: ties go
- * to the code with an even fraction (of two neighbours, whose codes differ
- * by one, the even code), magnitudes past 448 give 0x7E = 448, the nearest
- * finite code (saturation; the NaN code is never chosen), and the sign bit
- * is x's, also when the magnitude rounds to zero. */
+/* The code nearest to x: ties go to the code with an even fraction (of two
+ * neighbours, whose codes differ by one, the even code), magnitudes past 448
+ * give 0x7E = 448, the nearest finite code (saturation; the NaN code is
+ * never chosen), and the sign bit is x's, also when the magnitude rounds to
+ * zero.  The positive finite codes 0 .. 126 have rising values, so the two
+ * candidates are the largest code whose value is at most |x| and the next
+ * one; bisection finds them. */
+static double e4m3_pos[127];              /* value of each positive finite code */
+
+__attribute__((constructor)) static void e4m3_table(void) {
+    for (int c = 0; c < 127; ++c) e4m3_pos[c] = kvqo_e4m3_value((uint8_t)c);
+}
+
 uint8_t kvqo_e4m3_from_f32(float x) {
     assert(!isnan(x));
     const double a = fabs((double)x);
-    int best = 0;
-    double best_err = a;                 /* code 0: magnitude 0 */
-    for (int c = 1; c < 127; ++c) {      /* the finite positive codes */
-        const double err = fabs(kvqo_e4m3_value((uint8_t)c) - a);
-        if (err < best_err || (err == best_err && (c & 1) == 0)) {
-            best = c;
-            best_err = err;
+    int best;
+    if (a >= e4m3_pos[126]) {
+        best = 126;
+    } else {
+        int lo = 0, hi = 126;             /* value(lo) <= a < value(hi) */
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) / 2;
+            if (e4m3_pos[mid] <= a) lo = mid; else hi = mid;
         }
+        const double err_lo = a - e4m3_pos[lo];
+        const double err_hi = e4m3_pos[hi] - a;
+        if (err_lo < err_hi) best = lo;
+        else if (err_hi < err_lo) best = hi;
+        else best = (lo & 1) == 0 ? lo : hi;   /* a tie: the even code */
     }
     return (uint8_t)(best | (signbit(x) ? 0x80 : 0));
 }
@@ -298,8 +312,9 @@ void kvqo_quantize_v(const float* x, int64_t n_elems, uint8_t* out) {
 void kvqo_quantize_f8_rows(const float* x, int64_t n_rows, int32_t row_elems, uint8_t* out) {
     assert(row_elems % 32 == 0);
     const int64_t row_bytes = (int64_t)row_elems / 32 * 34;
-    uint8_t blk[34];
+#pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < n_rows; ++r) {
+        uint8_t blk[34];
         uint8_t* row = out + r * row_bytes;
         for (int32_t k = 0; k < row_elems / 32; ++k) {
             kvqo_f8_encode(x + r * row_elems + 32 * k, blk);

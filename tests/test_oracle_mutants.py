@@ -38,8 +38,10 @@ MUTANTS = {
     "q5_unrounded_min": ("float r = rintf((x[i] - ms) / ds);", "float r = rintf((x[i] - mn) / ds);"),
     "e4m3_bias_8": ("ldexp(1.0 + fr / 8.0, ex - 7)", "ldexp(1.0 + fr / 8.0, ex - 8)"),
     "e4m3_subnormal_exponent": ("ldexp((double)fr, -9)", "ldexp((double)fr, -10)"),
-    "e4m3_ties_odd": ("(err == best_err && (c & 1) == 0)", "(err == best_err && (c & 1) == 1)"),
-    "e4m3_ties_up": ("if (err < best_err || (err == best_err", "if (err <= best_err || (err == best_err"),
+    "e4m3_ties_odd": ("else best = (lo & 1) == 0 ? lo : hi;", "else best = (lo & 1) == 1 ? lo : hi;"),
+    "e4m3_ties_up": ("else best = (lo & 1) == 0 ? lo : hi;", "else best = hi;"),
+    "e4m3_nearest_swapped": ("if (err_lo < err_hi) best = lo;", "if (err_lo < err_hi) best = hi;"),
+    "e4m3_table_shifted": ("e4m3_pos[c] = kvqo_e4m3_value((uint8_t)c);", "e4m3_pos[c] = kvqo_e4m3_value((uint8_t)(c ? c - 1 : 0));"),
     "e4m3_sign_dropped": ("return (uint8_t)(best | (signbit(x) ? 0x80 : 0));", "return (uint8_t)best;"),
     "f8_unrounded_scale": ("kvqo_e4m3_from_f32(x[i] / ds)", "kvqo_e4m3_from_f32(x[i] / (amax / 448.0f))"),
     "f8_divisor_447": ("kvqo_f32_to_f16(amax / 448.0f)", "kvqo_f32_to_f16(amax / 447.0f)"),
