@@ -177,7 +177,8 @@ def build_layers(w, L, dev, split_rows, tiling="", grow_rows=8 * 1024, graph_mod
 
     from decode_attention_quantized_append_amd import KvqLayerCache
     cap = w.capacity(extra_steps=0) if w.ring_cap else int(w.lengths().max()) + grow_rows
-    caches = [KvqLayerCache(w.B, w.H, w.Hkv, w.hd, cap, w.window, w.ring_step, device=dev) for _ in range(L)]
+    caches = [KvqLayerCache(w.B, w.H, w.Hkv, w.hd, cap, w.window, w.ring_step, device=dev, fmt=w.fmt)
+              for _ in range(L)]
     if graph_mode:
         # decode plans for every length the plane allows, so that one
         # captured round replays while the lengths grow
@@ -440,7 +441,7 @@ def run_cpu_baseline(w, seconds):
 
     import oracle
     t_fill = time.perf_counter()
-    ref = oracle.OracleCache(w.B, w.Hkv, w.hd, w.capacity(), w.window, w.ring_step)
+    ref = oracle.OracleCache(w.B, w.Hkv, w.hd, w.capacity(), w.window, w.ring_step, fmt=w.fmt)
     for counts, starts, T in w.prefill_pieces():
         k, v = w.kv_block(counts, starts, T)
         ref.append(k, v, counts)
@@ -526,7 +527,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_line["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE,
         "data": "synthetic (seeded; shapes and distributions of the workload, no datasets or weights)",
-        "config": {"workload": w.name, "sessions": w.B, "q_heads": w.H, "kv_heads": w.Hkv,
+        "config": {"workload": w.name, "kv_format": w.fmt, "sessions": w.B, "q_heads": w.H, "kv_heads": w.Hkv,
                    "head_dim": w.hd, "query_rows": w.T, "visible_rows": int(w.visible().sum()),
                    "window": w.window, "ring_rows": w.ring_cap, "layers_rotated": r["L"],
                    "kv_footprint_bytes": r["footprint"], "kv_bytes_per_step": r["kv_bytes"],
@@ -565,8 +566,8 @@ def main():
 # profiles/: summaries of rocprofv3 runs of this script (kernel traces and the
 # FETCH_SIZE / WRITE_SIZE passes), rebuilt with --summarize-profiles DIR from
 # the directories the commands below write.
-TRACE_WORKLOADS = ("verify", "batched", "qwen_gqa", "prime")
-TRAFFIC_WORKLOADS = ("verify", "batched", "qwen_gqa")
+TRACE_WORKLOADS = ("verify", "batched", "qwen_gqa", "prime", "verify_f8", "batched_f8")
+TRAFFIC_WORKLOADS = ("verify", "batched", "qwen_gqa", "verify_f8", "batched_f8")
 PER_STEP = ("decode_stream", "decode_mfma", "combine_kernel", "combine_wave_kernel", "append_kernel", "set_kernel")
 
 

@@ -70,8 +70,26 @@ __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint8_t
 // Key of slot k (0..7) of lane group q4 in the P V operands.
 __device__ __forceinline__ int pkey(int q4, int k) { return (k < 4) ? 4 * q4 + k : 16 + 4 * q4 + (k - 4); }
 
+// The window geometry of one format: q8_0 / q5_1 blocks, or FP8 rows.
+template <int NB, bool F8>
+struct WinOf {
+    using type = StreamWin<NB>;
+};
 template <int NB>
-using Win = StreamWin<NB>;
+struct WinOf<NB, true> {
+    using type = StreamWinF8<NB>;
+};
+
+// 8 e4m3 codes (bytes of lo, then hi) -> fp16, exactly (every e4m3 value is an
+// fp16 value); the hardware conversion with a scale of 1.
+__device__ __forceinline__ h8 e4m3_codes(uint32_t lo, uint32_t hi) {
+    typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+    const h2v a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+    const h2v b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+    const h2v c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+    const h2v d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+    return (h8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
 
 template <int NL>
 __device__ __forceinline__ void wait_loads_upto() {
@@ -116,15 +134,17 @@ __device__ __forceinline__ h8 v_codes_sub(uint32_t lo, uint32_t hi) {
 // queries (a low fp16 part kept beside the high one); RS row streams (waves
 // of one head taking alternate tiles); RG row groups (waves of one head
 // taking 16 query rows each of the same tiles, which they load in step so
-// that the second copy comes from L2).
-template <int NB, int RTW, bool QLO, int RS, int RG, int DS>
+// that the second copy comes from L2); DS dim halves; F8: K and V as FP8
+// rows (a head's codes, then the piece of the row's scale area holding its
+// scales) instead of q8_0 / q5_1 blocks.
+template <int NB, int RTW, bool QLO, int RS, int RG, int DS, bool F8>
 __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RTW == 1 ? 8 : 4),
                              DS == 2 ? stream_ds_waves_per_simd(NB) : stream_waves_per_simd(NB, RTW, QLO)) void decode_stream(
     DecodeParams p) {
     static_assert(RS == 1 || RTW == 1 || DS == 2, "row streams need one row tile per wave, or dim halves");
     static_assert(RG == 1 || (RTW == 1 && RS == 1 && RG == 2), "row groups are two, one row tile per wave");
     static_assert(DS == 1 || (DS == 2 && RTW == 2 && RG == 1), "dim halves hold both row tiles");
-    using WN = Win<NB>;
+    using WN = typename WinOf<NB, F8>::type;
     constexpr int HD = NB * 32;     // dims of this wave's slice of a head
     // DS = 2: the two waves of a head take half of its dims each (NB blocks
     // of the 2 NB), for all R query rows: each loads and unpacks only its
@@ -179,23 +199,31 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
     const uint8_t* rk = tb0 + WN::KB;   // K rows of the current tile, stride KSTR
     const uint8_t* rv = tb0 + WN::VB;   // V rows of the current tile, stride VSTR
     const int hrow = SH ? rb : 0;       // first tile row this wave copies
-    // This head's windows: K from the 16-byte boundary at or below its first
-    // block (kofs bytes before it), V exactly its blocks.
-    const int kstart = (g * DS + half) * NB * 34;
-    const int kofs = kstart & 15;
-    const uint8_t* const kwin = p.k_planes + (int64_t)b * p.k_stride + (kstart - kofs);
-    const uint8_t* const vwin = p.v_planes + (int64_t)b * p.v_stride + (g * DS + half) * NB * 24;
+    // This head's windows.  q8_0 / q5_1: K from the 16-byte boundary at or
+    // below its first block (kofs bytes before it), V exactly its blocks.
+    // FP8: the codes of its blocks (16-byte aligned in the row), then the
+    // 16-byte piece of the row's scale area that holds its NB scales (at
+    // sofs within it); the same for K and V.
+    const int hs = g * DS + half;                       // this wave's NB-block slice of a row
+    const int kstart = F8 ? hs * NB * 32 : hs * NB * 34;
+    const int kofs = F8 ? 0 : (kstart & 15);
+    const int sofs = F8 ? (hs * 2 * NB) & 15 : 0;
+    const int spiece = F8 ? p.Hkv * p.hd + ((hs * 2 * NB) & ~15) : 0;
+    const uint8_t* const kwin = p.k_planes + (int64_t)b * p.k_stride + (F8 ? 0 : kstart - kofs);
+    const uint8_t* const vwin = p.v_planes + (int64_t)b * p.v_stride + (F8 ? 0 : hs * NB * 24);
     // per lane, the byte offset of its piece (instruction x) from the tile's first row
     uint32_t koff[NKH], voff[NVH];
 #pragma unroll
     for (int x = 0; x < NKH; ++x) {
         const int pc = x * 64 + lane, row = pc / WN::KWP, col = pc - row * WN::KWP;
-        koff[x] = (uint32_t)((hrow + row) * p.k_row + min(col, WN::KW - 1) * 16);
+        koff[x] = F8 ? (uint32_t)((hrow + row) * p.k_row + (col < 2 * NB ? kstart + col * 16 : spiece))
+                     : (uint32_t)((hrow + row) * p.k_row + min(col, WN::KW - 1) * 16);
     }
 #pragma unroll
     for (int x = 0; x < NVH; ++x) {
         const int pc = x * 64 + lane, row = pc / WN::VWP, col = pc - row * WN::VWP;
-        voff[x] = (uint32_t)((hrow + row) * p.v_row + min(col, WN::VW - 1) * 16);   // the pad piece re-reads a real one
+        voff[x] = F8 ? (uint32_t)((hrow + row) * p.v_row + (col < 2 * NB ? kstart + col * 16 : spiece))
+                     : (uint32_t)((hrow + row) * p.v_row + min(col, WN::VW - 1) * 16);   // the pad piece re-reads a real one
     }
     // Copy the K (or V) rows of the tile [t0, t0 + 32) into the buffer.  Rows
     // from c1 on (a session's last tile) are not loaded; rows below lo (first
@@ -250,7 +278,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
     const float sc2 = p.scale * kLog2e;
     float* const KSa = reinterpret_cast<float*>(scb + WN::KS);
     float* const VDa = reinterpret_cast<float*>(scb + WN::VD);
-    uint16_t* const VMa = reinterpret_cast<uint16_t*>(scb + WN::VM);
+    uint16_t* const VMa = reinterpret_cast<uint16_t*>(scb + WN::VM);   // q5_1 offsets (not FP8)
     const int vkey = pkey(q4, j16 >> 1);                 // V row of this lane's tr8 reads
     const int mk0 = pkey(q4, j16 >> 2), mk1 = pkey(q4, 4 + (j16 >> 2));
     const int mc = (4 * (j16 & 3) < NB) ? (j16 & 3) : 0;   // columns past NB of the offset product are unused
@@ -264,6 +292,21 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
     // Row stream str takes the chunk's tiles str, str + rs, ...; a stream
     // with fewer tiles than stream 0 meets stream 0's remaining barriers
     // after its loop.
+    if constexpr (F8) {
+        // A tile's rows past c1 are not loaded, and P V still multiplies their
+        // V codes (by a weight of 0).  Any byte is a valid q5_1 code, but
+        // e4m3 has NaN codes: zero this wave's V rows once, so that such rows
+        // hold zeros or an earlier tile's codes, never stale LDS bytes.
+        constexpr int VROWS = SH ? 16 : kTile;
+#pragma unroll
+        for (int bi = 0; bi < (SH ? 2 : 1); ++bi) {
+            uint8_t* const z = tb0 + bi * RAW + WN::VB + hrow * WN::VSTR;
+            for (int o = lane * 16; o < VROWS * WN::VSTR; o += 64 * 16)
+                *reinterpret_cast<uint4*>(z + o) = make_uint4(0u, 0u, 0u, 0u);
+        }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the zeros are written before any load lands
+    }
     const int ntiles = (c1 - c0 + kTile - 1) / kTile;
     const int nit = (ntiles + rs - 1) / rs;                   // stream 0's tiles
     const int mine = ntiles > str ? (ntiles - str + rs - 1) / rs : 0;
@@ -376,7 +419,8 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
             const int u = x * 64 + lane;
             if (SROWS * NB % 64 == 0 || u < SROWS * NB) {
                 const int key = hrow + u / NB, blk = u - (u / NB) * NB;
-                const uint16_t kd = *reinterpret_cast<const uint16_t*>(rk + key * WN::KSTR + kofs + blk * 34);
+                const uint16_t kd = F8 ? *reinterpret_cast<const uint16_t*>(rk + key * WN::KSTR + 32 * NB + sofs + 2 * blk)
+                                       : *reinterpret_cast<const uint16_t*>(rk + key * WN::KSTR + kofs + blk * 34);
                 KSa[blk * kTile + key] = (t0 + key < c1) ? f16_value(kd) * sc2 : 0.0f;
             }
         }
@@ -403,7 +447,10 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
                 const uint32_t* w = reinterpret_cast<const uint32_t*>(
                     rk + (uint32_t)(key * WN::KSTR + kofs + 8 * q4) + (cb & ~3));
                 h8 kf;
-                if ((cb & 3) == 2) {
+                if constexpr (F8) {
+                    const uint2 c8 = *reinterpret_cast<const uint2*>(rk + key * WN::KSTR + blk * 32 + 8 * q4);
+                    kf = e4m3_codes(c8.x, c8.y);
+                } else if ((cb & 3) == 2) {
                     const uint32_t x0 = w[0] ^ 0x80808080u, x1 = w[1] ^ 0x80808080u, x2 = w[2] ^ 0x80808080u;
                     kf = k_codes(x0, kSel23, x1, kSel01, x1, kSel23, x2, kSel01);
                 } else {
@@ -528,11 +575,18 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
             if (SROWS * NB % 64 == 0 || u < SROWS * NB) {
                 const int key = hrow + u / NB, blk = u - (u / NB) * NB;
                 const bool live = t0 + key < c1;
-                const uint32_t dm = *reinterpret_cast<const uint32_t*>(rv + key * WN::VSTR + blk * 24);
-                const float dv = live ? f16_value((uint16_t)(dm & 0xFFFF)) : 0.0f;
-                VDa[blk * kTile + key] = dv;
-                dmx = fmaxf(dmx, dv);
-                VMa[key * WN::VMS + blk] = live ? (uint16_t)(dm >> 16) : (uint16_t)0;
+                if constexpr (F8) {
+                    const uint16_t dq = *reinterpret_cast<const uint16_t*>(rv + key * WN::VSTR + 32 * NB + sofs + 2 * blk);
+                    const float dv = live ? f16_value(dq) : 0.0f;
+                    VDa[blk * kTile + key] = dv;
+                    dmx = fmaxf(dmx, dv);
+                } else {
+                    const uint32_t dm = *reinterpret_cast<const uint32_t*>(rv + key * WN::VSTR + blk * 24);
+                    const float dv = live ? f16_value((uint16_t)(dm & 0xFFFF)) : 0.0f;
+                    VDa[blk * kTile + key] = dv;
+                    dmx = fmaxf(dmx, dv);
+                    VMa[key * WN::VMS + blk] = live ? (uint16_t)(dm >> 16) : (uint16_t)0;
+                }
             }
         }
         if constexpr (SH) {
@@ -574,6 +628,30 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
             }
         }
 
+        // ---- P V, FP8: ds_read_b64_tr_b8 of the code bytes of 8 keys gives a
+        // lane dim j16 (and, 16 bytes on, dim 16 + j16) of the block
+        if constexpr (F8) {
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk) {
+                const uint8_t* vb = rv + vkey * WN::VSTR + blk * 32 + 8 * (j16 & 1);
+                const i2 ca = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(vb));
+                const i2 cb = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(vb + 16));
+                const h8 vf0 = e4m3_codes((uint32_t)ca[0], (uint32_t)ca[1]);
+                const h8 vf1 = e4m3_codes((uint32_t)cb[0], (uint32_t)cb[1]);
+                const float4 d0 = *reinterpret_cast<const float4*>(VDa + blk * kTile + 4 * q4);
+                const float4 d1 = *reinterpret_cast<const float4*>(VDa + blk * kTile + 16 + 4 * q4);
+#pragma unroll
+                for (int rt = 0; rt < RTW; ++rt) {
+                    const h8 pa = {(_Float16)(pv[rt][0][0] * d0.x), (_Float16)(pv[rt][0][1] * d0.y),
+                                   (_Float16)(pv[rt][0][2] * d0.z), (_Float16)(pv[rt][0][3] * d0.w),
+                                   (_Float16)(pv[rt][1][0] * d1.x), (_Float16)(pv[rt][1][1] * d1.y),
+                                   (_Float16)(pv[rt][1][2] * d1.z), (_Float16)(pv[rt][1][3] * d1.w)};
+                    oacc[rt][2 * blk] = dec::mfma(pa, vf0, oacc[rt][2 * blk]);
+                    oacc[rt][2 * blk + 1] = dec::mfma(pa, vf1, oacc[rt][2 * blk + 1]);
+                }
+                if (NB > 4) asm volatile("" ::: "memory");
+            }
+        } else {
         // ---- P V with the V codes built from the q5_1 bytes of 8 keys per lane group
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) {
@@ -621,6 +699,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
                 macc[rt] = dec::mfma(pu, mb, macc[rt]);
             }
         }
+        }   // q5_1
         if constexpr (SH) {
             lds_barrier();                          // both copies of V(t) are read
             if (has2) issue_v(tn + kTile, tb);
@@ -632,7 +711,9 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
         for (int it = mine; it < nit; ++it) __builtin_amdgcn_s_barrier();
 
     // ---- finish: row sums over the four lane groups; offsets into O
-    const float ounit = dec::pow2(24 + vsh);   // the code products carry 2^-24, P 2^-vsh
+    // q5_1 code products carry 2^-24 (codes as fp16 subnormals), FP8 ones
+    // none; P carries 2^-vsh
+    const float ounit = dec::pow2((F8 ? 0 : 24) + vsh);
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
         float l = lsum[rt];
@@ -643,7 +724,8 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
         for (int dt = 0; dt < 2 * NB; ++dt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                oacc[rt][dt][i] = fmaf(oacc[rt][dt][i], ounit, __shfl(macc[rt][i], 16 * q4 + dt / 2));
+                oacc[rt][dt][i] = F8 ? oacc[rt][dt][i] * ounit
+                                     : fmaf(oacc[rt][dt][i], ounit, __shfl(macc[rt][i], 16 * q4 + dt / 2));
     }
     // ---- row streams: the other streams hand (m, l, O) to stream 0 through
     // their own LDS buffers (lane-major, so that the 64 lanes hit 64 banks);

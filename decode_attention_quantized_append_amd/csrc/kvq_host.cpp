@@ -57,8 +57,10 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 kvq_status check_config(const kvq_config* c) {
     if (!c) return fail(KVQ_EINVAL, "config is NULL");
-    if (c->k_fmt != KVQ_FMT_Q8_0 || c->v_fmt != KVQ_FMT_Q5_1)
-        return fail(KVQ_EUNSUPPORTED, "only K = q8_0 and V = q5_1 are implemented");
+    const bool q8q5 = c->k_fmt == KVQ_FMT_Q8_0 && c->v_fmt == KVQ_FMT_Q5_1;
+    const bool f8 = c->k_fmt == KVQ_FMT_E4M3 && c->v_fmt == KVQ_FMT_E4M3;
+    if (!q8q5 && !f8)
+        return fail(KVQ_EUNSUPPORTED, "the formats must be K = q8_0 with V = q5_1, or K = V = e4m3");
     if (c->n_seqs < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1)
         return fail(KVQ_EINVAL, "n_seqs, n_q_heads and n_kv_heads must be >= 1");
     if (c->n_q_heads % c->n_kv_heads != 0)
@@ -71,6 +73,12 @@ kvq_status check_config(const kvq_config* c) {
     if (c->window < 0 || c->ring_step < 0) return fail(KVQ_EINVAL, "window and ring_step must be >= 0");
     if (c->ring_step > 0 && (c->window <= 0 || (int64_t)c->window + c->ring_step > c->capacity))
         return fail(KVQ_EINVAL, "a ring needs window > 0 and window + ring_step <= capacity");
+    // FP8 rows are decoded by the stream kernel only: 64-, 128- or 256-dim
+    // heads, and a ring base that stays on a 32-row boundary
+    if (f8 && c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)
+        return fail(KVQ_EUNSUPPORTED, "e4m3 K/V need head_dim 64, 128 or 256");
+    if (f8 && c->ring_step % 32 != 0)
+        return fail(KVQ_EUNSUPPORTED, "e4m3 K/V need a ring_step that is a multiple of 32");
     int64_t row = (int64_t)c->n_kv_heads * c->head_dim / 32 * 34;
     if (row * (int64_t)c->capacity > (int64_t)INT32_MAX * 4)
         return fail(KVQ_EUNSUPPORTED, "a session plane above 8 GiB is not supported");
@@ -82,16 +90,19 @@ kvq_status check_config(const kvq_config* c) {
 void sizes_of(const kvq_config* c, kvq_sizes* s) {
     int64_t blocks = (int64_t)c->n_kv_heads * c->head_dim / 32;
     s->k_row_bytes = (size_t)(blocks * 34);
-    s->v_row_bytes = (size_t)(blocks * 24);
+    s->v_row_bytes = (size_t)(blocks * (c->v_fmt == KVQ_FMT_E4M3 ? 34 : 24));
     s->k_session_stride = (size_t)round_up((int64_t)s->k_row_bytes * c->capacity, 256);
     s->v_session_stride = (size_t)round_up((int64_t)s->v_row_bytes * c->capacity, 256);
-    // + a 256-byte tail: the decode reads each KV head's q8_0 blocks from the
-    // 16-byte boundary at or below them, up to 12 bytes past the last head's
-    // blocks of a row
+    // + a 256-byte tail on each: the decode reads each KV head's q8_0 blocks
+    // from the 16-byte boundary at or below them, up to 12 bytes past the last
+    // head's blocks of a row, and an FP8 row's scales as the 16-byte piece that
+    // holds them, up to 12 bytes past the row
     s->k_planes_bytes = s->k_session_stride * (size_t)c->n_seqs + 256;
-    s->v_planes_bytes = s->v_session_stride * (size_t)c->n_seqs;
+    s->v_planes_bytes = s->v_session_stride * (size_t)c->n_seqs + 256;
     s->counters_bytes = (size_t)round_up(((int64_t)2 * c->n_seqs + 4) * 4, 256);
 }
+
+bool is_f8(const kvq_config& c) { return c.k_fmt == KVQ_FMT_E4M3; }
 
 int32_t* len_d(const kvq_cache* h) { return h->counters; }
 int32_t* base_d(const kvq_cache* h) { return h->counters + h->cfg.n_seqs; }
@@ -145,7 +156,7 @@ bool stream_ok(const kvq_config& c, int R, int gh) {
     if (gh < 1 || c.n_kv_heads % gh != 0) return false;
     const int RT = (R + 15) / 16;
     if (gh > (RT == 1 ? 8 : 4)) return false;
-    return gh * kvq::stream_wave_bytes(NB) <= kvq::kLdsBytes;
+    return gh * kvq::stream_wave_bytes(NB, is_f8(c)) <= kvq::kLdsBytes;
 }
 
 // Can the stream kernel run two waves per KV head (two row streams) in one
@@ -154,7 +165,7 @@ bool stream_rs2_ok(const kvq_config& c, int R, int gh) {
     const int NB = c.head_dim / 32;
     if (R > 16) return false;
     const int waves = 4 * kvq::stream_waves_per_simd(NB, 1, false);
-    return 2 * gh * kvq::stream_wave_bytes(NB) <= kvq::kLdsBytes && 2 * gh <= waves;
+    return 2 * gh * kvq::stream_wave_bytes(NB, is_f8(c)) <= kvq::kLdsBytes && 2 * gh <= waves;
 }
 
 // Can the stream kernel give each of the two 16-row groups of R > 16 query
@@ -164,7 +175,7 @@ bool stream_rg2_ok(const kvq_config& c, int R, int gh, bool f32_queries) {
     const int NB = c.head_dim / 32;
     if (R <= 16) return false;
     const int waves = 4 * kvq::stream_waves_per_simd(NB, 1, f32_queries);
-    return 2 * gh * kvq::stream_wave_bytes(NB) <= kvq::kLdsBytes && 2 * gh <= waves;
+    return 2 * gh * kvq::stream_wave_bytes(NB, is_f8(c)) <= kvq::kLdsBytes && 2 * gh <= waves;
 }
 
 // Can the stream kernel give each 128- or 256-dim KV head two waves of half
@@ -174,7 +185,7 @@ bool stream_ds_ok(const kvq_config& c, int R, int gh) {
     if ((c.head_dim != 128 && c.head_dim != 256) || R <= 16 || R > 32) return false;
     if (gh < 1 || c.n_kv_heads % gh != 0) return false;
     if (2 * gh > 8 || 2 * gh > 4 * kvq::stream_ds_waves_per_simd(c.head_dim / 64)) return false;
-    return gh * 2 * kvq::stream_ds_wave_bytes(c.head_dim) <= kvq::kLdsBytes;
+    return gh * 2 * kvq::stream_ds_wave_bytes(c.head_dim, is_f8(c)) <= kvq::kLdsBytes;
 }
 
 // Can dim halves also run two row streams per head (four waves per head,
@@ -185,7 +196,7 @@ bool stream_ds_rs2_ok(const kvq_config& c, int R, int gh) {
     if (c.head_dim != 256 || !stream_ds_ok(c, R, gh)) return false;
     const int waves = 4 * gh;
     return waves <= 8 && waves <= 4 * kvq::stream_ds_waves_per_simd(c.head_dim / 64) &&
-           gh * 4 * kvq::stream_ds_wave_bytes(c.head_dim) <= kvq::kLdsBytes;
+           gh * 4 * kvq::stream_ds_wave_bytes(c.head_dim, is_f8(c)) <= kvq::kLdsBytes;
 }
 
 // Is every session's first visible row, rounded down to 32, still resident?
@@ -219,12 +230,12 @@ bool choose_kernel(const kvq_cache* h, int R, int32_t T, bool f32_queries, Plan*
     p->rows = 256;
     int want = h->decode_kernel;
     if (want == KVQ_DECODE_AUTO) want = (NB == 2 || NB == 4 || NB == 8) ? KVQ_DECODE_STREAM : KVQ_DECODE_PER_HEAD;
-    if (want == KVQ_DECODE_PER_HEAD) return true;
+    if (want == KVQ_DECODE_PER_HEAD) return !is_f8(c);   // the per-head kernel reads q8_0 / q5_1 only
     // The stream kernel starts a session's first tile at the first visible
     // row rounded down to 32 and reads it whole, so that row must still be
     // resident (at or above base); else one KV head per workgroup, whose
     // loads clamp rows to the visible range.
-    if (!aligned_start_resident(h, T)) return true;
+    if (!aligned_start_resident(h, T)) return !is_f8(c);   // FP8 rings rebase in 32-row steps: never
     // 128- and 256-dim heads with 17..32 query rows: two waves per head,
     // each half of the dims (no unpacking done twice), in independent
     // workgroups of one head unless a head group is set
@@ -242,7 +253,7 @@ bool choose_kernel(const kvq_cache* h, int R, int32_t T, bool f32_queries, Plan*
     p->ds = 1;
     p->rs = 1;
     p->rg = 1;
-    p->lds = gh * kvq::stream_wave_bytes(NB);
+    p->lds = gh * kvq::stream_wave_bytes(NB, is_f8(c));
     p->rows = kvq::stream_rows_per_buffer(NB);
     if (ds) {
         // two waves per KV head, each half of a 128- or 256-dim head's
@@ -250,7 +261,7 @@ bool choose_kernel(const kvq_cache* h, int R, int32_t T, bool f32_queries, Plan*
         if (!stream_ds_ok(c, R, gh)) return false;
         p->ds = 2;
         p->rs = 0;
-        p->lds = gh * 2 * kvq::stream_ds_wave_bytes(c.head_dim);
+        p->lds = gh * 2 * kvq::stream_ds_wave_bytes(c.head_dim, is_f8(c));
         return true;
     }
     // sub_tiles = waves per KV head: row streams for R <= 16 query rows,
@@ -262,7 +273,7 @@ bool choose_kernel(const kvq_cache* h, int R, int32_t T, bool f32_queries, Plan*
         p->rg = 1;
     }
     if (p->rs == 2 && !stream_rs2_ok(c, R, gh)) return false;
-    p->lds = gh * std::max(1, p->rs) * p->rg * kvq::stream_wave_bytes(NB);
+    p->lds = gh * std::max(1, p->rs) * p->rg * kvq::stream_wave_bytes(NB, is_f8(c));
     p->rows = kvq::stream_rows_per_buffer(NB);
     return true;
 }
@@ -296,8 +307,8 @@ Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nul
             const int rtw = p.rg == 2 ? 1 : RT;   // row tiles per wave
             const int64_t waves_per_cu = ds ? 4 * kvq::stream_ds_waves_per_simd(c.head_dim / 64)
                                             : 4 * kvq::stream_waves_per_simd(c.head_dim / 32, rtw, f32_queries);
-            const int64_t lds = ds ? p.gh * rs * 2 * kvq::stream_ds_wave_bytes(c.head_dim)
-                                   : p.gh * rs * p.rg * kvq::stream_wave_bytes(c.head_dim / 32);
+            const int64_t lds = ds ? p.gh * rs * 2 * kvq::stream_ds_wave_bytes(c.head_dim, is_f8(c))
+                                   : p.gh * rs * p.rg * kvq::stream_wave_bytes(c.head_dim / 32, is_f8(c));
             const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kvq::kLdsBytes / lds,
                                                                            waves_per_cu / waves_per_wg));
             const int64_t slots = (int64_t)h->cus * per_cu;
@@ -317,8 +328,8 @@ Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nul
             const bool rs2 = p.ds == 2 ? stream_ds_rs2_ok(c, R, p.gh) : stream_rs2_ok(c, R, p.gh) && !f32_queries;
             if (p.rs == 0) p.rs = (rs2 && (chunk > 0 ? chunk : one_round(2)) >= 4 * 32) ? 2 : 1;
             if (p.rs == 2 && !rs2 && fits) *fits = false;
-            p.lds = p.ds == 2 ? p.gh * p.rs * 2 * kvq::stream_ds_wave_bytes(c.head_dim)
-                              : p.gh * p.rs * p.rg * kvq::stream_wave_bytes(c.head_dim / 32);
+            p.lds = p.ds == 2 ? p.gh * p.rs * 2 * kvq::stream_ds_wave_bytes(c.head_dim, is_f8(c))
+                              : p.gh * p.rs * p.rg * kvq::stream_wave_bytes(c.head_dim / 32, is_f8(c));
         }
         if (chunk <= 0) {
             chunk = one_round(p.rs);
@@ -329,7 +340,7 @@ Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nul
             if (h->head_group == 0 && p.rs == 1 && p.rg == 1 && p.ds == 1 &&
                 p.gh % 2 == 0 && chunk <= p.rows) {
                 p.gh /= 2;
-                p.lds = p.gh * kvq::stream_wave_bytes(c.head_dim / 32);
+                p.lds = p.gh * kvq::stream_wave_bytes(c.head_dim / 32, is_f8(c));
                 chunk = 2 * p.rows;
             }
         }
@@ -390,6 +401,7 @@ kvq_status decode_impl(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, 
     if (!aligned(ws, 256)) return fail(KVQ_EINVAL, "workspace must be 256-byte aligned");
     kvq::DecodeParams dp{};
     dp.q = q;
+    dp.f8 = is_f8(c);
     dp.dtype = dtype;
     dp.B = c.n_seqs;
     dp.T = T;
@@ -586,6 +598,7 @@ kvq_status kvq_append(kvq_cache* h, const void* k_new, const void* v_new, kvq_dt
         ap.base_d = base_d(h);
         ap.done = scratch_d(h);
         ap.overflow = scratch_d(h) + 1;
+        ap.f8 = is_f8(c);
         ap.dtype = dtype;
         ap.B = B;
         ap.T = T;
@@ -652,6 +665,7 @@ kvq_status kvq_importance(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t 
     }
     kvq::ImportanceParams ip{};
     ip.q = q;
+    ip.f8 = is_f8(c);
     ip.dtype = dtype;
     ip.B = c.n_seqs;
     ip.T = T;

@@ -29,6 +29,7 @@ struct AppendParams {
     int32_t* base_d;
     int32_t* done;              // completion counter, 0 between launches
     int32_t* overflow;          // set to 1 when rows did not fit the plane (sticky)
+    int32_t f8;                 // 1: K and V as FP8 rows (codes, then scales); 0: q8_0 / q5_1
     int32_t dtype;              // kvq_dtype
     int32_t B;                  // sessions in the input tensors
     int32_t T;                  // rows per session in the input tensors
@@ -73,6 +74,7 @@ struct MoveParams {
 // imp[b][j - base] += sum over (t, h) of exp(scale q.K'_j - lse[b, t, h]).
 struct ImportanceParams {
     const void* q;              // [B, T, H, hd]
+    int32_t f8;                 // K as FP8 rows (1) or q8_0 blocks (0)
     int32_t dtype;
     int32_t B, T, H, Hkv, hd, hpk, window, capacity;
     const uint8_t* k_planes;
@@ -114,19 +116,44 @@ struct StreamWin {
     static_assert(NKI <= 32 && NVI <= 32, "load counts must fit vmcnt");
 };
 
-inline int stream_wave_bytes(int NB) {
+// The same for FP8 rows, where a head's codes are 32 * NB contiguous,
+// 16-byte aligned bytes of the row and its NB fp16 scales lie in one 16-byte
+// piece of the row's scale area: a row window is the 2 NB code pieces plus
+// that piece (an odd count), for K and for V alike.  No V offsets.
+template <int NB>
+struct StreamWinF8 {
+    static constexpr int KW = 2 * NB + 1;                       // K pieces per row window
+    static constexpr int KWP = KW;
+    static constexpr int VW = KW;
+    static constexpr int VWP = VW;
+    static constexpr int TR = kRowTile;
+    static constexpr int KSTR = KWP * 16, VSTR = VWP * 16;
+    static constexpr int NKI = (TR * KWP + 63) / 64;
+    static constexpr int NVI = (TR * VWP + 63) / 64;
+    static constexpr int KB = 0;
+    static constexpr int VB = TR * KSTR;
+    static constexpr int SC = 32 * NB;                          // scale piece within a row window
+    static constexpr int VMS = 0;
+    static constexpr int KS = VB + TR * VSTR;                   // f32 [NB][32] K scales * scale * log2 e
+    static constexpr int VD = KS + NB * kRowTile * 4;           // f32 [NB][32] V scales
+    static constexpr int VM = VD + NB * kRowTile * 4;           // (no offsets)
+    static constexpr int BYTES = VM;
+    static_assert(NKI <= 32 && NVI <= 32, "load counts must fit vmcnt");
+};
+
+inline int stream_wave_bytes(int NB, bool f8 = false) {
     switch (NB) {
-        case 2: return StreamWin<2>::BYTES;
-        case 4: return StreamWin<4>::BYTES;
-        case 8: return StreamWin<8>::BYTES;
+        case 2: return f8 ? StreamWinF8<2>::BYTES : StreamWin<2>::BYTES;
+        case 4: return f8 ? StreamWinF8<4>::BYTES : StreamWin<4>::BYTES;
+        case 8: return f8 ? StreamWinF8<8>::BYTES : StreamWin<8>::BYTES;
         default: return 0;
     }
 }
 // LDS bytes per wave of the dim-split stream kernel (two waves per head of
 // head_dim / 2 dims each, both row tiles): the half-head window buffer and
 // two slots of partial scores.
-inline int stream_ds_wave_bytes(int head_dim) {
-    return (head_dim == 256 ? StreamWin<4>::BYTES : StreamWin<2>::BYTES) + 2 * 2 * 2 * 64 * 16;
+inline int stream_ds_wave_bytes(int head_dim, bool f8 = false) {
+    return stream_wave_bytes(head_dim == 256 ? 4 : 2, f8) + 2 * 2 * 2 * 64 * 16;
 }
 inline int stream_rows_per_buffer(int) { return kRowTile; }
 // Waves per SIMD the stream kernel is compiled for (its register budget is
@@ -146,6 +173,7 @@ enum DecodeKernel : int32_t { kPerHead = 0, kStream = 2 };
 // Split-K decode plus the log-sum-exp combine.
 struct DecodeParams {
     const void* q;              // [B, T, H, hd]
+    int32_t f8;                 // 1: K and V as FP8 rows (codes, then scales); 0: q8_0 / q5_1
     int32_t dtype;
     int32_t B, T, H, Hkv, hd, hpk, window;
     int32_t Tg;                 // query rows per decode workgroup: the grid's y index

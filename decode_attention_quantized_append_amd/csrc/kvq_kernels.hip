@@ -53,6 +53,22 @@ __device__ __forceinline__ float f16_value(uint16_t b) {
     return static_cast<float>(__builtin_bit_cast(_Float16, b));
 }
 
+// The OCP FP8 E4M3 code nearest to y (finite): bit 7 the sign (kept also
+// when the magnitude rounds to zero), magnitudes from 2^-6 up rounded to a
+// 3-bit fraction half to even, below 2^-6 to a multiple of 2^-9 half to
+// even, and everything past 448 (the largest finite value) saturated to 448.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+    const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+    const float a = fabsf(y);
+    if (a > 448.0f) return sign | 0x7Eu;
+    if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);   // 0 .. 8; 8 is 2^-6 = code 0x08
+    uint32_t u = __float_as_uint(a);
+    u += 0x7FFFFu + ((u >> 20) & 1u);          // round the 23-bit fraction to 3 bits, half to even
+    const uint32_t e = (u >> 23) - 120u;       // biased exponent 127 -> 7
+    const uint32_t code = (e << 3) | ((u >> 20) & 7u);
+    return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
@@ -143,6 +159,42 @@ __device__ __forceinline__ void append_unit(const AppendParams& p, int64_t unit,
         const size_t src = ((size_t)b * p.T + t) * (size_t)(p.Hkv * p.hd) + (size_t)blk * 32 + lane;
         xk = load_in(p.k_new, p.dtype, src);
         xv = load_in(p.v_new, p.dtype, src);
+    }
+    if (p.f8) {
+        // FP8 rows: each block's fp16 scale d = amax / 448, code = e4m3(x /
+        // stored d); a row holds its blocks' codes, then their scales
+        const int n_elem = nblk * 32;
+        const int64_t row_bytes = (int64_t)nblk * 34;
+        float ak = fabsf(xk), av = fabsf(xv);
+#pragma unroll
+        for (int m = 16; m >= 1; m >>= 1) {
+            ak = fmaxf(ak, __shfl_xor(ak, m));
+            av = fmaxf(av, __shfl_xor(av, m));
+        }
+        const uint16_t dk = f16_bits(ak / 448.0f), dv = f16_bits(av / 448.0f);
+        const float dks = f16_value(dk), dvs = f16_value(dv);
+        const uint32_t ck = dks != 0.0f ? e4m3_code(xk / dks) : 0u;
+        const uint32_t cv = dvs != 0.0f ? e4m3_code(xv / dvs) : 0u;
+        // four lanes' codes per word (lanes 4i .. 4i+3 of the half wave)
+        uint32_t wk = ck, wv = cv;
+#pragma unroll
+        for (int s = 1; s < 4; ++s) {
+            wk |= (uint32_t)__shfl_down((int)ck, s) << (8 * s);
+            wv |= (uint32_t)__shfl_down((int)cv, s) << (8 * s);
+        }
+        if (active) {
+            uint8_t* kr = p.k_planes + (int64_t)b * p.k_stride + prow * row_bytes;
+            uint8_t* vr = p.v_planes + (int64_t)b * p.v_stride + prow * row_bytes;
+            if ((lane & 3) == 0) {
+                *reinterpret_cast<uint32_t*>(kr + blk * 32 + lane) = wk;
+                *reinterpret_cast<uint32_t*>(vr + blk * 32 + lane) = wv;
+            }
+            if (lane == 0) {
+                *reinterpret_cast<uint16_t*>(kr + n_elem + 2 * blk) = dk;
+                *reinterpret_cast<uint16_t*>(vr + n_elem + 2 * blk) = dv;
+            }
+        }
+        return;
     }
     // q8_0
     float amax = fabsf(xk);
@@ -346,9 +398,10 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
 // Workgroups whose 16 keys all lie past the session's length return at once
 // (the grid covers the longest session, or in graph mode the plane).
 constexpr int kImpKeys = 16;
-// NB = head_dim / 32 (1 .. 8) and the query dtype are template arguments, so
+// NB = head_dim / 32 (1 .. 8), the query dtype and the K format (F8: FP8 rows,
+// the codes then the scales; else q8_0 blocks) are template arguments, so
 // that no branch separates the loads of a pair from each other.
-template <int NB, bool F32>
+template <int NB, bool F32, bool F8>
 __global__ __launch_bounds__(256) void importance_kernel(ImportanceParams p) {
     using dec::f4;
     using dec::h8;
@@ -389,12 +442,24 @@ __global__ __launch_bounds__(256) void importance_kernel(ImportanceParams p) {
 #pragma unroll
             for (int blk = 0; blk < 8; ++blk) {
                 if (blk < nb) {
-                    // the lane's 8 codes start 2 bytes into a word or on one:
-                    // three aligned words (one 12-byte load) hold them
-                    const uint8_t* const kb = krow_a + (g * nb + blk) * 34;
-                    const uintptr_t a = reinterpret_cast<uintptr_t>(kb + 2 + 8 * q4);
-                    __builtin_memcpy(kw[blk], reinterpret_cast<const void*>(a & ~uintptr_t(3)), 12);
-                    ks[blk] = *reinterpret_cast<const uint16_t*>(kb);
+                    if constexpr (F8) {
+                        // the lane's 8 codes are 8 bytes on a word boundary (a
+                        // row is a whole number of words); the scale is in the
+                        // row's scale area
+                        const uint32_t* const kc =
+                            reinterpret_cast<const uint32_t*>(krow_a + (g * nb + blk) * 32 + 8 * q4);
+                        kw[blk][0] = kc[0];
+                        kw[blk][1] = kc[1];
+                        kw[blk][2] = 0u;
+                        ks[blk] = *reinterpret_cast<const uint16_t*>(krow_a + p.Hkv * p.hd + 2 * (g * nb + blk));
+                    } else {
+                        // the lane's 8 codes start 2 bytes into a word or on one:
+                        // three aligned words (one 12-byte load) hold them
+                        const uint8_t* const kb = krow_a + (g * nb + blk) * 34;
+                        const uintptr_t a = reinterpret_cast<uintptr_t>(kb + 2 + 8 * q4);
+                        __builtin_memcpy(kw[blk], reinterpret_cast<const void*>(a & ~uintptr_t(3)), 12);
+                        ks[blk] = *reinterpret_cast<const uint16_t*>(kb);
+                    }
                 }
             }
         }
@@ -421,14 +486,18 @@ __global__ __launch_bounds__(256) void importance_kernel(ImportanceParams p) {
 #pragma unroll
             for (int blk = 0; blk < 8; ++blk) {
                 if (blk < nb) {
-                    const uintptr_t a = reinterpret_cast<uintptr_t>(krow_a + (g * nb + blk) * 34 + 2 + 8 * q4);
                     const uint32_t w0 = ka_ok ? kw[blk][0] : 0u;
                     const uint32_t w1 = ka_ok ? kw[blk][1] : 0u;
                     const uint32_t w2 = ka_ok ? kw[blk][2] : 0u;
-                    const bool odd = (a & 2) != 0;
-                    const uint32_t c0 = odd ? __builtin_amdgcn_alignbit(w1, w0, 16) : w0;
-                    const uint32_t c1 = odd ? __builtin_amdgcn_alignbit(w2, w1, 16) : w1;
-                    kf[blk] = dec::k_codes_f16(c0, c1);
+                    if constexpr (F8) {
+                        kf[blk] = stream::e4m3_codes(w0, w1);
+                    } else {
+                        const uintptr_t a = reinterpret_cast<uintptr_t>(krow_a + (g * nb + blk) * 34 + 2 + 8 * q4);
+                        const bool odd = (a & 2) != 0;
+                        const uint32_t c0 = odd ? __builtin_amdgcn_alignbit(w1, w0, 16) : w0;
+                        const uint32_t c1 = odd ? __builtin_amdgcn_alignbit(w2, w1, 16) : w1;
+                        kf[blk] = dec::k_codes_f16(c0, c1);
+                    }
                     // the scale of this lane's key, handed to the lanes whose
                     // D rows are keys 4 q4 + i
                     const float dself = ka_ok ? f16_value(ks[blk]) : 0.0f;
@@ -624,11 +693,11 @@ int launch_decode_t(const DecodeParams& p, hipStream_t st, const char** err) {
     return check(err);
 }
 
-template <int NB, int RTW, bool QLO, int RS, int RG, int DS = 1>
+template <int NB, int RTW, bool QLO, int RS, int RG, int DS, bool F8>
 int launch_stream_t(const DecodeParams& p, hipStream_t st, const char** err) {
     static bool configured = false;
     if (!configured) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&stream::decode_stream<NB, RTW, QLO, RS, RG, DS>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&stream::decode_stream<NB, RTW, QLO, RS, RG, DS, F8>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) != hipSuccess) {
             *err = "cannot raise the LDS limit of the decode kernel";
             return 1;
@@ -637,13 +706,13 @@ int launch_stream_t(const DecodeParams& p, hipStream_t st, const char** err) {
     }
     const int items = std::max(1, p.units) * (p.Hkv / p.gh);
     const int grid = (items + 7) & ~7;
-    hipLaunchKernelGGL((stream::decode_stream<NB, RTW, QLO, RS, RG, DS>), dim3(grid, (p.T + p.Tg - 1) / p.Tg),
+    hipLaunchKernelGGL((stream::decode_stream<NB, RTW, QLO, RS, RG, DS, F8>), dim3(grid, (p.T + p.Tg - 1) / p.Tg),
                        dim3(64 * p.gh * RS * RG * DS), p.lds, st, p);
     return check(err);
 }
 
-template <int NB>
-int launch_stream_nb(const DecodeParams& p, hipStream_t st, const char** err) {
+template <int NB, bool F8>
+int launch_stream_fmt(const DecodeParams& p, hipStream_t st, const char** err) {
     const int R = p.Tg * p.hpk;   // query rows per KV head of one group
     const bool qlo = p.dtype == 0;
     if (R > 16) {
@@ -651,27 +720,35 @@ int launch_stream_nb(const DecodeParams& p, hipStream_t st, const char** err) {
             constexpr int NH = NB / 2;
             if constexpr (NB == 8 || NB == 4) {
                 if (p.rs == 2)   // and two row streams
-                    return qlo ? launch_stream_t<NH, 2, true, 2, 1, 2>(p, st, err)
-                               : launch_stream_t<NH, 2, false, 2, 1, 2>(p, st, err);
-                return qlo ? launch_stream_t<NH, 2, true, 1, 1, 2>(p, st, err)
-                           : launch_stream_t<NH, 2, false, 1, 1, 2>(p, st, err);
+                    return qlo ? launch_stream_t<NH, 2, true, 2, 1, 2, F8>(p, st, err)
+                               : launch_stream_t<NH, 2, false, 2, 1, 2, F8>(p, st, err);
+                return qlo ? launch_stream_t<NH, 2, true, 1, 1, 2, F8>(p, st, err)
+                           : launch_stream_t<NH, 2, false, 1, 1, 2, F8>(p, st, err);
             }
             *err = "dim halves are built for head_dim 128 and 256";
             return 1;
         }
         if (p.rg == 2)   // two 16-row groups, one wave each
-            return qlo ? launch_stream_t<NB, 1, true, 1, 2>(p, st, err) : launch_stream_t<NB, 1, false, 1, 2>(p, st, err);
-        return qlo ? launch_stream_t<NB, 2, true, 1, 1>(p, st, err) : launch_stream_t<NB, 2, false, 1, 1>(p, st, err);
+            return qlo ? launch_stream_t<NB, 1, true, 1, 2, 1, F8>(p, st, err)
+                       : launch_stream_t<NB, 1, false, 1, 2, 1, F8>(p, st, err);
+        return qlo ? launch_stream_t<NB, 2, true, 1, 1, 1, F8>(p, st, err)
+                   : launch_stream_t<NB, 2, false, 1, 1, 1, F8>(p, st, err);
     }
     if (p.rs == 2) {
         // two row streams: bf16 queries and head_dim 64 or 128 only (the planner's rule)
         if constexpr (NB <= 4) {
-            if (!qlo) return launch_stream_t<NB, 1, false, 2, 1>(p, st, err);
+            if (!qlo) return launch_stream_t<NB, 1, false, 2, 1, 1, F8>(p, st, err);
         }
         *err = "two row streams are not built for this shape";
         return 1;
     }
-    return qlo ? launch_stream_t<NB, 1, true, 1, 1>(p, st, err) : launch_stream_t<NB, 1, false, 1, 1>(p, st, err);
+    return qlo ? launch_stream_t<NB, 1, true, 1, 1, 1, F8>(p, st, err)
+               : launch_stream_t<NB, 1, false, 1, 1, 1, F8>(p, st, err);
+}
+
+template <int NB>
+int launch_stream_nb(const DecodeParams& p, hipStream_t st, const char** err) {
+    return p.f8 ? launch_stream_fmt<NB, true>(p, st, err) : launch_stream_fmt<NB, false>(p, st, err);
 }
 
 template <int NB>
@@ -753,6 +830,10 @@ int launch_partials(const DecodeParams& p, hipStream_t st, const char** err) {
             default: *err = "the stream decode supports head_dim 64, 128 and 256"; return 1;
         }
     }
+    if (p.f8) {
+        *err = "the per-head decode reads q8_0 / q5_1 blocks only";
+        return 1;
+    }
     switch (p.hd / 32) {
         case 1: return launch_decode_nb<1>(p, st, err);
         case 2: return launch_decode_nb<2>(p, st, err);
@@ -770,15 +851,23 @@ int launch_partials(const DecodeParams& p, hipStream_t st, const char** err) {
 template <bool F32>
 bool launch_importance_dtype(const ImportanceParams& p, hipStream_t st) {
     const dim3 grid(p.tiles, p.B), block(256);
+    if (p.f8) {   // FP8 rows: head_dim 64, 128 or 256
+        switch (p.hd / 32) {
+            case 2: hipLaunchKernelGGL((importance_kernel<2, F32, true>), grid, block, 0, st, p); return true;
+            case 4: hipLaunchKernelGGL((importance_kernel<4, F32, true>), grid, block, 0, st, p); return true;
+            case 8: hipLaunchKernelGGL((importance_kernel<8, F32, true>), grid, block, 0, st, p); return true;
+            default: return false;
+        }
+    }
     switch (p.hd / 32) {
-        case 1: hipLaunchKernelGGL((importance_kernel<1, F32>), grid, block, 0, st, p); return true;
-        case 2: hipLaunchKernelGGL((importance_kernel<2, F32>), grid, block, 0, st, p); return true;
-        case 3: hipLaunchKernelGGL((importance_kernel<3, F32>), grid, block, 0, st, p); return true;
-        case 4: hipLaunchKernelGGL((importance_kernel<4, F32>), grid, block, 0, st, p); return true;
-        case 5: hipLaunchKernelGGL((importance_kernel<5, F32>), grid, block, 0, st, p); return true;
-        case 6: hipLaunchKernelGGL((importance_kernel<6, F32>), grid, block, 0, st, p); return true;
-        case 7: hipLaunchKernelGGL((importance_kernel<7, F32>), grid, block, 0, st, p); return true;
-        case 8: hipLaunchKernelGGL((importance_kernel<8, F32>), grid, block, 0, st, p); return true;
+        case 1: hipLaunchKernelGGL((importance_kernel<1, F32, false>), grid, block, 0, st, p); return true;
+        case 2: hipLaunchKernelGGL((importance_kernel<2, F32, false>), grid, block, 0, st, p); return true;
+        case 3: hipLaunchKernelGGL((importance_kernel<3, F32, false>), grid, block, 0, st, p); return true;
+        case 4: hipLaunchKernelGGL((importance_kernel<4, F32, false>), grid, block, 0, st, p); return true;
+        case 5: hipLaunchKernelGGL((importance_kernel<5, F32, false>), grid, block, 0, st, p); return true;
+        case 6: hipLaunchKernelGGL((importance_kernel<6, F32, false>), grid, block, 0, st, p); return true;
+        case 7: hipLaunchKernelGGL((importance_kernel<7, F32, false>), grid, block, 0, st, p); return true;
+        case 8: hipLaunchKernelGGL((importance_kernel<8, F32, false>), grid, block, 0, st, p); return true;
         default: return false;
     }
 }

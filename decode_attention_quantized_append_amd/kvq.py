@@ -20,7 +20,9 @@ NODEV_PATH = os.path.join(_PKG, "libkvq_nodev.so")
 
 KVQ_OK, KVQ_EINVAL, KVQ_ECAPACITY, KVQ_ERANGE, KVQ_EUNSUPPORTED, KVQ_EDEVICE = range(6)
 KVQ_F32, KVQ_BF16 = 0, 1
-KVQ_FMT_Q8_0, KVQ_FMT_Q5_1 = 1, 2
+KVQ_FMT_Q8_0, KVQ_FMT_Q5_1, KVQ_FMT_E4M3 = 1, 2, 3
+# cache formats by name: (k_fmt, v_fmt)
+FORMATS = {"q8_0/q5_1": (KVQ_FMT_Q8_0, KVQ_FMT_Q5_1), "e4m3": (KVQ_FMT_E4M3, KVQ_FMT_E4M3)}
 KVQ_DECODE_AUTO, KVQ_DECODE_PER_HEAD, KVQ_DECODE_STREAM = 0, 1, 3
 STATUS_NAMES = {0: "KVQ_OK", 1: "KVQ_EINVAL", 2: "KVQ_ECAPACITY", 3: "KVQ_ERANGE",
                 4: "KVQ_EUNSUPPORTED", 5: "KVQ_EDEVICE"}
@@ -133,9 +135,9 @@ def _i32_array(values):
     return (ctypes.c_int32 * len(vals))(*vals)
 
 
-def make_config(n_seqs, n_q_heads, n_kv_heads, head_dim, capacity, window=0, ring_step=0):
-    return kvq_config(n_seqs, n_q_heads, n_kv_heads, head_dim, capacity, window, ring_step,
-                      KVQ_FMT_Q8_0, KVQ_FMT_Q5_1)
+def make_config(n_seqs, n_q_heads, n_kv_heads, head_dim, capacity, window=0, ring_step=0, fmt="q8_0/q5_1"):
+    kf, vf = FORMATS[fmt]
+    return kvq_config(n_seqs, n_q_heads, n_kv_heads, head_dim, capacity, window, ring_step, kf, vf)
 
 
 # -- thin wrappers with the C names -------------------------------------------
@@ -257,10 +259,11 @@ class KvqLayerCache:
     `device`.  Tensors passed in must already live on that device."""
 
     def __init__(self, n_seqs, n_q_heads, n_kv_heads, head_dim, capacity, window=0,
-                 ring_step=0, device="cuda", stream=None):
+                 ring_step=0, device="cuda", stream=None, fmt="q8_0/q5_1"):
         import torch
         self.lib = load()
-        self.cfg = make_config(n_seqs, n_q_heads, n_kv_heads, head_dim, capacity, window, ring_step)
+        self.fmt = fmt
+        self.cfg = make_config(n_seqs, n_q_heads, n_kv_heads, head_dim, capacity, window, ring_step, fmt)
         self.sizes = kvq_required_bytes(self.cfg, self.lib)
         self.device = torch.device(device)
         alloc = lambda n: torch.empty(int(n) + 256, dtype=torch.uint8, device=self.device)  # noqa: E731

@@ -80,6 +80,7 @@ class Workload:
     io_dtype: str = "bf16"           # q/k/v input dtype: "f32" or "bf16"
     kv_dist: str = "normal"          # "normal" | "outlier" (outlier channels, v std 0.5)
     rollback_keep: int = 0           # after a T-row verify, keep this many of the T rows
+    fmt: str = "q8_0/q5_1"           # cache format: "q8_0/q5_1" or "e4m3" (K and V FP8 rows)
 
     @property
     def hpk(self) -> int:
@@ -95,7 +96,7 @@ class Workload:
 
     @property
     def v_row_bytes(self) -> int:
-        return self.Hkv * self.hd // 32 * 24
+        return self.Hkv * self.hd // 32 * (34 if self.fmt == "e4m3" else 24)
 
     def lengths(self) -> np.ndarray:
         """Committed rows per session after the step's append (the last query
@@ -220,6 +221,12 @@ WORKLOADS = {
                        rollback_keep=3),
     "prime": Workload("prime", 106, B=1, H=32, Hkv=8, hd=128, T=512, cached=32768,
                       window=4096, kv_dist="outlier"),
+    # the FP8 (e4m3) K/V variant on the two long-context shapes: the same
+    # seeds, so the same inputs, held as FP8 rows
+    "verify_f8": Workload("verify_f8", 105, B=2, H=16, Hkv=4, hd=256, T=8, cached=131072,
+                          rollback_keep=3, fmt="e4m3"),
+    "batched_f8": Workload("batched_f8", 103, B=16, H=40, Hkv=8, hd=128, T=1, cached=0,
+                           ragged=(1024, 32768), fmt="e4m3"),
 }
 
 

@@ -14,6 +14,17 @@
  *     block index/32, lane index%32; head_dim % 32 == 0, so no block
  *     straddles a head.  K row bytes = n_kv_heads*head_dim/32*34, V row bytes
  *     = n_kv_heads*head_dim/32*24.
+ *   - FP8 variant (memra-engine "Module cache" page, kv_fp8_on: full-attention
+ *     layers may hold K and V as e4m3; the pages give no layout): with
+ *     k_fmt = v_fmt = KVQ_FMT_E4M3 every 32-element block has an fp16 scale
+ *     d = amax/448 (round to nearest even) and 32 OCP FP8 E4M3 codes, each the
+ *     code nearest to x / stored d (ties to the even code, magnitudes past 448
+ *     saturating to +-448, the sign kept on zero; all 0 when d is 0); value =
+ *     d * code.  A token row of n = n_kv_heads*head_dim elements holds the
+ *     codes of all its blocks in element order (bytes 0 .. n-1), then the
+ *     blocks' scales in block order (block k's at bytes n + 2k): 34 bytes per
+ *     32 elements for K and for V.  Needs head_dim 64, 128 or 256 and a
+ *     ring_step that is a multiple of 32 (else EUNSUPPORTED).
  *   - Every session has a device-resident committed length len_d (int32) and
  *     ring base base_d (int32).  An append writes its rows at the slot held
  *     in len_d and then advances len_d; a decode takes its length from len_d;
@@ -73,7 +84,8 @@ typedef enum kvq_dtype {
 
 typedef enum kvq_format {
     KVQ_FMT_Q8_0 = 1,
-    KVQ_FMT_Q5_1 = 2
+    KVQ_FMT_Q5_1 = 2,
+    KVQ_FMT_E4M3 = 3   /* FP8 rows, for K and V together (see below) */
 } kvq_format;
 
 /* Geometry of one attention layer's cache for n_seqs sessions. */
@@ -86,20 +98,20 @@ typedef struct kvq_config {
     int32_t window;      /* 0 = full attention; else the sliding-window length */
     int32_t ring_step;   /* 0 = flat [0, capacity); else rebase granularity in rows
                             (needs window > 0 and window + ring_step <= capacity) */
-    int32_t k_fmt;       /* must be KVQ_FMT_Q8_0 */
-    int32_t v_fmt;       /* must be KVQ_FMT_Q5_1 */
+    int32_t k_fmt;       /* KVQ_FMT_Q8_0 with v_fmt KVQ_FMT_Q5_1, or KVQ_FMT_E4M3 for both */
+    int32_t v_fmt;
 } kvq_config;
 
 /* Device bytes the caller must provide for a configuration. */
 typedef struct kvq_sizes {
     size_t k_planes_bytes;    /* n_seqs * k_session_stride + 256 (read-only tail the
                                  decode may read past the last row; never written) */
-    size_t v_planes_bytes;    /* n_seqs * v_session_stride */
+    size_t v_planes_bytes;    /* n_seqs * v_session_stride + 256 (read-only tail as for K) */
     size_t counters_bytes;    /* int32 len_d[B], base_d[B], then library scratch:
                                  [2B] the append's completion counter, [2B + 1]
                                  the overflow word (see kvq_set_graph_mode) */
     size_t k_row_bytes;       /* Hkv*hd/32*34 */
-    size_t v_row_bytes;       /* Hkv*hd/32*24 */
+    size_t v_row_bytes;       /* Hkv*hd/32*24 (q5_1) or Hkv*hd/32*34 (e4m3) */
     size_t k_session_stride;  /* capacity*k_row_bytes rounded up to 256 */
     size_t v_session_stride;  /* capacity*v_row_bytes rounded up to 256 */
 } kvq_sizes;

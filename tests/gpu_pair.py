@@ -39,10 +39,10 @@ def assert_close(got, want, what="", atol=ATOL):
 
 
 class Pair:
-    def __init__(self, B, H, Hkv, hd, capacity, window=0, ring_step=0, io="bf16"):
-        self.B, self.H, self.Hkv, self.hd, self.io = B, H, Hkv, hd, io
-        self.gpu = KvqLayerCache(B, H, Hkv, hd, capacity, window, ring_step, device=DEV)
-        self.ref = OracleCache(B, Hkv, hd, capacity, window, ring_step)
+    def __init__(self, B, H, Hkv, hd, capacity, window=0, ring_step=0, io="bf16", fmt="q8_0/q5_1"):
+        self.B, self.H, self.Hkv, self.hd, self.io, self.fmt = B, H, Hkv, hd, io, fmt
+        self.gpu = KvqLayerCache(B, H, Hkv, hd, capacity, window, ring_step, device=DEV, fmt=fmt)
+        self.ref = OracleCache(B, Hkv, hd, capacity, window, ring_step, fmt=fmt)
         self.vmax = 0.0
 
     def append(self, k, v, counts=None):
@@ -81,7 +81,8 @@ class Pair:
             gk = kp[b].index_select(0, idx).cpu().numpy()
             gv = vp[b].index_select(0, idx).cpu().numpy()
             rk, rv = self.ref.k[b][sel], self.ref.v[b][sel]
-            for name, g, r, bb in (("K", gk, rk, 34), ("V", gv, rv, 24)):
+            vb = 34 if self.fmt == "e4m3" else 24     # an FP8 row shows as 34-byte groups
+            for name, g, r, bb in (("K", gk, rk, 34), ("V", gv, rv, vb)):
                 if not np.array_equal(g, r):
                     i = np.nonzero((g != r).any(1))[0][0]
                     gb, rb = g[i].reshape(-1, bb), r[i].reshape(-1, bb)

@@ -18,7 +18,7 @@ from gpu_pair import Pair  # noqa: E402
 
 def setup(name):
     w = workloads.get(name)
-    p = Pair(w.B, w.H, w.Hkv, w.hd, w.capacity(extra_steps=2), w.window, w.ring_step, io=w.io_dtype)
+    p = Pair(w.B, w.H, w.Hkv, w.hd, w.capacity(extra_steps=2), w.window, w.ring_step, io=w.io_dtype, fmt=w.fmt)
     for counts, starts, T in w.prefill_pieces():
         k, v = w.kv_block(counts, starts, T)
         p.append(k, v, counts)
@@ -32,7 +32,8 @@ def step(w, p, i):
     return w.q(i), w.sink_logits()
 
 
-@pytest.mark.parametrize("name", ["tiny", "qwen_gqa", "batched", "sink_ring", "verify", "prime"])
+@pytest.mark.parametrize("name", ["tiny", "qwen_gqa", "batched", "sink_ring", "verify", "prime", "verify_f8",
+                                  "batched_f8"])
 def test_full_size(name):
     w, p = setup(name)
     q, s = step(w, p, 0)

@@ -81,7 +81,7 @@ def test_required_bytes(lib):
     s = kvq.kvq_required_bytes(cfg, lib)
     assert (s.k_row_bytes, s.v_row_bytes) == (32 * 34, 32 * 24) == (1088, 768)
     assert s.k_session_stride == -(-1088 * 33000 // 256) * 256
-    assert s.k_planes_bytes == 16 * s.k_session_stride + 256 and s.v_planes_bytes == 16 * s.v_session_stride
+    assert s.k_planes_bytes == 16 * s.k_session_stride + 256 and s.v_planes_bytes == 16 * s.v_session_stride + 256
     assert s.counters_bytes >= (2 * 16 + 4) * 4 and s.counters_bytes % 256 == 0
 
 
@@ -573,3 +573,32 @@ def test_decode_noalloc_uses_the_scratch_and_refuses_what_does_not_fit(lib):
     assert log(lib) == [] and "scratch" in kvq.kvq_last_error(lib)
     kvq.kvq_decode(h, Q, kvq.KVQ_BF16, 512, None, 0.1, O, None, WS, 1 << 40, 0, lib)   # the workspace call still works
     assert len(log(lib)) == 1
+
+
+def test_f8_configuration_rules(lib):
+    """K = V = e4m3 rows: 34 bytes per 32 elements for both planes; the stream
+    kernel only (head_dim 64, 128 or 256, ring steps on 32-row boundaries),
+    so the per-head tiling is refused at decode; mixed formats are refused."""
+    s = kvq.kvq_required_bytes(kvq.make_config(2, 8, 2, 128, 100, fmt="e4m3"), lib)
+    assert s.k_row_bytes == s.v_row_bytes == 2 * 4 * 34
+    assert s.v_planes_bytes == 2 * s.v_session_stride + 256
+    E = kvq.KVQ_EUNSUPPORTED
+    assert err(lib, kvq.kvq_required_bytes, kvq.make_config(1, 4, 1, 96, 100, fmt="e4m3")) == E
+    assert err(lib, kvq.kvq_required_bytes, kvq.make_config(1, 4, 1, 64, 100, 40, 10, fmt="e4m3")) == E
+    mixed = kvq.make_config(1, 4, 1, 64, 100)
+    mixed.v_fmt = kvq.KVQ_FMT_E4M3
+    assert err(lib, kvq.kvq_required_bytes, mixed) == E
+    h = create(lib, n_seqs=1, n_q_heads=32, n_kv_heads=8, head_dim=128, capacity=3000, fmt="e4m3")
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 2048, None, 0, lib)
+    p = plan_of(lib, h)
+    assert p["kernel"] == 2
+    kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_PER_HEAD, 0, 0, lib)
+    lib.kvq_nodev_clear()
+    assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 1, None, 0.1, O, None, WS, 1 << 40) == kvq.KVQ_EINVAL
+    assert log(lib) == []
+    # an FP8 ring with 32-row steps keeps the stream kernel at every length
+    h = create(lib, n_seqs=1, n_q_heads=32, n_kv_heads=8, head_dim=128, capacity=100, window=60,
+               ring_step=32, fmt="e4m3")
+    for _ in range(120):
+        kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 1, None, 0, lib)
+        assert plan_of(lib, h)["kernel"] == 2
