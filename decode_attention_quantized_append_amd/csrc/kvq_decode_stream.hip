@@ -91,6 +91,20 @@ __device__ __forceinline__ h8 e4m3_codes(uint32_t lo, uint32_t hi) {
     return (h8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// The reference max of a row that has seen no visible key yet: finite, so
+// that exp2(score - max) needs no test (a masked score is -inf and gives 0),
+// and below every finite score, so that the first one always moves it.
+constexpr float kNoMax = -3.402823466e38f;
+
+// The fp16 steps of keys 4*q4 + i and 16 + 4*q4 + i (i = 0..3) of one block,
+// in the key order of the P V operands.
+__device__ __forceinline__ h8 steps_of(const uint16_t* vd, int q4) {
+    const uint2 a = *reinterpret_cast<const uint2*>(vd + 4 * q4);
+    const uint2 b = *reinterpret_cast<const uint2*>(vd + 16 + 4 * q4);
+    typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(h8, (u4v){a.x, a.y, b.x, b.y});
+}
+
 template <int NL>
 __device__ __forceinline__ void wait_loads_upto() {
     asm volatile("" ::: "memory");
@@ -211,8 +225,9 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
     const int spiece = F8 ? p.Hkv * p.hd + ((hs * 2 * NB) & ~15) : 0;
     const uint8_t* const kwin = p.k_planes + (int64_t)b * p.k_stride + (F8 ? 0 : kstart - kofs);
     const uint8_t* const vwin = p.v_planes + (int64_t)b * p.v_stride + (F8 ? 0 : hs * NB * 24);
-    // per lane, the byte offset of its piece (instruction x) from the tile's first row
-    uint32_t koff[NKH], voff[NVH];
+    // per lane, the byte offset of its piece (instruction x) from the tile's
+    // first row (FP8 K and V rows have one size and layout: one set serves both)
+    uint32_t koff[NKH], voff[F8 ? 1 : NVH];
 #pragma unroll
     for (int x = 0; x < NKH; ++x) {
         const int pc = x * 64 + lane, row = pc / WN::KWP, col = pc - row * WN::KWP;
@@ -220,10 +235,9 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
                      : (uint32_t)((hrow + row) * p.k_row + min(col, WN::KW - 1) * 16);
     }
 #pragma unroll
-    for (int x = 0; x < NVH; ++x) {
+    for (int x = 0; x < (F8 ? 0 : NVH); ++x) {
         const int pc = x * 64 + lane, row = pc / WN::VWP, col = pc - row * WN::VWP;
-        voff[x] = F8 ? (uint32_t)((hrow + row) * p.v_row + (col < 2 * NB ? kstart + col * 16 : spiece))
-                     : (uint32_t)((hrow + row) * p.v_row + min(col, WN::VW - 1) * 16);   // the pad piece re-reads a real one
+        voff[x] = (uint32_t)((hrow + row) * p.v_row + min(col, WN::VW - 1) * 16);   // the pad piece re-reads a real one
     }
     // Copy the K (or V) rows of the tile [t0, t0 + 32) into the buffer.  Rows
     // from c1 on (a session's last tile) are not loaded; rows below lo (first
@@ -250,12 +264,14 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
         uint8_t* const d = tb + WN::VB + hrow * WN::VSTR;
 #pragma unroll
         for (int x = 0; x < NVH; ++x) {
-            uint32_t o = voff[x];
+            uint32_t o = F8 ? koff[x] : voff[x];
             asm volatile("" : "+v"(o));
             if (lane < nrows * WN::VWP - x * 64) dma16(vt, o, d + x * 1024);
         }
     };
 
+    // macc: the q5_1 offset product, whose column NB is the row sums of P
+    // (FP8: a product with ones, every column the row sums)
     f4 oacc[RTW][2 * NB], macc[RTW];
     float mrow[RTW], lsum[RTW];
     int vis_lo[RTW], vis_hi[RTW];
@@ -264,7 +280,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
         macc[rt] = (f4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int dt = 0; dt < 2 * NB; ++dt) oacc[rt][dt] = (f4){0.f, 0.f, 0.f, 0.f};
-        mrow[rt] = -INFINITY;
+        mrow[rt] = kNoMax;
         lsum[rt] = 0.0f;
         vis_lo[rt] = vis_hi[rt] = 0;
         const int r = rb + rt * 16 + j16;
@@ -277,11 +293,13 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
     const int full_lo = max(p.window > 0 ? max(0, len - p.window) : 0, c0);
     const float sc2 = p.scale * kLog2e;
     float* const KSa = reinterpret_cast<float*>(scb + WN::KS);
-    float* const VDa = reinterpret_cast<float*>(scb + WN::VD);
+    uint16_t* const VDa = reinterpret_cast<uint16_t*>(scb + WN::VD);   // fp16 V steps
     uint16_t* const VMa = reinterpret_cast<uint16_t*>(scb + WN::VM);   // q5_1 offsets (not FP8)
     const int vkey = pkey(q4, j16 >> 1);                 // V row of this lane's tr8 reads
     const int mk0 = pkey(q4, j16 >> 2), mk1 = pkey(q4, 4 + (j16 >> 2));
-    const int mc = (4 * (j16 & 3) < NB) ? (j16 & 3) : 0;   // columns past NB of the offset product are unused
+    // columns of the offset product: NB offsets, then ones (column NB gives the
+    // row sums); the columns past the stored ones are unused
+    const int mc = (4 * (j16 & 3) < WN::VMS) ? (j16 & 3) : 0;
     const int sh_rot = ((j16 & 7) - 4) & 31;             // moves bit (j16 & 7) of each byte to bit 4
     const int src_lo = (16 * q4 + 4 + (j16 >> 3)) * 4;   // byte addresses of the lanes holding
     const int src_hi = (16 * q4 + 6 + (j16 >> 3)) * 4;   // this lane's high-bit bytes
@@ -292,6 +310,12 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
     // Row stream str takes the chunk's tiles str, str + rs, ...; a stream
     // with fewer tiles than stream 0 meets stream 0's remaining barriers
     // after its loop.
+    if constexpr (!F8) {
+        // the columns of ones after each row's NB offsets (never rewritten;
+        // with shared buffers both waves of a head write the same values)
+        constexpr int NO = WN::VMS - NB;
+        for (int u = lane; u < kTile * NO; u += 64) VMa[(u / NO) * WN::VMS + NB + u % NO] = 0x3C00;   // fp16 1.0
+    }
     if constexpr (F8) {
         // A tile's rows past c1 are not loaded, and P V still multiplies their
         // V codes (by a weight of 0).  Any byte is a valid q5_1 code, but
@@ -509,7 +533,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
         // ---- online softmax against a reference max that moves only when a
         // score passes it by more than 8 (so p <= 256, well inside fp16)
         const bool interior = t0 >= full_lo && t0 + kTile <= full_hi;
-        float pv[RTW][2][4];
+        h8 pu[RTW];   // P in fp16, the A operand of the products with V
 #pragma unroll
         for (int rt = 0; rt < RTW; ++rt) {
             float smax = -INFINITY;
@@ -526,13 +550,12 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
                     smax = fmaxf(smax, x);
                 }
             smax *= qup;                           // the scores of the scaled query rows, times qup
-            if (__any(smax > mrow[rt] + 8.0f)) {   // -inf never passes
+            if (__any(smax > mrow[rt] + 8.0f)) {   // -inf never passes, nor does a row's first finite max fail to
                 float mt = fmaxf(smax, __shfl_xor(smax, 16));
                 mt = fmaxf(mt, __shfl_xor(mt, 32));
                 const bool move = mt > mrow[rt] + 8.0f;
                 const float alpha = move ? __builtin_amdgcn_exp2f(mrow[rt] - mt) : 1.0f;
                 mrow[rt] = move ? mt : mrow[rt];
-                lsum[rt] *= alpha;
                 float ar[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * q4 + i);   // O rows 4*q4 + i
@@ -543,16 +566,12 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
 #pragma unroll
                 for (int i = 0; i < 4; ++i) macc[rt][i] *= ar[i];
             }
+            // a masked score gives exp2(-inf) = 0, also while mrow is still kNoMax
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float pe = (mrow[rt] == -INFINITY)
-                                         ? 0.0f
-                                         : __builtin_amdgcn_exp2f(fmaf(sv[rt][h][i], qup, -mrow[rt]));
-                    pv[rt][h][i] = pe;
-                    lsum[rt] += pe;
-                }
+                for (int i = 0; i < 4; ++i)
+                    pu[rt][4 * h + i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(sv[rt][h][i], qup, -mrow[rt]));
         }
 
         if constexpr (SH) {
@@ -568,7 +587,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
             else wait_loads_upto<0>();
         }
         // ---- V steps and offsets of the tile (rows past c1 hold stale bytes)
-        float dmx = 0.0f;   // the largest step this lane converts
+        uint32_t dmx = 0;   // the largest step this lane copies (fp16 bits; steps are >= 0)
 #pragma unroll
         for (int x = 0; x < (SROWS * NB + 63) / 64; ++x) {
             const int u = x * 64 + lane;
@@ -577,15 +596,14 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
                 const bool live = t0 + key < c1;
                 if constexpr (F8) {
                     const uint16_t dq = *reinterpret_cast<const uint16_t*>(rv + key * WN::VSTR + 32 * NB + sofs + 2 * blk);
-                    const float dv = live ? f16_value(dq) : 0.0f;
-                    VDa[blk * kTile + key] = dv;
-                    dmx = fmaxf(dmx, dv);
+                    const uint32_t dv = live ? dq : 0u;
+                    VDa[blk * kTile + key] = (uint16_t)dv;
+                    dmx = max(dmx, dv);
                 } else {
-                    const uint32_t dm = *reinterpret_cast<const uint32_t*>(rv + key * WN::VSTR + blk * 24);
-                    const float dv = live ? f16_value((uint16_t)(dm & 0xFFFF)) : 0.0f;
-                    VDa[blk * kTile + key] = dv;
-                    dmx = fmaxf(dmx, dv);
-                    VMa[key * WN::VMS + blk] = live ? (uint16_t)(dm >> 16) : (uint16_t)0;
+                    const uint32_t dm = live ? *reinterpret_cast<const uint32_t*>(rv + key * WN::VSTR + blk * 24) : 0u;
+                    VDa[blk * kTile + key] = (uint16_t)(dm & 0xFFFF);
+                    dmx = max(dmx, dm & 0xFFFF);
+                    VMa[key * WN::VMS + blk] = (uint16_t)(dm >> 16);
                 }
             }
         }
@@ -596,7 +614,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
 #pragma unroll
             for (int x = 0; x < (16 * NB + 63) / 64; ++x) {
                 const int u = x * 64 + lane;
-                if (16 * NB % 64 == 0 || u < 16 * NB) dmx = fmaxf(dmx, VDa[(u - (u / NB) * NB) * kTile + (hrow ^ 16) + u / NB]);
+                if (16 * NB % 64 == 0 || u < 16 * NB) dmx = max(dmx, (uint32_t)VDa[(u - (u / NB) * NB) * kTile + (hrow ^ 16) + u / NB]);
             }
         } else {
             dec::lds_order();
@@ -604,9 +622,9 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
         // A tile with a step of 2^7 or more: its steps are stored times
         // 2^-vsh (dec::v_shift; each lane rescales the ones it converted) and
         // the accumulators switch units.
-        const bool big = __any(dmx >= 128.0f);   // wave-uniform
+        const bool big = __any(dmx >= 0x5800u);   // fp16 128.0; wave-uniform
         if (big || vsh != 0) {
-            const int want = big ? __builtin_amdgcn_readfirstlane(dec::v_shift(dec::wave_max_dpp(dmx))) : 0;
+            const int want = big ? __builtin_amdgcn_readfirstlane(dec::v_shift(dec::wave_max_dpp(f16_value((uint16_t)dmx)))) : 0;
             if (want != vsh) {
                 const float f = dec::pow2(vsh - want);
 #pragma unroll
@@ -622,7 +640,10 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
 #pragma unroll
                 for (int x = 0; x < (SROWS * NB + 63) / 64; ++x) {
                     const int u = x * 64 + lane;
-                    if (SROWS * NB % 64 == 0 || u < SROWS * NB) VDa[(u - (u / NB) * NB) * kTile + hrow + u / NB] *= f;
+                    if (SROWS * NB % 64 == 0 || u < SROWS * NB) {
+                        uint16_t& e = VDa[(u - (u / NB) * NB) * kTile + hrow + u / NB];
+                        e = __builtin_bit_cast(uint16_t, (_Float16)(f16_value(e) * f));
+                    }
                 }
                 if constexpr (SH) lds_barrier(); else dec::lds_order();
             }
@@ -638,19 +659,19 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
                 const i2 cb = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(vb + 16));
                 const h8 vf0 = e4m3_codes((uint32_t)ca[0], (uint32_t)ca[1]);
                 const h8 vf1 = e4m3_codes((uint32_t)cb[0], (uint32_t)cb[1]);
-                const float4 d0 = *reinterpret_cast<const float4*>(VDa + blk * kTile + 4 * q4);
-                const float4 d1 = *reinterpret_cast<const float4*>(VDa + blk * kTile + 16 + 4 * q4);
+                const h8 dh = steps_of(VDa + blk * kTile, q4);
 #pragma unroll
                 for (int rt = 0; rt < RTW; ++rt) {
-                    const h8 pa = {(_Float16)(pv[rt][0][0] * d0.x), (_Float16)(pv[rt][0][1] * d0.y),
-                                   (_Float16)(pv[rt][0][2] * d0.z), (_Float16)(pv[rt][0][3] * d0.w),
-                                   (_Float16)(pv[rt][1][0] * d1.x), (_Float16)(pv[rt][1][1] * d1.y),
-                                   (_Float16)(pv[rt][1][2] * d1.z), (_Float16)(pv[rt][1][3] * d1.w)};
+                    const h8 pa = pu[rt] * dh;
                     oacc[rt][2 * blk] = dec::mfma(pa, vf0, oacc[rt][2 * blk]);
                     oacc[rt][2 * blk + 1] = dec::mfma(pa, vf1, oacc[rt][2 * blk + 1]);
                 }
                 if (NB > 4) asm volatile("" ::: "memory");
             }
+            const h8 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f,
+                             (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt) macc[rt] = dec::mfma(pu[rt], ones, macc[rt]);
         } else {
         // ---- P V with the V codes built from the q5_1 bytes of 8 keys per lane group
 #pragma unroll
@@ -674,14 +695,10 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
             const uint32_t c11 = (__builtin_amdgcn_alignbit(qb1, qb1, sh_rot) & m4) | (((uint32_t)nib[1] >> 4) & m0);
             const h8 vf0 = v_codes_sub(c00, c01);
             const h8 vf1 = v_codes_sub(c10, c11);
-            const float4 d0 = *reinterpret_cast<const float4*>(VDa + blk * kTile + 4 * q4);
-            const float4 d1 = *reinterpret_cast<const float4*>(VDa + blk * kTile + 16 + 4 * q4);
+            const h8 dh = steps_of(VDa + blk * kTile, q4);
 #pragma unroll
             for (int rt = 0; rt < RTW; ++rt) {
-                const h8 pa = {(_Float16)(pv[rt][0][0] * d0.x), (_Float16)(pv[rt][0][1] * d0.y),
-                               (_Float16)(pv[rt][0][2] * d0.z), (_Float16)(pv[rt][0][3] * d0.w),
-                               (_Float16)(pv[rt][1][0] * d1.x), (_Float16)(pv[rt][1][1] * d1.y),
-                               (_Float16)(pv[rt][1][2] * d1.z), (_Float16)(pv[rt][1][3] * d1.w)};
+                const h8 pa = pu[rt] * dh;
                 oacc[rt][2 * blk] = dec::mfma(pa, vf0, oacc[rt][2 * blk]);
                 oacc[rt][2 * blk + 1] = dec::mfma(pa, vf1, oacc[rt][2 * blk + 1]);
             }
@@ -692,12 +709,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
             const h8 mb = dec::tr16_pair(scb + WN::VM + (mk0 * WN::VMS + 4 * mc) * 2,
                                          scb + WN::VM + (mk1 * WN::VMS + 4 * mc) * 2);
 #pragma unroll
-            for (int rt = 0; rt < RTW; ++rt) {
-                const h8 pu = {(_Float16)pv[rt][0][0], (_Float16)pv[rt][0][1], (_Float16)pv[rt][0][2],
-                               (_Float16)pv[rt][0][3], (_Float16)pv[rt][1][0], (_Float16)pv[rt][1][1],
-                               (_Float16)pv[rt][1][2], (_Float16)pv[rt][1][3]};
-                macc[rt] = dec::mfma(pu, mb, macc[rt]);
-            }
+            for (int rt = 0; rt < RTW; ++rt) macc[rt] = dec::mfma(pu[rt], mb, macc[rt]);
         }
         }   // q5_1
         if constexpr (SH) {
@@ -716,10 +728,11 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
     const float ounit = dec::pow2((F8 ? 0 : 24) + vsh);
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
-        float l = lsum[rt];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
-        lsum[rt] = l;
+        // row j16's sum: element j16 & 3 of lane 16 * (j16 >> 2) + column
+        const int src = 16 * (j16 >> 2) + (F8 ? 0 : NB);
+        const float l0 = __shfl(macc[rt][0], src), l1 = __shfl(macc[rt][1], src);
+        const float l2 = __shfl(macc[rt][2], src), l3 = __shfl(macc[rt][3], src);
+        lsum[rt] = (j16 & 2) ? ((j16 & 1) ? l3 : l2) : ((j16 & 1) ? l1 : l0);
 #pragma unroll
         for (int dt = 0; dt < 2 * NB; ++dt)
 #pragma unroll
@@ -759,8 +772,8 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
                 for (int rt = 0; rt < RTW; ++rt) {
                     const float m1 = yb[MOFS + rt * 32 + j16], l1 = yb[MOFS + rt * 32 + 16 + j16];
                     const float M = fmaxf(mrow[rt], m1);
-                    const float a0 = (mrow[rt] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mrow[rt] - M);
-                    const float a1 = (m1 == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m1 - M);
+                    const float a0 = (mrow[rt] == kNoMax) ? 0.0f : __builtin_amdgcn_exp2f(mrow[rt] - M);
+                    const float a1 = (m1 == kNoMax) ? 0.0f : __builtin_amdgcn_exp2f(m1 - M);
                     lsum[rt] = a0 * lsum[rt] + a1 * l1;
                     mrow[rt] = M;
                     float A0[4], A1[4];
@@ -788,7 +801,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
         if (q4 == 0 && r < R && half == 0) {
             const int t = tq0 + r / p.hpk, hq = g * p.hpk + r % p.hpk;
             const size_t idx = (row0 + t) * p.H + hq;
-            p.part_ml[2 * idx] = (mrow[rt] == -INFINITY) ? -INFINITY : mrow[rt] * kLn2;
+            p.part_ml[2 * idx] = (mrow[rt] == kNoMax) ? -INFINITY : mrow[rt] * kLn2;
             p.part_ml[2 * idx + 1] = lsum[rt];
         }
 #pragma unroll

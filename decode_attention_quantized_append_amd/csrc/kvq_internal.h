@@ -108,10 +108,12 @@ struct StreamWin {
     static constexpr int NVI = (TR * VWP + 63) / 64;            // and V
     static constexpr int KB = 0;                                // K rows
     static constexpr int VB = TR * KSTR;                        // V rows
-    static constexpr int VMS = NB < 4 ? 4 : NB;
+    // V offset rows: the NB offsets, then at least one column of ones (the
+    // offset product's column NB is then the row sums of P)
+    static constexpr int VMS = (NB + 4) & ~3;
     static constexpr int KS = VB + TR * VSTR;                   // f32 [NB][32] K scales * scale * log2 e
-    static constexpr int VD = KS + NB * kRowTile * 4;           // f32 [NB][32] V steps
-    static constexpr int VM = VD + NB * kRowTile * 4;           // fp16 [32][VMS] V offsets
+    static constexpr int VD = KS + NB * kRowTile * 4;           // fp16 [NB][32] V steps
+    static constexpr int VM = VD + NB * kRowTile * 2;           // fp16 [32][VMS] V offsets, then ones
     static constexpr int BYTES = VM + kRowTile * VMS * 2;       // per wave
     static_assert(NKI <= 32 && NVI <= 32, "load counts must fit vmcnt");
 };
@@ -135,8 +137,8 @@ struct StreamWinF8 {
     static constexpr int SC = 32 * NB;                          // scale piece within a row window
     static constexpr int VMS = 0;
     static constexpr int KS = VB + TR * VSTR;                   // f32 [NB][32] K scales * scale * log2 e
-    static constexpr int VD = KS + NB * kRowTile * 4;           // f32 [NB][32] V scales
-    static constexpr int VM = VD + NB * kRowTile * 4;           // (no offsets)
+    static constexpr int VD = KS + NB * kRowTile * 4;           // fp16 [NB][32] V scales
+    static constexpr int VM = VD + NB * kRowTile * 2;           // (no offsets)
     static constexpr int BYTES = VM;
     static_assert(NKI <= 32 && NVI <= 32, "load counts must fit vmcnt");
 };

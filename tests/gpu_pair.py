@@ -53,10 +53,19 @@ class Pair:
     def pv_atol(self):
         """Bound on |o1 - o2| between two GPU decodes of the same rows that
         round P differently to fp16 (other split plans, tilings or row
-        groupings): each is within 2^-11 * sum_j p_j |v_j| / sum_j p_j of the
-        fp32 result, so together within 2^-10 * max |v|.  max |v| is taken
-        from the appended rows, with 5 % for the q5_1 rounding of the codes."""
-        return 2.0 ** -10 * 1.05 * self.vmax
+        groupings).  A decode rounds each weight p to fp16 (relative error at
+        most 2^-11), the product with the V step once more (2^-11), and sums
+        the rounded weights for the row sum (2^-11): each output is within
+        3 * 2^-11 * max |v| of the fp32 result, so two are within
+        3 * 2^-10 * max |v|.  max |v| is taken from the appended rows, with
+        5 % for the q5_1 rounding of the codes."""
+        return 3 * 2.0 ** -10 * 1.05 * self.vmax
+
+    def lse_atol(self):
+        """Bound on |lse1 - lse2| between two such decodes: each row sum adds
+        weights rounded to fp16, within a factor 1 +- 2^-11 of the exact sum,
+        so each log-sum-exp is within log(1 + 2^-11) < 4.9e-4 of it."""
+        return 2 * 4.9e-4
 
     def truncate(self, new_len):
         self.gpu.truncate(list(new_len))

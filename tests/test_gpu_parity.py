@@ -138,12 +138,12 @@ def test_decode_split_invariance():
         p.gpu.set_split_rows(rows_)
         o, l = p.gpu.decode(qd, scale)
         outs.append((o.cpu().numpy(), l.cpu().numpy()))
-    # P enters the P.V product as fp16, rounded relative to each split's own
-    # running max (unit roundoff 2^-11): outputs agree within Pair.pv_atol;
-    # the row sums stay fp32, so the log-sum-exps agree to fp32 rounding.
+    # P enters the P.V product and the row sums as fp16, rounded relative to
+    # each split's own running max: outputs agree within Pair.pv_atol, the
+    # log-sum-exps within Pair.lse_atol.
     for o, l in outs[1:]:
         np.testing.assert_allclose(o, outs[0][0], atol=p.pv_atol(), rtol=0)
-        np.testing.assert_allclose(l, outs[0][1], atol=1e-5, rtol=1e-5)
+        np.testing.assert_allclose(l, outs[0][1], atol=p.lse_atol(), rtol=0)
     p.decode(q, scale)
 
 
@@ -173,7 +173,7 @@ def test_decode_tiling_parity(name, kernel, gh, sub):
 @pytest.mark.parametrize("name", sorted(TILINGS))
 def test_decode_tilings_agree(name):
     """Every kernel and tiling gives the same outputs up to the fp16 rounding
-    of P (Pair.pv_atol)."""
+    of P (Pair.pv_atol, Pair.lse_atol)."""
     p, q, s, scale = build_small(name)
     io = SMALL[name][10]
     qd = to_dev(q, io)
@@ -187,7 +187,7 @@ def test_decode_tilings_agree(name):
             outs.append((o.cpu().numpy(), l.cpu().numpy()))
     for o, l in outs[1:]:
         np.testing.assert_allclose(o, outs[0][0], atol=p.pv_atol(), rtol=0)
-        np.testing.assert_allclose(l, outs[0][1], atol=1e-5, rtol=1e-5)
+        np.testing.assert_allclose(l, outs[0][1], atol=p.lse_atol(), rtol=0)
 
 
 # -- many query rows: groups of 32 / hpk rows per decode launch, one combine -------
@@ -359,7 +359,7 @@ def test_verify_rows_equal_sequential_single_rows():
         o1, l1 = s.gpu.decode(to_dev(q[:, t:t + 1], "bf16"), 0.088)
         # equal up to the fp16 rounding of P (Pair.pv_atol)
         np.testing.assert_allclose(o1.cpu().numpy()[:, 0], oa.cpu().numpy()[:, t], atol=a.pv_atol(), rtol=0)
-        np.testing.assert_allclose(l1.cpu().numpy()[:, 0], la.cpu().numpy()[:, t], atol=1e-5, rtol=1e-5)
+        np.testing.assert_allclose(l1.cpu().numpy()[:, 0], la.cpu().numpy()[:, t], atol=a.lse_atol(), rtol=0)
 
 
 def test_gqa_equals_repeated_heads():
@@ -374,7 +374,7 @@ def test_gqa_equals_repeated_heads():
     og, lg = g.gpu.decode(to_dev(q, "bf16"), 0.125)
     orr, lr = r.gpu.decode(to_dev(q, "bf16"), 0.125)
     np.testing.assert_allclose(og.cpu().numpy(), orr.cpu().numpy(), atol=g.pv_atol(), rtol=0)   # fp16 P
-    np.testing.assert_allclose(lg.cpu().numpy(), lr.cpu().numpy(), atol=1e-5, rtol=1e-5)
+    np.testing.assert_allclose(lg.cpu().numpy(), lr.cpu().numpy(), atol=g.lse_atol(), rtol=0)
     g.decode(q, 0.125, what="gqa")
 
 
