@@ -239,6 +239,12 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
         const int pc = x * 64 + lane, row = pc / WN::VWP, col = pc - row * WN::VWP;
         voff[x] = (uint32_t)((hrow + row) * p.v_row + min(col, WN::VW - 1) * 16);   // the pad piece re-reads a real one
     }
+    // kept in registers as they are (not recomputed at each use)
+#pragma unroll
+    for (int x = 0; x < NKH; ++x) asm volatile("" : "+v"(koff[x]));
+#pragma unroll
+    for (int x = 0; x < (F8 ? 0 : NVH); ++x) asm volatile("" : "+v"(voff[x]));
+    constexpr int CROWS = SH ? 16 : kTile;   // rows of one copy
     // Copy the K (or V) rows of the tile [t0, t0 + 32) into the buffer.  Rows
     // from c1 on (a session's last tile) are not loaded; rows below lo (first
     // tile) are resident and masked.  Every LDS read of the half being
@@ -249,11 +255,15 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
         const int nrows = SH ? min(16, max(0, c1 - t0 - hrow)) : min(kTile, c1 - t0);
         const uint8_t* const kt = kwin + (int64_t)(t0 - base) * p.k_row;
         uint8_t* const d = tb + WN::KB + hrow * WN::KSTR;
+        if (nrows == CROWS) {
+            // a whole copy: every instruction but a partial last one takes all lanes
 #pragma unroll
-        for (int x = 0; x < NKH; ++x) {
-            uint32_t o = koff[x];
-            asm volatile("" : "+v"(o));
-            if (lane < nrows * WN::KWP - x * 64) dma16(kt, o, d + x * 1024);
+            for (int x = 0; x < NKH; ++x)
+                if ((x + 1) * 64 <= CROWS * WN::KWP || lane < CROWS * WN::KWP - x * 64) dma16(kt, koff[x], d + x * 1024);
+        } else {
+#pragma unroll
+            for (int x = 0; x < NKH; ++x)
+                if (lane < nrows * WN::KWP - x * 64) dma16(kt, koff[x], d + x * 1024);
         }
     };
     auto issue_v = [&](int t0, uint8_t* tb) {
@@ -262,11 +272,15 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
         const int nrows = SH ? min(16, max(0, c1 - t0 - hrow)) : min(kTile, c1 - t0);
         const uint8_t* const vt = vwin + (int64_t)(t0 - base) * p.v_row;
         uint8_t* const d = tb + WN::VB + hrow * WN::VSTR;
+        if (nrows == CROWS) {
 #pragma unroll
-        for (int x = 0; x < NVH; ++x) {
-            uint32_t o = F8 ? koff[x] : voff[x];
-            asm volatile("" : "+v"(o));
-            if (lane < nrows * WN::VWP - x * 64) dma16(vt, o, d + x * 1024);
+            for (int x = 0; x < NVH; ++x)
+                if ((x + 1) * 64 <= CROWS * WN::VWP || lane < CROWS * WN::VWP - x * 64)
+                    dma16(vt, F8 ? koff[x] : voff[x], d + x * 1024);
+        } else {
+#pragma unroll
+            for (int x = 0; x < NVH; ++x)
+                if (lane < nrows * WN::VWP - x * 64) dma16(vt, F8 ? koff[x] : voff[x], d + x * 1024);
         }
     };
 
