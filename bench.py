@@ -586,6 +586,19 @@ def pmc_command(counter, wl):
             f"--no-others --no-ceiling")
 
 
+SQ_WORKLOADS = ("verify", "batched", "verify_f8", "batched_f8")
+SQ_PASSES = (("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU",
+              "SQ_ACTIVE_INST_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VALU"),
+             ("SQ_INSTS_LDS", "SQ_WAIT_ANY", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_SCA",
+              "SQ_INSTS_MFMA", "SQ_INST_CYCLES_VMEM", "SQ_ACTIVE_INST_MISC"))
+
+
+def sq_command(i, wl):
+    return (f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL 120 rocprofv3 --pmc {' '.join(SQ_PASSES[i])} "
+            f"-d <out>/sq{i + 1}_{wl} -o run -- python3 /root/repo/bench.py --workload {wl} --steps 5 --warmup 1 "
+            f"--layers 2 --graph off --no-cpu-baseline --no-others --no-ceiling")
+
+
 def _short(n):
     import re
     n = re.sub(r"^void ", "", n)
@@ -667,6 +680,50 @@ def summarize_profiles(d):
         for name, did, v in c.execute("select kernel_name, dispatch_id, value from counters_collection"):
             per[_short(name)][did] += v
         return {k: [v for _, v in sorted(dd.items())][-last:] for k, dd in per.items()}
+
+    sq_rows = []
+    for wl in SQ_WORKLOADS:
+        if not (os.path.isdir(os.path.join(d, f"sq1_{wl}")) and os.path.isdir(os.path.join(d, f"sq2_{wl}"))):
+            continue
+        got = {}
+        for i in (1, 2):
+            c = _db(os.path.join(d, f"sq{i}_{wl}"))
+            per = collections.defaultdict(lambda: collections.defaultdict(float))
+            for name, cn, did, v in c.execute(
+                    "select kernel_name, counter_name, dispatch_id, value from counters_collection"):
+                if "decode_stream" in name:
+                    per[(_short(name), cn)][did] += v
+            for (k, cn), dd in per.items():
+                last = [v for _, v in sorted(dd.items())][-5:]
+                got.setdefault(k, {})[cn] = sum(last) / len(last)
+        for k, g in got.items():
+            sq_rows.append((wl, k, g))
+    if sq_rows:
+        L = ["# SQ counters of the decode partials kernel", "",
+             "Commands (repo at /root/repo), two passes of eight counters per workload:", "", "```"]
+        for wl in dict.fromkeys(r[0] for r in sq_rows):
+            L += [sq_command(0, wl), sq_command(1, wl)]
+        L += ["```", "", f"Summarized by `python3 bench.py --summarize-profiles <out>`.  Source hash: `{H}`.  "
+              "Each value is the mean over the last 5 dispatches (counters summed over the device).", "",
+              "| workload | kernel | waves | VALU / wave | MFMA / wave | LDS / wave | SALU / wave | "
+              "VALU instr per KiB of K+V | VALU-issue share of wave cycles | wait share of wave cycles | "
+              "LDS bank-conflict cycles / LDS-active cycles |",
+              "|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+        for wl, k, g in sq_rows:
+            wv = g.get("SQ_WAVES", 0) or 1
+            kib = W.get(wl).kv_bytes_per_decode() / 1024
+            L.append(f"| {wl} | `{k}` | {wv:.0f} | {g.get('SQ_INSTS_VALU', 0) / wv:.0f} | "
+                     f"{g.get('SQ_INSTS_MFMA', 0) / wv:.0f} | {g.get('SQ_INSTS_LDS', 0) / wv:.0f} | "
+                     f"{g.get('SQ_INSTS_SALU', 0) / wv:.0f} | {g.get('SQ_INSTS_VALU', 0) / kib:.1f} | "
+                     f"{g.get('SQ_ACTIVE_INST_VALU', 0) / max(1, g.get('SQ_WAVE_CYCLES', 1)):.3f} | "
+                     f"{g.get('SQ_WAIT_INST_ANY', 0) / max(1, g.get('SQ_WAVE_CYCLES', 1)):.3f} | "
+                     f"{g.get('SQ_LDS_BANK_CONFLICT', 0) / max(1, g.get('SQ_ACTIVE_INST_LDS', 1)):.3f} |")
+        L += ["", "Raw means:", "", "| workload | counter | value |", "|---|---|---:|"]
+        for wl, k, g in sq_rows:
+            for cn in sorted(g):
+                L.append(f"| {wl} | {cn} | {g[cn]:.4g} |")
+        with open(os.path.join(out_dir, "decode_sq_counters.md"), "w") as f:
+            f.write("\n".join(L) + "\n")
 
     if not os.path.isdir(os.path.join(d, "FETCH_SIZE_copy")):
         return

@@ -190,6 +190,33 @@ def test_decode_tilings_agree(name):
         np.testing.assert_allclose(l, outs[0][1], atol=p.lse_atol(), rtol=0)
 
 
+@pytest.mark.parametrize("name", sorted(TILINGS))
+def test_decode_plans_exact_weights(name):
+    """With zero queries every visible row scores 0, so every weight is
+    exactly 1 in fp16 and in fp32, and so is each weight times its q5_1 step:
+    the only rounding left is the fp32 summation (and the sink's exp in the
+    combine).  Every kernel, tiling and split plan must then give the mean of
+    the visible V rows (with the sink in the denominator) and lse =
+    log(rows + sum of the sink's exp), as the oracle does, within 1e-5 of the
+    V scale: far below Pair.pv_atol, so a row dropped, counted twice or
+    masked wrongly by a plan shows up at any length here."""
+    p, q, s, scale = build_small(name)
+    q = np.zeros_like(q)
+    io = SMALL[name][10]
+    qd = to_dev(q, io)
+    sd = torch.from_numpy(s).to(DEV) if s is not None else None
+    want, want_lse = p.ref.attention(q, scale=scale, sinks=s)
+    atol = 1e-5 * max(1.0, p.vmax)
+    for kernel, gh, sub in [(PH, 0, 0), (kvq.KVQ_DECODE_AUTO, 0, 0)] + TILINGS[name]:
+        p.gpu.set_decode_tiling(kernel, gh, sub)
+        for rows_ in (0, 64, 256):
+            p.gpu.set_split_rows(rows_)
+            o, l = p.gpu.decode(qd, scale, sinks=sd)
+            what = f"{name} kernel={kernel} gh={gh} sub={sub} split={rows_}"
+            np.testing.assert_allclose(o.cpu().numpy(), want, atol=atol, rtol=0, err_msg=what)
+            np.testing.assert_allclose(l.cpu().numpy(), want_lse, atol=1e-5, rtol=0, err_msg=what)
+
+
 # -- many query rows: groups of 32 / hpk rows per decode launch, one combine -------
 MANY = {
     # name: (B, H, Hkv, hd, T, lengths, window, sinks, io, tiling)
