@@ -291,7 +291,11 @@ def run_gpu(w, args):
     comb_ms = [e[1].elapsed_time(e[2]) for e in ev_dec]
 
     # (2) the decode call (partials + combine) as back-to-back batches over
-    # the layers, with no host work between the calls
+    # the layers, with no host work between the calls, on each layer's state
+    # after a step's append (a ring's T query rows see rows that the
+    # truncate to the pre-step length leaves behind base)
+    for c in caches:
+        check(lib.kvq_append(c.h, kp, vp, dt, T, None, stream), "append")
     reps = max(1, -(-args.steps // L))
     calls = reps * L
     e0, e1 = _events(2)
@@ -302,6 +306,11 @@ def run_gpu(w, args):
     e1.record()
     torch.cuda.synchronize(dev)
     call_ms = e0.elapsed_time(e1) / calls
+    for c in caches:
+        if w.rollback_keep:
+            check(lib.kvq_rollback(c.h, drop_arr, stream), "rollback")
+        else:
+            check(lib.kvq_truncate(c.h, pre_arr, stream), "truncate")
 
     # (3) whole steps: one captured graph per layer, replayed
     use_graph = args.graph != "off"

@@ -447,6 +447,23 @@ extern "C" {
 
 const char* kvq_last_error(void) { return g_err.c_str(); }
 
+kvq_status kvq_ring_rows(int32_t window, int32_t max_chunk, int32_t ring_step, int32_t* rows) {
+    if (!rows) return fail(KVQ_EINVAL, "rows is NULL");
+    if (window < 1 || max_chunk < 1 || ring_step < 1)
+        return fail(KVQ_EINVAL, "window, max_chunk and ring_step must be >= 1");
+    // An append of n rows at length L rebases to the smallest base b' (a
+    // multiple of ring_step) with L + n - b' <= capacity, so b' < L + n -
+    // capacity + ring_step; its decode starts at (L + 1 - window) & ~31,
+    // which is >= b' for every L and n <= max_chunk when capacity >= window +
+    // max_chunk + ring_step - 2 (b' and the start both multiples of 32), or 31
+    // rows more when ring_step is not a multiple of 32.
+    int64_t r = (int64_t)window + max_chunk + ring_step - 2 + (ring_step % 32 == 0 ? 0 : 31);
+    r = std::max<int64_t>(r, (int64_t)window + ring_step);
+    if (r > INT32_MAX) return fail(KVQ_EINVAL, "ring rows overflow int32");
+    *rows = (int32_t)r;
+    return KVQ_OK;
+}
+
 kvq_status kvq_required_bytes(const kvq_config* cfg, kvq_sizes* out) {
     kvq_status s = check_config(cfg);
     if (s != KVQ_OK) return s;

@@ -224,16 +224,25 @@ __device__ __forceinline__ void append_unit(const AppendParams& p, int64_t unit,
     const uint64_t fifth = __ballot((cv >> 4) & 1);
     const uint32_t qh = (uint32_t)(fifth >> (threadIdx.x & 32));
     const int cv_hi = __shfl_xor(cv, 16);          // lane j < 16 gets code j + 16
+    // stores of whole 16- and 32-bit words: K code pairs (a K block starts at
+    // an even byte, its codes 2 bytes on), and V nibble bytes by fours (a V
+    // block starts on 8 bytes)
+    const uint32_t kb = (uint32_t)ck & 0xFFu;
+    const uint32_t kpair = kb | (((uint32_t)__shfl_down((int)kb, 1) & 0xFFu) << 8);
+    const uint32_t nib = (uint32_t)((cv & 15) | ((cv_hi & 15) << 4));
+    uint32_t nw = nib;
+#pragma unroll
+    for (int s = 1; s < 4; ++s) nw |= ((uint32_t)__shfl_down((int)nib, s) & 0xFFu) << (8 * s);
     if (active) {
         uint8_t* kd = p.k_planes + (int64_t)b * p.k_stride + prow * (int64_t)(nblk * 34) + blk * 34;
         if (lane == 0) *reinterpret_cast<uint16_t*>(kd) = dk16;
-        kd[2 + lane] = (uint8_t)(int8_t)ck;
+        if ((lane & 1) == 0) *reinterpret_cast<uint16_t*>(kd + 2 + lane) = (uint16_t)kpair;
         uint8_t* vd = p.v_planes + (int64_t)b * p.v_stride + prow * (int64_t)(nblk * 24) + blk * 24;
         if (lane == 0) {
             *reinterpret_cast<uint32_t*>(vd) = (uint32_t)dv16 | ((uint32_t)mv16 << 16);
             *reinterpret_cast<uint32_t*>(vd + 4) = qh;
         }
-        if (lane < 16) vd[8 + lane] = (uint8_t)((cv & 15) | ((cv_hi & 15) << 4));
+        if (lane < 16 && (lane & 3) == 0) *reinterpret_cast<uint32_t*>(vd + 8 + lane) = nw;
     }
 }
 
@@ -810,13 +819,22 @@ int launch_move(const MoveParams& p, void* stream, const char** err) {
 int launch_append(const AppendParams& p, void* stream, const char** err) {
     const int64_t units = (int64_t)p.nsess * p.T * (p.Hkv * p.hd / 32);
     // up to 32 blocks in one workgroup of 1024 threads, which then needs no
-    // completion counter; more over a grid of 256-thread workgroups
+    // completion counter
     if (units <= 32) {
         hipLaunchKernelGGL(append_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, p);
         return check(err);
     }
-    const int64_t grid = std::min<int64_t>((units + 7) / 8, 1024);
-    hipLaunchKernelGGL(append_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, p);
+    // At most 256 workgroups: every workgroup adds to the completion counter,
+    // and those device-scope atomics on one word are served one at a time,
+    // so past that count more workgroups cost more than the extra passes of
+    // fewer ones.  256 threads (8 blocks a pass) while one pass of them
+    // covers the launch, else 1024 (32 blocks a pass).
+    if ((units + 7) / 8 <= 256) {
+        hipLaunchKernelGGL(append_kernel, dim3((unsigned)((units + 7) / 8)), dim3(256), 0, (hipStream_t)stream, p);
+        return check(err);
+    }
+    const int64_t grid = std::min<int64_t>((units + 31) / 32, 256);
+    hipLaunchKernelGGL(append_kernel, dim3((unsigned)grid), dim3(1024), 0, (hipStream_t)stream, p);
     return check(err);
 }
 

@@ -28,7 +28,7 @@ STATUS_NAMES = {0: "KVQ_OK", 1: "KVQ_EINVAL", 2: "KVQ_ECAPACITY", 3: "KVQ_ERANGE
                 4: "KVQ_EUNSUPPORTED", 5: "KVQ_EDEVICE"}
 
 # Every entry point the header declares.
-EXPORTS = ("kvq_required_bytes", "kvq_create", "kvq_append", "kvq_decode_workspace_bytes",
+EXPORTS = ("kvq_required_bytes", "kvq_ring_rows", "kvq_create", "kvq_append", "kvq_decode_workspace_bytes",
            "kvq_decode", "kvq_decode_noalloc", "kvq_truncate", "kvq_set_split_rows", "kvq_set_decode_tiling", "kvq_info",
            "kvq_host_lengths", "kvq_set_graph_mode", "kvq_set_host_lengths", "kvq_importance",
            "kvq_rollback", "kvq_set_trace_events", "kvq_destroy", "kvq_last_error")
@@ -68,6 +68,7 @@ def _declare(lib):
     i32p, i64p = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
     sig = {
         "kvq_required_bytes": (st, [cfgp, szp]),
+        "kvq_ring_rows": (st, [i32, i32, i32, i32p]),
         "kvq_create": (st, [cfgp, vp, vp, vp, vp, ctypes.POINTER(vp)]),
         "kvq_append": (st, [vp, vp, vp, i32, i32, i32p, vp]),
         "kvq_decode_workspace_bytes": (st, [vp, i32, ctypes.POINTER(ctypes.c_size_t)]),
@@ -146,6 +147,13 @@ def kvq_required_bytes(cfg: kvq_config, lib=None) -> kvq_sizes:
     out = kvq_sizes()
     _check(lib, lib.kvq_required_bytes(ctypes.byref(cfg), ctypes.byref(out)))
     return out
+
+
+def kvq_ring_rows(window: int, max_chunk: int, ring_step: int, lib=None) -> int:
+    lib = lib or load()
+    out = ctypes.c_int32()
+    _check(lib, lib.kvq_ring_rows(window, max_chunk, ring_step, ctypes.byref(out)))
+    return out.value
 
 
 def kvq_create(cfg: kvq_config, k_planes: int, v_planes: int, counters: int, stream: int = 0,

@@ -25,7 +25,8 @@ Workloads (one attention layer each):
             T=8 causal verify rows, then rollback to len+3, bf16 q/k/v ~ N(0,1)
   prime     a prompt chunk: 1 session of the qwen_gqa shape and inputs, 512
             rows appended and attending causally, each within a 4096-row
-            sliding window, at 32768 rows (not one of the five measured
+            sliding window, at 32768 rows, served from a 5118-row ring that
+            advances 512 rows at a time (not one of the five measured
             configurations: the chunked prime of a long prompt)
 The k/v distribution named "as config 1" for the batched and verify shapes
 is read as the tiny shape's N(0,1); ``kv_dist="outlier"`` selects the other
@@ -219,8 +220,10 @@ WORKLOADS = {
                           window=1024, ring_cap=2048, ring_step=512, sinks=True),
     "verify": Workload("verify", 105, B=2, H=16, Hkv=4, hd=256, T=8, cached=131072,
                        rollback_keep=3),
+    # the prompt chunk is served from a ring of the rows kvq_ring_rows gives
+    # for a 4096-row window, 512-row chunks and 512-row steps
     "prime": Workload("prime", 106, B=1, H=32, Hkv=8, hd=128, T=512, cached=32768,
-                      window=4096, kv_dist="outlier"),
+                      window=4096, ring_cap=4096 + 512 + 512 - 2, ring_step=512, kv_dist="outlier"),
     # the FP8 (e4m3) K/V variant on the two long-context shapes: the same
     # seeds, so the same inputs, held as FP8 rows
     "verify_f8": Workload("verify_f8", 105, B=2, H=16, Hkv=4, hd=256, T=8, cached=131072,

@@ -141,6 +141,27 @@ typedef struct kvq_info_t {
  * Errors: EINVAL (NULL pointer, bad geometry), EUNSUPPORTED (format, head_dim). */
 kvq_status kvq_required_bytes(const kvq_config* cfg, kvq_sizes* out);
 
+/* Physical rows per session (kvq_config.capacity) of a ring that serves a
+ * window-row sliding window to prompt chunks of up to max_chunk rows, with
+ * base advancing ring_step rows at a time.  A decode starts each session at
+ * its first visible row rounded down to 32: for a chunk appended at length
+ * base_len that is (base_len - (window - 1)) & ~31, so at most 31 masked rows
+ * precede the window.  With at least *rows rows, every append of 1 to
+ * max_chunk rows, in any sequence from an empty session, neither drops a row
+ * it still sees (no ERANGE) nor moves base above that 32-aligned start (so
+ * the decode of its rows reads from the ring as it stands).  *rows =
+ * window + max_chunk + ring_step - 2, plus 31 when ring_step is not a
+ * multiple of 32, and at least window + ring_step; when ring_step is a
+ * multiple of 32 no smaller ring has both properties.
+ * Defined by: memra-engine "Module cache" page, constant
+ * PRIME_CHUNK_MAX_TOKENS (the ring carries one whole maximum-size prime
+ * chunk beyond the reader's window) and trait swa_ring_rows (the rows the
+ * reader contract requires; prime starts at the window's first row rounded
+ * down to 32).  The ring_step term is this library's: its ring rebases in
+ * whole steps instead of wrapping.  Pure host computation.
+ * Errors: EINVAL (rows NULL, an argument < 1, or a result above INT32_MAX). */
+kvq_status kvq_ring_rows(int32_t window, int32_t max_chunk, int32_t ring_step, int32_t* rows);
+
 /* Creates a handle over caller-owned device memory: k_planes / v_planes
  * (256-byte aligned, at least the sizes from kvq_required_bytes) and counters
  * (256-byte aligned, counters_bytes).  Enqueues the zeroing of len_d, base_d

@@ -290,20 +290,24 @@ def test_importance_parity(name):
         np.testing.assert_allclose(imp.sum(1).cpu().numpy(), 2 * T * H, rtol=1e-4)
 
 
-def test_chunked_prime_into_ring():
-    """A prompt primed into a sliding-window ring in chunks: each chunk's rows
-    are appended, then its rows attend causally (each within its window) to
-    what the ring holds; the ring is one chunk plus the window plus a rebase
-    step.  Every chunk's outputs against the oracle's."""
-    rng = np.random.default_rng(21)
-    B, H, Hkv, hd, W, C, step = 2, 16, 4, 64, 64, 48, 32
-    p = Pair(B, H, Hkv, hd, W + C + step, W, step)
+@pytest.mark.parametrize("step", [32, 20])
+def test_chunked_prime_into_ring(step):
+    """A prompt primed into a sliding-window ring of kvq_ring_rows rows in
+    chunks of up to C rows: each chunk's rows are appended, then its rows
+    attend causally (each within its window) to what the ring holds, through
+    the stream kernel (its 32-aligned start stays resident).  Every chunk's
+    outputs against the oracle's."""
+    rng = np.random.default_rng(21 + step)
+    B, H, Hkv, hd, W, C = 2, 16, 4, 64, 64, 48
+    cap = kvq.kvq_ring_rows(W, C, step)
+    p = Pair(B, H, Hkv, hd, cap, W, step)
     s = rng.standard_normal(H).astype(np.float32)
-    for it in range(9):
-        n = C if it < 8 else 13
+    for it in range(12):
+        n = C if it < 8 else int(rng.integers(1, C + 1))
         k, v = rows(rng, B, n, Hkv, hd)
         p.append(k, v)
         p.check_mirror()
+        assert np.all((np.maximum(0, p.ref.len - n + 1 - W) & ~31) >= p.ref.base)
         q = qrows(rng, B, n, H, hd)
         p.decode(q, 0.125, sinks=s, what=f"prime chunk {it}")
     assert int(p.ref.base[0]) > 0

@@ -490,6 +490,64 @@ def test_decode_ring_start_below_base_falls_back(lib):
         assert seen == {0, want}
 
 
+def _ring_model_ok(cap, W, C, S):
+    """The rebase rule kvq_append documents, over every session state reachable
+    from empty by appends of 1..C rows: True when no append drops a row its
+    first new row sees and no decode start (first visible row rounded down to
+    32) lies below base."""
+    if W + S > cap:
+        return False
+    seen, stack = {(0, 0)}, [(0, 0)]
+    while stack:
+        L, b = stack.pop()
+        for n in range(1, C + 1):
+            nb = b
+            while L + n - nb > cap:
+                nb += S
+            lo = max(0, L + 1 - W)
+            if (nb != b and lo < nb) or (lo & ~31) < nb:
+                return False
+            st = (L + n, nb)
+            if st[0] <= 4 * cap + 100 and st not in seen:
+                seen.add(st)
+                stack.append(st)
+    return True
+
+
+@pytest.mark.parametrize("W,C,S", [(64, 32, 32), (64, 40, 32), (64, 16, 64), (128, 64, 96), (100, 33, 48),
+                                   (96, 64, 40), (50, 20, 17), (80, 7, 5), (40, 1, 32)])
+def test_ring_rows_formula_against_the_rebase_rule(lib, W, C, S):
+    rows = kvq.kvq_ring_rows(W, C, S, lib)
+    assert rows == max(W + S, W + C + S - 2 + (0 if S % 32 == 0 else 31))
+    assert _ring_model_ok(rows, W, C, S)
+    if S % 32 == 0 and rows > W + S:
+        assert not _ring_model_ok(rows - 1, W, C, S)      # the smallest such ring
+
+
+def test_ring_rows_serves_prime_chunks_from_the_ring(lib):
+    """Random prompt chunks of up to C rows, then single rows, appended to a
+    ring of kvq_ring_rows rows: no append fails and every decode of the
+    appended rows runs the stream kernel (its 32-aligned start is resident)."""
+    rng = np.random.default_rng(5)
+    for W, C, S in ((96, 40, 32), (90, 33, 10), (256, 128, 64)):
+        cap = kvq.kvq_ring_rows(W, C, S, lib)
+        h = create(lib, n_seqs=1, n_q_heads=32, n_kv_heads=8, head_dim=128, capacity=cap, window=W, ring_step=S)
+        for i in range(120):
+            n = int(rng.integers(1, C + 1)) if i < 80 else 1
+            kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, n, None, 0, lib)
+            L, base = lengths(lib, h, 1)
+            assert ((max(0, L[0] - n + 1 - W)) & ~31) >= base[0]
+            assert plan_of(lib, h, T=n)["kernel"] == 2
+        kvq.kvq_destroy(h, lib)
+    from decode_attention_quantized_append_amd import workloads
+    w = workloads.get("prime")
+    assert w.ring_cap == kvq.kvq_ring_rows(w.window, w.T, w.ring_step, lib)
+    assert err(lib, kvq.kvq_ring_rows, 0, 8, 32) == kvq.KVQ_EINVAL
+    assert err(lib, kvq.kvq_ring_rows, 64, 0, 32) == kvq.KVQ_EINVAL
+    assert err(lib, kvq.kvq_ring_rows, 64, 8, 0) == kvq.KVQ_EINVAL
+    assert err(lib, kvq.kvq_ring_rows, 2 ** 31 - 1, 8, 32) == kvq.KVQ_EINVAL
+
+
 def test_launch_failure_reports_edevice_and_keeps_the_mirror(lib):
     h = create(lib)
     kvq.kvq_append(h, Q, Q, kvq.KVQ_F32, 10, None, 0, lib)
