@@ -701,6 +701,8 @@ kvq_status kvq_importance(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t 
     ip.lse = lse;
     ip.imp = imp;
     ip.tiles = (int32_t)ceil_div(std::max<int64_t>(maxspan, 1), 16);
+    if (!kvq::importance_group(ip.k_row, &ip.group_rows, &ip.rp))
+        return fail(KVQ_EUNSUPPORTED, "importance: 16 K rows do not fit the LDS");
     const char* err = nullptr;
     if (kvq::launch_importance(ip, stream, &err)) return fail(KVQ_EDEVICE, err ? err : "importance launch failed");
     return KVQ_OK;

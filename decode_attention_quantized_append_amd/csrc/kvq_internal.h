@@ -86,12 +86,29 @@ struct ImportanceParams {
     const float* lse;           // [B, T, H], natural log, the sink included
     float* imp;                 // [B, capacity] by physical row
     int32_t tiles;              // 16-row tiles per session in the grid
+    int32_t group_rows;         // rows (keys) per workgroup: a multiple of 16, at most 64
+    int32_t rp;                 // 16-byte pieces per K row in LDS (odd, >= (k_row + 30) / 16)
 };
+
 
 constexpr int kRowTile = 32;          // rows per tile of the stream kernel
 constexpr int kLdsBytes = 160 * 1024;
 
-// Geometry of the per-wave stream decode kernel for head_dim = 32 * NB (NB
+// The importance workgroup's rows and its LDS row stride in pieces for K
+// rows of k_row bytes: as many rows (16 .. 64, a multiple of 16) as half the
+// LDS holds next to the 2 KiB of per-wave key sums, so that two workgroups
+// share a CU, or all of it for long rows.  Returns false when not even 16
+// rows fit.
+inline bool importance_group(int k_row, int* rows, int* rp) {
+    *rp = ((k_row + 30) / 16) | 1;
+    const int bytes_per_row = *rp * 16;
+    int r = (kLdsBytes / 2 - 2048) / bytes_per_row;
+    if (r < 16) r = (kLdsBytes - 2048) / bytes_per_row;
+    r = r / 16 * 16;
+    if (r < 16) return false;
+    *rows = r > 64 ? 64 : r;
+    return true;
+}// Geometry of the per-wave stream decode kernel for head_dim = 32 * NB (NB
 // even): each wave copies its KV head's row windows of a 32-row tile, in
 // 16-byte pieces, into one private LDS buffer (K rows, then V rows), and
 // builds per-tile scale arrays.

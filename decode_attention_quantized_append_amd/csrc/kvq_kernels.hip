@@ -392,203 +392,163 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
 
 // ---------------------------------------------------------------------------
 // Attention importance (cortiq-engine "Struct LayerKvCache": attend_group's
-// imp_acc, accumulate_imp).  Workgroup (tile, session) takes 16 rows (keys)
-// of the session's visible union; its four waves share the (KV head, 16-row
-// tile of query rows) pairs, each a contiguous run of them.  Per pair, the
-// scores of the 16 keys against the 16 query rows are S^T = K Q^T on
-// v_mfma_f32_16x16x32_f16, one per 32-dim
-// block (the K codes exact in fp16, converted once per head; bf16 queries
-// exact in fp16, fp32 queries as an fp16 high and low part), each block's
-// product scaled by its keys' q8_0 scales.  Lane (q4, j16) then holds keys
-// 4 q4 + i against query row j16: the probability exp(scale s - lse) where
-// the key is visible to the row, else 0, summed over the 16 rows by
-// shuffles.  The waves' sums meet in LDS and one thread per key adds the
-// total to imp; a key belongs to one workgroup, so no atomics are needed.
-// Workgroups whose 16 keys all lie past the session's length return at once
-// (the grid covers the longest session, or in graph mode the plane).
-constexpr int kImpKeys = 16;
+// imp_acc, accumulate_imp).  Workgroup (group, session) takes group_rows
+// consecutive rows (keys) of the session's visible union.  Its waves first
+// copy the group's whole K rows into LDS with global_load_lds_dwordx4 (all
+// requests in flight at once; row r at r * rp 16-byte pieces, from the piece
+// at or below its first byte), then share the (KV head, 16-row tile of query
+// rows) pairs, one pair at a time each.  A wave converts its pair's query
+// rows once (each row divided by the power of two that puts its largest |q|
+// in [2^14, 2^15), dec::q_down, so that bf16 queries are exact in fp16 at
+// any magnitude; fp32 queries as an fp16 high and low part) and walks the
+// group's 16-key tiles: the scores of the 16 keys against the 16 query rows
+// are S^T = K Q^T on v_mfma_f32_16x16x32_f16, one per 32-dim block (the K
+// codes exact in fp16), each block's product scaled by its keys' q8_0 (or
+// FP8) scales.  Lane (q4, j16) then holds keys 4 q4 + i against query row
+// j16: the probability 2^(log2 e (scale s - lse)) where the key is visible
+// to the row, else 0, summed over the 16 rows by shuffles into the wave's
+// own LDS slot of the key.  At the end the waves' slots are added in a fixed
+// order and one thread per key adds the total to imp; a key belongs to one
+// workgroup, so no atomics are needed.  Workgroups whose keys all lie past
+// the session's length return at once (the grid covers the longest session,
+// or in graph mode the plane).
+constexpr int kImpWaves = 8;      // waves per workgroup, at most
+constexpr int kImpMaxRows = 64;   // rows (keys) per workgroup, at most
 // NB = head_dim / 32 (1 .. 8), the query dtype and the K format (F8: FP8 rows,
-// the codes then the scales; else q8_0 blocks) are template arguments, so
-// that no branch separates the loads of a pair from each other.
+// the codes then the scales; else q8_0 blocks) are template arguments.
 template <int NB, bool F32, bool F8>
-__global__ __launch_bounds__(256) void importance_kernel(ImportanceParams p) {
+__global__ __launch_bounds__(64 * kImpWaves) void importance_kernel(ImportanceParams p) {
     using dec::f4;
     using dec::h8;
-    __shared__ float part[4][kImpKeys];
+    extern __shared__ __align__(16) uint8_t krows[];   // group_rows x rp pieces of 16 bytes
+    __shared__ float slot[kImpWaves][kImpMaxRows];
     const int b = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     const int q4 = lane >> 4, j16 = lane & 15;
     const int len = p.len_d[b], base = p.base_d[b];
     const int lo = p.window > 0 ? max(0, len - p.T + 1 - p.window) : 0;
-    const int k0 = lo + blockIdx.x * kImpKeys;     // first key (logical row) of the tile
-    if (k0 >= len) return;                         // a tile past this session's rows (whole workgroup)
+    const int GR = p.group_rows, RP = p.rp;
+    const int kg0 = lo + blockIdx.x * GR;          // first key (logical row) of the group
+    if (kg0 >= len) return;                        // past this session's rows (whole workgroup)
+    const int nrows = min(GR, len - kg0);
+    const int ntile = (nrows + 15) / 16;
+
+    // ---- the group's K rows into LDS; pad pieces re-read a row's last one
+    const uint8_t* const plane = p.k_planes + (int64_t)b * p.k_stride;
+    const int64_t row0 = (int64_t)(kg0 - base) * p.k_row;
+    const uint8_t* const gbase = plane + (row0 & ~int64_t(15));
+    const int delta0 = (int)(row0 & 15);           // the group's first byte, from gbase
+    const int need = nrows * RP;
+    for (int x = wave; x * 64 < need; x += nw) {
+        const int s = x * 64 + lane;
+        const int r = s / RP, c = s - r * RP;
+        const int rb = delta0 + r * p.k_row;       // row r's first byte, from gbase
+        const int pc = min(rb / 16 + c, (rb + p.k_row - 1) / 16);
+        if (s < need) stream::dma16(gbase, (uint32_t)(pc * 16), krows + x * 1024);
+    }
+    for (int i = lane; i < kImpMaxRows; i += 64) slot[wave][i] = 0.0f;
+    stream::wait_loads_upto<0>();
+    __syncthreads();
+
     const int R = p.T * p.hpk;
-    constexpr int nb = NB;
     const int nrt = (R + 15) / 16;
     const int pairs = p.Hkv * nrt;
-    const uint8_t* const plane = p.k_planes + (int64_t)b * p.k_stride;
-    const int ka = k0 + j16;                       // this lane's key in the A operand
-    const bool ka_ok = ka < len;
-    const uint8_t* const krow_a = plane + (int64_t)(ka_ok ? ka - base : 0) * p.k_row;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    int gk = -1;
-    h8 kf[8];
-    float dk[8][4];
-    // wave w takes a contiguous run of pairs, so that the row tiles of one
-    // head follow each other and its K fragments are loaded once
-    const int ppw = (pairs + 3) / 4;
-    const int pend = min(pairs, (wave + 1) * ppw);
-    for (int pi = wave * ppw; pi < pend; ++pi) {
+    for (int pi = wave; pi < pairs; pi += nw) {
         const int g = pi / nrt, rt = pi - g * nrt;
-        const bool fresh = g != gk;                // K fragments and scales of head g needed
-        // Every load of the pair is issued before any value is used, so that
-        // they are in flight together: lanes whose key is past the length read
-        // row 0 of the plane, lanes past the R query rows read query row 0,
-        // and both drop what they read.
-        uint32_t kw[8][3];
-        uint16_t ks[8];
-        if (fresh) {
-#pragma unroll
-            for (int blk = 0; blk < 8; ++blk) {
-                if (blk < nb) {
-                    if constexpr (F8) {
-                        // the lane's 8 codes are 8 bytes on a word boundary (a
-                        // row is a whole number of words); the scale is in the
-                        // row's scale area
-                        const uint32_t* const kc =
-                            reinterpret_cast<const uint32_t*>(krow_a + (g * nb + blk) * 32 + 8 * q4);
-                        kw[blk][0] = kc[0];
-                        kw[blk][1] = kc[1];
-                        kw[blk][2] = 0u;
-                        ks[blk] = *reinterpret_cast<const uint16_t*>(krow_a + p.Hkv * p.hd + 2 * (g * nb + blk));
-                    } else {
-                        // the lane's 8 codes start 2 bytes into a word or on one:
-                        // three aligned words (one 12-byte load) hold them
-                        const uint8_t* const kb = krow_a + (g * nb + blk) * 34;
-                        const uintptr_t a = reinterpret_cast<uintptr_t>(kb + 2 + 8 * q4);
-                        __builtin_memcpy(kw[blk], reinterpret_cast<const void*>(a & ~uintptr_t(3)), 12);
-                        ks[blk] = *reinterpret_cast<const uint16_t*>(kb);
-                    }
-                }
-            }
-        }
-        const int r = rt * 16 + j16;               // this lane's query row in the B operand
+        // ---- the pair's query rows: this lane's row j16, dims 8 q4 .. of each block
+        const int r = rt * 16 + j16;
         const bool real = r < R;
         const int t = real ? r / p.hpk : 0, h = g * p.hpk + (real ? r % p.hpk : 0);
         const size_t qi = (((size_t)b * p.T + t) * p.H + h) * p.hd + 8 * q4;
-        uint4 qw[8][2];                            // bf16: [blk][0]; fp32: both, as float bits
-#pragma unroll
-        for (int blk = 0; blk < 8; ++blk) {
-            if (blk < nb) {
-                if constexpr (!F32) {
-                    qw[blk][0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + qi + blk * 32);
-                } else {
-                    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const float*>(p.q) + qi + blk * 32);
-                    qw[blk][0] = src[0];
-                    qw[blk][1] = src[1];
-                }
-            }
-        }
-        const float lraw = p.lse[((size_t)b * p.T + t) * p.H + h];
-        if (fresh) {
-            gk = g;
-#pragma unroll
-            for (int blk = 0; blk < 8; ++blk) {
-                if (blk < nb) {
-                    const uint32_t w0 = ka_ok ? kw[blk][0] : 0u;
-                    const uint32_t w1 = ka_ok ? kw[blk][1] : 0u;
-                    const uint32_t w2 = ka_ok ? kw[blk][2] : 0u;
-                    if constexpr (F8) {
-                        kf[blk] = stream::e4m3_codes(w0, w1);
-                    } else {
-                        const uintptr_t a = reinterpret_cast<uintptr_t>(krow_a + (g * nb + blk) * 34 + 2 + 8 * q4);
-                        const bool odd = (a & 2) != 0;
-                        const uint32_t c0 = odd ? __builtin_amdgcn_alignbit(w1, w0, 16) : w0;
-                        const uint32_t c1 = odd ? __builtin_amdgcn_alignbit(w2, w1, 16) : w1;
-                        kf[blk] = dec::k_codes_f16(c0, c1);
-                    }
-                    // the scale of this lane's key, handed to the lanes whose
-                    // D rows are keys 4 q4 + i
-                    const float dself = ka_ok ? f16_value(ks[blk]) : 0.0f;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) dk[blk][i] = __shfl(dself, 4 * q4 + i);
-                }
-            }
-        }
-        // the query row (this lane's 8 dims of each block; the row's other
-        // dims are with lanes j16 + 16, + 32, + 48) divided by the power of
-        // two that puts its largest |q| in [2^14, 2^15) (dec::q_down), so that
-        // bf16 queries are exact in fp16 at any magnitude
-        float qv[8][8];
+        // raw words (8 bf16 or 8 fp32 values per block), the row's largest
+        // magnitude from their bits, then the fp16 parts
+        constexpr int QW = F32 ? 8 : 4;
+        uint32_t qw[NB][QW];
         uint32_t mag = 0;
 #pragma unroll
-        for (int blk = 0; blk < 8; ++blk) {
-            if (blk < nb) {
-                if constexpr (!F32) {   // 8 bf16 values, 16 bytes
-                    const uint32_t w4[4] = {qw[blk][0].x, qw[blk][0].y, qw[blk][0].z, qw[blk][0].w};
+        for (int blk = 0; blk < NB; ++blk) {
+            if constexpr (!F32) {
+                const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + qi + blk * 32);
+                qw[blk][0] = u.x; qw[blk][1] = u.y; qw[blk][2] = u.z; qw[blk][3] = u.w;
+            } else {
+                const uint4* src = reinterpret_cast<const uint4*>(static_cast<const float*>(p.q) + qi + blk * 32);
+                const uint4 a = src[0], c = src[1];
+                qw[blk][0] = a.x; qw[blk][1] = a.y; qw[blk][2] = a.z; qw[blk][3] = a.w;
+                qw[blk][4] = c.x; qw[blk][5] = c.y; qw[blk][6] = c.z; qw[blk][7] = c.w;
+            }
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        qv[blk][2 * e] = __uint_as_float(w4[e] << 16);
-                        qv[blk][2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
-                    }
-                } else {
-                    const uint32_t w8[8] = {qw[blk][0].x, qw[blk][0].y, qw[blk][0].z, qw[blk][0].w,
-                                            qw[blk][1].x, qw[blk][1].y, qw[blk][1].z, qw[blk][1].w};
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) qv[blk][e] = __uint_as_float(w8[e]);
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    qv[blk][e] = real ? qv[blk][e] : 0.0f;
-                    mag = max(mag, __float_as_uint(qv[blk][e]) & 0x7FFFFFFFu);
-                }
+            for (int e = 0; e < QW; ++e) {
+                qw[blk][e] = real ? qw[blk][e] : 0u;
+                if (F32) mag = max(mag, qw[blk][e] & 0x7FFFFFFFu);
+                else mag = max(mag, max((qw[blk][e] << 16) & 0x7FFFFFFFu, qw[blk][e] & 0x7FFF0000u));
             }
         }
         mag = max(mag, (uint32_t)__shfl_xor((int)mag, 16));
         mag = max(mag, (uint32_t)__shfl_xor((int)mag, 32));
-        const float down = dec::q_down(dec::exp_of(mag));
-        f4 sv = {0.f, 0.f, 0.f, 0.f};
+        const float down = dec::q_down(dec::exp_of(mag)), up = dec::q_up(dec::exp_of(mag));
+        h8 qh[NB], ql[NB];
 #pragma unroll
-        for (int blk = 0; blk < 8; ++blk) {
-            if (blk < nb) {
-                h8 qh, ql;
+        for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float x = qv[blk][e] * down;
-                    qh[e] = (_Float16)x;
-                    ql[e] = (_Float16)(x - (float)qh[e]);
-                }
-                f4 d = dec::mfma(kf[blk], qh, (f4){0.f, 0.f, 0.f, 0.f});
-                if constexpr (F32) d = dec::mfma(kf[blk], ql, d);   // fp32 queries: the low part too
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sv[i] = fmaf(dk[blk][i], d[i], sv[i]);
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t wv = F32 ? qw[blk][e % QW] : ((e & 1) ? (qw[blk][e / 2] & 0xFFFF0000u) : (qw[blk][e / 2] << 16));
+                const float x = __uint_as_float(wv) * down;
+                qh[blk][e] = (_Float16)x;
+                if (F32) ql[blk][e] = (_Float16)(x - (float)qh[blk][e]);
             }
-        }
-        const float up = dec::q_up(dec::exp_of(mag));
-        const float l = real ? lraw : 0.0f;
+        const float l2 = real ? p.lse[((size_t)b * p.T + t) * p.H + h] * dec::kLog2e : 0.0f;
         const int upto = len - p.T + t + 1;
         const int first = p.window > 0 ? max(0, upto - p.window) : 0;
+        const float su2 = p.scale * up * dec::kLog2e;
+
+        // ---- the group's 16-key tiles
+        for (int ti = 0; ti < ntile; ++ti) {
+            const int kr = ti * 16 + j16;          // this lane's key row (A operand)
+            const bool ka_ok = kr < nrows;         // rows past the length were not loaded
+            const int rb = delta0 + kr * p.k_row;
+            const int krow = kr * RP * 16 + (rb & 15);   // the row's first byte in LDS
+            f4 sv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = k0 + 4 * q4 + i;
-            float pr = (real && key >= first && key < upto) ? expf(p.scale * (sv[i] * up) - l) : 0.0f;
-            pr += __shfl_xor(pr, 1);
-            pr += __shfl_xor(pr, 2);
-            pr += __shfl_xor(pr, 4);
-            pr += __shfl_xor(pr, 8);
-            acc[i] += pr;
+            for (int blk = 0; blk < NB; ++blk) {
+                // one block's reads at a time: tie them to the previous
+                // block's sums, so that the reads of all blocks are not held
+                // at once
+                if (NB >= 5) asm volatile("" : "+v"(sv));
+                // the lane's 8 codes from the 3 aligned words holding them
+                const int ca = krow + (F8 ? (g * NB + blk) * 32 : (g * NB + blk) * 34 + 2) + 8 * q4;
+                const uint32_t* const cw = reinterpret_cast<const uint32_t*>(krows + (ca & ~3));
+                const uint32_t sh = (uint32_t)(ca & 3) * 8;
+                const uint32_t w0 = ka_ok ? cw[0] : 0u, w1 = ka_ok ? cw[1] : 0u, w2 = ka_ok ? cw[2] : 0u;
+                const uint32_t c0 = __builtin_amdgcn_alignbit(w1, w0, sh);
+                const uint32_t c1 = __builtin_amdgcn_alignbit(w2, w1, sh);
+                const int sa = krow + (F8 ? p.Hkv * p.hd + 2 * (g * NB + blk) : (g * NB + blk) * 34);
+                const uint16_t sbits = *reinterpret_cast<const uint16_t*>(krows + sa);
+                const h8 kf = F8 ? stream::e4m3_codes(c0, c1) : dec::k_codes_f16(c0, c1);
+                // the scale of this lane's key, handed to the lanes whose D
+                // rows are keys 4 q4 + i
+                const float dself = ka_ok ? f16_value(sbits) : 0.0f;
+                f4 d = dec::mfma(kf, qh[blk], (f4){0.f, 0.f, 0.f, 0.f});
+                if constexpr (F32) d = dec::mfma(kf, ql[blk], d);   // fp32 queries: the low part too
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sv[i] = fmaf(__shfl(dself, 4 * q4 + i), d[i], sv[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = kg0 + ti * 16 + 4 * q4 + i;
+                float pr = (real && key >= first && key < upto) ? __builtin_amdgcn_exp2f(fmaf(su2, sv[i], -l2)) : 0.0f;
+                pr += __shfl_xor(pr, 1);
+                pr += __shfl_xor(pr, 2);
+                pr += __shfl_xor(pr, 4);
+                pr += __shfl_xor(pr, 8);
+                if (j16 == 0) slot[wave][ti * 16 + 4 * q4 + i] += pr;
+            }
         }
     }
-    if (j16 == 0)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) part[wave][4 * q4 + i] = acc[i];
     __syncthreads();
-    if (tid < kImpKeys) {
-        const int key = k0 + tid;
-        if (key < len) {
-            float* dst = p.imp + (size_t)b * p.capacity + (key - base);
-            *dst += ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
-        }
+    for (int i = threadIdx.x; i < nrows; i += blockDim.x) {
+        float s = 0.0f;
+        for (int w = 0; w < nw; ++w) s += slot[w][i];
+        p.imp[(size_t)b * p.capacity + (kg0 + i - base)] += s;
     }
 }
 
@@ -868,26 +828,31 @@ int launch_partials(const DecodeParams& p, hipStream_t st, const char** err) {
 
 template <bool F32>
 bool launch_importance_dtype(const ImportanceParams& p, hipStream_t st) {
-    const dim3 grid(p.tiles, p.B), block(256);
+    // the (KV head, row tile) pairs over at most kImpWaves waves
+    const int pairs = p.Hkv * ((p.T * p.hpk + 15) / 16);
+    const dim3 grid((p.tiles * 16 + p.group_rows - 1) / p.group_rows, p.B), block(64 * std::min(pairs, kImpWaves));
+    const size_t lds = (size_t)p.group_rows * p.rp * 16;
+#define KVQ_IMP(NB, F8) hipLaunchKernelGGL((importance_kernel<NB, F32, F8>), grid, block, lds, st, p); return true
     if (p.f8) {   // FP8 rows: head_dim 64, 128 or 256
         switch (p.hd / 32) {
-            case 2: hipLaunchKernelGGL((importance_kernel<2, F32, true>), grid, block, 0, st, p); return true;
-            case 4: hipLaunchKernelGGL((importance_kernel<4, F32, true>), grid, block, 0, st, p); return true;
-            case 8: hipLaunchKernelGGL((importance_kernel<8, F32, true>), grid, block, 0, st, p); return true;
+            case 2: KVQ_IMP(2, true);
+            case 4: KVQ_IMP(4, true);
+            case 8: KVQ_IMP(8, true);
             default: return false;
         }
     }
     switch (p.hd / 32) {
-        case 1: hipLaunchKernelGGL((importance_kernel<1, F32, false>), grid, block, 0, st, p); return true;
-        case 2: hipLaunchKernelGGL((importance_kernel<2, F32, false>), grid, block, 0, st, p); return true;
-        case 3: hipLaunchKernelGGL((importance_kernel<3, F32, false>), grid, block, 0, st, p); return true;
-        case 4: hipLaunchKernelGGL((importance_kernel<4, F32, false>), grid, block, 0, st, p); return true;
-        case 5: hipLaunchKernelGGL((importance_kernel<5, F32, false>), grid, block, 0, st, p); return true;
-        case 6: hipLaunchKernelGGL((importance_kernel<6, F32, false>), grid, block, 0, st, p); return true;
-        case 7: hipLaunchKernelGGL((importance_kernel<7, F32, false>), grid, block, 0, st, p); return true;
-        case 8: hipLaunchKernelGGL((importance_kernel<8, F32, false>), grid, block, 0, st, p); return true;
+        case 1: KVQ_IMP(1, false);
+        case 2: KVQ_IMP(2, false);
+        case 3: KVQ_IMP(3, false);
+        case 4: KVQ_IMP(4, false);
+        case 5: KVQ_IMP(5, false);
+        case 6: KVQ_IMP(6, false);
+        case 7: KVQ_IMP(7, false);
+        case 8: KVQ_IMP(8, false);
         default: return false;
     }
+#undef KVQ_IMP
 }
 
 int launch_importance(const ImportanceParams& p, void* stream, const char** err) {

@@ -70,7 +70,9 @@ int launch_decode(const DecodeParams& p, void*, void* const ev[3], const char** 
 }
 
 int launch_importance(const ImportanceParams& p, void*, const char** err) {
-    return record("importance T=" + std::to_string(p.T) + " tiles=" + std::to_string(p.tiles), err);
+    return record("importance T=" + std::to_string(p.T) + " tiles=" + std::to_string(p.tiles) +
+                      " group_rows=" + std::to_string(p.group_rows) + " rp=" + std::to_string(p.rp),
+                  err);
 }
 
 }  // namespace kvq

@@ -114,8 +114,9 @@ def load(path: Optional[str] = None):
 
 
 def load_nodev():
-    """The host logic linked to a recording launcher (CPU tests only)."""
-    lib = _declare(ctypes.CDLL(NODEV_PATH))
+    """The host logic linked to a recording launcher (CPU tests only;
+    KVQ_NODEV_LIB names another build of it, such as a sanitizer build)."""
+    lib = _declare(ctypes.CDLL(os.environ.get("KVQ_NODEV_LIB") or NODEV_PATH))
     lib.kvq_nodev_log.restype = ctypes.c_char_p
     lib.kvq_nodev_clear.restype = None
     lib.kvq_nodev_fail_next.restype = None

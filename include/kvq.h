@@ -264,13 +264,16 @@ kvq_status kvq_decode_noalloc(kvq_cache* h, const void* q, kvq_dtype dtype, int3
  * no query row sees get nothing; the sink's share is in lse but lands on no
  * row.  imp: device float [n_seqs, capacity], indexed by physical row (a ring
  * rebase moves K and V rows, not importance).  Call it before the cache
- * changes again.  One launch; the rows of a session are split over
- * workgroups, each adding to its own rows only; in graph mode the grid
- * covers every length the plane allows, like kvq_decode's.  Queries of any
+ * changes again.  One launch; the rows are cut into groups of up to 64
+ * consecutive rows of a session, each group taken by one workgroup, which
+ * alone adds to its rows; in graph mode the groups cover every length the
+ * plane allows, like kvq_decode's plan.  Queries of any
  * finite magnitude are taken as kvq_decode takes them; each probability is
  * exp of a binary32 score less the lse, so its relative error grows with
  * the score's magnitude (about 1e-2 at |score| near 1e5, 1e-4 near 1e3).
- * Errors: EINVAL, ERANGE (a visible row was rebased away), EDEVICE. */
+ * Errors: EINVAL, ERANGE (a visible row was rebased away), EUNSUPPORTED (K
+ * rows of more than 296 blocks of 32 elements, e.g. more than 37 KV heads of
+ * 256 dims: a workgroup stages 16 whole rows in its LDS), EDEVICE. */
 kvq_status kvq_importance(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t T, float scale,
                           const float* lse, float* imp, kvq_stream stream);
 

@@ -31,7 +31,8 @@ def load(path: str | None = None):
     global _lib
     if path is None and _lib is not None:
         return _lib
-    p = path or _LIB
+    # KVQ_ORACLE_LIB: another build of the same source (the sanitizer test's)
+    p = path or os.environ.get("KVQ_ORACLE_LIB") or _LIB
     if not os.path.exists(p):
         build_oracle(out=p)
     lib = ctypes.CDLL(p)

@@ -299,6 +299,9 @@ def test_importance_launch(lib):
     kvq.kvq_importance(h, Q, kvq.KVQ_BF16, 2, 0.1, O, O, 0, lib)
     (line,) = log(lib)
     assert fields(line)["tiles"] == -(-3000 // 16) and fields(line)["T"] == 2
+    # K rows of 2 heads x 64 dims: 136 bytes, 11 pieces of LDS each (odd, with
+    # room for a row starting up to 15 bytes into its first piece); 64 rows
+    assert fields(line)["rp"] == 11 and fields(line)["group_rows"] == 64
     lib.kvq_nodev_clear()
     assert err(lib, kvq.kvq_importance, h, Q, kvq.KVQ_BF16, 1001, 0.1, O, O) == kvq.KVQ_EINVAL
     assert err(lib, kvq.kvq_importance, h, Q, kvq.KVQ_BF16, 1, 0.1, O, 0) == kvq.KVQ_EINVAL
@@ -310,6 +313,19 @@ def test_importance_launch(lib):
     lib.kvq_nodev_clear()
     kvq.kvq_importance(hw, Q, kvq.KVQ_BF16, 3, 0.1, O, O, 0, lib)
     assert fields(log(lib)[0])["tiles"] == -(-(100 + 2) // 16)
+    # long rows: 37 KV heads x 256 dims (10064-byte rows) leave room for 16
+    # rows in the whole LDS; 38 heads x 256 not even for that
+    hl = create(lib, n_seqs=1, n_q_heads=37, n_kv_heads=37, head_dim=256, capacity=64)
+    kvq.kvq_append(hl, Q, Q, kvq.KVQ_BF16, 20, None, 0, lib)
+    lib.kvq_nodev_clear()
+    kvq.kvq_importance(hl, Q, kvq.KVQ_BF16, 1, 0.1, O, O, 0, lib)
+    f = fields(log(lib)[0])
+    assert f["rp"] == 631 and f["group_rows"] == 16
+    hx = create(lib, n_seqs=1, n_q_heads=38, n_kv_heads=38, head_dim=256, capacity=64)
+    kvq.kvq_append(hx, Q, Q, kvq.KVQ_BF16, 20, None, 0, lib)
+    lib.kvq_nodev_clear()
+    assert err(lib, kvq.kvq_importance, hx, Q, kvq.KVQ_BF16, 1, 0.1, O, O) == kvq.KVQ_EUNSUPPORTED
+    assert log(lib) == []
 
 
 def test_rollback_relative(lib):
