@@ -39,6 +39,7 @@ struct kvq_cache {
     int32_t cus;                 // compute units of the device the handle was created on
     void* trace[3];              // events kvq_decode records around its kernels (or null)
     void* scratch;               // the library's device scratch on the handle's device
+    float* imp;                  // importance moved along by rebases (kvq_set_importance), or null
 };
 
 namespace {
@@ -566,6 +567,8 @@ kvq_status kvq_append(kvq_cache* h, const void* k_new, const void* v_new, kvq_dt
         }
     for (int64_t slab = 0; slab < max_slabs; ++slab) {
         kvq::MoveParams mp{};
+        mp.imp = h->imp;
+        mp.capacity = c.capacity;
         mp.k_planes = h->k;
         mp.v_planes = h->v;
         mp.k_stride = (int64_t)h->sz.k_session_stride;
@@ -597,6 +600,29 @@ kvq_status kvq_append(kvq_cache* h, const void* k_new, const void* v_new, kvq_dt
         }
         kvq_status s = flush();
         if (s != KVQ_OK) return s;
+    }
+    if (h->imp) {
+        // the registered importance: the positions the survivors left are cleared
+        kvq::MoveParams zp{};
+        zp.imp = h->imp;
+        zp.capacity = c.capacity;
+        zp.zero = 1;
+        for (int b = 0; b < B; ++b) {
+            if (nbase[b] == h->base[b]) continue;
+            const int64_t keep = std::max<int64_t>(0, h->len[b] - nbase[b]);
+            zp.sess[zp.n] = b;
+            zp.dst_row[zp.n] = (int32_t)keep;
+            zp.rows[zp.n] = (int32_t)(c.capacity - keep);
+            if (++zp.n == kvq::kMaxSessionsPerLaunch || b == B - 1) {
+                const char* err = nullptr;
+                if (kvq::launch_move(zp, stream, &err)) return fail(KVQ_EDEVICE, err ? err : "move kernel launch failed");
+                zp.n = 0;
+            }
+        }
+        if (zp.n > 0) {
+            const char* err = nullptr;
+            if (kvq::launch_move(zp, stream, &err)) return fail(KVQ_EDEVICE, err ? err : "move kernel launch failed");
+        }
     }
     if (!set_idx.empty()) {
         kvq_status s = enqueue_sets(h->counters, set_idx, set_val, stream);
@@ -794,6 +820,13 @@ kvq_status kvq_host_lengths(const kvq_cache* h, int64_t* len, int64_t* base) {
         if (len) len[b] = h->len[b];
         if (base) base[b] = h->base[b];
     }
+    return KVQ_OK;
+}
+
+kvq_status kvq_set_importance(kvq_cache* h, float* imp) {
+    if (!h) return fail(KVQ_EINVAL, "handle is NULL");
+    if (!aligned(imp, 4)) return fail(KVQ_EINVAL, "imp must be 4-byte aligned");
+    h->imp = imp;
     return KVQ_OK;
 }
 

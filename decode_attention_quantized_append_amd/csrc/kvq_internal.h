@@ -55,8 +55,13 @@ struct SetParams {
 };
 
 // One non-overlapping slab per listed session: physical rows
-// [src_row, src_row + rows) -> [dst_row, dst_row + rows) of the K and V planes.
+// [src_row, src_row + rows) -> [dst_row, dst_row + rows) of the K and V planes
+// (and of imp, when set).  zero = 1: instead, imp's entries [dst_row, dst_row
+// + rows) of each listed session are set to 0 (the planes are not touched).
 struct MoveParams {
+    float* imp;                 // [B, capacity] importance by physical row, or null
+    int32_t capacity;
+    int32_t zero;
     uint8_t* k_planes;
     uint8_t* v_planes;
     int64_t k_stride;

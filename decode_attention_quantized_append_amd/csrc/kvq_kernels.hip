@@ -120,6 +120,18 @@ __device__ void copy_bytes(uint8_t* dst, const uint8_t* src, int64_t bytes) {
 __global__ void move_kernel(MoveParams p) {
     const int i = blockIdx.y;
     const int b = p.sess[i];
+    if (p.zero) {
+        float* const e = p.imp + (int64_t)b * p.capacity + p.dst_row[i];
+        for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < p.rows[i];
+             j += (int64_t)gridDim.x * blockDim.x)
+            e[j] = 0.0f;
+        return;
+    }
+    if (p.imp) {
+        float* const e = p.imp + (int64_t)b * p.capacity;
+        copy_bytes(reinterpret_cast<uint8_t*>(e + p.dst_row[i]), reinterpret_cast<const uint8_t*>(e + p.src_row[i]),
+                   (int64_t)p.rows[i] * 4);
+    }
     uint8_t* kp = p.k_planes + (int64_t)b * p.k_stride;
     uint8_t* vp = p.v_planes + (int64_t)b * p.v_stride;
     copy_bytes(kp + (int64_t)p.dst_row[i] * p.k_row, kp + (int64_t)p.src_row[i] * p.k_row,
@@ -770,7 +782,7 @@ int launch_set(const SetParams& p, void* stream, const char** err) {
 
 int launch_move(const MoveParams& p, void* stream, const char** err) {
     int64_t maxbytes = 0;
-    for (int i = 0; i < p.n; ++i) maxbytes = std::max<int64_t>(maxbytes, (int64_t)p.rows[i] * p.k_row);
+    for (int i = 0; i < p.n; ++i) maxbytes = std::max<int64_t>(maxbytes, (int64_t)p.rows[i] * (p.zero ? 4 : p.k_row));
     int gx = (int)std::min<int64_t>(1024, (maxbytes / 16 + 255) / 256 + 1);
     hipLaunchKernelGGL(move_kernel, dim3(gx, p.n), dim3(256), 0, (hipStream_t)stream, p);
     return check(err);

@@ -45,7 +45,13 @@ int launch_set(const SetParams& p, void*, const char** err) {
 }
 
 int launch_move(const MoveParams& p, void*, const char** err) {
-    std::string s = "move";
+    if (p.zero) {
+        std::string s = "zero_imp";
+        for (int i = 0; i < p.n; ++i)
+            s += " " + std::to_string(p.sess[i]) + "@" + std::to_string(p.dst_row[i]) + "+" + std::to_string(p.rows[i]);
+        return record(s, err);
+    }
+    std::string s = std::string(p.imp ? "move+imp" : "move");
     for (int i = 0; i < p.n; ++i)
         s += " " + std::to_string(p.sess[i]) + ":" + std::to_string(p.src_row[i]) + ">" +
              std::to_string(p.dst_row[i]) + "x" + std::to_string(p.rows[i]);

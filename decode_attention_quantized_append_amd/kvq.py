@@ -31,7 +31,7 @@ STATUS_NAMES = {0: "KVQ_OK", 1: "KVQ_EINVAL", 2: "KVQ_ECAPACITY", 3: "KVQ_ERANGE
 EXPORTS = ("kvq_required_bytes", "kvq_ring_rows", "kvq_create", "kvq_append", "kvq_decode_workspace_bytes",
            "kvq_decode", "kvq_decode_noalloc", "kvq_truncate", "kvq_set_split_rows", "kvq_set_decode_tiling", "kvq_info",
            "kvq_host_lengths", "kvq_set_graph_mode", "kvq_set_host_lengths", "kvq_importance",
-           "kvq_rollback", "kvq_set_trace_events", "kvq_destroy", "kvq_last_error")
+           "kvq_rollback", "kvq_set_importance", "kvq_set_trace_events", "kvq_destroy", "kvq_last_error")
 
 
 class kvq_config(ctypes.Structure):
@@ -82,6 +82,7 @@ def _declare(lib):
         "kvq_host_lengths": (st, [vp, i64p, i64p]),
         "kvq_set_graph_mode": (st, [vp, i32]),
         "kvq_set_trace_events": (st, [vp, vp, vp, vp]),
+        "kvq_set_importance": (st, [vp, vp]),
         "kvq_importance": (st, [vp, vp, i32, i32, f32, vp, vp, vp]),
         "kvq_set_host_lengths": (st, [vp, i64p, i64p]),
         "kvq_destroy": (None, [vp]),
@@ -221,6 +222,11 @@ def kvq_host_lengths(h: int, n_seqs: int, lib=None):
     bs = (ctypes.c_int64 * n_seqs)()
     _check(lib, lib.kvq_host_lengths(h, ln, bs))
     return list(ln), list(bs)
+
+
+def kvq_set_importance(h: int, imp: Optional[int], lib=None) -> None:
+    lib = lib or load()
+    _check(lib, lib.kvq_set_importance(h, imp or None))
 
 
 def kvq_set_trace_events(h: int, before_partials: Optional[int], before_combine: Optional[int],
@@ -366,6 +372,15 @@ class KvqLayerCache:
         kvq_importance(self.h, q.data_ptr(), self._dtype(q), T, float(scale), lse.data_ptr(),
                        imp.data_ptr(), self._stream(), self.lib)
         return imp
+
+    def set_importance(self, imp):
+        """Registers imp (float32 [B, capacity] on the device, or None) to be
+        moved along with the rows by every ring rebase; kept referenced."""
+        import torch
+        if imp is not None:
+            assert imp.dtype == torch.float32 and imp.is_contiguous() and imp.shape == (self.cfg.n_seqs, self.cfg.capacity)
+        self._imp = imp
+        kvq_set_importance(self.h, imp.data_ptr() if imp is not None else None, self.lib)
 
     def set_graph_mode(self, on=True):
         kvq_set_graph_mode(self.h, on, self.lib)

@@ -263,7 +263,8 @@ kvq_status kvq_decode_noalloc(kvq_cache* h, const void* q, kvq_dtype dtype, int3
  * exp(scale * q.K'_row - lse[b, t, h]): the row's softmax probability.  Rows
  * no query row sees get nothing; the sink's share is in lse but lands on no
  * row.  imp: device float [n_seqs, capacity], indexed by physical row (a ring
- * rebase moves K and V rows, not importance).  Call it before the cache
+ * rebase moves K and V rows, and moves imp with them only when imp is
+ * registered with kvq_set_importance).  Call it before the cache
  * changes again.  One launch; the rows are cut into groups of up to 64
  * consecutive rows of a session, each group taken by one workgroup, which
  * alone adds to its rows; in graph mode the groups cover every length the
@@ -359,6 +360,20 @@ kvq_status kvq_host_lengths(const kvq_cache* h, int64_t* len, int64_t* base);
  * + 1] to 1 (it stays 1).  After replays, kvq_set_host_lengths brings the
  * host mirror back in step.  Off (0) by default.  Errors: EINVAL. */
 kvq_status kvq_set_graph_mode(kvq_cache* h, int32_t on);
+
+/* Registers a device float array imp [n_seqs, capacity] (as kvq_importance
+ * fills, indexed by physical row; NULL unregisters) that every later ring
+ * rebase of this handle moves together with the K and V rows: the entries
+ * of the surviving rows go where their rows go, and the entries of the
+ * physical rows the rebase leaves unused (from the survivors' count up to
+ * capacity) are set to 0, so that imp stays the mass of the row stored at
+ * each position.  Flat caches never move rows.  The array must stay valid
+ * until it is unregistered or the handle destroyed.
+ * Defined by: cortiq-engine "Struct LayerKvCache" page, accumulate_imp (the
+ * importance accumulated per stored row); memra-engine "Struct KvLayer"
+ * page, base_d (the ring view that a rebase moves).
+ * Errors: EINVAL (NULL handle, imp not 4-byte aligned). */
+kvq_status kvq_set_importance(kvq_cache* h, float* imp);
 
 /* Instrumentation: events (hipEvent_t, created by the caller; NULL = none)
  * that every later kvq_decode on this handle records on its stream: before

@@ -290,6 +290,42 @@ def test_importance_parity(name):
         np.testing.assert_allclose(imp.sum(1).cpu().numpy(), 2 * T * H, rtol=1e-4)
 
 
+@pytest.mark.parametrize("fmt", ["q8_0/q5_1", "e4m3"])
+def test_registered_importance_follows_rebases(fmt):
+    """Importance accumulated step by step in a ring that rebases, with the
+    array registered (kvq_set_importance): after every step it holds the
+    oracle's mass accumulated per logical row at that row's current physical
+    position, and 0 where no live row is stored."""
+    rng = np.random.default_rng(31)
+    B, H, Hkv, hd, W, step, T = 2, 8, 2, 64, 48, 32, 3
+    cap = kvq.kvq_ring_rows(W, T, step)
+    p = Pair(B, H, Hkv, hd, cap, W, step, fmt=fmt)
+    imp = torch.zeros((B, cap), dtype=torch.float32, device=DEV)
+    p.gpu.set_importance(imp)
+    acc = [dict() for _ in range(B)]        # logical row -> mass
+    scale = float(np.float32(1 / np.sqrt(hd)))
+    rebases = 0
+    for it in range(70):
+        base0 = p.ref.base.copy()
+        k, v = rows(rng, B, T, Hkv, hd)
+        p.append(k, v)
+        rebases += int(np.any(p.ref.base != base0))
+        q = qrows(rng, B, T, H, hd)
+        qd = to_dev(q, "bf16")
+        _, lse = p.gpu.decode(qd, scale)
+        p.gpu.importance(qd, scale, lse, imp)
+        torch.cuda.synchronize(DEV)
+        step_mass = p.ref.importance(q, scale=scale)
+        want = np.zeros((B, cap))
+        for b in range(B):
+            base, ln = int(p.ref.base[b]), int(p.ref.len[b])
+            for r in range(ln - base):
+                acc[b][base + r] = acc[b].get(base + r, 0.0) + float(step_mass[b][r])
+                want[b][r] = acc[b][base + r]
+        assert_close(imp.cpu().numpy(), want, f"{fmt} step {it} importance")
+    assert rebases >= 3
+
+
 @pytest.mark.parametrize("step", [32, 20])
 def test_chunked_prime_into_ring(step):
     """A prompt primed into a sliding-window ring of kvq_ring_rows rows in

@@ -178,6 +178,31 @@ def test_ring_rebase_plan_matches_the_oracle_cache_model(lib):
             assert f"{B + b}={after[1][b]}" in [t for ln in log(lib) if ln.startswith("set") for t in ln.split()]
 
 
+def test_registered_importance_moves_with_the_rows(lib):
+    """With an importance array registered, every rebase slab moves its
+    entries too, and the positions past the survivors are cleared."""
+    B, cap, W, step = 2, 16, 8, 4
+    h = create(lib, n_seqs=B, capacity=cap, window=W, ring_step=step)
+    kvq.kvq_set_importance(h, 0x70000000, lib)
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_F32, 14, [14, 9], 0, lib)
+    lib.kvq_nodev_clear()
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_F32, 3, None, 0, lib)      # session 0: 17 rows > 16 -> base 4
+    lines = log(lib)
+    moves = [ln for ln in lines if ln.startswith("move")]
+    assert moves and all(ln.startswith("move+imp ") for ln in moves)
+    (zero,) = [ln for ln in lines if ln.startswith("zero_imp")]
+    assert zero == "zero_imp 0@10+6"                               # 14 - 4 survivors
+    assert lines.index(zero) > max(lines.index(m) for m in moves)
+    assert lengths(lib, h, B) == ([17, 12], [4, 0])
+    kvq.kvq_set_importance(h, None, lib)
+    lib.kvq_nodev_clear()
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_F32, 14, [4, 0], 0, lib)      # session 0: 21 rows -> base 8
+    lines = log(lib)
+    assert [ln for ln in lines if ln.startswith("move ")] and lengths(lib, h, B) == ([21, 12], [8, 0])
+    assert not [ln for ln in lines if ln.startswith(("move+imp", "zero_imp"))]
+    assert err(lib, kvq.kvq_set_importance, h, 0x70000002) == kvq.KVQ_EINVAL
+
+
 def test_ring_refuses_to_drop_visible_rows(lib):
     h = create(lib, n_seqs=1, capacity=16, window=8, ring_step=4)
     kvq.kvq_append(h, Q, Q, kvq.KVQ_F32, 14, None, 0, lib)
