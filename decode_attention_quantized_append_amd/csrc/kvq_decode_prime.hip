@@ -1,0 +1,449 @@
+// kvq_decode_prime.hip -- split-K decode for many query rows per KV head (a
+// prompt chunk), each KV tile unpacked once for eight query-row groups
+// (gfx950).  Included by kvq_kernels.hip (inside namespace kvq), after
+// kvq_decode_stream.hip.
+//
+// The same partials as the other decode kernels (cortiq-engine "Struct
+// LayerKvCache", attend_group_upto: every query row of the chunk attends
+// causally, within its window; memra-engine "Module cache", prime of a
+// prompt chunk into the ring):
+//   * a workgroup is (session, chunk of rows, KV head) on the grid's x index
+//     and a block of eight query-row groups on its y index; wave w computes
+//     group 8 y + w (32 query rows: Tg positions x hpk heads, two 16-row
+//     tiles) over all the head's dims.
+//   * per 32-row tile, the eight waves copy the tile's q8_0 / q5_1 blocks of
+//     the head into LDS together (global_load_lds_dwordx4, one instruction or
+//     two per wave) and then convert them together, once, into fp16 operands
+//     in LDS: the K codes (exact), the V codes as fp16 subnormals code x 2^-24
+//     (exact), the K scales (times scale * log2 e), the V steps (fp16) and the
+//     V offset rows (with a column of ones for the row sums).  Each wave then
+//     reads its matrix-core operands from there: ds_read_b128 for the K
+//     blocks (A of S^T = K Q^T), pairs of ds_read_b64_tr_b16 for the V codes
+//     (B of P V, 8 keys of one dim per lane).
+//   * raw rows and converted operands are both double-buffered: while the
+//     waves score tile t, tile t + 1's rows have landed and tile t + 2's are
+//     in flight; one workgroup barrier per tile separates the conversion of
+//     the next tile from the reads of the current one.
+//   * the softmax, the fp16 P, the packed P * step products, the offset and
+//     row-sum product and the range handling are those of the stream kernel.
+namespace prime {
+
+using dec::f4;
+using dec::h8;
+using dec::kLn2;
+using dec::kLog2e;
+
+constexpr int kTile = kRowTile;
+constexpr int kWaves = kPrimeGroups;
+constexpr int kRawBufs = kPrimeRawBufs;
+
+// vmcnt(n) for a count known only at run time (n < 0: wait for all).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+    switch (n) {
+        case 1: stream::wait_loads_upto<1>(); break;
+        case 2: stream::wait_loads_upto<2>(); break;
+        case 3: stream::wait_loads_upto<3>(); break;
+        case 4: stream::wait_loads_upto<4>(); break;
+        case 5: stream::wait_loads_upto<5>(); break;
+        case 6: stream::wait_loads_upto<6>(); break;
+        case 7: stream::wait_loads_upto<7>(); break;
+        default:
+            if (n >= 8) stream::wait_loads_upto<8>();
+            else stream::wait_loads_upto<0>();
+    }
+}
+
+template <int NB, bool QLO>
+__global__ __launch_bounds__(64 * kWaves, 1) void decode_prime(DecodeParams p) {
+    using LY = PrimeLayout<NB>;
+    static_assert(LY::BYTES <= kLdsBytes, "the prime layout must fit a CU's LDS");
+    using WN = typename LY::WN;
+    constexpr int HD = LY::HD;
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int q4 = lane >> 4, j16 = lane & 15;
+
+    // ---- the unit: (session, chunk, KV head) from the grid's x index, XCD by XCD
+    const int W = gridDim.x, wid = blockIdx.x;
+    const int L = (wid & 7) * (W >> 3) + (wid >> 3);
+    const int g = L % p.Hkv;
+    int b, s, len, base;
+    dec::locate_unit(p, L / p.Hkv, b, s, len, base);
+    if (b < 0) return;
+    const int lo = p.window > 0 ? max(0, len - p.T + 1 - p.window) : 0;
+    const int c0 = (lo & ~(kTile - 1)) + s * p.chunk;
+    const int c1 = min(c0 + p.chunk, len);
+    if (c0 >= c1) return;
+    // this workgroup's query positions, and the rows any of them sees
+    const int ngroups = (p.T + p.Tg - 1) / p.Tg;
+    const int gfirst = blockIdx.y * kWaves;
+    const int wlo = gfirst * p.Tg, whi = min(p.T, (gfirst + kWaves) * p.Tg);
+    const int seen_lo = p.window > 0 ? max(0, len - p.T + wlo + 1 - p.window) : 0;
+    const int seen_hi = len - p.T + whi;          // one past the last row the last position sees
+    const int t_begin = max(c0, seen_lo & ~(kTile - 1));
+    const int t_end = min(c1, seen_hi);
+    const int ntiles = t_begin < t_end ? (t_end - t_begin + kTile - 1) / kTile : 0;
+
+    // this wave's query rows
+    const int grp = gfirst + wave;
+    const bool active = grp < ngroups;
+    const int tq0 = active ? grp * p.Tg : 0;
+    const int Tq = active ? min(p.Tg, p.T - tq0) : 0;
+    const int R = Tq * p.hpk;
+
+    // ---- tile loads: instruction i of a tile's NIT (K pieces, then V pieces)
+    // is issued by wave i mod 8
+    const uint8_t* const kwin0 = p.k_planes + (int64_t)b * p.k_stride;
+    const int kstart = g * NB * 34;
+    const int kofs = kstart & 15;
+    const uint8_t* const kwin = kwin0 + kstart - kofs;
+    const uint8_t* const vwin = p.v_planes + (int64_t)b * p.v_stride + g * NB * 24;
+    // this wave's load instructions for the tile at t0: 0 past the last
+    // tile, -1 for a partial tile (its wave-wide empty loads may be skipped,
+    // so that only a wait for all loads is safe behind it)
+    auto my_loads = [&](int t0) -> int {
+        if (t0 >= t_begin + ntiles * kTile) return 0;
+        if (t0 + kTile > c1) return -1;
+        return (LY::NIT - wave + kWaves - 1) / kWaves;
+    };
+    auto issue = [&](int t0, int buf) {
+        asm volatile("" ::: "memory");
+        const int nrows = min(kTile, c1 - t0);
+        uint8_t* const rb = smem + buf * LY::RAW;
+        for (int i = wave; i < LY::NIT; i += kWaves) {
+            if (i < WN::NKI) {
+                const int pc = i * 64 + lane, row = pc / WN::KWP, col = pc - row * WN::KWP;
+                const uint32_t off = (uint32_t)(row * p.k_row + min(col, WN::KW - 1) * 16);
+                if (pc < nrows * WN::KWP)
+                    stream::dma16(kwin + (int64_t)(t0 - base) * p.k_row, off, rb + LY::RK + i * 1024);
+            } else {
+                const int x = i - WN::NKI;
+                const int pc = x * 64 + lane, row = pc / WN::VWP, col = pc - row * WN::VWP;
+                const uint32_t off = (uint32_t)(row * p.v_row + min(col, WN::VW - 1) * 16);
+                if (pc < nrows * WN::VWP)
+                    stream::dma16(vwin + (int64_t)(t0 - base) * p.v_row, off, rb + LY::RV + x * 1024);
+            }
+        }
+    };
+
+    // ---- conversion of one tile's raw rows into fp16 operands (all waves).
+    // Rows past c1 were not loaded: their steps and offsets are written as 0
+    // (P is 0 there, and 0 times a stale NaN would not be); their codes and K
+    // scales are finite or masked by the softmax.
+    const float sc2 = p.scale * kLog2e;
+    auto convert = [&](int t0, int rbuf, int cbuf) {
+        const uint8_t* const rk = smem + rbuf * LY::RAW + LY::RK;
+        const uint8_t* const rv = smem + rbuf * LY::RAW + LY::RV;
+        uint8_t* const cv = smem + kRawBufs * LY::RAW + cbuf * LY::CONV;
+        const int tid = threadIdx.x;
+        // K codes: task (key, blk, quarter) -> 8 fp16 codes
+        for (int u = tid; u < kTile * NB * 4; u += 64 * kWaves) {
+            const int key = u / (NB * 4), rem = u - key * (NB * 4), blk = rem >> 2, qq = rem & 3;
+            const int ca = key * WN::KSTR + kofs + blk * 34 + 2 + 8 * qq;
+            const uint32_t* const w = reinterpret_cast<const uint32_t*>(rk + (ca & ~3));
+            const uint32_t sh = (uint32_t)(ca & 3) * 8;
+            const uint32_t c0w = __builtin_amdgcn_alignbit(w[1], w[0], sh);
+            const uint32_t c1w = __builtin_amdgcn_alignbit(w[2], w[1], sh);
+            *reinterpret_cast<h8*>(cv + LY::KH + key * LY::ROWH + (blk * 32 + 8 * qq) * 2) = dec::k_codes_f16(c0w, c1w);
+        }
+        // V codes: task (key, blk, part) -> dims 8 part .. of the block
+        for (int u = tid; u < kTile * NB * 4; u += 64 * kWaves) {
+            const int key = u / (NB * 4), rem = u - key * (NB * 4), blk = rem >> 2, part = rem & 3;
+            const uint8_t* const vb = rv + key * WN::VSTR + blk * 24;
+            const uint2 nibw = *reinterpret_cast<const uint2*>(vb + 8 + 8 * (part & 1));
+            const uint32_t qh = *reinterpret_cast<const uint32_t*>(vb + 4);
+            const uint32_t hb = (qh >> (8 * part)) & 0xFFu;    // the fifth bits of dims 8 part .. + 7
+            const uint32_t shn = (part >> 1) * 4;              // high nibbles for dims 16 ..
+            // bit i of a 4-bit x goes to bit 0 of byte i: x * (1 + 2^7 + 2^14 + 2^21)
+            const uint32_t s0 = ((hb & 0xFu) * 0x00204081u) & 0x01010101u;
+            const uint32_t s1 = ((hb >> 4) * 0x00204081u) & 0x01010101u;
+            const uint32_t c0w = ((nibw.x >> shn) & 0x0F0F0F0Fu) | (s0 << 4);
+            const uint32_t c1w = ((nibw.y >> shn) & 0x0F0F0F0Fu) | (s1 << 4);
+            *reinterpret_cast<h8*>(cv + LY::VH + key * LY::ROWH + (blk * 32 + 8 * part) * 2) = stream::v_codes_sub(c0w, c1w);
+        }
+        // scales, steps, offsets: task (key, blk)
+        for (int u = tid; u < kTile * NB; u += 64 * kWaves) {
+            const int key = u / NB, blk = u - key * NB;
+            const bool live = t0 + key < c1;
+            const uint16_t kd = *reinterpret_cast<const uint16_t*>(rk + key * WN::KSTR + kofs + blk * 34);
+            reinterpret_cast<float*>(cv + LY::KS)[blk * kTile + key] = live ? f16_value(kd) * sc2 : 0.0f;
+            const uint32_t dm = live ? *reinterpret_cast<const uint32_t*>(rv + key * WN::VSTR + blk * 24) : 0u;
+            reinterpret_cast<uint16_t*>(cv + LY::VD)[blk * kTile + key] = (uint16_t)(dm & 0xFFFF);
+            reinterpret_cast<uint16_t*>(cv + LY::VM)[key * LY::VMS + blk] = (uint16_t)(dm >> 16);
+        }
+    };
+    // the columns of ones after each offset row, in both converted buffers (never rewritten)
+    for (int cb = 0; cb < 2; ++cb) {
+        uint16_t* const vm = reinterpret_cast<uint16_t*>(smem + kRawBufs * LY::RAW + cb * LY::CONV + LY::VM);
+        constexpr int NO = LY::VMS - NB;
+        for (int u = threadIdx.x; u < kTile * NO; u += 64 * kWaves) vm[(u / NO) * LY::VMS + NB + u % NO] = 0x3C00;
+    }
+
+    // ---- this wave's query rows as fp16 B operands, divided per wave by the
+    // power of two that puts their largest |q| in [2^14, 2^15)
+    constexpr int RTW = 2;
+    h8 qh[RTW][NB], ql[RTW][NB];
+    constexpr int QW = QLO ? 8 : 4;
+    uint32_t qw[RTW][NB][QW];
+    uint32_t mag = 0;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+        const int r = rt * 16 + j16;
+        const bool real = r < R;
+        const int t = real ? tq0 + r / p.hpk : 0, hh = real ? r % p.hpk : 0;
+        const size_t row0q = (((size_t)b * p.T + t) * p.H + g * p.hpk + hh) * HD + 8 * q4;
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+            uint32_t w[QW];
+#pragma unroll
+            for (int e = 0; e < QW; ++e) w[e] = 0u;
+            if (real) {
+                if constexpr (QLO) {
+                    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const float*>(p.q) + row0q + blk * 32);
+                    const uint4 a = src[0], c = src[1];
+                    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+                    if constexpr (QW == 8) { w[4] = c.x; w[5] = c.y; w[6] = c.z; w[7] = c.w; }
+                } else {
+                    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + row0q + blk * 32);
+                    w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < QW; ++e) {
+                if (QLO) mag = max(mag, w[e] & 0x7FFFFFFFu);
+                else mag = max(mag, max((w[e] << 16) & 0x7FFFFFFFu, w[e] & 0x7FFF0000u));
+                qw[rt][blk][e] = w[e];
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) mag = max(mag, (uint32_t)__shfl_xor((int)mag, m));
+    const uint32_t qexp = __builtin_amdgcn_readfirstlane(dec::exp_of(mag));
+    const float qdown = dec::q_down(qexp), qup = dec::q_up(qexp);
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = QLO ? __uint_as_float(qw[rt][blk][e % QW])
+                                    : __uint_as_float((e & 1) ? (qw[rt][blk][e / 2] & 0xFFFF0000u) : (qw[rt][blk][e / 2] << 16));
+                const float x = v * qdown;
+                const _Float16 xh = (_Float16)x;
+                qh[rt][blk][e] = xh;
+                if (QLO) ql[rt][blk][e] = (_Float16)(x - (float)xh);
+            }
+
+    f4 oacc[RTW][2 * NB], macc[RTW];
+    float mrow[RTW], lsum[RTW];
+    int vis_lo[RTW], vis_hi[RTW];
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+        macc[rt] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dt = 0; dt < 2 * NB; ++dt) oacc[rt][dt] = (f4){0.f, 0.f, 0.f, 0.f};
+        mrow[rt] = stream::kNoMax;
+        lsum[rt] = 0.0f;
+        vis_lo[rt] = vis_hi[rt] = 0;
+        const int r = rt * 16 + j16;
+        if (r < R) {
+            vis_hi[rt] = len - p.T + tq0 + r / p.hpk + 1;
+            vis_lo[rt] = p.window > 0 ? max(0, vis_hi[rt] - p.window) : 0;
+        }
+    }
+    // rows every query row of this wave sees (no masks needed inside)
+    const int full_hi = min(len - p.T + tq0 + 1, c1);
+    const int full_lo = max(p.window > 0 ? max(0, len - p.T + tq0 + Tq - p.window) : 0, c0);
+    const int mk0 = stream::pkey(q4, j16 >> 2), mk1 = stream::pkey(q4, 4 + (j16 >> 2));
+    const int mc = (4 * (j16 & 3) < LY::VMS) ? (j16 & 3) : 0;
+    int vsh = 0;
+
+    // ---- the products of one converted tile for this wave's query rows
+    auto compute = [&](int it, int t0) {
+        const uint8_t* const cv = smem + kRawBufs * LY::RAW + (it & 1) * LY::CONV;
+        const float* const KSa = reinterpret_cast<const float*>(cv + LY::KS);
+        const uint16_t* const VDa = reinterpret_cast<const uint16_t*>(cv + LY::VD);
+        // ---- scores S^T (base 2): sv[rt][h][i] = S[row rt*16 + j16][key 16h + 4*q4 + i]
+        float sv[RTW][2][4];
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sv[rt][h][i] = 0.0f;
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+            const float4 ks0 = *reinterpret_cast<const float4*>(KSa + blk * kTile + 4 * q4);
+            const float4 ks1 = *reinterpret_cast<const float4*>(KSa + blk * kTile + 16 + 4 * q4);
+            const float ksv[2][4] = {{ks0.x, ks0.y, ks0.z, ks0.w}, {ks1.x, ks1.y, ks1.z, ks1.w}};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const h8 kf = *reinterpret_cast<const h8*>(cv + LY::KH + (16 * h + j16) * LY::ROWH + (blk * 32 + 8 * q4) * 2);
+#pragma unroll
+                for (int rt = 0; rt < RTW; ++rt) {
+                    f4 d = dec::mfma(kf, qh[rt][blk], (f4){0.f, 0.f, 0.f, 0.f});
+                    if (QLO) d = dec::mfma(kf, ql[rt][blk], d);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sv[rt][h][i] = fmaf(ksv[h][i], d[i], sv[rt][h][i]);
+                }
+            }
+        }
+        // ---- online softmax against a reference max that moves only when a
+        // score passes it by more than 8 (so p <= 256, inside fp16)
+        const bool interior = t0 >= full_lo && t0 + kTile <= full_hi;
+        h8 pu[RTW];
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) {
+            float smax = -INFINITY;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float x = sv[rt][h][i];
+                    if (!interior) {
+                        const int j = t0 + 16 * h + 4 * q4 + i;
+                        x = (j >= vis_lo[rt] && j < vis_hi[rt]) ? x : -INFINITY;
+                    }
+                    sv[rt][h][i] = x;
+                    smax = fmaxf(smax, x);
+                }
+            smax *= qup;
+            if (__any(smax > mrow[rt] + 8.0f)) {
+                float mt = fmaxf(smax, __shfl_xor(smax, 16));
+                mt = fmaxf(mt, __shfl_xor(mt, 32));
+                const bool move = mt > mrow[rt] + 8.0f;
+                const float alpha = move ? __builtin_amdgcn_exp2f(mrow[rt] - mt) : 1.0f;
+                mrow[rt] = move ? mt : mrow[rt];
+                float ar[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * q4 + i);
+#pragma unroll
+                for (int dt = 0; dt < 2 * NB; ++dt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) oacc[rt][dt][i] *= ar[i];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) macc[rt][i] *= ar[i];
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    pu[rt][4 * h + i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(sv[rt][h][i], qup, -mrow[rt]));
+        }
+        // ---- the tile's largest step decides the accumulators' units
+        uint32_t dmx = 0;
+#pragma unroll
+        for (int x = 0; x < (kTile * NB + 63) / 64; ++x) {
+            const int u = x * 64 + lane;
+            if (kTile * NB % 64 == 0 || u < kTile * NB) dmx = max(dmx, (uint32_t)VDa[u]);
+        }
+        const bool big = __any(dmx >= 0x5800u);   // fp16 128.0
+        if (big || vsh != 0) {
+            const int want = big ? __builtin_amdgcn_readfirstlane(dec::v_shift(dec::wave_max_dpp(f16_value((uint16_t)dmx)))) : 0;
+            if (want != vsh) {
+                const float f = dec::pow2(vsh - want);
+#pragma unroll
+                for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                    for (int dt = 0; dt < 2 * NB; ++dt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) oacc[rt][dt][i] *= f;
+                vsh = want;
+            }
+        }
+        const _Float16 vdown = (_Float16)dec::pow2(-vsh);
+        // ---- P V: P' = fp16(P) * step (steps times 2^-vsh), V codes from the converted tile
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+            h8 dh = stream::steps_of(VDa + blk * kTile, q4);
+            if (vsh != 0) dh = dh * (h8){vdown, vdown, vdown, vdown, vdown, vdown, vdown, vdown};
+#pragma unroll
+            for (int dd = 0; dd < 2; ++dd) {
+                const int col = blk * 32 + 16 * dd + 4 * (j16 & 3);
+                const h8 vf = dec::tr16_pair(cv + LY::VH + mk0 * LY::ROWH + col * 2, cv + LY::VH + mk1 * LY::ROWH + col * 2);
+#pragma unroll
+                for (int rt = 0; rt < RTW; ++rt) {
+                    const h8 pa = pu[rt] * dh;
+                    oacc[rt][2 * blk + dd] = dec::mfma(pa, vf, oacc[rt][2 * blk + dd]);
+                }
+            }
+        }
+        // q5_1 offset term and the row sums (the ones column)
+        {
+            const h8 mb = dec::tr16_pair(cv + LY::VM + (mk0 * LY::VMS + 4 * mc) * 2, cv + LY::VM + (mk1 * LY::VMS + 4 * mc) * 2);
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt) macc[rt] = dec::mfma(pu[rt], mb, macc[rt]);
+        }
+    };
+
+    // ---- prologue: tiles 0, 1 and 2 requested, tile 0 converted
+    for (int x = 0; x < kRawBufs; ++x)
+        if (x < ntiles) issue(t_begin + x * kTile, x);
+    if (ntiles > 0) {
+        const int a = my_loads(t_begin + kTile), c = my_loads(t_begin + 2 * kTile);
+        wait_vmcnt(a < 0 || c < 0 ? 0 : a + c);
+        stream::lds_barrier();                       // every wave's pieces of tile 0 have landed
+        convert(t_begin, 0, 0);
+    }
+
+    int rnext = 1;                                   // raw buffer of tile it + 1
+    for (int it = 0; it < ntiles; ++it) {
+        const int t0 = t_begin + it * kTile;
+        // tile it + 1 has landed (tile it + 2 may still be in flight); after
+        // the barrier tile it is converted by all waves, tile it - 1's
+        // operands are no longer read, and tile it's raw buffer is free
+        if (it + 1 < ntiles) wait_vmcnt(my_loads(t0 + 2 * kTile));
+        stream::lds_barrier();
+        const int rfree = rnext == 0 ? kRawBufs - 1 : rnext - 1;
+        if (it + 3 < ntiles) issue(t0 + 3 * kTile, rfree);
+        // The conversion of tile it + 1 and the products of tile it, in
+        // opposite orders on the two waves that share a SIMD (waves w and
+        // w + 4), so that one converts (vector ALU, LDS) while the other
+        // multiplies (matrix cores).
+        const bool convert_first = wave < kWaves / 2;
+        if (convert_first && it + 1 < ntiles) convert(t0 + kTile, rnext, (it + 1) & 1);
+        if (active) compute(it, t0);
+        if (!convert_first && it + 1 < ntiles) convert(t0 + kTile, rnext, (it + 1) & 1);
+        rnext = rnext == kRawBufs - 1 ? 0 : rnext + 1;
+    }
+
+    if (!active) return;
+    // ---- finish: row sums from the ones column; offsets into O (the q5_1
+    // code products carry 2^-24, P * step carries 2^-vsh)
+    const float ounit = dec::pow2(24 + vsh);
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+        const int src = 16 * (j16 >> 2) + NB;
+        const float l0 = __shfl(macc[rt][0], src), l1 = __shfl(macc[rt][1], src);
+        const float l2 = __shfl(macc[rt][2], src), l3 = __shfl(macc[rt][3], src);
+        lsum[rt] = (j16 & 2) ? ((j16 & 1) ? l3 : l2) : ((j16 & 1) ? l1 : l0);
+#pragma unroll
+        for (int dt = 0; dt < 2 * NB; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) oacc[rt][dt][i] = fmaf(oacc[rt][dt][i], ounit, __shfl(macc[rt][i], 16 * q4 + dt / 2));
+    }
+    const size_t row0 = ((size_t)b * p.splits + s) * p.T;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+        const int r = rt * 16 + j16;
+        if (q4 == 0 && r < R) {
+            const int t = tq0 + r / p.hpk, hq = g * p.hpk + r % p.hpk;
+            const size_t idx = (row0 + t) * p.H + hq;
+            p.part_ml[2 * idx] = (mrow[rt] == stream::kNoMax) ? -INFINITY : mrow[rt] * kLn2;
+            p.part_ml[2 * idx + 1] = lsum[rt];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ro = rt * 16 + 4 * q4 + i;
+            if (ro < R) {
+                const int t = tq0 + ro / p.hpk, hq = g * p.hpk + ro % p.hpk;
+                float* o = p.part_o + ((row0 + t) * p.H + hq) * HD + j16;
+#pragma unroll
+                for (int dt = 0; dt < 2 * NB; ++dt) o[16 * dt] = oacc[rt][dt][i];
+            }
+        }
+    }
+}
+
+}  // namespace prime

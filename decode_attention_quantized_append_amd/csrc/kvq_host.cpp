@@ -220,6 +220,17 @@ int64_t span_of(const kvq_cache* h, int b, int32_t T) {
     return std::max<int64_t>(0, h->len[b] - (visible_lo(h, h->len[b], T) & ~int64_t(31)));
 }
 
+// Groups of query rows from which the planner takes the prime kernel.
+constexpr int64_t kPrimeMinGroups = 4;
+
+// Is the prime kernel built for this shape: q8_0 / q5_1 rows, head_dim 64 or
+// 128, and more than one group of query rows.
+bool prime_ok(const kvq_config& c, int R, int32_t T) {
+    const int NB = c.head_dim / 32;
+    const int hpk = c.n_q_heads / c.n_kv_heads;
+    return !is_f8(c) && (NB == 2 || NB == 4) && T > R / hpk;
+}
+
 // Chooses the decode kernel and its tiling.  Returns false when a kernel or
 // tiling set with kvq_set_decode_tiling does not fit the shape.
 bool choose_kernel(const kvq_cache* h, int R, int32_t T, bool f32_queries, Plan* p) {
@@ -232,6 +243,23 @@ bool choose_kernel(const kvq_cache* h, int R, int32_t T, bool f32_queries, Plan*
     int want = h->decode_kernel;
     if (want == KVQ_DECODE_AUTO) want = (NB == 2 || NB == 4 || NB == 8) ? KVQ_DECODE_STREAM : KVQ_DECODE_PER_HEAD;
     if (want == KVQ_DECODE_PER_HEAD) return !is_f8(c);   // the per-head kernel reads q8_0 / q5_1 only
+    // Many query rows per KV head (a prompt chunk): the prime kernel, whose
+    // eight waves share each converted KV tile, from kPrimeMinGroups groups
+    // of query rows on (fewer leave most of its waves idle)
+    const int hpk = c.n_q_heads / c.n_kv_heads;
+    const bool prime = want == KVQ_DECODE_PRIME ||
+                       (h->decode_kernel == KVQ_DECODE_AUTO && prime_ok(c, R, T) &&
+                        ceil_div(T, R / hpk) >= kPrimeMinGroups);
+    if (prime) {
+        if (!prime_ok(c, R, T)) return false;
+        if (!aligned_start_resident(h, T)) return h->decode_kernel == KVQ_DECODE_AUTO;
+        p->kernel = kvq::kPrime;
+        p->gh = 1;
+        p->rs = p->rg = p->ds = 1;
+        p->lds = kvq::prime_lds_bytes(NB);
+        p->rows = kvq::kRowTile;
+        return true;
+    }
     // The stream kernel starts a session's first tile at the first visible
     // row rounded down to 32 and reads it whole, so that row must still be
     // resident (at or above base); else one KV head per workgroup, whose
@@ -296,7 +324,22 @@ Plan make_plan(const kvq_cache* h, int32_t T, bool f32_queries, bool* fits = nul
     const bool ok = choose_kernel(h, R, T, f32_queries, &p);
     if (fits) *fits = ok;
     int64_t chunk = h->split_rows;
-    if (p.kernel != kvq::kPerHead) {
+    if (p.kernel == kvq::kPrime) {
+        // one workgroup per CU (eight waves of up to 256 registers): about
+        // as many workgroups as CUs, each a whole number of tiles
+        const int64_t yblocks = ceil_div(groups, kvq::kPrimeGroups);
+        const int64_t slots = std::max<int64_t>(1, h->cus);
+        if (chunk <= 0) {
+            chunk = round_up(std::max<int64_t>(1, ceil_div(total * c.n_kv_heads * yblocks, slots)), p.rows);
+            for (;;) {
+                int64_t wgs = 0;
+                for (int b = 0; b < c.n_seqs; ++b) wgs += ceil_div(span_of(h, b, T), chunk) * c.n_kv_heads * yblocks;
+                if (wgs <= slots) break;
+                chunk += p.rows;
+            }
+        }
+        chunk = round_up(chunk, p.rows);
+    } else if (p.kernel != kvq::kPerHead) {
         const int64_t ngrp = c.n_kv_heads / p.gh;
         const int RT = (R + 15) / 16;
         // one round of workgroups: as many as fit on the device's CUs at once
@@ -789,7 +832,8 @@ kvq_status kvq_set_split_rows(kvq_cache* h, int32_t rows) {
 
 kvq_status kvq_set_decode_tiling(kvq_cache* h, int32_t kernel, int32_t head_group, int32_t sub_tiles) {
     if (!h) return fail(KVQ_EINVAL, "handle is NULL");
-    if (kernel != KVQ_DECODE_AUTO && kernel != KVQ_DECODE_PER_HEAD && kernel != KVQ_DECODE_STREAM)
+    if (kernel != KVQ_DECODE_AUTO && kernel != KVQ_DECODE_PER_HEAD && kernel != KVQ_DECODE_STREAM &&
+        kernel != KVQ_DECODE_PRIME)
         return fail(KVQ_EINVAL, "unknown decode kernel");
     if (head_group < 0 || (head_group > 0 && h->cfg.n_kv_heads % head_group != 0))
         return fail(KVQ_EINVAL, "head_group must be 0 or a divisor of n_kv_heads");

@@ -165,6 +165,35 @@ struct StreamWinF8 {
     static_assert(NKI <= 32 && NVI <= 32, "load counts must fit vmcnt");
 };
 
+// The prime decode kernel (many query rows per KV head): a workgroup of
+// kPrimeGroups waves, one 32-row query group each, shares each KV tile.  Its
+// LDS for head_dim = 32 * NB: kPrimeRawBufs raw tile buffers (the stream
+// kernel's row windows, K rows then V rows) and two converted ones (fp16 K codes, fp16 V
+// codes times 2^-24, K scales, V steps, V offset rows with ones).
+constexpr int kPrimeGroups = 8;
+constexpr int kPrimeRawBufs = 3;    // raw tile buffers: two tiles in flight while one is converted
+template <int NB>
+struct PrimeLayout {
+    using WN = StreamWin<NB>;
+    static constexpr int HD = NB * 32;
+    static constexpr int RAW = kRowTile * (WN::KSTR + WN::VSTR);
+    static constexpr int RK = 0, RV = kRowTile * WN::KSTR;
+    static constexpr int ROWH = HD * 2 + 16;                    // fp16 row of a head, padded
+    static constexpr int VMS = WN::VMS;                         // offsets, then ones
+    static constexpr int KH = 0;                                // fp16 [32][HD] K codes
+    static constexpr int VH = KH + kRowTile * ROWH;             // fp16 [32][HD] V codes * 2^-24
+    static constexpr int KS = VH + kRowTile * ROWH;             // f32 [NB][32] K scales * scale * log2 e
+    static constexpr int VD = KS + NB * kRowTile * 4;           // fp16 [NB][32] V steps
+    static constexpr int VM = VD + NB * kRowTile * 2;           // fp16 [32][VMS] V offsets, then ones
+    static constexpr int CONV = VM + kRowTile * VMS * 2;        // one converted buffer
+    static constexpr int BYTES = kPrimeRawBufs * RAW + 2 * CONV;
+    static constexpr int NIT = WN::NKI + WN::NVI;               // load instructions per tile
+    static_assert(RAW % 16 == 0 && CONV % 16 == 0 && ROWH % 16 == 0, "16-byte alignment");
+};
+inline int prime_lds_bytes(int NB) {
+    return NB == 2 ? PrimeLayout<2>::BYTES : NB == 4 ? PrimeLayout<4>::BYTES : 0;
+}
+
 inline int stream_wave_bytes(int NB, bool f8 = false) {
     switch (NB) {
         case 2: return f8 ? StreamWinF8<2>::BYTES : StreamWin<2>::BYTES;
@@ -192,7 +221,7 @@ constexpr int stream_waves_per_simd(int NB, int RTW, bool QLO) {
 // head: 3 for 128-dim heads (64-dim halves), 2 for 256-dim heads.
 constexpr int stream_ds_waves_per_simd(int NB_half) { return NB_half <= 2 ? 3 : 2; }
 
-enum DecodeKernel : int32_t { kPerHead = 0, kStream = 2 };
+enum DecodeKernel : int32_t { kPerHead = 0, kStream = 2, kPrime = 3 };
 
 // Split-K decode plus the log-sum-exp combine.
 struct DecodeParams {

@@ -301,6 +301,7 @@ __global__ __launch_bounds__(1024) void append_kernel(AppendParams p) {
 // ---------------------------------------------------------------------------
 #include "kvq_decode.hip"
 #include "kvq_decode_stream.hip"
+#include "kvq_decode_prime.hip"
 
 // One workgroup per (session, row t, Q head h): fold the session's split
 // partials (m in natural-log units, l, o), adding the sink once as a
@@ -692,6 +693,26 @@ int launch_stream_t(const DecodeParams& p, hipStream_t st, const char** err) {
     return check(err);
 }
 
+template <int NB, bool QLO>
+int launch_prime_t(const DecodeParams& p, hipStream_t st, const char** err) {
+    constexpr int lds = PrimeLayout<NB>::BYTES;
+    static bool configured = false;
+    if (!configured) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&prime::decode_prime<NB, QLO>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess) {
+            *err = "cannot raise the LDS limit of the decode kernel";
+            return 1;
+        }
+        configured = true;
+    }
+    const int items = std::max(1, p.units) * p.Hkv;
+    const int grid = (items + 7) & ~7;
+    const int groups = (p.T + p.Tg - 1) / p.Tg;
+    hipLaunchKernelGGL((prime::decode_prime<NB, QLO>), dim3(grid, (groups + kPrimeGroups - 1) / kPrimeGroups),
+                       dim3(64 * kPrimeGroups), lds, st, p);
+    return check(err);
+}
+
 template <int NB, bool F8>
 int launch_stream_fmt(const DecodeParams& p, hipStream_t st, const char** err) {
     const int R = p.Tg * p.hpk;   // query rows per KV head of one group
@@ -812,6 +833,18 @@ int launch_append(const AppendParams& p, void* stream, const char** err) {
 
 namespace {
 int launch_partials(const DecodeParams& p, hipStream_t st, const char** err) {
+    if (p.kernel == kPrime) {
+        if (p.f8) {
+            *err = "the prime decode reads q8_0 / q5_1 blocks only";
+            return 1;
+        }
+        const bool qlo = p.dtype == 0;
+        switch (p.hd / 32) {
+            case 2: return qlo ? launch_prime_t<2, true>(p, st, err) : launch_prime_t<2, false>(p, st, err);
+            case 4: return qlo ? launch_prime_t<4, true>(p, st, err) : launch_prime_t<4, false>(p, st, err);
+            default: *err = "the prime decode supports head_dim 64 and 128"; return 1;
+        }
+    }
     if (p.kernel == kStream) {
         switch (p.hd / 32) {
             case 2: return launch_stream_nb<2>(p, st, err);

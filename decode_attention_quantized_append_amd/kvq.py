@@ -23,7 +23,7 @@ KVQ_F32, KVQ_BF16 = 0, 1
 KVQ_FMT_Q8_0, KVQ_FMT_Q5_1, KVQ_FMT_E4M3 = 1, 2, 3
 # cache formats by name: (k_fmt, v_fmt)
 FORMATS = {"q8_0/q5_1": (KVQ_FMT_Q8_0, KVQ_FMT_Q5_1), "e4m3": (KVQ_FMT_E4M3, KVQ_FMT_E4M3)}
-KVQ_DECODE_AUTO, KVQ_DECODE_PER_HEAD, KVQ_DECODE_STREAM = 0, 1, 3
+KVQ_DECODE_AUTO, KVQ_DECODE_PER_HEAD, KVQ_DECODE_STREAM, KVQ_DECODE_PRIME = 0, 1, 3, 4
 STATUS_NAMES = {0: "KVQ_OK", 1: "KVQ_EINVAL", 2: "KVQ_ECAPACITY", 3: "KVQ_ERANGE",
                 4: "KVQ_EUNSUPPORTED", 5: "KVQ_EDEVICE"}
 

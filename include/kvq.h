@@ -311,7 +311,10 @@ kvq_status kvq_set_split_rows(kvq_cache* h, int32_t rows);
 typedef enum kvq_decode_kernel {
     KVQ_DECODE_AUTO = 0,        /* chosen per call */
     KVQ_DECODE_PER_HEAD = 1,    /* one KV head per workgroup, any head_dim */
-    KVQ_DECODE_STREAM = 3       /* one or two waves per KV head, each streaming its rows through LDS */
+    KVQ_DECODE_STREAM = 3,      /* one or two waves per KV head, each streaming its rows through LDS */
+    KVQ_DECODE_PRIME = 4        /* many query rows per KV head (a prompt chunk): eight groups of query
+                                 * rows share each KV tile, converted once; q8_0 / q5_1, head_dim 64
+                                 * or 128, more than one group of query rows */
 } kvq_decode_kernel;
 
 /* Tuning: which kernel kvq_decode runs and how it tiles the cache (the

@@ -101,6 +101,9 @@ SMALL = {
     "hd96_window": (3, 6, 2, 96, 2, [300, 40, 2], 50, 320, 0, False, "bf16", False),
     "qwen_f32_small": (2, 32, 8, 128, 2, [900, 161], 0, 1000, 0, True, "f32", True),
     "verify_f32_small": (2, 16, 4, 256, 8, [500, 75], 0, 600, 0, True, "f32", False),
+    # prompt chunks (eight and five groups of query rows: the prime kernel)
+    "prime_small": (1, 32, 8, 128, 64, [700], 256, 1000, 0, True, "bf16", True),
+    "prime_ring_small": (2, 8, 2, 64, 40, [600, 300], 200, 400, 32, False, "f32", False),
 }
 
 
@@ -150,7 +153,7 @@ def test_decode_split_invariance():
 # Decode kernels and tilings (kernel, KV heads per workgroup, waves per KV
 # head) that fit each shape; the automatic choice is covered by
 # test_decode_parity.
-PH, ST = kvq.KVQ_DECODE_PER_HEAD, kvq.KVQ_DECODE_STREAM
+PH, ST, PR = kvq.KVQ_DECODE_PER_HEAD, kvq.KVQ_DECODE_STREAM, kvq.KVQ_DECODE_PRIME
 TILINGS = {
     "qwen_gqa_small": [(ST, 8, 0), (ST, 2, 0), (ST, 1, 0), (ST, 8, 1), (ST, 8, 2), (ST, 2, 2)],
     "batched_small": [(ST, 8, 0), (ST, 4, 0), (ST, 8, 2), (ST, 4, 2)],
@@ -160,6 +163,8 @@ TILINGS = {
     "qwen_f32_small": [(ST, 8, 0), (ST, 4, 0), (ST, 8, 1)],
     "tiny": [(ST, 1, 0)],
     "verify_f32_small": [(ST, 4, 1), (ST, 2, 1), (ST, 4, 2), (ST, 2, 2), (ST, 4, 3), (ST, 2, 3)],
+    "prime_small": [(PR, 0, 0), (ST, 0, 0), (ST, 4, 0), (ST, 0, 3)],
+    "prime_ring_small": [(PR, 0, 0), (ST, 0, 0), (ST, 2, 2)],
 }
 
 
@@ -231,6 +236,14 @@ MANY = {
     "hd64_T70_window": (2, 16, 4, 64, 70, [330, 71], 45, True, "bf16", None),
     "hd96_T33_window_f32": (2, 6, 2, 96, 33, [260, 40], 50, False, "f32", None),
     "hd128_T24_perhead_f32": (2, 32, 8, 128, 24, [300, 129], 0, True, "f32", (kvq.KVQ_DECODE_PER_HEAD, 0)),
+    # the prime kernel: eight groups of query rows per workgroup sharing each
+    # KV tile; partial groups (hpk 5: 30 of 32 rows), partial blocks of
+    # groups, a session holding exactly the T rows, windows, fp32 queries
+    "hd128_T200_prime_window_sinks": (2, 32, 8, 128, 200, [900, 260], 300, True, "bf16", (kvq.KVQ_DECODE_PRIME, 0)),
+    "hd64_hpk5_T77_prime_f32": (2, 10, 2, 64, 77, [500, 90], 0, False, "f32", (kvq.KVQ_DECODE_PRIME, 0)),
+    "hd128_hpk1_T70_prime_window_f32": (1, 4, 4, 128, 70, [333], 40, True, "f32", (kvq.KVQ_DECODE_PRIME, 0)),
+    "hd64_hpk8_T45_prime": (3, 16, 2, 64, 45, [45, 300, 1000], 0, True, "bf16", (kvq.KVQ_DECODE_PRIME, 0)),
+    "hd128_T600_prime_window": (1, 8, 2, 128, 600, [2000], 512, False, "bf16", (kvq.KVQ_DECODE_PRIME, 0)),
 }
 
 

@@ -37,6 +37,8 @@ SHAPES = {
     "hd96_perhead": (2, 6, 2, 96, 2, [300, 41], 50, "f32", None),
     "hd128_perhead_T8": (1, 32, 8, 128, 8, [333], 0, "bf16", (kvq.KVQ_DECODE_PER_HEAD, 0, 0)),
     "hd256_perhead_T8": (1, 16, 4, 256, 8, [260], 0, "bf16", (kvq.KVQ_DECODE_PER_HEAD, 0, 0)),
+    "hd128_prime_T40": (2, 32, 8, 128, 40, [500, 90], 0, "bf16", (kvq.KVQ_DECODE_PRIME, 0, 0)),
+    "hd64_prime_T70_window": (1, 16, 4, 64, 70, [400], 100, "bf16", None),
 }
 
 

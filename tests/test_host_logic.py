@@ -444,7 +444,7 @@ def test_decode_kernel_choice(lib):
     assert err(lib, kvq.kvq_set_decode_tiling, h, kvq.KVQ_DECODE_STREAM, 2, 4) == E      # 1 .. 3 waves per head
     assert err(lib, kvq.kvq_set_decode_tiling, h, kvq.KVQ_DECODE_PER_HEAD, 2, 0) == E    # no head groups there
     assert err(lib, kvq.kvq_set_decode_tiling, h, 2, 0, 0) == E                          # no kernel 2
-    assert err(lib, kvq.kvq_set_decode_tiling, h, 4, 0, 0) == E
+    assert err(lib, kvq.kvq_set_decode_tiling, h, 5, 0, 0) == E
     # two row streams of fp32 queries are not built: that call fails, enqueueing nothing
     kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_STREAM, 8, 2, lib)
     lib.kvq_nodev_clear()
@@ -510,6 +510,46 @@ def test_decode_row_streams(lib):
     assert plan_of(lib, h, T=8)["rg"] == 1
     kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_STREAM, 2, 2, lib)
     assert (plan_of(lib, h, T=8)["rg"], plan_of(lib, h, T=1)["rg"]) == (2, 1)
+
+
+def test_decode_prime_choice(lib):
+    """Prompt chunks (four or more groups of 32 / hpk query rows per KV head):
+    the prime kernel, one workgroup of eight row groups per (session, chunk,
+    KV head) and block of eight groups, about one workgroup per CU; q8_0 /
+    q5_1 at head_dim 64 and 128 only."""
+    STREAM, PRIME = 2, 3
+    lib.kvq_nodev_set_cus(256)
+    h = create(lib, n_seqs=1, n_q_heads=32, n_kv_heads=8, head_dim=128, capacity=9000)
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 8192, None, 0, lib)
+    p = plan_of(lib, h, T=512)
+    assert (p["kernel"], p["gh"], p["Tg"], p["groups"], p["lds"]) == (PRIME, 1, 8, 64, 61952)
+    assert p["chunk"] % 32 == 0 and p["units"] == p["splits"] == -(-8192 // p["chunk"])
+    assert p["units"] * 8 * 8 <= 256 < -(-8192 // (p["chunk"] - 32)) * 8 * 8   # one round, no smaller chunk
+    assert plan_of(lib, h, T=25)["kernel"] == PRIME          # 4 groups
+    assert plan_of(lib, h, T=24)["kernel"] == STREAM         # 3 groups
+    assert plan_of(lib, h, T=24, dtype=kvq.KVQ_F32)["kernel"] == STREAM
+    # set explicitly: any shape with two or more groups
+    kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_PRIME, 0, 0, lib)
+    assert plan_of(lib, h, T=9)["kernel"] == PRIME
+    lib.kvq_nodev_clear()
+    E = kvq.KVQ_EINVAL
+    assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 8, None, 0.1, O, None, WS, 1 << 40) == E   # one group
+    assert log(lib) == []
+    assert err(lib, kvq.kvq_set_decode_tiling, h, kvq.KVQ_DECODE_PRIME, 2, 0) == E
+    assert err(lib, kvq.kvq_set_decode_tiling, h, kvq.KVQ_DECODE_PRIME, 0, 1) == E
+    # head_dim 64: a smaller layout; 256 and FP8 rows: the stream kernel
+    h = create(lib, n_seqs=2, n_q_heads=16, n_kv_heads=4, head_dim=64, capacity=3000)
+    kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 2000, None, 0, lib)
+    p = plan_of(lib, h, T=100, dtype=kvq.KVQ_F32)
+    assert (p["kernel"], p["lds"], p["groups"]) == (PRIME, 32000, 13)
+    for kw in (dict(head_dim=256, n_q_heads=16, n_kv_heads=4), dict(head_dim=128, fmt="e4m3")):
+        h = create(lib, n_seqs=1, capacity=3000, **kw)
+        kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 2000, None, 0, lib)
+        assert plan_of(lib, h, T=200)["kernel"] == STREAM
+        kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_PRIME, 0, 0, lib)
+        lib.kvq_nodev_clear()
+        assert err(lib, kvq.kvq_decode, h, Q, kvq.KVQ_BF16, 200, None, 0.1, O, None, WS, 1 << 40) == E
+        assert log(lib) == []
 
 
 def test_decode_ring_start_below_base_falls_back(lib):
@@ -578,7 +618,8 @@ def test_ring_rows_serves_prime_chunks_from_the_ring(lib):
             kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, n, None, 0, lib)
             L, base = lengths(lib, h, 1)
             assert ((max(0, L[0] - n + 1 - W)) & ~31) >= base[0]
-            assert plan_of(lib, h, T=n)["kernel"] == 2
+            # the stream kernel, or from four groups of 8 rows on the prime kernel
+            assert plan_of(lib, h, T=n)["kernel"] == (3 if n > 24 else 2)
         kvq.kvq_destroy(h, lib)
     from decode_attention_quantized_append_amd import workloads
     w = workloads.get("prime")
