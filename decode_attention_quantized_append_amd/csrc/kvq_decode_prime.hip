@@ -14,18 +14,30 @@
 //   * per 32-row tile, the eight waves copy the tile's q8_0 / q5_1 blocks of
 //     the head into LDS together (global_load_lds_dwordx4, one instruction or
 //     two per wave) and then convert them together, once, into fp16 operands
-//     in LDS: the K codes (exact), the V codes as fp16 subnormals code x 2^-24
-//     (exact), the K scales (times scale * log2 e), the V steps (fp16) and the
-//     V offset rows (with a column of ones for the row sums).  Each wave then
-//     reads its matrix-core operands from there: ds_read_b128 for the K
-//     blocks (A of S^T = K Q^T), pairs of ds_read_b64_tr_b16 for the V codes
-//     (B of P V, 8 keys of one dim per lane).
-//   * raw rows and converted operands are both double-buffered: while the
-//     waves score tile t, tile t + 1's rows have landed and tile t + 2's are
-//     in flight; one workgroup barrier per tile separates the conversion of
-//     the next tile from the reads of the current one.
-//   * the softmax, the fp16 P, the packed P * step products, the offset and
-//     row-sum product and the range handling are those of the stream kernel.
+//     in LDS.  K: each element d * c (step times code) as an exact pair of
+//     fp16 values hi + lo (c has 8 significant bits and d 11, so hi holds the
+//     product rounded to 11 bits and lo the rest exactly), which lets the
+//     matrix cores sum the four blocks of a head in one accumulator with no
+//     per-block scaling.  V: the codes as fp16 subnormals c * 2^-24 (exact),
+//     the steps and the offsets; as in the stream kernel each wave multiplies
+//     its fp16 P by the steps (P' = P * d, the A operand of P V) and takes
+//     the offset term sum_key P * m, with the row sums from a column of ones,
+//     as one more product.  Each wave reads its matrix-core operands from
+//     there: ds_read_b128 for the K blocks (A of S^T = K Q^T), pairs of
+//     ds_read_b64_tr_b16 for the V codes (B of P V, 8 keys of one dim per
+//     lane).
+//   * three raw tile buffers and two converted ones: while the waves score
+//     tile t they convert tile t + 1, whose rows have landed, and tiles t + 2
+//     and t + 3 are in flight; one workgroup barrier per tile.  The two waves
+//     that share a SIMD take the conversion and the products in opposite
+//     orders, so that one works the vector ALU while the other works the
+//     matrix cores.
+//   * ranges: a tile with a K step of 2^8 or more stores its K products
+//     times 2^-E (and its scores are multiplied back by 2^E), a tile with a
+//     V step of 2^7 or more its steps times 2^-E (and the P V accumulators
+//     switch units), so that no fp16 product overflows; the query rows are
+//     scaled by a power of two as in the stream kernel, and P (at most 2^8,
+//     the lazily moved reference max) enters as fp16.
 namespace prime {
 
 using dec::f4;
@@ -128,26 +140,53 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_prime(DecodeParams p) {
     };
 
     // ---- conversion of one tile's raw rows into fp16 operands (all waves).
-    // Rows past c1 were not loaded: their steps and offsets are written as 0
-    // (P is 0 there, and 0 times a stale NaN would not be); their codes and K
-    // scales are finite or masked by the softmax.
-    const float sc2 = p.scale * kLog2e;
+    // First every wave finds the tile's range shifts itself (the same values
+    // in every wave): E_k for K steps of 2^8 or more, E_v for V steps of 2^7
+    // or more (fp16 bits 0x5C00, 0x5800).  Rows past c1 were not loaded:
+    // their steps and offsets are taken as 0, so that their products are 0
+    // whatever stale bytes their codes hold.
+    uint32_t ksh_next = 0, vsh_next = 0;     // the shifts of the tile last converted
     auto convert = [&](int t0, int rbuf, int cbuf) {
         const uint8_t* const rk = smem + rbuf * LY::RAW + LY::RK;
         const uint8_t* const rv = smem + rbuf * LY::RAW + LY::RV;
         uint8_t* const cv = smem + kRawBufs * LY::RAW + cbuf * LY::CONV;
         const int tid = threadIdx.x;
-        // K codes: task (key, blk, quarter) -> 8 fp16 codes
+        auto kstep = [&](int key, int blk) -> uint32_t {
+            return t0 + key < c1 ? *reinterpret_cast<const uint16_t*>(rk + key * WN::KSTR + kofs + blk * 34) & 0x7FFFu : 0u;
+        };
+        auto vstepm = [&](int key, int blk) -> uint32_t {
+            return t0 + key < c1 ? *reinterpret_cast<const uint32_t*>(rv + key * WN::VSTR + blk * 24) : 0u;
+        };
+        {
+            uint32_t km = 0, vm = 0;
+#pragma unroll
+            for (int x = 0; x < (kTile * NB + 63) / 64; ++x) {
+                const int u = x * 64 + lane;
+                if (kTile * NB % 64 == 0 || u < kTile * NB) {
+                    km = max(km, kstep(u / NB, u % NB));
+                    vm = max(vm, vstepm(u / NB, u % NB) & 0x7FFFu);
+                }
+            }
+            ksh_next = __any(km >= 0x5C00u) ? (dec::wave_max_u32(km) >> 10) - 22u : 0u;
+            vsh_next = __any(vm >= 0x5800u) ? (dec::wave_max_u32(vm) >> 10) - 21u : 0u;
+        }
+        const _Float16 kdown = (_Float16)dec::pow2(-(int)ksh_next);
+        // K: task (key, blk, quarter) -> 8 products d * c as hi + lo
         for (int u = tid; u < kTile * NB * 4; u += 64 * kWaves) {
             const int key = u / (NB * 4), rem = u - key * (NB * 4), blk = rem >> 2, qq = rem & 3;
             const int ca = key * WN::KSTR + kofs + blk * 34 + 2 + 8 * qq;
             const uint32_t* const w = reinterpret_cast<const uint32_t*>(rk + (ca & ~3));
             const uint32_t sh = (uint32_t)(ca & 3) * 8;
-            const uint32_t c0w = __builtin_amdgcn_alignbit(w[1], w[0], sh);
-            const uint32_t c1w = __builtin_amdgcn_alignbit(w[2], w[1], sh);
-            *reinterpret_cast<h8*>(cv + LY::KH + key * LY::ROWH + (blk * 32 + 8 * qq) * 2) = dec::k_codes_f16(c0w, c1w);
+            const h8 c = dec::k_codes_f16(__builtin_amdgcn_alignbit(w[1], w[0], sh), __builtin_amdgcn_alignbit(w[2], w[1], sh));
+            const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)kstep(key, blk)) * kdown;
+            const h8 dv = {d, d, d, d, d, d, d, d};
+            const h8 hi = c * dv;
+            const h8 lo = __builtin_elementwise_fma(c, dv, -hi);   // exact: c * d - hi fits in fp16
+            const int o = key * LY::ROWH + (blk * 32 + 8 * qq) * 2;
+            *reinterpret_cast<h8*>(cv + LY::KH + o) = hi;
+            *reinterpret_cast<h8*>(cv + LY::KL + o) = lo;
         }
-        // V codes: task (key, blk, part) -> dims 8 part .. of the block
+        // V: task (key, blk, part) -> dims 8 part .. 8 part + 7 of the block
         for (int u = tid; u < kTile * NB * 4; u += 64 * kWaves) {
             const int key = u / (NB * 4), rem = u - key * (NB * 4), blk = rem >> 2, part = rem & 3;
             const uint8_t* const vb = rv + key * WN::VSTR + blk * 24;
@@ -162,14 +201,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_prime(DecodeParams p) {
             const uint32_t c1w = ((nibw.y >> shn) & 0x0F0F0F0Fu) | (s1 << 4);
             *reinterpret_cast<h8*>(cv + LY::VH + key * LY::ROWH + (blk * 32 + 8 * part) * 2) = stream::v_codes_sub(c0w, c1w);
         }
-        // scales, steps, offsets: task (key, blk)
+        // V steps (times 2^-E_v) and offsets: task (key, blk)
+        const float vdown = dec::pow2(-(int)vsh_next);
         for (int u = tid; u < kTile * NB; u += 64 * kWaves) {
             const int key = u / NB, blk = u - key * NB;
-            const bool live = t0 + key < c1;
-            const uint16_t kd = *reinterpret_cast<const uint16_t*>(rk + key * WN::KSTR + kofs + blk * 34);
-            reinterpret_cast<float*>(cv + LY::KS)[blk * kTile + key] = live ? f16_value(kd) * sc2 : 0.0f;
-            const uint32_t dm = live ? *reinterpret_cast<const uint32_t*>(rv + key * WN::VSTR + blk * 24) : 0u;
-            reinterpret_cast<uint16_t*>(cv + LY::VD)[blk * kTile + key] = (uint16_t)(dm & 0xFFFF);
+            const uint32_t dm = vstepm(key, blk);
+            reinterpret_cast<_Float16*>(cv + LY::VD)[blk * kTile + key] = (_Float16)(f16_value((uint16_t)(dm & 0xFFFFu)) * vdown);
             reinterpret_cast<uint16_t*>(cv + LY::VM)[key * LY::VMS + blk] = (uint16_t)(dm >> 16);
         }
     };
@@ -259,56 +296,57 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_prime(DecodeParams p) {
     const int mc = (4 * (j16 & 3) < LY::VMS) ? (j16 & 3) : 0;
     int vsh = 0;
 
-    // ---- the products of one converted tile for this wave's query rows
-    auto compute = [&](int it, int t0) {
+    const float sc2 = p.scale * kLog2e;
+    // ---- the products of one converted tile for this wave's query rows;
+    // ksh, vsh_t: the tile's range shifts
+    auto compute = [&](int it, int t0, uint32_t ksh, uint32_t vsh_t) {
         const uint8_t* const cv = smem + kRawBufs * LY::RAW + (it & 1) * LY::CONV;
-        const float* const KSa = reinterpret_cast<const float*>(cv + LY::KS);
-        const uint16_t* const VDa = reinterpret_cast<const uint16_t*>(cv + LY::VD);
-        // ---- scores S^T (base 2): sv[rt][h][i] = S[row rt*16 + j16][key 16h + 4*q4 + i]
-        float sv[RTW][2][4];
+        // ---- raw scores S^T: acc[rt][h][i] = sum over the head's dims of
+        // (d * c)(key 16h + 4*q4 + i) * q'(row rt*16 + j16), hi and lo parts
+        f4 acc[RTW][2];
 #pragma unroll
         for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+            for (int h = 0; h < 2; ++h) acc[rt][h] = (f4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sv[rt][h][i] = 0.0f;
-#pragma unroll
-        for (int blk = 0; blk < NB; ++blk) {
-            const float4 ks0 = *reinterpret_cast<const float4*>(KSa + blk * kTile + 4 * q4);
-            const float4 ks1 = *reinterpret_cast<const float4*>(KSa + blk * kTile + 16 + 4 * q4);
-            const float ksv[2][4] = {{ks0.x, ks0.y, ks0.z, ks0.w}, {ks1.x, ks1.y, ks1.z, ks1.w}};
+        for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const h8 kf = *reinterpret_cast<const h8*>(cv + LY::KH + (16 * h + j16) * LY::ROWH + (blk * 32 + 8 * q4) * 2);
+                const int o = (16 * h + j16) * LY::ROWH + (blk * 32 + 8 * q4) * 2;
+                const h8 kh = *reinterpret_cast<const h8*>(cv + LY::KH + o);
+                const h8 kl = *reinterpret_cast<const h8*>(cv + LY::KL + o);
 #pragma unroll
                 for (int rt = 0; rt < RTW; ++rt) {
-                    f4 d = dec::mfma(kf, qh[rt][blk], (f4){0.f, 0.f, 0.f, 0.f});
-                    if (QLO) d = dec::mfma(kf, ql[rt][blk], d);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) sv[rt][h][i] = fmaf(ksv[h][i], d[i], sv[rt][h][i]);
+                    acc[rt][h] = dec::mfma(kh, qh[rt][blk], acc[rt][h]);
+                    acc[rt][h] = dec::mfma(kl, qh[rt][blk], acc[rt][h]);
+                    if (QLO) {
+                        acc[rt][h] = dec::mfma(kh, ql[rt][blk], acc[rt][h]);
+                        acc[rt][h] = dec::mfma(kl, ql[rt][blk], acc[rt][h]);
+                    }
                 }
             }
-        }
+        // base-2 scores: the raw ones times scale * log2 e, times 2^ksh, times
+        // the query rows' power of two
+        const float fs = sc2 * qup * dec::pow2((int)ksh);
         // ---- online softmax against a reference max that moves only when a
         // score passes it by more than 8 (so p <= 256, inside fp16)
         const bool interior = t0 >= full_lo && t0 + kTile <= full_hi;
+        if (!interior) {
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int j = t0 + 16 * h + 4 * q4 + i;
+                        acc[rt][h][i] = (j >= vis_lo[rt] && j < vis_hi[rt]) ? acc[rt][h][i] : -INFINITY;
+                    }
+        }
         h8 pu[RTW];
 #pragma unroll
         for (int rt = 0; rt < RTW; ++rt) {
-            float smax = -INFINITY;
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float x = sv[rt][h][i];
-                    if (!interior) {
-                        const int j = t0 + 16 * h + 4 * q4 + i;
-                        x = (j >= vis_lo[rt] && j < vis_hi[rt]) ? x : -INFINITY;
-                    }
-                    sv[rt][h][i] = x;
-                    smax = fmaxf(smax, x);
-                }
-            smax *= qup;
+            const float smax = fmaxf(fmaxf(fmaxf(acc[rt][0][0], acc[rt][0][1]), fmaxf(acc[rt][0][2], acc[rt][0][3])),
+                                     fmaxf(fmaxf(acc[rt][1][0], acc[rt][1][1]), fmaxf(acc[rt][1][2], acc[rt][1][3]))) * fs;
             if (__any(smax > mrow[rt] + 8.0f)) {
                 float mt = fmaxf(smax, __shfl_xor(smax, 16));
                 mt = fmaxf(mt, __shfl_xor(mt, 32));
@@ -329,52 +367,39 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_prime(DecodeParams p) {
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    pu[rt][4 * h + i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(sv[rt][h][i], qup, -mrow[rt]));
+                    pu[rt][4 * h + i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(acc[rt][h][i], fs, -mrow[rt]));
         }
-        // ---- the tile's largest step decides the accumulators' units
-        uint32_t dmx = 0;
+        // ---- the accumulators take the tile's V units (2^-vsh_t)
+        if (vsh_t != (uint32_t)vsh) {
+            const float f = dec::pow2(vsh - (int)vsh_t);
 #pragma unroll
-        for (int x = 0; x < (kTile * NB + 63) / 64; ++x) {
-            const int u = x * 64 + lane;
-            if (kTile * NB % 64 == 0 || u < kTile * NB) dmx = max(dmx, (uint32_t)VDa[u]);
+            for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                for (int dt = 0; dt < 2 * NB; ++dt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) oacc[rt][dt][i] *= f;
+            vsh = (int)vsh_t;
         }
-        const bool big = __any(dmx >= 0x5800u);   // fp16 128.0
-        if (big || vsh != 0) {
-            const int want = big ? __builtin_amdgcn_readfirstlane(dec::v_shift(dec::wave_max_dpp(f16_value((uint16_t)dmx)))) : 0;
-            if (want != vsh) {
-                const float f = dec::pow2(vsh - want);
-#pragma unroll
-                for (int rt = 0; rt < RTW; ++rt)
-#pragma unroll
-                    for (int dt = 0; dt < 2 * NB; ++dt)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) oacc[rt][dt][i] *= f;
-                vsh = want;
-            }
-        }
-        const _Float16 vdown = (_Float16)dec::pow2(-vsh);
-        // ---- P V: P' = fp16(P) * step (steps times 2^-vsh), V codes from the converted tile
+        // ---- P V: P' = fp16(P) * step (steps times 2^-vsh), 16 dims per product
+        const uint16_t* const VDa = reinterpret_cast<const uint16_t*>(cv + LY::VD);
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) {
-            h8 dh = stream::steps_of(VDa + blk * kTile, q4);
-            if (vsh != 0) dh = dh * (h8){vdown, vdown, vdown, vdown, vdown, vdown, vdown, vdown};
+            const h8 dh = stream::steps_of(VDa + blk * kTile, q4);
+            h8 pa[RTW];
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt) pa[rt] = pu[rt] * dh;
 #pragma unroll
             for (int dd = 0; dd < 2; ++dd) {
                 const int col = blk * 32 + 16 * dd + 4 * (j16 & 3);
                 const h8 vf = dec::tr16_pair(cv + LY::VH + mk0 * LY::ROWH + col * 2, cv + LY::VH + mk1 * LY::ROWH + col * 2);
 #pragma unroll
-                for (int rt = 0; rt < RTW; ++rt) {
-                    const h8 pa = pu[rt] * dh;
-                    oacc[rt][2 * blk + dd] = dec::mfma(pa, vf, oacc[rt][2 * blk + dd]);
-                }
+                for (int rt = 0; rt < RTW; ++rt) oacc[rt][2 * blk + dd] = dec::mfma(pa[rt], vf, oacc[rt][2 * blk + dd]);
             }
         }
         // q5_1 offset term and the row sums (the ones column)
-        {
-            const h8 mb = dec::tr16_pair(cv + LY::VM + (mk0 * LY::VMS + 4 * mc) * 2, cv + LY::VM + (mk1 * LY::VMS + 4 * mc) * 2);
+        const h8 mb = dec::tr16_pair(cv + LY::VM + (mk0 * LY::VMS + 4 * mc) * 2, cv + LY::VM + (mk1 * LY::VMS + 4 * mc) * 2);
 #pragma unroll
-            for (int rt = 0; rt < RTW; ++rt) macc[rt] = dec::mfma(pu[rt], mb, macc[rt]);
-        }
+        for (int rt = 0; rt < RTW; ++rt) macc[rt] = dec::mfma(pu[rt], mb, macc[rt]);
     };
 
     // ---- prologue: tiles 0, 1 and 2 requested, tile 0 converted
@@ -401,9 +426,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_prime(DecodeParams p) {
         // opposite orders on the two waves that share a SIMD (waves w and
         // w + 4), so that one converts (vector ALU, LDS) while the other
         // multiplies (matrix cores).
+        const uint32_t ksh = ksh_next, vsh_t = vsh_next;   // tile it's shifts
         const bool convert_first = wave < kWaves / 2;
         if (convert_first && it + 1 < ntiles) convert(t0 + kTile, rnext, (it + 1) & 1);
-        if (active) compute(it, t0);
+        if (active) compute(it, t0, ksh, vsh_t);
         if (!convert_first && it + 1 < ntiles) convert(t0 + kTile, rnext, (it + 1) & 1);
         rnext = rnext == kRawBufs - 1 ? 0 : rnext + 1;
     }

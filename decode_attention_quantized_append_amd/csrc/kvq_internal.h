@@ -168,8 +168,9 @@ struct StreamWinF8 {
 // The prime decode kernel (many query rows per KV head): a workgroup of
 // kPrimeGroups waves, one 32-row query group each, shares each KV tile.  Its
 // LDS for head_dim = 32 * NB: kPrimeRawBufs raw tile buffers (the stream
-// kernel's row windows, K rows then V rows) and two converted ones (fp16 K codes, fp16 V
-// codes times 2^-24, K scales, V steps, V offset rows with ones).
+// kernel's row windows, K rows then V rows) and two converted ones (K step x
+// code as fp16 hi and lo parts, V codes as fp16 subnormals, V steps, V offset
+// rows with ones).
 constexpr int kPrimeGroups = 8;
 constexpr int kPrimeRawBufs = 3;    // raw tile buffers: two tiles in flight while one is converted
 template <int NB>
@@ -180,10 +181,10 @@ struct PrimeLayout {
     static constexpr int RK = 0, RV = kRowTile * WN::KSTR;
     static constexpr int ROWH = HD * 2 + 16;                    // fp16 row of a head, padded
     static constexpr int VMS = WN::VMS;                         // offsets, then ones
-    static constexpr int KH = 0;                                // fp16 [32][HD] K codes
-    static constexpr int VH = KH + kRowTile * ROWH;             // fp16 [32][HD] V codes * 2^-24
-    static constexpr int KS = VH + kRowTile * ROWH;             // f32 [NB][32] K scales * scale * log2 e
-    static constexpr int VD = KS + NB * kRowTile * 4;           // fp16 [NB][32] V steps
+    static constexpr int KH = 0;                                // fp16 [32][HD] K products, high parts
+    static constexpr int KL = KH + kRowTile * ROWH;             // fp16 [32][HD] K products, low parts
+    static constexpr int VH = KL + kRowTile * ROWH;             // fp16 [32][HD] V codes * 2^-24
+    static constexpr int VD = VH + kRowTile * ROWH;             // fp16 [NB][32] V steps
     static constexpr int VM = VD + NB * kRowTile * 2;           // fp16 [32][VMS] V offsets, then ones
     static constexpr int CONV = VM + kRowTile * VMS * 2;        // one converted buffer
     static constexpr int BYTES = kPrimeRawBufs * RAW + 2 * CONV;

@@ -94,6 +94,46 @@ def test_decode_large_v_steps(name, v_mode):
     p.decode(q, float(np.float32(1 / np.sqrt(hd))), sinks=s, what=f"{name} v={v_mode}", atol=v_scale_atol(p))
 
 
+@pytest.mark.parametrize("name", sorted(SHAPES))
+def test_decode_large_and_tiny_k_steps(name):
+    """K blocks over the q8_0 range: in session 0 each row takes N(0,1),
+    uniform +-3e4 (step about 236) or uniform +-6e4 (step about 472, above
+    2^8) blocks, with queries of 3e-4 N(0,1) so that scores stay near 10; in
+    session 1 each row takes N(0,1) or 1e-6 N(0,1) blocks (subnormal fp16
+    steps) with N(0,1) queries.  Checks every kernel's K products (exact
+    codes times steps, or the exact fp16 pairs of the prime kernel, with its
+    shift for steps of 2^8 and more) against the oracle."""
+    B, H, Hkv, hd, T, lens, window, io, tiling = SHAPES[name]
+    B = 2
+    lens = (list(lens) + [lens[0]])[:2]
+    rng = np.random.default_rng(zlib.crc32(f"{name}/k".encode()))
+    p = Pair(B, H, Hkv, hd, max(lens) + 8, window, 0, io=io)
+    if tiling:
+        p.gpu.set_decode_tiling(*tiling)
+    lens = np.asarray(lens)
+    done = np.zeros(B, np.int64)
+    while np.any(done < lens):
+        n = np.minimum(lens - done, 400)
+        m = int(n.max())
+        k = rng.standard_normal((B, m, Hkv, hd))
+        cls = rng.integers(0, 3, size=(m, Hkv, 1))
+        k[0] = np.where(cls == 1, rng.uniform(-3e4, 3e4, (m, Hkv, hd)), k[0])
+        k[0] = np.where(cls == 2, rng.uniform(-6e4, 6e4, (m, Hkv, hd)), k[0])
+        k[1] = np.where(cls == 1, k[1] * 1e-6, k[1])
+        k = k.astype(np.float32)
+        v = rng.standard_normal((B, m, Hkv, hd)).astype(np.float32)
+        if io == "bf16":
+            k, v = round_bf16(k), round_bf16(v)
+        p.append(k, v, n.tolist())
+        done += n
+    q = rng.standard_normal((B, T, H, hd))
+    q[0] *= 3e-4
+    q = q.astype(np.float32)
+    q = round_bf16(q) if io == "bf16" else q
+    print(f"\ncase {name} k range", flush=True)
+    p.decode(q, float(np.float32(1 / np.sqrt(hd))), what=f"{name} k range")
+
+
 def extreme_q(rng, B, T, H, hd, io, big=1e5, spike_at=1e4):
     """Query rows of very different magnitudes: x big, x1e-6 (below fp16's
     normal range), x1e-30, all zero, one element spike_at among tiny ones
