@@ -331,16 +331,16 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_prime(DecodeParams p) {
         // ---- online softmax against a reference max that moves only when a
         // score passes it by more than 8 (so p <= 256, inside fp16)
         const bool interior = t0 >= full_lo && t0 + kTile <= full_hi;
-        if (!interior) {
+        if (!interior) {   // edge tiles: one unsigned compare per key against the row's visible range
 #pragma unroll
-            for (int rt = 0; rt < RTW; ++rt)
+            for (int rt = 0; rt < RTW; ++rt) {
+                const int jb = t0 + 4 * q4 - vis_lo[rt];
+                const uint32_t span = (uint32_t)(vis_hi[rt] - vis_lo[rt]);
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int j = t0 + 16 * h + 4 * q4 + i;
-                        acc[rt][h][i] = (j >= vis_lo[rt] && j < vis_hi[rt]) ? acc[rt][h][i] : -INFINITY;
-                    }
+                    for (int i = 0; i < 4; ++i) acc[rt][h][i] = (uint32_t)(jb + 16 * h + i) < span ? acc[rt][h][i] : -INFINITY;
+            }
         }
         h8 pu[RTW];
 #pragma unroll

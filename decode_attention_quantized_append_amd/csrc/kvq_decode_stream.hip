@@ -546,7 +546,21 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
 
         // ---- online softmax against a reference max that moves only when a
         // score passes it by more than 8 (so p <= 256, well inside fp16)
+        // Edge tiles: scores of keys outside a row's visible range become
+        // -inf (one unsigned compare per key, in one branch for the tile).
         const bool interior = t0 >= full_lo && t0 + kTile <= full_hi;
+        if (!interior) {
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt) {
+                const int jb = t0 + 4 * q4 - vis_lo[rt];
+                const uint32_t span = (uint32_t)(vis_hi[rt] - vis_lo[rt]);
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        sv[rt][h][i] = (uint32_t)(jb + 16 * h + i) < span ? sv[rt][h][i] : -INFINITY;
+            }
+        }
         h8 pu[RTW];   // P in fp16, the A operand of the products with V
 #pragma unroll
         for (int rt = 0; rt < RTW; ++rt) {
@@ -554,15 +568,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float x = sv[rt][h][i];
-                    if (!interior) {
-                        const int j = t0 + 16 * h + 4 * q4 + i;
-                        x = (j >= vis_lo[rt] && j < vis_hi[rt]) ? x : -INFINITY;
-                    }
-                    sv[rt][h][i] = x;
-                    smax = fmaxf(smax, x);
-                }
+                for (int i = 0; i < 4; ++i) smax = fmaxf(smax, sv[rt][h][i]);
             smax *= qup;                           // the scores of the scaled query rows, times qup
             if (__any(smax > mrow[rt] + 8.0f)) {   // -inf never passes, nor does a row's first finite max fail to
                 float mt = fmaxf(smax, __shfl_xor(smax, 16));
