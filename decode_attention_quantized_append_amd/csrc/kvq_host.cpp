@@ -252,7 +252,7 @@ bool choose_kernel(const kvq_cache* h, int R, int32_t T, bool f32_queries, Plan*
                         ceil_div(T, R / hpk) >= kPrimeMinGroups);
     if (prime) {
         if (!prime_ok(c, R, T)) return false;
-        if (!aligned_start_resident(h, T)) return h->decode_kernel == KVQ_DECODE_AUTO;
+        if (!aligned_start_resident(h, T)) return true;   // the per-head kernel, as for the stream kernel
         p->kernel = kvq::kPrime;
         p->gh = 1;
         p->rs = p->rg = p->ds = 1;

@@ -326,12 +326,16 @@ typedef enum kvq_decode_kernel {
  * holding both 16-row tiles or 2 row-group waves (17 to 32 rows), or 3 = two
  * waves each taking half of a 128- or 256-dim head for all rows (17 to 32
  * rows); 0 = chosen per call.  The stream kernel needs head_dim 64, 128 or
- * 256; a kernel or tiling that does not fit a call's shape makes that
- * kvq_decode fail with EINVAL, except that a session whose first visible
- * row, rounded down to 32, was rebased away is served by the per-head
- * kernel.  The result does not depend on the choice beyond float rounding.
+ * 256; the prime kernel (no head_group, no sub_tiles) q8_0 / q5_1 rows,
+ * head_dim 64 or 128 and more than one group of 32 / hpk query rows.  A
+ * kernel or tiling that does not fit a call's shape makes that kvq_decode
+ * fail with EINVAL, except that a session whose first visible row, rounded
+ * down to 32, was rebased away is served by the per-head kernel.  The
+ * automatic choice takes the prime kernel from four groups of query rows
+ * on.  The result does not depend on the choice beyond
+ * float rounding.
  * Errors: EINVAL (unknown kernel, head_group not dividing n_kv_heads,
- * head_group or sub_tiles given for the per-head kernel). */
+ * head_group or sub_tiles given for a kernel other than the stream one). */
 kvq_status kvq_set_decode_tiling(kvq_cache* h, int32_t kernel, int32_t head_group, int32_t sub_tiles);
 
 /* Copies the handle's configuration, sizes and buffer pointers.

@@ -569,6 +569,20 @@ def test_decode_ring_start_below_base_falls_back(lib):
             assert k == (want if (lo & ~31) >= base[0] else 0)
             seen.add(k)
         assert seen == {0, want}
+    # the prime kernel (two groups of 8 rows here, set explicitly) falls back the same way
+    h = create(lib, n_seqs=1, n_q_heads=32, n_kv_heads=8, head_dim=128, capacity=120, window=90,
+               ring_step=10)
+    kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_PRIME, 0, 0, lib)
+    seen = set()
+    for _ in range(150):
+        kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 1, None, 0, lib)
+        L, base = lengths(lib, h, 1)
+        if L[0] < 9:
+            continue
+        k = plan_of(lib, h, T=9)["kernel"]
+        assert k == (3 if (max(0, L[0] - 98) & ~31) >= base[0] else 0)
+        seen.add(k)
+    assert seen == {0, 3}
 
 
 def _ring_model_ok(cap, W, C, S):
