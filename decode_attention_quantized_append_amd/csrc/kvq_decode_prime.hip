@@ -48,6 +48,7 @@ using dec::kLog2e;
 constexpr int kTile = kRowTile;
 constexpr int kWaves = kPrimeGroups;
 constexpr int kRawBufs = kPrimeRawBufs;
+constexpr int kConvBufs = kPrimeConvBufs;
 
 // vmcnt(n) for a count known only at run time (n < 0: wait for all).
 __device__ __forceinline__ void wait_vmcnt(int n) {
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_prime(DecodeParams p) {
             const uint32_t s1 = ((hb >> 4) * 0x00204081u) & 0x01010101u;
             const uint32_t c0w = ((nibw.x >> shn) & 0x0F0F0F0Fu) | (s0 << 4);
             const uint32_t c1w = ((nibw.y >> shn) & 0x0F0F0F0Fu) | (s1 << 4);
-            *reinterpret_cast<h8*>(cv + LY::VH + key * LY::ROWH + (blk * 32 + 8 * part) * 2) = stream::v_codes_sub(c0w, c1w);
+            *reinterpret_cast<h8*>(cv + LY::VH + key * LY::ROWV + (blk * 32 + 8 * part) * 2) = stream::v_codes_sub(c0w, c1w);
         }
         // V steps (times 2^-E_v) and offsets: task (key, blk)
         const float vdown = dec::pow2(-(int)vsh_next);
@@ -211,7 +212,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_prime(DecodeParams p) {
         }
     };
     // the columns of ones after each offset row, in both converted buffers (never rewritten)
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < kConvBufs; ++cb) {
         uint16_t* const vm = reinterpret_cast<uint16_t*>(smem + kRawBufs * LY::RAW + cb * LY::CONV + LY::VM);
         constexpr int NO = LY::VMS - NB;
         for (int u = threadIdx.x; u < kTile * NO; u += 64 * kWaves) vm[(u / NO) * LY::VMS + NB + u % NO] = 0x3C00;
@@ -297,13 +298,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_prime(DecodeParams p) {
     int vsh = 0;
 
     const float sc2 = p.scale * kLog2e;
-    // ---- the products of one converted tile for this wave's query rows;
-    // ksh, vsh_t: the tile's range shifts
-    auto compute = [&](int it, int t0, uint32_t ksh, uint32_t vsh_t) {
-        const uint8_t* const cv = smem + kRawBufs * LY::RAW + (it & 1) * LY::CONV;
-        // ---- raw scores S^T: acc[rt][h][i] = sum over the head's dims of
-        // (d * c)(key 16h + 4*q4 + i) * q'(row rt*16 + j16), hi and lo parts
-        f4 acc[RTW][2];
+    // ---- the raw scores of one converted tile (converted buffer cb) for
+    // this wave's query rows: acc[rt][h][i] = sum over the head's dims of
+    // (d * c)(key 16h + 4*q4 + i) * q'(row rt*16 + j16), hi and lo parts
+    auto scores = [&](int cb, f4 (&acc)[RTW][2]) {
+        const uint8_t* const cv = smem + kRawBufs * LY::RAW + cb * LY::CONV;
 #pragma unroll
         for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
@@ -325,6 +324,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_prime(DecodeParams p) {
                     }
                 }
             }
+    };
+    // ---- softmax and P V of one tile (at t0, converted buffer cb) from its
+    // raw scores; ksh, vsh_t: the tile's range shifts
+    auto finish = [&](int cb, int t0, f4 (&acc)[RTW][2], uint32_t ksh, uint32_t vsh_t) {
+        const uint8_t* const cv = smem + kRawBufs * LY::RAW + cb * LY::CONV;
         // base-2 scores: the raw ones times scale * log2 e, times 2^ksh, times
         // the query rows' power of two
         const float fs = sc2 * qup * dec::pow2((int)ksh);
@@ -391,7 +395,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_prime(DecodeParams p) {
 #pragma unroll
             for (int dd = 0; dd < 2; ++dd) {
                 const int col = blk * 32 + 16 * dd + 4 * (j16 & 3);
-                const h8 vf = dec::tr16_pair(cv + LY::VH + mk0 * LY::ROWH + col * 2, cv + LY::VH + mk1 * LY::ROWH + col * 2);
+                const h8 vf = dec::tr16_pair(cv + LY::VH + mk0 * LY::ROWV + col * 2, cv + LY::VH + mk1 * LY::ROWV + col * 2);
 #pragma unroll
                 for (int rt = 0; rt < RTW; ++rt) oacc[rt][2 * blk + dd] = dec::mfma(pa[rt], vf, oacc[rt][2 * blk + dd]);
             }
@@ -402,36 +406,64 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_prime(DecodeParams p) {
         for (int rt = 0; rt < RTW; ++rt) macc[rt] = dec::mfma(pu[rt], mb, macc[rt]);
     };
 
-    // ---- prologue: tiles 0, 1 and 2 requested, tile 0 converted
+    // ---- the pipeline.  Tile t's rows go to raw buffer t mod 3 and its
+    // operands to converted buffer t mod 3.  Iteration it (after one barrier)
+    // requests tile it + 4, computes the scores of tile it + 1, the softmax
+    // and P V of tile it (whose scores the previous iteration computed) and
+    // converts tile it + 2; so the matrix cores take tile it + 1's scores
+    // while the vector ALU works tile it's softmax.
+    auto ring3 = [](int x) { return x == 2 ? 0 : x + 1; };
     for (int x = 0; x < kRawBufs; ++x)
         if (x < ntiles) issue(t_begin + x * kTile, x);
+    uint32_t ksh0 = 0, vsh0 = 0, ksh1 = 0, vsh1 = 0;   // the shifts of tiles it and it + 1
     if (ntiles > 0) {
         const int a = my_loads(t_begin + kTile), c = my_loads(t_begin + 2 * kTile);
         wait_vmcnt(a < 0 || c < 0 ? 0 : a + c);
         stream::lds_barrier();                       // every wave's pieces of tile 0 have landed
         convert(t_begin, 0, 0);
+        ksh0 = ksh_next;
+        vsh0 = vsh_next;
+    }
+    if (ntiles > 1) {
+        wait_vmcnt(my_loads(t_begin + 2 * kTile));
+        stream::lds_barrier();                       // tile 1 has landed; tile 0's raw buffer is free
+        if (ntiles > 3) issue(t_begin + 3 * kTile, 0);
+        convert(t_begin + kTile, 1, 1);
+        ksh1 = ksh_next;
+        vsh1 = vsh_next;
     }
 
-    int rnext = 1;                                   // raw buffer of tile it + 1
+    f4 acc_c[RTW][2], acc_n[RTW][2];
+    int b0 = 0;                                      // raw and converted buffer of tile it
     for (int it = 0; it < ntiles; ++it) {
         const int t0 = t_begin + it * kTile;
-        // tile it + 1 has landed (tile it + 2 may still be in flight); after
-        // the barrier tile it is converted by all waves, tile it - 1's
-        // operands are no longer read, and tile it's raw buffer is free
-        if (it + 1 < ntiles) wait_vmcnt(my_loads(t0 + 2 * kTile));
+        const int b1 = ring3(b0), b2 = ring3(b1);
+        // tile it + 2 has landed (tile it + 3 may still be in flight); after
+        // the barrier tiles it and it + 1 are converted by all waves, tile
+        // it - 1's operands are no longer read, and tile it + 1's raw buffer
+        // is free
+        if (it + 2 < ntiles) wait_vmcnt(my_loads(t0 + 3 * kTile));
         stream::lds_barrier();
-        const int rfree = rnext == 0 ? kRawBufs - 1 : rnext - 1;
-        if (it + 3 < ntiles) issue(t0 + 3 * kTile, rfree);
-        // The conversion of tile it + 1 and the products of tile it, in
-        // opposite orders on the two waves that share a SIMD (waves w and
-        // w + 4), so that one converts (vector ALU, LDS) while the other
-        // multiplies (matrix cores).
-        const uint32_t ksh = ksh_next, vsh_t = vsh_next;   // tile it's shifts
+        if (it + 4 < ntiles) issue(t0 + 4 * kTile, b1);
+        // the conversion of tile it + 2 and the products, in opposite orders
+        // on the two waves that share a SIMD (waves w and w + 4)
         const bool convert_first = wave < kWaves / 2;
-        if (convert_first && it + 1 < ntiles) convert(t0 + kTile, rnext, (it + 1) & 1);
-        if (active) compute(it, t0, ksh, vsh_t);
-        if (!convert_first && it + 1 < ntiles) convert(t0 + kTile, rnext, (it + 1) & 1);
-        rnext = rnext == kRawBufs - 1 ? 0 : rnext + 1;
+        if (convert_first && it + 2 < ntiles) convert(t0 + 2 * kTile, b2, b2);
+        if (active) {
+            if (it == 0) scores(b0, acc_c);
+            if (it + 1 < ntiles) scores(b1, acc_n);
+            finish(b0, t0, acc_c, ksh0, vsh0);
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) acc_c[rt][h] = acc_n[rt][h];
+        }
+        if (!convert_first && it + 2 < ntiles) convert(t0 + 2 * kTile, b2, b2);
+        ksh0 = ksh1;
+        vsh0 = vsh1;
+        ksh1 = ksh_next;
+        vsh1 = vsh_next;
+        b0 = b1;
     }
 
     if (!active) return;

@@ -168,28 +168,33 @@ struct StreamWinF8 {
 // The prime decode kernel (many query rows per KV head): a workgroup of
 // kPrimeGroups waves, one 32-row query group each, shares each KV tile.  Its
 // LDS for head_dim = 32 * NB: kPrimeRawBufs raw tile buffers (the stream
-// kernel's row windows, K rows then V rows) and two converted ones (K step x
+// kernel's row windows, K rows then V rows) and kPrimeConvBufs converted ones (K step x
 // code as fp16 hi and lo parts, V codes as fp16 subnormals, V steps, V offset
 // rows with ones).
 constexpr int kPrimeGroups = 8;
 constexpr int kPrimeRawBufs = 3;    // raw tile buffers: two tiles in flight while one is converted
+constexpr int kPrimeConvBufs = 3;   // converted tiles: one in softmax and P V, one in scores, one being written
 template <int NB>
 struct PrimeLayout {
     using WN = StreamWin<NB>;
     static constexpr int HD = NB * 32;
     static constexpr int RAW = kRowTile * (WN::KSTR + WN::VSTR);
     static constexpr int RK = 0, RV = kRowTile * WN::KSTR;
-    static constexpr int ROWH = HD * 2 + 16;                    // fp16 row of a head, padded
+    // fp16 rows of a head, padded: K rows (read 16 bytes a lane, 16 rows at
+    // once) by 4 banks a row, V rows (transposed 8-byte reads of 4 rows) by
+    // 8, so that neither read meets a bank twice
+    static constexpr int ROWH = HD * 2 + 16;
+    static constexpr int ROWV = HD * 2 + 32;
     static constexpr int VMS = WN::VMS;                         // offsets, then ones
     static constexpr int KH = 0;                                // fp16 [32][HD] K products, high parts
     static constexpr int KL = KH + kRowTile * ROWH;             // fp16 [32][HD] K products, low parts
     static constexpr int VH = KL + kRowTile * ROWH;             // fp16 [32][HD] V codes * 2^-24
-    static constexpr int VD = VH + kRowTile * ROWH;             // fp16 [NB][32] V steps
+    static constexpr int VD = VH + kRowTile * ROWV;             // fp16 [NB][32] V steps
     static constexpr int VM = VD + NB * kRowTile * 2;           // fp16 [32][VMS] V offsets, then ones
     static constexpr int CONV = VM + kRowTile * VMS * 2;        // one converted buffer
-    static constexpr int BYTES = kPrimeRawBufs * RAW + 2 * CONV;
+    static constexpr int BYTES = kPrimeRawBufs * RAW + kPrimeConvBufs * CONV;
     static constexpr int NIT = WN::NKI + WN::NVI;               // load instructions per tile
-    static_assert(RAW % 16 == 0 && CONV % 16 == 0 && ROWH % 16 == 0, "16-byte alignment");
+    static_assert(RAW % 16 == 0 && CONV % 16 == 0 && ROWH % 16 == 0 && ROWV % 16 == 0, "16-byte alignment");
 };
 inline int prime_lds_bytes(int NB) {
     return NB == 2 ? PrimeLayout<2>::BYTES : NB == 4 ? PrimeLayout<4>::BYTES : 0;

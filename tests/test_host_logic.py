@@ -522,7 +522,7 @@ def test_decode_prime_choice(lib):
     h = create(lib, n_seqs=1, n_q_heads=32, n_kv_heads=8, head_dim=128, capacity=9000)
     kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 8192, None, 0, lib)
     p = plan_of(lib, h, T=512)
-    assert (p["kernel"], p["gh"], p["Tg"], p["groups"], p["lds"]) == (PRIME, 1, 8, 64, 78336)
+    assert (p["kernel"], p["gh"], p["Tg"], p["groups"], p["lds"]) == (PRIME, 1, 8, 64, 106752)
     assert p["chunk"] % 32 == 0 and p["units"] == p["splits"] == -(-8192 // p["chunk"])
     assert p["units"] * 8 * 8 <= 256 < -(-8192 // (p["chunk"] - 32)) * 8 * 8   # one round, no smaller chunk
     assert plan_of(lib, h, T=25)["kernel"] == PRIME          # 4 groups
@@ -541,7 +541,7 @@ def test_decode_prime_choice(lib):
     h = create(lib, n_seqs=2, n_q_heads=16, n_kv_heads=4, head_dim=64, capacity=3000)
     kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 2000, None, 0, lib)
     p = plan_of(lib, h, T=100, dtype=kvq.KVQ_F32)
-    assert (p["kernel"], p["lds"], p["groups"]) == (PRIME, 40704, 13)
+    assert (p["kernel"], p["lds"], p["groups"]) == (PRIME, 56448, 13)
     for kw in (dict(head_dim=256, n_q_heads=16, n_kv_heads=4), dict(head_dim=128, fmt="e4m3")):
         h = create(lib, n_seqs=1, capacity=3000, **kw)
         kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 2000, None, 0, lib)
