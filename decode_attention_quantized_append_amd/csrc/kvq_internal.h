@@ -113,7 +113,9 @@ inline bool importance_group(int k_row, int* rows, int* rp) {
     if (r < 16) return false;
     *rows = r > 64 ? 64 : r;
     return true;
-}// Geometry of the per-wave stream decode kernel for head_dim = 32 * NB (NB
+}
+
+// Geometry of the per-wave stream decode kernel for head_dim = 32 * NB (NB
 // even): each wave copies its KV head's row windows of a 32-row tile, in
 // 16-byte pieces, into one private LDS buffer (K rows, then V rows), and
 // builds per-tile scale arrays.

@@ -417,10 +417,11 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
 // group's 16-key tiles: the scores of the 16 keys against the 16 query rows
 // are S^T = K Q^T on v_mfma_f32_16x16x32_f16, one per 32-dim block (the K
 // codes exact in fp16), each block's product scaled by its keys' q8_0 (or
-// FP8) scales.  Lane (q4, j16) then holds keys 4 q4 + i against query row
+// FP8) scales, which each lane reads from the rows in LDS for the keys of its
+// output rows.  Lane (q4, j16) then holds keys 4 q4 + i against query row
 // j16: the probability 2^(log2 e (scale s - lse)) where the key is visible
-// to the row, else 0, summed over the 16 rows by shuffles into the wave's
-// own LDS slot of the key.  At the end the waves' slots are added in a fixed
+// to the row, else 0, summed over the 16 rows by DPP row rotations into the
+// wave's own LDS slot of the key.  At the end the waves' slots are added in a fixed
 // order and one thread per key adds the total to imp; a key belongs to one
 // workgroup, so no atomics are needed.  Workgroups whose keys all lie past
 // the session's length return at once (the grid covers the longest session,
@@ -514,46 +515,47 @@ __global__ __launch_bounds__(64 * kImpWaves) void importance_kernel(ImportancePa
         const int first = p.window > 0 ? max(0, upto - p.window) : 0;
         const float su2 = p.scale * up * dec::kLog2e;
 
-        // ---- the group's 16-key tiles
+        // ---- the group's 16-key tiles.  Rows past the group's length hold
+        // stale bytes; their keys lie at or past the session's length, where
+        // the visibility test below selects 0 whatever their scores are.
         for (int ti = 0; ti < ntile; ++ti) {
             const int kr = ti * 16 + j16;          // this lane's key row (A operand)
-            const bool ka_ok = kr < nrows;         // rows past the length were not loaded
-            const int rb = delta0 + kr * p.k_row;
-            const int krow = kr * RP * 16 + (rb & 15);   // the row's first byte in LDS
+            const int krow = kr * RP * 16 + ((delta0 + kr * p.k_row) & 15);   // the row's first byte in LDS
+            // the first bytes of the rows whose keys this lane's D rows hold (4 q4 + i)
+            int srow[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = ti * 16 + 4 * q4 + i;
+                srow[i] = r * RP * 16 + ((delta0 + r * p.k_row) & 15);
+            }
             f4 sv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int blk = 0; blk < NB; ++blk) {
-                // one block's reads at a time: tie them to the previous
-                // block's sums, so that the reads of all blocks are not held
-                // at once
-                if (NB >= 5) asm volatile("" : "+v"(sv));
+                // fp32 queries: one block's reads at a time (tied to the
+                // previous block's sums), so that the reads of all blocks
+                // are not held at once
+                if (F32 && NB >= 5) asm volatile("" : "+v"(sv));
                 // the lane's 8 codes from the 3 aligned words holding them
                 const int ca = krow + (F8 ? (g * NB + blk) * 32 : (g * NB + blk) * 34 + 2) + 8 * q4;
                 const uint32_t* const cw = reinterpret_cast<const uint32_t*>(krows + (ca & ~3));
                 const uint32_t sh = (uint32_t)(ca & 3) * 8;
-                const uint32_t w0 = ka_ok ? cw[0] : 0u, w1 = ka_ok ? cw[1] : 0u, w2 = ka_ok ? cw[2] : 0u;
-                const uint32_t c0 = __builtin_amdgcn_alignbit(w1, w0, sh);
-                const uint32_t c1 = __builtin_amdgcn_alignbit(w2, w1, sh);
-                const int sa = krow + (F8 ? p.Hkv * p.hd + 2 * (g * NB + blk) : (g * NB + blk) * 34);
-                const uint16_t sbits = *reinterpret_cast<const uint16_t*>(krows + sa);
+                const uint32_t c0 = __builtin_amdgcn_alignbit(cw[1], cw[0], sh);
+                const uint32_t c1 = __builtin_amdgcn_alignbit(cw[2], cw[1], sh);
                 const h8 kf = F8 ? stream::e4m3_codes(c0, c1) : dec::k_codes_f16(c0, c1);
-                // the scale of this lane's key, handed to the lanes whose D
-                // rows are keys 4 q4 + i
-                const float dself = ka_ok ? f16_value(sbits) : 0.0f;
                 f4 d = dec::mfma(kf, qh[blk], (f4){0.f, 0.f, 0.f, 0.f});
                 if constexpr (F32) d = dec::mfma(kf, ql[blk], d);   // fp32 queries: the low part too
+                // the scales of the keys of this lane's D rows, read directly
+                const int so = F8 ? p.Hkv * p.hd + 2 * (g * NB + blk) : (g * NB + blk) * 34;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sv[i] = fmaf(__shfl(dself, 4 * q4 + i), d[i], sv[i]);
+                for (int i = 0; i < 4; ++i)
+                    sv[i] = fmaf(f16_value(*reinterpret_cast<const uint16_t*>(krows + srow[i] + so)), d[i], sv[i]);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int key = kg0 + ti * 16 + 4 * q4 + i;
-                float pr = (real && key >= first && key < upto) ? __builtin_amdgcn_exp2f(fmaf(su2, sv[i], -l2)) : 0.0f;
-                pr += __shfl_xor(pr, 1);
-                pr += __shfl_xor(pr, 2);
-                pr += __shfl_xor(pr, 4);
-                pr += __shfl_xor(pr, 8);
-                if (j16 == 0) slot[wave][ti * 16 + 4 * q4 + i] += pr;
+                const float pr = (real && key >= first && key < upto) ? __builtin_amdgcn_exp2f(fmaf(su2, sv[i], -l2)) : 0.0f;
+                const float tot = dec::row_sum16(pr);   // over the 16 query rows of the tile
+                if (j16 == 0) slot[wave][ti * 16 + 4 * q4 + i] += tot;
             }
         }
     }
