@@ -67,6 +67,12 @@ __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint8_t
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(l) : "memory");
 }
 
+// Lane L's value of x in every lane of its 16-lane row (DPP row_newbcast).
+template <int L>
+__device__ __forceinline__ uint32_t row_bcast(int x) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x150 + L, 0xF, 0xF, true);
+}
+
 // Key of slot k (0..7) of lane group q4 in the P V operands.
 __device__ __forceinline__ int pkey(int q4, int k) { return (k < 4) ? 4 * q4 + k : 16 + 4 * q4 + (k - 4); }
 
@@ -315,8 +321,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
     // row sums); the columns past the stored ones are unused
     const int mc = (4 * (j16 & 3) < WN::VMS) ? (j16 & 3) : 0;
     const int sh_rot = ((j16 & 7) - 4) & 31;             // moves bit (j16 & 7) of each byte to bit 4
-    const int src_lo = (16 * q4 + 4 + (j16 >> 3)) * 4;   // byte addresses of the lanes holding
-    const int src_hi = (16 * q4 + 6 + (j16 >> 3)) * 4;   // this lane's high-bit bytes
+    const bool hi8 = j16 >= 8;                            // this lane's dims take high-bit bytes 1 and 3
 
     // Loads in issue order: K(0) V(0) | K(1) .. V(1) | ...  K(t+1) is issued
     // once the scores of tile t have read the K rows, V(t+1) once its P V has
@@ -701,11 +706,19 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
             const i2 hdr = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(vb));       // d, m, high bits
             // lanes 4..7 of each 16-lane group now hold high-bit bytes 0..3 of
             // the 8 keys.  Dims j16 (first half) take byte j16 >> 3, dims
-            // 16 + j16 byte 2 + (j16 >> 3).
-            const uint32_t qa0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lo, hdr[0]);
-            const uint32_t qa1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lo, hdr[1]);
-            const uint32_t qb0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src_hi, hdr[0]);
-            const uint32_t qb1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src_hi, hdr[1]);
+            // 16 + j16 byte 2 + (j16 >> 3): DPP row broadcasts of lanes 4 and
+            // 5 (6 and 7), one of the two kept per lane (vector ALU only; a
+            // ds_bpermute would wait on the LDS pipe).  The broadcasts run
+            // with every lane active (a lane outside the mask would read as
+            // 0), so they are pinned before the per-lane choice.
+            uint32_t b4[2] = {row_bcast<4>(hdr[0]), row_bcast<4>(hdr[1])};
+            uint32_t b5[2] = {row_bcast<5>(hdr[0]), row_bcast<5>(hdr[1])};
+            uint32_t b6[2] = {row_bcast<6>(hdr[0]), row_bcast<6>(hdr[1])};
+            uint32_t b7[2] = {row_bcast<7>(hdr[0]), row_bcast<7>(hdr[1])};
+            asm volatile("" : "+v"(b4[0]), "+v"(b4[1]), "+v"(b5[0]), "+v"(b5[1]), "+v"(b6[0]), "+v"(b6[1]),
+                              "+v"(b7[0]), "+v"(b7[1]));
+            const uint32_t qa0 = hi8 ? b5[0] : b4[0], qa1 = hi8 ? b5[1] : b4[1];
+            const uint32_t qb0 = hi8 ? b7[0] : b6[0], qb1 = hi8 ? b7[1] : b6[1];
             // code = nibble | high bit << 4: rotating the high-bit bytes right by
             // (j16 & 7) - 4 puts bit (j16 & 7) of each byte at bit 4
             const uint32_t m4 = 0x10101010u, m0 = 0x0F0F0F0Fu;
