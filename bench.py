@@ -595,7 +595,7 @@ def pmc_command(counter, wl):
             f"--no-others --no-ceiling")
 
 
-SQ_WORKLOADS = ("verify", "batched", "verify_f8", "batched_f8")
+SQ_WORKLOADS = ("verify", "batched", "verify_f8", "batched_f8", "prime")
 SQ_PASSES = (("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU",
               "SQ_ACTIVE_INST_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VALU"),
              ("SQ_INSTS_LDS", "SQ_WAIT_ANY", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_SCA",
@@ -700,7 +700,7 @@ def summarize_profiles(d):
             per = collections.defaultdict(lambda: collections.defaultdict(float))
             for name, cn, did, v in c.execute(
                     "select kernel_name, counter_name, dispatch_id, value from counters_collection"):
-                if "decode_stream" in name:
+                if "decode_stream" in name or "decode_prime" in name:
                     per[(_short(name), cn)][did] += v
             for (k, cn), dd in per.items():
                 last = [v for _, v in sorted(dd.items())][-5:]
