@@ -577,7 +577,8 @@ def main():
 # the directories the commands below write.
 TRACE_WORKLOADS = ("verify", "batched", "qwen_gqa", "prime", "verify_f8", "batched_f8")
 TRAFFIC_WORKLOADS = ("verify", "batched", "qwen_gqa", "verify_f8", "batched_f8")
-PER_STEP = ("decode_stream", "decode_mfma", "combine_kernel", "combine_wave_kernel", "append_kernel", "set_kernel")
+PER_STEP = ("decode_stream", "decode_prime", "decode_mfma", "combine_kernel", "combine_wave_kernel", "append_kernel",
+            "set_kernel")
 
 
 def trace_command(wl):
@@ -666,6 +667,8 @@ def summarize_profiles(d):
         dec = sum(v for k, v in avg.items() if "decode_" in k)
         com = sum(v for k, v in avg.items() if "combine" in k)
         kv = w.kv_bytes_per_decode()
+        if dec <= 0:
+            raise RuntimeError(f"trace_{wl}: no decode kernel among the per-step kernels {sorted(avg)}")
         L += ["", f"- algorithmic K+V bytes per decode call: {kv}",
               f"- over the traced partials kernel: {kv / (dec * 1e-6) / 1e9:.1f} GB/s "
               f"({kv / (dec * 1e-6) / 1e9 / HBM_PEAK_GBPS:.4f} of 8 TB/s); over partials + combine "

@@ -26,12 +26,13 @@
 //     there: ds_read_b128 for the K blocks (A of S^T = K Q^T), pairs of
 //     ds_read_b64_tr_b16 for the V codes (B of P V, 8 keys of one dim per
 //     lane).
-//   * three raw tile buffers and two converted ones: while the waves score
-//     tile t they convert tile t + 1, whose rows have landed, and tiles t + 2
-//     and t + 3 are in flight; one workgroup barrier per tile.  The two waves
-//     that share a SIMD take the conversion and the products in opposite
-//     orders, so that one works the vector ALU while the other works the
-//     matrix cores.
+//   * three raw tile buffers and three converted ones, one workgroup barrier
+//     per tile: in the iteration of tile t a wave takes the scores of tile
+//     t + 1 on the matrix cores before the softmax and P V of tile t, the
+//     waves convert tile t + 2 (whose rows have landed), and tiles t + 3 and
+//     t + 4 are in flight.  The two waves that share a SIMD take the
+//     conversion and the products in opposite orders, so that one works the
+//     vector ALU while the other works the matrix cores.
 //   * ranges: a tile with a K step of 2^8 or more stores its K products
 //     times 2^-E (and its scores are multiplied back by 2^E), a tile with a
 //     V step of 2^7 or more its steps times 2^-E (and the P V accumulators

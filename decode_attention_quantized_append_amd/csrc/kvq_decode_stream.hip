@@ -30,8 +30,8 @@
 //   * the V operand comes straight from the q5_1 bytes: ds_read_b64_tr_b8 of
 //     the 16 nibble bytes of 8 keys gives a lane the codes of its dimension
 //     (low nibble) and of dimension + 16 (high nibble); a second transposed
-//     read of the block headers gives the high-bit bytes, which ds_bpermute
-//     hands to the lanes that need them.
+//     read of the block headers gives the high-bit bytes, which DPP row
+//     broadcasts hand to the lanes that need them.
 //   * the q5_1 step multiplies P per block (P' = P * step, fp16); the offset
 //     term sum_key P * m is one more MFMA per tile against the offsets.
 namespace stream {
