@@ -258,3 +258,54 @@ def test_rollback_replays_stop_at_the_floor():
     assert flat.gpu.device_lengths()[:2] == ([0, 0], [0, 0])
     ln, bs, _ = ring.gpu.device_lengths()
     assert bs == br and ln == [br[0] + 16]
+
+
+@pytest.mark.parametrize("window", [0, 200])
+def test_graph_mode_prompt_chunks_replay(window):
+    """Prompt chunks in graph mode: ONE captured step (append a chunk of 48
+    rows per session, decode all 48 rows causally on the prime kernel, add the
+    attention importance) replayed as the lengths grow by 48 per replay, each
+    replay's output, lse and importance against the oracle's at that length."""
+    rng = np.random.default_rng(480 + window)
+    B, H, Hkv, hd, T, cap = 2, 16, 4, 128, 48, 1000
+    pre = [300, 150]
+    p = Pair(B, H, Hkv, hd, cap, window, 0)
+    p.append(bf16_normal(rng, (B, 300, Hkv, hd)), bf16_normal(rng, (B, 300, Hkv, hd)), pre)
+    g = p.gpu
+    g.set_graph_mode(True)
+    scale = hd ** -0.5
+    kd = torch.zeros((B, T, Hkv, hd), dtype=torch.bfloat16, device=DEV)
+    vd, qd = torch.zeros_like(kd), torch.zeros((B, T, H, hd), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((B, T, H, hd), dtype=torch.float32, device=DEV)
+    lse = torch.empty((B, T, H), dtype=torch.float32, device=DEV)
+    imp = torch.zeros((B, cap), dtype=torch.float32, device=DEV)
+    g.workspace(T)
+    torch.cuda.synchronize(DEV)
+    graph = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream(DEV)
+    cs.wait_stream(torch.cuda.current_stream(DEV))
+    with torch.cuda.graph(graph, stream=cs):
+        g.append(kd, vd)
+        g.decode(qd, scale, out=out, lse=lse)
+        g.importance(qd, scale, lse, imp)
+    torch.cuda.synchronize(DEV)
+    for r in range(8):
+        kn, vn = bf16_normal(rng, (B, T, Hkv, hd)), bf16_normal(rng, (B, T, Hkv, hd))
+        q = bf16_normal(rng, (B, T, H, hd))
+        kd.copy_(to_dev(kn, "bf16"))
+        vd.copy_(to_dev(vn, "bf16"))
+        qd.copy_(to_dev(q, "bf16"))
+        out.fill_(float("nan"))
+        imp.zero_()
+        graph.replay()
+        torch.cuda.synchronize(DEV)
+        p.ref.append(kn, vn)
+        ref_o, ref_lse = p.ref.attention(q, scale=scale)
+        assert_close(out.cpu().numpy(), ref_o, f"replay {r} out")
+        assert_close(lse.cpu().numpy(), ref_lse, f"replay {r} lse")
+        assert_close(imp.cpu().numpy(), p.ref.importance(q, scale=scale), f"replay {r} importance")
+    ln, bs, overflow = g.device_lengths()
+    assert ln == p.ref.len.tolist() and bs == p.ref.base.tolist() and overflow == 0
+    g.set_host_lengths(ln, bs)
+    p.check_mirror()
+    p.check_planes()
