@@ -344,10 +344,14 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
         v[k] = (s0 + k * G < ns) ? *reinterpret_cast<const float4*>(o + (size_t)(s0 + k * G) * so)
                                  : make_float4(0.f, 0.f, 0.f, 0.f);
 
-    // M = max over splits (and the sink); weights; Z
-    float m_loc = -INFINITY;
-    for (int s = tid; s < ns; s += NT) m_loc = fmaxf(m_loc, p.part_ml[2 * (e0 + s * stride)]);
-    float mw = wave_max(m_loc);
+    // thread s < ns holds split s's (m, l) (at most kMaxSplits = 1024 splits,
+    // and fewer than 64 for the 256-thread variant); M = max over splits (and
+    // the sink); weights; Z
+    static_assert(kMaxSplits <= 1024, "a thread per split");
+    const bool mine = tid < ns;
+    const float2 mlv = mine ? *reinterpret_cast<const float2*>(p.part_ml + 2 * (e0 + tid * stride))
+                            : make_float2(-INFINITY, 0.0f);
+    float mw = wave_max(mlv.x);
     if (lane == 0) red[0][wave] = mw;
     __syncthreads();
     float M = red[0][0];
@@ -355,14 +359,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
     const bool has_sink = p.sinks != nullptr;
     const float sink = has_sink ? p.sinks[h] : 0.0f;
     if (has_sink) M = fmaxf(M, sink);
-    float z = 0.0f;
-    for (int s = tid; s < ns; s += NT) {
-        const float m = p.part_ml[2 * (e0 + s * stride)];
-        const float w = (m == -INFINITY) ? 0.0f : expf(m - M);
-        wts[s] = w;
-        z = fmaf(w, p.part_ml[2 * (e0 + s * stride) + 1], z);
-    }
-    z = wave_sum(z);
+    const float w = (mlv.x == -INFINITY) ? 0.0f : expf(mlv.x - M);
+    if (mine) wts[tid] = w;
+    float z = wave_sum(w * mlv.y);
     if (lane == 0) red[1][wave] = z;
     __syncthreads();   // wts and red are complete
     float Z = 0.0f;
@@ -567,16 +566,20 @@ __global__ __launch_bounds__(64 * kImpWaves) void importance_kernel(ImportancePa
     }
 }
 
-// Few splits (at most 16): one wave per (session, row t, Q head h), four per
-// workgroup.  Lane s < ns holds split s's (m, l) and weight e^(m_s - M); lane
-// (sg, dq) sums the 4-float slice dq of o over the splits sg, sg + G, ...
-// (G = 64 / (hd / 4) groups), the weights handed over by shuffles; the group
-// sums meet by shuffles in a fixed order.  The sink enters once, in M and Z.
+// Few splits (at most 16) and head_dim 64, 128 or 256: hd / 4 lanes per
+// (session, row t, Q head h) item, 64 / (hd / 4) items per wave, four waves
+// per workgroup.  Every lane reads all of its item's (m, l) pairs (the same
+// addresses across the item's lanes) and its 4-float slice of every split's
+// o in one round of loads, then forms M (the sink included), the weights
+// e^(m_s - M), Z and the weighted sum itself: no cross-lane traffic.  The
+// sink enters once, in M and Z.
 constexpr int kCombineWaveSplits = 16;
 __global__ __launch_bounds__(256) void combine_wave_kernel(DecodeParams p) {
     const int lane = threadIdx.x & 63;
-    const int idx = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int nq = p.hd >> 2;                      // lanes per item
+    const int idx = (blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / nq) + lane / nq;
     if (idx >= p.B * p.T * p.H) return;
+    const int dq = lane % nq;
     const int h = idx % p.H;
     const int t = (idx / p.H) % p.T;
     const int b = idx / (p.H * p.T);
@@ -586,54 +589,35 @@ __global__ __launch_bounds__(256) void combine_wave_kernel(DecodeParams p) {
     const int ns = min(p.splits, (len - org + p.chunk - 1) / p.chunk);
     const size_t stride = (size_t)p.T * p.H;
     const size_t e0 = ((size_t)b * p.splits * p.T + t) * p.H + h;
-    const int nq = p.hd >> 2, G = 64 / nq;
-    const int dq = lane % nq, sg = lane / nq;
-    // this lane's slices of o, requested before the weights are known
+    float2 ml[kCombineWaveSplits];
     float4 v[kCombineWaveSplits];
 #pragma unroll
     for (int k = 0; k < kCombineWaveSplits; ++k) {
-        const int sp = sg + k * G;
-        v[k] = (k * G < kCombineWaveSplits && sp < ns)
-                   ? *reinterpret_cast<const float4*>(p.part_o + (e0 + sp * stride) * p.hd + 4 * dq)
-                   : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    float m = -INFINITY, l = 0.0f;
-    if (lane < ns) {
-        const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + 2 * (e0 + lane * stride));
-        m = ml.x;
-        l = ml.y;
+        const bool live = k < ns;
+        ml[k] = live ? *reinterpret_cast<const float2*>(p.part_ml + 2 * (e0 + k * stride)) : make_float2(-INFINITY, 0.f);
+        v[k] = live ? *reinterpret_cast<const float4*>(p.part_o + (e0 + k * stride) * p.hd + 4 * dq)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     const bool has_sink = p.sinks != nullptr;
     const float sink = has_sink ? p.sinks[h] : 0.0f;
-    float M = wave_max(m);
-    if (has_sink) M = fmaxf(M, sink);
-    const float w = (m == -INFINITY) ? 0.0f : expf(m - M);
-    float Z = wave_sum(w * l);
-    if (has_sink) Z += expf(sink - M);
+    float M = has_sink ? sink : -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kCombineWaveSplits; ++k) M = fmaxf(M, ml[k].x);
+    float Z = has_sink ? expf(sink - M) : 0.0f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int k = 0; k < kCombineWaveSplits; ++k) {
-        const int sp = sg + k * G;
-        const float ws = __shfl(w, sp < 64 ? sp : 0);
-        if (k * G < kCombineWaveSplits && sp < ns) {
-            acc.x = fmaf(ws, v[k].x, acc.x);
-            acc.y = fmaf(ws, v[k].y, acc.y);
-            acc.z = fmaf(ws, v[k].z, acc.z);
-            acc.w = fmaf(ws, v[k].w, acc.w);
-        }
+        const float w = (ml[k].x == -INFINITY) ? 0.0f : expf(ml[k].x - M);
+        Z = fmaf(w, ml[k].y, Z);
+        acc.x = fmaf(w, v[k].x, acc.x);
+        acc.y = fmaf(w, v[k].y, acc.y);
+        acc.z = fmaf(w, v[k].z, acc.z);
+        acc.w = fmaf(w, v[k].w, acc.w);
     }
-    for (int off = nq; off < 64; off <<= 1) {   // the G group sums, same dq
-        acc.x += __shfl_xor(acc.x, off);
-        acc.y += __shfl_xor(acc.y, off);
-        acc.z += __shfl_xor(acc.z, off);
-        acc.w += __shfl_xor(acc.w, off);
-    }
-    if (sg == 0) {
-        const float invZ = 1.0f / Z;
-        acc.x *= invZ; acc.y *= invZ; acc.z *= invZ; acc.w *= invZ;
-        reinterpret_cast<float4*>(p.out + (((size_t)b * p.T + t) * p.H + h) * p.hd)[dq] = acc;
-    }
-    if (p.lse && lane == 0) p.lse[((size_t)b * p.T + t) * p.H + h] = M + logf(Z);
+    const float invZ = 1.0f / Z;
+    acc.x *= invZ; acc.y *= invZ; acc.z *= invZ; acc.w *= invZ;
+    reinterpret_cast<float4*>(p.out + (((size_t)b * p.T + t) * p.H + h) * p.hd)[dq] = acc;
+    if (p.lse && dq == 0) p.lse[((size_t)b * p.T + t) * p.H + h] = M + logf(Z);
 }
 
 // ---------------------------------------------------------------------------
@@ -648,11 +632,12 @@ int check(const char** err) {
 
 int launch_combine(const DecodeParams& p, hipStream_t st, const char** err) {
     const int items = p.B * p.T * p.H;
-    // a wave per item where the splits are few and a head's 4-float slices
-    // fill the wave in whole groups (head_dim 64, 128 or 256)
-    if (p.splits <= kCombineWaveSplits && (p.hd == 64 || p.hd == 128 || p.hd == 256))
-        hipLaunchKernelGGL(combine_wave_kernel, dim3((items + 3) / 4), dim3(256), 0, st, p);
-    else if (p.splits >= 64)
+    // hd / 4 lanes per item where the splits are few and an item's 4-float
+    // slices fill a wave in whole items (head_dim 64, 128 or 256)
+    if (p.splits <= kCombineWaveSplits && (p.hd == 64 || p.hd == 128 || p.hd == 256)) {
+        const int per_wg = 4 * (64 / (p.hd / 4));   // items per workgroup
+        hipLaunchKernelGGL(combine_wave_kernel, dim3((items + per_wg - 1) / per_wg), dim3(256), 0, st, p);
+    } else if (p.splits >= 64)
         hipLaunchKernelGGL(combine_kernel<1024>, dim3(p.B * p.T * p.H), dim3(1024), 0, st, p);
     else
         hipLaunchKernelGGL(combine_kernel<256>, dim3(p.B * p.T * p.H), dim3(256), 0, st, p);
