@@ -244,6 +244,8 @@ MANY = {
     "hd128_hpk1_T70_prime_window_f32": (1, 4, 4, 128, 70, [333], 40, True, "f32", (kvq.KVQ_DECODE_PRIME, 0)),
     "hd64_hpk8_T45_prime": (3, 16, 2, 64, 45, [45, 300, 1000], 0, True, "bf16", (kvq.KVQ_DECODE_PRIME, 0)),
     "hd128_T600_prime_window": (1, 8, 2, 128, 600, [2000], 512, False, "bf16", (kvq.KVQ_DECODE_PRIME, 0)),
+    "hd64_hpk32_T9_prime_sinks": (2, 32, 1, 64, 9, [200, 9], 0, True, "bf16", None),      # one row per group
+    "hd128_hpk3_T41_prime_window_f32": (2, 12, 4, 128, 41, [260, 100], 60, False, "f32", None),   # 30 of 32 rows
 }
 
 
