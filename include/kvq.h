@@ -218,16 +218,18 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache* h, int32_t T, size_t* byt
  * bytes, 256-byte aligned.  The committed length is read from len_d on the
  * device.  Requires len >= T for every session and H/Hkv <= 32.  Any T is
  * accepted (a prompt chunk attending causally, cortiq attend_group_upto with
- * many rows): decode workgroups take the rows in groups of 32/(H/Hkv) (the
- * launch's y index), and one combine folds all T rows; the workspace holds
- * the partials of all T rows.
+ * many rows): the rows go in groups of 32/(H/Hkv) (the launch's y index;
+ * from four groups on, with q8_0 / q5_1 rows at head_dim 64 or 128, eight
+ * groups share each workgroup and its converted KV tiles), and one combine
+ * folds all T rows; the workspace holds the partials of all T rows.
  * Input range: any finite queries and any q8_0 / q5_1 blocks (fp16 steps,
  * offsets and K scales up to 65504), as long as the scores scale * <q, k>
  * and the weighted V sums stay within binary32 range.  Query rows are
  * divided by a power of two before their fp16 cast (exact, so bf16 queries
  * keep every bit; fp32 queries keep about 22 bits as an fp16 high and low
- * part), and V steps of 2^7 or more switch the P V accumulator to units of
- * a power of two, so nothing overflows fp16.  The softmax weights enter
+ * part), V steps of 2^7 or more switch the P V accumulator to units of a
+ * power of two, and (prompt chunks) K steps of 2^8 or more scale a tile's K
+ * products by a power of two, so nothing overflows fp16.  The softmax weights enter
  * P V as fp16 (relative error 2^-11 each), so an output is within about
  * 2^-11 sum_j p_j |v_j| / sum_j p_j of the exact one.
  * Errors: EINVAL, ERANGE (a visible row was rebased away), EDEVICE. */
