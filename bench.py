@@ -575,7 +575,7 @@ def main():
 # profiles/: summaries of rocprofv3 runs of this script (kernel traces and the
 # FETCH_SIZE / WRITE_SIZE passes), rebuilt with --summarize-profiles DIR from
 # the directories the commands below write.
-TRACE_WORKLOADS = ("verify", "batched", "qwen_gqa", "prime", "verify_f8", "batched_f8")
+TRACE_WORKLOADS = ("verify", "batched", "qwen_gqa", "prime", "verify_f8", "batched_f8", "prime_f8")
 TRAFFIC_WORKLOADS = ("verify", "batched", "qwen_gqa", "verify_f8", "batched_f8")
 PER_STEP = ("decode_stream", "decode_prime", "decode_mfma", "combine_kernel", "combine_wave_kernel", "append_kernel",
             "set_kernel")

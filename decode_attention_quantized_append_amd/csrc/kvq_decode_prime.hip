@@ -22,7 +22,11 @@
 //     the steps and the offsets; as in the stream kernel each wave multiplies
 //     its fp16 P by the steps (P' = P * d, the A operand of P V) and takes
 //     the offset term sum_key P * m, with the row sums from a column of ones,
-//     as one more product.  Each wave reads its matrix-core operands from
+//     as one more product.  FP8 (e4m3) rows (memra-engine "Module cache",
+//     kv_fp8_on): K the same pairs (a code has 4 significant bits), V the
+//     codes' fp16 values (exact) with no offsets; rows past the loaded ones
+//     are written as zeros (e4m3 has NaN codes).  Each wave reads its
+//     matrix-core operands from
 //     there: ds_read_b128 for the K blocks (A of S^T = K Q^T), pairs of
 //     ds_read_b64_tr_b16 for the V codes (B of P V, 8 keys of one dim per
 //     lane).
@@ -33,7 +37,7 @@
 //     t + 4 are in flight.  The two waves that share a SIMD take the
 //     conversion and the products in opposite orders, so that one works the
 //     vector ALU while the other works the matrix cores.
-//   * ranges: a tile with a K step of 2^8 or more stores its K products
+//   * ranges: a tile with a K step of 2^8 (FP8: 2^7) or more stores its K products
 //     times 2^-E (and its scores are multiplied back by 2^E), a tile with a
 //     V step of 2^7 or more its steps times 2^-E (and the P V accumulators
 //     switch units), so that no fp16 product overflows; the query rows are
@@ -67,9 +71,9 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
     }
 }
 
-template <int NB, bool QLO>
+template <int NB, bool QLO, bool F8>
 __global__ __launch_bounds__(64 * kWaves, 1) void decode_prime(DecodeParams p) {
-    using LY = PrimeLayout<NB>;
+    using LY = PrimeLayout<NB, F8>;
     static_assert(LY::BYTES <= kLdsBytes, "the prime layout must fit a CU's LDS");
     using WN = typename LY::WN;
     constexpr int HD = LY::HD;
@@ -107,12 +111,17 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_prime(DecodeParams p) {
     const int R = Tq * p.hpk;
 
     // ---- tile loads: instruction i of a tile's NIT (K pieces, then V pieces)
-    // is issued by wave i mod 8
-    const uint8_t* const kwin0 = p.k_planes + (int64_t)b * p.k_stride;
-    const int kstart = g * NB * 34;
-    const int kofs = kstart & 15;
-    const uint8_t* const kwin = kwin0 + kstart - kofs;
-    const uint8_t* const vwin = p.v_planes + (int64_t)b * p.v_stride + g * NB * 24;
+    // is issued by wave i mod 8.  q8_0 / q5_1: the K blocks from the 16-byte
+    // boundary at or below them (kofs bytes before), the V blocks exactly.
+    // FP8 rows: the head's codes (16-byte aligned), then the 16-byte piece of
+    // the row's scale area that holds its NB scales (at sofs within it); the
+    // same for K and V.
+    const int kstart = F8 ? g * NB * 32 : g * NB * 34;
+    const int kofs = F8 ? 0 : (kstart & 15);
+    const int sofs = F8 ? (g * 2 * NB) & 15 : 0;
+    const int spiece = F8 ? p.Hkv * p.hd + ((g * 2 * NB) & ~15) : 0;
+    const uint8_t* const kwin = p.k_planes + (int64_t)b * p.k_stride + (F8 ? 0 : kstart - kofs);
+    const uint8_t* const vwin = p.v_planes + (int64_t)b * p.v_stride + (F8 ? 0 : g * NB * 24);
     // this wave's load instructions for the tile at t0: 0 past the last
     // tile, -1 for a partial tile (its wave-wide empty loads may be skipped,
     // so that only a wait for all loads is safe behind it)
@@ -128,13 +137,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_prime(DecodeParams p) {
         for (int i = wave; i < LY::NIT; i += kWaves) {
             if (i < WN::NKI) {
                 const int pc = i * 64 + lane, row = pc / WN::KWP, col = pc - row * WN::KWP;
-                const uint32_t off = (uint32_t)(row * p.k_row + min(col, WN::KW - 1) * 16);
+                const uint32_t off = F8 ? (uint32_t)(row * p.k_row + (col < 2 * NB ? kstart + col * 16 : spiece))
+                                        : (uint32_t)(row * p.k_row + min(col, WN::KW - 1) * 16);
                 if (pc < nrows * WN::KWP)
                     stream::dma16(kwin + (int64_t)(t0 - base) * p.k_row, off, rb + LY::RK + i * 1024);
             } else {
                 const int x = i - WN::NKI;
                 const int pc = x * 64 + lane, row = pc / WN::VWP, col = pc - row * WN::VWP;
-                const uint32_t off = (uint32_t)(row * p.v_row + min(col, WN::VW - 1) * 16);
+                const uint32_t off = F8 ? (uint32_t)(row * p.v_row + (col < 2 * NB ? kstart + col * 16 : spiece))
+                                        : (uint32_t)(row * p.v_row + min(col, WN::VW - 1) * 16);
                 if (pc < nrows * WN::VWP)
                     stream::dma16(vwin + (int64_t)(t0 - base) * p.v_row, off, rb + LY::RV + x * 1024);
             }
@@ -143,20 +154,26 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_prime(DecodeParams p) {
 
     // ---- conversion of one tile's raw rows into fp16 operands (all waves).
     // First every wave finds the tile's range shifts itself (the same values
-    // in every wave): E_k for K steps of 2^8 or more, E_v for V steps of 2^7
-    // or more (fp16 bits 0x5C00, 0x5800).  Rows past c1 were not loaded:
-    // their steps and offsets are taken as 0, so that their products are 0
-    // whatever stale bytes their codes hold.
+    // in every wave): E_k for K steps of 2^8 or more (FP8: 2^7, codes up to
+    // 448), E_v for V steps of 2^7 or more (fp16 bits 0x5C00, 0x5800).  Rows
+    // past c1 were not loaded: their steps and offsets are taken as 0, so
+    // that their products are 0 whatever stale bytes their q8_0 / q5_1 codes
+    // hold, and their FP8 codes (which may be NaN) as 0.
     uint32_t ksh_next = 0, vsh_next = 0;     // the shifts of the tile last converted
     auto convert = [&](int t0, int rbuf, int cbuf) {
         const uint8_t* const rk = smem + rbuf * LY::RAW + LY::RK;
         const uint8_t* const rv = smem + rbuf * LY::RAW + LY::RV;
         uint8_t* const cv = smem + kRawBufs * LY::RAW + cbuf * LY::CONV;
         const int tid = threadIdx.x;
+        // a K row's step (its fp16 bits, sign cleared); a V row's step in the
+        // low half and (q5_1) its offset in the high half
         auto kstep = [&](int key, int blk) -> uint32_t {
-            return t0 + key < c1 ? *reinterpret_cast<const uint16_t*>(rk + key * WN::KSTR + kofs + blk * 34) & 0x7FFFu : 0u;
+            const int o = F8 ? key * WN::KSTR + 32 * NB + sofs + 2 * blk : key * WN::KSTR + kofs + blk * 34;
+            return t0 + key < c1 ? *reinterpret_cast<const uint16_t*>(rk + o) & 0x7FFFu : 0u;
         };
         auto vstepm = [&](int key, int blk) -> uint32_t {
+            if constexpr (F8)
+                return t0 + key < c1 ? *reinterpret_cast<const uint16_t*>(rv + key * WN::VSTR + 32 * NB + sofs + 2 * blk) : 0u;
             return t0 + key < c1 ? *reinterpret_cast<const uint32_t*>(rv + key * WN::VSTR + blk * 24) : 0u;
         };
         {
@@ -169,21 +186,29 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_prime(DecodeParams p) {
                     vm = max(vm, vstepm(u / NB, u % NB) & 0x7FFFu);
                 }
             }
-            ksh_next = __any(km >= 0x5C00u) ? (dec::wave_max_u32(km) >> 10) - 22u : 0u;
+            constexpr uint32_t kbig = F8 ? 0x5800u : 0x5C00u, kexp = F8 ? 21u : 22u;
+            ksh_next = __any(km >= kbig) ? (dec::wave_max_u32(km) >> 10) - kexp : 0u;
             vsh_next = __any(vm >= 0x5800u) ? (dec::wave_max_u32(vm) >> 10) - 21u : 0u;
         }
         const _Float16 kdown = (_Float16)dec::pow2(-(int)ksh_next);
         // K: task (key, blk, quarter) -> 8 products d * c as hi + lo
         for (int u = tid; u < kTile * NB * 4; u += 64 * kWaves) {
             const int key = u / (NB * 4), rem = u - key * (NB * 4), blk = rem >> 2, qq = rem & 3;
-            const int ca = key * WN::KSTR + kofs + blk * 34 + 2 + 8 * qq;
-            const uint32_t* const w = reinterpret_cast<const uint32_t*>(rk + (ca & ~3));
-            const uint32_t sh = (uint32_t)(ca & 3) * 8;
-            const h8 c = dec::k_codes_f16(__builtin_amdgcn_alignbit(w[1], w[0], sh), __builtin_amdgcn_alignbit(w[2], w[1], sh));
+            h8 c;
+            if constexpr (F8) {
+                const uint2 c8 = t0 + key < c1 ? *reinterpret_cast<const uint2*>(rk + key * WN::KSTR + blk * 32 + 8 * qq)
+                                               : make_uint2(0u, 0u);
+                c = stream::e4m3_codes(c8.x, c8.y);
+            } else {
+                const int ca = key * WN::KSTR + kofs + blk * 34 + 2 + 8 * qq;
+                const uint32_t* const w = reinterpret_cast<const uint32_t*>(rk + (ca & ~3));
+                const uint32_t sh = (uint32_t)(ca & 3) * 8;
+                c = dec::k_codes_f16(__builtin_amdgcn_alignbit(w[1], w[0], sh), __builtin_amdgcn_alignbit(w[2], w[1], sh));
+            }
             const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)kstep(key, blk)) * kdown;
             const h8 dv = {d, d, d, d, d, d, d, d};
             const h8 hi = c * dv;
-            const h8 lo = __builtin_elementwise_fma(c, dv, -hi);   // exact: c * d - hi fits in fp16
+            const h8 lo = __builtin_elementwise_fma(c, dv, -hi);   // c * d - hi fits in fp16 (exactly, unless tiny)
             const int o = key * LY::ROWH + (blk * 32 + 8 * qq) * 2;
             *reinterpret_cast<h8*>(cv + LY::KH + o) = hi;
             *reinterpret_cast<h8*>(cv + LY::KL + o) = lo;
@@ -191,6 +216,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_prime(DecodeParams p) {
         // V: task (key, blk, part) -> dims 8 part .. 8 part + 7 of the block
         for (int u = tid; u < kTile * NB * 4; u += 64 * kWaves) {
             const int key = u / (NB * 4), rem = u - key * (NB * 4), blk = rem >> 2, part = rem & 3;
+            if constexpr (F8) {
+                const uint2 c8 = t0 + key < c1 ? *reinterpret_cast<const uint2*>(rv + key * WN::VSTR + blk * 32 + 8 * part)
+                                               : make_uint2(0u, 0u);
+                *reinterpret_cast<h8*>(cv + LY::VH + key * LY::ROWV + (blk * 32 + 8 * part) * 2) = stream::e4m3_codes(c8.x, c8.y);
+                continue;
+            }
             const uint8_t* const vb = rv + key * WN::VSTR + blk * 24;
             const uint2 nibw = *reinterpret_cast<const uint2*>(vb + 8 + 8 * (part & 1));
             const uint32_t qh = *reinterpret_cast<const uint32_t*>(vb + 4);
@@ -469,8 +500,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_prime(DecodeParams p) {
 
     if (!active) return;
     // ---- finish: row sums from the ones column; offsets into O (the q5_1
-    // code products carry 2^-24, P * step carries 2^-vsh)
-    const float ounit = dec::pow2(24 + vsh);
+    // code products carry 2^-24, FP8 ones none; P * step carries 2^-vsh)
+    const float ounit = dec::pow2((F8 ? 0 : 24) + vsh);
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
         const int src = 16 * (j16 >> 2) + NB;

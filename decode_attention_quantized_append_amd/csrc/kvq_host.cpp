@@ -223,12 +223,12 @@ int64_t span_of(const kvq_cache* h, int b, int32_t T) {
 // Groups of query rows from which the planner takes the prime kernel.
 constexpr int64_t kPrimeMinGroups = 4;
 
-// Is the prime kernel built for this shape: q8_0 / q5_1 rows, head_dim 64 or
-// 128, and more than one group of query rows.
+// Is the prime kernel built for this shape: head_dim 64 or 128 and more than
+// one group of query rows.
 bool prime_ok(const kvq_config& c, int R, int32_t T) {
     const int NB = c.head_dim / 32;
     const int hpk = c.n_q_heads / c.n_kv_heads;
-    return !is_f8(c) && (NB == 2 || NB == 4) && T > R / hpk;
+    return (NB == 2 || NB == 4) && T > R / hpk;
 }
 
 // Chooses the decode kernel and its tiling.  Returns false when a kernel or
@@ -252,11 +252,11 @@ bool choose_kernel(const kvq_cache* h, int R, int32_t T, bool f32_queries, Plan*
                         ceil_div(T, R / hpk) >= kPrimeMinGroups);
     if (prime) {
         if (!prime_ok(c, R, T)) return false;
-        if (!aligned_start_resident(h, T)) return true;   // the per-head kernel, as for the stream kernel
+        if (!aligned_start_resident(h, T)) return !is_f8(c);   // the per-head kernel, as for the stream kernel
         p->kernel = kvq::kPrime;
         p->gh = 1;
         p->rs = p->rg = p->ds = 1;
-        p->lds = kvq::prime_lds_bytes(NB);
+        p->lds = kvq::prime_lds_bytes(NB, is_f8(c));
         p->rows = kvq::kRowTile;
         return true;
     }

@@ -171,14 +171,22 @@ struct StreamWinF8 {
 // kPrimeGroups waves, one 32-row query group each, shares each KV tile.  Its
 // LDS for head_dim = 32 * NB: kPrimeRawBufs raw tile buffers (the stream
 // kernel's row windows, K rows then V rows) and kPrimeConvBufs converted ones (K step x
-// code as fp16 hi and lo parts, V codes as fp16 subnormals, V steps, V offset
-// rows with ones).
+// code as fp16 hi and lo parts, V codes as fp16 (q5_1: subnormals code x
+// 2^-24; FP8: their values), V steps, V offset rows with ones).
 constexpr int kPrimeGroups = 8;
 constexpr int kPrimeRawBufs = 3;    // raw tile buffers: two tiles in flight while one is converted
 constexpr int kPrimeConvBufs = 3;   // converted tiles: one in softmax and P V, one in scores, one being written
+template <int NB, bool F8>
+struct PrimeWin {
+    using type = StreamWin<NB>;
+};
 template <int NB>
+struct PrimeWin<NB, true> {
+    using type = StreamWinF8<NB>;
+};
+template <int NB, bool F8 = false>
 struct PrimeLayout {
-    using WN = StreamWin<NB>;
+    using WN = typename PrimeWin<NB, F8>::type;
     static constexpr int HD = NB * 32;
     static constexpr int RAW = kRowTile * (WN::KSTR + WN::VSTR);
     static constexpr int RK = 0, RV = kRowTile * WN::KSTR;
@@ -187,7 +195,7 @@ struct PrimeLayout {
     // 8, so that neither read meets a bank twice
     static constexpr int ROWH = HD * 2 + 16;
     static constexpr int ROWV = HD * 2 + 32;
-    static constexpr int VMS = WN::VMS;                         // offsets, then ones
+    static constexpr int VMS = (NB + 4) & ~3;                   // offsets (0 for FP8 rows), then ones
     static constexpr int KH = 0;                                // fp16 [32][HD] K products, high parts
     static constexpr int KL = KH + kRowTile * ROWH;             // fp16 [32][HD] K products, low parts
     static constexpr int VH = KL + kRowTile * ROWH;             // fp16 [32][HD] V codes * 2^-24
@@ -198,7 +206,8 @@ struct PrimeLayout {
     static constexpr int NIT = WN::NKI + WN::NVI;               // load instructions per tile
     static_assert(RAW % 16 == 0 && CONV % 16 == 0 && ROWH % 16 == 0 && ROWV % 16 == 0, "16-byte alignment");
 };
-inline int prime_lds_bytes(int NB) {
+inline int prime_lds_bytes(int NB, bool f8 = false) {
+    if (f8) return NB == 2 ? PrimeLayout<2, true>::BYTES : NB == 4 ? PrimeLayout<4, true>::BYTES : 0;
     return NB == 2 ? PrimeLayout<2>::BYTES : NB == 4 ? PrimeLayout<4>::BYTES : 0;
 }
 

@@ -680,12 +680,12 @@ int launch_stream_t(const DecodeParams& p, hipStream_t st, const char** err) {
     return check(err);
 }
 
-template <int NB, bool QLO>
+template <int NB, bool QLO, bool F8>
 int launch_prime_t(const DecodeParams& p, hipStream_t st, const char** err) {
-    constexpr int lds = PrimeLayout<NB>::BYTES;
+    constexpr int lds = PrimeLayout<NB, F8>::BYTES;
     static bool configured = false;
     if (!configured) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&prime::decode_prime<NB, QLO>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&prime::decode_prime<NB, QLO, F8>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess) {
             *err = "cannot raise the LDS limit of the decode kernel";
             return 1;
@@ -695,7 +695,7 @@ int launch_prime_t(const DecodeParams& p, hipStream_t st, const char** err) {
     const int items = std::max(1, p.units) * p.Hkv;
     const int grid = (items + 7) & ~7;
     const int groups = (p.T + p.Tg - 1) / p.Tg;
-    hipLaunchKernelGGL((prime::decode_prime<NB, QLO>), dim3(grid, (groups + kPrimeGroups - 1) / kPrimeGroups),
+    hipLaunchKernelGGL((prime::decode_prime<NB, QLO, F8>), dim3(grid, (groups + kPrimeGroups - 1) / kPrimeGroups),
                        dim3(64 * kPrimeGroups), lds, st, p);
     return check(err);
 }
@@ -821,16 +821,16 @@ int launch_append(const AppendParams& p, void* stream, const char** err) {
 namespace {
 int launch_partials(const DecodeParams& p, hipStream_t st, const char** err) {
     if (p.kernel == kPrime) {
-        if (p.f8) {
-            *err = "the prime decode reads q8_0 / q5_1 blocks only";
-            return 1;
-        }
         const bool qlo = p.dtype == 0;
-        switch (p.hd / 32) {
-            case 2: return qlo ? launch_prime_t<2, true>(p, st, err) : launch_prime_t<2, false>(p, st, err);
-            case 4: return qlo ? launch_prime_t<4, true>(p, st, err) : launch_prime_t<4, false>(p, st, err);
+#define KVQ_PRIME(NB, F8) return qlo ? launch_prime_t<NB, true, F8>(p, st, err) : launch_prime_t<NB, false, F8>(p, st, err)
+        switch ((p.hd / 32) * 2 + (p.f8 ? 1 : 0)) {
+            case 4: KVQ_PRIME(2, false);
+            case 5: KVQ_PRIME(2, true);
+            case 8: KVQ_PRIME(4, false);
+            case 9: KVQ_PRIME(4, true);
             default: *err = "the prime decode supports head_dim 64 and 128"; return 1;
         }
+#undef KVQ_PRIME
     }
     if (p.kernel == kStream) {
         switch (p.hd / 32) {

@@ -28,6 +28,9 @@ Workloads (one attention layer each):
             sliding window, at 32768 rows, served from a 5118-row ring that
             advances 512 rows at a time (not one of the five measured
             configurations: the chunked prime of a long prompt)
+  verify_f8, batched_f8, prime_f8
+            the verify, batched and prime inputs (the same seeds) held as
+            FP8 (e4m3) K and V rows
 The k/v distribution named "as config 1" for the batched and verify shapes
 is read as the tiny shape's N(0,1); ``kv_dist="outlier"`` selects the other
 reading (the qwen_gqa distribution).
@@ -230,6 +233,9 @@ WORKLOADS = {
                           rollback_keep=3, fmt="e4m3"),
     "batched_f8": Workload("batched_f8", 103, B=16, H=40, Hkv=8, hd=128, T=1, cached=0,
                            ragged=(1024, 32768), fmt="e4m3"),
+    "prime_f8": Workload("prime_f8", 106, B=1, H=32, Hkv=8, hd=128, T=512, cached=32768,
+                         window=4096, ring_cap=4096 + 512 + 512 - 2, ring_step=512, kv_dist="outlier",
+                         fmt="e4m3"),
 }
 
 

@@ -315,8 +315,8 @@ typedef enum kvq_decode_kernel {
     KVQ_DECODE_PER_HEAD = 1,    /* one KV head per workgroup, any head_dim */
     KVQ_DECODE_STREAM = 3,      /* one or two waves per KV head, each streaming its rows through LDS */
     KVQ_DECODE_PRIME = 4        /* many query rows per KV head (a prompt chunk): eight groups of query
-                                 * rows share each KV tile, converted once; q8_0 / q5_1, head_dim 64
-                                 * or 128, more than one group of query rows */
+                                 * rows share each KV tile, converted once; q8_0 / q5_1 or FP8 rows,
+                                 * head_dim 64 or 128, more than one group of query rows */
 } kvq_decode_kernel;
 
 /* Tuning: which kernel kvq_decode runs and how it tiles the cache (the
@@ -328,8 +328,8 @@ typedef enum kvq_decode_kernel {
  * holding both 16-row tiles or 2 row-group waves (17 to 32 rows), or 3 = two
  * waves each taking half of a 128- or 256-dim head for all rows (17 to 32
  * rows); 0 = chosen per call.  The stream kernel needs head_dim 64, 128 or
- * 256; the prime kernel (no head_group, no sub_tiles) q8_0 / q5_1 rows,
- * head_dim 64 or 128 and more than one group of 32 / hpk query rows.  A
+ * 256; the prime kernel (no head_group, no sub_tiles) head_dim 64 or 128
+ * and more than one group of 32 / hpk query rows.  A
  * kernel or tiling that does not fit a call's shape makes that kvq_decode
  * fail with EINVAL, except that a session whose first visible row, rounded
  * down to 32, was rebased away is served by the per-head kernel.  The

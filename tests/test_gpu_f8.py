@@ -3,8 +3,9 @@ page, kv_fp8_on) through the C ABI against the oracle: FP8 rows (the codes of
 a row's blocks, then their fp16 scales) byte for byte after every append, and
 decode outputs and log-sum-exps within |gpu - oracle| <= 2e-3 + 1e-2 |oracle|
 (2e-3 relative to the V scale for large V, as in test_gpu_range) on the
-layouts the stream kernel has, every e4m3 code read back, attention
-importance, and the large-V / extreme-query range.
+layouts the stream kernel has and on prompt chunks (the prime kernel),
+every e4m3 code read back, attention importance, and the large-V, large- and
+tiny-K and extreme-query range.
 """
 import numpy as np
 import pytest
@@ -99,10 +100,17 @@ SHAPES = {
     "hd256_rowtiles": (1, 16, 4, 256, 8, [300], 0, 320, 0, False, "bf16", False, (kvq.KVQ_DECODE_STREAM, 0, 1)),
     "hd128_headgroup2": (2, 32, 8, 128, 2, [900, 161], 0, 1000, 0, True, "f32", True, (kvq.KVQ_DECODE_STREAM, 2, 0)),
     "prime_T100": (1, 32, 8, 128, 100, [700], 300, 720, 0, True, "bf16", True, None),
+    # more prompt chunks on the prime kernel: head_dim 64 with fp32 inputs, a
+    # sliding-window ring, one query row per group (32 query heads per KV
+    # head), 30 of 32 rows per group (3 query heads per KV head)
+    "prime_hd64_f32": (2, 16, 4, 64, 40, [500, 90], 0, 560, 0, False, "f32", False, (kvq.KVQ_DECODE_PRIME, 0, 0)),
+    "prime_ring": (2, 8, 2, 64, 40, [600, 300], 200, 400, 32, False, "f32", False, (kvq.KVQ_DECODE_PRIME, 0, 0)),
+    "prime_hpk32_sinks": (2, 32, 1, 64, 9, [200, 9], 0, 220, 0, True, "bf16", False, None),
+    "prime_hd128_hpk3_window": (2, 12, 4, 128, 41, [260, 100], 60, 280, 0, False, "f32", True, None),
 }
 
 
-def build(name, seed=0, v_scale=1.0):
+def build(name, seed=0, v_scale=1.0, k_scale=1.0):
     B, H, Hkv, hd, T, lens, window, cap, step, sinks, io, outl, tiling = SHAPES[name]
     rng = np.random.default_rng(seed + 17 * len(name))
     p = Pair(B, H, Hkv, hd, cap, window, step, io=io, fmt=F8)
@@ -117,9 +125,15 @@ def build(name, seed=0, v_scale=1.0):
         if v_scale != 1.0:
             v = v * np.float32(v_scale)
             v = round_bf16(v) if io == "bf16" else v
+        if k_scale != 1.0:
+            k = k * np.float32(k_scale)
+            k = round_bf16(k) if io == "bf16" else k
         p.append(k, v, n.tolist())
         done += n
     q = qrows(rng, B, T, H, hd, io)
+    if k_scale != 1.0:
+        q = q * np.float32(1.0 / k_scale)
+        q = round_bf16(q) if io == "bf16" else q
     s = rng.standard_normal(H).astype(np.float32) if sinks else None
     return p, q, s, float(np.float32(1 / np.sqrt(hd)))
 
@@ -132,12 +146,35 @@ def test_f8_decode_parity(name):
     p.decode(q, scale, sinks=s, what=f"f8 {name}")
 
 
-@pytest.mark.parametrize("name", ["verify_dimhalves", "qwen_gqa", "hd64_rowgroups"])
+@pytest.mark.parametrize("name", ["verify_dimhalves", "qwen_gqa", "hd64_rowgroups", "prime_T100", "prime_hd64_f32"])
 def test_f8_decode_large_v(name):
     """V blocks of range up to 3e5 (steps to about 700, scale shift on)."""
     p, q, s, scale = build(name, seed=3, v_scale=1e5)
     atol = ATOL * max(1.0, 1.05 * p.vmax / 4.0)
     p.decode(q, scale, sinks=s, what=f"f8 {name} large v", atol=atol)
+
+
+@pytest.mark.parametrize("k_scale", [3e4, 1e-5])
+@pytest.mark.parametrize("name", ["qwen_gqa", "verify_dimhalves", "prime_T100", "prime_hd64_f32"])
+def test_f8_decode_large_and_tiny_k(name, k_scale):
+    """K rows times 3e4 (block scales of about 2^8, past the prime kernel's
+    K shift at 2^7) or times 1e-5 (subnormal fp16 scales), with the queries
+    divided by the same factor so that the scores keep their size."""
+    p, q, s, scale = build(name, seed=5, k_scale=k_scale)
+    print(f"\ncase {name} k x{k_scale:g}", flush=True)
+    p.decode(q, scale, sinks=s, what=f"f8 {name} k x{k_scale:g}")
+
+
+@pytest.mark.parametrize("name", ["qwen_gqa", "verify_f32_sinks", "prime_T100", "prime_hd64_f32"])
+def test_f8_decode_extreme_queries(name):
+    """Query rows of magnitudes 1e5, 1e-6, 1e-30, 0 and single spikes mixed
+    within every group of rows (the classes of test_gpu_range)."""
+    from test_gpu_range import extreme_q
+    p, _, s, scale = build(name, seed=7)
+    B, H, Hkv, hd, T, *_ = SHAPES[name]
+    q = extreme_q(np.random.default_rng(11), B, T, H, hd, SHAPES[name][10])
+    print(f"\ncase {name} extreme q", flush=True)
+    p.decode(q, scale, sinks=s, what=f"f8 {name} extreme q")
 
 
 def test_f8_decode_every_code():

@@ -33,7 +33,7 @@ def step(w, p, i):
 
 
 @pytest.mark.parametrize("name", ["tiny", "qwen_gqa", "batched", "sink_ring", "verify", "prime", "verify_f8",
-                                  "batched_f8"])
+                                  "batched_f8", "prime_f8"])
 def test_full_size(name):
     w, p = setup(name)
     q, s = step(w, p, 0)

@@ -537,12 +537,18 @@ def test_decode_prime_choice(lib):
     assert log(lib) == []
     assert err(lib, kvq.kvq_set_decode_tiling, h, kvq.KVQ_DECODE_PRIME, 2, 0) == E
     assert err(lib, kvq.kvq_set_decode_tiling, h, kvq.KVQ_DECODE_PRIME, 0, 1) == E
-    # head_dim 64: a smaller layout; 256 and FP8 rows: the stream kernel
+    # head_dim 64: a smaller layout; FP8 rows: raw tiles of codes plus a
+    # 16-byte scale piece per row; 256: the stream kernel
     h = create(lib, n_seqs=2, n_q_heads=16, n_kv_heads=4, head_dim=64, capacity=3000)
     kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 2000, None, 0, lib)
     p = plan_of(lib, h, T=100, dtype=kvq.KVQ_F32)
     assert (p["kernel"], p["lds"], p["groups"]) == (PRIME, 56448, 13)
-    for kw in (dict(head_dim=256, n_q_heads=16, n_kv_heads=4), dict(head_dim=128, fmt="e4m3")):
+    for hd, lds in ((128, 109824), (64, 59520)):
+        h = create(lib, n_seqs=1, n_q_heads=32, n_kv_heads=8, head_dim=hd, capacity=3000, fmt="e4m3")
+        kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 2000, None, 0, lib)
+        p = plan_of(lib, h, T=200)
+        assert (p["kernel"], p["lds"]) == (PRIME, lds)
+    for kw in (dict(head_dim=256, n_q_heads=16, n_kv_heads=4),):
         h = create(lib, n_seqs=1, capacity=3000, **kw)
         kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 2000, None, 0, lib)
         assert plan_of(lib, h, T=200)["kernel"] == STREAM
