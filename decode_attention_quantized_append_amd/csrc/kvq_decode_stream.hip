@@ -192,6 +192,9 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
     const int half = DS == 2 ? wave & 1 : 0;          // DS = 2: this wave's half of the dims
     const int str = RS > 1 ? wv / gh : 0;        // row stream
     const int rb = RG > 1 ? (wv / gh) * 16 : 0;     // first query row of this wave
+    // row tile rt holds query rows rb + 16 (rt ^ rsw) ..: with dim halves
+    // each wave's row tile 0 is the one whose softmax it takes
+    const int rsw = DS == 2 ? half : 0;
 
     const int W = gridDim.x, wid = blockIdx.x;
     const int L = (wid & 7) * (W >> 3) + (wid >> 3);
@@ -303,7 +306,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
         mrow[rt] = kNoMax;
         lsum[rt] = 0.0f;
         vis_lo[rt] = vis_hi[rt] = 0;
-        const int r = rb + rt * 16 + j16;
+        const int r = rb + (rt ^ rsw) * 16 + j16;
         if (r < R) {
             vis_hi[rt] = len - p.T + tq0 + r / p.hpk + 1;
             vis_lo[rt] = p.window > 0 ? max(0, vis_hi[rt] - p.window) : 0;
@@ -363,7 +366,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
         }
     }
 
-    // Q rows rt*16 + j16 as the B operand of S^T = K Q^T, read while the
+    // Q rows (tile rt, j16) as the B operand of S^T = K Q^T, read while the
     // first tile's rows are in flight.  The wave's rows are divided by the
     // power of two that puts their largest |q| in [2^14, 2^15) (dec::q_down;
     // with dim halves the exponent covers both halves, so that their partial
@@ -375,7 +378,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
     uint32_t mag = 0;
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
-        const int r = rb + rt * 16 + j16;
+        const int r = rb + (rt ^ rsw) * 16 + j16;
         const bool real = r < R;
         const int t = real ? tq0 + r / p.hpk : 0, hh = real ? r % p.hpk : 0;
         const size_t row0q = (((size_t)b * p.T + t) * p.H + g * p.hpk + hh) * HDR + 8 * q4;
@@ -469,7 +472,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
         }
         if constexpr (SH) lds_barrier(); else dec::lds_order();
 
-        // ---- scores S^T: sv[rt][h][i] = S[row rt*16 + j16][key 16h + 4*q4 + i] (base 2)
+        // ---- scores S^T: sv[rt][h][i] = S[row of tile rt, j16][key 16h + 4*q4 + i] (base 2)
 #pragma unroll
         for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
@@ -523,28 +526,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
         if constexpr (SH) {
             lds_barrier();                          // both copies of K(t) are read
             if (has2) issue_k(tn + kTile, tb);
-        } else if constexpr (DS == 2) {
-            // the two halves' partial sums: each wave adds the other's to its
-            // own (a + b == b + a, so both hold the same scores)
-            f4* const xo = reinterpret_cast<f4*>(wb + WN::BYTES) + (it & 1) * (RTW * 2 * 64);
-            const f4* const xp =
-                reinterpret_cast<const f4*>(smem + (wave ^ 1) * WSTR + WN::BYTES) + (it & 1) * (RTW * 2 * 64);
-#pragma unroll
-            for (int rt = 0; rt < RTW; ++rt)
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    xo[(rt * 2 + h) * 64 + lane] = (f4){sv[rt][h][0], sv[rt][h][1], sv[rt][h][2], sv[rt][h][3]};
-            lds_barrier();
-            if (next) issue_k(tn, tb);
-#pragma unroll
-            for (int rt = 0; rt < RTW; ++rt)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const f4 y = xp[(rt * 2 + h) * 64 + lane];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) sv[rt][h][i] += y[i];
-                }
-        } else {
+        } else if constexpr (DS == 1) {
             if (gh * rs > 1) __builtin_amdgcn_s_barrier();
             if (next) issue_k(tn, tb);
         }
@@ -554,9 +536,24 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
         // Edge tiles: scores of keys outside a row's visible range become
         // -inf (one unsigned compare per key, in one branch for the tile).
         const bool interior = t0 >= full_lo && t0 + kTile <= full_hi;
-        if (!interior) {
+        h8 pu[RTW];   // P in fp16, the A operand of the products with V
+        // the O and row-sum accumulators of row tile rt times alpha (each
+        // lane holds the factor of its row j16)
+        auto rescale_rows = [&](auto rt_c, float alpha) {
+            constexpr int rt = decltype(rt_c)::value;
+            float ar[4];
 #pragma unroll
-            for (int rt = 0; rt < RTW; ++rt) {
+            for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * q4 + i);   // O rows 4*q4 + i
+#pragma unroll
+            for (int dt = 0; dt < 2 * NB; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) oacc[rt][dt][i] *= ar[i];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) macc[rt][i] *= ar[i];
+        };
+        auto softmax_rows = [&](auto rt_c) {
+            constexpr int rt = decltype(rt_c)::value;
+            if (!interior) {
                 const int jb = t0 + 4 * q4 - vis_lo[rt];
                 const uint32_t span = (uint32_t)(vis_hi[rt] - vis_lo[rt]);
 #pragma unroll
@@ -565,10 +562,6 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
                     for (int i = 0; i < 4; ++i)
                         sv[rt][h][i] = (uint32_t)(jb + 16 * h + i) < span ? sv[rt][h][i] : -INFINITY;
             }
-        }
-        h8 pu[RTW];   // P in fp16, the A operand of the products with V
-#pragma unroll
-        for (int rt = 0; rt < RTW; ++rt) {
             float smax = -INFINITY;
 #pragma unroll
             for (int h = 0; h < 2; ++h)
@@ -581,15 +574,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
                 const bool move = mt > mrow[rt] + 8.0f;
                 const float alpha = move ? __builtin_amdgcn_exp2f(mrow[rt] - mt) : 1.0f;
                 mrow[rt] = move ? mt : mrow[rt];
-                float ar[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * q4 + i);   // O rows 4*q4 + i
-#pragma unroll
-                for (int dt = 0; dt < 2 * NB; ++dt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) oacc[rt][dt][i] *= ar[i];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) macc[rt][i] *= ar[i];
+                rescale_rows(rt_c, alpha);
             }
             // a masked score gives exp2(-inf) = 0, also while mrow is still kNoMax
 #pragma unroll
@@ -597,6 +582,44 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     pu[rt][4 * h + i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(sv[rt][h][i], qup, -mrow[rt]));
+        };
+        if constexpr (DS == 2) {
+            // Dim halves: each wave owns its row tile 0 (query rows 16 * half
+            // on).  It hands its partial scores of row tile 1 to its partner
+            // (whose row tile 0 they are) and adds the partner's partial of
+            // its own (a + b == b + a: both sums of a score are the same),
+            // takes the softmax of row tile 0 only, and hands over that
+            // tile's fp16 P and row maxima; the partner rescales its
+            // accumulators of those rows by the same factor exp2(old max -
+            // new max).  Two slots by tile parity: the scores a wave sends in
+            // the first half of its slot, its P and maxima in the second.
+            f4* const xo = reinterpret_cast<f4*>(wb + WN::BYTES) + (it & 1) * (RTW * 2 * 64);
+            const f4* const xp =
+                reinterpret_cast<const f4*>(smem + (wave ^ 1) * WSTR + WN::BYTES) + (it & 1) * (RTW * 2 * 64);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) xo[h * 64 + lane] = (f4){sv[1][h][0], sv[1][h][1], sv[1][h][2], sv[1][h][3]};
+            lds_barrier();
+            if (next) issue_k(tn, tb);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const f4 y = xp[h * 64 + lane];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sv[0][h][i] += y[i];
+            }
+            softmax_rows(std::integral_constant<int, 0>{});
+            *reinterpret_cast<h8*>(xo + 2 * 64 + lane) = pu[0];
+            reinterpret_cast<float*>(xo + 3 * 64)[lane] = mrow[0];
+            lds_barrier();
+            pu[1] = *reinterpret_cast<const h8*>(xp + 2 * 64 + lane);
+            const float mn = reinterpret_cast<const float*>(xp + 3 * 64)[lane];
+            if (__any(mn != mrow[1])) {
+                const float alpha = mn != mrow[1] ? __builtin_amdgcn_exp2f(mrow[1] - mn) : 1.0f;
+                mrow[1] = mn;
+                rescale_rows(std::integral_constant<int, 1>{}, alpha);
+            }
+        } else {
+            softmax_rows(std::integral_constant<int, 0>{});
+            if constexpr (RTW > 1) softmax_rows(std::integral_constant<int, RTW - 1>{});
         }
 
         if constexpr (SH) {
@@ -753,7 +776,10 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
         }
     }
     if (RS > 1)
-        for (int it = mine; it < nit; ++it) __builtin_amdgcn_s_barrier();
+        for (int it = mine; it < nit; ++it) {
+            __builtin_amdgcn_s_barrier();
+            if (DS == 2) __builtin_amdgcn_s_barrier();   // dim halves meet twice per tile
+        }
 
     // ---- finish: row sums over the four lane groups; offsets into O
     // q5_1 code products carry 2^-24 (codes as fp16 subnormals), FP8 ones
@@ -830,7 +856,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
     const size_t row0 = ((size_t)b * p.splits + s) * p.T;
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
-        const int r = rb + rt * 16 + j16;
+        const int r = rb + (rt ^ rsw) * 16 + j16;
         if (q4 == 0 && r < R && half == 0) {
             const int t = tq0 + r / p.hpk, hq = g * p.hpk + r % p.hpk;
             const size_t idx = (row0 + t) * p.H + hq;
@@ -839,7 +865,7 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int ro = rb + rt * 16 + 4 * q4 + i;
+            const int ro = rb + (rt ^ rsw) * 16 + 4 * q4 + i;
             if (ro < R) {
                 const int t = tq0 + ro / p.hpk, hq = g * p.hpk + ro % p.hpk;
                 float* o = p.part_o + ((row0 + t) * p.H + hq) * HDR + half * HD + j16;

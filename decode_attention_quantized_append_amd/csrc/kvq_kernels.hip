@@ -24,6 +24,7 @@
 #include <cmath>
 #include <cstdint>
 #include <mutex>
+#include <type_traits>
 
 #include "kvq_internal.h"
 
