@@ -596,7 +596,7 @@ def pmc_command(counter, wl):
             f"--no-others --no-ceiling")
 
 
-SQ_WORKLOADS = ("verify", "batched", "verify_f8", "batched_f8", "prime")
+SQ_WORKLOADS = ("verify", "batched", "verify_f8", "batched_f8", "prime", "prime_f8")
 SQ_PASSES = (("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU",
               "SQ_ACTIVE_INST_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VALU"),
              ("SQ_INSTS_LDS", "SQ_WAIT_ANY", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_SCA",
