@@ -269,7 +269,10 @@ def run_gpu(w, args):
         else:                                      # steady length: drop the step's rows (a ring
             check(lib.kvq_truncate(h, pre_arr, st), "truncate")   # keeps its window resident)
 
-    for i in range(args.warmup):
+    # every layer takes at least one untimed step: a ring's first step after
+    # the setup appends may rebase it (host-planned row moves), which the
+    # timed steps of a steady state do not
+    for i in range(max(args.warmup, L)):
         one_step(i)
     torch.cuda.synchronize(dev)
 
