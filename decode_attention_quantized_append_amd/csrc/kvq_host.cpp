@@ -267,10 +267,16 @@ bool choose_kernel(const kvq_cache* h, int R, int32_t T, bool f32_queries, Plan*
     if (!aligned_start_resident(h, T)) return !is_f8(c);   // FP8 rings rebase in 32-row steps: never
     // 128- and 256-dim heads with 17..32 query rows: two waves per head,
     // each half of the dims (no unpacking done twice), in independent
-    // workgroups of one head unless a head group is set
+    // workgroups of one head unless a head group is set.  FP8 rows: two
+    // heads per workgroup, whose waves then read the 16-byte pieces of a
+    // row's scale area together (with one head per workgroup those pieces
+    // were fetched from HBM about twice over: the FP8 verify kernel read
+    // 1.125 times its K and V bytes, 1.002 with two heads, and ran 7 %
+    // faster); q8_0 / q5_1 rows hold their scales in their blocks, and two
+    // heads per workgroup made the verify kernel 5 % slower.
     const bool ds = h->sub_tiles == 3 || (h->sub_tiles == 0 && stream_ds_ok(c, R, 1));
     int gh = h->head_group;
-    if (gh == 0 && ds) gh = 1;
+    if (gh == 0 && ds) gh = (is_f8(c) && c.n_kv_heads % 2 == 0 && stream_ds_ok(c, R, 2)) ? 2 : 1;
     if (gh == 0)
         // the largest head group: the waves of one workgroup share the
         // cache lines at the edges of adjacent head slices

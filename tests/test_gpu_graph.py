@@ -260,16 +260,17 @@ def test_rollback_replays_stop_at_the_floor():
     assert bs == br and ln == [br[0] + 16]
 
 
-@pytest.mark.parametrize("window", [0, 200])
-def test_graph_mode_prompt_chunks_replay(window):
+@pytest.mark.parametrize("window,fmt", [(0, "q8_0/q5_1"), (200, "q8_0/q5_1"), (200, "e4m3")])
+def test_graph_mode_prompt_chunks_replay(window, fmt):
     """Prompt chunks in graph mode: ONE captured step (append a chunk of 48
     rows per session, decode all 48 rows causally on the prime kernel, add the
     attention importance) replayed as the lengths grow by 48 per replay, each
-    replay's output, lse and importance against the oracle's at that length."""
+    replay's output, lse and importance against the oracle's at that length;
+    q8_0/q5_1 and FP8 rows."""
     rng = np.random.default_rng(480 + window)
     B, H, Hkv, hd, T, cap = 2, 16, 4, 128, 48, 1000
     pre = [300, 150]
-    p = Pair(B, H, Hkv, hd, cap, window, 0)
+    p = Pair(B, H, Hkv, hd, cap, window, 0, fmt=fmt)
     p.append(bf16_normal(rng, (B, 300, Hkv, hd)), bf16_normal(rng, (B, 300, Hkv, hd)), pre)
     g = p.gpu
     g.set_graph_mode(True)

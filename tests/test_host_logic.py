@@ -456,6 +456,16 @@ def test_decode_kernel_choice(lib):
     kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 4000, None, 0, lib)
     p = plan_of(lib, h, T=8)
     assert (p["kernel"], p["gh"], p["ds"], p["rg"]) == (STREAM, 1, 2, 1) and 4 * p["lds"] <= 160 * 1024
+    # FP8 rows: two heads per workgroup (their waves share the pieces of a
+    # row's scale area); with verify-length rows also two row streams
+    for cap, rs in ((5000, 1), (140000, 2)):
+        hf = create(lib, n_seqs=2, n_q_heads=16, n_kv_heads=4, head_dim=256, capacity=cap, fmt="e4m3")
+        kvq.kvq_append(hf, Q, Q, kvq.KVQ_BF16, cap - 100, None, 0, lib)
+        p = plan_of(lib, hf, T=8)
+        assert (p["kernel"], p["gh"], p["ds"], p["rs"]) == (STREAM, 2, 2, rs) and p["lds"] <= 160 * 1024
+    hf = create(lib, n_seqs=2, n_q_heads=16, n_kv_heads=4, head_dim=128, capacity=900, fmt="e4m3")
+    kvq.kvq_append(hf, Q, Q, kvq.KVQ_BF16, 500, None, 0, lib)
+    assert (plan_of(lib, hf, T=8)["gh"], plan_of(lib, hf, T=8)["ds"]) == (2, 2)
     kvq.kvq_set_decode_tiling(h, kvq.KVQ_DECODE_STREAM, 4, 3, lib)
     p = plan_of(lib, h, T=8)
     assert (p["kernel"], p["gh"], p["ds"]) == (STREAM, 4, 2) and p["lds"] <= 160 * 1024
