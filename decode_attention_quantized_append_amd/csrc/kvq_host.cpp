@@ -778,6 +778,13 @@ kvq_status kvq_importance(kvq_cache* h, const void* q, kvq_dtype dtype, int32_t 
     ip.tiles = (int32_t)ceil_div(std::max<int64_t>(maxspan, 1), 16);
     if (!kvq::importance_group(ip.k_row, &ip.group_rows, &ip.rp))
         return fail(KVQ_EUNSUPPORTED, "importance: 16 K rows do not fit the LDS");
+    // Many query rows (a prompt chunk): the (KV head, 16-row tile) pairs of a
+    // key group are shared by several workgroups, each adding its sums with
+    // atomics, so that the grid fills the device; up to kImpPairsPerWave
+    // pairs per wave, one workgroup per key group, whose sums are added in a
+    // fixed order.
+    const int64_t pairs = (int64_t)c.n_kv_heads * ceil_div((int64_t)T * ip.hpk, 16);
+    ip.pair_blocks = (int32_t)std::max<int64_t>(1, ceil_div(pairs, (int64_t)kvq::kImpWaves * kvq::kImpPairsPerWave));
     const char* err = nullptr;
     if (kvq::launch_importance(ip, stream, &err)) return fail(KVQ_EDEVICE, err ? err : "importance launch failed");
     return KVQ_OK;

@@ -93,10 +93,13 @@ struct ImportanceParams {
     int32_t tiles;              // 16-row tiles per session in the grid
     int32_t group_rows;         // rows (keys) per workgroup: a multiple of 16, at most 64
     int32_t rp;                 // 16-byte pieces per K row in LDS (odd, >= (k_row + 30) / 16)
+    int32_t pair_blocks;        // workgroups per key group, each a share of its (KV head, row tile) pairs
 };
 
 
 constexpr int kRowTile = 32;          // rows per tile of the stream kernel
+constexpr int kImpWaves = 8;          // waves per importance workgroup, at most
+constexpr int kImpPairsPerWave = 16;  // (KV head, row tile) pairs per importance wave before the pairs are split
 constexpr int kLdsBytes = 160 * 1024;
 
 // The importance workgroup's rows and its LDS row stride in pieces for K

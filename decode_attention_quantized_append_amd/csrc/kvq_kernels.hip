@@ -422,11 +422,12 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
 // j16: the probability 2^(log2 e (scale s - lse)) where the key is visible
 // to the row, else 0, summed over the 16 rows by DPP row rotations into the
 // wave's own LDS slot of the key.  At the end the waves' slots are added in a fixed
-// order and one thread per key adds the total to imp; a key belongs to one
-// workgroup, so no atomics are needed.  Workgroups whose keys all lie past
-// the session's length return at once (the grid covers the longest session,
-// or in graph mode the plane).
-constexpr int kImpWaves = 8;      // waves per workgroup, at most
+// order and one thread per key adds the total to imp: with one workgroup per
+// key group (pair_blocks = 1) in a fixed order, no atomics; with many query
+// rows the pairs are shared by pair_blocks workgroups (the grid's z index),
+// each adding its totals with a float atomic add.  Workgroups whose keys all
+// lie past the session's length return at once (the grid covers the longest
+// session, or in graph mode the plane).
 constexpr int kImpMaxRows = 64;   // rows (keys) per workgroup, at most
 // NB = head_dim / 32 (1 .. 8), the query dtype and the K format (F8: FP8 rows,
 // the codes then the scales; else q8_0 blocks) are template arguments.
@@ -446,6 +447,13 @@ __global__ __launch_bounds__(64 * kImpWaves) void importance_kernel(ImportancePa
     if (kg0 >= len) return;                        // past this session's rows (whole workgroup)
     const int nrows = min(GR, len - kg0);
     const int ntile = (nrows + 15) / 16;
+    // this workgroup's share of the (KV head, row tile) pairs
+    const int R = p.T * p.hpk;
+    const int nrt = (R + 15) / 16;
+    const int pairs = p.Hkv * nrt;
+    const int per_block = (pairs + p.pair_blocks - 1) / p.pair_blocks;
+    const int pair0 = blockIdx.z * per_block, pair1 = min(pairs, pair0 + per_block);
+    if (pair0 >= pair1) return;
 
     // ---- the group's K rows into LDS; pad pieces re-read a row's last one
     const uint8_t* const plane = p.k_planes + (int64_t)b * p.k_stride;
@@ -464,10 +472,7 @@ __global__ __launch_bounds__(64 * kImpWaves) void importance_kernel(ImportancePa
     stream::wait_loads_upto<0>();
     __syncthreads();
 
-    const int R = p.T * p.hpk;
-    const int nrt = (R + 15) / 16;
-    const int pairs = p.Hkv * nrt;
-    for (int pi = wave; pi < pairs; pi += nw) {
+    for (int pi = pair0 + wave; pi < pair1; pi += nw) {
         const int g = pi / nrt, rt = pi - g * nrt;
         // ---- the pair's query rows: this lane's row j16, dims 8 q4 .. of each block
         const int r = rt * 16 + j16;
@@ -563,7 +568,9 @@ __global__ __launch_bounds__(64 * kImpWaves) void importance_kernel(ImportancePa
     for (int i = threadIdx.x; i < nrows; i += blockDim.x) {
         float s = 0.0f;
         for (int w = 0; w < nw; ++w) s += slot[w][i];
-        p.imp[(size_t)b * p.capacity + (kg0 + i - base)] += s;
+        float* const dst = p.imp + (size_t)b * p.capacity + (kg0 + i - base);
+        if (p.pair_blocks == 1) *dst += s;
+        else atomicAdd(dst, s);
     }
 }
 
@@ -861,9 +868,12 @@ int launch_partials(const DecodeParams& p, hipStream_t st, const char** err) {
 
 template <bool F32>
 bool launch_importance_dtype(const ImportanceParams& p, hipStream_t st) {
-    // the (KV head, row tile) pairs over at most kImpWaves waves
+    // a workgroup's share of the (KV head, row tile) pairs over at most
+    // kImpWaves waves
     const int pairs = p.Hkv * ((p.T * p.hpk + 15) / 16);
-    const dim3 grid((p.tiles * 16 + p.group_rows - 1) / p.group_rows, p.B), block(64 * std::min(pairs, kImpWaves));
+    const int per_block = (pairs + p.pair_blocks - 1) / p.pair_blocks;
+    const dim3 grid((p.tiles * 16 + p.group_rows - 1) / p.group_rows, p.B, p.pair_blocks),
+        block(64 * std::min(per_block, kImpWaves));
     const size_t lds = (size_t)p.group_rows * p.rp * 16;
 #define KVQ_IMP(NB, F8) hipLaunchKernelGGL((importance_kernel<NB, F32, F8>), grid, block, lds, st, p); return true
     if (p.f8) {   // FP8 rows: head_dim 64, 128 or 256

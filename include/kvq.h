@@ -269,8 +269,12 @@ kvq_status kvq_decode_noalloc(kvq_cache* h, const void* q, kvq_dtype dtype, int3
  * registered with kvq_set_importance).  Call it before the cache
  * changes again.  One launch; the rows are cut into groups of up to 64
  * consecutive rows of a session, each group taken by one workgroup, which
- * alone adds to its rows; in graph mode the groups cover every length the
- * plane allows, like kvq_decode's plan.  Queries of any
+ * alone adds to its rows in a fixed order; with more than 128 (KV head,
+ * 16-row tile of T * hpk query rows) pairs (a prompt chunk) a group's pairs
+ * are shared by several workgroups, each adding its sums with a float atomic
+ * add (the order of those additions, and so the last bits, may vary between
+ * calls); in graph mode the groups cover every length the plane allows, like
+ * kvq_decode's plan.  Queries of any
  * finite magnitude are taken as kvq_decode takes them; each probability is
  * exp of a binary32 score less the lse, so its relative error grows with
  * the score's magnitude (about 1e-2 at |score| near 1e5, 1e-4 near 1e3).
