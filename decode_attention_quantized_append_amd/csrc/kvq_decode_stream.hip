@@ -587,12 +587,12 @@ __global__ __launch_bounds__(64 * (DS == 2 ? 8 : RS == 2 ? 16 : RG == 2 ? 8 : RT
             // Dim halves: each wave owns its row tile 0 (query rows 16 * half
             // on).  It hands its partial scores of row tile 1 to its partner
             // (whose row tile 0 they are) and adds the partner's partial of
-            // its own (a + b == b + a: both sums of a score are the same),
-            // takes the softmax of row tile 0 only, and hands over that
-            // tile's fp16 P and row maxima; the partner rescales its
-            // accumulators of those rows by the same factor exp2(old max -
-            // new max).  Two slots by tile parity: the scores a wave sends in
-            // the first half of its slot, its P and maxima in the second.
+            // its own, so that each score is summed once, takes the softmax
+            // of row tile 0 only, and hands over that tile's fp16 P and row
+            // maxima; the partner rescales its accumulators of those rows by
+            // the same factor exp2(old max - new max), computed from the same
+            // two maxima.  Two slots by tile parity: the scores a wave sends
+            // in the first half of its slot, its P and maxima in the second.
             f4* const xo = reinterpret_cast<f4*>(wb + WN::BYTES) + (it & 1) * (RTW * 2 * 64);
             const f4* const xp =
                 reinterpret_cast<const f4*>(smem + (wave ^ 1) * WSTR + WN::BYTES) + (it & 1) * (RTW * 2 * 64);
