@@ -193,10 +193,10 @@ struct PrimeLayout {
     static constexpr int HD = NB * 32;
     static constexpr int RAW = kRowTile * (WN::KSTR + WN::VSTR);
     static constexpr int RK = 0, RV = kRowTile * WN::KSTR;
-    // fp16 rows of a head, padded: K rows (read 16 bytes a lane, 16 rows at
-    // once) by 4 banks a row, V rows (transposed 8-byte reads of 4 rows) by
-    // 8, so that neither read meets a bank twice
-    static constexpr int ROWH = HD * 2 + 16;
+    // fp16 rows of a head, padded by 8 banks a row: K rows (read 16 bytes a
+    // lane, 16 rows at once; with a pad of 4 banks the kernel counted 4 times
+    // the bank-conflict cycles) and V rows (transposed 8-byte reads of 4 rows)
+    static constexpr int ROWH = HD * 2 + 32;
     static constexpr int ROWV = HD * 2 + 32;
     static constexpr int VMS = (NB + 4) & ~3;                   // offsets (0 for FP8 rows), then ones
     static constexpr int KH = 0;                                // fp16 [32][HD] K products, high parts

@@ -532,7 +532,7 @@ def test_decode_prime_choice(lib):
     h = create(lib, n_seqs=1, n_q_heads=32, n_kv_heads=8, head_dim=128, capacity=9000)
     kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 8192, None, 0, lib)
     p = plan_of(lib, h, T=512)
-    assert (p["kernel"], p["gh"], p["Tg"], p["groups"], p["lds"]) == (PRIME, 1, 8, 64, 106752)
+    assert (p["kernel"], p["gh"], p["Tg"], p["groups"], p["lds"]) == (PRIME, 1, 8, 64, 109824)
     assert p["chunk"] % 32 == 0 and p["units"] == p["splits"] == -(-8192 // p["chunk"])
     assert p["units"] * 8 * 8 <= 256 < -(-8192 // (p["chunk"] - 32)) * 8 * 8   # one round, no smaller chunk
     assert plan_of(lib, h, T=25)["kernel"] == PRIME          # 4 groups
@@ -552,8 +552,8 @@ def test_decode_prime_choice(lib):
     h = create(lib, n_seqs=2, n_q_heads=16, n_kv_heads=4, head_dim=64, capacity=3000)
     kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 2000, None, 0, lib)
     p = plan_of(lib, h, T=100, dtype=kvq.KVQ_F32)
-    assert (p["kernel"], p["lds"], p["groups"]) == (PRIME, 56448, 13)
-    for hd, lds in ((128, 109824), (64, 59520)):
+    assert (p["kernel"], p["lds"], p["groups"]) == (PRIME, 59520, 13)
+    for hd, lds in ((128, 112896), (64, 62592)):
         h = create(lib, n_seqs=1, n_q_heads=32, n_kv_heads=8, head_dim=hd, capacity=3000, fmt="e4m3")
         kvq.kvq_append(h, Q, Q, kvq.KVQ_BF16, 2000, None, 0, lib)
         p = plan_of(lib, h, T=200)
