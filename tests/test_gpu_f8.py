@@ -275,3 +275,39 @@ def test_f8_per_head_kernel_is_refused():
     with pytest.raises(kvq.KvqError) as e:
         p.gpu.decode(to_dev(q, "bf16"), scale)
     assert e.value.status == kvq.KVQ_EINVAL
+
+
+# Kernels and tilings (kernel, KV heads per workgroup, waves per KV head) that
+# fit each FP8 shape: the prime kernel and the stream kernel's layouts.
+PR, ST, AUTO = kvq.KVQ_DECODE_PRIME, kvq.KVQ_DECODE_STREAM, kvq.KVQ_DECODE_AUTO
+F8_TILINGS = {
+    "qwen_gqa": [(ST, 8, 0), (ST, 4, 0), (ST, 2, 0), (ST, 8, 1), (ST, 8, 2)],
+    "verify_dimhalves": [(ST, 0, 0), (ST, 1, 3), (ST, 2, 3), (ST, 4, 3), (ST, 0, 2), (ST, 0, 1)],
+    "hd128_T8_dimhalves": [(ST, 1, 3), (ST, 2, 3), (ST, 0, 2)],
+    "prime_T100": [(PR, 0, 0), (ST, 0, 0), (ST, 0, 3), (ST, 0, 2)],
+    "prime_hd64_f32": [(PR, 0, 0), (ST, 0, 0), (ST, 0, 2)],
+}
+
+
+@pytest.mark.parametrize("name", sorted(F8_TILINGS))
+def test_f8_plans_exact_weights(name):
+    """With zero queries every visible row scores 0 and every weight is
+    exactly 1, and so is each weight times its FP8 step: the output is the
+    mean of the visible V rows (the sink in the denominator) up to the fp32
+    summation, for every kernel, tiling and split plan, within 1e-5 of the V
+    scale (a row dropped, counted twice or masked wrongly shows up)."""
+    p, q, s, scale = build(name)
+    q = np.zeros_like(q)
+    io = SHAPES[name][10]
+    qd = to_dev(q, io)
+    sd = torch.from_numpy(s).to(DEV) if s is not None else None
+    want, want_lse = p.ref.attention(q, scale=scale, sinks=s)
+    atol = 1e-5 * max(1.0, p.vmax)
+    for kernel, gh, sub in [(AUTO, 0, 0)] + F8_TILINGS[name]:
+        p.gpu.set_decode_tiling(kernel, gh, sub)
+        for rows_ in (0, 64, 256):
+            p.gpu.set_split_rows(rows_)
+            o, l = p.gpu.decode(qd, scale, sinks=sd)
+            what = f"f8 {name} kernel={kernel} gh={gh} sub={sub} split={rows_}"
+            np.testing.assert_allclose(o.cpu().numpy(), want, atol=atol, rtol=0, err_msg=what)
+            np.testing.assert_allclose(l.cpu().numpy(), want_lse, atol=1e-5, rtol=0, err_msg=what)
