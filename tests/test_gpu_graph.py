@@ -72,11 +72,13 @@ def test_step_graph_replays_equal_eager(B, H, Hkv, hd, lens):
         assert torch.equal(out, want), f"eager step after replay {r} differs"
 
 
-@pytest.mark.parametrize("B,H,Hkv,hd,window,cap,step,pre,steps",
-                         [(2, 32, 8, 128, 0, 700, 0, [500, 77], 24),            # flat: the grid covers the plane
-                          (2, 16, 4, 64, 64, 128, 32, [200, 170], 20),         # ring: window + T - 1 + 31 rows
-                          (1, 16, 4, 256, 0, 500, 0, [300], 12)])
-def test_graph_mode_replays_as_lengths_grow(B, H, Hkv, hd, window, cap, step, pre, steps):
+@pytest.mark.parametrize("B,H,Hkv,hd,window,cap,step,pre,steps,fmt",
+                         [(2, 32, 8, 128, 0, 700, 0, [500, 77], 24, "q8_0/q5_1"),     # flat: the grid covers the plane
+                          (2, 16, 4, 64, 64, 128, 32, [200, 170], 20, "q8_0/q5_1"),  # ring: window + T - 1 + 31 rows
+                          (1, 16, 4, 256, 0, 500, 0, [300], 12, "q8_0/q5_1"),
+                          (2, 32, 8, 128, 0, 700, 0, [500, 77], 24, "e4m3"),          # FP8 rows, flat and ring
+                          (2, 16, 4, 64, 64, 128, 32, [200, 170], 20, "e4m3")])
+def test_graph_mode_replays_as_lengths_grow(B, H, Hkv, hd, window, cap, step, pre, steps, fmt):
     """Graph mode: ONE captured step (append a row per session, decode, add
     the attention importance) is replayed `steps` times with no host call
     between replays, each time on the next row and query written into the
@@ -84,7 +86,7 @@ def test_graph_mode_replays_as_lengths_grow(B, H, Hkv, hd, window, cap, step, pr
     every replay's output and importance are the oracle's at that length.  Afterwards the host mirror is set from the
     device counters and eager steps continue (through a ring rebase)."""
     rng = np.random.default_rng(hd + cap)
-    p = Pair(B, H, Hkv, hd, cap, window, step)
+    p = Pair(B, H, Hkv, hd, cap, window, step, fmt=fmt)
     done = np.zeros(B, np.int64)
     while np.any(done < pre):                    # pieces a ring can take without dropping visible rows
         n = np.minimum(np.asarray(pre) - done, 32)
@@ -186,15 +188,16 @@ def test_graph_replay_past_the_plane_stops_at_capacity():
     p.check_planes()
 
 
-def test_graph_mode_verify_rounds_replay():
+@pytest.mark.parametrize("fmt", ["q8_0/q5_1", "e4m3"])
+def test_graph_mode_verify_rounds_replay(fmt):
     """A speculative-verify round (append 8 drafted rows, decode them
     causally, roll back the 5 not accepted) captured once in graph mode and
     replayed: each replay keeps 3 more rows, and every replay's output is the
-    oracle's."""
+    oracle's; q8_0/q5_1 and FP8 rows."""
     rng = np.random.default_rng(77)
     B, H, Hkv, hd, T, keep = 2, 16, 4, 256, 8, 3
     pre = [300, 177]
-    p = Pair(B, H, Hkv, hd, 420)
+    p = Pair(B, H, Hkv, hd, 420, fmt=fmt)
     p.append(bf16_normal(rng, (B, 300, Hkv, hd)), bf16_normal(rng, (B, 300, Hkv, hd)), pre)
     g = p.gpu
     g.set_graph_mode(True)
