@@ -16,8 +16,8 @@ pytestmark = pytest.mark.gpu
 from gpu_pair import DEV, Pair, assert_close, to_dev  # noqa: E402
 
 
-def filled(rng, B, H, Hkv, hd, lens, io):
-    p = Pair(B, H, Hkv, hd, max(lens) + 16, io=io)
+def filled(rng, B, H, Hkv, hd, lens, io, fmt="q8_0/q5_1"):
+    p = Pair(B, H, Hkv, hd, max(lens) + 16, io=io, fmt=fmt)
     lens = np.asarray(lens)
     done = np.zeros(B, np.int64)
     while np.any(done < lens):
@@ -62,6 +62,17 @@ def test_noalloc_equals_decode_two_calls_second_smaller():
     both(small, rng, 1, "f32")
     # and the first handle again
     both(big, rng, 2, "bf16")
+
+
+def test_noalloc_prompt_chunk_and_fp8_rows():
+    """FP8 rows: a prompt chunk of 64 rows (eight groups of query rows, the
+    prime kernel), then a smaller verify-like call on another handle, each
+    equal to kvq_decode bit for bit."""
+    rng = np.random.default_rng(79)
+    chunk = filled(rng, 1, 32, 8, 128, [900], "bf16", fmt="e4m3")
+    both(chunk, rng, 64, "bf16", sinks=True)
+    small = filled(rng, 2, 16, 4, 256, [400, 200], "bf16", fmt="e4m3")
+    both(small, rng, 8, "bf16")
 
 
 def test_noalloc_refuses_partials_beyond_the_scratch():
