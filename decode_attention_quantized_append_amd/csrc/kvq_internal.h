@@ -99,7 +99,7 @@ struct ImportanceParams {
 
 constexpr int kRowTile = 32;          // rows per tile of the stream kernel
 constexpr int kImpWaves = 8;          // waves per importance workgroup, at most
-constexpr int kImpPairsPerWave = 16;  // (KV head, row tile) pairs per importance wave before the pairs are split
+constexpr int kImpPairsPerWave = 4;   // (KV head, row tile) pairs per importance wave before the pairs are split
 constexpr int kLdsBytes = 160 * 1024;
 
 // The importance workgroup's rows and its LDS row stride in pieces for K

@@ -269,7 +269,7 @@ kvq_status kvq_decode_noalloc(kvq_cache* h, const void* q, kvq_dtype dtype, int3
  * registered with kvq_set_importance).  Call it before the cache
  * changes again.  One launch; the rows are cut into groups of up to 64
  * consecutive rows of a session, each group taken by one workgroup, which
- * alone adds to its rows in a fixed order; with more than 128 (KV head,
+ * alone adds to its rows in a fixed order; with more than 32 (KV head,
  * 16-row tile of T * hpk query rows) pairs (a prompt chunk) a group's pairs
  * are shared by several workgroups, each adding its sums with a float atomic
  * add (the order of those additions, and so the last bits, may vary between

@@ -221,7 +221,7 @@ def test_f8_importance_parity():
             (2, 32, 8, 128, 1, [700, 300], 0, 720, 0, False, "bf16"),
             (2, 16, 4, 64, 1, [330, 250], 64, 128, 32, True, "bf16"),
             (1, 16, 4, 256, 8, [400], 0, 420, 0, True, "f32"),
-            (1, 32, 8, 128, 160, [700], 0, 720, 0, False, "bf16")):   # 320 pairs, 3 workgroups per key group
+            (1, 32, 8, 128, 160, [700], 0, 720, 0, False, "bf16")):   # 320 pairs, 10 workgroups per key group
         p = Pair(B, H, Hkv, hd, cap, window, step, io=io, fmt=F8)
         done = np.zeros(B, np.int64)
         while np.any(done < lens):

@@ -272,7 +272,7 @@ IMPORTANCE = {
     "hd256_verify_f32": (1, 16, 4, 256, 8, [400], 0, 420, 0, True, "f32"),
     "hd128_prime_window": (1, 8, 2, 128, 40, [300], 100, 320, 0, True, "bf16"),
     # prompt chunks with more (KV head, 16-row tile) pairs than one workgroup
-    # per key group takes: 400 and 300 pairs, shared by 4 and 3 workgroups
+    # per key group takes: 400 and 300 pairs, shared by 13 and 10 workgroups
     "hd128_prime_T200_shared_pairs": (2, 32, 8, 128, 200, [900, 260], 300, 920, 0, True, "bf16"),
     "hd64_prime_T300_shared_pairs_f32": (1, 16, 2, 64, 300, [600], 0, 620, 0, False, "f32"),
 }
