@@ -666,6 +666,14 @@ def summarize_profiles(d):
             t = dd[-steps:]
             avg[n] = sum(t) / len(t)
             L.append(f"| `{n}` | {len(t)} | {avg[n]:.2f} | {min(t):.2f} | {max(t):.2f} |")
+        # the eager timed steps: after max(warmup, layers) untimed steps, the
+        # dispatches whose duration the bench line's kernel_ms measures
+        eager = {}
+        if b:
+            w0 = max(b["warmup"], b["config"].get("layers_rotated", 1))
+            for n, dd in by.items():
+                if "decode_" in n and len(dd) >= w0 + b["steps"]:
+                    eager[n] = dd[w0:w0 + b["steps"]]
         w = W.get(wl)
         dec = sum(v for k, v in avg.items() if "decode_" in k)
         com = sum(v for k, v in avg.items() if "combine" in k)
@@ -676,6 +684,9 @@ def summarize_profiles(d):
               f"- over the traced partials kernel: {kv / (dec * 1e-6) / 1e9:.1f} GB/s "
               f"({kv / (dec * 1e-6) / 1e9 / HBM_PEAK_GBPS:.4f} of 8 TB/s); over partials + combine "
               f"({dec:.2f} + {com:.2f} us): {kv / ((dec + com) * 1e-6) / 1e9:.1f} GB/s"]
+        for n, t in eager.items():
+            L.append(f"- `{n}` in the eager timed steps (dispatches {w0 + 1}..{w0 + len(t)}, the ones the bench "
+                     f"line's kernel_ms times): avg {sum(t) / len(t):.2f} us, min {min(t):.2f}, max {max(t):.2f}")
         if b:
             ro = b["roofline"]
             L += [f"- the same run's bench line (under the profiler): partials kernel "
