@@ -636,11 +636,11 @@ def _bench_line(log):
     return None
 
 
-def summarize_profiles(d):
+def summarize_profiles(d, out_dir=None):
     import collections
 
     from decode_attention_quantized_append_amd import workloads as W
-    out_dir = os.path.join(ROOT, "profiles")
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
     H = source_hash()
     for wl in TRACE_WORKLOADS:
         path = os.path.join(d, f"trace_{wl}")
