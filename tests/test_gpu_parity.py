@@ -345,17 +345,18 @@ def test_registered_importance_follows_rebases(fmt):
     assert rebases >= 3
 
 
-@pytest.mark.parametrize("step", [32, 20])
-def test_chunked_prime_into_ring(step):
+@pytest.mark.parametrize("step,fmt", [(32, "q8_0/q5_1"), (20, "q8_0/q5_1"), (32, "e4m3"), (64, "e4m3")])
+def test_chunked_prime_into_ring(step, fmt):
     """A prompt primed into a sliding-window ring of kvq_ring_rows rows in
     chunks of up to C rows: each chunk's rows are appended, then its rows
     attend causally (each within its window) to what the ring holds, through
-    the stream kernel (its 32-aligned start stays resident).  Every chunk's
-    outputs against the oracle's."""
+    the prime kernel for the 48-row chunks (six groups of query rows) and the
+    stream kernel for the smaller ones, whose 32-aligned start stays resident;
+    q8_0/q5_1 and FP8 rows.  Every chunk's outputs against the oracle's."""
     rng = np.random.default_rng(21 + step)
     B, H, Hkv, hd, W, C = 2, 16, 4, 64, 64, 48
     cap = kvq.kvq_ring_rows(W, C, step)
-    p = Pair(B, H, Hkv, hd, cap, W, step)
+    p = Pair(B, H, Hkv, hd, cap, W, step, fmt=fmt)
     s = rng.standard_normal(H).astype(np.float32)
     for it in range(12):
         n = C if it < 8 else int(rng.integers(1, C + 1))
