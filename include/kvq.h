@@ -316,7 +316,7 @@ kvq_status kvq_set_split_rows(kvq_cache* h, int32_t rows);
 /* Decode kernels (kvq_set_decode_tiling).  The value 2 is not used. */
 typedef enum kvq_decode_kernel {
     KVQ_DECODE_AUTO = 0,        /* chosen per call */
-    KVQ_DECODE_PER_HEAD = 1,    /* one KV head per workgroup, any head_dim */
+    KVQ_DECODE_PER_HEAD = 1,    /* one KV head per workgroup, any head_dim, q8_0 / q5_1 rows only */
     KVQ_DECODE_STREAM = 3,      /* one or two waves per KV head, each streaming its rows through LDS */
     KVQ_DECODE_PRIME = 4        /* many query rows per KV head (a prompt chunk): eight groups of query
                                  * rows share each KV tile, converted once; q8_0 / q5_1 or FP8 rows,
@@ -336,10 +336,11 @@ typedef enum kvq_decode_kernel {
  * and more than one group of 32 / hpk query rows.  A
  * kernel or tiling that does not fit a call's shape makes that kvq_decode
  * fail with EINVAL, except that a session whose first visible row, rounded
- * down to 32, was rebased away is served by the per-head kernel.  The
+ * down to 32, was rebased away is served by the per-head kernel (FP8
+ * rings rebase in steps of 32 rows, so it never happens to them).  The
  * automatic choice takes the prime kernel from four groups of query rows
- * on.  The result does not depend on the choice beyond
- * float rounding.
+ * on; for FP8 rows with dim halves it puts two KV heads in a workgroup.
+ * The result does not depend on the choice beyond float rounding.
  * Errors: EINVAL (unknown kernel, head_group not dividing n_kv_heads,
  * head_group or sub_tiles given for a kernel other than the stream one). */
 kvq_status kvq_set_decode_tiling(kvq_cache* h, int32_t kernel, int32_t head_group, int32_t sub_tiles);
